@@ -1,0 +1,6 @@
+"""CPU oracle for KDA: test infrastructure, never part of the product path.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+import anything under this directory.
+"""
+from .kda_oracle import kda_recurrence, kda_decode_step, as_f64  # noqa: F401
