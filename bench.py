@@ -1,0 +1,239 @@
+"""KDA benchmark on one MI355X: chunked prefill tokens/s (plus decode state
+GB/s) with roofline fractions and the CPU oracle as a reported baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+
+A step is one kda_prefill_chunked call over the H=16, T=4096, d=128 bf16
+workload (B=1, C=64, inputs already resident in HBM).  Prints ONE JSON line.
+Alongside the headline it measures, on the same GPU:
+  * decode: 256 sequences x 32 heads, 64 KiB fp32 state per head, in-place
+    kda_decode_step calls (state GB/s against the HBM peak);
+  * the B=8, H=32, T=8192 prefill (tokens/s and roofline);
+  * the float64 oracle on the host cores over a bounded sample (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def prefill_alg_bytes(B, T, H, dk, dv, esize, with_s0):
+    """Inputs and outputs only: q, k, v, o in the I/O dtype, fp32 alpha and
+    beta, the final state (and the initial state when one is given)."""
+    tok = B * T * H
+    per_tok = esize * (2 * dk + dv) + 4 * dk + 4 + esize * dv
+    state = B * H * dk * dv * 4
+    return tok * per_tok + state * (2 if with_s0 else 1)
+
+
+def prefill_flops(B, T, H, dk, dv, C):
+    """Useful flops: 6 dk dv per token-head for the state work (W S, Q S,
+    K^T U) plus 2 C (3 dk + 2 dv) for the chunk-local products (gated K K^T,
+    gated Q K^T, W, U~, P U)."""
+    return B * T * H * (6 * dk * dv + 2 * C * (3 * dk + 2 * dv))
+
+
+def decode_alg_bytes(N, H, dk, dv, esize):
+    per_head = 2 * dk * dv * 4 + esize * (2 * dk + dv) + 4 * dk + 4 + esize * dv
+    return N * H * per_head
+
+
+def time_launches(fn, steps, warmup, torch):
+    """Warm up, then time `steps` calls bracketed by synchronisations, with
+    HIP events on the current stream (the stream the kernels run on)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        fn()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / steps, wall * 1e3 / steps
+
+
+def _oracle_chain(args):
+    import numpy as np  # noqa: F401
+    from oracle import kda_recurrence
+    q, k, v, a, b = args
+    t = time.perf_counter()
+    kda_recurrence(q, k, v, a, b, None)
+    return time.perf_counter() - t
+
+
+def cpu_baseline(inp, torch):
+    """The float64 oracle as it stands, one process per host core, each
+    running whole (b, h) chains with single-threaded BLAS."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    B, T, H, _ = inp["q"].shape
+    chains = [(inp["q"][b:b + 1, :, h:h + 1].numpy(), inp["k"][b:b + 1, :, h:h + 1].numpy(),
+               inp["v"][b:b + 1, :, h:h + 1].numpy(), inp["alpha"][b:b + 1, :, h:h + 1].numpy(),
+               inp["beta"][b:b + 1, :, h:h + 1].numpy())
+              for b in range(B) for h in range(H)]
+    cores = min(len(os.sched_getaffinity(0)), 16, len(chains))
+    t0 = time.perf_counter()
+    ctx = mp.get_context("spawn")
+    with cf.ProcessPoolExecutor(max_workers=cores, mp_context=ctx,
+                                initializer=_single_thread_blas) as ex:
+        busy = sum(ex.map(_oracle_chain, chains))
+    wall = time.perf_counter() - t0
+    return dict(value=B * T / wall, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"the whole H=16 T=4096 d=128 workload ({B * T * H} token-heads, "
+                       f"{len(chains)} chains over {cores} processes); {busy:.1f} core-s of "
+                       f"oracle work, {wall:.1f} s wall",
+                tok_heads_per_s=B * T * H / wall)
+
+
+def _single_thread_blas():
+    for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[v] = "1"
+    sys.path.insert(0, ROOT)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="headline prefill only (no decode / large prefill lines)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(chains are independent, so N GPUs would each run their own share).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_108_amd as kda
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    out = {}
+
+    # ---------------- headline: prefill, H=16, T=4096, d=128, bf16, C=64
+    spec = wl.PREFILL["prefill_h16_t4k"]
+    C = 64
+    inp_cpu = wl.make_prefill_inputs(spec, "cpu")
+    g = {k: (None if t is None else t.to(dev)) for k, t in inp_cpu.items()}
+    o = torch.empty(spec.B, spec.T, spec.H, spec.dv, dtype=spec.dtype, device=dev)
+    S_T = torch.empty(spec.B, spec.H, spec.dk, spec.dv, dtype=torch.float32, device=dev)
+
+    def step():
+        kda.prefill_chunked(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["S0"], chunk=C,
+                            out=o, state_out=S_T)
+
+    ms_ev, ms_wall = time_launches(step, args.steps, args.warmup, torch)
+    B, T, H, dk, dv = spec.B, spec.T, spec.H, spec.dk, spec.dv
+    nbytes = prefill_alg_bytes(B, T, H, dk, dv, 2, g["S0"] is not None)
+    flops = prefill_flops(B, T, H, dk, dv, C)
+    gbs = nbytes / (ms_ev * 1e-3) / 1e9
+    tfl = flops / (ms_ev * 1e-3) / 1e12
+    tokens_per_s = B * T / (ms_wall * 1e-3)
+    out.update({
+        "metric": "KDA prefill tokens/s + % bf16 MFMA peak; decode state GB/s + % HBM peak",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_wall,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_h16_t4k", "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
+                   "C": C, "io_dtype": "bf16", "state_dtype": "fp32"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kda_prefill_kernel<bf16,128,64,16>",
+                     "kernel_ms": ms_ev, "alg_bytes_per_launch": nbytes},
+        "mfma": {"achieved_tflops": tfl, "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                 "frac": tfl / MFMA_BF16_PEAK_TFLOPS, "flops_per_launch": flops},
+        "tok_heads_per_s": B * T * H / (ms_wall * 1e-3),
+    })
+    print(f"# prefill_h16_t4k: {ms_ev * 1e3:.1f} us/launch (events), {gbs:.0f} GB/s, "
+          f"{tfl:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    if not args.no_extra:
+        # ---------------- decode: 256 x 32 heads, d = 128, in place
+        dspec = wl.DECODE["decode_n256_h32"]
+        S = wl.make_decode_state(dspec, dev)
+        nst = 8
+        st = wl.make_decode_steps(dspec, dev, steps=nst)
+        od = torch.empty(dspec.N, dspec.H, dspec.dv, dtype=dspec.dtype, device=dev)
+        it = [0]
+
+        def dstep():
+            i = it[0] % nst
+            it[0] += 1
+            kda.decode_step(st["q"][i], st["k"][i], st["v"][i], st["alpha"][i], st["beta"][i],
+                            S, out=od)
+
+        dsteps = max(args.steps, 20)
+        ms_d, ms_dw = time_launches(dstep, dsteps, args.warmup, torch)
+        state_bytes = 2 * dspec.N * dspec.H * dspec.dk * dspec.dv * 4
+        dbytes = decode_alg_bytes(dspec.N, dspec.H, dspec.dk, dspec.dv, 2)
+        out["decode"] = {
+            "workload": "decode_n256_h32", "N": dspec.N, "H": dspec.H, "dk": dspec.dk,
+            "dv": dspec.dv, "us_per_step": ms_d * 1e3,
+            "state_GBps": state_bytes / (ms_d * 1e-3) / 1e9,
+            "alg_GBps": dbytes / (ms_d * 1e-3) / 1e9,
+            "frac_hbm": dbytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "head_steps_per_s": dspec.N * dspec.H / (ms_dw * 1e-3),
+        }
+        print(f"# decode_n256_h32: {ms_d * 1e3:.1f} us/step, "
+              f"{out['decode']['alg_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+        del S, st, od
+        torch.cuda.empty_cache()
+
+        # ---------------- large prefill: B=8, H=32, T=8192
+        lspec = wl.PREFILL["prefill_b8_h32_t8k"]
+        lg = wl.make_prefill_inputs(lspec, dev)
+        lo = torch.empty(lspec.B, lspec.T, lspec.H, lspec.dv, dtype=lspec.dtype, device=dev)
+        lS = torch.empty(lspec.B, lspec.H, lspec.dk, lspec.dv, dtype=torch.float32, device=dev)
+
+        def lstep():
+            kda.prefill_chunked(lg["q"], lg["k"], lg["v"], lg["alpha"], lg["beta"], lg["S0"],
+                                chunk=64, out=lo, state_out=lS)
+
+        lsteps = max(3, args.steps // 5)
+        ms_l, ms_lw = time_launches(lstep, lsteps, 2, torch)
+        lb = prefill_alg_bytes(lspec.B, lspec.T, lspec.H, 128, 128, 2, True)
+        lf = prefill_flops(lspec.B, lspec.T, lspec.H, 128, 128, 64)
+        out["prefill_b8_h32_t8k"] = {
+            "C": 64, "ms_per_launch": ms_l, "tokens_per_s": lspec.B * lspec.T / (ms_lw * 1e-3),
+            "GBps": lb / (ms_l * 1e-3) / 1e9, "frac_hbm": lb / (ms_l * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "tflops": lf / (ms_l * 1e-3) / 1e12,
+            "frac_mfma": lf / (ms_l * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        }
+        print(f"# prefill_b8_h32_t8k: {ms_l:.3f} ms/launch", file=sys.stderr, flush=True)
+        del lg, lo, lS
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(inp_cpu, torch)
+        print(f"# cpu_baseline: {out['cpu_baseline']['value']:.1f} tokens/s",
+              file=sys.stderr, flush=True)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

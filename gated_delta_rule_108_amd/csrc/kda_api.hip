@@ -1,0 +1,147 @@
+// C ABI of libkda: argument validation, then dispatch to the kernels.
+// Every check runs on the host before any launch; see include/kda.h for the
+// contract of each entry point.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/kda.h"
+#include "kda_launch.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other.  Only caches an immutable fact.
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+kda_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return KDA_ERR_DEVICE;
+  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return KDA_ERR_HIP;
+    st = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? KDA_OK : KDA_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Span span(const void* p, size_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Span{a, a + bytes};
+}
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "a size is out of range";
+    case KDA_ERR_UNSUPPORTED: return "unsupported dk, dv, chunk size or dtype";
+    case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case KDA_ERR_ALIAS: return "an output overlaps an input";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_DEVICE: return "current device is not gfx950";
+    case KDA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t kda_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int C, kda_dtype dt) {
+  if (B < 1 || H < 1 || T < 0) return static_cast<size_t>(-1);
+  if (dt != KDA_F32 && dt != KDA_BF16) return static_cast<size_t>(-1);
+  if (!dim_ok(dk) || !dim_ok(dv)) return static_cast<size_t>(-1);
+  if (!kda::prefill_supported(dk, dv, C, dt == KDA_BF16)) return static_cast<size_t>(-1);
+  return 0;
+}
+
+kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, const float* S0, void* o, float* S_T, int B,
+                               int T, int H, int dk, int dv, int C, kda_dtype dt, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (B < 1 || H < 1 || T < 0) return KDA_ERR_SHAPE;
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+  if (!kda::prefill_supported(dk, dv, C, dt == KDA_BF16)) return KDA_ERR_UNSUPPORTED;
+  const bool has_tokens = T > 0;
+  if (has_tokens && (!q || !k || !v || !alpha || !beta || !o)) return KDA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, alpha, beta, S0, o, S_T, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+  (void)workspace_bytes;  // the current kernels need none (query returns 0)
+
+  const size_t e = (dt == KDA_BF16) ? 2 : 4;
+  const size_t ntok = static_cast<size_t>(B) * T * H;
+  const size_t nst = static_cast<size_t>(B) * H * dk * dv * 4;
+  if (has_tokens) {
+    const Span so = span(o, ntok * dv * e);
+    const Span ins[] = {span(q, ntok * dk * e), span(k, ntok * dk * e), span(v, ntok * dv * e),
+                        span(alpha, ntok * dk * 4), span(beta, ntok * 4),
+                        S0 ? span(S0, nst) : Span{0, 0}, S_T ? span(S_T, nst) : Span{0, 0}};
+    for (const Span& s : ins)
+      if (overlap(so, s)) return KDA_ERR_ALIAS;
+  }
+  if (S_T) {
+    const Span st = span(S_T, nst);
+    if (S0 && S0 != S_T && overlap(st, span(S0, nst))) return KDA_ERR_ALIAS;
+    if (has_tokens) {
+      const Span ins[] = {span(q, ntok * dk * e), span(k, ntok * dk * e), span(v, ntok * dv * e),
+                          span(alpha, ntok * dk * 4), span(beta, ntok * 4)};
+      for (const Span& s : ins)
+        if (overlap(st, s)) return KDA_ERR_ALIAS;
+    }
+  }
+  const kda_status dev = check_device();
+  if (dev != KDA_OK) return dev;
+  if (!S_T && !has_tokens) return KDA_OK;  // nothing to compute or write
+
+  kda::PrefillArgs a{q, k, v, alpha, beta, S0, o, S_T, B, T, H, dk, dv, C, dt == KDA_BF16, stream};
+  if (kda::launch_prefill(a) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* S_in, void* o, float* S_out, int N,
+                           int H, int dk, int dv, kda_dtype dt, void* stream) {
+  if (N < 1 || H < 1) return KDA_ERR_SHAPE;
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !alpha || !beta || !S_in || !o || !S_out) return KDA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, alpha, beta, S_in, o, S_out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return KDA_ERR_ALIGN;
+  const size_t e = (dt == KDA_BF16) ? 2 : 4;
+  const size_t nh = static_cast<size_t>(N) * H;
+  const size_t nst = nh * dk * dv * 4;
+  const Span ins[] = {span(q, nh * dk * e), span(k, nh * dk * e), span(v, nh * dv * e),
+                      span(alpha, nh * dk * 4), span(beta, nh * 4), span(S_in, nst)};
+  const Span so = span(o, nh * dv * e), ss = span(S_out, nst);
+  for (const Span& s : ins)
+    if (overlap(so, s)) return KDA_ERR_ALIAS;
+  for (int i = 0; i < 5; ++i)
+    if (overlap(ss, ins[i])) return KDA_ERR_ALIAS;
+  if (overlap(so, ss)) return KDA_ERR_ALIAS;
+  if (S_out != S_in && overlap(ss, ins[5])) return KDA_ERR_ALIAS;  // equal is in place
+  const kda_status dev = check_device();
+  if (dev != KDA_OK) return dev;
+  kda::DecodeArgs a{q, k, v, alpha, beta, S_in, o, S_out, N, H, dk, dv, dt == KDA_BF16, stream};
+  if (kda::launch_decode(a) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// Host-side launch descriptors shared by the C ABI (kda_api.hip) and the
+// kernel translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace kda {
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* S_in;
+  void* o;
+  float* S_out;
+  int N, H, dk, dv;
+  bool bf16;
+  void* stream;
+};
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* S0;   // may be null (zeros)
+  void* o;
+  float* S_T;        // may be null (not written)
+  int B, T, H, dk, dv, C;
+  bool bf16;
+  void* stream;
+};
+
+hipError_t launch_decode(const DecodeArgs& a);
+
+// Returns hipErrorInvalidValue when no compiled kernel covers (dk, C, dtype).
+hipError_t launch_prefill(const PrefillArgs& a);
+bool prefill_supported(int dk, int dv, int C, bool bf16);
+
+}  // namespace kda

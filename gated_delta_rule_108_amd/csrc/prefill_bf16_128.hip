@@ -1,0 +1,6 @@
+// Chunked-prefill kernels for bf16 q/k/v/o and dk = 128.
+#include "prefill_kernel.hpp"
+
+namespace kda {
+KDA_PREFILL_INSTANCE(bf16_t, bf16, 128)
+}  // namespace kda

@@ -1,0 +1,6 @@
+// Chunked-prefill kernels for f32 q/k/v/o and dk = 32.
+#include "prefill_kernel.hpp"
+
+namespace kda {
+KDA_PREFILL_INSTANCE(float, f32, 32)
+}  // namespace kda

@@ -1,0 +1,780 @@
+// KDA chunked prefill: one fused kernel per (chain, dv tile).
+//
+// A workgroup of four waves owns one (batch, head) chain and a DVT-wide
+// column slab of its dk x dv state, and walks the chunks of C tokens in
+// order.  The fp32 state slab lives in registers for the whole sequence;
+// every per-chunk intermediate lives in LDS; HBM sees each input once and
+// each output once.  (Columns of the state evolve independently, so slabs of
+// one chain run in parallel workgroups; they recompute the column-free
+// chunk work and share its inputs through L2.)
+//
+// Chunk algebra.  For a chunk with start state S, rows r = 0..C-1 and the
+// per-channel cumulative decay E_r = prod_{j<=r} alpha_j (E'_r = prod_{j>r}):
+//   A[r][i]  = sum_c k_r[c] k_i[c] E_r[c]/E_i[c]       (i <  r)  gated K K^T
+//   P[r][i]  = sum_c q_r[c] k_i[c] E_r[c]/E_i[c]       (i <= r)  gated Q K^T
+//   (I + L) Y = I,   L = strict_lower(Diag(beta) A)            UT transform
+//   W = Y Diag(beta) (K . E),   U~ = Y Diag(beta) V             WY factors
+//   U = U~ - W S
+//   O = (Q . E) S + P U
+//   S <- Diag(E_{C-1}) S + (K . E')^T U
+// With alpha = 1 this is the chunkwise delta rule of "From GPT-2 to Kimi K3,
+// Explained", section "DeltaNet (Parallelizing Linear Transformers with Delta
+// Rule)" (T there is Y Diag(beta), built by forward substitution; the
+// correction u = U - W S; o = q S + tril(q k^T) u; S += k^T u).  The ratio
+// E_r/E_i is the cumulative decay of section "Gated Delta Net", one value per
+// channel as in section "KDA/Kimi Linear".
+//
+// Overflow-free gates.  E_r/E_i is never formed as a quotient of chunk-level
+// products (E_i underflows fp32 within one chunk for strong gates).  The
+// chunk is cut into 16-row sub-blocks; within block J, F_r = prod of alpha
+// from the block start through r and H_i = prod from i+1 through the block
+// end.  For r in block R and i in block I < R
+//     E_r/E_i = F_r * prod_{I<J<R} BT_J * H_i          (every factor <= 1)
+// with BT_J the block's total decay, so the off-diagonal 16x16 tiles of A and
+// P are products of pre-scaled operands on the matrix cores.  On diagonal
+// tiles the ratio is F_r * (1/F_i), exact as long as the block total stays
+// above 2^-100 per channel; a channel below that (a zero gate, or extreme
+// decay) is masked out of the matrix product and added exactly on the vector
+// units from running products of alpha.
+#pragma once
+
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+constexpr float kUnsafeBlockDecay = 7.888609052210118e-31f;  // 2^-100
+
+// ----------------------------------------------------------------------------
+// MFMA fragment sources.  A source yields, for the calling lane, the operand
+// fragment of rows row0 + (lane % 16) and contraction indices k0 + n*(lane/16)
+// .. + n-1, n = 8 (bf16, K=32), 4 (bf16, K=16) or 1 (fp32, K=4).
+// ----------------------------------------------------------------------------
+template <typename OpT, int KS> struct Frag;
+template <> struct Frag<bf16_t, 32> { using T = bf16x8; static constexpr int N = 8; };
+template <> struct Frag<bf16_t, 16> { using T = bf16x4; static constexpr int N = 4; };
+template <> struct Frag<float, 4> { using T = float; static constexpr int N = 1; };
+
+__device__ __forceinline__ int lane_g() { return (threadIdx.x & 63) >> 4; }
+__device__ __forceinline__ int lane_i() { return threadIdx.x & 15; }
+
+// OpT rows, K-contiguous.
+template <typename OpT> struct Src {
+  using E = typename Ty<OpT>::Elem;
+  const E* p;
+  int ld;
+  template <int KS>
+  __device__ __forceinline__ typename Frag<OpT, KS>::T get(int k0) const {
+    using F = Frag<OpT, KS>;
+    const E* a = p + lane_i() * ld + k0 + F::N * lane_g();
+    if constexpr (F::N == 1) return *a;
+    else return *reinterpret_cast<const typename F::T*>(a);
+  }
+};
+
+// OpT rows, element k multiplied by s[k] (an fp32 vector over K).
+template <typename OpT> struct SrcScaled {
+  using E = typename Ty<OpT>::Elem;
+  const E* p;
+  int ld;
+  const float* s;
+  template <int KS>
+  __device__ __forceinline__ typename Frag<OpT, KS>::T get(int k0) const {
+    using F = Frag<OpT, KS>;
+    const int kk = k0 + F::N * lane_g();
+    const E* a = p + lane_i() * ld + kk;
+    if constexpr (F::N == 1) {
+      return *a * s[kk];
+    } else {
+      typename F::T v = *reinterpret_cast<const typename F::T*>(a);
+#pragma unroll
+      for (int e = 0; e < F::N; ++e) v[e] = static_cast<__bf16>(static_cast<float>(v[e]) * s[kk + e]);
+      return v;
+    }
+  }
+};
+
+// fp32 rows converted to OpT.
+template <typename OpT> struct SrcF32 {
+  const float* p;
+  int ld;
+  template <int KS>
+  __device__ __forceinline__ typename Frag<OpT, KS>::T get(int k0) const {
+    using F = Frag<OpT, KS>;
+    const float* a = p + lane_i() * ld + k0 + F::N * lane_g();
+    if constexpr (F::N == 1) {
+      return *a;
+    } else {
+      typename F::T v;
+#pragma unroll
+      for (int e = 0; e < F::N; ++e) v[e] = static_cast<__bf16>(a[e]);
+      return v;
+    }
+  }
+};
+
+// fp32 column source for the fp32 MFMA: B^T[n][k] = M[k][n] of a row-major M.
+struct SrcColF32 {
+  const float* p;
+  int ld;
+  template <int KS>
+  __device__ __forceinline__ float get(int k0) const {
+    return p[(k0 + lane_g()) * ld + lane_i()];
+  }
+};
+
+// Two adjacent elements loaded with one access (c even, so 4- or 8-byte aligned).
+template <typename OpT> struct Pair;
+template <> struct Pair<bf16_t> {
+  using T = uint32_t;
+  __device__ __forceinline__ static T load(const uint16_t* p) {
+    return *reinterpret_cast<const uint32_t*>(p);
+  }
+  __device__ __forceinline__ static T zero() { return 0u; }
+  __device__ __forceinline__ static float get(T v, int x) {
+    return bf16_to_f32(static_cast<uint16_t>(x ? (v >> 16) : (v & 0xffffu)));
+  }
+};
+template <> struct Pair<float> {
+  using T = float2;
+  __device__ __forceinline__ static T load(const float* p) {
+    return *reinterpret_cast<const float2*>(p);
+  }
+  __device__ __forceinline__ static T zero() { return make_float2(0.f, 0.f); }
+  __device__ __forceinline__ static float get(T v, int x) { return x ? v.y : v.x; }
+};
+
+template <typename OpT, int KS>
+__device__ __forceinline__ f32x4 mfma(typename Frag<OpT, KS>::T a, typename Frag<OpT, KS>::T b,
+                                      f32x4 c) {
+  if constexpr (KS == 32) return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  else if constexpr (KS == 16) return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// acc += A[.., kb..ke) * B[kb..ke, ..]  (kb, ke multiples of 16)
+template <typename OpT, class SA, class SB>
+__device__ __forceinline__ void mma_k(f32x4& acc, int kb, int ke, const SA& sa, const SB& sb) {
+  if constexpr (sizeof(typename Ty<OpT>::Elem) == 2) {
+    int k = kb;
+    for (; k + 32 <= ke; k += 32)
+      acc = mfma<OpT, 32>(sa.template get<32>(k), sb.template get<32>(k), acc);
+    if (k < ke) acc = mfma<OpT, 16>(sa.template get<16>(k), sb.template get<16>(k), acc);
+  } else {
+    for (int k = kb; k < ke; k += 4)
+      acc = mfma<OpT, 4>(sa.template get<4>(k), sb.template get<4>(k), acc);
+  }
+}
+
+// Two products sharing the B operand: acc1 += A1 B, acc2 += A2 B.
+template <typename OpT, class SA1, class SA2, class SB>
+__device__ __forceinline__ void mma_k2(f32x4& acc1, f32x4& acc2, int kb, int ke, const SA1& a1,
+                                       const SA2& a2, const SB& sb) {
+  if constexpr (sizeof(typename Ty<OpT>::Elem) == 2) {
+    int k = kb;
+    for (; k + 32 <= ke; k += 32) {
+      auto b = sb.template get<32>(k);
+      acc1 = mfma<OpT, 32>(a1.template get<32>(k), b, acc1);
+      acc2 = mfma<OpT, 32>(a2.template get<32>(k), b, acc2);
+    }
+    if (k < ke) {
+      auto b = sb.template get<16>(k);
+      acc1 = mfma<OpT, 16>(a1.template get<16>(k), b, acc1);
+      acc2 = mfma<OpT, 16>(a2.template get<16>(k), b, acc2);
+    }
+  } else {
+    for (int k = kb; k < ke; k += 4) {
+      float b = sb.template get<4>(k);
+      acc1 = mfma<OpT, 4>(a1.template get<4>(k), b, acc1);
+      acc2 = mfma<OpT, 4>(a2.template get<4>(k), b, acc2);
+    }
+  }
+}
+
+// fp32 products used by the triangular solve, independent of OpT.
+template <class SA, class SB>
+__device__ __forceinline__ void mma_f32(f32x4& acc, int kb, int ke, const SA& sa, const SB& sb) {
+  for (int k = kb; k < ke; k += 4)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sa.template get<4>(k), sb.template get<4>(k), acc,
+                                               0, 0, 0);
+}
+
+// ----------------------------------------------------------------------------
+// LDS plan (element counts; every region 16-byte aligned).
+// ----------------------------------------------------------------------------
+__host__ __device__ constexpr int imax(int a, int b) { return a > b ? a : b; }
+__host__ __device__ constexpr int align16(int bytes) { return (bytes + 15) & ~15; }
+
+template <typename OpT, int DK, int C, int DVT>
+struct PCfg {
+  static constexpr int NTH = 256, NW = 4;
+  static constexpr int NB = C / 16;            // 16-row sub-blocks per chunk
+  static constexpr int NJ = DVT / 16;          // 16-column tiles of the slab
+  static constexpr int NCB = DK / 16;          // 16-channel tiles
+  static constexpr int EB = Ty<OpT>::kBytes;
+  static constexpr int PADE = 16 / EB;         // one 16-byte pad per row
+  static constexpr int LDK = DK + PADE;        // rows of length DK
+  static constexpr int LDC = C + PADE;         // rows of length C
+  static constexpr int LDT = C + 4;            // fp32 C x C
+  static constexpr int LDZ = 20;               // fp32 16 x 16 scratch
+
+  // region sizes in bytes
+  static constexpr int kZ1 = align16(imax(imax(2 * C * LDK, DVT * LDC), DVT * LDK) * EB);
+  static constexpr int kR1 = align16(C * LDK * EB);
+  static constexpr int kR2 = align16(imax(C * LDK, DVT * LDC) * EB);
+  static constexpr int kKT = align16(DK * LDC * EB);
+  static constexpr int kTT = align16(C * LDT * 4);
+  static constexpr int kZB = align16(imax(NB - 1, 1) * 16 * LDZ * 4);
+  static constexpr int kPP = align16(C * LDC * EB);
+  static constexpr int kBT = align16(NB * DK * 4);
+  static constexpr int kMID = align16(imax(NB * NB, 1) * DK * 4);
+  static constexpr int kGC = align16(DK * 4);
+  static constexpr int kBE = align16(C * 4);
+  static constexpr int kFL = align16(NB * 4);
+
+  static constexpr int oZ1 = 0;
+  static constexpr int oR1 = oZ1 + kZ1;
+  static constexpr int oR2 = oR1 + kR1;
+  static constexpr int oKB = oR2 + kR2;
+  static constexpr int oKG = oKB + kKT;
+  static constexpr int oTT = oKG + kKT;
+  static constexpr int oZB = oTT + kTT;
+  static constexpr int oPP = oZB + kZB;
+  static constexpr int oBT = oPP + kPP;
+  static constexpr int oPRE = oBT + kBT;
+  static constexpr int oMID = oPRE + kBT;
+  static constexpr int oGC = oMID + kMID;
+  static constexpr int oBE = oGC + kGC;
+  static constexpr int oFL = oBE + kBE;
+  static constexpr int kLds = oFL + kFL;
+
+  // work items
+  static constexpr int NGI = NB * DK / 2;                  // (block, channel pair)
+  static constexpr int NGT = (NGI + NTH - 1) / NTH;
+  static constexpr int NVI = NB * DVT / 2;                 // (block, value-column pair)
+  static constexpr int NVT = (NVI + NTH - 1) / NTH;
+  static constexpr int NS = NCB * NJ;                      // state tiles
+  static constexpr int NSW = (NS + NW - 1) / NW;
+  static constexpr int NU = NB * NJ;                       // chunk-output tiles
+  static constexpr int NUW = (NU + NW - 1) / NW;
+  static constexpr int NAP = NB * (NB + 1) / 2;            // lower block pairs
+};
+
+constexpr int kMaxLds = 160 * 1024;
+
+template <typename OpT, int DK, int C, int DVT>
+__global__ void __launch_bounds__(256)
+kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
+                   const typename Ty<OpT>::Elem* __restrict__ gk,
+                   const typename Ty<OpT>::Elem* __restrict__ gv,
+                   const float* __restrict__ galpha, const float* __restrict__ gbeta,
+                   const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float* gST,
+                   int B, int T, int H, int DV) {
+  using Cf = PCfg<OpT, DK, C, DVT>;
+  using E = typename Ty<OpT>::Elem;
+  constexpr int NB = Cf::NB, NJ = Cf::NJ, NW = Cf::NW, NTH = Cf::NTH;
+  constexpr int LDK = Cf::LDK, LDC = Cf::LDC, LDT = Cf::LDT, LDZ = Cf::LDZ;
+  static_assert(Cf::kLds <= kMaxLds, "LDS plan exceeds 160 KiB");
+
+  __shared__ __attribute__((aligned(16))) char smem[Cf::kLds];
+  E* Ki = reinterpret_cast<E*>(smem + Cf::oZ1);             // [C][LDK]
+  E* Kinv = Ki + C * LDK;                                     // [C][LDK]
+  E* VbT = reinterpret_cast<E*>(smem + Cf::oZ1);             // [DVT][LDC]  (after A/P)
+  E* ST = reinterpret_cast<E*>(smem + Cf::oZ1);              // [DVT][LDK]  (scan)
+  E* Kr = reinterpret_cast<E*>(smem + Cf::oR1);              // [C][LDK]
+  E* Wm = reinterpret_cast<E*>(smem + Cf::oR1);              // [C][LDK]   (after A/P)
+  E* Qr = reinterpret_cast<E*>(smem + Cf::oR2);              // [C][LDK]
+  E* UT = reinterpret_cast<E*>(smem + Cf::oR2);              // [DVT][LDC] (scan)
+  E* KbT = reinterpret_cast<E*>(smem + Cf::oKB);             // [DK][LDC]
+  E* KgT = reinterpret_cast<E*>(smem + Cf::oKG);             // [DK][LDC]
+  float* TT = reinterpret_cast<float*>(smem + Cf::oTT);      // [C][LDT]
+  float* ZB = reinterpret_cast<float*>(smem + Cf::oZB);      // [NB-1][16][LDZ]
+  E* PP = reinterpret_cast<E*>(smem + Cf::oPP);              // [C][LDC]
+  float* sBT = reinterpret_cast<float*>(smem + Cf::oBT);     // [NB][DK]
+  float* sPRE = reinterpret_cast<float*>(smem + Cf::oPRE);   // [NB][DK]
+  float* sMID = reinterpret_cast<float*>(smem + Cf::oMID);   // [NB][NB][DK]
+  float* sGC = reinterpret_cast<float*>(smem + Cf::oGC);     // [DK]
+  float* sBE = reinterpret_cast<float*>(smem + Cf::oBE);     // [C]
+  int* sFL = reinterpret_cast<int*>(smem + Cf::oFL);         // [NB]
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int g = lane_g(), li = lane_i();
+
+  // Workgroup -> (chain, slab).  Consecutive workgroups are dealt round-robin
+  // to the 8 XCDs; keep all slabs of one chain on one XCD so they share L2.
+  const int ntiles = DV / DVT;
+  const int total = gridDim.x;
+  int L = blockIdx.x;
+  if (ntiles > 1 && (total % 8) == 0) L = (blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
+  const int chain = L / ntiles;
+  const int j0 = (L % ntiles) * DVT;
+  const int b = chain / H, h = chain % H;
+
+  const size_t tokstride = static_cast<size_t>(H);  // tokens are H apart in [B,T,H,*]
+  auto tok = [&](int t) -> size_t { return (static_cast<size_t>(b) * T + t) * tokstride + h; };
+
+  // ---- state slab in registers: tile s of wave w is sigma = w + NW*s = (Cb, Jb)
+  f32x4 Sreg[Cf::NSW];
+#pragma unroll
+  for (int s = 0; s < Cf::NSW; ++s) {
+    const int sg = wave + NW * s;
+    Sreg[s] = zero4();
+    if (sg < Cf::NS && gS0 != nullptr) {
+      const int Cb = sg / NJ, Jb = sg % NJ;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = 16 * Cb + 4 * g + r;
+        Sreg[s][r] = gS0[(static_cast<size_t>(chain) * DK + c) * DV + j0 + 16 * Jb + li];
+      }
+    }
+  }
+  // Upper block triangles of TT and PP are never written again: zero once.
+  for (int x = tid; x < C * C; x += NTH) {
+    const int r = x / C, c = x % C;
+    if (c / 16 > r / 16) {
+      TT[r * LDT + c] = 0.f;
+      PP[r * LDC + c] = Ty<OpT>::from_f32(0.f);
+    }
+  }
+
+  const int NC = (T + C - 1) / C;
+  for (int ch = 0; ch < NC; ++ch) {
+    const int t0 = ch * C;
+    // ================= G1: load the chunk, within-block cumulative gates
+    float ga[Cf::NGT][16][2];     // alpha, two channels
+    typename Pair<OpT>::T gkk[Cf::NGT][16], gqq[Cf::NGT][16];
+    typename Pair<OpT>::T gvv[Cf::NVT][16];
+    if (tid < C) {
+      const int t = t0 + tid;
+      sBE[tid] = (t < T) ? gbeta[tok(t)] : 0.f;
+    }
+    if (tid < NB) sFL[tid] = 0;
+#pragma unroll
+    for (int it = 0; it < Cf::NGT; ++it) {
+      const int item = tid + NTH * it;
+      if (item < Cf::NGI) {
+        const int J = item / (DK / 2), c = 2 * (item % (DK / 2));
+        float f0 = 1.f, f1 = 1.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int t = t0 + 16 * J + j;
+          if (t < T) {
+            const size_t base = tok(t) * DK + c;
+            const float2 a2 = *reinterpret_cast<const float2*>(galpha + base);
+            ga[it][j][0] = a2.x;
+            ga[it][j][1] = a2.y;
+            gkk[it][j] = Pair<OpT>::load(gk + base);
+            gqq[it][j] = Pair<OpT>::load(gq + base);
+          } else {
+            ga[it][j][0] = ga[it][j][1] = 1.f;
+            gkk[it][j] = Pair<OpT>::zero();
+            gqq[it][j] = Pair<OpT>::zero();
+          }
+          f0 *= ga[it][j][0];
+          f1 *= ga[it][j][1];
+        }
+        sBT[J * DK + c] = f0;
+        sBT[J * DK + c + 1] = f1;
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < Cf::NVT; ++it) {
+      const int item = tid + NTH * it;
+      if (item < Cf::NVI) {
+        const int J = item / (DVT / 2), cc = 2 * (item % (DVT / 2));
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int t = t0 + 16 * J + j;
+          gvv[it][j] = (t < T) ? Pair<OpT>::load(gv + tok(t) * DV + j0 + cc) : Pair<OpT>::zero();
+        }
+      }
+    }
+    __syncthreads();
+
+    // ================= G2: chunk-level gate products and MFMA operands
+    if (tid < DK) {
+      const int c = tid;
+      float acc = 1.f;
+      for (int J = 0; J < NB; ++J) {
+        sPRE[J * DK + c] = acc;
+        acc *= sBT[J * DK + c];
+      }
+      sGC[c] = acc;
+      for (int R = 2; R < NB; ++R)
+        for (int I = 0; I + 1 < R; ++I) {
+          float m = 1.f;
+          for (int J = I + 1; J < R; ++J) m *= sBT[J * DK + c];
+          sMID[(R * NB + I) * DK + c] = m;
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < Cf::NGT; ++it) {
+      const int item = tid + NTH * it;
+      if (item < Cf::NGI) {
+        const int J = item / (DK / 2), c = 2 * (item % (DK / 2));
+        float pre[2] = {1.f, 1.f}, suf[2] = {1.f, 1.f};
+        bool unsafe = false;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          for (int JJ = 0; JJ < J; ++JJ) pre[x] *= sBT[JJ * DK + c + x];
+          for (int JJ = J + 1; JJ < NB; ++JJ) suf[x] *= sBT[JJ * DK + c + x];
+          unsafe |= !(sBT[J * DK + c + x] >= kUnsafeBlockDecay);
+        }
+        if (unsafe) atomicOr(&sFL[J], 1);
+        // reverse exclusive products H_j = prod_{j' > j in block} alpha
+        float hx[16][2];
+        hx[15][0] = hx[15][1] = 1.f;
+#pragma unroll
+        for (int j = 14; j >= 0; --j) {
+          hx[j][0] = hx[j + 1][0] * ga[it][j + 1][0];
+          hx[j][1] = hx[j + 1][1] * ga[it][j + 1][1];
+        }
+        float f[2] = {1.f, 1.f};
+        E kbt[2][16], kgt[2][16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int r = 16 * J + j;
+          const float be = sBE[r];
+          E kr2[2], qr2[2], ki2[2], kv2[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            f[x] *= ga[it][j][x];
+            const float kk = Pair<OpT>::get(gkk[it][j], x);
+            const float qq = Pair<OpT>::get(gqq[it][j], x);
+            const bool safe = sBT[J * DK + c + x] >= kUnsafeBlockDecay;
+            kr2[x] = Ty<OpT>::from_f32(kk * f[x]);
+            qr2[x] = Ty<OpT>::from_f32(qq * f[x]);
+            ki2[x] = Ty<OpT>::from_f32(kk * hx[j][x]);
+            kv2[x] = Ty<OpT>::from_f32(safe ? kk / f[x] : 0.f);
+            kbt[x][j] = Ty<OpT>::from_f32(be * kk * f[x] * pre[x]);
+            kgt[x][j] = Ty<OpT>::from_f32(kk * hx[j][x] * suf[x]);
+          }
+          Kr[r * LDK + c] = kr2[0]; Kr[r * LDK + c + 1] = kr2[1];
+          Qr[r * LDK + c] = qr2[0]; Qr[r * LDK + c + 1] = qr2[1];
+          Ki[r * LDK + c] = ki2[0]; Ki[r * LDK + c + 1] = ki2[1];
+          Kinv[r * LDK + c] = kv2[0]; Kinv[r * LDK + c + 1] = kv2[1];
+        }
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            KbT[(c + x) * LDC + 16 * J + j] = kbt[x][j];
+            KgT[(c + x) * LDC + 16 * J + j] = kgt[x][j];
+          }
+      }
+    }
+    __syncthreads();
+
+    // ================= AP: gated K K^T (-> L in TT) and Q K^T (-> P) tiles
+    for (int p = wave; p < Cf::NAP; p += NW) {
+      int R = 0, rem = p;
+      while (rem > R) { rem -= R + 1; ++R; }
+      const int I = rem;
+      f32x4 accA = zero4(), accP = zero4();
+      const Src<OpT> sKr{Kr + 16 * R * LDK, LDK}, sQr{Qr + 16 * R * LDK, LDK};
+      if (I < R) {
+        if (R == I + 1) {
+          mma_k2<OpT>(accA, accP, 0, DK, sKr, sQr, Src<OpT>{Ki + 16 * I * LDK, LDK});
+        } else {
+          mma_k2<OpT>(accA, accP, 0, DK, sKr, sQr,
+                      SrcScaled<OpT>{Ki + 16 * I * LDK, LDK, sMID + (R * NB + I) * DK});
+        }
+      } else {
+        mma_k2<OpT>(accA, accP, 0, DK, sKr, sQr, Src<OpT>{Kinv + 16 * R * LDK, LDK});
+        if (sFL[R]) {
+          // Channels whose block decay fell below 2^-100: exact pairwise
+          // products of alpha on the vector units.
+          for (int c = 0; c < DK; ++c) {
+            if (sBT[R * DK + c] >= kUnsafeBlockDecay) continue;
+            const int ti = t0 + 16 * R + li;
+            const float ki = (ti < T) ? Ty<OpT>::to_f32(gk[tok(ti) * DK + c]) : 0.f;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int rl = 4 * g + rr;
+              if (li > rl) continue;
+              float ratio = 1.f;
+              for (int j = li + 1; j <= rl; ++j) {
+                const int tj = t0 + 16 * R + j;
+                ratio *= (tj < T) ? galpha[tok(tj) * DK + c] : 1.f;
+              }
+              const int tr = t0 + 16 * R + rl;
+              const float kr = (tr < T) ? Ty<OpT>::to_f32(gk[tok(tr) * DK + c]) : 0.f;
+              const float qr = (tr < T) ? Ty<OpT>::to_f32(gq[tok(tr) * DK + c]) : 0.f;
+              accA[rr] += kr * ki * ratio;
+              accP[rr] += qr * ki * ratio;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int rl = 4 * g + rr, r = 16 * R + rl, i = 16 * I + li;
+        const bool diag = (I == R);
+        const float a = (diag && li >= rl) ? 0.f : accA[rr];
+        const float pv = (diag && li > rl) ? 0.f : accP[rr];
+        TT[r * LDT + i] = sBE[r] * a;
+        PP[r * LDC + i] = Ty<OpT>::from_f32(pv);
+      }
+    }
+    __syncthreads();
+
+    // ================= SD: invert the 16x16 diagonal blocks of I + L
+    // (forward substitution, one column per lane) while the other lanes
+    // stage beta-scaled values, transposed, for U~ = Y Diag(beta) V.
+#pragma unroll
+    for (int it = 0; it < Cf::NVT; ++it) {
+      const int item = tid + NTH * it;
+      if (item < Cf::NVI) {
+        const int J = item / (DVT / 2), cc = 2 * (item % (DVT / 2));
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          E col[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            col[j] = Ty<OpT>::from_f32(sBE[16 * J + j] * Pair<OpT>::get(gvv[it][j], x));
+#pragma unroll
+          for (int j = 0; j < 16; ++j) VbT[(cc + x) * LDC + 16 * J + j] = col[j];
+        }
+      }
+    }
+    {
+      const int R = 4 * wave + g;   // lane group -> diagonal block
+      if (R < NB) {
+        const int j = li;
+        const float* Lb = TT + 16 * R * LDT + 16 * R;
+        float y[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float s = 0.f;
+#pragma unroll
+          for (int m = 0; m < r; ++m) s += Lb[r * LDT + m] * y[m];
+          y[r] = (r < j) ? 0.f : ((r == j) ? 1.f : -s);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) TT[(16 * R + r) * LDT + 16 * R + j] = y[r];
+      }
+    }
+    __syncthreads();
+
+    // ================= SO: off-diagonal blocks of Y, one block row at a time
+    //   Y_RI = -Y_RR * sum_{J=I}^{R-1} L_RJ Y_JI
+    for (int R = 1; R < NB; ++R) {
+      for (int I = wave; I < R; I += NW) {
+        f32x4 z = zero4();
+        for (int J = I; J < R; ++J)
+          mma_f32(z, 0, 16, Src<float>{TT + 16 * R * LDT + 16 * J, LDT},
+                  SrcColF32{TT + 16 * J * LDT + 16 * I, LDT});
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) ZB[(I * 16 + 4 * g + rr) * LDZ + li] = z[rr];
+      }
+      __syncthreads();
+      for (int I = wave; I < R; I += NW) {
+        f32x4 y = zero4();
+        mma_f32(y, 0, 16, Src<float>{TT + 16 * R * LDT + 16 * R, LDT},
+                SrcColF32{ZB + I * 16 * LDZ, LDZ});
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) TT[(16 * R + 4 * g + rr) * LDT + 16 * I + li] = -y[rr];
+      }
+      __syncthreads();
+    }
+
+    // ================= WU: W = Y (beta K E) (stored row-major) and U~ = Y (beta V)
+    for (int w = wave; w < Cf::NCB * NB; w += NW) {
+      const int Cb = w / NB, R = w % NB;
+      f32x4 acc = zero4();
+      mma_k<OpT>(acc, 0, 16 * (R + 1), Src<OpT>{KbT + 16 * Cb * LDC, LDC},
+                 SrcF32<OpT>{TT + 16 * R * LDT, LDT});
+      // acc[rr] = W^T[c = 16Cb + 4g + rr][r = 16R + li]
+      E* dst = Wm + (16 * R + li) * LDK + 16 * Cb + 4 * g;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(acc[rr]);
+    }
+    f32x4 Ureg[Cf::NUW];
+#pragma unroll
+    for (int u = 0; u < Cf::NUW; ++u) {
+      const int tau = wave + NW * u;
+      Ureg[u] = zero4();
+      if (tau < Cf::NU) {
+        const int R = tau / NJ, Jb = tau % NJ;
+        mma_k<OpT>(Ureg[u], 0, 16 * (R + 1), SrcF32<OpT>{TT + 16 * R * LDT, LDT},
+                   Src<OpT>{VbT + 16 * Jb * LDC, LDC});
+      }
+    }
+    __syncthreads();
+
+    // ================= scan: U = U~ - W S,  O = (Q E) S + P U,  S update
+#pragma unroll
+    for (int s = 0; s < Cf::NSW; ++s) {
+      const int sg = wave + NW * s;
+      if (sg < Cf::NS) {
+        const int Cb = sg / NJ, Jb = sg % NJ;
+        E* dst = ST + (16 * Jb + li) * LDK + 16 * Cb + 4 * g;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(Sreg[s][rr]);
+      }
+    }
+    __syncthreads();
+    f32x4 Oreg[Cf::NUW];
+#pragma unroll
+    for (int u = 0; u < Cf::NUW; ++u) {
+      const int tau = wave + NW * u;
+      Oreg[u] = zero4();
+      if (tau < Cf::NU) {
+        const int R = tau / NJ, Jb = tau % NJ;
+        f32x4 x = zero4();
+        mma_k2<OpT>(x, Oreg[u], 0, DK, Src<OpT>{Wm + 16 * R * LDK, LDK},
+                    SrcScaled<OpT>{Qr + 16 * R * LDK, LDK, sPRE + R * DK},
+                    Src<OpT>{ST + 16 * Jb * LDK, LDK});
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) Ureg[u][rr] -= x[rr];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < Cf::NUW; ++u) {
+      const int tau = wave + NW * u;
+      if (tau < Cf::NU) {
+        const int R = tau / NJ, Jb = tau % NJ;
+        E* dst = UT + (16 * Jb + li) * LDC + 16 * R + 4 * g;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(Ureg[u][rr]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < Cf::NUW; ++u) {
+      const int tau = wave + NW * u;
+      if (tau < Cf::NU) {
+        const int R = tau / NJ, Jb = tau % NJ;
+        mma_k<OpT>(Oreg[u], 0, 16 * (R + 1), Src<OpT>{PP + 16 * R * LDC, LDC},
+                   Src<OpT>{UT + 16 * Jb * LDC, LDC});
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int t = t0 + 16 * R + 4 * g + rr;
+          if (t < T) go[tok(t) * DV + j0 + 16 * Jb + li] = Ty<OpT>::from_f32(Oreg[u][rr]);
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < Cf::NSW; ++s) {
+      const int sg = wave + NW * s;
+      if (sg < Cf::NS) {
+        const int Cb = sg / NJ, Jb = sg % NJ;
+        f32x4 acc = zero4();
+        mma_k<OpT>(acc, 0, C, Src<OpT>{KgT + 16 * Cb * LDC, LDC},
+                   Src<OpT>{UT + 16 * Jb * LDC, LDC});
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          Sreg[s][rr] = sGC[16 * Cb + 4 * g + rr] * Sreg[s][rr] + acc[rr];
+      }
+    }
+    __syncthreads();
+  }
+
+  if (gST != nullptr) {
+#pragma unroll
+    for (int s = 0; s < Cf::NSW; ++s) {
+      const int sg = wave + NW * s;
+      if (sg < Cf::NS) {
+        const int Cb = sg / NJ, Jb = sg % NJ;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = 16 * Cb + 4 * g + r;
+          gST[(static_cast<size_t>(chain) * DK + c) * DV + j0 + 16 * Jb + li] = Sreg[s][r];
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Host dispatch
+// ----------------------------------------------------------------------------
+template <typename OpT, int DK, int C, int DVT>
+hipError_t launch_one(const PrefillArgs& a) {
+  using E = typename Ty<OpT>::Elem;
+  const long chains = static_cast<long>(a.B) * a.H;
+  dim3 grid(static_cast<unsigned>(chains * (a.dv / DVT)));
+  hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT>), grid, dim3(256), 0,
+                     static_cast<hipStream_t>(a.stream), static_cast<const E*>(a.q),
+                     static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.alpha, a.beta,
+                     a.S0, static_cast<E*>(a.o), a.S_T, a.B, a.T, a.H, a.dv);
+  return hipGetLastError();
+}
+
+template <typename OpT, int DK, int C, int DVT>
+constexpr bool fits() {
+  return DVT <= 128 && PCfg<OpT, DK, C, DVT>::kLds <= kMaxLds;
+}
+
+// Widest slab that fits, narrowed while the chip would be under-filled.
+template <typename OpT, int DK, int C>
+int pick_dvt(long chains, int dv) {
+  int best = 0;
+  for (int d = 16; d <= dv; d *= 2) {
+    bool ok = false;
+    if (d == 16) ok = fits<OpT, DK, C, 16>();
+    if (d == 32) ok = fits<OpT, DK, C, 32>();
+    if (d == 64) ok = fits<OpT, DK, C, 64>();
+    if (d == 128) ok = fits<OpT, DK, C, 128>();
+    if (ok) best = d;
+  }
+  if (best == 0) return 0;
+  while (best > 16 && chains * (dv / best) < 256) best /= 2;
+  return best;
+}
+
+template <typename OpT, int DK, int C>
+hipError_t launch_c(const PrefillArgs& a) {
+  const int dvt = pick_dvt<OpT, DK, C>(static_cast<long>(a.B) * a.H, a.dv);
+  switch (dvt) {
+    case 16: if constexpr (fits<OpT, DK, C, 16>()) return launch_one<OpT, DK, C, 16>(a); break;
+    case 32: if constexpr (fits<OpT, DK, C, 32>()) return launch_one<OpT, DK, C, 32>(a); break;
+    case 64: if constexpr (fits<OpT, DK, C, 64>()) return launch_one<OpT, DK, C, 64>(a); break;
+    case 128: if constexpr (fits<OpT, DK, C, 128>()) return launch_one<OpT, DK, C, 128>(a); break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename OpT, int DK>
+hipError_t launch_dk(const PrefillArgs& a) {
+  switch (a.C) {
+    case 16: return launch_c<OpT, DK, 16>(a);
+    case 32: return launch_c<OpT, DK, 32>(a);
+    case 64: return launch_c<OpT, DK, 64>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename OpT, int DK>
+bool supported_dk(int dv, int C) {
+  switch (C) {
+    case 16: return pick_dvt<OpT, DK, 16>(1 << 20, dv) > 0;
+    case 32: return pick_dvt<OpT, DK, 32>(1 << 20, dv) > 0;
+    case 64: return pick_dvt<OpT, DK, 64>(1 << 20, dv) > 0;
+  }
+  return false;
+}
+
+// One translation unit per (element type, dk) instantiates these.
+#define KDA_PREFILL_INSTANCE(OPT, NAME, DK)                                        \
+  hipError_t launch_prefill_##NAME##_##DK(const PrefillArgs& a) {                   \
+    return launch_dk<OPT, DK>(a);                                                   \
+  }                                                                                 \
+  bool prefill_supported_##NAME##_##DK(int dv, int C) { return supported_dk<OPT, DK>(dv, C); }
+
+#define KDA_PREFILL_DECLARE(NAME, DK)                                               \
+  hipError_t launch_prefill_##NAME##_##DK(const PrefillArgs& a);                    \
+  bool prefill_supported_##NAME##_##DK(int dv, int C);
+
+KDA_PREFILL_DECLARE(bf16, 16)
+KDA_PREFILL_DECLARE(bf16, 32)
+KDA_PREFILL_DECLARE(bf16, 64)
+KDA_PREFILL_DECLARE(bf16, 128)
+KDA_PREFILL_DECLARE(f32, 16)
+KDA_PREFILL_DECLARE(f32, 32)
+KDA_PREFILL_DECLARE(f32, 64)
+KDA_PREFILL_DECLARE(f32, 128)
+
+}  // namespace kda

@@ -1,0 +1,153 @@
+/*
+ * kda.h — C ABI of libkda, Kimi Delta Attention (KDA) on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What is computed
+ * ----------------
+ * One independent chain per (batch b, head h).  Row-vector convention: q_t and
+ * k_t are rows of length dk, v_t a row of length dv, the state S is dk x dv.
+ * For t = 0 .. T-1:
+ *
+ *     S'   = Diag(alpha_t) S              decay first, one gate per key channel
+ *     r    = k_t S'                       read the state at the key
+ *     u    = beta_t (v_t - r)             the delta
+ *     S    = S' + k_t^T u                 write
+ *     o_t  = q_t S                        read after the write, no normaliser
+ *
+ * i.e. S_t = (I - beta_t k_t^T k_t) Diag(alpha_t) S_{t-1} + beta_t k_t^T v_t.
+ *
+ * Sources, by page title and section:
+ *   - "From GPT-2 to Kimi K3, Explained" (marvinlee.cn), section "DeltaNet
+ *     (Fast Weight Programmers)": the read / delta / write / read step with a
+ *     per-token write strength beta and no denominator;
+ *   - same page, section "DeltaNet (Parallelizing Linear Transformers with
+ *     Delta Rule)": the sequential prefill writes before it reads, the
+ *     Householder reparameterisation, and the chunkwise form with a
+ *     triangular (UT) transform that these kernels generalise;
+ *   - same page, section "Gated Delta Net": a gate in [0,1] decays the old
+ *     state before the precise write; 1 is plain DeltaNet, 0 clears memory;
+ *   - same page, section "KDA/Kimi Linear", and "Kimi Delta Attention (KDA):
+ *     что это за механизм внимания" (ai-flip.ru), section "Как KDA развивает
+ *     идею Gated DeltaNet": the gate becomes one value per channel, a diagonal
+ *     gate matrix.
+ * Readings where the pages are silent: the gate scales the key dimension (the
+ * rows of S) and acts before the read-back; the output reads the state after
+ * the write; q and k are used exactly as given (no scaling, no feature map);
+ * a missing initial state is zero.
+ *
+ * Conventions common to every entry point
+ * ---------------------------------------
+ *   - Every array argument is a DEVICE pointer owned by the caller, contiguous,
+ *     row-major, and 16-byte aligned.  The library allocates nothing and keeps
+ *     no mutable global state; calls are asynchronous on `stream` (an opaque
+ *     hipStream_t; NULL means the null stream) and reentrant.
+ *   - q, k, v and o have the element type `dt`; alpha, beta and the states are
+ *     always float32.
+ *   - Arguments are validated on the host before any launch; a failed
+ *     validation returns a negative status and launches nothing.  A launch
+ *     failure returns KDA_ERR_HIP.  Faults inside a kernel surface at the
+ *     caller's next synchronisation.  No C++ exception crosses this ABI.
+ *   - Supported sizes: dk, dv in {16, 32, 64, 128}.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kda_status;
+
+enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = -1,        /* a required pointer is NULL                          */
+  KDA_ERR_SHAPE = -2,       /* a size is out of range (B, H, N < 1; T < 0)         */
+  KDA_ERR_UNSUPPORTED = -3, /* dk, dv, C or dtype not supported by any kernel      */
+  KDA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                    */
+  KDA_ERR_ALIAS = -5,       /* an output overlaps an input it may not overlap      */
+  KDA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than the query says    */
+  KDA_ERR_DEVICE = -7,      /* current device is not gfx950                        */
+  KDA_ERR_HIP = -8          /* a HIP runtime call or kernel launch failed          */
+};
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/*
+ * kda_prefill_workspace_bytes — bytes of device workspace kda_prefill_chunked
+ * needs for these sizes.  Returns 0 when no workspace is needed (the current
+ * kernels keep every intermediate on chip) and (size_t)-1 when the sizes are
+ * not supported.
+ */
+size_t kda_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int C,
+                                   kda_dtype dt);
+
+/*
+ * kda_prefill_chunked — KDA over a whole sequence for B x H chains, chunk by
+ * chunk ("From GPT-2 to Kimi K3, Explained", section "DeltaNet (Parallelizing
+ * Linear Transformers with Delta Rule)", generalised to the per-channel gate
+ * of section "KDA/Kimi Linear").
+ *
+ *   q, k   [B, T, H, dk]  dt        queries and keys (used as given)
+ *   v      [B, T, H, dv]  dt        values
+ *   alpha  [B, T, H, dk]  float32   per-channel forget gate, expected in [0, 1]
+ *   beta   [B, T, H]      float32   per-token write strength, expected in [0, 1]
+ *   S0     [B, H, dk, dv] float32   initial state, or NULL for zeros
+ *   o      [B, T, H, dv]  dt        output o_t = q_t S_t (written)
+ *   S_T    [B, H, dk, dv] float32   final state (written), or NULL to skip;
+ *                                   may be equal to S0 (in place) but may not
+ *                                   overlap it otherwise
+ *   C                               chunk length in {16, 32, 64}; a
+ *                                   performance knob only: the result does not
+ *                                   depend on C beyond rounding
+ *   workspace, workspace_bytes      caller-owned scratch of at least
+ *                                   kda_prefill_workspace_bytes(...) bytes
+ *                                   (may be NULL when that is 0)
+ *
+ * Any T >= 0 is accepted; a tail shorter than C is handled as identity
+ * padding (gate 1, strength 0), and T = 0 copies S0 (or zeros) to S_T.
+ * o may not overlap any input.  Errors: KDA_ERR_NULL, KDA_ERR_SHAPE,
+ * KDA_ERR_UNSUPPORTED, KDA_ERR_ALIGN, KDA_ERR_ALIAS, KDA_ERR_WORKSPACE,
+ * KDA_ERR_DEVICE, KDA_ERR_HIP.
+ */
+kda_status kda_prefill_chunked(const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta,
+                               const float* S0, void* o, float* S_T,
+                               int B, int T, int H, int dk, int dv, int C,
+                               kda_dtype dt, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * kda_decode_step — one recurrence step for N sequences x H heads (the same
+ * step as one token of the prefill; the pages' decode path calls the layer
+ * with t = 1 and the cached state, "From GPT-2 to Kimi K3, Explained",
+ * sections "Linear Attention" and "DeltaNet (Fast Weight Programmers)").
+ *
+ *   q, k   [N, H, dk]      dt
+ *   v      [N, H, dv]      dt
+ *   alpha  [N, H, dk]      float32
+ *   beta   [N, H]          float32
+ *   S_in   [N, H, dk, dv]  float32  state before the step
+ *   o      [N, H, dv]      dt       output (written); may not overlap inputs
+ *   S_out  [N, H, dk, dv]  float32  state after the step (written); may be
+ *                                   equal to S_in (in place) but may not
+ *                                   overlap it otherwise
+ *
+ * Errors: as kda_prefill_chunked (no workspace).
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta,
+                           const float* S_in, void* o, float* S_out,
+                           int N, int H, int dk, int dv, kda_dtype dt,
+                           void* stream);
+
+/* kda_status_string — static, human-readable text for a status code. */
+const char* kda_status_string(kda_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

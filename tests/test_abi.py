@@ -1,0 +1,127 @@
+"""The C ABI on the CPU: the library loads, exports every entry point that
+include/kda.h declares, and rejects bad arguments on the host before any GPU
+call (no pointer is dereferenced, so fake aligned addresses are enough).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def _lib():
+    from gated_delta_rule_108_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libkda.so is not built (run __graft_entry__.build())")
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    assert declared_functions() == ["kda_decode_step", "kda_prefill_chunked",
+                                    "kda_prefill_workspace_bytes", "kda_status_string"]
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(L.SIGNATURES) == set(declared_functions())
+
+
+def test_status_strings():
+    L = _lib()
+    for code in range(-8, 1):
+        s = L.status_string(code)
+        assert s and s != "unknown status"
+    assert L.status_string(5) == "unknown status"
+
+
+# fake, 16-byte aligned, non-overlapping device addresses (never dereferenced)
+BASE = 1 << 40
+SPAN = 1 << 36
+
+
+def addr(i):
+    return BASE + i * SPAN
+
+
+def prefill(lib, **kw):
+    a = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), S0=addr(5),
+             o=addr(6), S_T=addr(7), B=1, T=64, H=2, dk=128, dv=128, C=64, dt=1,
+             ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.kda_prefill_chunked(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"],
+                                   a["o"], a["S_T"], a["B"], a["T"], a["H"], a["dk"], a["dv"],
+                                   a["C"], a["dt"], a["ws"], a["wsb"], a["stream"])
+
+
+def decode(lib, **kw):
+    a = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), S=addr(5),
+             o=addr(6), S_out=addr(5), N=4, H=2, dk=128, dv=128, dt=1, stream=None)
+    a.update(kw)
+    return lib.kda_decode_step(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S"], a["o"],
+                               a["S_out"], a["N"], a["H"], a["dk"], a["dv"], a["dt"], a["stream"])
+
+
+def test_prefill_validation_errors():
+    L = _lib()
+    lib = L.load()
+    assert prefill(lib, q=None) == L.KDA_ERR_NULL
+    assert prefill(lib, o=None) == L.KDA_ERR_NULL
+    assert prefill(lib, B=0) == L.KDA_ERR_SHAPE
+    assert prefill(lib, H=0) == L.KDA_ERR_SHAPE
+    assert prefill(lib, T=-1) == L.KDA_ERR_SHAPE
+    assert prefill(lib, dk=48) == L.KDA_ERR_UNSUPPORTED
+    assert prefill(lib, dv=256) == L.KDA_ERR_UNSUPPORTED
+    assert prefill(lib, C=8) == L.KDA_ERR_UNSUPPORTED
+    assert prefill(lib, C=128) == L.KDA_ERR_UNSUPPORTED
+    assert prefill(lib, dt=7) == L.KDA_ERR_UNSUPPORTED
+    assert prefill(lib, dt=0) == L.KDA_ERR_UNSUPPORTED          # fp32, dk=128, C=64: no fit
+    assert prefill(lib, alpha=addr(3) + 4) == L.KDA_ERR_ALIGN
+    assert prefill(lib, o=addr(0)) == L.KDA_ERR_ALIAS            # o on top of q
+    assert prefill(lib, S_T=addr(5) + 256) == L.KDA_ERR_ALIAS    # partial overlap with S0
+    assert prefill(lib, S_T=addr(1)) == L.KDA_ERR_ALIAS          # S_T on top of k
+
+
+def test_prefill_valid_arguments_reach_the_device_check():
+    L = _lib()
+    lib = L.load()
+    # In-place state (S_T == S0) and T = 0 with NULL token arrays are valid; on
+    # a machine without a GPU the call then fails at the device query.
+    for kw in (dict(), dict(S_T=addr(5)), dict(S0=None),
+               dict(T=0, q=None, k=None, v=None, alpha=None, beta=None, o=None)):
+        st = prefill(lib, **kw)
+        assert st in (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE), (kw, st)
+
+
+def test_decode_validation_errors():
+    L = _lib()
+    lib = L.load()
+    assert decode(lib, S=None) == L.KDA_ERR_NULL
+    assert decode(lib, N=0) == L.KDA_ERR_SHAPE
+    assert decode(lib, dk=8) == L.KDA_ERR_UNSUPPORTED
+    assert decode(lib, beta=addr(4) + 8) == L.KDA_ERR_ALIGN
+    assert decode(lib, o=addr(2)) == L.KDA_ERR_ALIAS
+    assert decode(lib, S_out=addr(5) + 64) == L.KDA_ERR_ALIAS
+    assert decode(lib, S_out=addr(3)) == L.KDA_ERR_ALIAS
+    assert decode(lib, S_out=addr(7)) in (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+
+
+def test_workspace_query():
+    L = _lib()
+    lib = L.load()
+    bad = (1 << 64) - 1
+    assert lib.kda_prefill_workspace_bytes(1, 4096, 16, 128, 128, 64, 1) == 0
+    assert lib.kda_prefill_workspace_bytes(1, 256, 1, 16, 16, 16, 0) == 0
+    assert lib.kda_prefill_workspace_bytes(1, 256, 1, 16, 16, 12, 0) == bad
+    assert lib.kda_prefill_workspace_bytes(0, 256, 1, 16, 16, 16, 0) == bad

@@ -1,0 +1,63 @@
+"""Status codes of the C ABI with a GPU present: every validation error is
+returned before any launch, and valid calls return KDA_OK."""
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def L():
+    from gated_delta_rule_108_amd import _lib
+    _lib.load()
+    return _lib
+
+
+def bufs(B=1, T=64, H=2, dk=128, dv=128, dt=torch.bfloat16):
+    z = lambda *s, d=dt: torch.zeros(*s, dtype=d, device=DEV)  # noqa: E731
+    return dict(q=z(B, T, H, dk), k=z(B, T, H, dk), v=z(B, T, H, dv),
+                alpha=z(B, T, H, dk, d=torch.float32), beta=z(B, T, H, d=torch.float32),
+                S0=z(B, H, dk, dv, d=torch.float32), o=z(B, T, H, dv),
+                S_T=z(B, H, dk, dv, d=torch.float32))
+
+
+def call(b, B=1, T=64, H=2, dk=128, dv=128, C=64, dt=1, **ov):
+    p = {k: t.data_ptr() for k, t in b.items()}
+    p.update(ov)
+    return L().load().kda_prefill_chunked(p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["S0"],
+                                          p["o"], p["S_T"], B, T, H, dk, dv, C, dt, None, 0,
+                                          torch.cuda.current_stream().cuda_stream)
+
+
+def test_prefill_status_codes():
+    lib = L()
+    b = bufs()
+    assert call(b) == lib.KDA_OK
+    assert call(b, S0=None) == lib.KDA_OK
+    assert call(b, S_T=b["S0"].data_ptr()) == lib.KDA_OK       # in place
+    assert call(b, q=None) == lib.KDA_ERR_NULL
+    assert call(b, T=-3) == lib.KDA_ERR_SHAPE
+    assert call(b, C=128) == lib.KDA_ERR_UNSUPPORTED
+    assert call(b, dk=100) == lib.KDA_ERR_UNSUPPORTED
+    assert call(b, k=b["k"].data_ptr() + 2) == lib.KDA_ERR_ALIGN
+    assert call(b, o=b["v"].data_ptr()) == lib.KDA_ERR_ALIAS
+    assert call(b, S_T=b["S0"].data_ptr() + 1024) == lib.KDA_ERR_ALIAS
+    torch.cuda.synchronize()
+
+
+def test_decode_status_codes():
+    lib = L()
+    N, H, d = 2, 3, 64
+    z = lambda *s, dt=torch.bfloat16: torch.zeros(*s, dtype=dt, device=DEV)  # noqa: E731
+    q, k, v, o = z(N, H, d), z(N, H, d), z(N, H, d), z(N, H, d)
+    a, bt = z(N, H, d, dt=torch.float32), z(N, H, dt=torch.float32)
+    S = z(N, H, d, d, dt=torch.float32)
+    f = lib.load().kda_decode_step
+    s = torch.cuda.current_stream().cuda_stream
+    P = lambda t: t.data_ptr()  # noqa: E731
+    assert f(P(q), P(k), P(v), P(a), P(bt), P(S), P(o), P(S), N, H, d, d, 1, s) == lib.KDA_OK
+    assert f(P(q), P(k), P(v), P(a), P(bt), P(S), P(o), None, N, H, d, d, 1, s) == lib.KDA_ERR_NULL
+    assert f(P(q), P(k), P(v), P(a), P(bt), P(S), P(q), P(S), N, H, d, d, 1, s) == lib.KDA_ERR_ALIAS
+    assert f(P(q), P(k), P(v), P(a), P(bt), P(S), P(o), P(S), N, H, 48, d, 1, s) \
+        == lib.KDA_ERR_UNSUPPORTED
+    torch.cuda.synchronize()

@@ -1,0 +1,104 @@
+"""Decode steps on the GPU against the float64 oracle (one recurrence step
+per call; the state is updated in place unless an output state is given)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import kda_decode_step
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def kda():
+    import gated_delta_rule_108_amd as m
+    return m
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def f64(t):
+    return t.detach().to("cpu").double().numpy()
+
+
+@pytest.mark.parametrize("dk,dv,N,H,dtype", [
+    (16, 16, 3, 2, torch.float32), (32, 128, 2, 5, torch.float32), (128, 16, 1, 3, torch.float32),
+    (64, 64, 4, 4, torch.bfloat16), (128, 128, 2, 3, torch.bfloat16), (16, 32, 7, 1, torch.bfloat16),
+    (128, 128, 64, 32, torch.bfloat16),
+])
+def test_decode_steps_shapes(dk, dv, N, H, dtype):
+    g = torch.Generator().manual_seed(dk + 7 * dv + N)
+    S = 0.1 * torch.randn(N, H, dk, dv, generator=g)
+    Sg = S.to(DEV)
+    Sr = S.double().numpy()
+    tol = 1e-4 if dtype == torch.float32 else 2e-2
+    for step in range(5):
+        q = torch.randn(N, H, dk, generator=g)
+        k = torch.randn(N, H, dk, generator=g)
+        q = (q / q.norm(dim=-1, keepdim=True)).to(dtype)
+        k = (k / k.norm(dim=-1, keepdim=True)).to(dtype)
+        v = torch.randn(N, H, dv, generator=g).to(dtype)
+        alpha = 0.9 + 0.1 * torch.rand(N, H, dk, generator=g)
+        if step == 2:
+            alpha[:, :, 0] = 0.0
+        beta = torch.rand(N, H, generator=g)
+        og, Sg = kda().decode_step(q.to(DEV), k.to(DEV), v.to(DEV), alpha.to(DEV), beta.to(DEV),
+                                   Sg)
+        orf, Sr = kda_decode_step(q, k, v, alpha, beta, Sr)
+        torch.cuda.synchronize()
+        assert rel(f64(og), orf) < tol
+    assert rel(f64(Sg), Sr) < tol
+
+
+def test_out_of_place_equals_in_place():
+    g = torch.Generator().manual_seed(3)
+    N, H, d = 5, 4, 128
+    S = torch.randn(N, H, d, d, generator=g).to(DEV)
+    q = torch.randn(N, H, d, generator=g).bfloat16().to(DEV)
+    k = torch.randn(N, H, d, generator=g).bfloat16().to(DEV)
+    v = torch.randn(N, H, d, generator=g).bfloat16().to(DEV)
+    a = torch.rand(N, H, d, generator=g).to(DEV)
+    b = torch.rand(N, H, generator=g).to(DEV)
+    S_out = torch.empty_like(S)
+    o1, S1 = kda().decode_step(q, k, v, a, b, S, state_out=S_out)
+    S_keep = S.clone()
+    o2, S2 = kda().decode_step(q, k, v, a, b, S)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    assert not torch.equal(S_keep, S2)
+
+
+def test_decode_n256_h32_1000_steps():
+    """The decode workload in full (256 sequences x 32 heads, 1000 in-place
+    steps, inputs pre-generated on the device); the oracle follows sequences
+    0 and 255 over every step."""
+    spec = wl.DECODE["decode_n256_h32"]
+    torch.cuda.empty_cache()
+    S = wl.make_decode_state(spec, DEV)
+    steps = wl.make_decode_steps(spec, DEV)
+    seqs = [0, 255]
+    Sr = f64(S[seqs])
+    ref_steps = {k: t[:, seqs].cpu() for k, t in steps.items()}
+    outs = []
+    for s in range(spec.steps):
+        o, S = kda().decode_step(steps["q"][s], steps["k"][s], steps["v"][s], steps["alpha"][s],
+                                 steps["beta"][s], S)
+        outs.append(o[seqs].clone())
+    torch.cuda.synchronize()
+    og = f64(torch.stack(outs))
+    orf = []
+    for s in range(spec.steps):
+        o_r, Sr = kda_decode_step(ref_steps["q"][s], ref_steps["k"][s], ref_steps["v"][s],
+                                  ref_steps["alpha"][s], ref_steps["beta"][s], Sr)
+        orf.append(o_r)
+    eo = rel(og, np.stack(orf))
+    es = rel(f64(S[seqs]), Sr)
+    print(f"[decode_n256_h32 1000 steps, seqs {seqs}] rel_o={eo:.3e} rel_S={es:.3e}", flush=True)
+    assert eo < 2e-2 and es < 2e-2
+    del steps
+    torch.cuda.empty_cache()
