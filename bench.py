@@ -80,9 +80,10 @@ def cpu_baseline(inp, torch):
     import concurrent.futures as cf
     import multiprocessing as mp
     B, T, H, _ = inp["q"].shape
-    chains = [(inp["q"][b:b + 1, :, h:h + 1].numpy(), inp["k"][b:b + 1, :, h:h + 1].numpy(),
-               inp["v"][b:b + 1, :, h:h + 1].numpy(), inp["alpha"][b:b + 1, :, h:h + 1].numpy(),
-               inp["beta"][b:b + 1, :, h:h + 1].numpy())
+    f = lambda t: t.float().numpy()  # noqa: E731  (bf16 -> fp32 is exact)
+    chains = [(f(inp["q"][b:b + 1, :, h:h + 1]), f(inp["k"][b:b + 1, :, h:h + 1]),
+               f(inp["v"][b:b + 1, :, h:h + 1]), f(inp["alpha"][b:b + 1, :, h:h + 1]),
+               f(inp["beta"][b:b + 1, :, h:h + 1]))
               for b in range(B) for h in range(H)]
     cores = min(len(os.sched_getaffinity(0)), 16, len(chains))
     t0 = time.perf_counter()
@@ -112,6 +113,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="headline prefill only (no decode / large prefill lines)")
+    ap.add_argument("--only", choices=["prefill", "decode", "large", "copy"], default=None,
+                    help="run one leg only (for profiler runs); 'copy' times a plain "
+                         "1 GiB device-to-device copy used to calibrate HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -126,11 +130,33 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     out = {}
+    if args.only == "copy":
+        n = 1 << 28                                     # 2^28 floats = 1 GiB
+        x = torch.ones(n, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        ms, _ = time_launches(lambda: y.copy_(x), args.steps, args.warmup, torch)
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
+                          "ms_per_copy": ms, "GBps": 8 * n / (ms * 1e-3) / 1e9}), flush=True)
+        return
+    legs = {"prefill", "decode", "large"} if args.only is None else {args.only}
+    if args.no_extra:
+        legs = {"prefill"}
 
     # ---------------- headline: prefill, H=16, T=4096, d=128, bf16, C=64
     spec = wl.PREFILL["prefill_h16_t4k"]
-    C = 64
     inp_cpu = wl.make_prefill_inputs(spec, "cpu")
+    if "prefill" in legs:
+        headline(args, spec, inp_cpu, out, torch, kda, dev)
+    extras(args, legs, out, torch, kda, wl, dev)
+    if not args.no_cpu and args.only is None:
+        out["cpu_baseline"] = cpu_baseline(inp_cpu, torch)
+        print(f"# cpu_baseline: {out['cpu_baseline']['value']:.1f} tokens/s",
+              file=sys.stderr, flush=True)
+    print(json.dumps(out), flush=True)
+
+
+def headline(args, spec, inp_cpu, out, torch, kda, dev):
+    C = 64
     g = {k: (None if t is None else t.to(dev)) for k, t in inp_cpu.items()}
     o = torch.empty(spec.B, spec.T, spec.H, spec.dv, dtype=spec.dtype, device=dev)
     S_T = torch.empty(spec.B, spec.H, spec.dk, spec.dv, dtype=torch.float32, device=dev)
@@ -172,7 +198,10 @@ def main():
     print(f"# prefill_h16_t4k: {ms_ev * 1e3:.1f} us/launch (events), {gbs:.0f} GB/s, "
           f"{tfl:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
-    if not args.no_extra:
+
+
+def extras(args, legs, out, torch, kda, wl, dev):
+    if "decode" in legs:
         # ---------------- decode: 256 x 32 heads, d = 128, in place
         dspec = wl.DECODE["decode_n256_h32"]
         S = wl.make_decode_state(dspec, dev)
@@ -204,6 +233,7 @@ def main():
         del S, st, od
         torch.cuda.empty_cache()
 
+    if "large" in legs:
         # ---------------- large prefill: B=8, H=32, T=8192
         lspec = wl.PREFILL["prefill_b8_h32_t8k"]
         lg = wl.make_prefill_inputs(lspec, dev)
@@ -227,12 +257,6 @@ def main():
         print(f"# prefill_b8_h32_t8k: {ms_l:.3f} ms/launch", file=sys.stderr, flush=True)
         del lg, lo, lS
         torch.cuda.empty_cache()
-
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(inp_cpu, torch)
-        print(f"# cpu_baseline: {out['cpu_baseline']['value']:.1f} tokens/s",
-              file=sys.stderr, flush=True)
-    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

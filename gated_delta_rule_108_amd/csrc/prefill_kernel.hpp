@@ -49,24 +49,36 @@ constexpr float kUnsafeBlockDecay = 7.888609052210118e-31f;  // 2^-100
 // MFMA fragment sources.  A source yields, for the calling lane, the operand
 // fragment of rows row0 + (lane % 16) and contraction indices k0 + n*(lane/16)
 // .. + n-1, n = 8 (bf16, K=32), 4 (bf16, K=16) or 1 (fp32, K=4).
+//
+// Lane coordinates come from `Lane`, re-derived once per phase through an
+// opaque move so that the compiler computes fragment addresses where they are
+// used instead of hoisting hundreds of them out of the chunk loop (which
+// exhausts the register file).
 // ----------------------------------------------------------------------------
 template <typename OpT, int KS> struct Frag;
 template <> struct Frag<bf16_t, 32> { using T = bf16x8; static constexpr int N = 8; };
 template <> struct Frag<bf16_t, 16> { using T = bf16x4; static constexpr int N = 4; };
 template <> struct Frag<float, 4> { using T = float; static constexpr int N = 1; };
 
-__device__ __forceinline__ int lane_g() { return (threadIdx.x & 63) >> 4; }
-__device__ __forceinline__ int lane_i() { return threadIdx.x & 15; }
+struct Lane {
+  int i, g;  // i = lane % 16, g = (lane % 64) / 16
+};
+__device__ __forceinline__ Lane lane_now() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return Lane{t & 15, (t & 63) >> 4};
+}
 
 // OpT rows, K-contiguous.
 template <typename OpT> struct Src {
   using E = typename Ty<OpT>::Elem;
   const E* p;
   int ld;
+  Lane l;
   template <int KS>
   __device__ __forceinline__ typename Frag<OpT, KS>::T get(int k0) const {
     using F = Frag<OpT, KS>;
-    const E* a = p + lane_i() * ld + k0 + F::N * lane_g();
+    const E* a = p + l.i * ld + k0 + F::N * l.g;
     if constexpr (F::N == 1) return *a;
     else return *reinterpret_cast<const typename F::T*>(a);
   }
@@ -78,11 +90,12 @@ template <typename OpT> struct SrcScaled {
   const E* p;
   int ld;
   const float* s;
+  Lane l;
   template <int KS>
   __device__ __forceinline__ typename Frag<OpT, KS>::T get(int k0) const {
     using F = Frag<OpT, KS>;
-    const int kk = k0 + F::N * lane_g();
-    const E* a = p + lane_i() * ld + kk;
+    const int kk = k0 + F::N * l.g;
+    const E* a = p + l.i * ld + kk;
     if constexpr (F::N == 1) {
       return *a * s[kk];
     } else {
@@ -98,10 +111,11 @@ template <typename OpT> struct SrcScaled {
 template <typename OpT> struct SrcF32 {
   const float* p;
   int ld;
+  Lane l;
   template <int KS>
   __device__ __forceinline__ typename Frag<OpT, KS>::T get(int k0) const {
     using F = Frag<OpT, KS>;
-    const float* a = p + lane_i() * ld + k0 + F::N * lane_g();
+    const float* a = p + l.i * ld + k0 + F::N * l.g;
     if constexpr (F::N == 1) {
       return *a;
     } else {
@@ -117,9 +131,10 @@ template <typename OpT> struct SrcF32 {
 struct SrcColF32 {
   const float* p;
   int ld;
+  Lane l;
   template <int KS>
   __device__ __forceinline__ float get(int k0) const {
-    return p[(k0 + lane_g()) * ld + lane_i()];
+    return p[(k0 + l.g) * ld + l.i];
   }
 };
 
@@ -134,6 +149,7 @@ template <> struct Pair<bf16_t> {
   __device__ __forceinline__ static float get(T v, int x) {
     return bf16_to_f32(static_cast<uint16_t>(x ? (v >> 16) : (v & 0xffffu)));
   }
+  __device__ __forceinline__ static T pack(float lo, float hi) { return pack_bf16x2(lo, hi); }
 };
 template <> struct Pair<float> {
   using T = float2;
@@ -142,6 +158,29 @@ template <> struct Pair<float> {
   }
   __device__ __forceinline__ static T zero() { return make_float2(0.f, 0.f); }
   __device__ __forceinline__ static float get(T v, int x) { return x ? v.y : v.x; }
+  __device__ __forceinline__ static T pack(float lo, float hi) { return make_float2(lo, hi); }
+};
+
+// Sixteen consecutive elements of one row (16 tokens of one channel), built
+// two at a time and stored with 16-byte writes.
+template <typename OpT> struct Col16;
+template <> struct Col16<bf16_t> {
+  uint32_t w[8];
+  __device__ __forceinline__ void put2(int j, float a, float b) { w[j >> 1] = pack_bf16x2(a, b); }
+  __device__ __forceinline__ void store(uint16_t* dst) const {
+    uint4* d = reinterpret_cast<uint4*>(dst);
+    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+};
+template <> struct Col16<float> {
+  float w[16];
+  __device__ __forceinline__ void put2(int j, float a, float b) { w[j] = a; w[j + 1] = b; }
+  __device__ __forceinline__ void store(float* dst) const {
+    float4* d = reinterpret_cast<float4*>(dst);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d[q] = make_float4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+  }
 };
 
 template <typename OpT, int KS>
@@ -221,8 +260,9 @@ struct PCfg {
   // region sizes in bytes
   static constexpr int kZ1 = align16(imax(imax(2 * C * LDK, DVT * LDC), DVT * LDK) * EB);
   static constexpr int kR1 = align16(C * LDK * EB);
-  static constexpr int kR2 = align16(imax(C * LDK, DVT * LDC) * EB);
+  static constexpr int kR2 = align16(C * LDK * EB);
   static constexpr int kKT = align16(DK * LDC * EB);
+  static constexpr int kKB = align16(imax(DK, DVT) * LDC * EB);
   static constexpr int kTT = align16(C * LDT * 4);
   static constexpr int kZB = align16(imax(NB - 1, 1) * 16 * LDZ * 4);
   static constexpr int kPP = align16(C * LDC * EB);
@@ -236,7 +276,7 @@ struct PCfg {
   static constexpr int oR1 = oZ1 + kZ1;
   static constexpr int oR2 = oR1 + kR1;
   static constexpr int oKB = oR2 + kR2;
-  static constexpr int oKG = oKB + kKT;
+  static constexpr int oKG = oKB + kKB;
   static constexpr int oTT = oKG + kKT;
   static constexpr int oZB = oTT + kTT;
   static constexpr int oPP = oZB + kZB;
@@ -272,6 +312,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
                    int B, int T, int H, int DV) {
   using Cf = PCfg<OpT, DK, C, DVT>;
   using E = typename Ty<OpT>::Elem;
+  using PT = typename Pair<OpT>::T;
   constexpr int NB = Cf::NB, NJ = Cf::NJ, NW = Cf::NW, NTH = Cf::NTH;
   constexpr int LDK = Cf::LDK, LDC = Cf::LDC, LDT = Cf::LDT, LDZ = Cf::LDZ;
   static_assert(Cf::kLds <= kMaxLds, "LDS plan exceeds 160 KiB");
@@ -284,8 +325,8 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
   E* Kr = reinterpret_cast<E*>(smem + Cf::oR1);              // [C][LDK]
   E* Wm = reinterpret_cast<E*>(smem + Cf::oR1);              // [C][LDK]   (after A/P)
   E* Qr = reinterpret_cast<E*>(smem + Cf::oR2);              // [C][LDK]
-  E* UT = reinterpret_cast<E*>(smem + Cf::oR2);              // [DVT][LDC] (scan)
   E* KbT = reinterpret_cast<E*>(smem + Cf::oKB);             // [DK][LDC]
+  E* UT = reinterpret_cast<E*>(smem + Cf::oKB);              // [DVT][LDC] (scan)
   E* KgT = reinterpret_cast<E*>(smem + Cf::oKG);             // [DK][LDC]
   float* TT = reinterpret_cast<float*>(smem + Cf::oTT);      // [C][LDT]
   float* ZB = reinterpret_cast<float*>(smem + Cf::oZB);      // [NB-1][16][LDZ]
@@ -298,8 +339,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
   int* sFL = reinterpret_cast<int*>(smem + Cf::oFL);         // [NB]
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
-  const int g = lane_g(), li = lane_i();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
   // Workgroup -> (chain, slab).  Consecutive workgroups are dealt round-robin
   // to the 8 XCDs; keep all slabs of one chain on one XCD so they share L2.
@@ -311,21 +351,25 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
   const int j0 = (L % ntiles) * DVT;
   const int b = chain / H, h = chain % H;
 
-  const size_t tokstride = static_cast<size_t>(H);  // tokens are H apart in [B,T,H,*]
-  auto tok = [&](int t) -> size_t { return (static_cast<size_t>(b) * T + t) * tokstride + h; };
+  // Token t of this chain sits at row (b*T + t)*H + h of the [B*T*H, *]
+  // arrays.  Within a chunk, rows are H apart: each chunk gets wave-uniform
+  // 64-bit base pointers and 32-bit per-lane offsets.
+  const size_t row0 = static_cast<size_t>(b) * T * H + h;
+  const int rsK = H * DK, rsV = H * DV;
 
   // ---- state slab in registers: tile s of wave w is sigma = w + NW*s = (Cb, Jb)
   f32x4 Sreg[Cf::NSW];
+  {
+    const Lane ln = lane_now();
 #pragma unroll
-  for (int s = 0; s < Cf::NSW; ++s) {
-    const int sg = wave + NW * s;
-    Sreg[s] = zero4();
-    if (sg < Cf::NS && gS0 != nullptr) {
-      const int Cb = sg / NJ, Jb = sg % NJ;
+    for (int s = 0; s < Cf::NSW; ++s) {
+      const int sg = wave + NW * s;
+      Sreg[s] = zero4();
+      if (sg < Cf::NS && gS0 != nullptr) {
+        const int Cb = sg / NJ, Jb = sg % NJ;
+        const float* src = gS0 + static_cast<size_t>(chain) * DK * DV + j0 + 16 * Jb;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int c = 16 * Cb + 4 * g + r;
-        Sreg[s][r] = gS0[(static_cast<size_t>(chain) * DK + c) * DV + j0 + 16 * Jb + li];
+        for (int r = 0; r < 4; ++r) Sreg[s][r] = src[(16 * Cb + 4 * ln.g + r) * DV + ln.i];
       }
     }
   }
@@ -338,38 +382,87 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     }
   }
 
+  // Raw chunk inputs live in registers and are fetched one chunk ahead: the
+  // loads for chunk ch+1 are issued as soon as chunk ch is done with the
+  // previous contents, so their latency hides behind chunk ch's compute.
+  // Rows are clamped to the last token; rows past T are replaced by identity
+  // padding (gate 1, key/query/value 0, strength 0) when consumed.
+  float ga[Cf::NGT][16][2];     // alpha, two channels
+  PT gkk[Cf::NGT][16], gqq[Cf::NGT][16];
+  PT gvv[Cf::NVT][16];
+  float gbe = 0.f;
+  auto fetch_gates = [&](int tn) {
+    const size_t base = (row0 + static_cast<size_t>(tn) * H) * DK;
+    const float* pa = galpha + base;
+    const E* pk = gk + base;
+    const E* pq = gq + base;
+    const int jmax = T - 1 - tn;
+    int t_ = tid;
+    asm volatile("" : "+v"(t_));
+#pragma unroll
+    for (int it = 0; it < Cf::NGT; ++it) {
+      const int item = t_ + NTH * it;
+      if (Cf::NGI % NTH == 0 || item < Cf::NGI) {
+        const int J = item / (DK / 2), c = 2 * (item % (DK / 2));
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int off = min(16 * J + j, jmax) * rsK + c;
+          const float2 a2 = *reinterpret_cast<const float2*>(pa + off);
+          ga[it][j][0] = a2.x;
+          ga[it][j][1] = a2.y;
+          gkk[it][j] = Pair<OpT>::load(pk + off);
+          gqq[it][j] = Pair<OpT>::load(pq + off);
+        }
+      }
+    }
+  };
+  auto fetch_values = [&](int tn) {
+    const E* pv = gv + (row0 + static_cast<size_t>(tn) * H) * DV + j0;
+    const int jmax = T - 1 - tn;
+    int t_ = tid;
+    asm volatile("" : "+v"(t_));
+#pragma unroll
+    for (int it = 0; it < Cf::NVT; ++it) {
+      const int item = t_ + NTH * it;
+      if (Cf::NVI % NTH == 0 || item < Cf::NVI) {
+        const int J = item / (DVT / 2), cc = 2 * (item % (DVT / 2));
+#pragma unroll
+        for (int j = 0; j < 16; ++j) gvv[it][j] = Pair<OpT>::load(pv + min(16 * J + j, jmax) * rsV + cc);
+      }
+    }
+  };
+  auto fetch_beta = [&](int tn) {
+    if (tid < C) gbe = gbeta[row0 + static_cast<size_t>(min(tn + tid, T - 1)) * H];
+  };
+
   const int NC = (T + C - 1) / C;
+  if (NC > 0) {
+    fetch_gates(0);
+    fetch_values(0);
+    fetch_beta(0);
+  }
   for (int ch = 0; ch < NC; ++ch) {
     const int t0 = ch * C;
-    // ================= G1: load the chunk, within-block cumulative gates
-    float ga[Cf::NGT][16][2];     // alpha, two channels
-    typename Pair<OpT>::T gkk[Cf::NGT][16], gqq[Cf::NGT][16];
-    typename Pair<OpT>::T gvv[Cf::NVT][16];
-    if (tid < C) {
-      const int t = t0 + tid;
-      sBE[tid] = (t < T) ? gbeta[tok(t)] : 0.f;
-    }
+    const bool more = ch + 1 < NC;
+    const bool full = t0 + C <= T;   // no padding rows in this chunk
+    // ================= G1: pad the fetched chunk, within-block cumulative gates
+    if (tid < C) sBE[tid] = (t0 + tid < T) ? gbe : 0.f;
+    if (more) fetch_beta(t0 + C);
     if (tid < NB) sFL[tid] = 0;
 #pragma unroll
     for (int it = 0; it < Cf::NGT; ++it) {
       const int item = tid + NTH * it;
-      if (item < Cf::NGI) {
+      if (Cf::NGI % NTH == 0 || item < Cf::NGI) {
         const int J = item / (DK / 2), c = 2 * (item % (DK / 2));
         float f0 = 1.f, f1 = 1.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int t = t0 + 16 * J + j;
-          if (t < T) {
-            const size_t base = tok(t) * DK + c;
-            const float2 a2 = *reinterpret_cast<const float2*>(galpha + base);
-            ga[it][j][0] = a2.x;
-            ga[it][j][1] = a2.y;
-            gkk[it][j] = Pair<OpT>::load(gk + base);
-            gqq[it][j] = Pair<OpT>::load(gq + base);
-          } else {
-            ga[it][j][0] = ga[it][j][1] = 1.f;
-            gkk[it][j] = Pair<OpT>::zero();
-            gqq[it][j] = Pair<OpT>::zero();
+          if (!full) {
+            const bool valid = t0 + 16 * J + j < T;
+            ga[it][j][0] = valid ? ga[it][j][0] : 1.f;
+            ga[it][j][1] = valid ? ga[it][j][1] : 1.f;
+            gkk[it][j] = valid ? gkk[it][j] : Pair<OpT>::zero();
+            gqq[it][j] = valid ? gqq[it][j] : Pair<OpT>::zero();
           }
           f0 *= ga[it][j][0];
           f1 *= ga[it][j][1];
@@ -381,12 +474,12 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
 #pragma unroll
     for (int it = 0; it < Cf::NVT; ++it) {
       const int item = tid + NTH * it;
-      if (item < Cf::NVI) {
-        const int J = item / (DVT / 2), cc = 2 * (item % (DVT / 2));
+      if (Cf::NVI % NTH == 0 || item < Cf::NVI) {
+        const int J = item / (DVT / 2);
+        if (!full) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int t = t0 + 16 * J + j;
-          gvv[it][j] = (t < T) ? Pair<OpT>::load(gv + tok(t) * DV + j0 + cc) : Pair<OpT>::zero();
+          for (int j = 0; j < 16; ++j)
+            gvv[it][j] = (t0 + 16 * J + j < T) ? gvv[it][j] : Pair<OpT>::zero();
         }
       }
     }
@@ -411,7 +504,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
 #pragma unroll
     for (int it = 0; it < Cf::NGT; ++it) {
       const int item = tid + NTH * it;
-      if (item < Cf::NGI) {
+      if (Cf::NGI % NTH == 0 || item < Cf::NGI) {
         const int J = item / (DK / 2), c = 2 * (item % (DK / 2));
         float pre[2] = {1.f, 1.f}, suf[2] = {1.f, 1.f};
         bool unsafe = false;
@@ -430,118 +523,131 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
           hx[j][0] = hx[j + 1][0] * ga[it][j + 1][0];
           hx[j][1] = hx[j + 1][1] * ga[it][j + 1][1];
         }
-        float f[2] = {1.f, 1.f};
-        E kbt[2][16], kgt[2][16];
+        bool safe[2];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int r = 16 * J + j;
-          const float be = sBE[r];
-          E kr2[2], qr2[2], ki2[2], kv2[2];
+        for (int x = 0; x < 2; ++x) safe[x] = sBT[J * DK + c + x] >= kUnsafeBlockDecay;
+        float f[2] = {1.f, 1.f};
+        Col16<OpT> kbt[2], kgt[2];
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+          float kb[2][2], kg[2][2];   // [channel][row of the pair]
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const int jj = j + d, r = 16 * J + jj;
+            const float be = sBE[r];
+            float kr[2], qr[2], ki[2], kv[2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+              f[x] *= ga[it][jj][x];
+              const float kk = Pair<OpT>::get(gkk[it][jj], x);
+              const float qq = Pair<OpT>::get(gqq[it][jj], x);
+              kr[x] = kk * f[x];
+              qr[x] = qq * f[x];
+              ki[x] = kk * hx[jj][x];
+              kv[x] = safe[x] ? kk * __builtin_amdgcn_rcpf(f[x]) : 0.f;
+              kb[x][d] = be * kr[x] * pre[x];
+              kg[x][d] = ki[x] * suf[x];
+            }
+            *reinterpret_cast<PT*>(Kr + r * LDK + c) = Pair<OpT>::pack(kr[0], kr[1]);
+            *reinterpret_cast<PT*>(Qr + r * LDK + c) = Pair<OpT>::pack(qr[0], qr[1]);
+            *reinterpret_cast<PT*>(Ki + r * LDK + c) = Pair<OpT>::pack(ki[0], ki[1]);
+            *reinterpret_cast<PT*>(Kinv + r * LDK + c) = Pair<OpT>::pack(kv[0], kv[1]);
+          }
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
-            f[x] *= ga[it][j][x];
-            const float kk = Pair<OpT>::get(gkk[it][j], x);
-            const float qq = Pair<OpT>::get(gqq[it][j], x);
-            const bool safe = sBT[J * DK + c + x] >= kUnsafeBlockDecay;
-            kr2[x] = Ty<OpT>::from_f32(kk * f[x]);
-            qr2[x] = Ty<OpT>::from_f32(qq * f[x]);
-            ki2[x] = Ty<OpT>::from_f32(kk * hx[j][x]);
-            kv2[x] = Ty<OpT>::from_f32(safe ? kk / f[x] : 0.f);
-            kbt[x][j] = Ty<OpT>::from_f32(be * kk * f[x] * pre[x]);
-            kgt[x][j] = Ty<OpT>::from_f32(kk * hx[j][x] * suf[x]);
+            kbt[x].put2(j, kb[x][0], kb[x][1]);
+            kgt[x].put2(j, kg[x][0], kg[x][1]);
           }
-          Kr[r * LDK + c] = kr2[0]; Kr[r * LDK + c + 1] = kr2[1];
-          Qr[r * LDK + c] = qr2[0]; Qr[r * LDK + c + 1] = qr2[1];
-          Ki[r * LDK + c] = ki2[0]; Ki[r * LDK + c + 1] = ki2[1];
-          Kinv[r * LDK + c] = kv2[0]; Kinv[r * LDK + c + 1] = kv2[1];
         }
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            KbT[(c + x) * LDC + 16 * J + j] = kbt[x][j];
-            KgT[(c + x) * LDC + 16 * J + j] = kgt[x][j];
-          }
+        for (int x = 0; x < 2; ++x) {
+          kbt[x].store(KbT + (c + x) * LDC + 16 * J);
+          kgt[x].store(KgT + (c + x) * LDC + 16 * J);
+        }
       }
     }
+    if (more) fetch_gates(t0 + C);
     __syncthreads();
 
     // ================= AP: gated K K^T (-> L in TT) and Q K^T (-> P) tiles
-    for (int p = wave; p < Cf::NAP; p += NW) {
-      int R = 0, rem = p;
-      while (rem > R) { rem -= R + 1; ++R; }
-      const int I = rem;
-      f32x4 accA = zero4(), accP = zero4();
-      const Src<OpT> sKr{Kr + 16 * R * LDK, LDK}, sQr{Qr + 16 * R * LDK, LDK};
-      if (I < R) {
-        if (R == I + 1) {
-          mma_k2<OpT>(accA, accP, 0, DK, sKr, sQr, Src<OpT>{Ki + 16 * I * LDK, LDK});
+    {
+      const Lane ln = lane_now();
+      for (int p = wave; p < Cf::NAP; p += NW) {
+        int R = 0, rem = p;
+        while (rem > R) { rem -= R + 1; ++R; }
+        const int I = rem;
+        f32x4 accA = zero4(), accP = zero4();
+        const Src<OpT> sKr{Kr + 16 * R * LDK, LDK, ln}, sQr{Qr + 16 * R * LDK, LDK, ln};
+        if (I < R) {
+          if (R == I + 1) {
+            mma_k2<OpT>(accA, accP, 0, DK, sKr, sQr, Src<OpT>{Ki + 16 * I * LDK, LDK, ln});
+          } else {
+            mma_k2<OpT>(accA, accP, 0, DK, sKr, sQr,
+                        SrcScaled<OpT>{Ki + 16 * I * LDK, LDK, sMID + (R * NB + I) * DK, ln});
+          }
         } else {
-          mma_k2<OpT>(accA, accP, 0, DK, sKr, sQr,
-                      SrcScaled<OpT>{Ki + 16 * I * LDK, LDK, sMID + (R * NB + I) * DK});
-        }
-      } else {
-        mma_k2<OpT>(accA, accP, 0, DK, sKr, sQr, Src<OpT>{Kinv + 16 * R * LDK, LDK});
-        if (sFL[R]) {
-          // Channels whose block decay fell below 2^-100: exact pairwise
-          // products of alpha on the vector units.
-          for (int c = 0; c < DK; ++c) {
-            if (sBT[R * DK + c] >= kUnsafeBlockDecay) continue;
-            const int ti = t0 + 16 * R + li;
-            const float ki = (ti < T) ? Ty<OpT>::to_f32(gk[tok(ti) * DK + c]) : 0.f;
+          mma_k2<OpT>(accA, accP, 0, DK, sKr, sQr, Src<OpT>{Kinv + 16 * R * LDK, LDK, ln});
+          if (sFL[R]) {
+            // Channels whose block decay fell below 2^-100: exact pairwise
+            // products of alpha on the vector units.
+            const size_t cb = (row0 + static_cast<size_t>(t0 + 16 * R) * H) * DK;
+            const int jmax = T - 1 - (t0 + 16 * R);
+            for (int c = 0; c < DK; ++c) {
+              if (sBT[R * DK + c] >= kUnsafeBlockDecay) continue;
+              const float ki = (ln.i <= jmax) ? Ty<OpT>::to_f32(gk[cb + ln.i * rsK + c]) : 0.f;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              const int rl = 4 * g + rr;
-              if (li > rl) continue;
-              float ratio = 1.f;
-              for (int j = li + 1; j <= rl; ++j) {
-                const int tj = t0 + 16 * R + j;
-                ratio *= (tj < T) ? galpha[tok(tj) * DK + c] : 1.f;
+              for (int rr = 0; rr < 4; ++rr) {
+                const int rl = 4 * ln.g + rr;
+                if (ln.i > rl) continue;
+                float ratio = 1.f;
+                for (int j = ln.i + 1; j <= rl; ++j)
+                  ratio *= (j <= jmax) ? galpha[cb + j * rsK + c] : 1.f;
+                const float kr = (rl <= jmax) ? Ty<OpT>::to_f32(gk[cb + rl * rsK + c]) : 0.f;
+                const float qr = (rl <= jmax) ? Ty<OpT>::to_f32(gq[cb + rl * rsK + c]) : 0.f;
+                accA[rr] += kr * ki * ratio;
+                accP[rr] += qr * ki * ratio;
               }
-              const int tr = t0 + 16 * R + rl;
-              const float kr = (tr < T) ? Ty<OpT>::to_f32(gk[tok(tr) * DK + c]) : 0.f;
-              const float qr = (tr < T) ? Ty<OpT>::to_f32(gq[tok(tr) * DK + c]) : 0.f;
-              accA[rr] += kr * ki * ratio;
-              accP[rr] += qr * ki * ratio;
             }
           }
         }
-      }
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int rl = 4 * g + rr, r = 16 * R + rl, i = 16 * I + li;
-        const bool diag = (I == R);
-        const float a = (diag && li >= rl) ? 0.f : accA[rr];
-        const float pv = (diag && li > rl) ? 0.f : accP[rr];
-        TT[r * LDT + i] = sBE[r] * a;
-        PP[r * LDC + i] = Ty<OpT>::from_f32(pv);
+        for (int rr = 0; rr < 4; ++rr) {
+          const int rl = 4 * ln.g + rr, r = 16 * R + rl, i = 16 * I + ln.i;
+          const bool diag = (I == R);
+          const float a = (diag && ln.i >= rl) ? 0.f : accA[rr];
+          const float pv = (diag && ln.i > rl) ? 0.f : accP[rr];
+          TT[r * LDT + i] = sBE[r] * a;
+          PP[r * LDC + i] = Ty<OpT>::from_f32(pv);
+        }
       }
     }
     __syncthreads();
 
     // ================= SD: invert the 16x16 diagonal blocks of I + L
-    // (forward substitution, one column per lane) while the other lanes
-    // stage beta-scaled values, transposed, for U~ = Y Diag(beta) V.
+    // (forward substitution, one column per lane) while every thread stages
+    // beta-scaled values, transposed, for U~ = Y Diag(beta) V.
 #pragma unroll
     for (int it = 0; it < Cf::NVT; ++it) {
       const int item = tid + NTH * it;
-      if (item < Cf::NVI) {
+      if (Cf::NVI % NTH == 0 || item < Cf::NVI) {
         const int J = item / (DVT / 2), cc = 2 * (item % (DVT / 2));
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-          E col[16];
+          Col16<OpT> col;
 #pragma unroll
-          for (int j = 0; j < 16; ++j)
-            col[j] = Ty<OpT>::from_f32(sBE[16 * J + j] * Pair<OpT>::get(gvv[it][j], x));
-#pragma unroll
-          for (int j = 0; j < 16; ++j) VbT[(cc + x) * LDC + 16 * J + j] = col[j];
+          for (int j = 0; j < 16; j += 2)
+            col.put2(j, sBE[16 * J + j] * Pair<OpT>::get(gvv[it][j], x),
+                     sBE[16 * J + j + 1] * Pair<OpT>::get(gvv[it][j + 1], x));
+          col.store(VbT + (cc + x) * LDC + 16 * J);
         }
       }
     }
+    if (more) fetch_values(t0 + C);
     {
-      const int R = 4 * wave + g;   // lane group -> diagonal block
+      const Lane ln = lane_now();
+      const int R = 4 * wave + ln.g;   // lane group -> diagonal block
       if (R < NB) {
-        const int j = li;
+        const int j = ln.i;
         const float* Lb = TT + 16 * R * LDT + 16 * R;
         float y[16];
 #pragma unroll
@@ -560,129 +666,136 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     // ================= SO: off-diagonal blocks of Y, one block row at a time
     //   Y_RI = -Y_RR * sum_{J=I}^{R-1} L_RJ Y_JI
     for (int R = 1; R < NB; ++R) {
+      const Lane ln = lane_now();
       for (int I = wave; I < R; I += NW) {
         f32x4 z = zero4();
         for (int J = I; J < R; ++J)
-          mma_f32(z, 0, 16, Src<float>{TT + 16 * R * LDT + 16 * J, LDT},
-                  SrcColF32{TT + 16 * J * LDT + 16 * I, LDT});
+          mma_f32(z, 0, 16, Src<float>{TT + 16 * R * LDT + 16 * J, LDT, ln},
+                  SrcColF32{TT + 16 * J * LDT + 16 * I, LDT, ln});
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) ZB[(I * 16 + 4 * g + rr) * LDZ + li] = z[rr];
+        for (int rr = 0; rr < 4; ++rr) ZB[(I * 16 + 4 * ln.g + rr) * LDZ + ln.i] = z[rr];
       }
       __syncthreads();
       for (int I = wave; I < R; I += NW) {
         f32x4 y = zero4();
-        mma_f32(y, 0, 16, Src<float>{TT + 16 * R * LDT + 16 * R, LDT},
-                SrcColF32{ZB + I * 16 * LDZ, LDZ});
+        mma_f32(y, 0, 16, Src<float>{TT + 16 * R * LDT + 16 * R, LDT, ln},
+                SrcColF32{ZB + I * 16 * LDZ, LDZ, ln});
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) TT[(16 * R + 4 * g + rr) * LDT + 16 * I + li] = -y[rr];
+        for (int rr = 0; rr < 4; ++rr)
+          TT[(16 * R + 4 * ln.g + rr) * LDT + 16 * I + ln.i] = -y[rr];
       }
       __syncthreads();
     }
 
     // ================= WU: W = Y (beta K E) (stored row-major) and U~ = Y (beta V)
-    for (int w = wave; w < Cf::NCB * NB; w += NW) {
-      const int Cb = w / NB, R = w % NB;
-      f32x4 acc = zero4();
-      mma_k<OpT>(acc, 0, 16 * (R + 1), Src<OpT>{KbT + 16 * Cb * LDC, LDC},
-                 SrcF32<OpT>{TT + 16 * R * LDT, LDT});
-      // acc[rr] = W^T[c = 16Cb + 4g + rr][r = 16R + li]
-      E* dst = Wm + (16 * R + li) * LDK + 16 * Cb + 4 * g;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(acc[rr]);
-    }
     f32x4 Ureg[Cf::NUW];
+    {
+      const Lane ln = lane_now();
+      for (int w = wave; w < Cf::NCB * NB; w += NW) {
+        const int Cb = w / NB, R = w % NB;
+        f32x4 acc = zero4();
+        mma_k<OpT>(acc, 0, 16 * (R + 1), Src<OpT>{KbT + 16 * Cb * LDC, LDC, ln},
+                   SrcF32<OpT>{TT + 16 * R * LDT, LDT, ln});
+        // acc[rr] = W^T[c = 16Cb + 4g + rr][r = 16R + i]
+        E* dst = Wm + (16 * R + ln.i) * LDK + 16 * Cb + 4 * ln.g;
 #pragma unroll
-    for (int u = 0; u < Cf::NUW; ++u) {
-      const int tau = wave + NW * u;
-      Ureg[u] = zero4();
-      if (tau < Cf::NU) {
-        const int R = tau / NJ, Jb = tau % NJ;
-        mma_k<OpT>(Ureg[u], 0, 16 * (R + 1), SrcF32<OpT>{TT + 16 * R * LDT, LDT},
-                   Src<OpT>{VbT + 16 * Jb * LDC, LDC});
+        for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(acc[rr]);
+      }
+#pragma unroll
+      for (int u = 0; u < Cf::NUW; ++u) {
+        const int tau = wave + NW * u;
+        Ureg[u] = zero4();
+        if (tau < Cf::NU) {
+          const int R = tau / NJ, Jb = tau % NJ;
+          mma_k<OpT>(Ureg[u], 0, 16 * (R + 1), SrcF32<OpT>{TT + 16 * R * LDT, LDT, ln},
+                     Src<OpT>{VbT + 16 * Jb * LDC, LDC, ln});
+        }
       }
     }
     __syncthreads();
 
     // ================= scan: U = U~ - W S,  O = (Q E) S + P U,  S update
+    {
+      const Lane ln = lane_now();
 #pragma unroll
-    for (int s = 0; s < Cf::NSW; ++s) {
-      const int sg = wave + NW * s;
-      if (sg < Cf::NS) {
-        const int Cb = sg / NJ, Jb = sg % NJ;
-        E* dst = ST + (16 * Jb + li) * LDK + 16 * Cb + 4 * g;
+      for (int s = 0; s < Cf::NSW; ++s) {
+        const int sg = wave + NW * s;
+        if (sg < Cf::NS) {
+          const int Cb = sg / NJ, Jb = sg % NJ;
+          E* dst = ST + (16 * Jb + ln.i) * LDK + 16 * Cb + 4 * ln.g;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(Sreg[s][rr]);
-      }
-    }
-    __syncthreads();
-    f32x4 Oreg[Cf::NUW];
-#pragma unroll
-    for (int u = 0; u < Cf::NUW; ++u) {
-      const int tau = wave + NW * u;
-      Oreg[u] = zero4();
-      if (tau < Cf::NU) {
-        const int R = tau / NJ, Jb = tau % NJ;
-        f32x4 x = zero4();
-        mma_k2<OpT>(x, Oreg[u], 0, DK, Src<OpT>{Wm + 16 * R * LDK, LDK},
-                    SrcScaled<OpT>{Qr + 16 * R * LDK, LDK, sPRE + R * DK},
-                    Src<OpT>{ST + 16 * Jb * LDK, LDK});
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) Ureg[u][rr] -= x[rr];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < Cf::NUW; ++u) {
-      const int tau = wave + NW * u;
-      if (tau < Cf::NU) {
-        const int R = tau / NJ, Jb = tau % NJ;
-        E* dst = UT + (16 * Jb + li) * LDC + 16 * R + 4 * g;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(Ureg[u][rr]);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < Cf::NUW; ++u) {
-      const int tau = wave + NW * u;
-      if (tau < Cf::NU) {
-        const int R = tau / NJ, Jb = tau % NJ;
-        mma_k<OpT>(Oreg[u], 0, 16 * (R + 1), Src<OpT>{PP + 16 * R * LDC, LDC},
-                   Src<OpT>{UT + 16 * Jb * LDC, LDC});
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int t = t0 + 16 * R + 4 * g + rr;
-          if (t < T) go[tok(t) * DV + j0 + 16 * Jb + li] = Ty<OpT>::from_f32(Oreg[u][rr]);
+          for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(Sreg[s][rr]);
         }
       }
     }
+    __syncthreads();
+    {
+      const Lane ln = lane_now();
 #pragma unroll
-    for (int s = 0; s < Cf::NSW; ++s) {
-      const int sg = wave + NW * s;
-      if (sg < Cf::NS) {
-        const int Cb = sg / NJ, Jb = sg % NJ;
-        f32x4 acc = zero4();
-        mma_k<OpT>(acc, 0, C, Src<OpT>{KgT + 16 * Cb * LDC, LDC},
-                   Src<OpT>{UT + 16 * Jb * LDC, LDC});
+      for (int u = 0; u < Cf::NUW; ++u) {
+        const int tau = wave + NW * u;
+        if (tau < Cf::NU) {
+          const int R = tau / NJ, Jb = tau % NJ;
+          f32x4 x = zero4();
+          mma_k<OpT>(x, 0, DK, Src<OpT>{Wm + 16 * R * LDK, LDK, ln},
+                     Src<OpT>{ST + 16 * Jb * LDK, LDK, ln});
+          // U = U~ - W S, staged transposed for the products over tokens
+          E* dst = UT + (16 * Jb + ln.i) * LDC + 16 * R + 4 * ln.g;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          Sreg[s][rr] = sGC[16 * Cb + 4 * g + rr] * Sreg[s][rr] + acc[rr];
+          for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(Ureg[u][rr] - x[rr]);
+        }
+      }
+    }
+    __syncthreads();
+    {
+      // O = (Q E) S + P U, straight to HBM
+      const Lane ln = lane_now();
+      E* po = go + (row0 + static_cast<size_t>(t0) * H) * DV + j0;
+      const int jmax = T - 1 - t0;
+#pragma unroll
+      for (int u = 0; u < Cf::NUW; ++u) {
+        const int tau = wave + NW * u;
+        if (tau < Cf::NU) {
+          const int R = tau / NJ, Jb = tau % NJ;
+          f32x4 acc = zero4();
+          mma_k<OpT>(acc, 0, DK, SrcScaled<OpT>{Qr + 16 * R * LDK, LDK, sPRE + R * DK, ln},
+                     Src<OpT>{ST + 16 * Jb * LDK, LDK, ln});
+          mma_k<OpT>(acc, 0, 16 * (R + 1), Src<OpT>{PP + 16 * R * LDC, LDC, ln},
+                     Src<OpT>{UT + 16 * Jb * LDC, LDC, ln});
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int rl = 16 * R + 4 * ln.g + rr;
+            if (full || rl <= jmax) po[rl * rsV + 16 * Jb + ln.i] = Ty<OpT>::from_f32(acc[rr]);
+          }
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < Cf::NSW; ++s) {
+        const int sg = wave + NW * s;
+        if (sg < Cf::NS) {
+          const int Cb = sg / NJ, Jb = sg % NJ;
+          f32x4 acc = zero4();
+          mma_k<OpT>(acc, 0, C, Src<OpT>{KgT + 16 * Cb * LDC, LDC, ln},
+                     Src<OpT>{UT + 16 * Jb * LDC, LDC, ln});
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            Sreg[s][rr] = sGC[16 * Cb + 4 * ln.g + rr] * Sreg[s][rr] + acc[rr];
+        }
       }
     }
     __syncthreads();
   }
 
   if (gST != nullptr) {
+    const Lane ln = lane_now();
 #pragma unroll
     for (int s = 0; s < Cf::NSW; ++s) {
       const int sg = wave + NW * s;
       if (sg < Cf::NS) {
         const int Cb = sg / NJ, Jb = sg % NJ;
+        float* dst = gST + static_cast<size_t>(chain) * DK * DV + j0 + 16 * Jb;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int c = 16 * Cb + 4 * g + r;
-          gST[(static_cast<size_t>(chain) * DK + c) * DV + j0 + 16 * Jb + li] = Sreg[s][r];
-        }
+        for (int r = 0; r < 4; ++r) dst[(16 * Cb + 4 * ln.g + r) * DV + ln.i] = Sreg[s][r];
       }
     }
   }
