@@ -47,6 +47,38 @@ def decode_alg_bytes(N, H, dk, dv, esize):
     return N * H * per_head
 
 
+def kernel_source_hash():
+    """sha256 over the library's kernel sources (names and contents)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_108_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(name):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE
+    (profiles/<name>.txt), or None when the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"{name}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, _, v = line.partition(":")
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def time_launches(fn, steps, warmup, torch):
     """Warm up, then time `steps` calls bracketed by synchronisations, with
     HIP events on the current stream (the stream the kernels run on)."""
@@ -188,7 +220,7 @@ def headline(args, spec, inp_cpu, out, torch, kda, dev):
         "config": {"workload": "prefill_h16_t4k", "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
                    "C": C, "io_dtype": "bf16", "state_dtype": "fp32"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": profiled_traffic("prefill_h16_t4k"),
                      "kernel": "kda_prefill_kernel<bf16,128,64,16>",
                      "kernel_ms": ms_ev, "alg_bytes_per_launch": nbytes},
         "mfma": {"achieved_tflops": tfl, "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
@@ -226,6 +258,7 @@ def extras(args, legs, out, torch, kda, wl, dev):
             "state_GBps": state_bytes / (ms_d * 1e-3) / 1e9,
             "alg_GBps": dbytes / (ms_d * 1e-3) / 1e9,
             "frac_hbm": dbytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": profiled_traffic("decode_n256_h32"), "alg_bytes_per_step": dbytes,
             "head_steps_per_s": dspec.N * dspec.H / (ms_dw * 1e-3),
         }
         print(f"# decode_n256_h32: {ms_d * 1e3:.1f} us/step, "
@@ -251,6 +284,7 @@ def extras(args, legs, out, torch, kda, wl, dev):
         out["prefill_b8_h32_t8k"] = {
             "C": 64, "ms_per_launch": ms_l, "tokens_per_s": lspec.B * lspec.T / (ms_lw * 1e-3),
             "GBps": lb / (ms_l * 1e-3) / 1e9, "frac_hbm": lb / (ms_l * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": profiled_traffic("prefill_b8_h32_t8k"), "alg_bytes_per_launch": lb,
             "tflops": lf / (ms_l * 1e-3) / 1e12,
             "frac_mfma": lf / (ms_l * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         }

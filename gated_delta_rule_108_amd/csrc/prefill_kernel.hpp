@@ -191,41 +191,67 @@ __device__ __forceinline__ f32x4 mfma(typename Frag<OpT, KS>::T a, typename Frag
   else return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// acc += A[.., kb..ke) * B[kb..ke, ..]  (kb, ke multiples of 16)
+// Products on the matrix cores.  Each call returns A[.., kb..ke) * B[kb..ke, ..]
+// (kb, ke multiples of 16) in fresh accumulators; callers combine partial
+// products with vector adds.  A chain on one accumulator only ever uses one
+// instruction kind: a 16-wide K tail after 32-wide steps is issued into its
+// own zero accumulator.  (A 16x16x16 bf16 MFMA that reads, as its C operand,
+// the result of the 16x16x32 MFMA issued just before it was seen to read
+// stale values for two of the four accumulator registers, so the kernels
+// never chain the two kinds.)
+__device__ __forceinline__ void add4(f32x4& a, const f32x4& b) {
+  a[0] += b[0]; a[1] += b[1]; a[2] += b[2]; a[3] += b[3];
+}
+
 template <typename OpT, class SA, class SB>
-__device__ __forceinline__ void mma_k(f32x4& acc, int kb, int ke, const SA& sa, const SB& sb) {
+__device__ __forceinline__ f32x4 mma_k(int kb, int ke, const SA& sa, const SB& sb) {
+  f32x4 acc = zero4();
   if constexpr (sizeof(typename Ty<OpT>::Elem) == 2) {
     int k = kb;
     for (; k + 32 <= ke; k += 32)
       acc = mfma<OpT, 32>(sa.template get<32>(k), sb.template get<32>(k), acc);
-    if (k < ke) acc = mfma<OpT, 16>(sa.template get<16>(k), sb.template get<16>(k), acc);
+    if (k < ke) {
+      if (k == kb) {
+        acc = mfma<OpT, 16>(sa.template get<16>(k), sb.template get<16>(k), acc);
+      } else {
+        add4(acc, mfma<OpT, 16>(sa.template get<16>(k), sb.template get<16>(k), zero4()));
+      }
+    }
   } else {
     for (int k = kb; k < ke; k += 4)
       acc = mfma<OpT, 4>(sa.template get<4>(k), sb.template get<4>(k), acc);
   }
+  return acc;
 }
 
-// Two products sharing the B operand: acc1 += A1 B, acc2 += A2 B.
+// Two products sharing the B operand: r1 = A1 B, r2 = A2 B.
 template <typename OpT, class SA1, class SA2, class SB>
-__device__ __forceinline__ void mma_k2(f32x4& acc1, f32x4& acc2, int kb, int ke, const SA1& a1,
+__device__ __forceinline__ void mma_k2(f32x4& r1, f32x4& r2, int kb, int ke, const SA1& a1,
                                        const SA2& a2, const SB& sb) {
+  r1 = zero4();
+  r2 = zero4();
   if constexpr (sizeof(typename Ty<OpT>::Elem) == 2) {
     int k = kb;
     for (; k + 32 <= ke; k += 32) {
       auto b = sb.template get<32>(k);
-      acc1 = mfma<OpT, 32>(a1.template get<32>(k), b, acc1);
-      acc2 = mfma<OpT, 32>(a2.template get<32>(k), b, acc2);
+      r1 = mfma<OpT, 32>(a1.template get<32>(k), b, r1);
+      r2 = mfma<OpT, 32>(a2.template get<32>(k), b, r2);
     }
     if (k < ke) {
       auto b = sb.template get<16>(k);
-      acc1 = mfma<OpT, 16>(a1.template get<16>(k), b, acc1);
-      acc2 = mfma<OpT, 16>(a2.template get<16>(k), b, acc2);
+      if (k == kb) {
+        r1 = mfma<OpT, 16>(a1.template get<16>(k), b, r1);
+        r2 = mfma<OpT, 16>(a2.template get<16>(k), b, r2);
+      } else {
+        add4(r1, mfma<OpT, 16>(a1.template get<16>(k), b, zero4()));
+        add4(r2, mfma<OpT, 16>(a2.template get<16>(k), b, zero4()));
+      }
     }
   } else {
     for (int k = kb; k < ke; k += 4) {
       float b = sb.template get<4>(k);
-      acc1 = mfma<OpT, 4>(a1.template get<4>(k), b, acc1);
-      acc2 = mfma<OpT, 4>(a2.template get<4>(k), b, acc2);
+      r1 = mfma<OpT, 4>(a1.template get<4>(k), b, r1);
+      r2 = mfma<OpT, 4>(a2.template get<4>(k), b, r2);
     }
   }
 }
@@ -237,6 +263,62 @@ __device__ __forceinline__ void mma_f32(f32x4& acc, int kb, int ke, const SA& sa
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sa.template get<4>(k), sb.template get<4>(k), acc,
                                                0, 0, 0);
 }
+
+// out[b] = A * B_b for a row of NBT tiles sharing the A operand; tile b's B
+// source is `sb` moved by b * bstride elements.  Same chaining rule as mma_k.
+template <typename OpT, int NBT, class SA, class SB>
+__device__ __forceinline__ void mma_row(f32x4 (&out)[NBT], int kb, int ke, const SA& sa,
+                                        const SB& sb, int bstride) {
+#pragma unroll
+  for (int b = 0; b < NBT; ++b) out[b] = zero4();
+  if constexpr (sizeof(typename Ty<OpT>::Elem) == 2) {
+    int k = kb;
+    for (; k + 32 <= ke; k += 32) {
+      const auto a = sa.template get<32>(k);
+#pragma unroll
+      for (int b = 0; b < NBT; ++b) {
+        SB t = sb;
+        t.p += b * bstride;
+        out[b] = mfma<OpT, 32>(a, t.template get<32>(k), out[b]);
+      }
+    }
+    if (k < ke) {
+      const auto a = sa.template get<16>(k);
+      const bool first = (k == kb);
+#pragma unroll
+      for (int b = 0; b < NBT; ++b) {
+        SB t = sb;
+        t.p += b * bstride;
+        if (first) out[b] = mfma<OpT, 16>(a, t.template get<16>(k), out[b]);
+        else add4(out[b], mfma<OpT, 16>(a, t.template get<16>(k), zero4()));
+      }
+    }
+  } else {
+    for (int k = kb; k < ke; k += 4) {
+      const float a = sa.template get<4>(k);
+#pragma unroll
+      for (int b = 0; b < NBT; ++b) {
+        SB t = sb;
+        t.p += b * bstride;
+        out[b] = mfma<OpT, 4>(a, t.template get<4>(k), out[b]);
+      }
+    }
+  }
+}
+
+// Ownership of an NR x NCOL grid of 16x16 tiles by NW waves.  A wave owns
+// tiles (row0(w) + a, col0(w) + b) with a < RA and b < CA known at compile
+// time, so one wave-dependent base addresses all of them.  Grids too small
+// to split evenly go to wave 0 alone.
+template <int NR, int NCOL, int NW>
+struct TileMap {
+  static constexpr int kMode = (NR % NW == 0) ? 0 : ((NCOL % NW == 0) ? 1 : 2);
+  static constexpr int RA = kMode == 0 ? NR / NW : NR;
+  static constexpr int CA = kMode == 1 ? NCOL / NW : NCOL;
+  __device__ __forceinline__ static bool active(int w) { return kMode != 2 || w == 0; }
+  __device__ __forceinline__ static int row0(int w) { return kMode == 0 ? w * RA : 0; }
+  __device__ __forceinline__ static int col0(int w) { return kMode == 1 ? w * CA : 0; }
+};
 
 // ----------------------------------------------------------------------------
 // LDS plan (element counts; every region 16-byte aligned).
@@ -267,7 +349,7 @@ struct PCfg {
   static constexpr int kZB = align16(imax(NB - 1, 1) * 16 * LDZ * 4);
   static constexpr int kPP = align16(C * LDC * EB);
   static constexpr int kBT = align16(NB * DK * 4);
-  static constexpr int kMID = align16(imax(NB * NB, 1) * DK * 4);
+  static constexpr int kMID = align16(imax(imax(NB * NB, 1) * DK * 4, C * LDC * EB));
   static constexpr int kGC = align16(DK * 4);
   static constexpr int kBE = align16(C * 4);
   static constexpr int kFL = align16(NB * 4);
@@ -316,6 +398,12 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
   constexpr int NB = Cf::NB, NJ = Cf::NJ, NW = Cf::NW, NTH = Cf::NTH;
   constexpr int LDK = Cf::LDK, LDC = Cf::LDC, LDT = Cf::LDT, LDZ = Cf::LDZ;
   static_assert(Cf::kLds <= kMaxLds, "LDS plan exceeds 160 KiB");
+  constexpr bool kBF = sizeof(E) == 2;
+  constexpr int LDO = DVT + 16 / static_cast<int>(sizeof(E));
+  constexpr bool kStageO = C * LDO * static_cast<int>(sizeof(E)) <= Cf::kR1;
+  using SM = TileMap<Cf::NCB, NJ, NW>;   // state tiles (Cb, Jb)
+  using UM = TileMap<NB, NJ, NW>;        // chunk-output tiles (R, Jb)
+  using WMp = TileMap<Cf::NCB, NB, NW>;  // W^T tiles (Cb, R)
 
   __shared__ __attribute__((aligned(16))) char smem[Cf::kLds];
   E* Ki = reinterpret_cast<E*>(smem + Cf::oZ1);             // [C][LDK]
@@ -334,6 +422,8 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
   float* sBT = reinterpret_cast<float*>(smem + Cf::oBT);     // [NB][DK]
   float* sPRE = reinterpret_cast<float*>(smem + Cf::oPRE);   // [NB][DK]
   float* sMID = reinterpret_cast<float*>(smem + Cf::oMID);   // [NB][NB][DK]
+  E* Yb = reinterpret_cast<E*>(smem + Cf::oMID);             // [C][LDC]  (after A/P)
+  E* OS = reinterpret_cast<E*>(smem + Cf::oR1);              // [C][LDO]  (output staging)
   float* sGC = reinterpret_cast<float*>(smem + Cf::oGC);     // [DK]
   float* sBE = reinterpret_cast<float*>(smem + Cf::oBE);     // [C]
   int* sFL = reinterpret_cast<int*>(smem + Cf::oFL);         // [NB]
@@ -357,21 +447,22 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
   const size_t row0 = static_cast<size_t>(b) * T * H + h;
   const int rsK = H * DK, rsV = H * DV;
 
-  // ---- state slab in registers: tile s of wave w is sigma = w + NW*s = (Cb, Jb)
-  f32x4 Sreg[Cf::NSW];
+  // ---- state slab in registers, tiles (Cb, Jb) of the state map
+  f32x4 Sreg[SM::RA][SM::CA];
   {
     const Lane ln = lane_now();
 #pragma unroll
-    for (int s = 0; s < Cf::NSW; ++s) {
-      const int sg = wave + NW * s;
-      Sreg[s] = zero4();
-      if (sg < Cf::NS && gS0 != nullptr) {
-        const int Cb = sg / NJ, Jb = sg % NJ;
-        const float* src = gS0 + static_cast<size_t>(chain) * DK * DV + j0 + 16 * Jb;
+    for (int a = 0; a < SM::RA; ++a)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Sreg[s][r] = src[(16 * Cb + 4 * ln.g + r) * DV + ln.i];
+      for (int bb = 0; bb < SM::CA; ++bb) {
+        Sreg[a][bb] = zero4();
+        if (SM::active(wave) && gS0 != nullptr) {
+          const int Cb = SM::row0(wave) + a, Jb = SM::col0(wave) + bb;
+          const float* src = gS0 + static_cast<size_t>(chain) * DK * DV + j0 + 16 * Jb;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Sreg[a][bb][r] = src[(16 * Cb + 4 * ln.g + r) * DV + ln.i];
+        }
       }
-    }
   }
   // Upper block triangles of TT and PP are never written again: zero once.
   for (int x = tid; x < C * C; x += NTH) {
@@ -576,7 +667,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         int R = 0, rem = p;
         while (rem > R) { rem -= R + 1; ++R; }
         const int I = rem;
-        f32x4 accA = zero4(), accP = zero4();
+        f32x4 accA, accP;
         const Src<OpT> sKr{Kr + 16 * R * LDK, LDK, ln}, sQr{Qr + 16 * R * LDK, LDK, ln};
         if (I < R) {
           if (R == I + 1) {
@@ -643,6 +734,14 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       }
     }
     if (more) fetch_values(t0 + C);
+    // Q E = Q F * (decay of the blocks before), in place: P is done with Q F.
+    for (int x = tid; x < C * DK / 2; x += NTH) {
+      const int r = x / (DK / 2), c = 2 * (x % (DK / 2));
+      PT* qp = reinterpret_cast<PT*>(Qr + r * LDK + c);
+      const float* pr = sPRE + (r / 16) * DK + c;
+      const PT v = *qp;
+      *qp = Pair<OpT>::pack(Pair<OpT>::get(v, 0) * pr[0], Pair<OpT>::get(v, 1) * pr[1]);
+    }
     {
       const Lane ln = lane_now();
       const int R = 4 * wave + ln.g;   // lane group -> diagonal block
@@ -658,7 +757,10 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
           y[r] = (r < j) ? 0.f : ((r == j) ? 1.f : -s);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) TT[(16 * R + r) * LDT + 16 * R + j] = y[r];
+        for (int r = 0; r < 16; ++r) {
+          TT[(16 * R + r) * LDT + 16 * R + j] = y[r];
+          if constexpr (kBF) Yb[(16 * R + r) * LDC + 16 * R + j] = Ty<OpT>::from_f32(y[r]);
+        }
       }
     }
     __syncthreads();
@@ -681,123 +783,162 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         mma_f32(y, 0, 16, Src<float>{TT + 16 * R * LDT + 16 * R, LDT, ln},
                 SrcColF32{ZB + I * 16 * LDZ, LDZ, ln});
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          TT[(16 * R + 4 * ln.g + rr) * LDT + 16 * I + ln.i] = -y[rr];
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = 16 * R + 4 * ln.g + rr, i = 16 * I + ln.i;
+          TT[r * LDT + i] = -y[rr];
+          if constexpr (kBF) Yb[r * LDC + i] = Ty<OpT>::from_f32(-y[rr]);
+        }
       }
       __syncthreads();
     }
 
+    // Y as a matrix-core operand: the bf16 copy, or the fp32 original.
+    auto ysrc = [&](int R, const Lane& ln) {
+      if constexpr (kBF) return Src<OpT>{Yb + 16 * R * LDC, LDC, ln};
+      else return Src<OpT>{TT + 16 * R * LDT, LDT, ln};
+    };
+
     // ================= WU: W = Y (beta K E) (stored row-major) and U~ = Y (beta V)
-    f32x4 Ureg[Cf::NUW];
+    f32x4 Ureg[UM::RA][UM::CA];
     {
       const Lane ln = lane_now();
-      for (int w = wave; w < Cf::NCB * NB; w += NW) {
-        const int Cb = w / NB, R = w % NB;
-        f32x4 acc = zero4();
-        mma_k<OpT>(acc, 0, 16 * (R + 1), Src<OpT>{KbT + 16 * Cb * LDC, LDC, ln},
-                   SrcF32<OpT>{TT + 16 * R * LDT, LDT, ln});
-        // acc[rr] = W^T[c = 16Cb + 4g + rr][r = 16R + i]
-        E* dst = Wm + (16 * R + ln.i) * LDK + 16 * Cb + 4 * ln.g;
+      if (WMp::active(wave)) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(acc[rr]);
+        for (int a = 0; a < WMp::RA; ++a) {
+          const int Cb = WMp::row0(wave) + a;
+#pragma unroll
+          for (int bb = 0; bb < WMp::CA; ++bb) {
+            const int R = WMp::col0(wave) + bb;
+            const f32x4 acc =
+                mma_k<OpT>(0, 16 * (R + 1), Src<OpT>{KbT + 16 * Cb * LDC, LDC, ln}, ysrc(R, ln));
+            // acc[rr] = W^T[c = 16Cb + 4g + rr][r = 16R + i]
+            E* dst = Wm + (16 * R + ln.i) * LDK + 16 * Cb + 4 * ln.g;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(acc[rr]);
+          }
+        }
       }
 #pragma unroll
-      for (int u = 0; u < Cf::NUW; ++u) {
-        const int tau = wave + NW * u;
-        Ureg[u] = zero4();
-        if (tau < Cf::NU) {
-          const int R = tau / NJ, Jb = tau % NJ;
-          mma_k<OpT>(Ureg[u], 0, 16 * (R + 1), SrcF32<OpT>{TT + 16 * R * LDT, LDT, ln},
-                     Src<OpT>{VbT + 16 * Jb * LDC, LDC, ln});
+      for (int a = 0; a < UM::RA; ++a) {
+#pragma unroll
+        for (int bb = 0; bb < UM::CA; ++bb) Ureg[a][bb] = zero4();
+        if (UM::active(wave)) {
+          const int R = UM::row0(wave) + a;
+          mma_row<OpT, UM::CA>(Ureg[a], 0, 16 * (R + 1), ysrc(R, ln),
+                               Src<OpT>{VbT + 16 * UM::col0(wave) * LDC, LDC, ln}, 16 * LDC);
         }
       }
     }
     __syncthreads();
 
     // ================= scan: U = U~ - W S,  O = (Q E) S + P U,  S update
-    {
+    if (SM::active(wave)) {
       const Lane ln = lane_now();
 #pragma unroll
-      for (int s = 0; s < Cf::NSW; ++s) {
-        const int sg = wave + NW * s;
-        if (sg < Cf::NS) {
-          const int Cb = sg / NJ, Jb = sg % NJ;
+      for (int a = 0; a < SM::RA; ++a)
+#pragma unroll
+        for (int bb = 0; bb < SM::CA; ++bb) {
+          const int Cb = SM::row0(wave) + a, Jb = SM::col0(wave) + bb;
           E* dst = ST + (16 * Jb + ln.i) * LDK + 16 * Cb + 4 * ln.g;
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(Sreg[s][rr]);
+          for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(Sreg[a][bb][rr]);
         }
-      }
     }
     __syncthreads();
-    {
+    if (UM::active(wave)) {
       const Lane ln = lane_now();
 #pragma unroll
-      for (int u = 0; u < Cf::NUW; ++u) {
-        const int tau = wave + NW * u;
-        if (tau < Cf::NU) {
-          const int R = tau / NJ, Jb = tau % NJ;
-          f32x4 x = zero4();
-          mma_k<OpT>(x, 0, DK, Src<OpT>{Wm + 16 * R * LDK, LDK, ln},
-                     Src<OpT>{ST + 16 * Jb * LDK, LDK, ln});
-          // U = U~ - W S, staged transposed for the products over tokens
+      for (int a = 0; a < UM::RA; ++a) {
+        const int R = UM::row0(wave) + a;
+        f32x4 x[UM::CA];
+        mma_row<OpT, UM::CA>(x, 0, DK, Src<OpT>{Wm + 16 * R * LDK, LDK, ln},
+                             Src<OpT>{ST + 16 * UM::col0(wave) * LDK, LDK, ln}, 16 * LDK);
+        // U = U~ - W S, staged transposed for the products over tokens
+#pragma unroll
+        for (int bb = 0; bb < UM::CA; ++bb) {
+          const int Jb = UM::col0(wave) + bb;
           E* dst = UT + (16 * Jb + ln.i) * LDC + 16 * R + 4 * ln.g;
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(Ureg[u][rr] - x[rr]);
+          for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(Ureg[a][bb][rr] - x[bb][rr]);
         }
       }
     }
     __syncthreads();
+    E* po = go + (row0 + static_cast<size_t>(t0) * H) * DV + j0;
+    const int nrows = min(C, T - t0);
     {
-      // O = (Q E) S + P U, straight to HBM
+      // O = (Q E) S + P U
       const Lane ln = lane_now();
-      E* po = go + (row0 + static_cast<size_t>(t0) * H) * DV + j0;
-      const int jmax = T - 1 - t0;
+      if (UM::active(wave)) {
 #pragma unroll
-      for (int u = 0; u < Cf::NUW; ++u) {
-        const int tau = wave + NW * u;
-        if (tau < Cf::NU) {
-          const int R = tau / NJ, Jb = tau % NJ;
-          f32x4 acc = zero4();
-          mma_k<OpT>(acc, 0, DK, SrcScaled<OpT>{Qr + 16 * R * LDK, LDK, sPRE + R * DK, ln},
-                     Src<OpT>{ST + 16 * Jb * LDK, LDK, ln});
-          mma_k<OpT>(acc, 0, 16 * (R + 1), Src<OpT>{PP + 16 * R * LDC, LDC, ln},
-                     Src<OpT>{UT + 16 * Jb * LDC, LDC, ln});
+        for (int a = 0; a < UM::RA; ++a) {
+          const int R = UM::row0(wave) + a;
+          f32x4 o[UM::CA], pu[UM::CA];
+          mma_row<OpT, UM::CA>(o, 0, DK, Src<OpT>{Qr + 16 * R * LDK, LDK, ln},
+                               Src<OpT>{ST + 16 * UM::col0(wave) * LDK, LDK, ln}, 16 * LDK);
+          mma_row<OpT, UM::CA>(pu, 0, 16 * (R + 1), Src<OpT>{PP + 16 * R * LDC, LDC, ln},
+                               Src<OpT>{UT + 16 * UM::col0(wave) * LDC, LDC, ln}, 16 * LDC);
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int rl = 16 * R + 4 * ln.g + rr;
-            if (full || rl <= jmax) po[rl * rsV + 16 * Jb + ln.i] = Ty<OpT>::from_f32(acc[rr]);
+          for (int bb = 0; bb < UM::CA; ++bb) add4(o[bb], pu[bb]);
+#pragma unroll
+          for (int bb = 0; bb < UM::CA; ++bb) {
+            const int Jb = UM::col0(wave) + bb;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int rl = 16 * R + 4 * ln.g + rr;
+              if constexpr (kStageO) {
+                OS[rl * LDO + 16 * Jb + ln.i] = Ty<OpT>::from_f32(o[bb][rr]);
+              } else {
+                if (full || rl < nrows) po[rl * rsV + 16 * Jb + ln.i] = Ty<OpT>::from_f32(o[bb][rr]);
+              }
+            }
           }
         }
       }
+      // S <- Diag(decay of the chunk) S + (K E')^T U
+      if (SM::active(wave)) {
 #pragma unroll
-      for (int s = 0; s < Cf::NSW; ++s) {
-        const int sg = wave + NW * s;
-        if (sg < Cf::NS) {
-          const int Cb = sg / NJ, Jb = sg % NJ;
-          f32x4 acc = zero4();
-          mma_k<OpT>(acc, 0, C, Src<OpT>{KgT + 16 * Cb * LDC, LDC, ln},
-                     Src<OpT>{UT + 16 * Jb * LDC, LDC, ln});
+        for (int a = 0; a < SM::RA; ++a) {
+          const int Cb = SM::row0(wave) + a;
+          f32x4 acc[SM::CA];
+          mma_row<OpT, SM::CA>(acc, 0, C, Src<OpT>{KgT + 16 * Cb * LDC, LDC, ln},
+                               Src<OpT>{UT + 16 * SM::col0(wave) * LDC, LDC, ln}, 16 * LDC);
+          const float4 gc = *reinterpret_cast<const float4*>(sGC + 16 * Cb + 4 * ln.g);
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            Sreg[s][rr] = sGC[16 * Cb + 4 * ln.g + rr] * Sreg[s][rr] + acc[rr];
+          for (int bb = 0; bb < SM::CA; ++bb) {
+            Sreg[a][bb][0] = gc.x * Sreg[a][bb][0] + acc[bb][0];
+            Sreg[a][bb][1] = gc.y * Sreg[a][bb][1] + acc[bb][1];
+            Sreg[a][bb][2] = gc.z * Sreg[a][bb][2] + acc[bb][2];
+            Sreg[a][bb][3] = gc.w * Sreg[a][bb][3] + acc[bb][3];
+          }
         }
       }
     }
     __syncthreads();
-  }
-
-  if (gST != nullptr) {
-    const Lane ln = lane_now();
-#pragma unroll
-    for (int s = 0; s < Cf::NSW; ++s) {
-      const int sg = wave + NW * s;
-      if (sg < Cf::NS) {
-        const int Cb = sg / NJ, Jb = sg % NJ;
-        float* dst = gST + static_cast<size_t>(chain) * DK * DV + j0 + 16 * Jb;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(16 * Cb + 4 * ln.g + r) * DV + ln.i] = Sreg[s][r];
+    if constexpr (kStageO) {
+      // staged output rows -> HBM with 16-byte stores
+      constexpr int VPR = DVT * static_cast<int>(sizeof(E)) / 16;   // vectors per row
+      constexpr int EPV = 16 / static_cast<int>(sizeof(E));          // elements per vector
+      for (int x = tid; x < C * VPR; x += NTH) {
+        const int r = x / VPR, cv = x % VPR;
+        if (full || r < nrows)
+          *reinterpret_cast<uint4*>(po + r * rsV + cv * EPV) =
+              *reinterpret_cast<const uint4*>(OS + r * LDO + cv * EPV);
       }
     }
+  }
+
+  if (gST != nullptr && SM::active(wave)) {
+    const Lane ln = lane_now();
+#pragma unroll
+    for (int a = 0; a < SM::RA; ++a)
+#pragma unroll
+      for (int bb = 0; bb < SM::CA; ++bb) {
+        const int Cb = SM::row0(wave) + a, Jb = SM::col0(wave) + bb;
+        float* dst = gST + static_cast<size_t>(chain) * DK * DV + j0 + 16 * Jb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(16 * Cb + 4 * ln.g + r) * DV + ln.i] = Sreg[a][bb][r];
+      }
   }
 }
 

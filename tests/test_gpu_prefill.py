@@ -127,6 +127,32 @@ def test_head_dims(dk, dv, dtype, C):
     check(dict(q=q, k=k, v=v, alpha=alpha, beta=beta, S0=S0), C, label=f"dk={dk} dv={dv}")
 
 
+@pytest.mark.parametrize("dk", [32, 64, 128])
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("alpha_one", [True, False])
+def test_inter_chunk_read_alone(dk, C, alpha_one):
+    """beta = 0 never writes, so o_t = q_t Diag(alpha_1..alpha_t) S0 (pure
+    decayed read of the initial state): isolates the (Q E) S product,
+    including its first rows, from the intra-chunk terms."""
+    g = torch.Generator().manual_seed(dk + C)
+    B, T, H, dv = 1, 48, 2, 128
+    q = torch.randn(B, T, H, dk, generator=g)
+    q = (q / q.norm(dim=-1, keepdim=True)).bfloat16()
+    k = torch.randn(B, T, H, dk, generator=g)
+    k = (k / k.norm(dim=-1, keepdim=True)).bfloat16()
+    v = torch.randn(B, T, H, dv, generator=g).bfloat16()
+    alpha = torch.ones(B, T, H, dk) if alpha_one else 0.9 + 0.1 * torch.rand(B, T, H, dk, generator=g)
+    beta = torch.zeros(B, T, H)
+    S0 = torch.randn(B, H, dk, dv, generator=g)
+    inp = dict(q=q, k=k, v=v, alpha=alpha, beta=beta, S0=S0)
+    o, S = run(inp, C)
+    o_ref, S_ref = oracle(inp)
+    rows = np.linalg.norm(f64(o) - o_ref, axis=-1) / np.linalg.norm(o_ref, axis=-1)
+    print(f"[read alone dk={dk} C={C}] worst row rel={rows.max():.3e}", flush=True)
+    assert rows.max() < 1e-2
+    assert rel(f64(S), S_ref) < 1e-5
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_zero_and_extreme_gates(dtype):
     """Exact zero gates (memory cleared) and gates so small that a 16-row
