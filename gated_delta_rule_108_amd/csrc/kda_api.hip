@@ -67,7 +67,7 @@ size_t kda_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int C, k
   if (dt != KDA_F32 && dt != KDA_BF16) return static_cast<size_t>(-1);
   if (!dim_ok(dk) || !dim_ok(dv)) return static_cast<size_t>(-1);
   if (!kda::prefill_supported(dk, dv, C, dt == KDA_BF16)) return static_cast<size_t>(-1);
-  return 0;
+  return kda::prefill_workspace(B, T, H, dk, dv, C, dt == KDA_BF16);
 }
 
 kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, const float* alpha,
@@ -83,7 +83,8 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
   const void* ptrs[] = {q, k, v, alpha, beta, S0, o, S_T, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return KDA_ERR_ALIGN;
-  (void)workspace_bytes;  // the current kernels need none (query returns 0)
+  const size_t ws_need = kda::prefill_workspace(B, T, H, dk, dv, C, dt == KDA_BF16);
+  if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need)) return KDA_ERR_WORKSPACE;
 
   const size_t e = (dt == KDA_BF16) ? 2 : 4;
   const size_t ntok = static_cast<size_t>(B) * T * H;
@@ -95,6 +96,14 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
                         S0 ? span(S0, nst) : Span{0, 0}, S_T ? span(S_T, nst) : Span{0, 0}};
     for (const Span& s : ins)
       if (overlap(so, s)) return KDA_ERR_ALIAS;
+  }
+  if (ws_need > 0) {
+    const Span sw = span(workspace, ws_need);
+    const Span all[] = {span(q, ntok * dk * e), span(k, ntok * dk * e), span(v, ntok * dv * e),
+                        span(alpha, ntok * dk * 4), span(beta, ntok * 4), span(o, ntok * dv * e),
+                        S0 ? span(S0, nst) : Span{0, 0}, S_T ? span(S_T, nst) : Span{0, 0}};
+    for (const Span& s : all)
+      if (overlap(sw, s)) return KDA_ERR_ALIAS;
   }
   if (S_T) {
     const Span st = span(S_T, nst);
@@ -110,7 +119,8 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
   if (dev != KDA_OK) return dev;
   if (!S_T && !has_tokens) return KDA_OK;  // nothing to compute or write
 
-  kda::PrefillArgs a{q, k, v, alpha, beta, S0, o, S_T, B, T, H, dk, dv, C, dt == KDA_BF16, stream};
+  kda::PrefillArgs a{q, k, v, alpha, beta, S0, o, S_T, B, T, H, dk, dv, C, dt == KDA_BF16, stream,
+                     workspace, workspace_bytes};
   if (kda::launch_prefill(a) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
 }

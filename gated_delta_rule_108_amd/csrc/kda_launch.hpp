@@ -33,6 +33,8 @@ struct PrefillArgs {
   int B, T, H, dk, dv, C;
   bool bf16;
   void* stream;
+  void* workspace;          // split path only (see prefill_workspace)
+  size_t workspace_bytes;
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
@@ -40,5 +42,7 @@ hipError_t launch_decode(const DecodeArgs& a);
 // Returns hipErrorInvalidValue when no compiled kernel covers (dk, C, dtype).
 hipError_t launch_prefill(const PrefillArgs& a);
 bool prefill_supported(int dk, int dv, int C, bool bf16);
+// Device workspace bytes the prefill needs for these sizes (0: none).
+size_t prefill_workspace(int B, int T, int H, int dk, int dv, int C, bool bf16);
 
 }  // namespace kda

@@ -1,6 +1,6 @@
 // Dispatch of kda_prefill_chunked over (element type, dk); the kernels are
 // instantiated in prefill_<type>_<dk>.hip so they compile in parallel.
-#include "prefill_kernel.hpp"
+#include "scan_kernel.hpp"
 
 namespace kda {
 
@@ -12,6 +12,16 @@ bool prefill_supported(int dk, int dv, int C, bool bf16) {
     case 128: return bf16 ? prefill_supported_bf16_128(dv, C) : prefill_supported_f32_128(dv, C);
   }
   return false;
+}
+
+size_t prefill_workspace(int B, int T, int H, int dk, int dv, int C, bool bf16) {
+  switch (dk) {
+    case 16: return bf16 ? prefill_workspace_bf16_16(B, T, H, dv, C) : prefill_workspace_f32_16(B, T, H, dv, C);
+    case 32: return bf16 ? prefill_workspace_bf16_32(B, T, H, dv, C) : prefill_workspace_f32_32(B, T, H, dv, C);
+    case 64: return bf16 ? prefill_workspace_bf16_64(B, T, H, dv, C) : prefill_workspace_f32_64(B, T, H, dv, C);
+    case 128: return bf16 ? prefill_workspace_bf16_128(B, T, H, dv, C) : prefill_workspace_f32_128(B, T, H, dv, C);
+  }
+  return 0;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {

@@ -1,5 +1,5 @@
 // Chunked-prefill kernels for bf16 q/k/v/o and dk = 16.
-#include "prefill_kernel.hpp"
+#include "scan_kernel.hpp"
 
 namespace kda {
 KDA_PREFILL_INSTANCE(bf16_t, bf16, 16)

@@ -1,5 +1,5 @@
 // Chunked-prefill kernels for f32 q/k/v/o and dk = 32.
-#include "prefill_kernel.hpp"
+#include "scan_kernel.hpp"
 
 namespace kda {
 KDA_PREFILL_INSTANCE(float, f32, 32)

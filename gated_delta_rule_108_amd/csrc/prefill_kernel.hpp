@@ -183,6 +183,15 @@ template <> struct Col16<float> {
   }
 };
 
+// Orders this wave's LDS writes before its later LDS reads (no other wave
+// takes part, so no barrier is needed).
+__device__ __forceinline__ void wave_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+// Index of the off-diagonal block (R, I), I < R, in row-major lower order.
+__host__ __device__ constexpr int yf_block(int R, int I) { return R * (R - 1) / 2 + I; }
+
 template <typename OpT, int KS>
 __device__ __forceinline__ f32x4 mfma(typename Frag<OpT, KS>::T a, typename Frag<OpT, KS>::T b,
                                       f32x4 c) {
@@ -306,19 +315,78 @@ __device__ __forceinline__ void mma_row(f32x4 (&out)[NBT], int kb, int ke, const
   }
 }
 
-// Ownership of an NR x NCOL grid of 16x16 tiles by NW waves.  A wave owns
-// tiles (row0(w) + a, col0(w) + b) with a < RA and b < CA known at compile
-// time, so one wave-dependent base addresses all of them.  Grids too small
-// to split evenly go to wave 0 alone.
+// Ownership of an NR x NCOL grid of 16x16 tiles by NW waves.  The waves form a
+// WR x WC grid (WR divides NR, WC divides NCOL, WR * WC <= NW, as many active
+// waves as possible); wave w < WR * WC owns the RA x CA block of tiles
+// (row0(w) + a, col0(w) + b), a and b known at compile time, so one
+// wave-dependent base addresses all of them.  Other waves own nothing.
+__host__ __device__ constexpr int largest_divisor_le(int n, int cap) {
+  int best = 1;
+  for (int d = 1; d <= n && d <= cap; ++d)
+    if (n % d == 0) best = d;
+  return best;
+}
+__host__ __device__ constexpr int tile_wr(int NR, int NCOL, int NW) {
+  int best_wr = 1, best_act = 0;
+  for (int wr = 1; wr <= NR && wr <= NW; ++wr) {
+    if (NR % wr) continue;
+    const int wc = largest_divisor_le(NCOL, NW / wr);
+    if (wr * wc > best_act) { best_act = wr * wc; best_wr = wr; }
+  }
+  return best_wr;
+}
 template <int NR, int NCOL, int NW>
 struct TileMap {
-  static constexpr int kMode = (NR % NW == 0) ? 0 : ((NCOL % NW == 0) ? 1 : 2);
-  static constexpr int RA = kMode == 0 ? NR / NW : NR;
-  static constexpr int CA = kMode == 1 ? NCOL / NW : NCOL;
-  __device__ __forceinline__ static bool active(int w) { return kMode != 2 || w == 0; }
-  __device__ __forceinline__ static int row0(int w) { return kMode == 0 ? w * RA : 0; }
-  __device__ __forceinline__ static int col0(int w) { return kMode == 1 ? w * CA : 0; }
+  static constexpr int WR = tile_wr(NR, NCOL, NW);
+  static constexpr int WC = largest_divisor_le(NCOL, NW / WR);
+  static constexpr int RA = NR / WR;
+  static constexpr int CA = NCOL / WC;
+  __device__ __forceinline__ static bool active(int w) { return w < WR * WC; }
+  __device__ __forceinline__ static int row0(int w) { return (w / WC) * RA; }
+  __device__ __forceinline__ static int col0(int w) { return (w % WC) * CA; }
 };
+
+// ----------------------------------------------------------------------------
+// Workspace record of one chunk (written by the prep kernel, read by the scan
+// kernel), elements of the operand type unless noted:
+//   W [C][DK] | Q.E [C][DK] | (K.E')^T [DK][C] | P [C][C] | Y [C][C] |
+//   chunk decay E_{C-1} [DK] float32
+// ----------------------------------------------------------------------------
+template <typename OpT, int DK, int C>
+struct RecCfg {
+  static constexpr int EB = Ty<OpT>::kBytes;
+  static constexpr size_t kW = 0;
+  static constexpr size_t kQ = static_cast<size_t>(C) * DK;
+  static constexpr size_t kKG = 2 * static_cast<size_t>(C) * DK;
+  static constexpr size_t kP = 3 * static_cast<size_t>(C) * DK;
+  static constexpr size_t kY = kP + static_cast<size_t>(C) * C;
+  static constexpr size_t kElems = kY + static_cast<size_t>(C) * C;
+  static constexpr size_t kGcByte = kElems * EB;
+  static constexpr size_t kBytes = (kGcByte + 4 * DK + 255) / 256 * 256;
+};
+
+// rows x n elements between a dense array (row length n) and a padded LDS
+// array (row length ld), 16-byte vectors; n * sizeof(T) is a multiple of 16.
+template <typename T>
+__device__ __forceinline__ void copy_rows(T* dense, const T* padded, int rows, int n, int ld,
+                                          int tid, int nth) {
+  const int vpr = n * static_cast<int>(sizeof(T)) / 16, epv = 16 / static_cast<int>(sizeof(T));
+  for (int x = tid; x < rows * vpr; x += nth) {
+    const int r = x / vpr, cv = x % vpr;
+    *reinterpret_cast<uint4*>(dense + static_cast<size_t>(r) * n + cv * epv) =
+        *reinterpret_cast<const uint4*>(padded + r * ld + cv * epv);
+  }
+}
+template <typename T>
+__device__ __forceinline__ void copy_rows_in(T* padded, const T* dense, int rows, int n, int ld,
+                                             int tid, int nth) {
+  const int vpr = n * static_cast<int>(sizeof(T)) / 16, epv = 16 / static_cast<int>(sizeof(T));
+  for (int x = tid; x < rows * vpr; x += nth) {
+    const int r = x / vpr, cv = x % vpr;
+    *reinterpret_cast<uint4*>(padded + r * ld + cv * epv) =
+        *reinterpret_cast<const uint4*>(dense + static_cast<size_t>(r) * n + cv * epv);
+  }
+}
 
 // ----------------------------------------------------------------------------
 // LDS plan (element counts; every region 16-byte aligned).
@@ -328,7 +396,7 @@ __host__ __device__ constexpr int align16(int bytes) { return (bytes + 15) & ~15
 
 template <typename OpT, int DK, int C, int DVT>
 struct PCfg {
-  static constexpr int NTH = 256, NW = 4;
+  static constexpr int NTH = 512, NW = 8;
   static constexpr int NB = C / 16;            // 16-row sub-blocks per chunk
   static constexpr int NJ = DVT / 16;          // 16-column tiles of the slab
   static constexpr int NCB = DK / 16;          // 16-channel tiles
@@ -347,6 +415,7 @@ struct PCfg {
   static constexpr int kKB = align16(imax(DK, DVT) * LDC * EB);
   static constexpr int kTT = align16(C * LDT * 4);
   static constexpr int kZB = align16(imax(NB - 1, 1) * 16 * LDZ * 4);
+  static constexpr int kYF = align16(imax(NB * (NB - 1) / 2, 1) * 16 * LDZ * 4);
   static constexpr int kPP = align16(C * LDC * EB);
   static constexpr int kBT = align16(NB * DK * 4);
   static constexpr int kMID = align16(imax(imax(NB * NB, 1) * DK * 4, C * LDC * EB));
@@ -361,7 +430,8 @@ struct PCfg {
   static constexpr int oKG = oKB + kKB;
   static constexpr int oTT = oKG + kKT;
   static constexpr int oZB = oTT + kTT;
-  static constexpr int oPP = oZB + kZB;
+  static constexpr int oYF = oZB + kZB;
+  static constexpr int oPP = oYF + kYF;
   static constexpr int oBT = oPP + kPP;
   static constexpr int oPRE = oBT + kBT;
   static constexpr int oMID = oPRE + kBT;
@@ -384,14 +454,18 @@ struct PCfg {
 
 constexpr int kMaxLds = 160 * 1024;
 
-template <typename OpT, int DK, int C, int DVT>
-__global__ void __launch_bounds__(256)
+// kPrep = false: the fused prefill (all chunks of a chain, state in
+// registers).  kPrep = true: one workgroup per chunk computes only the
+// column-free chunk quantities and writes them to the workspace record of
+// that chunk (W, Q.E, (K.E')^T, P, Y, chunk decay) for the scan kernel.
+template <typename OpT, int DK, int C, int DVT, bool kPrep = false>
+__global__ void __launch_bounds__(512)
 kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
                    const typename Ty<OpT>::Elem* __restrict__ gk,
                    const typename Ty<OpT>::Elem* __restrict__ gv,
                    const float* __restrict__ galpha, const float* __restrict__ gbeta,
                    const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float* gST,
-                   int B, int T, int H, int DV) {
+                   int B, int T, int H, int DV, char* __restrict__ gws) {
   using Cf = PCfg<OpT, DK, C, DVT>;
   using E = typename Ty<OpT>::Elem;
   using PT = typename Pair<OpT>::T;
@@ -418,6 +492,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
   E* KgT = reinterpret_cast<E*>(smem + Cf::oKG);             // [DK][LDC]
   float* TT = reinterpret_cast<float*>(smem + Cf::oTT);      // [C][LDT]
   float* ZB = reinterpret_cast<float*>(smem + Cf::oZB);      // [NB-1][16][LDZ]
+  float* YF = reinterpret_cast<float*>(smem + Cf::oYF);      // off-diagonal Y blocks, fp32
   E* PP = reinterpret_cast<E*>(smem + Cf::oPP);              // [C][LDC]
   float* sBT = reinterpret_cast<float*>(smem + Cf::oBT);     // [NB][DK]
   float* sPRE = reinterpret_cast<float*>(smem + Cf::oPRE);   // [NB][DK]
@@ -433,12 +508,15 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
 
   // Workgroup -> (chain, slab).  Consecutive workgroups are dealt round-robin
   // to the 8 XCDs; keep all slabs of one chain on one XCD so they share L2.
-  const int ntiles = DV / DVT;
+  const int NC = (T + C - 1) / C;
+  const int ntiles = kPrep ? NC : DV / DVT;
   const int total = gridDim.x;
   int L = blockIdx.x;
-  if (ntiles > 1 && (total % 8) == 0) L = (blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
+  if (!kPrep && ntiles > 1 && (total % 8) == 0) L = (blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
   const int chain = L / ntiles;
-  const int j0 = (L % ntiles) * DVT;
+  const int j0 = kPrep ? 0 : (L % ntiles) * DVT;
+  const int ch_begin = kPrep ? L % ntiles : 0;
+  const int ch_end = kPrep ? ch_begin + 1 : NC;
   const int b = chain / H, h = chain % H;
 
   // Token t of this chain sits at row (b*T + t)*H + h of the [B*T*H, *]
@@ -456,7 +534,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
 #pragma unroll
       for (int bb = 0; bb < SM::CA; ++bb) {
         Sreg[a][bb] = zero4();
-        if (SM::active(wave) && gS0 != nullptr) {
+        if (!kPrep && SM::active(wave) && gS0 != nullptr) {
           const int Cb = SM::row0(wave) + a, Jb = SM::col0(wave) + bb;
           const float* src = gS0 + static_cast<size_t>(chain) * DK * DV + j0 + 16 * Jb;
 #pragma unroll
@@ -526,15 +604,14 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     if (tid < C) gbe = gbeta[row0 + static_cast<size_t>(min(tn + tid, T - 1)) * H];
   };
 
-  const int NC = (T + C - 1) / C;
-  if (NC > 0) {
-    fetch_gates(0);
-    fetch_values(0);
-    fetch_beta(0);
+  if (ch_begin < ch_end) {
+    fetch_gates(ch_begin * C);
+    if constexpr (!kPrep) fetch_values(0);
+    fetch_beta(ch_begin * C);
   }
-  for (int ch = 0; ch < NC; ++ch) {
+  for (int ch = ch_begin; ch < ch_end; ++ch) {
     const int t0 = ch * C;
-    const bool more = ch + 1 < NC;
+    const bool more = ch + 1 < ch_end;
     const bool full = t0 + C <= T;   // no padding rows in this chunk
     // ================= G1: pad the fetched chunk, within-block cumulative gates
     if (tid < C) sBE[tid] = (t0 + tid < T) ? gbe : 0.f;
@@ -563,7 +640,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       }
     }
 #pragma unroll
-    for (int it = 0; it < Cf::NVT; ++it) {
+    for (int it = 0; it < (kPrep ? 0 : Cf::NVT); ++it) {
       const int item = tid + NTH * it;
       if (Cf::NVI % NTH == 0 || item < Cf::NVI) {
         const int J = item / (DVT / 2);
@@ -660,47 +737,13 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     if (more) fetch_gates(t0 + C);
     __syncthreads();
 
-    // ================= AP: gated K K^T (-> L in TT) and Q K^T (-> P) tiles
+    // ================= AP + SD: gated K K^T (-> L in TT) and Q K^T (-> P) tiles.
+    // Wave R < NB computes the diagonal pair (R, R) and inverts the 16x16
+    // block I + L_RR straight away (its own LDS writes, no barrier); the
+    // other waves compute the off-diagonal pairs meanwhile.
     {
       const Lane ln = lane_now();
-      for (int p = wave; p < Cf::NAP; p += NW) {
-        int R = 0, rem = p;
-        while (rem > R) { rem -= R + 1; ++R; }
-        const int I = rem;
-        f32x4 accA, accP;
-        const Src<OpT> sKr{Kr + 16 * R * LDK, LDK, ln}, sQr{Qr + 16 * R * LDK, LDK, ln};
-        if (I < R) {
-          if (R == I + 1) {
-            mma_k2<OpT>(accA, accP, 0, DK, sKr, sQr, Src<OpT>{Ki + 16 * I * LDK, LDK, ln});
-          } else {
-            mma_k2<OpT>(accA, accP, 0, DK, sKr, sQr,
-                        SrcScaled<OpT>{Ki + 16 * I * LDK, LDK, sMID + (R * NB + I) * DK, ln});
-          }
-        } else {
-          mma_k2<OpT>(accA, accP, 0, DK, sKr, sQr, Src<OpT>{Kinv + 16 * R * LDK, LDK, ln});
-          if (sFL[R]) {
-            // Channels whose block decay fell below 2^-100: exact pairwise
-            // products of alpha on the vector units.
-            const size_t cb = (row0 + static_cast<size_t>(t0 + 16 * R) * H) * DK;
-            const int jmax = T - 1 - (t0 + 16 * R);
-            for (int c = 0; c < DK; ++c) {
-              if (sBT[R * DK + c] >= kUnsafeBlockDecay) continue;
-              const float ki = (ln.i <= jmax) ? Ty<OpT>::to_f32(gk[cb + ln.i * rsK + c]) : 0.f;
-#pragma unroll
-              for (int rr = 0; rr < 4; ++rr) {
-                const int rl = 4 * ln.g + rr;
-                if (ln.i > rl) continue;
-                float ratio = 1.f;
-                for (int j = ln.i + 1; j <= rl; ++j)
-                  ratio *= (j <= jmax) ? galpha[cb + j * rsK + c] : 1.f;
-                const float kr = (rl <= jmax) ? Ty<OpT>::to_f32(gk[cb + rl * rsK + c]) : 0.f;
-                const float qr = (rl <= jmax) ? Ty<OpT>::to_f32(gq[cb + rl * rsK + c]) : 0.f;
-                accA[rr] += kr * ki * ratio;
-                accP[rr] += qr * ki * ratio;
-              }
-            }
-          }
-        }
+      auto store_tiles = [&](int R, int I, const f32x4& accA, const f32x4& accP) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int rl = 4 * ln.g + rr, r = 16 * R + rl, i = 16 * I + ln.i;
@@ -710,15 +753,81 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
           TT[r * LDT + i] = sBE[r] * a;
           PP[r * LDC + i] = Ty<OpT>::from_f32(pv);
         }
+      };
+      if (wave < NB) {
+        const int R = wave;
+        f32x4 accA, accP;
+        mma_k2<OpT>(accA, accP, 0, DK, Src<OpT>{Kr + 16 * R * LDK, LDK, ln},
+                    Src<OpT>{Qr + 16 * R * LDK, LDK, ln}, Src<OpT>{Kinv + 16 * R * LDK, LDK, ln});
+        if (sFL[R]) {
+          // Channels whose block decay fell below 2^-100: exact pairwise
+          // products of alpha on the vector units.
+          const size_t cb = (row0 + static_cast<size_t>(t0 + 16 * R) * H) * DK;
+          const int jmax = T - 1 - (t0 + 16 * R);
+          for (int c = 0; c < DK; ++c) {
+            if (sBT[R * DK + c] >= kUnsafeBlockDecay) continue;
+            const float ki = (ln.i <= jmax) ? Ty<OpT>::to_f32(gk[cb + ln.i * rsK + c]) : 0.f;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int rl = 4 * ln.g + rr;
+              if (ln.i > rl) continue;
+              float ratio = 1.f;
+              for (int j = ln.i + 1; j <= rl; ++j)
+                ratio *= (j <= jmax) ? galpha[cb + j * rsK + c] : 1.f;
+              const float kr = (rl <= jmax) ? Ty<OpT>::to_f32(gk[cb + rl * rsK + c]) : 0.f;
+              const float qr = (rl <= jmax) ? Ty<OpT>::to_f32(gq[cb + rl * rsK + c]) : 0.f;
+              accA[rr] += kr * ki * ratio;
+              accP[rr] += qr * ki * ratio;
+            }
+          }
+        }
+        store_tiles(R, R, accA, accP);
+        wave_fence();
+        // Forward substitution for (I + L_RR) Y_RR = I, one column per lane of
+        // the first lane group, column-oriented so the updates are independent.
+        if (ln.g == 0) {
+          const int j = ln.i;
+          const float* Lb = TT + 16 * R * LDT + 16 * R;
+          float y[16], acc[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+          for (int m = 0; m < 16; ++m) {
+            y[m] = (m < j) ? 0.f : ((m == j) ? 1.f : -acc[m]);
+#pragma unroll
+            for (int r = m + 1; r < 16; ++r) acc[r] += Lb[r * LDT + m] * y[m];
+          }
+          wave_fence();
+          // (Yb shares LDS with the MID scale table, which other waves may
+          // still be reading in this phase: Yb is filled after the barrier.)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) TT[(16 * R + r) * LDT + 16 * R + j] = y[r];
+        }
+      } else {
+        for (int p = wave - NB; p < Cf::NAP - NB; p += NW - NB) {
+          int R = 1, rem = p;
+          while (rem >= R) { rem -= R; ++R; }
+          const int I = rem;
+          f32x4 accA, accP;
+          const Src<OpT> sKr{Kr + 16 * R * LDK, LDK, ln}, sQr{Qr + 16 * R * LDK, LDK, ln};
+          if (R == I + 1) {
+            mma_k2<OpT>(accA, accP, 0, DK, sKr, sQr, Src<OpT>{Ki + 16 * I * LDK, LDK, ln});
+          } else {
+            mma_k2<OpT>(accA, accP, 0, DK, sKr, sQr,
+                        SrcScaled<OpT>{Ki + 16 * I * LDK, LDK, sMID + (R * NB + I) * DK, ln});
+          }
+          store_tiles(R, I, accA, accP);
+        }
       }
     }
     __syncthreads();
 
-    // ================= SD: invert the 16x16 diagonal blocks of I + L
-    // (forward substitution, one column per lane) while every thread stages
-    // beta-scaled values, transposed, for U~ = Y Diag(beta) V.
+    // ================= SO: stage beta V (transposed) for U~, then the
+    // off-diagonal blocks of Y, one block row per barrier:
+    //   Y_RI = -Y_RR * sum_{J=I}^{R-1} L_RJ Y_JI
+    // L stays in TT; off-diagonal Y goes to YF (fp32) and to Yb.
 #pragma unroll
-    for (int it = 0; it < Cf::NVT; ++it) {
+    for (int it = 0; it < (kPrep ? 0 : Cf::NVT); ++it) {
       const int item = tid + NTH * it;
       if (Cf::NVI % NTH == 0 || item < Cf::NVI) {
         const int J = item / (DVT / 2), cc = 2 * (item % (DVT / 2));
@@ -734,6 +843,43 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       }
     }
     if (more) fetch_values(t0 + C);
+    // diagonal blocks of Y into the operand-type copy
+    for (int x = tid; x < NB * 256; x += NTH) {
+      const int R = x / 256, r = (x % 256) / 16, j = x % 16;
+      Yb[(16 * R + r) * LDC + 16 * R + j] = Ty<OpT>::from_f32(TT[(16 * R + r) * LDT + 16 * R + j]);
+    }
+    for (int R = 1; R < NB; ++R) {
+      const Lane ln = lane_now();
+      for (int I = wave; I < R; I += NW) {
+        f32x4 z = zero4();
+        for (int J = I; J < R; ++J) {
+          const float* yj = (J == I) ? TT + 16 * I * LDT + 16 * I : YF + yf_block(J, I) * 16 * LDZ;
+          const int ldy = (J == I) ? LDT : LDZ;
+          mma_f32(z, 0, 16, Src<float>{TT + 16 * R * LDT + 16 * J, LDT, ln},
+                  SrcColF32{yj, ldy, ln});
+        }
+        float* zb = ZB + I * 16 * LDZ;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) zb[(4 * ln.g + rr) * LDZ + ln.i] = z[rr];
+        wave_fence();
+        f32x4 y = zero4();
+        mma_f32(y, 0, 16, Src<float>{TT + 16 * R * LDT + 16 * R, LDT, ln}, SrcColF32{zb, LDZ, ln});
+        float* yf = YF + yf_block(R, I) * 16 * LDZ;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int rl = 4 * ln.g + rr;
+          yf[rl * LDZ + ln.i] = -y[rr];
+          Yb[(16 * R + rl) * LDC + 16 * I + ln.i] = Ty<OpT>::from_f32(-y[rr]);
+        }
+      }
+      __syncthreads();
+    }
+    if (NB == 1) __syncthreads();
+
+    // Y as a matrix-core operand (a copy in the operand type).
+    auto ysrc = [&](int R, const Lane& ln) { return Src<OpT>{Yb + 16 * R * LDC, LDC, ln}; };
+
+    // ================= WU: W = Y (beta K E) (stored row-major) and U~ = Y (beta V)
     // Q E = Q F * (decay of the blocks before), in place: P is done with Q F.
     for (int x = tid; x < C * DK / 2; x += NTH) {
       const int r = x / (DK / 2), c = 2 * (x % (DK / 2));
@@ -742,63 +888,6 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       const PT v = *qp;
       *qp = Pair<OpT>::pack(Pair<OpT>::get(v, 0) * pr[0], Pair<OpT>::get(v, 1) * pr[1]);
     }
-    {
-      const Lane ln = lane_now();
-      const int R = 4 * wave + ln.g;   // lane group -> diagonal block
-      if (R < NB) {
-        const int j = ln.i;
-        const float* Lb = TT + 16 * R * LDT + 16 * R;
-        float y[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float s = 0.f;
-#pragma unroll
-          for (int m = 0; m < r; ++m) s += Lb[r * LDT + m] * y[m];
-          y[r] = (r < j) ? 0.f : ((r == j) ? 1.f : -s);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          TT[(16 * R + r) * LDT + 16 * R + j] = y[r];
-          if constexpr (kBF) Yb[(16 * R + r) * LDC + 16 * R + j] = Ty<OpT>::from_f32(y[r]);
-        }
-      }
-    }
-    __syncthreads();
-
-    // ================= SO: off-diagonal blocks of Y, one block row at a time
-    //   Y_RI = -Y_RR * sum_{J=I}^{R-1} L_RJ Y_JI
-    for (int R = 1; R < NB; ++R) {
-      const Lane ln = lane_now();
-      for (int I = wave; I < R; I += NW) {
-        f32x4 z = zero4();
-        for (int J = I; J < R; ++J)
-          mma_f32(z, 0, 16, Src<float>{TT + 16 * R * LDT + 16 * J, LDT, ln},
-                  SrcColF32{TT + 16 * J * LDT + 16 * I, LDT, ln});
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) ZB[(I * 16 + 4 * ln.g + rr) * LDZ + ln.i] = z[rr];
-      }
-      __syncthreads();
-      for (int I = wave; I < R; I += NW) {
-        f32x4 y = zero4();
-        mma_f32(y, 0, 16, Src<float>{TT + 16 * R * LDT + 16 * R, LDT, ln},
-                SrcColF32{ZB + I * 16 * LDZ, LDZ, ln});
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int r = 16 * R + 4 * ln.g + rr, i = 16 * I + ln.i;
-          TT[r * LDT + i] = -y[rr];
-          if constexpr (kBF) Yb[r * LDC + i] = Ty<OpT>::from_f32(-y[rr]);
-        }
-      }
-      __syncthreads();
-    }
-
-    // Y as a matrix-core operand: the bf16 copy, or the fp32 original.
-    auto ysrc = [&](int R, const Lane& ln) {
-      if constexpr (kBF) return Src<OpT>{Yb + 16 * R * LDC, LDC, ln};
-      else return Src<OpT>{TT + 16 * R * LDT, LDT, ln};
-    };
-
-    // ================= WU: W = Y (beta K E) (stored row-major) and U~ = Y (beta V)
     f32x4 Ureg[UM::RA][UM::CA];
     {
       const Lane ln = lane_now();
@@ -819,7 +908,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         }
       }
 #pragma unroll
-      for (int a = 0; a < UM::RA; ++a) {
+      for (int a = 0; a < (kPrep ? 0 : UM::RA); ++a) {
 #pragma unroll
         for (int bb = 0; bb < UM::CA; ++bb) Ureg[a][bb] = zero4();
         if (UM::active(wave)) {
@@ -830,6 +919,20 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       }
     }
     __syncthreads();
+
+    if constexpr (kPrep) {
+      // chunk record -> workspace, 16-byte vectors
+      using RC = RecCfg<OpT, DK, C>;
+      char* rec = gws + (static_cast<size_t>(chain) * NC + ch) * RC::kBytes;
+      E* rw = reinterpret_cast<E*>(rec);
+      copy_rows<E>(rw + RC::kW, Wm, C, DK, LDK, tid, NTH);
+      copy_rows<E>(rw + RC::kQ, Qr, C, DK, LDK, tid, NTH);
+      copy_rows<E>(rw + RC::kKG, KgT, DK, C, LDC, tid, NTH);
+      copy_rows<E>(rw + RC::kP, PP, C, C, LDC, tid, NTH);
+      copy_rows<E>(rw + RC::kY, Yb, C, C, LDC, tid, NTH);
+      copy_rows<float>(reinterpret_cast<float*>(rec + RC::kGcByte), sGC, 1, DK, DK, tid, NTH);
+      continue;
+    }
 
     // ================= scan: U = U~ - W S,  O = (Q E) S + P U,  S update
     if (SM::active(wave)) {
@@ -928,7 +1031,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     }
   }
 
-  if (gST != nullptr && SM::active(wave)) {
+  if (!kPrep && gST != nullptr && SM::active(wave)) {
     const Lane ln = lane_now();
 #pragma unroll
     for (int a = 0; a < SM::RA; ++a)
@@ -950,10 +1053,10 @@ hipError_t launch_one(const PrefillArgs& a) {
   using E = typename Ty<OpT>::Elem;
   const long chains = static_cast<long>(a.B) * a.H;
   dim3 grid(static_cast<unsigned>(chains * (a.dv / DVT)));
-  hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT>), grid, dim3(256), 0,
+  hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT>), grid, dim3(PCfg<OpT, DK, C, DVT>::NTH), 0,
                      static_cast<hipStream_t>(a.stream), static_cast<const E*>(a.q),
                      static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.alpha, a.beta,
-                     a.S0, static_cast<E*>(a.o), a.S_T, a.B, a.T, a.H, a.dv);
+                     a.S0, static_cast<E*>(a.o), a.S_T, a.B, a.T, a.H, a.dv, nullptr);
   return hipGetLastError();
 }
 
@@ -990,45 +1093,5 @@ hipError_t launch_c(const PrefillArgs& a) {
   }
   return hipErrorInvalidValue;
 }
-
-template <typename OpT, int DK>
-hipError_t launch_dk(const PrefillArgs& a) {
-  switch (a.C) {
-    case 16: return launch_c<OpT, DK, 16>(a);
-    case 32: return launch_c<OpT, DK, 32>(a);
-    case 64: return launch_c<OpT, DK, 64>(a);
-  }
-  return hipErrorInvalidValue;
-}
-
-template <typename OpT, int DK>
-bool supported_dk(int dv, int C) {
-  switch (C) {
-    case 16: return pick_dvt<OpT, DK, 16>(1 << 20, dv) > 0;
-    case 32: return pick_dvt<OpT, DK, 32>(1 << 20, dv) > 0;
-    case 64: return pick_dvt<OpT, DK, 64>(1 << 20, dv) > 0;
-  }
-  return false;
-}
-
-// One translation unit per (element type, dk) instantiates these.
-#define KDA_PREFILL_INSTANCE(OPT, NAME, DK)                                        \
-  hipError_t launch_prefill_##NAME##_##DK(const PrefillArgs& a) {                   \
-    return launch_dk<OPT, DK>(a);                                                   \
-  }                                                                                 \
-  bool prefill_supported_##NAME##_##DK(int dv, int C) { return supported_dk<OPT, DK>(dv, C); }
-
-#define KDA_PREFILL_DECLARE(NAME, DK)                                               \
-  hipError_t launch_prefill_##NAME##_##DK(const PrefillArgs& a);                    \
-  bool prefill_supported_##NAME##_##DK(int dv, int C);
-
-KDA_PREFILL_DECLARE(bf16, 16)
-KDA_PREFILL_DECLARE(bf16, 32)
-KDA_PREFILL_DECLARE(bf16, 64)
-KDA_PREFILL_DECLARE(bf16, 128)
-KDA_PREFILL_DECLARE(f32, 16)
-KDA_PREFILL_DECLARE(f32, 32)
-KDA_PREFILL_DECLARE(f32, 64)
-KDA_PREFILL_DECLARE(f32, 128)
 
 }  // namespace kda

@@ -58,7 +58,7 @@ def addr(i):
 def prefill(lib, **kw):
     a = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), S0=addr(5),
              o=addr(6), S_T=addr(7), B=1, T=64, H=2, dk=128, dv=128, C=64, dt=1,
-             ws=None, wsb=0, stream=None)
+             ws=addr(8), wsb=1 << 34, stream=None)
     a.update(kw)
     return lib.kda_prefill_chunked(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"],
                                    a["o"], a["S_T"], a["B"], a["T"], a["H"], a["dk"], a["dv"],
@@ -117,11 +117,29 @@ def test_decode_validation_errors():
     assert decode(lib, S_out=addr(7)) in (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
 
 
+def test_prefill_workspace_errors():
+    L = _lib()
+    lib = L.load()
+    # few chains take the split path, which needs the workspace
+    assert prefill(lib, ws=None) == L.KDA_ERR_WORKSPACE
+    need = lib.kda_prefill_workspace_bytes(1, 64, 2, 128, 128, 64, 1)
+    assert need > 0
+    assert prefill(lib, wsb=need - 1) == L.KDA_ERR_WORKSPACE
+    assert prefill(lib, ws=addr(8) + 8) == L.KDA_ERR_ALIGN
+    assert prefill(lib, ws=addr(2)) == L.KDA_ERR_ALIAS              # workspace on top of v
+    assert prefill(lib, wsb=need) in (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+
+
 def test_workspace_query():
     L = _lib()
     lib = L.load()
     bad = (1 << 64) - 1
-    assert lib.kda_prefill_workspace_bytes(1, 4096, 16, 128, 128, 64, 1) == 0
-    assert lib.kda_prefill_workspace_bytes(1, 256, 1, 16, 16, 16, 0) == 0
+    # one record per chunk: W, Q.E, (K.E')^T [C x dk each], P, Y [C x C], decay [dk] fp32
+    rec = (3 * 64 * 128 + 2 * 64 * 64) * 2 + 4 * 128
+    rec = (rec + 255) // 256 * 256
+    assert lib.kda_prefill_workspace_bytes(1, 4096, 16, 128, 128, 64, 1) == 16 * 64 * rec
+    assert lib.kda_prefill_workspace_bytes(8, 8192, 32, 128, 128, 64, 1) == 0   # fused path
+    rec16 = ((3 * 16 * 16 + 2 * 16 * 16) * 4 + 4 * 16 + 255) // 256 * 256
+    assert lib.kda_prefill_workspace_bytes(1, 256, 1, 16, 16, 16, 0) == 16 * rec16
     assert lib.kda_prefill_workspace_bytes(1, 256, 1, 16, 16, 12, 0) == bad
     assert lib.kda_prefill_workspace_bytes(0, 256, 1, 16, 16, 16, 0) == bad

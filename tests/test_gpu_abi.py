@@ -21,11 +21,22 @@ def bufs(B=1, T=64, H=2, dk=128, dv=128, dt=torch.bfloat16):
                 S_T=z(B, H, dk, dv, d=torch.float32))
 
 
-def call(b, B=1, T=64, H=2, dk=128, dv=128, C=64, dt=1, **ov):
+def workspace(B=1, T=64, H=2, dk=128, dv=128, C=64, dt=1):
+    n = L().load().kda_prefill_workspace_bytes(B, T, H, dk, dv, C, dt)
+    if n == (1 << 64) - 1:        # unsupported sizes: the call itself reports it
+        n = 0
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=DEV), n
+
+
+def call(b, B=1, T=64, H=2, dk=128, dv=128, C=64, dt=1, ws=None, **ov):
     p = {k: t.data_ptr() for k, t in b.items()}
     p.update(ov)
+    if ws is None:
+        ws = workspace(B, T, H, dk, dv, C, dt)
+    buf, n = ws
+    wsp = p.pop("ws_ptr", buf.data_ptr())
     return L().load().kda_prefill_chunked(p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["S0"],
-                                          p["o"], p["S_T"], B, T, H, dk, dv, C, dt, None, 0,
+                                          p["o"], p["S_T"], B, T, H, dk, dv, C, dt, wsp, n,
                                           torch.cuda.current_stream().cuda_stream)
 
 
@@ -42,6 +53,11 @@ def test_prefill_status_codes():
     assert call(b, k=b["k"].data_ptr() + 2) == lib.KDA_ERR_ALIGN
     assert call(b, o=b["v"].data_ptr()) == lib.KDA_ERR_ALIAS
     assert call(b, S_T=b["S0"].data_ptr() + 1024) == lib.KDA_ERR_ALIAS
+    buf, n = workspace()
+    assert n > 0                                                 # 2 chains: split path
+    assert call(b, ws=(buf, n - 1)) == lib.KDA_ERR_WORKSPACE
+    assert call(b, ws_ptr=None) == lib.KDA_ERR_WORKSPACE
+    assert call(b, ws_ptr=b["v"].data_ptr()) == lib.KDA_ERR_ALIAS
     torch.cuda.synchronize()
 
 

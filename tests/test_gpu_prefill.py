@@ -176,6 +176,26 @@ def test_zero_and_extreme_gates(dtype):
     check(dict(q=q, k=k, v=v, alpha=alpha, beta=beta, S0=S0), C, label="zero gates")
 
 
+@pytest.mark.parametrize("C", [16, 32, 64])
+def test_split_and_fused_paths_agree(C):
+    """Few chains take the split path (chunk-parallel prep + scan, with a
+    workspace); 128 or more take the fused kernel.  The same 4 chains, run
+    alone and inside a batch of 128 chains, both match the oracle."""
+    spec = wl.PREFILL["prefill_h16_t4k"]
+    big = wl.make_prefill_inputs(spec, T=160, B=32, H=4)
+    big["S0"] = 0.05 * torch.randn(32, 4, 128, 128, generator=torch.Generator().manual_seed(C))
+    ws_few = kda().prefill_workspace_bytes(1, 160, 4, 128, 128, C)
+    ws_many = kda().prefill_workspace_bytes(32, 160, 4, 128, 128, C)
+    assert ws_few > 0 and ws_many == 0
+    o_big, S_big = run(big, C)
+    few = {k: (v[3:4].contiguous() if v is not None else v) for k, v in big.items()}
+    o_few, S_few = run(few, C)
+    o_ref, S_ref = oracle(few)
+    for o, S in ((o_big[3:4], S_big[3:4]), (o_few, S_few)):
+        assert rel(f64(o), o_ref) < 2e-2 and rel(f64(S), S_ref) < 2e-2
+    assert rel(f64(o_big[3:4]), f64(o_few)) < 1e-2
+
+
 def test_split_resume_and_in_place_state():
     spec = wl.PREFILL["prefill_h16_t4k"]
     inp = wl.make_prefill_inputs(spec, T=300, H=2)
