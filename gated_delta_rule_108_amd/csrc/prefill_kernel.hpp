@@ -347,46 +347,87 @@ struct TileMap {
 };
 
 // ----------------------------------------------------------------------------
-// Workspace record of one chunk (written by the prep kernel, read by the scan
-// kernel), elements of the operand type unless noted:
-//   W [C][DK] | Q.E [C][DK] | (K.E')^T [DK][C] | P [C][C] | Y [C][C] |
-//   chunk decay E_{C-1} [DK] float32
+// Workspace record of one chunk, written by the prep kernel and read by the
+// scan kernel.  Matrices are stored as matrix-core operand packets so that a
+// wave loads each fragment with one contiguous access (64 lanes x n elements):
+//   A packet (16-row block b, K step s of width KS): lane l holds row
+//   16b + l%16, columns s*KS + (KS/4)*(l/16) .. + KS/4 - 1.
+//   Accumulator packet (row block R, column tile j): lane l holds rows
+//   16R + 4(l/16) .. + 3 of column 16j + l%16.
+// Layout (elements of the operand type unless noted):
+//   W [C x DK] A packets (KS = KSD) | Q.E [C x DK] (KSD) | (K.E')^T [DK x C] (KSC) |
+//   P [C x C] (KSC) | decay E_{C-1} [DK] fp32 | U~ = Y Diag(beta) V [C x dv] accumulator packets
+// KSD / KSC: the widest matrix-core K step that divides DK / C.
 // ----------------------------------------------------------------------------
+template <typename OpT, int K>
+__host__ __device__ constexpr int kstep() {
+  return Ty<OpT>::kBytes == 2 ? (K % 32 == 0 ? 32 : 16) : 4;
+}
+
 template <typename OpT, int DK, int C>
 struct RecCfg {
   static constexpr int EB = Ty<OpT>::kBytes;
+  static constexpr int KSD = kstep<OpT, DK>(), KSC = kstep<OpT, C>();
+  static constexpr int NKD = DK / KSD, NKC = C / KSC;
   static constexpr size_t kW = 0;
   static constexpr size_t kQ = static_cast<size_t>(C) * DK;
   static constexpr size_t kKG = 2 * static_cast<size_t>(C) * DK;
   static constexpr size_t kP = 3 * static_cast<size_t>(C) * DK;
-  static constexpr size_t kY = kP + static_cast<size_t>(C) * C;
-  static constexpr size_t kElems = kY + static_cast<size_t>(C) * C;
-  static constexpr size_t kGcByte = kElems * EB;
-  static constexpr size_t kBytes = (kGcByte + 4 * DK + 255) / 256 * 256;
+  static constexpr size_t kGcByte = (kP + static_cast<size_t>(C) * C) * EB;
+  static constexpr size_t kUByte = kGcByte + 4 * DK;
+  __host__ __device__ static constexpr size_t bytes(int dv) {
+    return (kUByte + static_cast<size_t>(C) * dv * EB + 255) / 256 * 256;
+  }
 };
 
-// rows x n elements between a dense array (row length n) and a padded LDS
-// array (row length ld), 16-byte vectors; n * sizeof(T) is a multiple of 16.
-template <typename T>
-__device__ __forceinline__ void copy_rows(T* dense, const T* padded, int rows, int n, int ld,
-                                          int tid, int nth) {
-  const int vpr = n * static_cast<int>(sizeof(T)) / 16, epv = 16 / static_cast<int>(sizeof(T));
-  for (int x = tid; x < rows * vpr; x += nth) {
-    const int r = x / vpr, cv = x % vpr;
-    *reinterpret_cast<uint4*>(dense + static_cast<size_t>(r) * n + cv * epv) =
-        *reinterpret_cast<const uint4*>(padded + r * ld + cv * epv);
+// Padded LDS matrix (row stride ld) -> A packets of width KS, 16-byte (or
+// smaller) vectors; `blocks` 16-row blocks, `nks` K steps.
+template <typename OpT, int KS>
+__device__ __forceinline__ void copy_packets(typename Ty<OpT>::Elem* dst,
+                                             const typename Ty<OpT>::Elem* src, int blocks,
+                                             int nks, int ld, int tid, int nth) {
+  using F = Frag<OpT, KS>;
+  using V = typename F::T;
+  for (int x = tid; x < blocks * nks * 64; x += nth) {
+    const int l = x % 64, bs = x / 64, blk = bs / nks, s = bs % nks;
+    const typename Ty<OpT>::Elem* a = src + (16 * blk + l % 16) * ld + s * KS + F::N * (l / 16);
+    *reinterpret_cast<V*>(dst + static_cast<size_t>(x) * F::N) = *reinterpret_cast<const V*>(a);
   }
 }
-template <typename T>
-__device__ __forceinline__ void copy_rows_in(T* padded, const T* dense, int rows, int n, int ld,
-                                             int tid, int nth) {
-  const int vpr = n * static_cast<int>(sizeof(T)) / 16, epv = 16 / static_cast<int>(sizeof(T));
-  for (int x = tid; x < rows * vpr; x += nth) {
-    const int r = x / vpr, cv = x % vpr;
-    *reinterpret_cast<uint4*>(padded + r * ld + cv * epv) =
-        *reinterpret_cast<const uint4*>(dense + static_cast<size_t>(r) * n + cv * epv);
+
+// Four accumulator values of one lane in the operand type.
+template <typename OpT> struct Acc4;
+template <> struct Acc4<bf16_t> {
+  using Raw = uint2;
+  __device__ __forceinline__ static void store(uint16_t* p, const f32x4& v) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
   }
-}
+  __device__ __forceinline__ static Raw load(const uint16_t* p) {
+    return *reinterpret_cast<const uint2*>(p);
+  }
+  __device__ __forceinline__ static f32x4 cvt(Raw r) {
+    f32x4 v;
+    v[0] = bf16_to_f32(static_cast<uint16_t>(r.x & 0xffffu));
+    v[1] = bf16_to_f32(static_cast<uint16_t>(r.x >> 16));
+    v[2] = bf16_to_f32(static_cast<uint16_t>(r.y & 0xffffu));
+    v[3] = bf16_to_f32(static_cast<uint16_t>(r.y >> 16));
+    return v;
+  }
+};
+template <> struct Acc4<float> {
+  using Raw = float4;
+  __device__ __forceinline__ static void store(float* p, const f32x4& v) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  __device__ __forceinline__ static Raw load(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+  }
+  __device__ __forceinline__ static f32x4 cvt(Raw r) {
+    f32x4 v;
+    v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+    return v;
+  }
+};
 
 // ----------------------------------------------------------------------------
 // LDS plan (element counts; every region 16-byte aligned).
@@ -455,9 +496,9 @@ struct PCfg {
 constexpr int kMaxLds = 160 * 1024;
 
 // kPrep = false: the fused prefill (all chunks of a chain, state in
-// registers).  kPrep = true: one workgroup per chunk computes only the
-// column-free chunk quantities and writes them to the workspace record of
-// that chunk (W, Q.E, (K.E')^T, P, Y, chunk decay) for the scan kernel.
+// registers).  kPrep = true: one workgroup per chunk (DVT = dv) computes the
+// state-free chunk quantities and writes them to the workspace record of that
+// chunk (W, Q.E, (K.E')^T, P, chunk decay, U~) for the scan kernel.
 template <typename OpT, int DK, int C, int DVT, bool kPrep = false>
 __global__ void __launch_bounds__(512)
 kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
@@ -606,7 +647,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
 
   if (ch_begin < ch_end) {
     fetch_gates(ch_begin * C);
-    if constexpr (!kPrep) fetch_values(0);
+    fetch_values(ch_begin * C);
     fetch_beta(ch_begin * C);
   }
   for (int ch = ch_begin; ch < ch_end; ++ch) {
@@ -640,7 +681,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       }
     }
 #pragma unroll
-    for (int it = 0; it < (kPrep ? 0 : Cf::NVT); ++it) {
+    for (int it = 0; it < Cf::NVT; ++it) {
       const int item = tid + NTH * it;
       if (Cf::NVI % NTH == 0 || item < Cf::NVI) {
         const int J = item / (DVT / 2);
@@ -827,7 +868,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     //   Y_RI = -Y_RR * sum_{J=I}^{R-1} L_RJ Y_JI
     // L stays in TT; off-diagonal Y goes to YF (fp32) and to Yb.
 #pragma unroll
-    for (int it = 0; it < (kPrep ? 0 : Cf::NVT); ++it) {
+    for (int it = 0; it < Cf::NVT; ++it) {
       const int item = tid + NTH * it;
       if (Cf::NVI % NTH == 0 || item < Cf::NVI) {
         const int J = item / (DVT / 2), cc = 2 * (item % (DVT / 2));
@@ -908,7 +949,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         }
       }
 #pragma unroll
-      for (int a = 0; a < (kPrep ? 0 : UM::RA); ++a) {
+      for (int a = 0; a < UM::RA; ++a) {
 #pragma unroll
         for (int bb = 0; bb < UM::CA; ++bb) Ureg[a][bb] = zero4();
         if (UM::active(wave)) {
@@ -921,16 +962,27 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     __syncthreads();
 
     if constexpr (kPrep) {
-      // chunk record -> workspace, 16-byte vectors
+      // chunk record -> workspace: operand packets, decay, U~ (this slab is all of dv)
       using RC = RecCfg<OpT, DK, C>;
-      char* rec = gws + (static_cast<size_t>(chain) * NC + ch) * RC::kBytes;
+      char* rec = gws + (static_cast<size_t>(chain) * NC + ch) * RC::bytes(DV);
       E* rw = reinterpret_cast<E*>(rec);
-      copy_rows<E>(rw + RC::kW, Wm, C, DK, LDK, tid, NTH);
-      copy_rows<E>(rw + RC::kQ, Qr, C, DK, LDK, tid, NTH);
-      copy_rows<E>(rw + RC::kKG, KgT, DK, C, LDC, tid, NTH);
-      copy_rows<E>(rw + RC::kP, PP, C, C, LDC, tid, NTH);
-      copy_rows<E>(rw + RC::kY, Yb, C, C, LDC, tid, NTH);
-      copy_rows<float>(reinterpret_cast<float*>(rec + RC::kGcByte), sGC, 1, DK, DK, tid, NTH);
+      copy_packets<OpT, RC::KSD>(rw + RC::kW, Wm, NB, RC::NKD, LDK, tid, NTH);
+      copy_packets<OpT, RC::KSD>(rw + RC::kQ, Qr, NB, RC::NKD, LDK, tid, NTH);
+      copy_packets<OpT, RC::KSC>(rw + RC::kKG, KgT, Cf::NCB, RC::NKC, LDC, tid, NTH);
+      copy_packets<OpT, RC::KSC>(rw + RC::kP, PP, NB, RC::NKC, LDC, tid, NTH);
+      if (tid < DK / 4)
+        reinterpret_cast<float4*>(rec + RC::kGcByte)[tid] = reinterpret_cast<const float4*>(sGC)[tid];
+      if (UM::active(wave)) {
+        const int lane = tid % kWave;
+        E* ru = reinterpret_cast<E*>(rec + RC::kUByte);
+#pragma unroll
+        for (int a = 0; a < UM::RA; ++a)
+#pragma unroll
+          for (int bb = 0; bb < UM::CA; ++bb) {
+            const int R = UM::row0(wave) + a, Jb = UM::col0(wave) + bb;
+            Acc4<OpT>::store(ru + (static_cast<size_t>(R * NJ + Jb) * kWave + lane) * 4, Ureg[a][bb]);
+          }
+      }
       continue;
     }
 

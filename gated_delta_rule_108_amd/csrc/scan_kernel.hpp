@@ -1,315 +1,273 @@
 // KDA chunk scan: the sequential half of the split prefill.
 //
 // The prep kernel (kda_prefill_kernel<..., kPrep = true>) has already written,
-// for every chunk of every chain, the column-free chunk quantities
-//   W = Y Diag(beta)(K.E),  Q.E,  (K.E')^T,  P (gated Q K^T, lower),  Y,
-//   and the chunk decay E_{C-1}
-// to a workspace record (RecCfg).  This kernel walks the chunks of one chain
-// in order.  Each computing wave owns a 16-column tile of the state and does
-// all of its column work alone:
-//   U~ = Y Diag(beta) V,  U = U~ - W S,  O = (Q.E) S + P U,
-//   S <- Diag(E_{C-1}) S + (K.E')^T U
+// for every chunk of every chain, the state-free chunk quantities
+//   W = Y Diag(beta)(K.E),  Q.E,  (K.E')^T,  P (gated Q K^T, lower),
+//   the chunk decay E_{C-1},  U~ = Y Diag(beta) V
+// to a workspace record (RecCfg), as matrix-core operand packets.  This
+// kernel walks the chunks of one chain in order for one 16-column tile of the
+// state:
+//   U = U~ - W S,  O = (Q.E) S + P U,  S <- Diag(E_{C-1}) S + (K.E')^T U
 // (the chunk algebra of "From GPT-2 to Kimi K3, Explained", section "DeltaNet
 // (Parallelizing Linear Transformers with Delta Rule)", with the per-channel
-// decay of section "KDA/Kimi Linear").  The only data the waves share, the
-// chunk record, is staged in LDS once per chunk, and the next chunk's record
-// is fetched into registers while the current one is consumed; a chunk costs
-// two workgroup barriers.
+// decay of section "KDA/Kimi Linear").
+//
+// A workgroup has one wave per 16-row block R of the chunk.  Wave R computes
+// rows R of U and O and owns state row blocks R, R + C/16, ...; the state
+// tile (S^T) and U^T are exchanged through LDS, two LDS-only barriers per
+// chunk.  Every record operand goes straight from global memory into the
+// registers of the wave that uses it, one chunk ahead, so the chain of
+// dependent work per chunk is a handful of short MFMA chains.
 #pragma once
 
 #include "prefill_kernel.hpp"
 
 namespace kda {
 
-template <typename OpT, int DK, int C, int NJ>
+template <typename OpT, int DK, int C>
 struct SCfg {
-  static constexpr int NTH = 512, NW = 8;
-  static_assert(NJ >= 1 && NJ <= NW, "computing waves");
   static constexpr int NB = C / 16, NCB = DK / 16;
+  static constexpr int NTH = kWave * NB;
+  static constexpr int CPW = (NCB + NB - 1) / NB;    // state row blocks per wave
   static constexpr int EB = Ty<OpT>::kBytes, PADE = 16 / EB;
   static constexpr int LDK = DK + PADE, LDC = C + PADE;
-  static constexpr int kW = align16(C * LDK * EB);
-  static constexpr int kKG = align16(DK * LDC * EB);
-  static constexpr int kP = align16(C * LDC * EB);
-  static constexpr int oW = 0, oQ = kW, oKG = oQ + kW, oP = oKG + kKG, oY = oP + kP;
-  static constexpr int oGC = oY + kP;
-  static constexpr int oBE = oGC + align16(DK * 4);
-  static constexpr int oWV = oBE + align16(C * 4);
-  static constexpr int kST = align16(16 * LDK * EB), kUT = align16(16 * LDC * EB);
-  static constexpr int kPW = kST + 2 * kUT;          // per wave: S^T, U^T, (beta V)^T
-  static constexpr int kLds = oWV + NJ * kPW;
   using RC = RecCfg<OpT, DK, C>;
-  // the record as 16-byte vectors, and its segments
-  static constexpr int vK = DK * EB / 16, vC = C * EB / 16;
-  static constexpr int nW = C * vK, nKG = DK * vC, nP = C * vC, nGC = DK * 4 / 16;
-  static constexpr int NVEC = 2 * nW + nKG + 2 * nP + nGC;
-  static constexpr int NPV = (NVEC + NTH - 1) / NTH;
-  // the wave's value tile, C rows x 16 columns, as 16-byte vectors
-  static constexpr int VPR = 16 * EB / 16;           // vectors per value row
-  static constexpr int NVV = C * VPR;
-  static constexpr int NVL = (NVV + kWave - 1) / kWave;
+  static constexpr int KSD = RC::KSD, KSC = RC::KSC, NKD = RC::NKD, NKC = RC::NKC;
 };
 
-// LDS byte offset of record vector x (row padding applied per segment).
-template <class Cf>
-__device__ __forceinline__ int rec_vec_lds(int x) {
-  constexpr int EB = Cf::EB;
-  if (x < Cf::nW) return Cf::oW + (x / Cf::vK) * Cf::LDK * EB + (x % Cf::vK) * 16;
-  x -= Cf::nW;
-  if (x < Cf::nW) return Cf::oQ + (x / Cf::vK) * Cf::LDK * EB + (x % Cf::vK) * 16;
-  x -= Cf::nW;
-  if (x < Cf::nKG) return Cf::oKG + (x / Cf::vC) * Cf::LDC * EB + (x % Cf::vC) * 16;
-  x -= Cf::nKG;
-  if (x < Cf::nP) return Cf::oP + (x / Cf::vC) * Cf::LDC * EB + (x % Cf::vC) * 16;
-  x -= Cf::nP;
-  if (x < Cf::nP) return Cf::oY + (x / Cf::vC) * Cf::LDC * EB + (x % Cf::vC) * 16;
-  x -= Cf::nP;
-  return Cf::oGC + x * 16;
+// Orders LDS accesses across the workgroup without waiting for outstanding
+// global loads or stores (a plain __syncthreads() would drain both).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// One chunk's record operands for wave R.
+template <typename OpT, int DK, int C>
+struct ScanOps {
+  using Cf = SCfg<OpT, DK, C>;
+  using FD = typename Frag<OpT, Cf::KSD>::T;
+  using FC = typename Frag<OpT, Cf::KSC>::T;
+  FD w[Cf::NKD], q[Cf::NKD];
+  FC p[Cf::NKC];
+  FC kg[Cf::CPW][Cf::NKC];
+  typename Acc4<OpT>::Raw ut;
+  float4 gc[Cf::CPW];
+};
 
-// Element q of a 16-byte vector holding 16 / sizeof(E) values.
-template <typename OpT>
-__device__ __forceinline__ float vec_elem(const u32x4& v, int q) {
-  if constexpr (Ty<OpT>::kBytes == 2)
-    return bf16_to_f32(static_cast<uint16_t>((v[q >> 1] >> (16 * (q & 1))) & 0xffffu));
-  else
-    return __uint_as_float(v[q]);
-}
-
-template <typename OpT, int DK, int C, int NJ>
-__global__ void __launch_bounds__(512)
-kda_scan_kernel(const typename Ty<OpT>::Elem* __restrict__ gv, const float* __restrict__ gbeta,
-                const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float* gST,
+template <typename OpT, int DK, int C>
+__global__ void __launch_bounds__(kWave * (C / 16))
+kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float* gST,
                 const char* __restrict__ gws, int B, int T, int H, int DV) {
-  using Cf = SCfg<OpT, DK, C, NJ>;
+  using Cf = SCfg<OpT, DK, C>;
   using RC = typename Cf::RC;
   using E = typename Ty<OpT>::Elem;
-  constexpr int NB = Cf::NB, NCB = Cf::NCB, NTH = Cf::NTH;
-  constexpr int LDK = Cf::LDK, LDC = Cf::LDC, EB = Cf::EB;
-  static_assert(Cf::kLds <= kMaxLds, "scan LDS plan exceeds 160 KiB");
+  using Ops = ScanOps<OpT, DK, C>;
+  constexpr int NB = Cf::NB, NCB = Cf::NCB, CPW = Cf::CPW, LDK = Cf::LDK, LDC = Cf::LDC;
+  constexpr int KSD = Cf::KSD, KSC = Cf::KSC, NKD = Cf::NKD, NKC = Cf::NKC;
+  constexpr int ND = KSD / 4, NCK = KSC / 4;   // elements per lane of one packet
 
-  __shared__ __attribute__((aligned(16))) char smem[Cf::kLds];
-  const E* Wm = reinterpret_cast<const E*>(smem + Cf::oW);
-  const E* Qg = reinterpret_cast<const E*>(smem + Cf::oQ);
-  const E* KgT = reinterpret_cast<const E*>(smem + Cf::oKG);
-  const E* PP = reinterpret_cast<const E*>(smem + Cf::oP);
-  const E* Yb = reinterpret_cast<const E*>(smem + Cf::oY);
-  const float* sGC = reinterpret_cast<const float*>(smem + Cf::oGC);
+  __shared__ __attribute__((aligned(16))) E ST[16 * LDK];   // S^T of the tile
+  __shared__ __attribute__((aligned(16))) E UT[16 * LDC];   // U^T of the tile
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int lane = tid % kWave;
-  const bool comp = wave < NJ;
+  const int lane = threadIdx.x % kWave;
+  const int R = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
-  // Workgroup -> (chain, slab of 16*NJ columns), all slabs of a chain on one XCD.
-  const int ntiles = DV / (16 * NJ);
+  // Workgroup -> (chain, column tile); all tiles of a chain on one XCD so the
+  // chain's records are read from HBM once and then hit that XCD's L2.
+  const int NJV = DV / 16;
   const int total = gridDim.x;
   int L = blockIdx.x;
-  if (ntiles > 1 && (total % 8) == 0) L = (blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
-  const int chain = L / ntiles;
-  const int jw = (L % ntiles) * 16 * NJ + 16 * (comp ? wave : 0);   // this wave's columns
+  if (NJV > 1 && (total % 8) == 0) L = (blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
+  const int chain = L / NJV, jt = L % NJV;
   const int b = chain / H, h = chain % H;
   const int NC = (T + C - 1) / C;
   const size_t row0 = static_cast<size_t>(b) * T * H + h;
+  const size_t rbytes = RC::bytes(DV);
+  const char* rec0 = gws + static_cast<size_t>(chain) * NC * rbytes;
 
-  E* ST = reinterpret_cast<E*>(smem + Cf::oWV + (comp ? wave : 0) * Cf::kPW);   // [16][LDK]
-  E* UT = ST + Cf::kST / EB;                                                      // [16][LDC]
-  E* VbT = UT + Cf::kUT / EB;                                                     // [16][LDC]
-  float* sBE = reinterpret_cast<float*>(smem + Cf::oBE);
-
-  // state tiles (Cb, this wave's columns) in registers
-  f32x4 S[NCB];
+  // state row blocks cb = R + NB*m of the tile, in registers
+  f32x4 S[CPW];
   {
     const Lane ln = lane_now();
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      S[cb] = zero4();
-      if (comp && gS0 != nullptr) {
-        const float* src = gS0 + static_cast<size_t>(chain) * DK * DV + jw;
+    for (int m = 0; m < CPW; ++m) {
+      const int cb = R + NB * m;
+      S[m] = zero4();
+      if (cb < NCB && gS0 != nullptr) {
+        const float* src = gS0 + static_cast<size_t>(chain) * DK * DV + 16 * jt;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[cb][r] = src[(16 * cb + 4 * ln.g + r) * DV + ln.i];
+        for (int r = 0; r < 4; ++r) S[m][r] = src[(16 * cb + 4 * ln.g + r) * DV + ln.i];
       }
     }
   }
 
-  // next chunk, fetched into registers one chunk ahead
-  u32x4 pf[Cf::NPV];
-  u32x4 pv[Cf::NVL];
-  float pbe = 0.f;
-  const char* rec0 = gws + static_cast<size_t>(chain) * NC * RC::kBytes;
-  auto fetch = [&](int ch) {
-    const u32x4* rv = reinterpret_cast<const u32x4*>(rec0 + static_cast<size_t>(ch) * RC::kBytes);
+  auto fetch = [&](Ops& x, int ch) {
+    const char* rc = rec0 + static_cast<size_t>(ch) * rbytes;
+    const E* rw = reinterpret_cast<const E*>(rc);
+    int l = lane;
+    asm volatile("" : "+v"(l));
 #pragma unroll
-    for (int i = 0; i < Cf::NPV; ++i) {
-      const int x = tid + NTH * i;
-      if (Cf::NVEC % NTH == 0 || x < Cf::NVEC) pf[i] = rv[x];
+    for (int s = 0; s < NKD; ++s) {
+      const size_t o = (static_cast<size_t>(R * NKD + s) * kWave + l) * ND;
+      x.w[s] = *reinterpret_cast<const typename Ops::FD*>(rw + RC::kW + o);
+      x.q[s] = *reinterpret_cast<const typename Ops::FD*>(rw + RC::kQ + o);
     }
-    const int tn = ch * C;
-    if (tid < C) pbe = gbeta[row0 + static_cast<size_t>(min(tn + tid, T - 1)) * H];
-    if (comp) {
 #pragma unroll
-      for (int i = 0; i < Cf::NVL; ++i) {
-        const int v = lane + kWave * i;
-        if (Cf::NVV % kWave == 0 || v < Cf::NVV) {
-          const int r = min(tn + v / Cf::VPR, T - 1);
-          pv[i] = *reinterpret_cast<const u32x4*>(
-              gv + (row0 + static_cast<size_t>(r) * H) * DV + jw + (v % Cf::VPR) * (16 / EB));
-        }
+    for (int s = 0; s < NKC; ++s)
+      x.p[s] = *reinterpret_cast<const typename Ops::FC*>(
+          rw + RC::kP + (static_cast<size_t>(R * NKC + s) * kWave + l) * NCK);
+#pragma unroll
+    for (int m = 0; m < CPW; ++m) {
+      const int cb = R + NB * m;
+      if (cb < NCB) {
+#pragma unroll
+        for (int s = 0; s < NKC; ++s)
+          x.kg[m][s] = *reinterpret_cast<const typename Ops::FC*>(
+              rw + RC::kKG + (static_cast<size_t>(cb * NKC + s) * kWave + l) * NCK);
+        x.gc[m] = *reinterpret_cast<const float4*>(rc + RC::kGcByte + 4 * (16 * cb + 4 * (l / 16)));
       }
     }
+    x.ut = Acc4<OpT>::load(reinterpret_cast<const E*>(rc + RC::kUByte) +
+                           (static_cast<size_t>(R * NJV + jt) * kWave + l) * 4);
   };
 
-  if (NC > 0) fetch(0);
+  Ops cur, nxt;
+  if (NC > 0) fetch(nxt, 0);
+  E* po0 = go + row0 * DV + 16 * jt;
+  const int rsV = H * DV;
   for (int ch = 0; ch < NC; ++ch) {
+    cur = nxt;
+    if (ch + 1 < NC) fetch(nxt, ch + 1);
     const int t0 = ch * C;
     const int nrows = min(C, T - t0);
-    __syncthreads();   // every wave is done with the previous chunk's record
-#pragma unroll
-    for (int i = 0; i < Cf::NPV; ++i) {
-      const int x = tid + NTH * i;
-      if (Cf::NVEC % NTH == 0 || x < Cf::NVEC)
-        *reinterpret_cast<u32x4*>(smem + rec_vec_lds<Cf>(x)) = pf[i];
-    }
-    if (tid < C) sBE[tid] = (tid < nrows) ? pbe : 0.f;
-    __syncthreads();
-    if (comp) {
-      // (beta V)^T of this wave's columns, rows past T as zeros
-#pragma unroll
-      for (int i = 0; i < Cf::NVL; ++i) {
-        const int v = lane + kWave * i;
-        if (Cf::NVV % kWave == 0 || v < Cf::NVV) {
-          const int r = v / Cf::VPR, c0 = (v % Cf::VPR) * (16 / EB);
-          const float be = sBE[r];
-#pragma unroll
-          for (int q = 0; q < 16 / EB; ++q)
-            VbT[(c0 + q) * LDC + r] = Ty<OpT>::from_f32(be * vec_elem<OpT>(pv[i], q));
-        }
-      }
-    }
-    if (ch + 1 < NC) fetch(ch + 1);
-    if (comp) {
-      const Lane ln = lane_now();
-      // S^T of this wave's tile, as the B operand of the products over channels
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        E* dst = ST + ln.i * LDK + 16 * cb + 4 * ln.g;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(S[cb][rr]);
-      }
-      wave_fence();
-      // U = Y (beta V) - W S
-#pragma unroll
-      for (int R = 0; R < NB; ++R) {
-        f32x4 u = mma_k<OpT>(0, 16 * (R + 1), Src<OpT>{Yb + 16 * R * LDC, LDC, ln},
-                             Src<OpT>{VbT, LDC, ln});
-        const f32x4 x = mma_k<OpT>(0, DK, Src<OpT>{Wm + 16 * R * LDK, LDK, ln},
-                                   Src<OpT>{ST, LDK, ln});
-        E* dst = UT + ln.i * LDC + 16 * R + 4 * ln.g;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(u[rr] - x[rr]);
-      }
-      wave_fence();
-      // O = (Q E) S + P U
-      E* po = go + (row0 + static_cast<size_t>(t0) * H) * DV + jw;
-      const int rsV = H * DV;
-#pragma unroll
-      for (int R = 0; R < NB; ++R) {
-        f32x4 o = mma_k<OpT>(0, DK, Src<OpT>{Qg + 16 * R * LDK, LDK, ln}, Src<OpT>{ST, LDK, ln});
-        add4(o, mma_k<OpT>(0, 16 * (R + 1), Src<OpT>{PP + 16 * R * LDC, LDC, ln},
-                           Src<OpT>{UT, LDC, ln}));
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int rl = 16 * R + 4 * ln.g + rr;
-          if (rl < nrows) po[rl * rsV + ln.i] = Ty<OpT>::from_f32(o[rr]);
-        }
-      }
-      // S <- Diag(E_{C-1}) S + (K E')^T U
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const f32x4 acc = mma_k<OpT>(0, C, Src<OpT>{KgT + 16 * cb * LDC, LDC, ln},
-                                     Src<OpT>{UT, LDC, ln});
-        const float4 gc = *reinterpret_cast<const float4*>(sGC + 16 * cb + 4 * ln.g);
-        S[cb][0] = gc.x * S[cb][0] + acc[0];
-        S[cb][1] = gc.y * S[cb][1] + acc[1];
-        S[cb][2] = gc.z * S[cb][2] + acc[2];
-        S[cb][3] = gc.w * S[cb][3] + acc[3];
-      }
-    }
-  }
-
-  if (comp && gST != nullptr) {
     const Lane ln = lane_now();
-    float* dst = gST + static_cast<size_t>(chain) * DK * DV + jw;
+
+    // publish this wave's state rows as S^T (operand type)
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
+    for (int m = 0; m < CPW; ++m) {
+      const int cb = R + NB * m;
+      if (cb < NCB) Acc4<OpT>::store(ST + ln.i * LDK + 16 * cb + 4 * ln.g, S[m]);
+    }
+    lds_barrier();
+    typename Ops::FD stf[NKD];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(16 * cb + 4 * ln.g + r) * DV + ln.i] = S[cb][r];
+    for (int s = 0; s < NKD; ++s) stf[s] = Src<OpT>{ST, LDK, ln}.template get<KSD>(s * KSD);
+    // U_R = U~_R - W_R S  and the first half of O_R = (Q.E)_R S
+    f32x4 x = zero4(), o = zero4();
+#pragma unroll
+    for (int s = 0; s < NKD; ++s) x = mfma<OpT, KSD>(cur.w[s], stf[s], x);
+#pragma unroll
+    for (int s = 0; s < NKD; ++s) o = mfma<OpT, KSD>(cur.q[s], stf[s], o);
+    f32x4 u = Acc4<OpT>::cvt(cur.ut);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) u[r] -= x[r];
+    // U^T[n][16R + 4g + r]
+    Acc4<OpT>::store(UT + ln.i * LDC + 16 * R + 4 * ln.g, u);
+    lds_barrier();
+    typename Ops::FC utf[NKC];
+#pragma unroll
+    for (int s = 0; s < NKC; ++s) utf[s] = Src<OpT>{UT, LDC, ln}.template get<KSC>(s * KSC);
+    // O_R += P_R U  (P is block-lower; its upper blocks are zeros)
+    f32x4 pu = zero4();
+#pragma unroll
+    for (int s = 0; s < NKC; ++s) pu = mfma<OpT, KSC>(cur.p[s], utf[s], pu);
+    add4(o, pu);
+    E* po = po0 + static_cast<size_t>(t0) * rsV;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rl = 16 * R + 4 * ln.g + r;
+      if (rl < nrows) po[rl * rsV + ln.i] = Ty<OpT>::from_f32(o[r]);
+    }
+    // S <- Diag(E_{C-1}) S + (K.E')^T U  for this wave's row blocks
+#pragma unroll
+    for (int m = 0; m < CPW; ++m) {
+      const int cb = R + NB * m;
+      if (cb < NCB) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < NKC; ++s) acc = mfma<OpT, KSC>(cur.kg[m][s], utf[s], acc);
+        const float4 gc = cur.gc[m];
+        S[m][0] = gc.x * S[m][0] + acc[0];
+        S[m][1] = gc.y * S[m][1] + acc[1];
+        S[m][2] = gc.z * S[m][2] + acc[2];
+        S[m][3] = gc.w * S[m][3] + acc[3];
+      }
+    }
+  }
+
+  if (gST != nullptr) {
+    const Lane ln = lane_now();
+    float* dst = gST + static_cast<size_t>(chain) * DK * DV + 16 * jt;
+#pragma unroll
+    for (int m = 0; m < CPW; ++m) {
+      const int cb = R + NB * m;
+      if (cb < NCB) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(16 * cb + 4 * ln.g + r) * DV + ln.i] = S[m][r];
+      }
+    }
   }
 }
 
 // ----------------------------------------------------------------------------
-// Split path: prep kernel over all chunks, then the scan.
+// Split path: prep kernel over all chunks (one workgroup per chunk, all dv
+// columns), then the scan.
 // ----------------------------------------------------------------------------
-template <typename OpT, int DK, int C, int NJ>
-constexpr bool scan_fits() {
-  return SCfg<OpT, DK, C, NJ>::kLds <= kMaxLds;
-}
-
-// Most computing waves (16 columns each) that divide dv and fit in LDS.
 template <typename OpT, int DK, int C>
-int pick_scan_nj(int dv) {
-  int best = 0;
-  if (dv % 16 == 0 && scan_fits<OpT, DK, C, 1>()) best = 1;
-  if (dv % 32 == 0 && scan_fits<OpT, DK, C, 2>()) best = 2;
-  if (dv % 64 == 0 && scan_fits<OpT, DK, C, 4>()) best = 4;
-  if (dv % 128 == 0 && scan_fits<OpT, DK, C, 8>()) best = 8;
-  return best;
+bool split_fits(int dv) {
+  switch (dv) {
+    case 16: return fits<OpT, DK, C, 16>();
+    case 32: return fits<OpT, DK, C, 32>();
+    case 64: return fits<OpT, DK, C, 64>();
+    case 128: return fits<OpT, DK, C, 128>();
+  }
+  return false;
 }
 
 template <typename OpT, int DK, int C>
-size_t split_workspace_bytes(int B, int T, int H) {
+size_t split_workspace_bytes(int B, int T, int H, int dv) {
   const size_t nc = static_cast<size_t>((T + C - 1) / C);
-  return static_cast<size_t>(B) * H * nc * RecCfg<OpT, DK, C>::kBytes;
+  return static_cast<size_t>(B) * H * nc * RecCfg<OpT, DK, C>::bytes(dv);
 }
 
-template <typename OpT, int DK, int C, int NJ>
-hipError_t launch_scan(const PrefillArgs& a) {
+template <typename OpT, int DK, int C, int DVT>
+hipError_t launch_prep(const PrefillArgs& a) {
   using E = typename Ty<OpT>::Elem;
-  const long chains = static_cast<long>(a.B) * a.H;
-  dim3 grid(static_cast<unsigned>(chains * (a.dv / (16 * NJ))));
-  hipLaunchKernelGGL((kda_scan_kernel<OpT, DK, C, NJ>), grid, dim3(512), 0,
-                     static_cast<hipStream_t>(a.stream), static_cast<const E*>(a.v), a.beta,
-                     a.S0, static_cast<E*>(a.o), a.S_T, static_cast<const char*>(a.workspace),
-                     a.B, a.T, a.H, a.dv);
-  return hipGetLastError();
+  if constexpr (!fits<OpT, DK, C, DVT>()) {
+    return hipErrorInvalidValue;
+  } else {
+    const long chains = static_cast<long>(a.B) * a.H;
+    const int nc = (a.T + C - 1) / C;
+    if (nc == 0) return hipSuccess;
+    dim3 grid(static_cast<unsigned>(chains * nc));
+    hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT, true>), grid, dim3(512), 0,
+                       static_cast<hipStream_t>(a.stream), static_cast<const E*>(a.q),
+                       static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.alpha, a.beta,
+                       a.S0, static_cast<E*>(a.o), a.S_T, a.B, a.T, a.H, a.dv,
+                       static_cast<char*>(a.workspace));
+    return hipGetLastError();
+  }
 }
 
 template <typename OpT, int DK, int C>
 hipError_t launch_split(const PrefillArgs& a) {
   using E = typename Ty<OpT>::Elem;
-  constexpr int kPrepDvt = 16;   // the prep kernel touches no value columns
-  if constexpr (!fits<OpT, DK, C, kPrepDvt>()) return hipErrorInvalidValue;
+  hipError_t e = hipErrorInvalidValue;
+  switch (a.dv) {
+    case 16: e = launch_prep<OpT, DK, C, 16>(a); break;
+    case 32: e = launch_prep<OpT, DK, C, 32>(a); break;
+    case 64: e = launch_prep<OpT, DK, C, 64>(a); break;
+    case 128: e = launch_prep<OpT, DK, C, 128>(a); break;
+  }
+  if (e != hipSuccess) return e;
   const long chains = static_cast<long>(a.B) * a.H;
-  const int nc = (a.T + C - 1) / C;
-  if constexpr (fits<OpT, DK, C, kPrepDvt>()) if (nc > 0) {
-    dim3 grid(static_cast<unsigned>(chains * nc));
-    hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, kPrepDvt, true>), grid, dim3(512), 0,
-                       static_cast<hipStream_t>(a.stream), static_cast<const E*>(a.q),
-                       static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.alpha, a.beta,
-                       a.S0, static_cast<E*>(a.o), a.S_T, a.B, a.T, a.H, a.dv,
-                       static_cast<char*>(a.workspace));
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  switch (pick_scan_nj<OpT, DK, C>(a.dv)) {
-    case 1: if constexpr (scan_fits<OpT, DK, C, 1>()) return launch_scan<OpT, DK, C, 1>(a); break;
-    case 2: if constexpr (scan_fits<OpT, DK, C, 2>()) return launch_scan<OpT, DK, C, 2>(a); break;
-    case 4: if constexpr (scan_fits<OpT, DK, C, 4>()) return launch_scan<OpT, DK, C, 4>(a); break;
-    case 8: if constexpr (scan_fits<OpT, DK, C, 8>()) return launch_scan<OpT, DK, C, 8>(a); break;
-  }
-  return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(chains * (a.dv / 16)));
+  hipLaunchKernelGGL((kda_scan_kernel<OpT, DK, C>), grid, dim3(SCfg<OpT, DK, C>::NTH), 0,
+                     static_cast<hipStream_t>(a.stream), a.S0, static_cast<E*>(a.o), a.S_T,
+                     static_cast<const char*>(a.workspace), a.B, a.T, a.H, a.dv);
+  return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------
@@ -324,8 +282,7 @@ constexpr long kSplitMaxChains = 127;
 
 template <typename OpT, int DK, int C>
 bool use_split(long chains, int dv) {
-  return chains <= kSplitMaxChains && fits<OpT, DK, C, 16>() &&
-         pick_scan_nj<OpT, DK, C>(dv) > 0;
+  return chains <= kSplitMaxChains && split_fits<OpT, DK, C>(dv);
 }
 
 template <typename OpT, int DK, int C>
@@ -363,7 +320,7 @@ bool supported_dk(int dv, int C) {
 template <typename OpT, int DK, int C>
 size_t workspace_c(int B, int T, int H, int dv) {
   if (!use_split<OpT, DK, C>(static_cast<long>(B) * H, dv)) return 0;
-  return split_workspace_bytes<OpT, DK, C>(B, T, H);
+  return split_workspace_bytes<OpT, DK, C>(B, T, H, dv);
 }
 
 template <typename OpT, int DK>

@@ -134,12 +134,13 @@ def test_workspace_query():
     L = _lib()
     lib = L.load()
     bad = (1 << 64) - 1
-    # one record per chunk: W, Q.E, (K.E')^T [C x dk each], P, Y [C x C], decay [dk] fp32
-    rec = (3 * 64 * 128 + 2 * 64 * 64) * 2 + 4 * 128
-    rec = (rec + 255) // 256 * 256
-    assert lib.kda_prefill_workspace_bytes(1, 4096, 16, 128, 128, 64, 1) == 16 * 64 * rec
+    # one record per chunk: W, Q.E, (K.E')^T [C x dk each], P [C x C] in the
+    # operand type, decay [dk] fp32, U~ [C x dv] in the operand type
+    def rec(C, dk, dv, eb):
+        return ((3 * C * dk + C * C + C * dv) * eb + 4 * dk + 255) // 256 * 256
+    assert lib.kda_prefill_workspace_bytes(1, 4096, 16, 128, 128, 64, 1) == 16 * 64 * rec(64, 128, 128, 2)
+    assert lib.kda_prefill_workspace_bytes(1, 4096, 16, 128, 64, 64, 1) == 16 * 64 * rec(64, 128, 64, 2)
     assert lib.kda_prefill_workspace_bytes(8, 8192, 32, 128, 128, 64, 1) == 0   # fused path
-    rec16 = ((3 * 16 * 16 + 2 * 16 * 16) * 4 + 4 * 16 + 255) // 256 * 256
-    assert lib.kda_prefill_workspace_bytes(1, 256, 1, 16, 16, 16, 0) == 16 * rec16
+    assert lib.kda_prefill_workspace_bytes(1, 256, 1, 16, 16, 16, 0) == 16 * rec(16, 16, 16, 4)
     assert lib.kda_prefill_workspace_bytes(1, 256, 1, 16, 16, 12, 0) == bad
     assert lib.kda_prefill_workspace_bytes(0, 256, 1, 16, 16, 16, 0) == bad
