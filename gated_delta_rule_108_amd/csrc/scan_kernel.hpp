@@ -20,6 +20,8 @@
 // dependent work per chunk is a handful of short MFMA chains.
 #pragma once
 
+#include <type_traits>
+
 #include "prefill_kernel.hpp"
 
 namespace kda {
@@ -100,28 +102,40 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
 #pragma unroll
         for (int r = 0; r < 4; ++r) S[m][r] = src[(16 * cb + 4 * ln.g + r) * DV + ln.i];
       }
+      // Land the loads here: a load still in flight at the loop entry makes
+      // every chunk wait for all outstanding memory traffic.
+      asm volatile("" : "+v"(S[m][0]), "+v"(S[m][1]), "+v"(S[m][2]), "+v"(S[m][3]));
     }
   }
 
-  auto fetch = [&](Ops& x, int ch) {
+  // The next chunk's operands, in four parts.  A CU's vector memory path
+  // moves about 64 bytes per clock, so one wave issuing all of its ~17 KB at
+  // once would stall on issue for most of a chunk; the parts are spread over
+  // the phases of the chunk instead.
+  auto fetch = [&](Ops& x, int ch, auto part) {
+    constexpr int kPart = decltype(part)::value;
     const char* rc = rec0 + static_cast<size_t>(ch) * rbytes;
     const E* rw = reinterpret_cast<const E*>(rc);
     int l = lane;
     asm volatile("" : "+v"(l));
+    if constexpr (kPart == 0 || kPart == 1) {
 #pragma unroll
-    for (int s = 0; s < NKD; ++s) {
-      const size_t o = (static_cast<size_t>(R * NKD + s) * kWave + l) * ND;
-      x.w[s] = *reinterpret_cast<const typename Ops::FD*>(rw + RC::kW + o);
-      x.q[s] = *reinterpret_cast<const typename Ops::FD*>(rw + RC::kQ + o);
-    }
+      for (int s = 0; s < NKD; ++s) {
+        const size_t o = (static_cast<size_t>(R * NKD + s) * kWave + l) * ND;
+        if constexpr (kPart == 0) x.w[s] = *reinterpret_cast<const typename Ops::FD*>(rw + RC::kW + o);
+        else x.q[s] = *reinterpret_cast<const typename Ops::FD*>(rw + RC::kQ + o);
+      }
+    } else if constexpr (kPart == 2) {
 #pragma unroll
-    for (int s = 0; s < NKC; ++s)
-      x.p[s] = *reinterpret_cast<const typename Ops::FC*>(
-          rw + RC::kP + (static_cast<size_t>(R * NKC + s) * kWave + l) * NCK);
+      for (int s = 0; s < NKC; ++s)
+        x.p[s] = *reinterpret_cast<const typename Ops::FC*>(
+            rw + RC::kP + (static_cast<size_t>(R * NKC + s) * kWave + l) * NCK);
+      x.ut = Acc4<OpT>::load(reinterpret_cast<const E*>(rc + RC::kUByte) +
+                             (static_cast<size_t>(R * NJV + jt) * kWave + l) * 4);
+    } else {
 #pragma unroll
-    for (int m = 0; m < CPW; ++m) {
-      const int cb = R + NB * m;
-      if (cb < NCB) {
+      for (int m = 0; m < CPW; ++m) {
+        const int cb = min(R + NB * m, NCB - 1);   // blocks past dk: loaded, never used
 #pragma unroll
         for (int s = 0; s < NKC; ++s)
           x.kg[m][s] = *reinterpret_cast<const typename Ops::FC*>(
@@ -129,17 +143,29 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
         x.gc[m] = *reinterpret_cast<const float4*>(rc + RC::kGcByte + 4 * (16 * cb + 4 * (l / 16)));
       }
     }
-    x.ut = Acc4<OpT>::load(reinterpret_cast<const E*>(rc + RC::kUByte) +
-                           (static_cast<size_t>(R * NJV + jt) * kWave + l) * 4);
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
+  auto fetch_all = [&](Ops& x, int ch) {
+    fetch(x, ch, P0{});
+    fetch(x, ch, P1{});
+    fetch(x, ch, P2{});
+    fetch(x, ch, P3{});
   };
 
-  Ops cur, nxt;
-  if (NC > 0) fetch(nxt, 0);
+
   E* po0 = go + row0 * DV + 16 * jt;
   const int rsV = H * DV;
-  for (int ch = 0; ch < NC; ++ch) {
-    cur = nxt;
-    if (ch + 1 < NC) fetch(nxt, ch + 1);
+  // One chunk: consumes `cur`, meanwhile the next chunk's operands load into
+  // `nxt`.  Every chunk issues the same memory operations (the last one
+  // re-fetches itself; only the partial last chunk masks its stores), so the
+  // compiler's wait counts stay exact instead of draining all traffic.
+  auto step = [&](const Ops& cur, Ops& nxt, int ch, auto tail) {
+    const int chn = min(ch + 1, NC - 1);
+    fetch(nxt, chn, P0{});
+    __builtin_amdgcn_sched_barrier(0);
     const int t0 = ch * C;
     const int nrows = min(C, T - t0);
     const Lane ln = lane_now();
@@ -160,6 +186,9 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
     for (int s = 0; s < NKD; ++s) x = mfma<OpT, KSD>(cur.w[s], stf[s], x);
 #pragma unroll
     for (int s = 0; s < NKD; ++s) o = mfma<OpT, KSD>(cur.q[s], stf[s], o);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(nxt, chn, P1{});
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 u = Acc4<OpT>::cvt(cur.ut);
 #pragma unroll
     for (int r = 0; r < 4; ++r) u[r] -= x[r];
@@ -169,32 +198,60 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
     typename Ops::FC utf[NKC];
 #pragma unroll
     for (int s = 0; s < NKC; ++s) utf[s] = Src<OpT>{UT, LDC, ln}.template get<KSC>(s * KSC);
-    // O_R += P_R U  (P is block-lower; its upper blocks are zeros)
+    // S <- Diag(E_{C-1}) S + (K.E')^T U for this wave's row blocks (first:
+    // the next chunk waits on it), then O_R += P_R U (P is block-lower, its
+    // upper blocks are zeros).
+    f32x4 acc[CPW];
+#pragma unroll
+    for (int m = 0; m < CPW; ++m) {
+      acc[m] = zero4();
+      if (R + NB * m < NCB) {
+#pragma unroll
+        for (int s = 0; s < NKC; ++s) acc[m] = mfma<OpT, KSC>(cur.kg[m][s], utf[s], acc[m]);
+      }
+    }
     f32x4 pu = zero4();
 #pragma unroll
     for (int s = 0; s < NKC; ++s) pu = mfma<OpT, KSC>(cur.p[s], utf[s], pu);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(nxt, chn, P2{});
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < CPW; ++m) {
+      if (R + NB * m < NCB) {
+        const float4 gc = cur.gc[m];
+        S[m][0] = gc.x * S[m][0] + acc[m][0];
+        S[m][1] = gc.y * S[m][1] + acc[m][1];
+        S[m][2] = gc.z * S[m][2] + acc[m][2];
+        S[m][3] = gc.w * S[m][3] + acc[m][3];
+      }
+    }
     add4(o, pu);
     E* po = po0 + static_cast<size_t>(t0) * rsV;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int rl = 16 * R + 4 * ln.g + r;
-      if (rl < nrows) po[rl * rsV + ln.i] = Ty<OpT>::from_f32(o[r]);
+      if (!decltype(tail)::value || rl < nrows) po[rl * rsV + ln.i] = Ty<OpT>::from_f32(o[r]);
     }
-    // S <- Diag(E_{C-1}) S + (K.E')^T U  for this wave's row blocks
-#pragma unroll
-    for (int m = 0; m < CPW; ++m) {
-      const int cb = R + NB * m;
-      if (cb < NCB) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int s = 0; s < NKC; ++s) acc = mfma<OpT, KSC>(cur.kg[m][s], utf[s], acc);
-        const float4 gc = cur.gc[m];
-        S[m][0] = gc.x * S[m][0] + acc[0];
-        S[m][1] = gc.y * S[m][1] + acc[1];
-        S[m][2] = gc.z * S[m][2] + acc[2];
-        S[m][3] = gc.w * S[m][3] + acc[3];
-      }
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(nxt, chn, P3{});
+  };
+  // Two operand sets in alternation (no register copies between chunks).
+  using Full = std::integral_constant<bool, false>;
+  using Tail = std::integral_constant<bool, true>;
+  Ops opa, opb;
+  if (NC > 0) fetch_all(opa, 0);
+  const int nfull = T / C;
+  int ch = 0;
+  for (; ch + 2 <= nfull; ch += 2) {
+    step(opa, opb, ch, Full{});
+    step(opb, opa, ch + 1, Full{});
+  }
+  // at most two chunks left: one full and/or the partial last one
+  if (ch < NC) {
+    if (ch < nfull) step(opa, opb, ch, Full{});
+    else step(opa, opb, ch, Tail{});
+    if (ch + 1 < NC) step(opb, opa, ch + 1, Tail{});
   }
 
   if (gST != nullptr) {
