@@ -79,6 +79,14 @@ def profiled_traffic(name):
         return None
 
 
+def prefill_kernels(kda, B, T, H, dk, dv, C):
+    """Names of the kernels one prefill call launches (the path the library
+    picks: a workspace means the split path, prep kernel + scan kernel)."""
+    if kda.prefill_workspace_bytes(B, T, H, dk, dv, C) > 0:
+        return f"kda_prefill_kernel<bf16,{dk},{C},{dv},prep> + kda_scan_kernel<bf16,{dk},{C}>"
+    return f"kda_prefill_kernel<bf16,{dk},{C},dv-slab>"
+
+
 def time_launches(fn, steps, warmup, torch):
     """Warm up, then time `steps` calls bracketed by synchronisations, with
     HIP events on the current stream (the stream the kernels run on)."""
@@ -221,7 +229,7 @@ def headline(args, spec, inp_cpu, out, torch, kda, dev):
                    "C": C, "io_dtype": "bf16", "state_dtype": "fp32"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": profiled_traffic("prefill_h16_t4k"),
-                     "kernel": "kda_prefill_kernel<bf16,128,64,16>",
+                     "kernel": prefill_kernels(kda, B, T, H, dk, dv, C),
                      "kernel_ms": ms_ev, "alg_bytes_per_launch": nbytes},
         "mfma": {"achieved_tflops": tfl, "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                  "frac": tfl / MFMA_BF16_PEAK_TFLOPS, "flops_per_launch": flops},
@@ -282,7 +290,8 @@ def extras(args, legs, out, torch, kda, wl, dev):
         lb = prefill_alg_bytes(lspec.B, lspec.T, lspec.H, 128, 128, 2, True)
         lf = prefill_flops(lspec.B, lspec.T, lspec.H, 128, 128, 64)
         out["prefill_b8_h32_t8k"] = {
-            "C": 64, "ms_per_launch": ms_l, "tokens_per_s": lspec.B * lspec.T / (ms_lw * 1e-3),
+            "C": 64, "kernel": prefill_kernels(kda, lspec.B, lspec.T, lspec.H, 128, 128, 64),
+            "ms_per_launch": ms_l, "tokens_per_s": lspec.B * lspec.T / (ms_lw * 1e-3),
             "GBps": lb / (ms_l * 1e-3) / 1e9, "frac_hbm": lb / (ms_l * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "traffic": profiled_traffic("prefill_b8_h32_t8k"), "alg_bytes_per_launch": lb,
             "tflops": lf / (ms_l * 1e-3) / 1e12,

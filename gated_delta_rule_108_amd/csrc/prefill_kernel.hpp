@@ -496,9 +496,11 @@ struct PCfg {
 constexpr int kMaxLds = 160 * 1024;
 
 // kPrep = false: the fused prefill (all chunks of a chain, state in
-// registers).  kPrep = true: one workgroup per chunk (DVT = dv) computes the
-// state-free chunk quantities and writes them to the workspace record of that
-// chunk (W, Q.E, (K.E')^T, P, chunk decay, U~) for the scan kernel.
+// registers).  kPrep = true: each workgroup (DVT = dv) takes a run of cpb
+// consecutive chunks of one chain, computes their state-free quantities and
+// writes them to the chunks' workspace records (W, Q.E, (K.E')^T, P, chunk
+// decay, U~) for the scan kernel; the next chunk's inputs load while the
+// current one is processed.
 template <typename OpT, int DK, int C, int DVT, bool kPrep = false>
 __global__ void __launch_bounds__(512)
 kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
@@ -506,7 +508,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
                    const typename Ty<OpT>::Elem* __restrict__ gv,
                    const float* __restrict__ galpha, const float* __restrict__ gbeta,
                    const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float* gST,
-                   int B, int T, int H, int DV, char* __restrict__ gws) {
+                   int B, int T, int H, int DV, char* __restrict__ gws, int cpb) {
   using Cf = PCfg<OpT, DK, C, DVT>;
   using E = typename Ty<OpT>::Elem;
   using PT = typename Pair<OpT>::T;
@@ -549,15 +551,16 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
 
   // Workgroup -> (chain, slab).  Consecutive workgroups are dealt round-robin
   // to the 8 XCDs; keep all slabs of one chain on one XCD so they share L2.
+  // Prep mode: workgroup -> (chain, run of cpb consecutive chunks).
   const int NC = (T + C - 1) / C;
-  const int ntiles = kPrep ? NC : DV / DVT;
+  const int ntiles = kPrep ? (NC + cpb - 1) / cpb : DV / DVT;
   const int total = gridDim.x;
   int L = blockIdx.x;
   if (!kPrep && ntiles > 1 && (total % 8) == 0) L = (blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
   const int chain = L / ntiles;
   const int j0 = kPrep ? 0 : (L % ntiles) * DVT;
-  const int ch_begin = kPrep ? L % ntiles : 0;
-  const int ch_end = kPrep ? ch_begin + 1 : NC;
+  const int ch_begin = kPrep ? (L % ntiles) * cpb : 0;
+  const int ch_end = kPrep ? min(ch_begin + cpb, NC) : NC;
   const int b = chain / H, h = chain % H;
 
   // Token t of this chain sits at row (b*T + t)*H + h of the [B*T*H, *]
@@ -1108,7 +1111,7 @@ hipError_t launch_one(const PrefillArgs& a) {
   hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT>), grid, dim3(PCfg<OpT, DK, C, DVT>::NTH), 0,
                      static_cast<hipStream_t>(a.stream), static_cast<const E*>(a.q),
                      static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.alpha, a.beta,
-                     a.S0, static_cast<E*>(a.o), a.S_T, a.B, a.T, a.H, a.dv, nullptr);
+                     a.S0, static_cast<E*>(a.o), a.S_T, a.B, a.T, a.H, a.dv, nullptr, 0);
   return hipGetLastError();
 }
 

@@ -289,6 +289,16 @@ size_t split_workspace_bytes(int B, int T, int H, int dv) {
   return static_cast<size_t>(B) * H * nc * RecCfg<OpT, DK, C>::bytes(dv);
 }
 
+// Chunks per prep workgroup: about one workgroup per CU in total.
+inline int prep_chunks_per_block(long chains, int nc) {
+  constexpr long kCUs = 256;
+  const long total = chains * nc;
+  long cpb = (total + kCUs - 1) / kCUs;
+  if (cpb < 1) cpb = 1;
+  if (cpb > nc) cpb = nc;
+  return static_cast<int>(cpb);
+}
+
 template <typename OpT, int DK, int C, int DVT>
 hipError_t launch_prep(const PrefillArgs& a) {
   using E = typename Ty<OpT>::Elem;
@@ -298,12 +308,15 @@ hipError_t launch_prep(const PrefillArgs& a) {
     const long chains = static_cast<long>(a.B) * a.H;
     const int nc = (a.T + C - 1) / C;
     if (nc == 0) return hipSuccess;
-    dim3 grid(static_cast<unsigned>(chains * nc));
-    hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT, true>), grid, dim3(512), 0,
-                       static_cast<hipStream_t>(a.stream), static_cast<const E*>(a.q),
+    // One workgroup per CU at this LDS size: give each a run of chunks so that
+    // all but the first chunk's loads hide behind compute.
+    const int cpb = prep_chunks_per_block(chains, nc);
+    const long blocks = chains * ((nc + cpb - 1) / cpb);
+    hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT, true>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(512), 0, static_cast<hipStream_t>(a.stream), static_cast<const E*>(a.q),
                        static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.alpha, a.beta,
                        a.S0, static_cast<E*>(a.o), a.S_T, a.B, a.T, a.H, a.dv,
-                       static_cast<char*>(a.workspace));
+                       static_cast<char*>(a.workspace), cpb);
     return hipGetLastError();
   }
 }
