@@ -161,33 +161,67 @@ template <> struct Pair<float> {
   __device__ __forceinline__ static T pack(float lo, float hi) { return make_float2(lo, hi); }
 };
 
-// Sixteen consecutive elements of one row (16 tokens of one channel), built
-// two at a time and stored with 16-byte writes.
-template <typename OpT> struct Col16;
-template <> struct Col16<bf16_t> {
-  uint32_t w[8];
-  __device__ __forceinline__ void put2(int j, float a, float b) { w[j >> 1] = pack_bf16x2(a, b); }
-  __device__ __forceinline__ void store(uint16_t* dst) const {
-    uint4* d = reinterpret_cast<uint4*>(dst);
-    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+// Four adjacent elements with one access (8 bytes bf16, 16 bytes fp32).
+template <typename OpT> struct Quad;
+template <> struct Quad<bf16_t> {
+  using T = uint2;
+  __device__ __forceinline__ static T load(const uint16_t* p) {
+    return *reinterpret_cast<const uint2*>(p);
+  }
+  __device__ __forceinline__ static T zero() { return make_uint2(0u, 0u); }
+  __device__ __forceinline__ static float get(T v, int x) {
+    const uint32_t w = x < 2 ? v.x : v.y;
+    return bf16_to_f32(static_cast<uint16_t>((x & 1) ? (w >> 16) : (w & 0xffffu)));
+  }
+  __device__ __forceinline__ static void store(uint16_t* p, float a, float b, float c, float d) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
   }
 };
-template <> struct Col16<float> {
-  float w[16];
-  __device__ __forceinline__ void put2(int j, float a, float b) { w[j] = a; w[j + 1] = b; }
-  __device__ __forceinline__ void store(float* dst) const {
-    float4* d = reinterpret_cast<float4*>(dst);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) d[q] = make_float4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+template <> struct Quad<float> {
+  using T = float4;
+  __device__ __forceinline__ static T load(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+  }
+  __device__ __forceinline__ static T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ static float get(T v, int x) {
+    return x == 0 ? v.x : x == 1 ? v.y : x == 2 ? v.z : v.w;
+  }
+  __device__ __forceinline__ static void store(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
   }
 };
+
+// A 16-byte vector of 16 / sizeof(element) values.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <typename OpT>
+__device__ __forceinline__ float vec_elem(const u32x4& v, int q) {
+  if constexpr (Ty<OpT>::kBytes == 2)
+    return bf16_to_f32(static_cast<uint16_t>((v[q >> 1] >> (16 * (q & 1))) & 0xffffu));
+  else
+    return __uint_as_float(v[q]);
+}
+
+// Value of lane K of this lane's group of four (a DPP move, no LDS).
+template <int K>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), K * 0x55, 0xF, 0xF, false));
+}
 
 // Orders this wave's LDS writes before its later LDS reads (no other wave
 // takes part, so no barrier is needed).
 __device__ __forceinline__ void wave_fence() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
+}
+// Workgroup barrier for LDS only: orders LDS accesses across the waves
+// without waiting for outstanding global loads or stores (__syncthreads()
+// would drain both, which throws away the prefetch of the next chunk and
+// stalls on every output store).  No workgroup reads back global memory it
+// wrote, so LDS is the only memory shared across waves.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 // Index of the off-diagonal block (R, I), I < R, in row-major lower order.
 __host__ __device__ constexpr int yf_block(int R, int I) { return R * (R - 1) / 2 + I; }
@@ -482,9 +516,13 @@ struct PCfg {
   static constexpr int kLds = oFL + kFL;
 
   // work items
-  static constexpr int NGI = NB * DK / 2;                  // (block, channel pair)
+  // Gate items (block J, channel quad, row quarter): four rows x four
+  // channels; the four quarters of a (block, quad) are adjacent lanes.
+  static constexpr int NGI = NB * DK;
   static constexpr int NGT = (NGI + NTH - 1) / NTH;
-  static constexpr int NVI = NB * DVT / 2;                 // (block, value-column pair)
+  // Value items (block J, 16-byte column vector, row quarter).
+  static constexpr int VEC = 16 / EB;                      // value columns per vector
+  static constexpr int NVI = NB * (DVT / VEC) * 4;
   static constexpr int NVT = (NVI + NTH - 1) / NTH;
   static constexpr int NS = NCB * NJ;                      // state tiles
   static constexpr int NSW = (NS + NW - 1) / NW;
@@ -600,9 +638,10 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
   // previous contents, so their latency hides behind chunk ch's compute.
   // Rows are clamped to the last token; rows past T are replaced by identity
   // padding (gate 1, key/query/value 0, strength 0) when consumed.
-  float ga[Cf::NGT][16][2];     // alpha, two channels
-  PT gkk[Cf::NGT][16], gqq[Cf::NGT][16];
-  PT gvv[Cf::NVT][16];
+  using QT = typename Quad<OpT>::T;
+  float ga[Cf::NGT][4][4];      // alpha [row][channel]
+  QT gkk[Cf::NGT][4], gqq[Cf::NGT][4];
+  u32x4 gvv[Cf::NVT][4];
   float gbe = 0.f;
   auto fetch_gates = [&](int tn) {
     const size_t base = (row0 + static_cast<size_t>(tn) * H) * DK;
@@ -616,15 +655,18 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     for (int it = 0; it < Cf::NGT; ++it) {
       const int item = t_ + NTH * it;
       if (Cf::NGI % NTH == 0 || item < Cf::NGI) {
-        const int J = item / (DK / 2), c = 2 * (item % (DK / 2));
+        const int h = item % 4, g = item / 4;
+        const int J = g / (DK / 4), c = 4 * (g % (DK / 4));
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int off = min(16 * J + j, jmax) * rsK + c;
-          const float2 a2 = *reinterpret_cast<const float2*>(pa + off);
-          ga[it][j][0] = a2.x;
-          ga[it][j][1] = a2.y;
-          gkk[it][j] = Pair<OpT>::load(pk + off);
-          gqq[it][j] = Pair<OpT>::load(pq + off);
+        for (int j = 0; j < 4; ++j) {
+          const int off = min(16 * J + 4 * h + j, jmax) * rsK + c;
+          const float4 a4 = *reinterpret_cast<const float4*>(pa + off);
+          ga[it][j][0] = a4.x;
+          ga[it][j][1] = a4.y;
+          ga[it][j][2] = a4.z;
+          ga[it][j][3] = a4.w;
+          gkk[it][j] = Quad<OpT>::load(pk + off);
+          gqq[it][j] = Quad<OpT>::load(pq + off);
         }
       }
     }
@@ -638,9 +680,11 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     for (int it = 0; it < Cf::NVT; ++it) {
       const int item = t_ + NTH * it;
       if (Cf::NVI % NTH == 0 || item < Cf::NVI) {
-        const int J = item / (DVT / 2), cc = 2 * (item % (DVT / 2));
+        const int h = item % 4, g = item / 4;
+        const int J = g / (DVT / Cf::VEC), cc = Cf::VEC * (g % (DVT / Cf::VEC));
 #pragma unroll
-        for (int j = 0; j < 16; ++j) gvv[it][j] = Pair<OpT>::load(pv + min(16 * J + j, jmax) * rsV + cc);
+        for (int j = 0; j < 4; ++j)
+          gvv[it][j] = *reinterpret_cast<const u32x4*>(pv + min(16 * J + 4 * h + j, jmax) * rsV + cc);
       }
     }
   };
@@ -661,41 +705,54 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     if (tid < C) sBE[tid] = (t0 + tid < T) ? gbe : 0.f;
     if (more) fetch_beta(t0 + C);
     if (tid < NB) sFL[tid] = 0;
+    // Per gate item: quarter products of alpha, combined across the four
+    // quarters of the block (lanes of one group of four) into the block total
+    // BT and this quarter's offsets: Foff = product over earlier quarters,
+    // Hoff = product over later quarters.
+    float foff[Cf::NGT][4], hoff[Cf::NGT][4], bt[Cf::NGT][4];
 #pragma unroll
     for (int it = 0; it < Cf::NGT; ++it) {
       const int item = tid + NTH * it;
       if (Cf::NGI % NTH == 0 || item < Cf::NGI) {
-        const int J = item / (DK / 2), c = 2 * (item % (DK / 2));
-        float f0 = 1.f, f1 = 1.f;
+        const int h = item % 4, g = item / 4;
+        const int J = g / (DK / 4), c = 4 * (g % (DK / 4));
+        if (!full) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          if (!full) {
-            const bool valid = t0 + 16 * J + j < T;
-            ga[it][j][0] = valid ? ga[it][j][0] : 1.f;
-            ga[it][j][1] = valid ? ga[it][j][1] : 1.f;
-            gkk[it][j] = valid ? gkk[it][j] : Pair<OpT>::zero();
-            gqq[it][j] = valid ? gqq[it][j] : Pair<OpT>::zero();
+          for (int j = 0; j < 4; ++j) {
+            const bool valid = t0 + 16 * J + 4 * h + j < T;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) ga[it][j][x] = valid ? ga[it][j][x] : 1.f;
+            gkk[it][j] = valid ? gkk[it][j] : Quad<OpT>::zero();
+            gqq[it][j] = valid ? gqq[it][j] : Quad<OpT>::zero();
           }
-          f0 *= ga[it][j][0];
-          f1 *= ga[it][j][1];
         }
-        sBT[J * DK + c] = f0;
-        sBT[J * DK + c + 1] = f1;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const float p = ga[it][0][x] * ga[it][1][x] * ga[it][2][x] * ga[it][3][x];
+          const float p0 = quad_bcast<0>(p), p1 = quad_bcast<1>(p);
+          const float p2 = quad_bcast<2>(p), p3 = quad_bcast<3>(p);
+          foff[it][x] = h == 0 ? 1.f : h == 1 ? p0 : h == 2 ? p0 * p1 : p0 * p1 * p2;
+          hoff[it][x] = h == 3 ? 1.f : h == 2 ? p3 : h == 1 ? p2 * p3 : p1 * p2 * p3;
+          bt[it][x] = (p0 * p1) * (p2 * p3);
+        }
+        if (h == 0)
+          *reinterpret_cast<float4*>(sBT + J * DK + c) =
+              make_float4(bt[it][0], bt[it][1], bt[it][2], bt[it][3]);
       }
     }
 #pragma unroll
     for (int it = 0; it < Cf::NVT; ++it) {
       const int item = tid + NTH * it;
       if (Cf::NVI % NTH == 0 || item < Cf::NVI) {
-        const int J = item / (DVT / 2);
+        const int h = item % 4, J = (item / 4) / (DVT / Cf::VEC);
         if (!full) {
 #pragma unroll
-          for (int j = 0; j < 16; ++j)
-            gvv[it][j] = (t0 + 16 * J + j < T) ? gvv[it][j] : Pair<OpT>::zero();
+          for (int j = 0; j < 4; ++j)
+            gvv[it][j] = (t0 + 16 * J + 4 * h + j < T) ? gvv[it][j] : u32x4{0u, 0u, 0u, 0u};
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ================= G2: chunk-level gate products and MFMA operands
     if (tid < DK) {
@@ -717,69 +774,67 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     for (int it = 0; it < Cf::NGT; ++it) {
       const int item = tid + NTH * it;
       if (Cf::NGI % NTH == 0 || item < Cf::NGI) {
-        const int J = item / (DK / 2), c = 2 * (item % (DK / 2));
-        float pre[2] = {1.f, 1.f}, suf[2] = {1.f, 1.f};
+        const int h = item % 4, g = item / 4;
+        const int J = g / (DK / 4), c = 4 * (g % (DK / 4));
+        // decay of the blocks before / after J, and 1/BT_J (zero for an
+        // unsafe block: its diagonal tile is then done exactly on the VALUs)
+        float pre[4], suf[4], rbt[4];
         bool unsafe = false;
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
+        for (int x = 0; x < 4; ++x) {
+          pre[x] = 1.f;
+          suf[x] = 1.f;
           for (int JJ = 0; JJ < J; ++JJ) pre[x] *= sBT[JJ * DK + c + x];
           for (int JJ = J + 1; JJ < NB; ++JJ) suf[x] *= sBT[JJ * DK + c + x];
-          unsafe |= !(sBT[J * DK + c + x] >= kUnsafeBlockDecay);
+          const bool safe = bt[it][x] >= kUnsafeBlockDecay;
+          unsafe |= !safe;
+          // 1/F_i = H_i / BT_J: one reciprocal per channel instead of per row
+          rbt[x] = safe ? __builtin_amdgcn_rcpf(bt[it][x]) : 0.f;
         }
-        if (unsafe) atomicOr(&sFL[J], 1);
-        // reverse exclusive products H_j = prod_{j' > j in block} alpha
-        float hx[16][2];
-        hx[15][0] = hx[15][1] = 1.f;
+        if (unsafe && h == 0) atomicOr(&sFL[J], 1);
+        // H_r = product of alpha after row r within the block
+        float hx[4][4];
 #pragma unroll
-        for (int j = 14; j >= 0; --j) {
-          hx[j][0] = hx[j + 1][0] * ga[it][j + 1][0];
-          hx[j][1] = hx[j + 1][1] * ga[it][j + 1][1];
+        for (int x = 0; x < 4; ++x) {
+          hx[3][x] = hoff[it][x];
+#pragma unroll
+          for (int j = 2; j >= 0; --j) hx[j][x] = hx[j + 1][x] * ga[it][j + 1][x];
         }
-        bool safe[2];
+        float f[4];
 #pragma unroll
-        for (int x = 0; x < 2; ++x) safe[x] = sBT[J * DK + c + x] >= kUnsafeBlockDecay;
-        float f[2] = {1.f, 1.f};
-        Col16<OpT> kbt[2], kgt[2];
+        for (int x = 0; x < 4; ++x) f[x] = foff[it][x];
+        float kb[4][4], kg[4][4];   // [channel][row of the quarter]
 #pragma unroll
-        for (int j = 0; j < 16; j += 2) {
-          float kb[2][2], kg[2][2];   // [channel][row of the pair]
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * J + 4 * h + j;
+          const float be = sBE[r];
+          float kr[4], qr[4], ki[4], kv[4];
 #pragma unroll
-          for (int d = 0; d < 2; ++d) {
-            const int jj = j + d, r = 16 * J + jj;
-            const float be = sBE[r];
-            float kr[2], qr[2], ki[2], kv[2];
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-              f[x] *= ga[it][jj][x];
-              const float kk = Pair<OpT>::get(gkk[it][jj], x);
-              const float qq = Pair<OpT>::get(gqq[it][jj], x);
-              kr[x] = kk * f[x];
-              qr[x] = qq * f[x];
-              ki[x] = kk * hx[jj][x];
-              kv[x] = safe[x] ? kk * __builtin_amdgcn_rcpf(f[x]) : 0.f;
-              kb[x][d] = be * kr[x] * pre[x];
-              kg[x][d] = ki[x] * suf[x];
-            }
-            *reinterpret_cast<PT*>(Kr + r * LDK + c) = Pair<OpT>::pack(kr[0], kr[1]);
-            *reinterpret_cast<PT*>(Qr + r * LDK + c) = Pair<OpT>::pack(qr[0], qr[1]);
-            *reinterpret_cast<PT*>(Ki + r * LDK + c) = Pair<OpT>::pack(ki[0], ki[1]);
-            *reinterpret_cast<PT*>(Kinv + r * LDK + c) = Pair<OpT>::pack(kv[0], kv[1]);
+          for (int x = 0; x < 4; ++x) {
+            f[x] *= ga[it][j][x];
+            const float kk = Quad<OpT>::get(gkk[it][j], x);
+            const float qq = Quad<OpT>::get(gqq[it][j], x);
+            kr[x] = kk * f[x];
+            qr[x] = qq * f[x];
+            ki[x] = kk * hx[j][x];
+            kv[x] = ki[x] * rbt[x];
+            kb[x][j] = be * kr[x] * pre[x];
+            kg[x][j] = ki[x] * suf[x];
           }
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            kbt[x].put2(j, kb[x][0], kb[x][1]);
-            kgt[x].put2(j, kg[x][0], kg[x][1]);
-          }
+          Quad<OpT>::store(Kr + r * LDK + c, kr[0], kr[1], kr[2], kr[3]);
+          Quad<OpT>::store(Qr + r * LDK + c, qr[0], qr[1], qr[2], qr[3]);
+          Quad<OpT>::store(Ki + r * LDK + c, ki[0], ki[1], ki[2], ki[3]);
+          Quad<OpT>::store(Kinv + r * LDK + c, kv[0], kv[1], kv[2], kv[3]);
         }
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          kbt[x].store(KbT + (c + x) * LDC + 16 * J);
-          kgt[x].store(KgT + (c + x) * LDC + 16 * J);
+        for (int x = 0; x < 4; ++x) {
+          Quad<OpT>::store(KbT + (c + x) * LDC + 16 * J + 4 * h, kb[x][0], kb[x][1], kb[x][2], kb[x][3]);
+          Quad<OpT>::store(KgT + (c + x) * LDC + 16 * J + 4 * h, kg[x][0], kg[x][1], kg[x][2], kg[x][3]);
         }
       }
     }
     if (more) fetch_gates(t0 + C);
-    __syncthreads();
+    lds_barrier();
 
     // ================= AP + SD: gated K K^T (-> L in TT) and Q K^T (-> P) tiles.
     // Wave R < NB computes the diagonal pair (R, R) and inverts the 16x16
@@ -864,7 +919,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ================= SO: stage beta V (transposed) for U~, then the
     // off-diagonal blocks of Y, one block row per barrier:
@@ -874,16 +929,15 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     for (int it = 0; it < Cf::NVT; ++it) {
       const int item = tid + NTH * it;
       if (Cf::NVI % NTH == 0 || item < Cf::NVI) {
-        const int J = item / (DVT / 2), cc = 2 * (item % (DVT / 2));
+        const int h = item % 4, g = item / 4;
+        const int J = g / (DVT / Cf::VEC), cc = Cf::VEC * (g % (DVT / Cf::VEC));
+        const int r0 = 16 * J + 4 * h;
+        const float b0 = sBE[r0], b1 = sBE[r0 + 1], b2 = sBE[r0 + 2], b3 = sBE[r0 + 3];
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          Col16<OpT> col;
-#pragma unroll
-          for (int j = 0; j < 16; j += 2)
-            col.put2(j, sBE[16 * J + j] * Pair<OpT>::get(gvv[it][j], x),
-                     sBE[16 * J + j + 1] * Pair<OpT>::get(gvv[it][j + 1], x));
-          col.store(VbT + (cc + x) * LDC + 16 * J);
-        }
+        for (int x = 0; x < Cf::VEC; ++x)
+          Quad<OpT>::store(VbT + (cc + x) * LDC + r0, b0 * vec_elem<OpT>(gvv[it][0], x),
+                           b1 * vec_elem<OpT>(gvv[it][1], x), b2 * vec_elem<OpT>(gvv[it][2], x),
+                           b3 * vec_elem<OpT>(gvv[it][3], x));
       }
     }
     if (more) fetch_values(t0 + C);
@@ -916,9 +970,9 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
           Yb[(16 * R + rl) * LDC + 16 * I + ln.i] = Ty<OpT>::from_f32(-y[rr]);
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
-    if (NB == 1) __syncthreads();
+    if (NB == 1) lds_barrier();
 
     // Y as a matrix-core operand (a copy in the operand type).
     auto ysrc = [&](int R, const Lane& ln) { return Src<OpT>{Yb + 16 * R * LDC, LDC, ln}; };
@@ -962,7 +1016,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     if constexpr (kPrep) {
       // chunk record -> workspace: operand packets, decay, U~ (this slab is all of dv)
@@ -1002,7 +1056,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
           for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(Sreg[a][bb][rr]);
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (UM::active(wave)) {
       const Lane ln = lane_now();
 #pragma unroll
@@ -1021,7 +1075,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     E* po = go + (row0 + static_cast<size_t>(t0) * H) * DV + j0;
     const int nrows = min(C, T - t0);
     {
@@ -1072,7 +1126,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     if constexpr (kStageO) {
       // staged output rows -> HBM with 16-byte stores
       constexpr int VPR = DVT * static_cast<int>(sizeof(E)) / 16;   // vectors per row

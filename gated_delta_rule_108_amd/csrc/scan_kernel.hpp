@@ -37,14 +37,6 @@ struct SCfg {
   static constexpr int KSD = RC::KSD, KSC = RC::KSC, NKD = RC::NKD, NKC = RC::NKC;
 };
 
-// Orders LDS accesses across the workgroup without waiting for outstanding
-// global loads or stores (a plain __syncthreads() would drain both).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // One chunk's record operands for wave R.
 template <typename OpT, int DK, int C>
 struct ScanOps {
