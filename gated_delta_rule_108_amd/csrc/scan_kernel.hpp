@@ -12,12 +12,13 @@
 // (Parallelizing Linear Transformers with Delta Rule)", with the per-channel
 // decay of section "KDA/Kimi Linear").
 //
-// A workgroup has one wave per 16-row block R of the chunk.  Wave R computes
-// rows R of U and O and owns state row blocks R, R + C/16, ...; the state
-// tile (S^T) and U^T are exchanged through LDS, two LDS-only barriers per
-// chunk.  Every record operand goes straight from global memory into the
-// registers of the wave that uses it, one chunk ahead, so the chain of
-// dependent work per chunk is a handful of short MFMA chains.
+// A workgroup has two waves per 16-row block R of the chunk.  The state
+// wave of R computes rows R of U and owns state row blocks R, R + C/16, ...:
+// it carries the recurrence (S -> U -> S).  The output wave of R computes
+// rows R of O from the same S and U, off that critical path.  S^T and U^T are
+// exchanged through LDS, two LDS-only barriers per chunk.  Every record
+// operand goes straight from global memory into the registers of the wave
+// that uses it, one chunk ahead.
 #pragma once
 
 #include <type_traits>
@@ -29,35 +30,46 @@ namespace kda {
 template <typename OpT, int DK, int C>
 struct SCfg {
   static constexpr int NB = C / 16, NCB = DK / 16;
-  static constexpr int NTH = kWave * NB;
-  static constexpr int CPW = (NCB + NB - 1) / NB;    // state row blocks per wave
+  static constexpr int NTH = 2 * kWave * NB;         // state waves, then output waves
+  static constexpr int CPW = (NCB + NB - 1) / NB;    // state row blocks per state wave
   static constexpr int EB = Ty<OpT>::kBytes, PADE = 16 / EB;
   static constexpr int LDK = DK + PADE, LDC = C + PADE;
   using RC = RecCfg<OpT, DK, C>;
   static constexpr int KSD = RC::KSD, KSC = RC::KSC, NKD = RC::NKD, NKC = RC::NKC;
 };
 
-// One chunk's record operands for wave R.
+// One chunk's record operands of a state wave (W_R, U~_R, (K.E')^T rows,
+// decay) and of an output wave (Q.E_R, P_R).
 template <typename OpT, int DK, int C>
-struct ScanOps {
+struct StateOps {
   using Cf = SCfg<OpT, DK, C>;
   using FD = typename Frag<OpT, Cf::KSD>::T;
   using FC = typename Frag<OpT, Cf::KSC>::T;
-  FD w[Cf::NKD], q[Cf::NKD];
-  FC p[Cf::NKC];
+  FD w[Cf::NKD];
   FC kg[Cf::CPW][Cf::NKC];
   typename Acc4<OpT>::Raw ut;
   float4 gc[Cf::CPW];
 };
+template <typename OpT, int DK, int C>
+struct OutOps {
+  using Cf = SCfg<OpT, DK, C>;
+  using FD = typename Frag<OpT, Cf::KSD>::T;
+  using FC = typename Frag<OpT, Cf::KSC>::T;
+  FD q[Cf::NKD];
+  FC p[Cf::NKC];
+};
 
 template <typename OpT, int DK, int C>
-__global__ void __launch_bounds__(kWave * (C / 16))
+__global__ void __launch_bounds__(2 * kWave * (C / 16))
 kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float* gST,
                 const char* __restrict__ gws, int B, int T, int H, int DV) {
   using Cf = SCfg<OpT, DK, C>;
   using RC = typename Cf::RC;
   using E = typename Ty<OpT>::Elem;
-  using Ops = ScanOps<OpT, DK, C>;
+  using SO = StateOps<OpT, DK, C>;
+  using OO = OutOps<OpT, DK, C>;
+  using FD = typename SO::FD;
+  using FC = typename SO::FC;
   constexpr int NB = Cf::NB, NCB = Cf::NCB, CPW = Cf::CPW, LDK = Cf::LDK, LDC = Cf::LDC;
   constexpr int KSD = Cf::KSD, KSC = Cf::KSC, NKD = Cf::NKD, NKC = Cf::NKC;
   constexpr int ND = KSD / 4, NCK = KSC / 4;   // elements per lane of one packet
@@ -66,7 +78,9 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
   __shared__ __attribute__((aligned(16))) E UT[16 * LDC];   // U^T of the tile
 
   const int lane = threadIdx.x % kWave;
-  const int R = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int R = wv % NB;
+  const bool state_wave = wv < NB;
 
   // Workgroup -> (chain, column tile); all tiles of a chain on one XCD so the
   // chain's records are read from HBM once and then hit that XCD's L2.
@@ -77,185 +91,190 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
   const int chain = L / NJV, jt = L % NJV;
   const int b = chain / H, h = chain % H;
   const int NC = (T + C - 1) / C;
+  const int nfull = T / C;
   const size_t row0 = static_cast<size_t>(b) * T * H + h;
   const size_t rbytes = RC::bytes(DV);
   const char* rec0 = gws + static_cast<size_t>(chain) * NC * rbytes;
-
-  // state row blocks cb = R + NB*m of the tile, in registers
-  f32x4 S[CPW];
-  {
-    const Lane ln = lane_now();
-#pragma unroll
-    for (int m = 0; m < CPW; ++m) {
-      const int cb = R + NB * m;
-      S[m] = zero4();
-      if (cb < NCB && gS0 != nullptr) {
-        const float* src = gS0 + static_cast<size_t>(chain) * DK * DV + 16 * jt;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S[m][r] = src[(16 * cb + 4 * ln.g + r) * DV + ln.i];
-      }
-      // Land the loads here: a load still in flight at the loop entry makes
-      // every chunk wait for all outstanding memory traffic.
-      asm volatile("" : "+v"(S[m][0]), "+v"(S[m][1]), "+v"(S[m][2]), "+v"(S[m][3]));
-    }
-  }
-
-  // The next chunk's operands, in four parts.  A CU's vector memory path
-  // moves about 64 bytes per clock, so one wave issuing all of its ~17 KB at
-  // once would stall on issue for most of a chunk; the parts are spread over
-  // the phases of the chunk instead.
-  auto fetch = [&](Ops& x, int ch, auto part) {
-    constexpr int kPart = decltype(part)::value;
-    const char* rc = rec0 + static_cast<size_t>(ch) * rbytes;
-    const E* rw = reinterpret_cast<const E*>(rc);
-    int l = lane;
-    asm volatile("" : "+v"(l));
-    if constexpr (kPart == 0 || kPart == 1) {
-#pragma unroll
-      for (int s = 0; s < NKD; ++s) {
-        const size_t o = (static_cast<size_t>(R * NKD + s) * kWave + l) * ND;
-        if constexpr (kPart == 0) x.w[s] = *reinterpret_cast<const typename Ops::FD*>(rw + RC::kW + o);
-        else x.q[s] = *reinterpret_cast<const typename Ops::FD*>(rw + RC::kQ + o);
-      }
-    } else if constexpr (kPart == 2) {
-#pragma unroll
-      for (int s = 0; s < NKC; ++s)
-        x.p[s] = *reinterpret_cast<const typename Ops::FC*>(
-            rw + RC::kP + (static_cast<size_t>(R * NKC + s) * kWave + l) * NCK);
-      x.ut = Acc4<OpT>::load(reinterpret_cast<const E*>(rc + RC::kUByte) +
-                             (static_cast<size_t>(R * NJV + jt) * kWave + l) * 4);
-    } else {
-#pragma unroll
-      for (int m = 0; m < CPW; ++m) {
-        const int cb = min(R + NB * m, NCB - 1);   // blocks past dk: loaded, never used
-#pragma unroll
-        for (int s = 0; s < NKC; ++s)
-          x.kg[m][s] = *reinterpret_cast<const typename Ops::FC*>(
-              rw + RC::kKG + (static_cast<size_t>(cb * NKC + s) * kWave + l) * NCK);
-        x.gc[m] = *reinterpret_cast<const float4*>(rc + RC::kGcByte + 4 * (16 * cb + 4 * (l / 16)));
-      }
-    }
-  };
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  using P2 = std::integral_constant<int, 2>;
-  using P3 = std::integral_constant<int, 3>;
-  auto fetch_all = [&](Ops& x, int ch) {
-    fetch(x, ch, P0{});
-    fetch(x, ch, P1{});
-    fetch(x, ch, P2{});
-    fetch(x, ch, P3{});
-  };
-
-
-  E* po0 = go + row0 * DV + 16 * jt;
-  const int rsV = H * DV;
-  // One chunk: consumes `cur`, meanwhile the next chunk's operands load into
-  // `nxt`.  Every chunk issues the same memory operations (the last one
-  // re-fetches itself; only the partial last chunk masks its stores), so the
-  // compiler's wait counts stay exact instead of draining all traffic.
-  auto step = [&](const Ops& cur, Ops& nxt, int ch, auto tail) {
-    const int chn = min(ch + 1, NC - 1);
-    fetch(nxt, chn, P0{});
-    __builtin_amdgcn_sched_barrier(0);
-    const int t0 = ch * C;
-    const int nrows = min(C, T - t0);
-    const Lane ln = lane_now();
-
-    // publish this wave's state rows as S^T (operand type)
-#pragma unroll
-    for (int m = 0; m < CPW; ++m) {
-      const int cb = R + NB * m;
-      if (cb < NCB) Acc4<OpT>::store(ST + ln.i * LDK + 16 * cb + 4 * ln.g, S[m]);
-    }
-    lds_barrier();
-    typename Ops::FD stf[NKD];
-#pragma unroll
-    for (int s = 0; s < NKD; ++s) stf[s] = Src<OpT>{ST, LDK, ln}.template get<KSD>(s * KSD);
-    // U_R = U~_R - W_R S  and the first half of O_R = (Q.E)_R S
-    f32x4 x = zero4(), o = zero4();
-#pragma unroll
-    for (int s = 0; s < NKD; ++s) x = mfma<OpT, KSD>(cur.w[s], stf[s], x);
-#pragma unroll
-    for (int s = 0; s < NKD; ++s) o = mfma<OpT, KSD>(cur.q[s], stf[s], o);
-    __builtin_amdgcn_sched_barrier(0);
-    fetch(nxt, chn, P1{});
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 u = Acc4<OpT>::cvt(cur.ut);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) u[r] -= x[r];
-    // U^T[n][16R + 4g + r]
-    Acc4<OpT>::store(UT + ln.i * LDC + 16 * R + 4 * ln.g, u);
-    lds_barrier();
-    typename Ops::FC utf[NKC];
-#pragma unroll
-    for (int s = 0; s < NKC; ++s) utf[s] = Src<OpT>{UT, LDC, ln}.template get<KSC>(s * KSC);
-    // S <- Diag(E_{C-1}) S + (K.E')^T U for this wave's row blocks (first:
-    // the next chunk waits on it), then O_R += P_R U (P is block-lower, its
-    // upper blocks are zeros).
-    f32x4 acc[CPW];
-#pragma unroll
-    for (int m = 0; m < CPW; ++m) {
-      acc[m] = zero4();
-      if (R + NB * m < NCB) {
-#pragma unroll
-        for (int s = 0; s < NKC; ++s) acc[m] = mfma<OpT, KSC>(cur.kg[m][s], utf[s], acc[m]);
-      }
-    }
-    f32x4 pu = zero4();
-#pragma unroll
-    for (int s = 0; s < NKC; ++s) pu = mfma<OpT, KSC>(cur.p[s], utf[s], pu);
-    __builtin_amdgcn_sched_barrier(0);
-    fetch(nxt, chn, P2{});
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < CPW; ++m) {
-      if (R + NB * m < NCB) {
-        const float4 gc = cur.gc[m];
-        S[m][0] = gc.x * S[m][0] + acc[m][0];
-        S[m][1] = gc.y * S[m][1] + acc[m][1];
-        S[m][2] = gc.z * S[m][2] + acc[m][2];
-        S[m][3] = gc.w * S[m][3] + acc[m][3];
-      }
-    }
-    add4(o, pu);
-    E* po = po0 + static_cast<size_t>(t0) * rsV;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rl = 16 * R + 4 * ln.g + r;
-      if (!decltype(tail)::value || rl < nrows) po[rl * rsV + ln.i] = Ty<OpT>::from_f32(o[r]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    fetch(nxt, chn, P3{});
-  };
-  // Two operand sets in alternation (no register copies between chunks).
   using Full = std::integral_constant<bool, false>;
   using Tail = std::integral_constant<bool, true>;
-  Ops opa, opb;
-  if (NC > 0) fetch_all(opa, 0);
-  const int nfull = T / C;
-  int ch = 0;
-  for (; ch + 2 <= nfull; ch += 2) {
-    step(opa, opb, ch, Full{});
-    step(opb, opa, ch + 1, Full{});
-  }
-  // at most two chunks left: one full and/or the partial last one
-  if (ch < NC) {
-    if (ch < nfull) step(opa, opb, ch, Full{});
-    else step(opa, opb, ch, Tail{});
-    if (ch + 1 < NC) step(opb, opa, ch + 1, Tail{});
-  }
+  // Every chunk issues the same memory operations (the last one re-fetches
+  // itself; only the partial last chunk masks its stores), so the compiler's
+  // wait counts stay exact instead of draining all outstanding traffic.
 
-  if (gST != nullptr) {
-    const Lane ln = lane_now();
-    float* dst = gST + static_cast<size_t>(chain) * DK * DV + 16 * jt;
+  if (state_wave) {
+    // ---------------- state wave: S -> U -> S
+    f32x4 S[CPW];
+    {
+      const Lane ln = lane_now();
 #pragma unroll
-    for (int m = 0; m < CPW; ++m) {
-      const int cb = R + NB * m;
-      if (cb < NCB) {
+      for (int m = 0; m < CPW; ++m) {
+        const int cb = R + NB * m;
+        S[m] = zero4();
+        if (cb < NCB && gS0 != nullptr) {
+          const float* src = gS0 + static_cast<size_t>(chain) * DK * DV + 16 * jt;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(16 * cb + 4 * ln.g + r) * DV + ln.i] = S[m][r];
+          for (int r = 0; r < 4; ++r) S[m][r] = src[(16 * cb + 4 * ln.g + r) * DV + ln.i];
+        }
+        // Land the loads here: a load still in flight at the loop entry makes
+        // every chunk wait for all outstanding memory traffic.
+        asm volatile("" : "+v"(S[m][0]), "+v"(S[m][1]), "+v"(S[m][2]), "+v"(S[m][3]));
       }
+    }
+    // The next chunk's operands in two parts (a CU's vector memory path moves
+    // about 64 bytes per clock; one wave issuing all at once stalls on issue).
+    auto fetch = [&](SO& x, int ch, auto part) {
+      const char* rc = rec0 + static_cast<size_t>(ch) * rbytes;
+      const E* rw = reinterpret_cast<const E*>(rc);
+      int l = lane;
+      asm volatile("" : "+v"(l));
+      if constexpr (decltype(part)::value == 0) {
+#pragma unroll
+        for (int s = 0; s < NKD; ++s)
+          x.w[s] = *reinterpret_cast<const FD*>(
+              rw + RC::kW + (static_cast<size_t>(R * NKD + s) * kWave + l) * ND);
+        x.ut = Acc4<OpT>::load(reinterpret_cast<const E*>(rc + RC::kUByte) +
+                               (static_cast<size_t>(R * NJV + jt) * kWave + l) * 4);
+      } else {
+#pragma unroll
+        for (int m = 0; m < CPW; ++m) {
+          const int cb = min(R + NB * m, NCB - 1);   // blocks past dk: loaded, never used
+#pragma unroll
+          for (int s = 0; s < NKC; ++s)
+            x.kg[m][s] = *reinterpret_cast<const FC*>(
+                rw + RC::kKG + (static_cast<size_t>(cb * NKC + s) * kWave + l) * NCK);
+          x.gc[m] = *reinterpret_cast<const float4*>(rc + RC::kGcByte + 4 * (16 * cb + 4 * (l / 16)));
+        }
+      }
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    auto step = [&](const SO& cur, SO& nxt, int ch) {
+      const int chn = min(ch + 1, NC - 1);
+      fetch(nxt, chn, P0{});
+      __builtin_amdgcn_sched_barrier(0);
+      const Lane ln = lane_now();
+      // publish this wave's state rows as S^T (operand type)
+#pragma unroll
+      for (int m = 0; m < CPW; ++m) {
+        const int cb = R + NB * m;
+        if (cb < NCB) Acc4<OpT>::store(ST + ln.i * LDK + 16 * cb + 4 * ln.g, S[m]);
+      }
+      lds_barrier();
+      FD stf[NKD];
+#pragma unroll
+      for (int s = 0; s < NKD; ++s) stf[s] = Src<OpT>{ST, LDK, ln}.template get<KSD>(s * KSD);
+      // U_R = U~_R - W_R S, published as U^T[n][16R + 4g + r]
+      f32x4 x = zero4();
+#pragma unroll
+      for (int s = 0; s < NKD; ++s) x = mfma<OpT, KSD>(cur.w[s], stf[s], x);
+      f32x4 u = Acc4<OpT>::cvt(cur.ut);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) u[r] -= x[r];
+      Acc4<OpT>::store(UT + ln.i * LDC + 16 * R + 4 * ln.g, u);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(nxt, chn, P1{});
+      __builtin_amdgcn_sched_barrier(0);
+      FC utf[NKC];
+#pragma unroll
+      for (int s = 0; s < NKC; ++s) utf[s] = Src<OpT>{UT, LDC, ln}.template get<KSC>(s * KSC);
+      // S <- Diag(E_{C-1}) S + (K.E')^T U for this wave's row blocks
+#pragma unroll
+      for (int m = 0; m < CPW; ++m) {
+        if (R + NB * m < NCB) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int s = 0; s < NKC; ++s) acc = mfma<OpT, KSC>(cur.kg[m][s], utf[s], acc);
+          const float4 gc = cur.gc[m];
+          S[m][0] = gc.x * S[m][0] + acc[0];
+          S[m][1] = gc.y * S[m][1] + acc[1];
+          S[m][2] = gc.z * S[m][2] + acc[2];
+          S[m][3] = gc.w * S[m][3] + acc[3];
+        }
+      }
+    };
+    // Two operand sets in alternation (no register copies between chunks).
+    SO opa, opb;
+    if (NC > 0) {
+      fetch(opa, 0, P0{});
+      fetch(opa, 0, P1{});
+    }
+    int ch = 0;
+    for (; ch + 2 <= NC; ch += 2) {
+      step(opa, opb, ch);
+      step(opb, opa, ch + 1);
+    }
+    if (ch < NC) step(opa, opb, ch);
+
+    if (gST != nullptr) {
+      const Lane ln = lane_now();
+      float* dst = gST + static_cast<size_t>(chain) * DK * DV + 16 * jt;
+#pragma unroll
+      for (int m = 0; m < CPW; ++m) {
+        const int cb = R + NB * m;
+        if (cb < NCB) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[(16 * cb + 4 * ln.g + r) * DV + ln.i] = S[m][r];
+        }
+      }
+    }
+  } else {
+    // ---------------- output wave: O_R = (Q.E)_R S + P_R U
+    auto fetch = [&](OO& x, int ch) {
+      const E* rw = reinterpret_cast<const E*>(rec0 + static_cast<size_t>(ch) * rbytes);
+      int l = lane;
+      asm volatile("" : "+v"(l));
+#pragma unroll
+      for (int s = 0; s < NKD; ++s)
+        x.q[s] = *reinterpret_cast<const FD*>(
+            rw + RC::kQ + (static_cast<size_t>(R * NKD + s) * kWave + l) * ND);
+#pragma unroll
+      for (int s = 0; s < NKC; ++s)
+        x.p[s] = *reinterpret_cast<const FC*>(
+            rw + RC::kP + (static_cast<size_t>(R * NKC + s) * kWave + l) * NCK);
+    };
+    E* po0 = go + row0 * DV + 16 * jt;
+    const int rsV = H * DV;
+    auto step = [&](const OO& cur, OO& nxt, int ch, auto tail) {
+      fetch(nxt, min(ch + 1, NC - 1));
+      const int t0 = ch * C;
+      const int nrows = min(C, T - t0);
+      const Lane ln = lane_now();
+      lds_barrier();
+      FD stf[NKD];
+#pragma unroll
+      for (int s = 0; s < NKD; ++s) stf[s] = Src<OpT>{ST, LDK, ln}.template get<KSD>(s * KSD);
+      f32x4 o = zero4();
+#pragma unroll
+      for (int s = 0; s < NKD; ++s) o = mfma<OpT, KSD>(cur.q[s], stf[s], o);
+      lds_barrier();
+      FC utf[NKC];
+#pragma unroll
+      for (int s = 0; s < NKC; ++s) utf[s] = Src<OpT>{UT, LDC, ln}.template get<KSC>(s * KSC);
+      // P is block-lower; its upper blocks are zeros
+      f32x4 pu = zero4();
+#pragma unroll
+      for (int s = 0; s < NKC; ++s) pu = mfma<OpT, KSC>(cur.p[s], utf[s], pu);
+      add4(o, pu);
+      E* po = po0 + static_cast<size_t>(t0) * rsV;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rl = 16 * R + 4 * ln.g + r;
+        if (!decltype(tail)::value || rl < nrows) po[rl * rsV + ln.i] = Ty<OpT>::from_f32(o[r]);
+      }
+    };
+    OO opa, opb;
+    if (NC > 0) fetch(opa, 0);
+    int ch = 0;
+    for (; ch + 2 <= nfull; ch += 2) {
+      step(opa, opb, ch, Full{});
+      step(opb, opa, ch + 1, Full{});
+    }
+    // at most two chunks left: one full and/or the partial last one
+    if (ch < NC) {
+      if (ch < nfull) step(opa, opb, ch, Full{});
+      else step(opa, opb, ch, Tail{});
+      if (ch + 1 < NC) step(opb, opa, ch + 1, Tail{});
     }
   }
 }
