@@ -12,13 +12,18 @@
 // (Parallelizing Linear Transformers with Delta Rule)", with the per-channel
 // decay of section "KDA/Kimi Linear").
 //
-// A workgroup has two waves per 16-row block R of the chunk.  The state
+// A workgroup has three waves per 16-row block R of the chunk.  The state
 // wave of R computes rows R of U and owns state row blocks R, R + C/16, ...:
-// it carries the recurrence (S -> U -> S).  The output wave of R computes
-// rows R of O from the same S and U, off that critical path.  S^T and U^T are
-// exchanged through LDS, two LDS-only barriers per chunk.  Every record
-// operand goes straight from global memory into the registers of the wave
-// that uses it, one chunk ahead.
+// it carries the recurrence (S -> U -> S) and touches only LDS and registers.
+// The output wave of R computes rows R of O from the same S and U (its Q.E
+// and P operands load into its registers one chunk ahead).  The loader wave
+// of R streams the state wave's operands (W_R, the owned rows of (K.E')^T,
+// U~_R of this tile, the decay) two chunks ahead from the record into one of
+// three LDS buffers with direct global-to-LDS loads.  A CU's vector memory
+// path takes about 64 bytes per clock, so the ~60 KB a chunk needs occupy it
+// for most of a chunk; the waves that wait on that path are never the ones
+// the recurrence waits on.  S^T and U^T are exchanged through LDS; two
+// barriers per chunk.
 #pragma once
 
 #include <type_traits>
@@ -30,26 +35,68 @@ namespace kda {
 template <typename OpT, int DK, int C>
 struct SCfg {
   static constexpr int NB = C / 16, NCB = DK / 16;
-  static constexpr int NTH = 2 * kWave * NB;         // state waves, then output waves
+  static constexpr int NTH = 3 * kWave * NB;         // state, output, loader waves
   static constexpr int CPW = (NCB + NB - 1) / NB;    // state row blocks per state wave
   static constexpr int EB = Ty<OpT>::kBytes, PADE = 16 / EB;
-  static constexpr int LDK = DK + PADE, LDC = C + PADE;
+  static constexpr int LDK = DK + PADE, LDC = C + PADE, LDO = 16 + PADE;
   using RC = RecCfg<OpT, DK, C>;
   static constexpr int KSD = RC::KSD, KSC = RC::KSC, NKD = RC::NKD, NKC = RC::NKC;
+  // one LDS operand buffer (byte offsets), laid out as in the record
+  static constexpr int kWR = 16 * DK * EB;           // W rows of one block R
+  static constexpr int kKR = 16 * C * EB;            // (K.E')^T rows of one block cb
+  static constexpr int kUR = 256 * EB;               // one U~ accumulator packet
+  static constexpr int oW = 0, oKG = oW + NB * kWR, oU = oKG + NCB * kKR, oGC = oU + NB * kUR;
+  static constexpr int kBuf = align16(oGC + 4 * DK);
+  // LDS: three operand buffers, S^T, U^T, O staging (one tile per output
+  // wave), as separate arrays so that the compiler can tell that LDS reads of
+  // the last three never wait for the direct loads into the first.
+  static constexpr int kNBuf = 3;
+  static constexpr int kOS = align16(16 * LDO * EB);
+  static constexpr int kLds = kNBuf * kBuf + align16(16 * LDK * EB) + align16(16 * LDC * EB) + NB * kOS;
 };
 
-// One chunk's record operands of a state wave (W_R, U~_R, (K.E')^T rows,
-// decay) and of an output wave (Q.E_R, P_R).
-template <typename OpT, int DK, int C>
-struct StateOps {
-  using Cf = SCfg<OpT, DK, C>;
-  using FD = typename Frag<OpT, Cf::KSD>::T;
-  using FC = typename Frag<OpT, Cf::KSC>::T;
-  FD w[Cf::NKD];
-  FC kg[Cf::CPW][Cf::NKC];
-  typename Acc4<OpT>::Raw ut;
-  float4 gc[Cf::CPW];
-};
+// s_waitcnt immediate that waits until at most n vector memory operations of
+// this wave are in flight (gfx9 encoding: vmcnt in bits 3:0 and 15:14; the
+// export and LDS/scalar counters left at their maxima, i.e. not waited on).
+__host__ __device__ constexpr int vmcnt_only(int n) {
+  return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8);
+}
+
+// Workgroup barrier for a wave whose direct global-to-LDS loads must stay in
+// flight across it (a release fence on LDS would wait for them): its own LDS
+// operations complete, then the barrier; the asm also keeps the compiler from
+// moving memory accesses across.  Pairs with lds_barrier() in other waves.
+__device__ __forceinline__ void barrier_keep_fills() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+using lds_void = __attribute__((address_space(3))) void;
+using gbl_void = const __attribute__((address_space(1))) void;
+
+// BYTES contiguous bytes, global -> LDS, by one wave: 16-byte lanes when the
+// size is a multiple of 1 KiB, else 4-byte lanes (the last pass masked, lane 0
+// always active).  fill_insts: the number of load instructions it issues.
+template <int BYTES>
+__host__ __device__ constexpr int fill_insts() {
+  return BYTES % 1024 == 0 ? BYTES / 1024 : (BYTES + 255) / 256;
+}
+template <int BYTES>
+__device__ __forceinline__ void lds_fill(char* dst, const char* src, int lane) {
+  static_assert(BYTES % 4 == 0, "4-byte granules");
+  if constexpr (BYTES % 1024 == 0) {
+#pragma unroll
+    for (int i = 0; i < BYTES / 1024; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_void*)(src + 1024 * i + 16 * lane),
+                                       (lds_void*)(dst + 1024 * i), 16, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < (BYTES + 255) / 256; ++i)
+      if ((BYTES % 256 == 0) || 256 * i + 4 * lane < BYTES)
+        __builtin_amdgcn_global_load_lds((gbl_void*)(src + 256 * i + 4 * lane),
+                                         (lds_void*)(dst + 256 * i), 4, 0, 0);
+  }
+}
+
 template <typename OpT, int DK, int C>
 struct OutOps {
   using Cf = SCfg<OpT, DK, C>;
@@ -60,27 +107,29 @@ struct OutOps {
 };
 
 template <typename OpT, int DK, int C>
-__global__ void __launch_bounds__(2 * kWave * (C / 16))
+__global__ void __launch_bounds__(3 * kWave * (C / 16))
 kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float* gST,
                 const char* __restrict__ gws, int B, int T, int H, int DV) {
   using Cf = SCfg<OpT, DK, C>;
   using RC = typename Cf::RC;
   using E = typename Ty<OpT>::Elem;
-  using SO = StateOps<OpT, DK, C>;
   using OO = OutOps<OpT, DK, C>;
-  using FD = typename SO::FD;
-  using FC = typename SO::FC;
+  using FD = typename OO::FD;
+  using FC = typename OO::FC;
   constexpr int NB = Cf::NB, NCB = Cf::NCB, CPW = Cf::CPW, LDK = Cf::LDK, LDC = Cf::LDC;
   constexpr int KSD = Cf::KSD, KSC = Cf::KSC, NKD = Cf::NKD, NKC = Cf::NKC;
   constexpr int ND = KSD / 4, NCK = KSC / 4;   // elements per lane of one packet
+  static_assert(Cf::kLds <= kMaxLds, "scan LDS plan exceeds 160 KiB");
 
+  __shared__ __attribute__((aligned(16))) char opbuf[Cf::kNBuf * Cf::kBuf];
   __shared__ __attribute__((aligned(16))) E ST[16 * LDK];   // S^T of the tile
   __shared__ __attribute__((aligned(16))) E UT[16 * LDC];   // U^T of the tile
+  __shared__ __attribute__((aligned(16))) E OSall[NB * Cf::kOS / Cf::EB];
 
   const int lane = threadIdx.x % kWave;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int R = wv % NB;
-  const bool state_wave = wv < NB;
+  const int role = wv / NB;   // 0 state, 1 output, 2 loader
 
   // Workgroup -> (chain, column tile); all tiles of a chain on one XCD so the
   // chain's records are read from HBM once and then hit that XCD's L2.
@@ -95,14 +144,10 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
   const size_t row0 = static_cast<size_t>(b) * T * H + h;
   const size_t rbytes = RC::bytes(DV);
   const char* rec0 = gws + static_cast<size_t>(chain) * NC * rbytes;
-  using Full = std::integral_constant<bool, false>;
-  using Tail = std::integral_constant<bool, true>;
-  // Every chunk issues the same memory operations (the last one re-fetches
-  // itself; only the partial last chunk masks its stores), so the compiler's
-  // wait counts stay exact instead of draining all outstanding traffic.
+  auto buf = [&](int ch) { return opbuf + (ch % Cf::kNBuf) * Cf::kBuf; };
 
-  if (state_wave) {
-    // ---------------- state wave: S -> U -> S
+  if (role == 0) {
+    // ---------------- state wave: S -> U -> S, LDS and registers only
     f32x4 S[CPW];
     {
       const Lane ln = lane_now();
@@ -115,96 +160,54 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
 #pragma unroll
           for (int r = 0; r < 4; ++r) S[m][r] = src[(16 * cb + 4 * ln.g + r) * DV + ln.i];
         }
-        // Land the loads here: a load still in flight at the loop entry makes
-        // every chunk wait for all outstanding memory traffic.
-        asm volatile("" : "+v"(S[m][0]), "+v"(S[m][1]), "+v"(S[m][2]), "+v"(S[m][3]));
       }
     }
-    // The next chunk's operands in two parts (a CU's vector memory path moves
-    // about 64 bytes per clock; one wave issuing all at once stalls on issue).
-    auto fetch = [&](SO& x, int ch, auto part) {
-      const char* rc = rec0 + static_cast<size_t>(ch) * rbytes;
-      const E* rw = reinterpret_cast<const E*>(rc);
-      int l = lane;
-      asm volatile("" : "+v"(l));
-      if constexpr (decltype(part)::value == 0) {
-#pragma unroll
-        for (int s = 0; s < NKD; ++s)
-          x.w[s] = *reinterpret_cast<const FD*>(
-              rw + RC::kW + (static_cast<size_t>(R * NKD + s) * kWave + l) * ND);
-        x.ut = Acc4<OpT>::load(reinterpret_cast<const E*>(rc + RC::kUByte) +
-                               (static_cast<size_t>(R * NJV + jt) * kWave + l) * 4);
-      } else {
-#pragma unroll
-        for (int m = 0; m < CPW; ++m) {
-          const int cb = min(R + NB * m, NCB - 1);   // blocks past dk: loaded, never used
-#pragma unroll
-          for (int s = 0; s < NKC; ++s)
-            x.kg[m][s] = *reinterpret_cast<const FC*>(
-                rw + RC::kKG + (static_cast<size_t>(cb * NKC + s) * kWave + l) * NCK);
-          x.gc[m] = *reinterpret_cast<const float4*>(rc + RC::kGcByte + 4 * (16 * cb + 4 * (l / 16)));
-        }
-      }
-    };
-    using P0 = std::integral_constant<int, 0>;
-    using P1 = std::integral_constant<int, 1>;
-    auto step = [&](const SO& cur, SO& nxt, int ch) {
-      const int chn = min(ch + 1, NC - 1);
-      fetch(nxt, chn, P0{});
-      __builtin_amdgcn_sched_barrier(0);
+    for (int ch = 0; ch < NC; ++ch) {
       const Lane ln = lane_now();
+      const char* ob = buf(ch);
       // publish this wave's state rows as S^T (operand type)
 #pragma unroll
       for (int m = 0; m < CPW; ++m) {
         const int cb = R + NB * m;
         if (cb < NCB) Acc4<OpT>::store(ST + ln.i * LDK + 16 * cb + 4 * ln.g, S[m]);
       }
-      lds_barrier();
+      lds_barrier();   // S^T published; this chunk's operand buffer is filled
       FD stf[NKD];
 #pragma unroll
       for (int s = 0; s < NKD; ++s) stf[s] = Src<OpT>{ST, LDK, ln}.template get<KSD>(s * KSD);
       // U_R = U~_R - W_R S, published as U^T[n][16R + 4g + r]
+      const E* wr = reinterpret_cast<const E*>(ob + Cf::oW + R * Cf::kWR);
       f32x4 x = zero4();
 #pragma unroll
-      for (int s = 0; s < NKD; ++s) x = mfma<OpT, KSD>(cur.w[s], stf[s], x);
-      f32x4 u = Acc4<OpT>::cvt(cur.ut);
+      for (int s = 0; s < NKD; ++s)
+        x = mfma<OpT, KSD>(*reinterpret_cast<const FD*>(wr + (s * kWave + lane) * ND), stf[s], x);
+      f32x4 u = Acc4<OpT>::cvt(
+          Acc4<OpT>::load(reinterpret_cast<const E*>(ob + Cf::oU + R * Cf::kUR) + 4 * lane));
 #pragma unroll
       for (int r = 0; r < 4; ++r) u[r] -= x[r];
       Acc4<OpT>::store(UT + ln.i * LDC + 16 * R + 4 * ln.g, u);
       lds_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      fetch(nxt, chn, P1{});
-      __builtin_amdgcn_sched_barrier(0);
       FC utf[NKC];
 #pragma unroll
       for (int s = 0; s < NKC; ++s) utf[s] = Src<OpT>{UT, LDC, ln}.template get<KSC>(s * KSC);
       // S <- Diag(E_{C-1}) S + (K.E')^T U for this wave's row blocks
 #pragma unroll
       for (int m = 0; m < CPW; ++m) {
-        if (R + NB * m < NCB) {
+        const int cb = R + NB * m;
+        if (cb < NCB) {
+          const E* kr = reinterpret_cast<const E*>(ob + Cf::oKG + cb * Cf::kKR);
           f32x4 acc = zero4();
 #pragma unroll
-          for (int s = 0; s < NKC; ++s) acc = mfma<OpT, KSC>(cur.kg[m][s], utf[s], acc);
-          const float4 gc = cur.gc[m];
+          for (int s = 0; s < NKC; ++s)
+            acc = mfma<OpT, KSC>(*reinterpret_cast<const FC*>(kr + (s * kWave + lane) * NCK), utf[s], acc);
+          const float4 gc = *reinterpret_cast<const float4*>(ob + Cf::oGC + 4 * (16 * cb + 4 * ln.g));
           S[m][0] = gc.x * S[m][0] + acc[0];
           S[m][1] = gc.y * S[m][1] + acc[1];
           S[m][2] = gc.z * S[m][2] + acc[2];
           S[m][3] = gc.w * S[m][3] + acc[3];
         }
       }
-    };
-    // Two operand sets in alternation (no register copies between chunks).
-    SO opa, opb;
-    if (NC > 0) {
-      fetch(opa, 0, P0{});
-      fetch(opa, 0, P1{});
     }
-    int ch = 0;
-    for (; ch + 2 <= NC; ch += 2) {
-      step(opa, opb, ch);
-      step(opb, opa, ch + 1);
-    }
-    if (ch < NC) step(opa, opb, ch);
 
     if (gST != nullptr) {
       const Lane ln = lane_now();
@@ -218,7 +221,7 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
         }
       }
     }
-  } else {
+  } else if (role == 1) {
     // ---------------- output wave: O_R = (Q.E)_R S + P_R U
     auto fetch = [&](OO& x, int ch) {
       const E* rw = reinterpret_cast<const E*>(rec0 + static_cast<size_t>(ch) * rbytes);
@@ -233,21 +236,25 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
         x.p[s] = *reinterpret_cast<const FC*>(
             rw + RC::kP + (static_cast<size_t>(R * NKC + s) * kWave + l) * NCK);
     };
+    E* OS = OSall + R * (Cf::kOS / Cf::EB);
     E* po0 = go + row0 * DV + 16 * jt;
     const int rsV = H * DV;
+    // Every chunk issues the same memory operations (the last one re-fetches
+    // itself; only the partial last chunk masks its store), so the compiler's
+    // wait counts stay exact instead of draining all outstanding traffic.
     auto step = [&](const OO& cur, OO& nxt, int ch, auto tail) {
-      fetch(nxt, min(ch + 1, NC - 1));
       const int t0 = ch * C;
       const int nrows = min(C, T - t0);
       const Lane ln = lane_now();
-      lds_barrier();
+      lds_barrier();   // S^T of this chunk published
+      fetch(nxt, min(ch + 1, NC - 1));
       FD stf[NKD];
 #pragma unroll
       for (int s = 0; s < NKD; ++s) stf[s] = Src<OpT>{ST, LDK, ln}.template get<KSD>(s * KSD);
       f32x4 o = zero4();
 #pragma unroll
       for (int s = 0; s < NKD; ++s) o = mfma<OpT, KSD>(cur.q[s], stf[s], o);
-      lds_barrier();
+      lds_barrier();   // U^T published
       FC utf[NKC];
 #pragma unroll
       for (int s = 0; s < NKC; ++s) utf[s] = Src<OpT>{UT, LDC, ln}.template get<KSC>(s * KSC);
@@ -256,13 +263,18 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
 #pragma unroll
       for (int s = 0; s < NKC; ++s) pu = mfma<OpT, KSC>(cur.p[s], utf[s], pu);
       add4(o, pu);
-      E* po = po0 + static_cast<size_t>(t0) * rsV;
+      // O tile through LDS: one 4-element row segment per lane, one store
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = 16 * R + 4 * ln.g + r;
-        if (!decltype(tail)::value || rl < nrows) po[rl * rsV + ln.i] = Ty<OpT>::from_f32(o[r]);
-      }
+      for (int r = 0; r < 4; ++r) OS[(4 * ln.g + r) * Cf::LDO + ln.i] = Ty<OpT>::from_f32(o[r]);
+      wave_fence();
+      const int orow = lane / 4, ocol = 4 * (lane % 4);
+      const typename Quad<OpT>::T ov = *reinterpret_cast<const typename Quad<OpT>::T*>(OS + orow * Cf::LDO + ocol);
+      const int rl = 16 * R + orow;
+      if (!decltype(tail)::value || rl < nrows)
+        *reinterpret_cast<typename Quad<OpT>::T*>(po0 + static_cast<size_t>(t0 + rl) * rsV + ocol) = ov;
     };
+    using Full = std::integral_constant<bool, false>;
+    using Tail = std::integral_constant<bool, true>;
     OO opa, opb;
     if (NC > 0) fetch(opa, 0);
     int ch = 0;
@@ -276,6 +288,51 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
       else step(opa, opb, ch, Tail{});
       if (ch + 1 < NC) step(opb, opa, ch + 1, Tail{});
     }
+  } else {
+    // ---------------- loader wave: state-wave operands, two chunks ahead.
+    // Operands of state wave R for chunk ch go into buffer ch % 3.  Blocks
+    // past dk are clamped (the same bytes written twice, never read).
+    // Two halves, issued in the two halves of a chunk so that the issue
+    // stalls of this wave never hold up a barrier for long.
+    auto fill_a = [&](int ch) {
+      const char* rc = rec0 + static_cast<size_t>(ch) * rbytes;
+      char* ob = buf(ch);
+      lds_fill<Cf::kWR>(ob + Cf::oW + R * Cf::kWR, rc + RC::kW * Cf::EB + R * Cf::kWR, lane);
+      lds_fill<4 * DK / NB>(ob + Cf::oGC + R * (4 * DK / NB), rc + RC::kGcByte + R * (4 * DK / NB), lane);
+    };
+    auto fill_b = [&](int ch) {
+      const char* rc = rec0 + static_cast<size_t>(ch) * rbytes;
+      char* ob = buf(ch);
+#pragma unroll
+      for (int m = 0; m < CPW; ++m) {
+        const int cb = min(R + NB * m, NCB - 1);
+        lds_fill<Cf::kKR>(ob + Cf::oKG + cb * Cf::kKR, rc + RC::kKG * Cf::EB + cb * Cf::kKR, lane);
+      }
+      lds_fill<Cf::kUR>(ob + Cf::oU + R * Cf::kUR,
+                        rc + RC::kUByte + static_cast<size_t>(R * NJV + jt) * Cf::kUR, lane);
+    };
+    // This wave issues nothing but fills, kFill instructions per chunk: at
+    // the end of chunk ch, at most kFill in flight means the fills for ch+1
+    // (issued one chunk earlier) have landed in LDS.
+    constexpr int kFill = fill_insts<Cf::kWR>() + CPW * fill_insts<Cf::kKR>() +
+                          fill_insts<Cf::kUR>() + fill_insts<4 * DK / NB>();
+    static_assert(kFill < 63, "vmcnt range");
+    if (NC > 0) {
+      fill_a(0);
+      fill_b(0);
+      fill_a(min(1, NC - 1));
+      fill_b(min(1, NC - 1));
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(kFill));   // buffer 0 ready
+    }
+    for (int ch = 0; ch < NC; ++ch) {
+      const int chf = min(ch + 2, NC - 1);
+      barrier_keep_fills();   // chunk ch starts; buffer (ch + 2) % 3 is free
+      fill_a(chf);
+      barrier_keep_fills();
+      fill_b(chf);
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(kFill));   // buffer ch + 1 ready
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));   // no fill left in flight
   }
 }
 
@@ -284,7 +341,13 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
 // columns), then the scan.
 // ----------------------------------------------------------------------------
 template <typename OpT, int DK, int C>
+constexpr bool scan_fits() {
+  return SCfg<OpT, DK, C>::kLds <= kMaxLds;
+}
+
+template <typename OpT, int DK, int C>
 bool split_fits(int dv) {
+  if (!scan_fits<OpT, DK, C>()) return false;
   switch (dv) {
     case 16: return fits<OpT, DK, C, 16>();
     case 32: return fits<OpT, DK, C, 32>();
@@ -343,11 +406,15 @@ hipError_t launch_split(const PrefillArgs& a) {
     case 128: e = launch_prep<OpT, DK, C, 128>(a); break;
   }
   if (e != hipSuccess) return e;
-  const long chains = static_cast<long>(a.B) * a.H;
-  dim3 grid(static_cast<unsigned>(chains * (a.dv / 16)));
-  hipLaunchKernelGGL((kda_scan_kernel<OpT, DK, C>), grid, dim3(SCfg<OpT, DK, C>::NTH), 0,
-                     static_cast<hipStream_t>(a.stream), a.S0, static_cast<E*>(a.o), a.S_T,
-                     static_cast<const char*>(a.workspace), a.B, a.T, a.H, a.dv);
+  if constexpr (!scan_fits<OpT, DK, C>()) {
+    return hipErrorInvalidValue;
+  } else {
+    const long chains = static_cast<long>(a.B) * a.H;
+    dim3 grid(static_cast<unsigned>(chains * (a.dv / 16)));
+    hipLaunchKernelGGL((kda_scan_kernel<OpT, DK, C>), grid, dim3(SCfg<OpT, DK, C>::NTH), 0,
+                       static_cast<hipStream_t>(a.stream), a.S0, static_cast<E*>(a.o), a.S_T,
+                       static_cast<const char*>(a.workspace), a.B, a.T, a.H, a.dv);
+  }
   return hipGetLastError();
 }
 
