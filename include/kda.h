@@ -77,9 +77,18 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 
 /*
  * kda_prefill_workspace_bytes — bytes of device workspace kda_prefill_chunked
- * needs for these sizes.  Returns 0 when no workspace is needed (the current
- * kernels keep every intermediate on chip) and (size_t)-1 when the sizes are
- * not supported.
+ * needs for these sizes, or (size_t)-1 when the sizes are not supported.
+ *
+ * The library picks one of two paths from the sizes alone (the same choice in
+ * this query and in the call):
+ *   - few chains (B*H <= 127, when the chunk kernels fit on chip for these
+ *     dk, dv, C, dt): a chunk-parallel kernel first writes one record per
+ *     chunk to the workspace (the state-free chunk quantities W, Q.E,
+ *     (K.E')^T, P, the chunk decay and Y diag(beta) V), then a scan kernel
+ *     walks the chunks in order.  Workspace = B*H*ceil(T/C) records of
+ *       round_up((3*C*dk + C*C + C*dv) * sizeof(dt) + 4*dk, 256) bytes;
+ *   - otherwise one fused kernel per (chain, value-column slab) keeps every
+ *     intermediate on chip, and the query returns 0.
  */
 size_t kda_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int C,
                                    kda_dtype dt);
@@ -102,15 +111,20 @@ size_t kda_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int C,
  *   C                               chunk length in {16, 32, 64}; a
  *                                   performance knob only: the result does not
  *                                   depend on C beyond rounding
- *   workspace, workspace_bytes      caller-owned scratch of at least
- *                                   kda_prefill_workspace_bytes(...) bytes
- *                                   (may be NULL when that is 0)
+ *   workspace, workspace_bytes      caller-owned device scratch of at least
+ *                                   kda_prefill_workspace_bytes(...) bytes,
+ *                                   16-byte aligned, overlapping no other
+ *                                   argument (may be NULL when the query
+ *                                   returns 0).  Its contents are overwritten
+ *                                   and carry nothing between calls; two
+ *                                   calls in flight at once need two
+ *                                   workspaces.
  *
  * Any T >= 0 is accepted; a tail shorter than C is handled as identity
  * padding (gate 1, strength 0), and T = 0 copies S0 (or zeros) to S_T.
  * o may not overlap any input.  Errors: KDA_ERR_NULL, KDA_ERR_SHAPE,
- * KDA_ERR_UNSUPPORTED, KDA_ERR_ALIGN, KDA_ERR_ALIAS, KDA_ERR_WORKSPACE,
- * KDA_ERR_DEVICE, KDA_ERR_HIP.
+ * KDA_ERR_UNSUPPORTED, KDA_ERR_ALIGN, KDA_ERR_ALIAS, KDA_ERR_WORKSPACE (NULL
+ * or smaller than the query when one is needed), KDA_ERR_DEVICE, KDA_ERR_HIP.
  */
 kda_status kda_prefill_chunked(const void* q, const void* k, const void* v,
                                const float* alpha, const float* beta,
