@@ -489,7 +489,7 @@ struct PCfg {
   static constexpr int kKT = align16(DK * LDC * EB);
   static constexpr int kKB = align16(imax(DK, DVT) * LDC * EB);
   static constexpr int kTT = align16(C * LDT * 4);
-  static constexpr int kZB = align16(imax(NB - 1, 1) * 16 * LDZ * 4);
+  static constexpr int kZB = align16(imax(NB, 1) * 16 * LDZ * 4);
   static constexpr int kYF = align16(imax(NB * (NB - 1) / 2, 1) * 16 * LDZ * 4);
   static constexpr int kPP = align16(C * LDC * EB);
   static constexpr int kBT = align16(NB * DK * 4);
@@ -946,6 +946,65 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       const int R = x / 256, r = (x % 256) / 16, j = x % 16;
       Yb[(16 * R + r) * LDC + 16 * R + j] = Ty<OpT>::from_f32(TT[(16 * R + r) * LDT + 16 * R + j]);
     }
+    if constexpr (NB == 4) {
+      // Four blocks: two levels instead of three.  Level 1: Y10 and Y32, the
+      // off-diagonal blocks inside each half.  Level 2: the lower-left half
+      // block  Y[23][01] = -Y[23][23] (L[23][01] Y[01][01]),  one wave per
+      // block column c: M_Rc = L_R0 Y_0c + L_R1 Y_1c (R = 2, 3), then
+      // Y_2c = -Y22 M_2c,  Y_3c = -(Y32 M_2c + Y33 M_3c).
+      const Lane ln = lane_now();
+      auto ydiag = [&](int J) { return SrcColF32{TT + 16 * J * LDT + 16 * J, LDT, ln}; };
+      auto lsrc = [&](int R, int J) { return Src<float>{TT + 16 * R * LDT + 16 * J, LDT, ln}; };
+      auto put_y = [&](int R, int I, const f32x4& y, bool keep_f32) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int rl = 4 * ln.g + rr;
+          if (keep_f32) YF[yf_block(R, I) * 16 * LDZ + rl * LDZ + ln.i] = -y[rr];
+          Yb[(16 * R + rl) * LDC + 16 * I + ln.i] = Ty<OpT>::from_f32(-y[rr]);
+        }
+      };
+      if (wave < 2) {
+        const int I = 2 * wave, R = I + 1;   // (1, 0) or (3, 2)
+        f32x4 z = zero4();
+        mma_f32(z, 0, 16, lsrc(R, I), ydiag(I));
+        float* zb = ZB + wave * 16 * LDZ;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) zb[(4 * ln.g + rr) * LDZ + ln.i] = z[rr];
+        wave_fence();
+        f32x4 y = zero4();
+        mma_f32(y, 0, 16, lsrc(R, R), SrcColF32{zb, LDZ, ln});
+        put_y(R, I, y, true);
+      }
+      lds_barrier();
+      if (wave < 2) {
+        const int c = wave;
+        // Y_1c: Y10 (fp32 copy) for c = 0, Y11 (diagonal) for c = 1; Y_0c = 0 for c = 1
+        const SrcColF32 y1c = (c == 0) ? SrcColF32{YF + yf_block(1, 0) * 16 * LDZ, LDZ, ln} : ydiag(1);
+        float* m2 = ZB + (2 * c) * 16 * LDZ;
+        float* m3 = ZB + (2 * c + 1) * 16 * LDZ;
+        f32x4 a2 = zero4(), a3 = zero4();
+        if (c == 0) {
+          mma_f32(a2, 0, 16, lsrc(2, 0), ydiag(0));
+          mma_f32(a3, 0, 16, lsrc(3, 0), ydiag(0));
+        }
+        mma_f32(a2, 0, 16, lsrc(2, 1), y1c);
+        mma_f32(a3, 0, 16, lsrc(3, 1), y1c);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          m2[(4 * ln.g + rr) * LDZ + ln.i] = a2[rr];
+          m3[(4 * ln.g + rr) * LDZ + ln.i] = a3[rr];
+        }
+        wave_fence();
+        f32x4 y2 = zero4(), y3 = zero4();
+        mma_f32(y2, 0, 16, lsrc(2, 2), SrcColF32{m2, LDZ, ln});
+        // Y32 sits in YF (-Y32 stored as Y32 there: YF holds the blocks of Y)
+        mma_f32(y3, 0, 16, Src<float>{YF + yf_block(3, 2) * 16 * LDZ, LDZ, ln}, SrcColF32{m2, LDZ, ln});
+        mma_f32(y3, 0, 16, lsrc(3, 3), SrcColF32{m3, LDZ, ln});
+        put_y(2, c, y2, false);
+        put_y(3, c, y3, false);
+      }
+      lds_barrier();
+    } else {
     for (int R = 1; R < NB; ++R) {
       const Lane ln = lane_now();
       for (int I = wave; I < R; I += NW) {
@@ -973,6 +1032,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       lds_barrier();
     }
     if (NB == 1) lds_barrier();
+    }
 
     // Y as a matrix-core operand (a copy in the operand type).
     auto ysrc = [&](int R, const Lane& ln) { return Src<OpT>{Yb + 16 * R * LDC, LDC, ln}; };
