@@ -780,12 +780,21 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         // unsafe block: its diagonal tile is then done exactly on the VALUs)
         float pre[4], suf[4], rbt[4];
         bool unsafe = false;
+        // block decays of all blocks for this channel quad (16-byte reads),
+        // multiplied in under selects instead of loops of divergent length
+        float4 btq[NB];
+#pragma unroll
+        for (int JJ = 0; JJ < NB; ++JJ) btq[JJ] = *reinterpret_cast<const float4*>(sBT + JJ * DK + c);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           pre[x] = 1.f;
           suf[x] = 1.f;
-          for (int JJ = 0; JJ < J; ++JJ) pre[x] *= sBT[JJ * DK + c + x];
-          for (int JJ = J + 1; JJ < NB; ++JJ) suf[x] *= sBT[JJ * DK + c + x];
+#pragma unroll
+          for (int JJ = 0; JJ < NB; ++JJ) {
+            const float b = x == 0 ? btq[JJ].x : x == 1 ? btq[JJ].y : x == 2 ? btq[JJ].z : btq[JJ].w;
+            pre[x] *= (JJ < J) ? b : 1.f;
+            suf[x] *= (JJ > J) ? b : 1.f;
+          }
           const bool safe = bt[it][x] >= kUnsafeBlockDecay;
           unsafe |= !safe;
           // 1/F_i = H_i / BT_J: one reciprocal per channel instead of per row
