@@ -213,6 +213,13 @@ __device__ __forceinline__ void wave_fence() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
 }
+// s_waitcnt immediate that waits until at most n vector memory operations of
+// this wave are in flight (gfx9 encoding: vmcnt in bits 3:0 and 15:14; the
+// export and LDS/scalar counters left at their maxima, i.e. not waited on).
+__host__ __device__ constexpr int vmcnt_only(int n) {
+  return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8);
+}
+
 // Workgroup barrier for LDS only: orders LDS accesses across the waves
 // without waiting for outstanding global loads or stores (__syncthreads()
 // would drain both, which throws away the prefetch of the next chunk and
@@ -688,8 +695,8 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       }
     }
   };
-  auto fetch_beta = [&](int tn) {
-    if (tid < C) gbe = gbeta[row0 + static_cast<size_t>(min(tn + tid, T - 1)) * H];
+  auto fetch_beta = [&](int tn) {   // every thread loads (only tid < C keep it): no branch
+    gbe = gbeta[row0 + static_cast<size_t>(min(tn + tid % C, T - 1)) * H];
   };
 
   if (ch_begin < ch_end) {
@@ -697,13 +704,18 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     fetch_values(ch_begin * C);
     fetch_beta(ch_begin * C);
   }
+  // Land every load issued so far (the first chunk needs them at once).  A
+  // load still in flight at the loop entry would make the compiler assume, on
+  // every chunk, that the registers it fills were loaded last, and wait for
+  // all outstanding memory traffic (the previous chunk's stores included).
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   for (int ch = ch_begin; ch < ch_end; ++ch) {
     const int t0 = ch * C;
     const bool more = ch + 1 < ch_end;
     const bool full = t0 + C <= T;   // no padding rows in this chunk
     // ================= G1: pad the fetched chunk, within-block cumulative gates
     if (tid < C) sBE[tid] = (t0 + tid < T) ? gbe : 0.f;
-    if (more) fetch_beta(t0 + C);
+    fetch_beta(more ? t0 + C : t0);   // unconditional: uniform memory-op counts
     if (tid < NB) sFL[tid] = 0;
     // Per gate item: quarter products of alpha, combined across the four
     // quarters of the block (lanes of one group of four) into the block total
@@ -842,7 +854,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         }
       }
     }
-    if (more) fetch_gates(t0 + C);
+    fetch_gates(more ? t0 + C : t0);
     lds_barrier();
 
     // ================= AP + SD: gated K K^T (-> L in TT) and Q K^T (-> P) tiles.
@@ -949,7 +961,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
                            b3 * vec_elem<OpT>(gvv[it][3], x));
       }
     }
-    if (more) fetch_values(t0 + C);
+    fetch_values(more ? t0 + C : t0);
     // diagonal blocks of Y into the operand-type copy
     for (int x = tid; x < NB * 256; x += NTH) {
       const int R = x / 256, r = (x % 256) / 16, j = x % 16;

@@ -55,13 +55,6 @@ struct SCfg {
   static constexpr int kLds = kNBuf * kBuf + align16(16 * LDK * EB) + align16(16 * LDC * EB) + NB * kOS;
 };
 
-// s_waitcnt immediate that waits until at most n vector memory operations of
-// this wave are in flight (gfx9 encoding: vmcnt in bits 3:0 and 15:14; the
-// export and LDS/scalar counters left at their maxima, i.e. not waited on).
-__host__ __device__ constexpr int vmcnt_only(int n) {
-  return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8);
-}
-
 // Workgroup barrier for a wave whose direct global-to-LDS loads must stay in
 // flight across it (a release fence on LDS would wait for them): its own LDS
 // operations complete, then the barrier; the asm also keeps the compiler from
