@@ -423,16 +423,25 @@ struct RecCfg {
 
 // Padded LDS matrix (row stride ld) -> A packets of width KS, 16-byte (or
 // smaller) vectors; `blocks` 16-row blocks, `nks` K steps.
-template <typename OpT, int KS>
+// When the packet count is a multiple of the thread count every thread
+// issues the same, compile-time number of stores (no loop, no branch), so the
+// compiler can count the memory operations in flight exactly.
+template <typename OpT, int KS, int BLOCKS, int NKS, int NTH>
 __device__ __forceinline__ void copy_packets(typename Ty<OpT>::Elem* dst,
-                                             const typename Ty<OpT>::Elem* src, int blocks,
-                                             int nks, int ld, int tid, int nth) {
+                                             const typename Ty<OpT>::Elem* src, int ld, int tid) {
   using F = Frag<OpT, KS>;
   using V = typename F::T;
-  for (int x = tid; x < blocks * nks * 64; x += nth) {
-    const int l = x % 64, bs = x / 64, blk = bs / nks, s = bs % nks;
+  constexpr int kTotal = BLOCKS * NKS * 64;
+  auto one = [&](int x) {
+    const int l = x % 64, bs = x / 64, blk = bs / NKS, s = bs % NKS;
     const typename Ty<OpT>::Elem* a = src + (16 * blk + l % 16) * ld + s * KS + F::N * (l / 16);
     *reinterpret_cast<V*>(dst + static_cast<size_t>(x) * F::N) = *reinterpret_cast<const V*>(a);
+  };
+  if constexpr (kTotal % NTH == 0) {
+#pragma unroll
+    for (int k = 0; k < kTotal / NTH; ++k) one(tid + NTH * k);
+  } else {
+    for (int x = tid; x < kTotal; x += NTH) one(x);
   }
 }
 
@@ -1104,13 +1113,17 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       using RC = RecCfg<OpT, DK, C>;
       char* rec = gws + (static_cast<size_t>(chain) * NC + ch) * RC::bytes(DV);
       E* rw = reinterpret_cast<E*>(rec);
-      copy_packets<OpT, RC::KSD>(rw + RC::kW, Wm, NB, RC::NKD, LDK, tid, NTH);
-      copy_packets<OpT, RC::KSD>(rw + RC::kQ, Qr, NB, RC::NKD, LDK, tid, NTH);
-      copy_packets<OpT, RC::KSC>(rw + RC::kKG, KgT, Cf::NCB, RC::NKC, LDC, tid, NTH);
-      copy_packets<OpT, RC::KSC>(rw + RC::kP, PP, NB, RC::NKC, LDC, tid, NTH);
-      if (tid < DK / 4)
-        reinterpret_cast<float4*>(rec + RC::kGcByte)[tid] = reinterpret_cast<const float4*>(sGC)[tid];
-      if (UM::active(wave)) {
+      copy_packets<OpT, RC::KSD, NB, RC::NKD, NTH>(rw + RC::kW, Wm, LDK, tid);
+      copy_packets<OpT, RC::KSD, NB, RC::NKD, NTH>(rw + RC::kQ, Qr, LDK, tid);
+      copy_packets<OpT, RC::KSC, Cf::NCB, RC::NKC, NTH>(rw + RC::kKG, KgT, LDC, tid);
+      copy_packets<OpT, RC::KSC, NB, RC::NKC, NTH>(rw + RC::kP, PP, LDC, tid);
+      {
+        // every thread stores (threads past the decay vector repeat its last
+        // 16 bytes): one store per thread, no branch
+        const int v = min(tid, DK / 4 - 1);
+        reinterpret_cast<float4*>(rec + RC::kGcByte)[v] = reinterpret_cast<const float4*>(sGC)[v];
+      }
+      if (UM::WR * UM::WC == NW || UM::active(wave)) {
         const int lane = tid % kWave;
         E* ru = reinterpret_cast<E*>(rec + RC::kUByte);
 #pragma unroll
