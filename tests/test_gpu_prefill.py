@@ -112,6 +112,7 @@ def test_empty_sequence_copies_state():
     (16, 16, torch.float32, 16), (32, 64, torch.float32, 32), (64, 16, torch.float32, 32),
     (128, 32, torch.float32, 32), (16, 128, torch.bfloat16, 16), (32, 32, torch.bfloat16, 64),
     (64, 128, torch.bfloat16, 64), (128, 64, torch.bfloat16, 32), (128, 16, torch.bfloat16, 64),
+    (16, 64, torch.bfloat16, 64), (16, 16, torch.float32, 64),
 ])
 def test_head_dims(dk, dv, dtype, C):
     g = torch.Generator().manual_seed(dk * 1000 + dv)
@@ -194,6 +195,17 @@ def test_split_and_fused_paths_agree(C):
     for o, S in ((o_big[3:4], S_big[3:4]), (o_few, S_few)):
         assert rel(f64(o), o_ref) < 2e-2 and rel(f64(S), S_ref) < 2e-2
     assert rel(f64(o_big[3:4]), f64(o_few)) < 1e-2
+
+
+def test_prep_chunk_runs_ragged():
+    """Split path with several chunks per prep workgroup: 8 chains x 101
+    chunks gives runs of 4 chunks, the last run of each chain holds one chunk,
+    and the last chunk holds 23 of its 64 rows."""
+    spec = wl.PREFILL["prefill_h16_t4k"]
+    T = 64 * 100 + 23
+    inp = wl.make_prefill_inputs(spec, T=T, H=8)
+    assert kda().prefill_workspace_bytes(1, T, 8, 128, 128, 64) > 0   # split path
+    check(inp, 64, label="prep runs, ragged")
 
 
 def test_split_resume_and_in_place_state():
