@@ -801,21 +801,25 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         // unsafe block: its diagonal tile is then done exactly on the VALUs)
         float pre[4], suf[4], rbt[4];
         bool unsafe = false;
-        // block decays of all blocks for this channel quad (16-byte reads),
-        // multiplied in under selects instead of loops of divergent length
-        float4 btq[NB];
-#pragma unroll
-        for (int JJ = 0; JJ < NB; ++JJ) btq[JJ] = *reinterpret_cast<const float4*>(sBT + JJ * DK + c);
+        // decay of the blocks before and after J for this channel quad.  With
+        // dk >= 64 all items of a wave share J, so the loops run on the scalar
+        // unit with no divergence and only the needed products on the VALUs.
+        const int Ju = (DK >= 64 && Cf::NGI % NTH == 0) ? __builtin_amdgcn_readfirstlane(J) : J;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           pre[x] = 1.f;
           suf[x] = 1.f;
+        }
+        for (int JJ = 0; JJ < Ju; ++JJ) {
+          const float4 b = *reinterpret_cast<const float4*>(sBT + JJ * DK + c);
+          pre[0] *= b.x; pre[1] *= b.y; pre[2] *= b.z; pre[3] *= b.w;
+        }
+        for (int JJ = Ju + 1; JJ < NB; ++JJ) {
+          const float4 b = *reinterpret_cast<const float4*>(sBT + JJ * DK + c);
+          suf[0] *= b.x; suf[1] *= b.y; suf[2] *= b.z; suf[3] *= b.w;
+        }
 #pragma unroll
-          for (int JJ = 0; JJ < NB; ++JJ) {
-            const float b = x == 0 ? btq[JJ].x : x == 1 ? btq[JJ].y : x == 2 ? btq[JJ].z : btq[JJ].w;
-            pre[x] *= (JJ < J) ? b : 1.f;
-            suf[x] *= (JJ > J) ? b : 1.f;
-          }
+        for (int x = 0; x < 4; ++x) {
           const bool safe = bt[it][x] >= kUnsafeBlockDecay;
           unsafe |= !safe;
           // 1/F_i = H_i / BT_J: one reciprocal per channel instead of per row
