@@ -18,8 +18,9 @@
 // The output wave of R computes rows R of O from the same S and U (its Q.E
 // and P operands load into its registers one chunk ahead).  The loader wave
 // of R streams the state wave's operands (W_R, the owned rows of (K.E')^T,
-// U~_R of this tile, the decay) two chunks ahead from the record into one of
-// three LDS buffers with direct global-to-LDS loads.  A CU's vector memory
+// U~_R of this tile, the decay) three chunks ahead from the record into one
+// of four LDS buffers (two and three where four do not fit) with direct
+// global-to-LDS loads.  A CU's vector memory
 // path takes about 64 bytes per clock, so the ~60 KB a chunk needs occupy it
 // for most of a chunk; the waves that wait on that path are never the ones
 // the recurrence waits on.  S^T and U^T are exchanged through LDS; two
@@ -47,12 +48,15 @@ struct SCfg {
   static constexpr int kUR = 256 * EB;               // one U~ accumulator packet
   static constexpr int oW = 0, oKG = oW + NB * kWR, oU = oKG + NCB * kKR, oGC = oU + NB * kUR;
   static constexpr int kBuf = align16(oGC + 4 * DK);
-  // LDS: three operand buffers, S^T, U^T, O staging (one tile per output
-  // wave), as separate arrays so that the compiler can tell that LDS reads of
-  // the last three never wait for the direct loads into the first.
-  static constexpr int kNBuf = 3;
+  // LDS: operand buffers, S^T, U^T, O staging (one tile per output wave), as
+  // separate arrays so that the compiler can tell that LDS reads of the last
+  // three never wait for the direct loads into the first.  Four buffers
+  // (loads three chunks ahead) where they fit, else three (two ahead).
   static constexpr int kOS = align16(16 * LDO * EB);
-  static constexpr int kLds = kNBuf * kBuf + align16(16 * LDK * EB) + align16(16 * LDC * EB) + NB * kOS;
+  static constexpr int kRest = align16(16 * LDK * EB) + align16(16 * LDC * EB) + NB * kOS;
+  static constexpr int kNBuf = (4 * kBuf + kRest <= kMaxLds) ? 4 : 3;
+  static constexpr int kAhead = kNBuf - 1;
+  static constexpr int kLds = kNBuf * kBuf + kRest;
 };
 
 // Workgroup barrier for a wave whose direct global-to-LDS loads must stay in
@@ -282,8 +286,8 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
       if (ch + 1 < NC) step(opb, opa, ch + 1, Tail{});
     }
   } else {
-    // ---------------- loader wave: state-wave operands, two chunks ahead.
-    // Operands of state wave R for chunk ch go into buffer ch % 3.  Blocks
+    // ---------------- loader wave: state-wave operands, kAhead chunks ahead.
+    // Operands of state wave R for chunk ch go into buffer ch % kNBuf.  Blocks
     // past dk are clamped (the same bytes written twice, never read).
     // Two halves, issued in the two halves of a chunk so that the issue
     // stalls of this wave never hold up a barrier for long.
@@ -305,25 +309,27 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
                         rc + RC::kUByte + static_cast<size_t>(R * NJV + jt) * Cf::kUR, lane);
     };
     // This wave issues nothing but fills, kFill instructions per chunk: at
-    // the end of chunk ch, at most kFill in flight means the fills for ch+1
-    // (issued one chunk earlier) have landed in LDS.
+    // the end of chunk ch, at most (kAhead - 1) * kFill in flight means the
+    // fills for ch+1 (issued kAhead - 1 chunks earlier) have landed in LDS.
+    constexpr int kAhead = Cf::kAhead;
     constexpr int kFill = fill_insts<Cf::kWR>() + CPW * fill_insts<Cf::kKR>() +
                           fill_insts<Cf::kUR>() + fill_insts<4 * DK / NB>();
-    static_assert(kFill < 63, "vmcnt range");
+    static_assert((kAhead - 1) * kFill < 63, "vmcnt range");
     if (NC > 0) {
-      fill_a(0);
-      fill_b(0);
-      fill_a(min(1, NC - 1));
-      fill_b(min(1, NC - 1));
-      __builtin_amdgcn_s_waitcnt(vmcnt_only(kFill));   // buffer 0 ready
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) {
+        fill_a(min(i, NC - 1));
+        fill_b(min(i, NC - 1));
+      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_only((kAhead - 1) * kFill));   // buffer 0 ready
     }
     for (int ch = 0; ch < NC; ++ch) {
-      const int chf = min(ch + 2, NC - 1);
-      barrier_keep_fills();   // chunk ch starts; buffer (ch + 2) % 3 is free
+      const int chf = min(ch + kAhead, NC - 1);
+      barrier_keep_fills();   // chunk ch starts; buffer (ch + kAhead) % kNBuf is free
       fill_a(chf);
       barrier_keep_fills();
       fill_b(chf);
-      __builtin_amdgcn_s_waitcnt(vmcnt_only(kFill));   // buffer ch + 1 ready
+      __builtin_amdgcn_s_waitcnt(vmcnt_only((kAhead - 1) * kFill));   // buffer ch + 1 ready
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_only(0));   // no fill left in flight
   }
