@@ -1,12 +1,16 @@
-// KDA chunked prefill: one fused kernel per (chain, dv tile).
+// KDA chunked prefill: the chunk kernel, in two modes.
 //
-// A workgroup of four waves owns one (batch, head) chain and a DVT-wide
-// column slab of its dk x dv state, and walks the chunks of C tokens in
-// order.  The fp32 state slab lives in registers for the whole sequence;
+// Fused mode: a workgroup of eight waves owns one (batch, head) chain and a
+// DVT-wide column slab of its dk x dv state, and walks the chunks of C tokens
+// in order.  The fp32 state slab lives in registers for the whole sequence;
 // every per-chunk intermediate lives in LDS; HBM sees each input once and
 // each output once.  (Columns of the state evolve independently, so slabs of
 // one chain run in parallel workgroups; they recompute the column-free
 // chunk work and share its inputs through L2.)
+//
+// Prep mode (few chains): the same chunk work for a run of chunks per
+// workgroup, all chunks in parallel across the chip, writing each chunk's
+// state-free quantities to a workspace record for the scan kernel.
 //
 // Chunk algebra.  For a chunk with start state S, rows r = 0..C-1 and the
 // per-channel cumulative decay E_r = prod_{j<=r} alpha_j (E'_r = prod_{j>r}):
@@ -102,26 +106,6 @@ template <typename OpT> struct SrcScaled {
       typename F::T v = *reinterpret_cast<const typename F::T*>(a);
 #pragma unroll
       for (int e = 0; e < F::N; ++e) v[e] = static_cast<__bf16>(static_cast<float>(v[e]) * s[kk + e]);
-      return v;
-    }
-  }
-};
-
-// fp32 rows converted to OpT.
-template <typename OpT> struct SrcF32 {
-  const float* p;
-  int ld;
-  Lane l;
-  template <int KS>
-  __device__ __forceinline__ typename Frag<OpT, KS>::T get(int k0) const {
-    using F = Frag<OpT, KS>;
-    const float* a = p + l.i * ld + k0 + F::N * l.g;
-    if constexpr (F::N == 1) {
-      return *a;
-    } else {
-      typename F::T v;
-#pragma unroll
-      for (int e = 0; e < F::N; ++e) v[e] = static_cast<__bf16>(a[e]);
       return v;
     }
   }
