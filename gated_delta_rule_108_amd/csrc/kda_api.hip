@@ -34,6 +34,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
+// Chunk length the kernels run for a requested C.  A 128-token chunk runs as
+// two 64-token chunks: its C x C solve matrix, P and Y tiles do not fit the
+// CU's 160 KiB of LDS beside the K, Q, V tiles, and by the chunk algebra two
+// consecutive 64-token chunks give the same result up to rounding.
+int chunk_run(int C) { return C == 128 ? 64 : C; }
+
 struct Span {
   uintptr_t lo, hi;  // [lo, hi)
 };
@@ -63,6 +69,7 @@ const char* kda_status_string(kda_status s) {
 }
 
 size_t kda_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int C, kda_dtype dt) {
+  C = chunk_run(C);
   if (B < 1 || H < 1 || T < 0) return static_cast<size_t>(-1);
   if (dt != KDA_F32 && dt != KDA_BF16) return static_cast<size_t>(-1);
   if (!dim_ok(dk) || !dim_ok(dv)) return static_cast<size_t>(-1);
@@ -74,6 +81,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
                                const float* beta, const float* S0, void* o, float* S_T, int B,
                                int T, int H, int dk, int dv, int C, kda_dtype dt, void* workspace,
                                size_t workspace_bytes, void* stream) {
+  C = chunk_run(C);
   if (B < 1 || H < 1 || T < 0) return KDA_ERR_SHAPE;
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;

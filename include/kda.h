@@ -108,9 +108,12 @@ size_t kda_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int C,
  *   S_T    [B, H, dk, dv] float32   final state (written), or NULL to skip;
  *                                   may be equal to S0 (in place) but may not
  *                                   overlap it otherwise
- *   C                               chunk length in {16, 32, 64}; a
+ *   C                               chunk length in {16, 32, 64, 128}; a
  *                                   performance knob only: the result does not
- *                                   depend on C beyond rounding
+ *                                   depend on C beyond rounding.  C = 128 runs
+ *                                   as two 64-token chunks (a 128-row chunk's
+ *                                   tiles do not fit one CU's LDS), so its
+ *                                   workspace and results are those of C = 64
  *   workspace, workspace_bytes      caller-owned device scratch of at least
  *                                   kda_prefill_workspace_bytes(...) bytes,
  *                                   16-byte aligned, overlapping no other

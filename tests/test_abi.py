@@ -84,7 +84,6 @@ def test_prefill_validation_errors():
     assert prefill(lib, dk=48) == L.KDA_ERR_UNSUPPORTED
     assert prefill(lib, dv=256) == L.KDA_ERR_UNSUPPORTED
     assert prefill(lib, C=8) == L.KDA_ERR_UNSUPPORTED
-    assert prefill(lib, C=128) == L.KDA_ERR_UNSUPPORTED
     assert prefill(lib, dt=7) == L.KDA_ERR_UNSUPPORTED
     assert prefill(lib, dt=0) == L.KDA_ERR_UNSUPPORTED          # fp32, dk=128, C=64: no fit
     assert prefill(lib, alpha=addr(3) + 4) == L.KDA_ERR_ALIGN
@@ -141,6 +140,10 @@ def test_workspace_query():
     assert lib.kda_prefill_workspace_bytes(1, 4096, 16, 128, 128, 64, 1) == 16 * 64 * rec(64, 128, 128, 2)
     assert lib.kda_prefill_workspace_bytes(1, 4096, 16, 128, 64, 64, 1) == 16 * 64 * rec(64, 128, 64, 2)
     assert lib.kda_prefill_workspace_bytes(8, 8192, 32, 128, 128, 64, 1) == 0   # fused path
+    # C = 128 runs as 64-token chunks: same workspace as C = 64
+    for args in ((1, 4096, 16, 128, 128), (1, 100, 3, 64, 32), (8, 8192, 32, 128, 128)):
+        assert (lib.kda_prefill_workspace_bytes(*args, 128, 1)
+                == lib.kda_prefill_workspace_bytes(*args, 64, 1))
     assert lib.kda_prefill_workspace_bytes(1, 256, 1, 16, 16, 16, 0) == 16 * rec(16, 16, 16, 4)
     assert lib.kda_prefill_workspace_bytes(1, 256, 1, 16, 16, 12, 0) == bad
     assert lib.kda_prefill_workspace_bytes(0, 256, 1, 16, 16, 16, 0) == bad

@@ -18,7 +18,7 @@ from tests import chunk_model as cm
 from tests.oracle_pins import rand_case, rel
 
 
-@pytest.mark.parametrize("C", [1, 4, 16, 32, 64])
+@pytest.mark.parametrize("C", [1, 4, 16, 32, 64, 128])
 @pytest.mark.parametrize("factored,blocked", [(False, False), (True, True)])
 def test_chunk_form_matches_recurrence(C, factored, blocked):
     q, k, v, alpha, beta, S0 = rand_case(31, B=1, T=150, H=1, dk=12, dv=7, alo=0.6)

@@ -63,7 +63,7 @@ def check(inp, C, tol=None, label=""):
     return o, S
 
 
-@pytest.mark.parametrize("C", [16, 32])
+@pytest.mark.parametrize("C", [16, 32, 128])
 def test_tiny_fp32_full(C):
     spec = wl.PREFILL["tiny_fp32"]
     check(wl.make_prefill_inputs(spec), C, label="tiny_fp32")
@@ -78,19 +78,30 @@ def test_tiny_fp32_null_state_equals_explicit_zeros():
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 
-@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("C", [16, 32, 64, 128])
 def test_prefill_h16_t4k_chunks(C):
-    """The bf16 H=16, T=4096, d=128 workload in full; every chunk size."""
+    """The bf16 H=16, T=4096, d=128 workload in full; every chunk size (128
+    runs as two 64-token chunks)."""
     spec = wl.PREFILL["prefill_h16_t4k"]
     check(wl.make_prefill_inputs(spec), C, label="h16_t4k")
 
 
-@pytest.mark.parametrize("T", [1, 15, 17, 63, 65, 200])
-def test_ragged_lengths(T):
+def test_chunk_128_runs_as_64():
+    """C = 128 is accepted and computed with 64-token chunks: bit-identical."""
+    spec = wl.PREFILL["prefill_h16_t4k"]
+    inp = wl.make_prefill_inputs(spec, T=300, H=4)
+    o1, S1 = run(inp, 64)
+    o2, S2 = run(inp, 128)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("T,C", [(1, 64), (15, 64), (17, 64), (63, 64), (65, 64), (200, 64),
+                                 (127, 128), (200, 128)])
+def test_ragged_lengths(T, C):
     spec = wl.PREFILL["prefill_h16_t4k"]
     inp = wl.make_prefill_inputs(spec, T=T, H=3)
     inp["S0"] = 0.1 * torch.randn(1, 3, 128, 128, generator=torch.Generator().manual_seed(T))
-    check(inp, 64, label=f"ragged T={T}")
+    check(inp, C, label=f"ragged T={T}")
 
 
 def test_empty_sequence_copies_state():
@@ -177,7 +188,7 @@ def test_zero_and_extreme_gates(dtype):
     check(dict(q=q, k=k, v=v, alpha=alpha, beta=beta, S0=S0), C, label="zero gates")
 
 
-@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("C", [16, 32, 64, 128])
 def test_split_and_fused_paths_agree(C):
     """Few chains take the split path (chunk-parallel prep + scan, with a
     workspace); 128 or more take the fused kernel.  The same 4 chains, run
