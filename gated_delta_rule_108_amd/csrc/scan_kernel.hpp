@@ -16,7 +16,7 @@
 // wave of R computes rows R of U and owns state row blocks R, R + C/16, ...:
 // it carries the recurrence (S -> U -> S) and touches only LDS and registers.
 // The output wave of R computes rows R of O from the same S and U (its Q.E
-// and P operands load into its registers one chunk ahead).  The loader wave
+// and P operands load into its registers three chunks ahead).  The loader wave
 // of R streams the state wave's operands (W_R, the owned rows of (K.E')^T,
 // U~_R of this tile, the decay) three chunks ahead from the record into one
 // of four LDS buffers (two and three where four do not fit) with direct
@@ -58,6 +58,10 @@ struct SCfg {
   static constexpr int kAhead = kNBuf - 1;
   static constexpr int kLds = kNBuf * kBuf + kRest;
 };
+
+// Register sets of record operands an output wave rotates through (opa..opd
+// below): it loads chunk ch + kOutSets - 1 while computing chunk ch.
+constexpr int kOutSets = 4;
 
 // Workgroup barrier for a wave whose direct global-to-LDS loads must stay in
 // flight across it (a release fence on LDS would wait for them): its own LDS
@@ -244,7 +248,7 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
       const int nrows = min(C, T - t0);
       const Lane ln = lane_now();
       lds_barrier();   // S^T of this chunk published
-      fetch(nxt, min(ch + 1, NC - 1));
+      fetch(nxt, min(ch + kOutSets - 1, NC - 1));
       FD stf[NKD];
 #pragma unroll
       for (int s = 0; s < NKD; ++s) stf[s] = Src<OpT>{ST, LDK, ln}.template get<KSD>(s * KSD);
@@ -272,19 +276,25 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
     };
     using Full = std::integral_constant<bool, false>;
     using Tail = std::integral_constant<bool, true>;
-    OO opa, opb;
-    if (NC > 0) fetch(opa, 0);
+    // Four register sets in rotation: the operands of chunk ch + 3 load while
+    // chunk ch is computed, so the record reads have three chunks to land.
+    OO opa, opb, opc, opd;
+    if (NC > 0) {
+      fetch(opa, 0);
+      fetch(opb, min(1, NC - 1));
+      fetch(opc, min(2, NC - 1));
+    }
     int ch = 0;
-    for (; ch + 2 <= nfull; ch += 2) {
-      step(opa, opb, ch, Full{});
+    for (; ch + 4 <= nfull; ch += 4) {
+      step(opa, opd, ch, Full{});
       step(opb, opa, ch + 1, Full{});
+      step(opc, opb, ch + 2, Full{});
+      step(opd, opc, ch + 3, Full{});
     }
-    // at most two chunks left: one full and/or the partial last one
-    if (ch < NC) {
-      if (ch < nfull) step(opa, opb, ch, Full{});
-      else step(opa, opb, ch, Tail{});
-      if (ch + 1 < NC) step(opb, opa, ch + 1, Tail{});
-    }
+    if (ch < NC) step(opa, opd, ch, Tail{});
+    if (ch + 1 < NC) step(opb, opa, ch + 1, Tail{});
+    if (ch + 2 < NC) step(opc, opb, ch + 2, Tail{});
+    if (ch + 3 < NC) step(opd, opc, ch + 3, Tail{});
   } else {
     // ---------------- loader wave: state-wave operands, kAhead chunks ahead.
     // Operands of state wave R for chunk ch go into buffer ch % kNBuf.  Blocks

@@ -48,7 +48,8 @@ def test_prefill_status_codes():
     assert call(b, S_T=b["S0"].data_ptr()) == lib.KDA_OK       # in place
     assert call(b, q=None) == lib.KDA_ERR_NULL
     assert call(b, T=-3) == lib.KDA_ERR_SHAPE
-    assert call(b, C=128) == lib.KDA_ERR_UNSUPPORTED
+    assert call(b, C=128) == lib.KDA_OK                       # runs as C = 64
+    assert call(b, C=8) == lib.KDA_ERR_UNSUPPORTED
     assert call(b, dk=100) == lib.KDA_ERR_UNSUPPORTED
     assert call(b, k=b["k"].data_ptr() + 2) == lib.KDA_ERR_ALIGN
     assert call(b, o=b["v"].data_ptr()) == lib.KDA_ERR_ALIAS
