@@ -534,11 +534,12 @@ struct PCfg {
 constexpr int kMaxLds = 160 * 1024;
 
 // kPrep = false: the fused prefill (all chunks of a chain, state in
-// registers).  kPrep = true: each workgroup (DVT = dv) takes a run of cpb
-// consecutive chunks of one chain, computes their state-free quantities and
+// registers; cpb, seg0, segn unused).  kPrep = true: each workgroup (DVT =
+// dv) takes a run of cpb consecutive chunks of one chain within the segment
+// of chunks [seg0, seg0 + segn), computes their state-free quantities and
 // writes them to the chunks' workspace records (W, Q.E, (K.E')^T, P, chunk
-// decay, U~) for the scan kernel; the next chunk's inputs load while the
-// current one is processed.
+// decay, U~; segn records per chain) for the scan kernel; the next chunk's
+// inputs load while the current one is processed.
 template <typename OpT, int DK, int C, int DVT, bool kPrep = false>
 __global__ void __launch_bounds__(512)
 kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
@@ -546,7 +547,8 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
                    const typename Ty<OpT>::Elem* __restrict__ gv,
                    const float* __restrict__ galpha, const float* __restrict__ gbeta,
                    const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float* gST,
-                   int B, int T, int H, int DV, char* __restrict__ gws, int cpb) {
+                   int B, int T, int H, int DV, char* __restrict__ gws, int cpb, int seg0,
+                   int segn) {
   using Cf = PCfg<OpT, DK, C, DVT>;
   using E = typename Ty<OpT>::Elem;
   using PT = typename Pair<OpT>::T;
@@ -589,16 +591,17 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
 
   // Workgroup -> (chain, slab).  Consecutive workgroups are dealt round-robin
   // to the 8 XCDs; keep all slabs of one chain on one XCD so they share L2.
-  // Prep mode: workgroup -> (chain, run of cpb consecutive chunks).
+  // Prep mode: workgroup -> (chain, run of cpb consecutive chunks of the
+  // segment [seg0, seg0 + segn)); the segment's records are numbered from 0.
   const int NC = (T + C - 1) / C;
-  const int ntiles = kPrep ? (NC + cpb - 1) / cpb : DV / DVT;
+  const int ntiles = kPrep ? (segn + cpb - 1) / cpb : DV / DVT;
   const int total = gridDim.x;
   int L = blockIdx.x;
   if (!kPrep && ntiles > 1 && (total % 8) == 0) L = (blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
   const int chain = L / ntiles;
   const int j0 = kPrep ? 0 : (L % ntiles) * DVT;
-  const int ch_begin = kPrep ? (L % ntiles) * cpb : 0;
-  const int ch_end = kPrep ? min(ch_begin + cpb, NC) : NC;
+  const int ch_begin = kPrep ? seg0 + (L % ntiles) * cpb : 0;
+  const int ch_end = kPrep ? min(ch_begin + cpb, seg0 + segn) : NC;
   const int b = chain / H, h = chain % H;
 
   // Token t of this chain sits at row (b*T + t)*H + h of the [B*T*H, *]
@@ -1099,7 +1102,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     if constexpr (kPrep) {
       // chunk record -> workspace: operand packets, decay, U~ (this slab is all of dv)
       using RC = RecCfg<OpT, DK, C>;
-      char* rec = gws + (static_cast<size_t>(chain) * NC + ch) * RC::bytes(DV);
+      char* rec = gws + (static_cast<size_t>(chain) * segn + (ch - seg0)) * RC::bytes(DV);
       E* rw = reinterpret_cast<E*>(rec);
       copy_packets<OpT, RC::KSD, NB, RC::NKD, NTH>(rw + RC::kW, Wm, LDK, tid);
       copy_packets<OpT, RC::KSD, NB, RC::NKD, NTH>(rw + RC::kQ, Qr, LDK, tid);
@@ -1247,7 +1250,7 @@ hipError_t launch_one(const PrefillArgs& a) {
   hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT>), grid, dim3(PCfg<OpT, DK, C, DVT>::NTH), 0,
                      static_cast<hipStream_t>(a.stream), static_cast<const E*>(a.q),
                      static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.alpha, a.beta,
-                     a.S0, static_cast<E*>(a.o), a.S_T, a.B, a.T, a.H, a.dv, nullptr, 0);
+                     a.S0, static_cast<E*>(a.o), a.S_T, a.B, a.T, a.H, a.dv, nullptr, 0, 0, 0);
   return hipGetLastError();
 }
 

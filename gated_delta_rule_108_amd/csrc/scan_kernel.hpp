@@ -27,6 +27,7 @@
 // barriers per chunk.
 #pragma once
 
+#include <algorithm>
 #include <type_traits>
 
 #include "prefill_kernel.hpp"
@@ -110,7 +111,7 @@ struct OutOps {
 template <typename OpT, int DK, int C>
 __global__ void __launch_bounds__(3 * kWave * (C / 16))
 kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float* gST,
-                const char* __restrict__ gws, int B, int T, int H, int DV) {
+                const char* __restrict__ gws, int B, int T, int H, int DV, int seg0, int segn) {
   using Cf = SCfg<OpT, DK, C>;
   using RC = typename Cf::RC;
   using E = typename Ty<OpT>::Elem;
@@ -140,8 +141,11 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
   if (NJV > 1 && (total % 8) == 0) L = (blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
   const int chain = L / NJV, jt = L % NJV;
   const int b = chain / H, h = chain % H;
-  const int NC = (T + C - 1) / C;
-  const int nfull = T / C;
+  // This launch walks the segment of chunks [seg0, seg0 + segn): NC records
+  // per chain, the first nfull of them full chunks; local chunk ch holds
+  // tokens from (seg0 + ch) * C.
+  const int NC = segn;
+  const int nfull = max(0, min(segn, T / C - seg0));
   const size_t row0 = static_cast<size_t>(b) * T * H + h;
   const size_t rbytes = RC::bytes(DV);
   const char* rec0 = gws + static_cast<size_t>(chain) * NC * rbytes;
@@ -244,7 +248,7 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
     // itself; only the partial last chunk masks its store), so the compiler's
     // wait counts stay exact instead of draining all outstanding traffic.
     auto step = [&](const OO& cur, OO& nxt, int ch, auto tail) {
-      const int t0 = ch * C;
+      const int t0 = (seg0 + ch) * C;
       const int nrows = min(C, T - t0);
       const Lane ln = lane_now();
       lds_barrier();   // S^T of this chunk published
@@ -366,10 +370,42 @@ bool split_fits(int dv) {
   return false;
 }
 
+// The split path walks the sequence in segments of whole chunks: the prep
+// kernel writes the records of one segment, the scan consumes them, and the
+// next segment reuses the same records.  A segment's records are kept within
+// kSegmentBudget bytes so that they stay in the chip's last-level cache
+// (256 MiB of Infinity Cache on MI355X) between the two kernels, and the
+// workspace does not grow with T.  Between segments the fp32 state goes
+// through a carry region after the records.
+constexpr size_t kSegmentBudget = size_t{160} << 20;
+
+struct SplitPlan {
+  int nc = 0;        // chunks per chain
+  int nseg = 0;      // segments
+  int segch = 0;     // chunks per segment (the last one may have fewer)
+  size_t records = 0, carry = 0;   // workspace bytes: records, then carry
+};
+
+template <typename OpT, int DK, int C>
+SplitPlan split_plan(int B, int T, int H, int dv) {
+  SplitPlan p;
+  const size_t chains = static_cast<size_t>(B) * H;
+  const size_t rec = RecCfg<OpT, DK, C>::bytes(dv);
+  p.nc = (T + C - 1) / C;
+  if (p.nc == 0) return p;
+  const size_t per_chunk = chains * rec;   // one chunk of every chain
+  const size_t segmax = std::max<size_t>(1, kSegmentBudget / per_chunk);
+  p.nseg = static_cast<int>((static_cast<size_t>(p.nc) + segmax - 1) / segmax);
+  p.segch = (p.nc + p.nseg - 1) / p.nseg;
+  p.records = chains * p.segch * rec;
+  p.carry = p.nseg > 1 ? chains * DK * dv * sizeof(float) : 0;
+  return p;
+}
+
 template <typename OpT, int DK, int C>
 size_t split_workspace_bytes(int B, int T, int H, int dv) {
-  const size_t nc = static_cast<size_t>((T + C - 1) / C);
-  return static_cast<size_t>(B) * H * nc * RecCfg<OpT, DK, C>::bytes(dv);
+  const SplitPlan p = split_plan<OpT, DK, C>(B, T, H, dv);
+  return p.records + p.carry;
 }
 
 // Chunks per prep workgroup: about one workgroup per CU in total.
@@ -383,23 +419,22 @@ inline int prep_chunks_per_block(long chains, int nc) {
 }
 
 template <typename OpT, int DK, int C, int DVT>
-hipError_t launch_prep(const PrefillArgs& a) {
+hipError_t launch_prep(const PrefillArgs& a, int seg0, int segn) {
   using E = typename Ty<OpT>::Elem;
   if constexpr (!fits<OpT, DK, C, DVT>()) {
     return hipErrorInvalidValue;
   } else {
+    if (segn == 0) return hipSuccess;
     const long chains = static_cast<long>(a.B) * a.H;
-    const int nc = (a.T + C - 1) / C;
-    if (nc == 0) return hipSuccess;
     // One workgroup per CU at this LDS size: give each a run of chunks so that
     // all but the first chunk's loads hide behind compute.
-    const int cpb = prep_chunks_per_block(chains, nc);
-    const long blocks = chains * ((nc + cpb - 1) / cpb);
+    const int cpb = prep_chunks_per_block(chains, segn);
+    const long blocks = chains * ((segn + cpb - 1) / cpb);
     hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT, true>), dim3(static_cast<unsigned>(blocks)),
                        dim3(512), 0, static_cast<hipStream_t>(a.stream), static_cast<const E*>(a.q),
                        static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.alpha, a.beta,
                        a.S0, static_cast<E*>(a.o), a.S_T, a.B, a.T, a.H, a.dv,
-                       static_cast<char*>(a.workspace), cpb);
+                       static_cast<char*>(a.workspace), cpb, seg0, segn);
     return hipGetLastError();
   }
 }
@@ -407,24 +442,36 @@ hipError_t launch_prep(const PrefillArgs& a) {
 template <typename OpT, int DK, int C>
 hipError_t launch_split(const PrefillArgs& a) {
   using E = typename Ty<OpT>::Elem;
-  hipError_t e = hipErrorInvalidValue;
-  switch (a.dv) {
-    case 16: e = launch_prep<OpT, DK, C, 16>(a); break;
-    case 32: e = launch_prep<OpT, DK, C, 32>(a); break;
-    case 64: e = launch_prep<OpT, DK, C, 64>(a); break;
-    case 128: e = launch_prep<OpT, DK, C, 128>(a); break;
-  }
-  if (e != hipSuccess) return e;
   if constexpr (!scan_fits<OpT, DK, C>()) {
     return hipErrorInvalidValue;
   } else {
+    const SplitPlan p = split_plan<OpT, DK, C>(a.B, a.T, a.H, a.dv);
     const long chains = static_cast<long>(a.B) * a.H;
-    dim3 grid(static_cast<unsigned>(chains * (a.dv / 16)));
-    hipLaunchKernelGGL((kda_scan_kernel<OpT, DK, C>), grid, dim3(SCfg<OpT, DK, C>::NTH), 0,
-                       static_cast<hipStream_t>(a.stream), a.S0, static_cast<E*>(a.o), a.S_T,
-                       static_cast<const char*>(a.workspace), a.B, a.T, a.H, a.dv);
+    float* carry = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + p.records);
+    // T = 0 still runs one (empty) scan: it copies S0, or zeros, to S_T.
+    const int nlaunch = p.nseg > 0 ? p.nseg : 1;
+    for (int sgi = 0; sgi < nlaunch; ++sgi) {
+      const int seg0 = sgi * p.segch;
+      const int segn = p.nseg > 0 ? std::min(p.segch, p.nc - seg0) : 0;
+      hipError_t e = hipErrorInvalidValue;
+      switch (a.dv) {
+        case 16: e = launch_prep<OpT, DK, C, 16>(a, seg0, segn); break;
+        case 32: e = launch_prep<OpT, DK, C, 32>(a, seg0, segn); break;
+        case 64: e = launch_prep<OpT, DK, C, 64>(a, seg0, segn); break;
+        case 128: e = launch_prep<OpT, DK, C, 128>(a, seg0, segn); break;
+      }
+      if (e != hipSuccess) return e;
+      const float* s_in = sgi == 0 ? a.S0 : carry;
+      float* s_out = sgi == nlaunch - 1 ? a.S_T : carry;   // in place between segments
+      dim3 grid(static_cast<unsigned>(chains * (a.dv / 16)));
+      hipLaunchKernelGGL((kda_scan_kernel<OpT, DK, C>), grid, dim3(SCfg<OpT, DK, C>::NTH), 0,
+                         static_cast<hipStream_t>(a.stream), s_in, static_cast<E*>(a.o), s_out,
+                         static_cast<const char*>(a.workspace), a.B, a.T, a.H, a.dv, seg0, segn);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
-  return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------

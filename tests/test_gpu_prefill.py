@@ -219,6 +219,43 @@ def test_prep_chunk_runs_ragged():
     check(inp, 64, label="prep runs, ragged")
 
 
+def test_split_segments():
+    """A sequence whose records exceed one segment: 16 chains x 313 chunks
+    (T = 20000, the last chunk 32 rows) run as three segments of 105, 105 and
+    103 chunks with the state carried between them.  Two chains match the
+    oracle; resuming at a chunk boundary (tokens 6720.., itself two segments
+    with other boundaries) reproduces the full run bit for bit."""
+    spec = wl.PREFILL["prefill_h16_t4k"]
+    T, H, cut = 20000, 16, 105 * 64
+    ws = kda().prefill_workspace_bytes(1, T, H, 128, 128, 64)
+    assert ws == 16 * 105 * 74240 + 16 * 128 * 128 * 4            # three segments
+    inp = wl.make_prefill_inputs(spec, T=T, H=H)
+    inp["S0"] = 0.05 * torch.randn(1, H, 128, 128, generator=torch.Generator().manual_seed(7))
+    g = to_dev(inp)
+    o, S = kda().prefill_chunked(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["S0"], chunk=64)
+    torch.cuda.synchronize()
+    for h in (0, 11):
+        sl = {k: (inp[k][:, :, h:h + 1].contiguous() if k != "S0" else inp[k][:, h:h + 1].contiguous())
+              for k in inp}
+        o_ref, S_ref = oracle(sl)
+        eo, es = rel(f64(o[:, :, h:h + 1]), o_ref), rel(f64(S[:, h:h + 1]), S_ref)
+        print(f"[segments T={T} head {h}] rel_o={eo:.3e} rel_S={es:.3e}", flush=True)
+        assert eo < 2e-2 and es < 2e-2
+    first = {k: (g[k][:, :cut].contiguous() if k != "S0" else g[k]) for k in g}
+    rest = {k: g[k][:, cut:].contiguous() for k in g if k != "S0"}
+    o1, S1 = kda().prefill_chunked(first["q"], first["k"], first["v"], first["alpha"], first["beta"],
+                                   first["S0"], chunk=64)
+    o2, S2 = kda().prefill_chunked(rest["q"], rest["k"], rest["v"], rest["alpha"], rest["beta"], S1,
+                                   chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o[:, :cut]) and torch.equal(o2, o[:, cut:]) and torch.equal(S2, S)
+    # no final state requested: the carried state still links the segments
+    o3, _ = kda().prefill_chunked(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["S0"], chunk=64,
+                                  return_state=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o)
+
+
 def test_split_resume_and_in_place_state():
     spec = wl.PREFILL["prefill_h16_t4k"]
     inp = wl.make_prefill_inputs(spec, T=300, H=2)
