@@ -9,8 +9,9 @@
 // chunk work and share its inputs through L2.)
 //
 // Prep mode (few chains): the same chunk work for a run of chunks per
-// workgroup, all chunks in parallel across the chip, writing each chunk's
-// state-free quantities to a workspace record for the scan kernel.
+// workgroup, all chunks of a segment in parallel across the chip, writing
+// each chunk's state-free quantities to a workspace record for the scan
+// kernel.
 //
 // Chunk algebra.  For a chunk with start state S, rows r = 0..C-1 and the
 // per-channel cumulative decay E_r = prod_{j<=r} alpha_j (E'_r = prod_{j>r}):

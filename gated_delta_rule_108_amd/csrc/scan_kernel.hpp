@@ -1,7 +1,8 @@
 // KDA chunk scan: the sequential half of the split prefill.
 //
 // The prep kernel (kda_prefill_kernel<..., kPrep = true>) has already written,
-// for every chunk of every chain, the state-free chunk quantities
+// for every chunk of the current segment of every chain, the state-free chunk
+// quantities
 //   W = Y Diag(beta)(K.E),  Q.E,  (K.E')^T,  P (gated Q K^T, lower),
 //   the chunk decay E_{C-1},  U~ = Y Diag(beta) V
 // to a workspace record (RecCfg), as matrix-core operand packets.  This
@@ -350,8 +351,8 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
 }
 
 // ----------------------------------------------------------------------------
-// Split path: prep kernel over all chunks (one workgroup per chunk, all dv
-// columns), then the scan.
+// Split path: per segment of chunks, the prep kernel over all its chunks
+// (runs of chunks per workgroup, all dv columns), then the scan.
 // ----------------------------------------------------------------------------
 template <typename OpT, int DK, int C>
 constexpr bool scan_fits() {
