@@ -33,6 +33,20 @@ struct DecodeCfg {
   static_assert(RPT * RG == DK, "rows must split evenly");
 };
 
+// The new state goes out with non-temporal stores: nothing reads it again in
+// this step, and keeping it from allocating in the caches lets the reads of
+// the old state stream at a higher rate (256 x 32 heads: 216 -> 161 us).
+// Non-temporal loads of the old state measured slower (198 us).
+__device__ __forceinline__ void store_streaming(float* p, const float4& w) {
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  f4v t;
+  t.x = w.x;
+  t.y = w.y;
+  t.z = w.z;
+  t.w = w.w;
+  __builtin_nontemporal_store(t, reinterpret_cast<f4v*>(p));
+}
+
 template <typename IO, int DK, int CW>
 __global__ void __launch_bounds__(256)
 kda_decode_kernel(const typename Ty<IO>::Elem* __restrict__ q,
@@ -126,7 +140,7 @@ kda_decode_kernel(const typename Ty<IO>::Elem* __restrict__ q,
     const int r = rg + RG * i;
     float4 w = s[i];
     w.x += kr[i] * u[0]; w.y += kr[i] * u[1]; w.z += kr[i] * u[2]; w.w += kr[i] * u[3];
-    *reinterpret_cast<float4*>(S_out + sbase + static_cast<size_t>(r) * DV + col0 + 4 * cg) = w;
+    store_streaming(S_out + sbase + static_cast<size_t>(r) * DV + col0 + 4 * cg, w);
   }
 }
 
