@@ -283,6 +283,7 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
     using Tail = std::integral_constant<bool, true>;
     // Four register sets in rotation: the operands of chunk ch + 3 load while
     // chunk ch is computed, so the record reads have three chunks to land.
+    static_assert(kOutSets == 4, "the rotation below has four register sets");
     OO opa, opb, opc, opd;
     if (NC > 0) {
       fetch(opa, 0);
