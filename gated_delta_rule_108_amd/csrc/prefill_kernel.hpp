@@ -1260,20 +1260,32 @@ constexpr bool fits() {
   return DVT <= 128 && PCfg<OpT, DK, C, DVT>::kLds <= kMaxLds;
 }
 
-// Widest slab that fits, narrowed while the chip would be under-filled.
+// Slab width for the fused kernel.  Every slab of a chain repeats the
+// chain's column-free chunk work, so a slab costs about (1 + DVT/300) units
+// per chunk (measured at dk = dv = 128, C = 64: 10.8 us per chunk at DVT =
+// 64, 12.7 us at 128), and the grid runs in rounds of one workgroup per CU.
+// Pick the width that fits with the fewest rounds x cost, the wider on a tie:
+// narrow slabs fill the chip when chains are few, and a width that would
+// spill a second, partly empty round is avoided.
 template <typename OpT, int DK, int C>
 int pick_dvt(long chains, int dv) {
+  constexpr long kCUs = 256;
   int best = 0;
+  double best_cost = 0.0;
   for (int d = 16; d <= dv; d *= 2) {
     bool ok = false;
     if (d == 16) ok = fits<OpT, DK, C, 16>();
     if (d == 32) ok = fits<OpT, DK, C, 32>();
     if (d == 64) ok = fits<OpT, DK, C, 64>();
     if (d == 128) ok = fits<OpT, DK, C, 128>();
-    if (ok) best = d;
+    if (!ok) continue;
+    const long rounds = (chains * (dv / d) + kCUs - 1) / kCUs;
+    const double cost = static_cast<double>(rounds) * (1.0 + d / 300.0);
+    if (best == 0 || cost <= best_cost) {
+      best = d;
+      best_cost = cost;
+    }
   }
-  if (best == 0) return 0;
-  while (best > 16 && chains * (dv / best) < 256) best /= 2;
   return best;
 }
 

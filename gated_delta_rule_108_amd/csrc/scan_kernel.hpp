@@ -410,14 +410,15 @@ size_t split_workspace_bytes(int B, int T, int H, int dv) {
   return p.records + p.carry;
 }
 
-// Chunks per prep workgroup: about one workgroup per CU in total.
+// Chunks per prep workgroup: each chain's nc chunks split into at most
+// floor(256 / chains) equal runs (at least one), so that the grid is one
+// round of at most one workgroup per CU whenever chains <= 256.
 inline int prep_chunks_per_block(long chains, int nc) {
   constexpr long kCUs = 256;
-  const long total = chains * nc;
-  long cpb = (total + kCUs - 1) / kCUs;
-  if (cpb < 1) cpb = 1;
-  if (cpb > nc) cpb = nc;
-  return static_cast<int>(cpb);
+  long runs = kCUs / (chains > 0 ? chains : 1);
+  if (runs < 1) runs = 1;
+  if (runs > nc) runs = nc;
+  return static_cast<int>((nc + runs - 1) / runs);
 }
 
 template <typename OpT, int DK, int C, int DVT>
@@ -482,9 +483,11 @@ hipError_t launch_split(const PrefillArgs& a) {
 //   many chains -> fused kernel (no workspace)
 // The fused kernel serialises the column-free chunk work on one workgroup
 // per chain (and per slab); with few chains that leaves most of the chip
-// idle, while the split path runs it for every chunk at once.
+// idle, while the split path runs it for every chunk at once.  Measured at
+// dk = dv = 128, C = 64, T = 8192: 128 chains take 1.22 ms split and 1.39 ms
+// fused, 160 chains 1.97 ms split and 1.65 ms fused.
 // ----------------------------------------------------------------------------
-constexpr long kSplitMaxChains = 127;
+constexpr long kSplitMaxChains = 128;
 
 template <typename OpT, int DK, int C>
 bool use_split(long chains, int dv) {

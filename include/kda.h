@@ -81,7 +81,7 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *
  * The library picks one of two paths from the sizes alone (the same choice in
  * this query and in the call):
- *   - few chains (B*H <= 127, when the chunk kernels fit on chip for these
+ *   - few chains (B*H <= 128, when the chunk kernels fit on chip for these
  *     dk, dv, C, dt): a chunk-parallel kernel first writes one record per
  *     chunk to the workspace (the state-free chunk quantities W, Q.E,
  *     (K.E')^T, P, the chunk decay and Y diag(beta) V), then a scan kernel

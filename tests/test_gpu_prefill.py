@@ -191,13 +191,13 @@ def test_zero_and_extreme_gates(dtype):
 @pytest.mark.parametrize("C", [16, 32, 64, 128])
 def test_split_and_fused_paths_agree(C):
     """Few chains take the split path (chunk-parallel prep + scan, with a
-    workspace); 128 or more take the fused kernel.  The same 4 chains, run
-    alone and inside a batch of 128 chains, both match the oracle."""
+    workspace); more than 128 take the fused kernel.  The same 4 chains, run
+    alone and inside a batch of 132 chains, both match the oracle."""
     spec = wl.PREFILL["prefill_h16_t4k"]
-    big = wl.make_prefill_inputs(spec, T=160, B=32, H=4)
-    big["S0"] = 0.05 * torch.randn(32, 4, 128, 128, generator=torch.Generator().manual_seed(C))
+    big = wl.make_prefill_inputs(spec, T=160, B=33, H=4)
+    big["S0"] = 0.05 * torch.randn(33, 4, 128, 128, generator=torch.Generator().manual_seed(C))
     ws_few = kda().prefill_workspace_bytes(1, 160, 4, 128, 128, C)
-    ws_many = kda().prefill_workspace_bytes(32, 160, 4, 128, 128, C)
+    ws_many = kda().prefill_workspace_bytes(33, 160, 4, 128, 128, C)
     assert ws_few > 0 and ws_many == 0
     o_big, S_big = run(big, C)
     few = {k: (v[3:4].contiguous() if v is not None else v) for k, v in big.items()}
