@@ -8,6 +8,15 @@ stream.  Every step of the computation runs in the library's HIP kernels.
     o, S_T = prefill_chunked(q, k, v, alpha, beta, S0=None, chunk=64)
     o, S   = decode_step(q, k, v, alpha, beta, S)            # in place on S
 
+With the input prologue fused into the kernels (raw projections in):
+
+    o, S_T = prefill_chunked_logits(q, k, v, g, b, S0=None, chunk=64, qk_map="l2")
+    o, S   = decode_step_logits(q, k, v, g, b, S, qk_map="l2")
+
+where alpha = exp(-softplus(g)) (g has the dtype of q), beta = sigmoid(b)
+(b float32), and qk_map is "as_given", "l2" (x / max(|x|, 1e-12)) or
+"silu_l2" (the same after SiLU).
+
 Layouts (token-major, as the attention projections produce them):
     prefill  q,k [B,T,H,dk]  v [B,T,H,dv]  alpha [B,T,H,dk]  beta [B,T,H]
              S0, S_T [B,H,dk,dv]  o [B,T,H,dv]
@@ -23,9 +32,11 @@ import torch
 from . import _lib
 from ._lib import KDAError  # noqa: F401
 
-__all__ = ["prefill_chunked", "decode_step", "prefill_workspace_bytes", "KDAError", "lib"]
+__all__ = ["prefill_chunked", "decode_step", "prefill_chunked_logits", "decode_step_logits",
+           "prefill_workspace_bytes", "KDAError", "lib"]
 
 _DT = {torch.bfloat16: _lib.KDA_BF16, torch.float32: _lib.KDA_F32}
+_QK = {"as_given": _lib.KDA_QK_AS_GIVEN, "l2": _lib.KDA_QK_L2, "silu_l2": _lib.KDA_QK_SILU_L2}
 
 
 def lib():
@@ -58,6 +69,19 @@ def prefill_workspace_bytes(B, T, H, dk, dv, chunk, dtype=torch.bfloat16) -> int
 def prefill_chunked(q, k, v, alpha, beta, S0=None, chunk=64, out=None, state_out=None,
                     return_state=True):
     """KDA over whole sequences; returns (o, S_T) (S_T None if not requested)."""
+    return _prefill(q, k, v, alpha, beta, S0, chunk, out, state_out, return_state, None)
+
+
+def prefill_chunked_logits(q, k, v, g, b, S0=None, chunk=64, qk_map="l2", out=None,
+                           state_out=None, return_state=True):
+    """KDA over whole sequences from raw projections: alpha = exp(-softplus(g)),
+    beta = sigmoid(b), q and k mapped by qk_map, all inside the kernels."""
+    if qk_map not in _QK:
+        raise ValueError(f"qk_map {qk_map!r}: expected one of {sorted(_QK)}")
+    return _prefill(q, k, v, g, b, S0, chunk, out, state_out, return_state, _QK[qk_map])
+
+
+def _prefill(q, k, v, gate, beta, S0, chunk, out, state_out, return_state, qk):
     L = lib()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -65,9 +89,10 @@ def prefill_chunked(q, k, v, alpha, beta, S0=None, chunk=64, out=None, state_out
     if q.dtype not in _DT:
         raise TypeError(f"q: dtype {q.dtype} not supported")
     dt = q.dtype
+    gname, gdt = ("alpha", torch.float32) if qk is None else ("g", dt)
     for n, t, d, s in (("q", q, dt, (B, T, H, dk)), ("k", k, dt, (B, T, H, dk)),
-                       ("v", v, dt, (B, T, H, dv)), ("alpha", alpha, torch.float32, (B, T, H, dk)),
-                       ("beta", beta, torch.float32, (B, T, H))):
+                       ("v", v, dt, (B, T, H, dv)), (gname, gate, gdt, (B, T, H, dk)),
+                       ("beta" if qk is None else "b", beta, torch.float32, (B, T, H))):
         _check(n, t, d, s, dev)
     if S0 is not None:
         _check("S0", S0, torch.float32, (B, H, dk, dv), dev)
@@ -82,16 +107,35 @@ def prefill_chunked(q, k, v, alpha, beta, S0=None, chunk=64, out=None, state_out
     if ws_bytes == (1 << 64) - 1:
         raise KDAError(_lib.KDA_ERR_UNSUPPORTED, "kda_prefill_workspace_bytes")
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
-    st = L.kda_prefill_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0),
-                               _ptr(o), _ptr(S_T), B, T, H, dk, dv, chunk, _DT[dt], _ptr(ws),
-                               ws_bytes, _stream(dev))
+    if qk is None:
+        st = L.kda_prefill_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S0),
+                                   _ptr(o), _ptr(S_T), B, T, H, dk, dv, chunk, _DT[dt],
+                                   _ptr(ws), ws_bytes, _stream(dev))
+        where = "kda_prefill_chunked"
+    else:
+        st = L.kda_prefill_chunked_logits(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
+                                          _ptr(S0), _ptr(o), _ptr(S_T), B, T, H, dk, dv, chunk,
+                                          _DT[dt], qk, _ptr(ws), ws_bytes, _stream(dev))
+        where = "kda_prefill_chunked_logits"
     if st != _lib.KDA_OK:
-        raise KDAError(st, "kda_prefill_chunked")
+        raise KDAError(st, where)
     return o, S_T
 
 
 def decode_step(q, k, v, alpha, beta, S, out=None, state_out=None):
     """One recurrence step; state_out defaults to S itself (in place)."""
+    return _decode(q, k, v, alpha, beta, S, out, state_out, None)
+
+
+def decode_step_logits(q, k, v, g, b, S, qk_map="l2", out=None, state_out=None):
+    """One recurrence step from raw projections (see prefill_chunked_logits);
+    state_out defaults to S itself (in place)."""
+    if qk_map not in _QK:
+        raise ValueError(f"qk_map {qk_map!r}: expected one of {sorted(_QK)}")
+    return _decode(q, k, v, g, b, S, out, state_out, _QK[qk_map])
+
+
+def _decode(q, k, v, gate, beta, S, out, state_out, qk):
     L = lib()
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -99,17 +143,25 @@ def decode_step(q, k, v, alpha, beta, S, out=None, state_out=None):
     if q.dtype not in _DT:
         raise TypeError(f"q: dtype {q.dtype} not supported")
     dt = q.dtype
+    gname, gdt = ("alpha", torch.float32) if qk is None else ("g", dt)
     for n, t, d, s in (("q", q, dt, (N, H, dk)), ("k", k, dt, (N, H, dk)),
-                       ("v", v, dt, (N, H, dv)), ("alpha", alpha, torch.float32, (N, H, dk)),
-                       ("beta", beta, torch.float32, (N, H)),
+                       ("v", v, dt, (N, H, dv)), (gname, gate, gdt, (N, H, dk)),
+                       ("beta" if qk is None else "b", beta, torch.float32, (N, H)),
                        ("S", S, torch.float32, (N, H, dk, dv))):
         _check(n, t, d, s, dev)
     o = torch.empty((N, H, dv), dtype=dt, device=dev) if out is None else out
     _check("out", o, dt, (N, H, dv), dev)
     S_out = S if state_out is None else state_out
     _check("state_out", S_out, torch.float32, (N, H, dk, dv), dev)
-    st = L.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S),
-                           _ptr(o), _ptr(S_out), N, H, dk, dv, _DT[dt], _stream(dev))
+    if qk is None:
+        st = L.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S),
+                               _ptr(o), _ptr(S_out), N, H, dk, dv, _DT[dt], _stream(dev))
+        where = "kda_decode_step"
+    else:
+        st = L.kda_decode_step_logits(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
+                                      _ptr(S), _ptr(o), _ptr(S_out), N, H, dk, dv, _DT[dt], qk,
+                                      _stream(dev))
+        where = "kda_decode_step_logits"
     if st != _lib.KDA_OK:
-        raise KDAError(st, "kda_decode_step")
+        raise KDAError(st, where)
     return o, S_out

@@ -24,6 +24,10 @@ KDA_ERR_HIP = -8
 KDA_F32 = 0
 KDA_BF16 = 1
 
+KDA_QK_AS_GIVEN = 0
+KDA_QK_L2 = 1
+KDA_QK_SILU_L2 = 2
+
 # (name, restype, argtypes) for every entry point of include/kda.h
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 SIGNATURES = {
@@ -32,6 +36,11 @@ SIGNATURES = {
                                              _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "kda_decode_step": (ctypes.c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _i, _i, _i, _i, _i, _vp]),
+    "kda_prefill_chunked_logits": (ctypes.c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                    _i, _i, _i, _i, _i, _i, _i, _i, _vp, _sz,
+                                                    _vp]),
+    "kda_decode_step_logits": (ctypes.c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                _i, _i, _i, _i, _i, _i, _vp]),
     "kda_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
 }
 

@@ -17,6 +17,12 @@
 // (one 16-byte load per row), so the two column reductions and the update
 // happen in a single pass; reductions over rows go through cross-lane
 // exchanges inside a wave and a small LDS exchange between waves.
+//
+// kLogit = true runs the input prologue on the fly (kda_device.hpp): the gate
+// comes as logits g in the I/O type, beta as its logit, and q, k pass through
+// qk_map.  The row norms of q and k ride along the same reductions (two more
+// sums), and since every use of k and q is linear in them they are applied
+// after the reductions: r_k, r_q and q.k are rescaled, k^T u uses k / |k|.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -47,14 +53,14 @@ __device__ __forceinline__ void store_streaming(float* p, const float4& w) {
   __builtin_nontemporal_store(t, reinterpret_cast<f4v*>(p));
 }
 
-template <typename IO, int DK, int CW>
+template <typename IO, int DK, int CW, bool kLogit>
 __global__ void __launch_bounds__(256)
 kda_decode_kernel(const typename Ty<IO>::Elem* __restrict__ q,
                   const typename Ty<IO>::Elem* __restrict__ k,
                   const typename Ty<IO>::Elem* __restrict__ v,
-                  const float* __restrict__ alpha, const float* __restrict__ beta,
+                  const void* __restrict__ gate, const float* __restrict__ beta,
                   const float* S_in, typename Ty<IO>::Elem* __restrict__ o, float* S_out,
-                  int NH, int DV) {
+                  int NH, int DV, int qk_map) {
   using Cf = DecodeCfg<DK, CW>;
   using E = typename Ty<IO>::Elem;
   constexpr int CG = Cf::CG, RG = Cf::RG, RPT = Cf::RPT, NWV = Cf::NWV;
@@ -69,12 +75,16 @@ kda_decode_kernel(const typename Ty<IO>::Elem* __restrict__ q,
   const size_t sbase = static_cast<size_t>(nh) * DK * DV;
   const E* qh = q + static_cast<size_t>(nh) * DK;
   const E* kh = k + static_cast<size_t>(nh) * DK;
-  const float* ah = alpha + static_cast<size_t>(nh) * DK;
-  const float bt = beta[nh];
+  const float* ah = static_cast<const float*>(gate) + static_cast<size_t>(nh) * DK;
+  const E* gh = static_cast<const E*>(gate) + static_cast<size_t>(nh) * DK;
+  const float bt = kLogit ? sigmoid_f(beta[nh]) : beta[nh];
+  const bool qk_silu = kLogit && qk_map == kQkSiluL2;
+  const bool qk_norm = kLogit && qk_map != kQkAsGiven;
 
   float4 s[RPT];
   float kr[RPT];
   float rk[4] = {0.f, 0.f, 0.f, 0.f}, rq[4] = {0.f, 0.f, 0.f, 0.f}, qk = 0.f;
+  float nk = 0.f, nq = 0.f;   // sums of squares of k and q (prologue)
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rg + RG * i;
@@ -83,9 +93,18 @@ kda_decode_kernel(const typename Ty<IO>::Elem* __restrict__ q,
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rg + RG * i;
-    const float a = ah[r];
-    const float kv = Ty<IO>::to_f32(kh[r]);
-    const float qv = Ty<IO>::to_f32(qh[r]);
+    float a, kv = Ty<IO>::to_f32(kh[r]), qv = Ty<IO>::to_f32(qh[r]);
+    if constexpr (kLogit) {
+      a = gate_from_logit(Ty<IO>::to_f32(gh[r]));
+      if (qk_silu) {   // rounded back to the I/O type, as the prefill does
+        kv = Ty<IO>::to_f32(Ty<IO>::from_f32(silu_f(kv)));
+        qv = Ty<IO>::to_f32(Ty<IO>::from_f32(silu_f(qv)));
+      }
+      nk += kv * kv;
+      nq += qv * qv;
+    } else {
+      a = ah[r];
+    }
     kr[i] = kv;
     s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;
     rk[0] += kv * s[i].x; rk[1] += kv * s[i].y; rk[2] += kv * s[i].z; rk[3] += kv * s[i].w;
@@ -101,9 +120,13 @@ kda_decode_kernel(const typename Ty<IO>::Elem* __restrict__ q,
       rq[j] += __shfl_xor(rq[j], off);
     }
     qk += __shfl_xor(qk, off);
+    if constexpr (kLogit) {
+      nk += __shfl_xor(nk, off);
+      nq += __shfl_xor(nq, off);
+    }
   }
   if constexpr (NWV > 1) {
-    __shared__ float red[NWV][CG][9];
+    __shared__ float red[NWV][CG][kLogit ? 11 : 9];
     if (lane < CG) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -111,11 +134,17 @@ kda_decode_kernel(const typename Ty<IO>::Elem* __restrict__ q,
         red[wave][cg][4 + j] = rq[j];
       }
       red[wave][cg][8] = qk;
+      if constexpr (kLogit) {
+        red[wave][cg][9] = nk;
+        red[wave][cg][10] = nq;
+      }
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 4; ++j) { rk[j] = 0.f; rq[j] = 0.f; }
     qk = 0.f;
+    nk = 0.f;
+    nq = 0.f;
 #pragma unroll
     for (int w = 0; w < NWV; ++w) {
 #pragma unroll
@@ -124,7 +153,22 @@ kda_decode_kernel(const typename Ty<IO>::Elem* __restrict__ q,
         rq[j] += red[w][cg][4 + j];
       }
       qk += red[w][cg][8];
+      if constexpr (kLogit) {
+        nk += red[w][cg][9];
+        nq += red[w][cg][10];
+      }
     }
+  }
+  float sk = 1.f;   // 1 / |k| (prologue)
+  if (qk_norm) {
+    sk = inv_l2(nk);
+    const float sq = inv_l2(nq);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      rk[j] *= sk;
+      rq[j] *= sq;
+    }
+    qk *= sk * sq;
   }
   const E* vh = v + static_cast<size_t>(nh) * DV + col0 + 4 * cg;
   float u[4];
@@ -139,7 +183,8 @@ kda_decode_kernel(const typename Ty<IO>::Elem* __restrict__ q,
   for (int i = 0; i < RPT; ++i) {
     const int r = rg + RG * i;
     float4 w = s[i];
-    w.x += kr[i] * u[0]; w.y += kr[i] * u[1]; w.z += kr[i] * u[2]; w.w += kr[i] * u[3];
+    const float kn = kr[i] * sk;
+    w.x += kn * u[0]; w.y += kn * u[1]; w.z += kn * u[2]; w.w += kn * u[3];
     store_streaming(S_out + sbase + static_cast<size_t>(r) * DV + col0 + 4 * cg, w);
   }
 }
@@ -152,45 +197,46 @@ static int pick_cw(long nh, int dv) {
   return cw;
 }
 
-template <typename IO, int DK, int CW>
+template <typename IO, int DK, int CW, bool kLogit>
 static hipError_t launch_dec(const DecodeArgs& a) {
   using Cf = DecodeCfg<DK, CW>;
   using E = typename Ty<IO>::Elem;
   const long nh = static_cast<long>(a.N) * a.H;
   dim3 grid(static_cast<unsigned>(nh * (a.dv / CW)));
-  hipLaunchKernelGGL((kda_decode_kernel<IO, DK, CW>), grid, dim3(Cf::NTH), 0,
+  hipLaunchKernelGGL((kda_decode_kernel<IO, DK, CW, kLogit>), grid, dim3(Cf::NTH), 0,
                      static_cast<hipStream_t>(a.stream),
                      static_cast<const E*>(a.q), static_cast<const E*>(a.k),
-                     static_cast<const E*>(a.v), a.alpha, a.beta, a.S_in,
-                     static_cast<E*>(a.o), a.S_out, static_cast<int>(nh), a.dv);
+                     static_cast<const E*>(a.v), a.gate, a.beta, a.S_in,
+                     static_cast<E*>(a.o), a.S_out, static_cast<int>(nh), a.dv, a.qk_map);
   return hipGetLastError();
 }
 
-template <typename IO, int DK>
+template <typename IO, int DK, bool kLogit>
 static hipError_t dispatch_cw(const DecodeArgs& a, int cw) {
   switch (cw) {
-    case 16: return launch_dec<IO, DK, 16>(a);
-    case 32: return launch_dec<IO, DK, 32>(a);
-    case 64: return launch_dec<IO, DK, 64>(a);
-    case 128: return launch_dec<IO, DK, 128>(a);
+    case 16: return launch_dec<IO, DK, 16, kLogit>(a);
+    case 32: return launch_dec<IO, DK, 32, kLogit>(a);
+    case 64: return launch_dec<IO, DK, 64, kLogit>(a);
+    case 128: return launch_dec<IO, DK, 128, kLogit>(a);
   }
   return hipErrorInvalidValue;
 }
 
-template <typename IO>
+template <typename IO, bool kLogit>
 static hipError_t dispatch_dk(const DecodeArgs& a, int cw) {
   switch (a.dk) {
-    case 16: return dispatch_cw<IO, 16>(a, cw);
-    case 32: return dispatch_cw<IO, 32>(a, cw);
-    case 64: return dispatch_cw<IO, 64>(a, cw);
-    case 128: return dispatch_cw<IO, 128>(a, cw);
+    case 16: return dispatch_cw<IO, 16, kLogit>(a, cw);
+    case 32: return dispatch_cw<IO, 32, kLogit>(a, cw);
+    case 64: return dispatch_cw<IO, 64, kLogit>(a, cw);
+    case 128: return dispatch_cw<IO, 128, kLogit>(a, cw);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const DecodeArgs& a) {
   const int cw = pick_cw(static_cast<long>(a.N) * a.H, a.dv);
-  return a.bf16 ? dispatch_dk<bf16_t>(a, cw) : dispatch_dk<float>(a, cw);
+  if (a.logits) return a.bf16 ? dispatch_dk<bf16_t, true>(a, cw) : dispatch_dk<float, true>(a, cw);
+  return a.bf16 ? dispatch_dk<bf16_t, false>(a, cw) : dispatch_dk<float, false>(a, cw);
 }
 
 }  // namespace kda

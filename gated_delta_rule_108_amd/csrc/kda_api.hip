@@ -58,7 +58,7 @@ const char* kda_status_string(kda_status s) {
     case KDA_OK: return "ok";
     case KDA_ERR_NULL: return "a required pointer is NULL";
     case KDA_ERR_SHAPE: return "a size is out of range";
-    case KDA_ERR_UNSUPPORTED: return "unsupported dk, dv, chunk size or dtype";
+    case KDA_ERR_UNSUPPORTED: return "unsupported dk, dv, chunk size, dtype or q/k map";
     case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case KDA_ERR_ALIAS: return "an output overlaps an input";
     case KDA_ERR_WORKSPACE: return "workspace missing or too small";
@@ -77,10 +77,16 @@ size_t kda_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int C, k
   return kda::prefill_workspace(B, T, H, dk, dv, C, dt == KDA_BF16);
 }
 
-kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, const float* alpha,
-                               const float* beta, const float* S0, void* o, float* S_T, int B,
-                               int T, int H, int dk, int dv, int C, kda_dtype dt, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by kda_prefill_chunked (alpha: fp32 gates) and
+// kda_prefill_chunked_logits (alpha: gate logits of type dt, beta: logits).
+kda_status prefill_impl(const void* q, const void* k, const void* v, const void* alpha,
+                        const float* beta, const float* S0, void* o, float* S_T, int B, int T,
+                        int H, int dk, int dv, int C, kda_dtype dt, bool logits, int qk_map,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   C = chunk_run(C);
   if (B < 1 || H < 1 || T < 0) return KDA_ERR_SHAPE;
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
@@ -95,12 +101,13 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
   if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need)) return KDA_ERR_WORKSPACE;
 
   const size_t e = (dt == KDA_BF16) ? 2 : 4;
+  const size_t ea = logits ? e : 4;   // gate element: logit of type dt, or fp32 alpha
   const size_t ntok = static_cast<size_t>(B) * T * H;
   const size_t nst = static_cast<size_t>(B) * H * dk * dv * 4;
   if (has_tokens) {
     const Span so = span(o, ntok * dv * e);
     const Span ins[] = {span(q, ntok * dk * e), span(k, ntok * dk * e), span(v, ntok * dv * e),
-                        span(alpha, ntok * dk * 4), span(beta, ntok * 4),
+                        span(alpha, ntok * dk * ea), span(beta, ntok * 4),
                         S0 ? span(S0, nst) : Span{0, 0}, S_T ? span(S_T, nst) : Span{0, 0}};
     for (const Span& s : ins)
       if (overlap(so, s)) return KDA_ERR_ALIAS;
@@ -108,7 +115,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
   if (ws_need > 0) {
     const Span sw = span(workspace, ws_need);
     const Span all[] = {span(q, ntok * dk * e), span(k, ntok * dk * e), span(v, ntok * dv * e),
-                        span(alpha, ntok * dk * 4), span(beta, ntok * 4), span(o, ntok * dv * e),
+                        span(alpha, ntok * dk * ea), span(beta, ntok * 4), span(o, ntok * dv * e),
                         S0 ? span(S0, nst) : Span{0, 0}, S_T ? span(S_T, nst) : Span{0, 0}};
     for (const Span& s : all)
       if (overlap(sw, s)) return KDA_ERR_ALIAS;
@@ -118,7 +125,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
     if (S0 && S0 != S_T && overlap(st, span(S0, nst))) return KDA_ERR_ALIAS;
     if (has_tokens) {
       const Span ins[] = {span(q, ntok * dk * e), span(k, ntok * dk * e), span(v, ntok * dv * e),
-                          span(alpha, ntok * dk * 4), span(beta, ntok * 4)};
+                          span(alpha, ntok * dk * ea), span(beta, ntok * 4)};
       for (const Span& s : ins)
         if (overlap(st, s)) return KDA_ERR_ALIAS;
     }
@@ -127,15 +134,16 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
   if (dev != KDA_OK) return dev;
   if (!S_T && !has_tokens) return KDA_OK;  // nothing to compute or write
 
-  kda::PrefillArgs a{q, k, v, alpha, beta, S0, o, S_T, B, T, H, dk, dv, C, dt == KDA_BF16, stream,
-                     workspace, workspace_bytes};
+  kda::PrefillArgs a{q,  k,  v,  alpha, beta, S0, o,  S_T,          B,         T,
+                     H,  dk, dv, C,     dt == KDA_BF16,   stream, workspace, workspace_bytes,
+                     logits, qk_map};
   if (kda::launch_prefill(a) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
 }
 
-kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* alpha,
-                           const float* beta, const float* S_in, void* o, float* S_out, int N,
-                           int H, int dk, int dv, kda_dtype dt, void* stream) {
+kda_status decode_impl(const void* q, const void* k, const void* v, const void* alpha,
+                       const float* beta, const float* S_in, void* o, float* S_out, int N, int H,
+                       int dk, int dv, kda_dtype dt, bool logits, int qk_map, void* stream) {
   if (N < 1 || H < 1) return KDA_ERR_SHAPE;
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
@@ -144,10 +152,11 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
   for (const void* p : ptrs)
     if (!aligned16(p)) return KDA_ERR_ALIGN;
   const size_t e = (dt == KDA_BF16) ? 2 : 4;
+  const size_t ea = logits ? e : 4;
   const size_t nh = static_cast<size_t>(N) * H;
   const size_t nst = nh * dk * dv * 4;
   const Span ins[] = {span(q, nh * dk * e), span(k, nh * dk * e), span(v, nh * dv * e),
-                      span(alpha, nh * dk * 4), span(beta, nh * 4), span(S_in, nst)};
+                      span(alpha, nh * dk * ea), span(beta, nh * 4), span(S_in, nst)};
   const Span so = span(o, nh * dv * e), ss = span(S_out, nst);
   for (const Span& s : ins)
     if (overlap(so, s)) return KDA_ERR_ALIAS;
@@ -157,9 +166,49 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
   if (S_out != S_in && overlap(ss, ins[5])) return KDA_ERR_ALIAS;  // equal is in place
   const kda_status dev = check_device();
   if (dev != KDA_OK) return dev;
-  kda::DecodeArgs a{q, k, v, alpha, beta, S_in, o, S_out, N, H, dk, dv, dt == KDA_BF16, stream};
+  kda::DecodeArgs a{q, k, v, alpha, beta, S_in, o, S_out, N, H, dk, dv, dt == KDA_BF16, stream,
+                    logits, qk_map};
   if (kda::launch_decode(a) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
+}
+
+bool qk_map_ok(kda_qk_map m) { return m == KDA_QK_AS_GIVEN || m == KDA_QK_L2 || m == KDA_QK_SILU_L2; }
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, const float* S0, void* o, float* S_T, int B,
+                               int T, int H, int dk, int dv, int C, kda_dtype dt, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return prefill_impl(q, k, v, alpha, beta, S0, o, S_T, B, T, H, dk, dv, C, dt, false, 0,
+                      workspace, workspace_bytes, stream);
+}
+
+kda_status kda_prefill_chunked_logits(const void* q, const void* k, const void* v, const void* g,
+                                      const float* b, const float* S0, void* o, float* S_T, int B,
+                                      int T, int H, int dk, int dv, int C, kda_dtype dt,
+                                      kda_qk_map qk_map, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (!qk_map_ok(qk_map)) return KDA_ERR_UNSUPPORTED;
+  return prefill_impl(q, k, v, g, b, S0, o, S_T, B, T, H, dk, dv, C, dt, true,
+                      static_cast<int>(qk_map), workspace, workspace_bytes, stream);
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* S_in, void* o, float* S_out, int N,
+                           int H, int dk, int dv, kda_dtype dt, void* stream) {
+  return decode_impl(q, k, v, alpha, beta, S_in, o, S_out, N, H, dk, dv, dt, false, 0, stream);
+}
+
+kda_status kda_decode_step_logits(const void* q, const void* k, const void* v, const void* g,
+                                  const float* b, const float* S_in, void* o, float* S_out,
+                                  int N, int H, int dk, int dv, kda_dtype dt, kda_qk_map qk_map,
+                                  void* stream) {
+  if (!qk_map_ok(qk_map)) return KDA_ERR_UNSUPPORTED;
+  return decode_impl(q, k, v, g, b, S_in, o, S_out, N, H, dk, dv, dt, true,
+                     static_cast<int>(qk_map), stream);
 }
 
 }  // extern "C"

@@ -52,6 +52,31 @@ template <> struct Ty<bf16_t> {
 };
 
 // ---------------------------------------------------------------------------
+// Input prologue: the recurrence's inputs from raw projections.
+//   gate:     alpha = exp(-softplus(g)) = 1 / (1 + e^g)   (0 at g = +inf, 1 at -inf)
+//   strength: beta = sigmoid(b) = 1 / (1 + e^-b)
+//   feature:  silu(x) = x sigmoid(x), then x / max(||x||_2, 1e-12) per row
+// The SiLU and the sigmoid of the write strength follow the DeltaNet module on
+// "22580: от GPT-2 до Kimi K3, объяснение", section "DeltaNet, или Fast Weight
+// Programmers"; the gate form keeps every real logit inside (0, 1), as the
+// gate of section "Gated Delta Net" of "From GPT-2 to Kimi K3, Explained"
+// must be.  Hardware exp2 and reciprocal, each within about one ulp.
+// ---------------------------------------------------------------------------
+enum QkMap : int { kQkAsGiven = 0, kQkL2 = 1, kQkSiluL2 = 2 };
+
+__device__ __forceinline__ float gate_from_logit(float g) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(g));
+}
+__device__ __forceinline__ float sigmoid_f(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(-x));
+}
+__device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
+// 1 / max(sqrt(sum of squares), 1e-12).
+__device__ __forceinline__ float inv_l2(float sumsq) {
+  return sumsq < 1e-24f ? 1e12f : __builtin_amdgcn_rsqf(sumsq);
+}
+
+// ---------------------------------------------------------------------------
 // 16x16 output tiles on the matrix cores (used by the prefill kernel).
 //
 // Every operand is read from a row-major array whose rows are indexed by the

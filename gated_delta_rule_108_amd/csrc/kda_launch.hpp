@@ -11,22 +11,24 @@ struct DecodeArgs {
   const void* q;
   const void* k;
   const void* v;
-  const float* alpha;
-  const float* beta;
+  const void* gate;   // alpha (fp32), or gate logits g in the I/O type when logits
+  const float* beta;  // beta, or its logit when logits
   const float* S_in;
   void* o;
   float* S_out;
   int N, H, dk, dv;
   bool bf16;
   void* stream;
+  bool logits;        // run the input prologue (see kda_device.hpp)
+  int qk_map;         // QkMap, used when logits
 };
 
 struct PrefillArgs {
   const void* q;
   const void* k;
   const void* v;
-  const float* alpha;
-  const float* beta;
+  const void* gate;   // alpha (fp32), or gate logits g in the I/O type when logits
+  const float* beta;  // beta, or its logit when logits
   const float* S0;   // may be null (zeros)
   void* o;
   float* S_T;        // may be null (not written)
@@ -35,6 +37,8 @@ struct PrefillArgs {
   void* stream;
   void* workspace;          // split path only (see prefill_workspace)
   size_t workspace_bytes;
+  bool logits;              // run the input prologue (see kda_device.hpp)
+  int qk_map;               // QkMap, used when logits
 };
 
 hipError_t launch_decode(const DecodeArgs& a);

@@ -161,6 +161,9 @@ template <> struct Quad<bf16_t> {
   __device__ __forceinline__ static void store(uint16_t* p, float a, float b, float c, float d) {
     *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
   }
+  __device__ __forceinline__ static T make(float a, float b, float c, float d) {
+    return make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+  }
 };
 template <> struct Quad<float> {
   using T = float4;
@@ -173,6 +176,9 @@ template <> struct Quad<float> {
   }
   __device__ __forceinline__ static void store(float* p, float a, float b, float c, float d) {
     *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  }
+  __device__ __forceinline__ static T make(float a, float b, float c, float d) {
+    return make_float4(a, b, c, d);
   }
 };
 
@@ -541,15 +547,23 @@ constexpr int kMaxLds = 160 * 1024;
 // writes them to the chunks' workspace records (W, Q.E, (K.E')^T, P, chunk
 // decay, U~; segn records per chain) for the scan kernel; the next chunk's
 // inputs load while the current one is processed.
-template <typename OpT, int DK, int C, int DVT, bool kPrep = false>
+//
+// kLogit = false: ggate is alpha (fp32), gbeta is beta, q and k are used as
+// given.  kLogit = true: the input prologue runs on the fly: ggate holds
+// gate logits g in the I/O type (alpha = 1 / (1 + e^g)), gbeta holds
+// write-strength logits (beta = sigmoid), and q, k pass through qk_map
+// (QkMap: as given, L2-normalised, or SiLU then L2-normalised per token).
+// The row norms are sums of squares over the chunk's registers, reduced
+// across the lanes of a wave and, at dk = 128, across two waves in LDS.
+template <typename OpT, int DK, int C, int DVT, bool kPrep = false, bool kLogit = false>
 __global__ void __launch_bounds__(512)
 kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
                    const typename Ty<OpT>::Elem* __restrict__ gk,
                    const typename Ty<OpT>::Elem* __restrict__ gv,
-                   const float* __restrict__ galpha, const float* __restrict__ gbeta,
+                   const void* __restrict__ ggate, const float* __restrict__ gbeta,
                    const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float* gST,
                    int B, int T, int H, int DV, char* __restrict__ gws, int cpb, int seg0,
-                   int segn) {
+                   int segn, int qk_map) {
   using Cf = PCfg<OpT, DK, C, DVT>;
   using E = typename Ty<OpT>::Elem;
   using PT = typename Pair<OpT>::T;
@@ -589,6 +603,13 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const float* galpha = static_cast<const float*>(ggate);   // kLogit = false
+  const E* glogit = static_cast<const E*>(ggate);           // kLogit = true
+  // Per-row sums of squares of k and q, [part][k, q][C], part = which half of
+  // the channels at dk = 128.  Lives in ZB, which is idle until phase SO.
+  float* sNRM = ZB;
+  const bool qk_norm = kLogit && qk_map != kQkAsGiven;
+  const bool qk_silu = kLogit && qk_map == kQkSiluL2;
 
   // Workgroup -> (chain, slab).  Consecutive workgroups are dealt round-robin
   // to the 8 XCDs; keep all slabs of one chain on one XCD so they share L2.
@@ -644,12 +665,14 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
   // padding (gate 1, key/query/value 0, strength 0) when consumed.
   using QT = typename Quad<OpT>::T;
   float ga[Cf::NGT][4][4];      // alpha [row][channel]
+  QT gg[Cf::NGT][4];            // gate logits (kLogit), converted to ga in G1
   QT gkk[Cf::NGT][4], gqq[Cf::NGT][4];
   u32x4 gvv[Cf::NVT][4];
   float gbe = 0.f;
   auto fetch_gates = [&](int tn) {
     const size_t base = (row0 + static_cast<size_t>(tn) * H) * DK;
     const float* pa = galpha + base;
+    const E* pg = glogit + base;
     const E* pk = gk + base;
     const E* pq = gq + base;
     const int jmax = T - 1 - tn;
@@ -664,11 +687,15 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int off = min(16 * J + 4 * h + j, jmax) * rsK + c;
-          const float4 a4 = *reinterpret_cast<const float4*>(pa + off);
-          ga[it][j][0] = a4.x;
-          ga[it][j][1] = a4.y;
-          ga[it][j][2] = a4.z;
-          ga[it][j][3] = a4.w;
+          if constexpr (kLogit) {
+            gg[it][j] = Quad<OpT>::load(pg + off);
+          } else {
+            const float4 a4 = *reinterpret_cast<const float4*>(pa + off);
+            ga[it][j][0] = a4.x;
+            ga[it][j][1] = a4.y;
+            ga[it][j][2] = a4.z;
+            ga[it][j][3] = a4.w;
+          }
           gkk[it][j] = Quad<OpT>::load(pk + off);
           gqq[it][j] = Quad<OpT>::load(pq + off);
         }
@@ -711,7 +738,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     const bool more = ch + 1 < ch_end;
     const bool full = t0 + C <= T;   // no padding rows in this chunk
     // ================= G1: pad the fetched chunk, within-block cumulative gates
-    if (tid < C) sBE[tid] = (t0 + tid < T) ? gbe : 0.f;
+    if (tid < C) sBE[tid] = (t0 + tid < T) ? (kLogit ? sigmoid_f(gbe) : gbe) : 0.f;
     fetch_beta(more ? t0 + C : t0);   // unconditional: uniform memory-op counts
     if (tid < NB) sFL[tid] = 0;
     // Per gate item: quarter products of alpha, combined across the four
@@ -725,6 +752,12 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       if (Cf::NGI % NTH == 0 || item < Cf::NGI) {
         const int h = item % 4, g = item / 4;
         const int J = g / (DK / 4), c = 4 * (g % (DK / 4));
+        if constexpr (kLogit) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) ga[it][j][x] = gate_from_logit(Quad<OpT>::get(gg[it][j], x));
+        }
         if (!full) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -733,6 +766,16 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
             for (int x = 0; x < 4; ++x) ga[it][j][x] = valid ? ga[it][j][x] : 1.f;
             gkk[it][j] = valid ? gkk[it][j] : Quad<OpT>::zero();
             gqq[it][j] = valid ? gqq[it][j] : Quad<OpT>::zero();
+          }
+        }
+        if (qk_silu) {   // SiLU in place (rounded back to the I/O type)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const QT kq = gkk[it][j], qq = gqq[it][j];
+            gkk[it][j] = Quad<OpT>::make(silu_f(Quad<OpT>::get(kq, 0)), silu_f(Quad<OpT>::get(kq, 1)),
+                                         silu_f(Quad<OpT>::get(kq, 2)), silu_f(Quad<OpT>::get(kq, 3)));
+            gqq[it][j] = Quad<OpT>::make(silu_f(Quad<OpT>::get(qq, 0)), silu_f(Quad<OpT>::get(qq, 1)),
+                                         silu_f(Quad<OpT>::get(qq, 2)), silu_f(Quad<OpT>::get(qq, 3)));
           }
         }
 #pragma unroll
@@ -747,6 +790,44 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         if (h == 0)
           *reinterpret_cast<float4*>(sBT + J * DK + c) =
               make_float4(bt[it][0], bt[it][1], bt[it][2], bt[it][3]);
+      }
+      if (qk_norm) {
+        // Row sums of squares of k and q: this lane's four channels, then the
+        // lanes of the wave that hold the same rows (lane bits 2.. pick the
+        // channel quad), then, at dk = 128, the two waves of a block in LDS.
+        constexpr int QPW = (DK / 4) < 16 ? (DK / 4) : 16;   // quads of a row per wave
+        const bool active = Cf::NGI % NTH == 0 || item < Cf::NGI;
+        float nk[4], nq[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          nk[j] = 0.f;
+          nq[j] = 0.f;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const float kx = Quad<OpT>::get(gkk[it][j], x), qx = Quad<OpT>::get(gqq[it][j], x);
+            nk[j] += kx * kx;
+            nq[j] += qx * qx;
+          }
+          nk[j] = active ? nk[j] : 0.f;
+          nq[j] = active ? nq[j] : 0.f;
+        }
+#pragma unroll
+        for (int off = 4; off < 4 * QPW; off <<= 1)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            nk[j] += __shfl_xor(nk[j], off);
+            nq[j] += __shfl_xor(nq[j], off);
+          }
+        const int h = item % 4, g = item / 4;
+        const int J = g / (DK / 4), part = (g % (DK / 4)) / 16;
+        if (active && (g % QPW) == 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 16 * J + 4 * h + j;
+            sNRM[(2 * part) * C + r] = nk[j];
+            sNRM[(2 * part + 1) * C + r] = nq[j];
+          }
+        }
       }
     }
 #pragma unroll
@@ -830,12 +911,22 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         for (int j = 0; j < 4; ++j) {
           const int r = 16 * J + 4 * h + j;
           const float be = sBE[r];
+          float sk = 1.f, sq = 1.f;   // 1 / row norms (prologue)
+          if (qk_norm) {
+            float nk = sNRM[r], nq = sNRM[C + r];
+            if constexpr (DK > 64) {
+              nk += sNRM[2 * C + r];
+              nq += sNRM[3 * C + r];
+            }
+            sk = inv_l2(nk);
+            sq = inv_l2(nq);
+          }
           float kr[4], qr[4], ki[4], kv[4];
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             f[x] *= ga[it][j][x];
-            const float kk = Quad<OpT>::get(gkk[it][j], x);
-            const float qq = Quad<OpT>::get(gqq[it][j], x);
+            const float kk = Quad<OpT>::get(gkk[it][j], x) * sk;
+            const float qq = Quad<OpT>::get(gqq[it][j], x) * sq;
             kr[x] = kk * f[x];
             qr[x] = qq * f[x];
             ki[x] = kk * hx[j][x];
@@ -885,18 +976,34 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
           // products of alpha on the vector units.
           const size_t cb = (row0 + static_cast<size_t>(t0 + 16 * R) * H) * DK;
           const int jmax = T - 1 - (t0 + 16 * R);
+          // prologue on single elements: feature map and 1 / row norm
+          auto feat = [&](const E* src, int row, int kq) {
+            float x = Ty<OpT>::to_f32(src[cb + row * rsK]);
+            if (qk_silu) x = Ty<OpT>::to_f32(Ty<OpT>::from_f32(silu_f(x)));
+            if (qk_norm) {
+              const int r = 16 * R + row;
+              float n = sNRM[kq * C + r];
+              if constexpr (DK > 64) n += sNRM[(2 + kq) * C + r];
+              x *= inv_l2(n);
+            }
+            return x;
+          };
+          auto gate = [&](int row, int c) {
+            if constexpr (kLogit) return gate_from_logit(Ty<OpT>::to_f32(glogit[cb + row * rsK + c]));
+            else return galpha[cb + row * rsK + c];
+          };
           for (int c = 0; c < DK; ++c) {
             if (sBT[R * DK + c] >= kUnsafeBlockDecay) continue;
-            const float ki = (ln.i <= jmax) ? Ty<OpT>::to_f32(gk[cb + ln.i * rsK + c]) : 0.f;
+            const float ki = (ln.i <= jmax) ? feat(gk + c, ln.i, 0) : 0.f;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
               const int rl = 4 * ln.g + rr;
               if (ln.i > rl) continue;
               float ratio = 1.f;
               for (int j = ln.i + 1; j <= rl; ++j)
-                ratio *= (j <= jmax) ? galpha[cb + j * rsK + c] : 1.f;
-              const float kr = (rl <= jmax) ? Ty<OpT>::to_f32(gk[cb + rl * rsK + c]) : 0.f;
-              const float qr = (rl <= jmax) ? Ty<OpT>::to_f32(gq[cb + rl * rsK + c]) : 0.f;
+                ratio *= (j <= jmax) ? gate(j, c) : 1.f;
+              const float kr = (rl <= jmax) ? feat(gk + c, rl, 0) : 0.f;
+              const float qr = (rl <= jmax) ? feat(gq + c, rl, 1) : 0.f;
               accA[rr] += kr * ki * ratio;
               accP[rr] += qr * ki * ratio;
             }
@@ -1243,15 +1350,16 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
 // ----------------------------------------------------------------------------
 // Host dispatch
 // ----------------------------------------------------------------------------
-template <typename OpT, int DK, int C, int DVT>
+template <typename OpT, int DK, int C, int DVT, bool kLogit>
 hipError_t launch_one(const PrefillArgs& a) {
   using E = typename Ty<OpT>::Elem;
   const long chains = static_cast<long>(a.B) * a.H;
   dim3 grid(static_cast<unsigned>(chains * (a.dv / DVT)));
-  hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT>), grid, dim3(PCfg<OpT, DK, C, DVT>::NTH), 0,
-                     static_cast<hipStream_t>(a.stream), static_cast<const E*>(a.q),
-                     static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.alpha, a.beta,
-                     a.S0, static_cast<E*>(a.o), a.S_T, a.B, a.T, a.H, a.dv, nullptr, 0, 0, 0);
+  hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT, false, kLogit>), grid,
+                     dim3(PCfg<OpT, DK, C, DVT>::NTH), 0, static_cast<hipStream_t>(a.stream),
+                     static_cast<const E*>(a.q), static_cast<const E*>(a.k),
+                     static_cast<const E*>(a.v), a.gate, a.beta, a.S0, static_cast<E*>(a.o),
+                     a.S_T, a.B, a.T, a.H, a.dv, nullptr, 0, 0, 0, a.qk_map);
   return hipGetLastError();
 }
 
@@ -1289,14 +1397,14 @@ int pick_dvt(long chains, int dv) {
   return best;
 }
 
-template <typename OpT, int DK, int C>
+template <typename OpT, int DK, int C, bool kLogit>
 hipError_t launch_c(const PrefillArgs& a) {
   const int dvt = pick_dvt<OpT, DK, C>(static_cast<long>(a.B) * a.H, a.dv);
   switch (dvt) {
-    case 16: if constexpr (fits<OpT, DK, C, 16>()) return launch_one<OpT, DK, C, 16>(a); break;
-    case 32: if constexpr (fits<OpT, DK, C, 32>()) return launch_one<OpT, DK, C, 32>(a); break;
-    case 64: if constexpr (fits<OpT, DK, C, 64>()) return launch_one<OpT, DK, C, 64>(a); break;
-    case 128: if constexpr (fits<OpT, DK, C, 128>()) return launch_one<OpT, DK, C, 128>(a); break;
+    case 16: if constexpr (fits<OpT, DK, C, 16>()) return launch_one<OpT, DK, C, 16, kLogit>(a); break;
+    case 32: if constexpr (fits<OpT, DK, C, 32>()) return launch_one<OpT, DK, C, 32, kLogit>(a); break;
+    case 64: if constexpr (fits<OpT, DK, C, 64>()) return launch_one<OpT, DK, C, 64, kLogit>(a); break;
+    case 128: if constexpr (fits<OpT, DK, C, 128>()) return launch_one<OpT, DK, C, 128, kLogit>(a); break;
   }
   return hipErrorInvalidValue;
 }

@@ -421,7 +421,7 @@ inline int prep_chunks_per_block(long chains, int nc) {
   return static_cast<int>((nc + runs - 1) / runs);
 }
 
-template <typename OpT, int DK, int C, int DVT>
+template <typename OpT, int DK, int C, int DVT, bool kLogit>
 hipError_t launch_prep(const PrefillArgs& a, int seg0, int segn) {
   using E = typename Ty<OpT>::Elem;
   if constexpr (!fits<OpT, DK, C, DVT>()) {
@@ -433,16 +433,17 @@ hipError_t launch_prep(const PrefillArgs& a, int seg0, int segn) {
     // all but the first chunk's loads hide behind compute.
     const int cpb = prep_chunks_per_block(chains, segn);
     const long blocks = chains * ((segn + cpb - 1) / cpb);
-    hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT, true>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(512), 0, static_cast<hipStream_t>(a.stream), static_cast<const E*>(a.q),
-                       static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.alpha, a.beta,
+    hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT, true, kLogit>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(512), 0,
+                       static_cast<hipStream_t>(a.stream), static_cast<const E*>(a.q),
+                       static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.gate, a.beta,
                        a.S0, static_cast<E*>(a.o), a.S_T, a.B, a.T, a.H, a.dv,
-                       static_cast<char*>(a.workspace), cpb, seg0, segn);
+                       static_cast<char*>(a.workspace), cpb, seg0, segn, a.qk_map);
     return hipGetLastError();
   }
 }
 
-template <typename OpT, int DK, int C>
+template <typename OpT, int DK, int C, bool kLogit>
 hipError_t launch_split(const PrefillArgs& a) {
   using E = typename Ty<OpT>::Elem;
   if constexpr (!scan_fits<OpT, DK, C>()) {
@@ -458,10 +459,10 @@ hipError_t launch_split(const PrefillArgs& a) {
       const int segn = p.nseg > 0 ? std::min(p.segch, p.nc - seg0) : 0;
       hipError_t e = hipErrorInvalidValue;
       switch (a.dv) {
-        case 16: e = launch_prep<OpT, DK, C, 16>(a, seg0, segn); break;
-        case 32: e = launch_prep<OpT, DK, C, 32>(a, seg0, segn); break;
-        case 64: e = launch_prep<OpT, DK, C, 64>(a, seg0, segn); break;
-        case 128: e = launch_prep<OpT, DK, C, 128>(a, seg0, segn); break;
+        case 16: e = launch_prep<OpT, DK, C, 16, kLogit>(a, seg0, segn); break;
+        case 32: e = launch_prep<OpT, DK, C, 32, kLogit>(a, seg0, segn); break;
+        case 64: e = launch_prep<OpT, DK, C, 64, kLogit>(a, seg0, segn); break;
+        case 128: e = launch_prep<OpT, DK, C, 128, kLogit>(a, seg0, segn); break;
       }
       if (e != hipSuccess) return e;
       const float* s_in = sgi == 0 ? a.S0 : carry;
@@ -497,8 +498,10 @@ bool use_split(long chains, int dv) {
 template <typename OpT, int DK, int C>
 hipError_t launch_any(const PrefillArgs& a) {
   const long chains = static_cast<long>(a.B) * a.H;
-  if (use_split<OpT, DK, C>(chains, a.dv)) return launch_split<OpT, DK, C>(a);
-  return launch_c<OpT, DK, C>(a);
+  const bool split = use_split<OpT, DK, C>(chains, a.dv);
+  if (a.logits)
+    return split ? launch_split<OpT, DK, C, true>(a) : launch_c<OpT, DK, C, true>(a);
+  return split ? launch_split<OpT, DK, C, false>(a) : launch_c<OpT, DK, C, false>(a);
 }
 
 template <typename OpT, int DK>

@@ -65,7 +65,7 @@ enum {
   KDA_OK = 0,
   KDA_ERR_NULL = -1,        /* a required pointer is NULL                          */
   KDA_ERR_SHAPE = -2,       /* a size is out of range (B, H, N < 1; T < 0)         */
-  KDA_ERR_UNSUPPORTED = -3, /* dk, dv, C or dtype not supported by any kernel      */
+  KDA_ERR_UNSUPPORTED = -3, /* dk, dv, C, dtype or q/k map not supported            */
   KDA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                    */
   KDA_ERR_ALIAS = -5,       /* an output overlaps an input it may not overlap      */
   KDA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than the query says    */
@@ -74,6 +74,15 @@ enum {
 };
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Feature map the *_logits entry points apply to q and k, per token and head:
+ *   KDA_QK_AS_GIVEN  q, k used as given
+ *   KDA_QK_L2        x / max(||x||_2, 1e-12) over the head dimension
+ *   KDA_QK_SILU_L2   the same after silu(x) = x * sigmoid(x); the SiLU
+ *                    output is rounded to the I/O type before the norm
+ * (the DeltaNet module on "22580: от GPT-2 до Kimi K3, объяснение", section
+ * "DeltaNet, или Fast Weight Programmers", normalises silu(q) and silu(k)). */
+typedef enum { KDA_QK_AS_GIVEN = 0, KDA_QK_L2 = 1, KDA_QK_SILU_L2 = 2 } kda_qk_map;
 
 /*
  * kda_prefill_workspace_bytes — bytes of device workspace kda_prefill_chunked
@@ -145,6 +154,38 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v,
                                size_t workspace_bytes, void* stream);
 
 /*
+ * kda_prefill_chunked_logits — kda_prefill_chunked with the input prologue
+ * fused into its kernels: the caller passes raw projections and every
+ * transform below runs on chip, in fp32, as each chunk is loaded.
+ *
+ *   q, k   [B, T, H, dk]  dt        raw queries and keys, mapped by qk_map
+ *   v      [B, T, H, dv]  dt        values
+ *   g      [B, T, H, dk]  dt        gate logits: alpha = exp(-softplus(g))
+ *                                   = 1 / (1 + e^g), in (0, 1) for every
+ *                                   real g (+inf gives 0, -inf gives 1)
+ *   b      [B, T, H]      float32   write-strength logits: beta = sigmoid(b)
+ *   qk_map                          KDA_QK_AS_GIVEN, KDA_QK_L2 or
+ *                                   KDA_QK_SILU_L2 (see kda_qk_map)
+ *   all other arguments as kda_prefill_chunked, including the workspace
+ *   (kda_prefill_workspace_bytes gives its size; the records are the same)
+ *
+ * The result equals kda_prefill_chunked on alpha = exp(-softplus(g)), beta =
+ * sigmoid(b) and the mapped q, k, up to rounding.  The gate is read at the
+ * I/O type's width (bf16: 2 bytes instead of 4 per key channel and token).
+ * Sources: the module on "22580: от GPT-2 до Kimi K3, объяснение", section
+ * "DeltaNet, или Fast Weight Programmers" (SiLU, L2 norm, sigmoid strength);
+ * the gate must lie in [0, 1] ("From GPT-2 to Kimi K3, Explained", section
+ * "Gated Delta Net"), which exp(-softplus(g)) guarantees.
+ * Errors: as kda_prefill_chunked; an unknown qk_map is KDA_ERR_UNSUPPORTED.
+ */
+kda_status kda_prefill_chunked_logits(const void* q, const void* k, const void* v,
+                                      const void* g, const float* b, const float* S0,
+                                      void* o, float* S_T, int B, int T, int H, int dk,
+                                      int dv, int C, kda_dtype dt, kda_qk_map qk_map,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/*
  * kda_decode_step — one recurrence step for N sequences x H heads (the same
  * step as one token of the prefill; the pages' decode path calls the layer
  * with t = 1 and the cached state, "From GPT-2 to Kimi K3, Explained",
@@ -167,6 +208,19 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            const float* S_in, void* o, float* S_out,
                            int N, int H, int dk, int dv, kda_dtype dt,
                            void* stream);
+
+/*
+ * kda_decode_step_logits — kda_decode_step with the input prologue of
+ * kda_prefill_chunked_logits fused in: q, k [N, H, dk] raw (mapped by
+ * qk_map), g [N, H, dk] gate logits of type dt, b [N, H] float32
+ * write-strength logits; all other arguments as kda_decode_step.  One call
+ * is exactly one token of kda_prefill_chunked_logits.
+ * Errors: as kda_decode_step; an unknown qk_map is KDA_ERR_UNSUPPORTED.
+ */
+kda_status kda_decode_step_logits(const void* q, const void* k, const void* v,
+                                  const void* g, const float* b, const float* S_in,
+                                  void* o, float* S_out, int N, int H, int dk, int dv,
+                                  kda_dtype dt, kda_qk_map qk_map, void* stream);
 
 /* kda_status_string — static, human-readable text for a status code. */
 const char* kda_status_string(kda_status s);

@@ -25,8 +25,9 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_four_calls():
-    assert declared_functions() == ["kda_decode_step", "kda_prefill_chunked",
+def test_header_declares_the_six_calls():
+    assert declared_functions() == ["kda_decode_step", "kda_decode_step_logits",
+                                    "kda_prefill_chunked", "kda_prefill_chunked_logits",
                                     "kda_prefill_workspace_bytes", "kda_status_string"]
 
 
@@ -171,3 +172,47 @@ def test_workspace_query():
     assert lib.kda_prefill_workspace_bytes(1, 256, 1, 16, 16, 16, 0) == 16 * rec(16, 16, 16, 4)
     assert lib.kda_prefill_workspace_bytes(1, 256, 1, 16, 16, 12, 0) == bad
     assert lib.kda_prefill_workspace_bytes(0, 256, 1, 16, 16, 16, 0) == bad
+
+
+def prefill_logits(lib, **kw):
+    a = dict(q=addr(0), k=addr(1), v=addr(2), g=addr(3), b=addr(4), S0=addr(5),
+             o=addr(6), S_T=addr(7), B=1, T=64, H=2, dk=128, dv=128, C=64, dt=1, qk=1,
+             ws=addr(8), wsb=1 << 34, stream=None)
+    a.update(kw)
+    return lib.kda_prefill_chunked_logits(a["q"], a["k"], a["v"], a["g"], a["b"], a["S0"],
+                                          a["o"], a["S_T"], a["B"], a["T"], a["H"], a["dk"],
+                                          a["dv"], a["C"], a["dt"], a["qk"], a["ws"], a["wsb"],
+                                          a["stream"])
+
+
+def decode_logits(lib, **kw):
+    a = dict(q=addr(0), k=addr(1), v=addr(2), g=addr(3), b=addr(4), S=addr(5),
+             o=addr(6), S_out=addr(5), N=4, H=2, dk=128, dv=128, dt=1, qk=2, stream=None)
+    a.update(kw)
+    return lib.kda_decode_step_logits(a["q"], a["k"], a["v"], a["g"], a["b"], a["S"], a["o"],
+                                      a["S_out"], a["N"], a["H"], a["dk"], a["dv"], a["dt"],
+                                      a["qk"], a["stream"])
+
+
+def test_logits_entry_points_validate_like_the_plain_ones():
+    L = _lib()
+    lib = L.load()
+    for qk in (3, -1):
+        assert prefill_logits(lib, qk=qk) == L.KDA_ERR_UNSUPPORTED
+        assert decode_logits(lib, qk=qk) == L.KDA_ERR_UNSUPPORTED
+    assert prefill_logits(lib, g=None) == L.KDA_ERR_NULL
+    assert prefill_logits(lib, b=addr(4) + 4) == L.KDA_ERR_ALIGN
+    assert prefill_logits(lib, ws=None) == L.KDA_ERR_WORKSPACE
+    assert decode_logits(lib, g=None) == L.KDA_ERR_NULL
+    assert decode_logits(lib, N=0) == L.KDA_ERR_SHAPE
+    # the gate logits have the I/O type's width: with bf16 the gate array of
+    # B*T*H*dk elements spans 2 bytes each, so an output just past it is fine
+    # and one inside it overlaps
+    ntok = 1 * 64 * 2
+    g_end = addr(3) + ntok * 128 * 2
+    assert prefill_logits(lib, o=g_end - 16) == L.KDA_ERR_ALIAS
+    assert prefill_logits(lib, o=g_end) in (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+    assert prefill_logits(lib, o=g_end, dt=0, C=32) == L.KDA_ERR_ALIAS   # fp32: 4 bytes each
+    for qk in (0, 1, 2):
+        assert prefill_logits(lib, qk=qk) in (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+        assert decode_logits(lib, qk=qk) in (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)

@@ -1,0 +1,204 @@
+"""The fused input prologue on the GPU (kda_prefill_chunked_logits,
+kda_decode_step_logits) against the float64 prologue oracle.
+
+Each case draws raw projections once (seeded): q, k, v, gate logits g and
+write-strength logits b.  The same tensors go to the HIP path through the C
+ABI binding and, upcast to float64, to oracle.kda_recurrence_logits, which
+maps them (alpha = exp(-softplus(g)), beta = sigmoid(b), q/k normalised,
+optionally after SiLU) and runs the sequential recurrence.  The error is the
+relative Frobenius norm, separately for o and the state; the bar is 1e-4 for
+fp32 inputs and 2e-2 for bf16 inputs.
+
+With the identity map, raw Gaussian keys would make the recurrence blow up
+(|1 - beta |k|^2| >> 1), so those cases hand in keys already scaled to unit
+length, as the plain entry point expects.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import kda_decode_step_logits, kda_recurrence_logits
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+DEV = "cuda:0"
+QKI = {"as_given": 0, "l2": 1, "silu_l2": 2}
+
+
+def kda():
+    import gated_delta_rule_108_amd as m
+    return m
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def f64(t):
+    return t.detach().to("cpu").double().numpy()
+
+
+def unit_qk(inp):
+    """Scale q and k to unit rows (input preparation for the identity map)."""
+    out = dict(inp)
+    for n in ("q", "k"):
+        x = inp[n].float()
+        out[n] = (x / x.norm(dim=-1, keepdim=True).clamp_min(1e-30)).to(inp[n].dtype)
+    return out
+
+
+def run(inp, C, qk):
+    d = {k: (None if t is None else t.to(DEV)) for k, t in inp.items()}
+    o, S = kda().prefill_chunked_logits(d["q"], d["k"], d["v"], d["g"], d["b"], d["S0"],
+                                        chunk=C, qk_map=qk)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def oracle(inp, qk):
+    return kda_recurrence_logits(inp["q"], inp["k"], inp["v"], inp["g"], inp["b"], inp["S0"],
+                                 qk_map=QKI[qk])
+
+
+def check(inp, C, qk, label=""):
+    tol = TOL[inp["q"].dtype]
+    o, S = run(inp, C, qk)
+    o_ref, S_ref = oracle(inp, qk)
+    eo, es = rel(f64(o), o_ref), rel(f64(S), S_ref)
+    print(f"[{label} C={C} qk={qk}] rel_o={eo:.3e} rel_S={es:.3e}", flush=True)
+    assert np.isfinite(f64(o)).all() and np.isfinite(f64(S)).all()
+    assert eo < tol and es < tol, (eo, es)
+    return o, S
+
+
+@pytest.mark.parametrize("qk", ["as_given", "l2", "silu_l2"])
+@pytest.mark.parametrize("C", [16, 32])
+def test_tiny_fp32(qk, C):
+    inp = wl.make_prefill_logit_inputs(wl.PREFILL["tiny_fp32"])
+    if qk == "as_given":
+        inp = unit_qk(inp)
+    check(inp, C, qk, label="tiny fp32")
+
+
+@pytest.mark.parametrize("qk,C", [("l2", 64), ("silu_l2", 64), ("l2", 128)])
+def test_prefill_h16_t4k(qk, C):
+    """The H=16, T=4096 workload in full (split path), from raw projections."""
+    spec = wl.PREFILL["prefill_h16_t4k"]
+    inp = wl.make_prefill_logit_inputs(spec)
+    assert kda().prefill_workspace_bytes(1, 4096, 16, 128, 128, C) > 0
+    check(inp, C, qk, label="h16 t4k")
+
+
+@pytest.mark.parametrize("qk", ["l2", "silu_l2"])
+def test_fused_and_split_paths(qk):
+    """132 chains take the fused kernel, a single chain the split path; the
+    same chain matches the oracle both ways."""
+    spec = wl.PREFILL["prefill_b8_h32_t8k"]
+    big = wl.make_prefill_logit_inputs(spec, T=160, B=33, H=4)
+    assert kda().prefill_workspace_bytes(33, 160, 4, 128, 128, 64) == 0
+    o_big, S_big = run(big, 64, qk)
+    few = {k: (v[3:4].contiguous() if v is not None else v) for k, v in big.items()}
+    o_few, S_few = run(few, 64, qk)
+    o_ref, S_ref = oracle(few, qk)
+    for o, S in ((o_big[3:4], S_big[3:4]), (o_few, S_few)):
+        eo, es = rel(f64(o), o_ref), rel(f64(S), S_ref)
+        print(f"[paths qk={qk}] rel_o={eo:.3e} rel_S={es:.3e}", flush=True)
+        assert eo < 2e-2 and es < 2e-2
+
+
+@pytest.mark.parametrize("dk,dv,dtype,C,T,qk", [
+    (16, 16, torch.float32, 16, 77, "silu_l2"),
+    (32, 64, torch.float32, 32, 77, "l2"),
+    (64, 128, torch.float32, 16, 45, "silu_l2"),
+    (16, 32, torch.bfloat16, 16, 200, "l2"),
+    (64, 32, torch.bfloat16, 64, 77, "silu_l2"),
+    (128, 64, torch.bfloat16, 32, 77, "l2"),
+    (128, 128, torch.bfloat16, 64, 1, "silu_l2"),
+    (128, 128, torch.bfloat16, 64, 131, "l2"),
+])
+def test_head_dims_and_ragged_lengths(dk, dv, dtype, C, T, qk):
+    spec = wl.PrefillSpec("case", 2, 3, T, dk, dv, dtype, (C,), 40 + dk + dv, "softplus",
+                          0.05, "sigmoid")
+    check(wl.make_prefill_logit_inputs(spec), C, qk, label=f"dk={dk} dv={dv} T={T}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_extreme_logits_and_zero_rows(dtype):
+    """Infinite and huge logits (alpha exactly 0 or 1, beta exactly 0 or 1),
+    gates strong enough that a 16-row block's decay falls below 2^-100 (the
+    exact per-channel fallback), and all-zero q and k rows (norm floor)."""
+    g = torch.Generator().manual_seed(17)
+    B, T, H, d = 1, 160, 2, 32 if dtype == torch.float32 else 128
+    q = torch.randn(B, T, H, d, generator=g)
+    k = torch.randn(B, T, H, d, generator=g)
+    v = torch.randn(B, T, H, d, generator=g)
+    gl = torch.randn(B, T, H, d, generator=g)
+    b = torch.randn(B, T, H, generator=g)
+    gl[:, 5, :, 3] = float("inf")                # alpha = 0 exactly
+    gl[:, 40:56, 0, 7] = 1e4                     # e^g overflows: alpha = 0
+    gl[:, 70:90, 1, :8] = 30.0                   # alpha ~ 1e-13: below 2^-100 per block
+    gl[:, 100, :, :] = float("inf")              # every channel cleared at t = 100
+    gl[:, 110:120, :, :] = -float("inf")         # alpha = 1
+    b[:, 20] = float("inf")                      # beta = 1
+    b[:, 21] = -float("inf")                     # beta = 0
+    q[:, 30, 0] = 0.0                            # zero rows stay zero
+    k[:, 31, 1] = 0.0
+    S0 = torch.randn(B, H, d, d, generator=g)
+    inp = dict(q=q.to(dtype), k=k.to(dtype), v=v.to(dtype), g=gl.to(dtype), b=b, S0=S0)
+    for qk in ("l2", "silu_l2"):
+        check(inp, 32, qk, label="extreme logits")
+
+
+@pytest.mark.parametrize("dk,dv,N,H,dtype,qk", [
+    (16, 16, 3, 2, torch.float32, "as_given"), (32, 128, 2, 5, torch.float32, "l2"),
+    (128, 16, 1, 3, torch.float32, "silu_l2"), (64, 64, 4, 4, torch.bfloat16, "l2"),
+    (128, 128, 2, 3, torch.bfloat16, "silu_l2"), (128, 128, 64, 32, torch.bfloat16, "l2"),
+])
+def test_decode_steps(dk, dv, N, H, dtype, qk):
+    spec = wl.DecodeSpec("case", N, H, dk, dv, dtype, 5, dk + dv + N, 0.1, 0.0, 0.0)
+    S = wl.make_decode_state(spec)
+    st = wl.make_decode_logit_steps(spec)
+    if qk == "as_given":
+        st = unit_qk(st)
+    Sg, Sr = S.to(DEV), S.double().numpy()
+    tol = TOL[dtype]
+    for s in range(5):
+        a = {k: t[s].contiguous() for k, t in st.items()}
+        ag = {k: t.to(DEV) for k, t in a.items()}
+        og, Sg = kda().decode_step_logits(ag["q"], ag["k"], ag["v"], ag["g"], ag["b"], Sg,
+                                          qk_map=qk)
+        orf, Sr = kda_decode_step_logits(a["q"], a["k"], a["v"], a["g"], a["b"], Sr,
+                                         qk_map=QKI[qk])
+        torch.cuda.synchronize()
+        assert rel(f64(og), orf) < tol
+    es = rel(f64(Sg), Sr)
+    print(f"[decode dk={dk} dv={dv} qk={qk}] rel_S={es:.3e}", flush=True)
+    assert es < tol
+
+
+@pytest.mark.parametrize("qk", ["l2", "silu_l2"])
+def test_prefill_then_decode_equals_longer_prefill(qk):
+    """A state is the whole cache: prefill over T tokens then n decode steps
+    gives the outputs and state of a prefill over T + n tokens."""
+    spec = wl.PREFILL["prefill_h16_t4k"]
+    inp = wl.make_prefill_logit_inputs(spec, T=105, H=4)
+    T0 = 100
+    head = {k: (v[:, :T0].contiguous() if v is not None and v.dim() > 2 and k != "S0" else v)
+            for k, v in inp.items()}
+    o_long, S_long = run(inp, 64, qk)
+    _, S = run(head, 64, qk)
+    outs = []
+    for t in range(T0, 105):
+        og, S = kda().decode_step_logits(*(inp[n][:, t].contiguous().to(DEV)
+                                           for n in ("q", "k", "v", "g", "b")), S, qk_map=qk)
+        outs.append(og)
+    torch.cuda.synchronize()
+    o_dec = torch.stack(outs, 1)
+    o_ref, S_ref = oracle(inp, qk)
+    assert rel(f64(o_dec), o_ref[:, T0:]) < 2e-2 and rel(f64(S), S_ref) < 2e-2
+    assert rel(f64(o_dec), f64(o_long[:, T0:])) < 2e-2
+    assert rel(f64(S), f64(S_long)) < 1e-2

@@ -25,6 +25,12 @@ Workloads (token-major layouts: q,k [B,T,H,dk], v [B,T,H,dv], alpha
                     over t) draw alpha ~ U(0,0.5), the rest ~ U(0.99,1.0);
                     q,k,v,beta as prefill_h16_t4k; then 256 decode steps.
 
+Raw-projection inputs for the fused prologue (make_prefill_logit_inputs,
+make_decode_logit_steps) use the same shapes and draw the pre-activation
+values the recipes above name: q, k ~ N(0,1) NOT normalised, gate logits
+g ~ N(0,1) in the I/O dtype (the recurrence then uses alpha = exp(-softplus(g))),
+write-strength logits b ~ N(0,1) fp32 (beta = sigmoid(b)).
+
 Random numbers come from torch.Generator(device).manual_seed(seed).  The
 streams differ between CPU and GPU generators, so a test that compares the
 two paths always generates once and hands the same tensors to both.
@@ -38,7 +44,7 @@ import torch
 
 __all__ = ["PrefillSpec", "DecodeSpec", "PREFILL", "DECODE",
            "make_prefill_inputs", "make_decode_state", "make_decode_step_inputs",
-           "make_decode_steps"]
+           "make_decode_steps", "make_prefill_logit_inputs", "make_decode_logit_steps"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -157,6 +163,43 @@ def make_prefill_inputs(spec: PrefillSpec, device="cpu", T=None, B=None, H=None)
     return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(),
                 alpha=alpha.float().contiguous(), beta=beta.float().contiguous(),
                 S0=None if S0 is None else S0.float().contiguous())
+
+
+def make_prefill_logit_inputs(spec: PrefillSpec, device="cpu", T=None, B=None, H=None):
+    """Raw projections for the fused prologue: q, k, v and g in spec.dtype,
+    b fp32, S0 as make_prefill_inputs.  Returns a dict of contiguous tensors
+    (keys q, k, v, g, b, S0)."""
+    B = spec.B if B is None else B
+    H = spec.H if H is None else H
+    T = spec.T if T is None else T
+    dk, dv = spec.dk, spec.dv
+    g = _gen(device, spec.seed + 1000)
+    q = torch.randn(B, T, H, dk, generator=g, device=device).to(spec.dtype)
+    k = torch.randn(B, T, H, dk, generator=g, device=device).to(spec.dtype)
+    v = torch.randn(B, T, H, dv, generator=g, device=device).to(spec.dtype)
+    gl = torch.randn(B, T, H, dk, generator=g, device=device).to(spec.dtype)
+    b = torch.randn(B, T, H, generator=g, device=device)
+    S0 = None
+    if spec.s0_std > 0:
+        S0 = (spec.s0_std * torch.randn(B, H, dk, dv, generator=g, device=device)).float()
+    return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), g=gl.contiguous(),
+                b=b.float().contiguous(), S0=None if S0 is None else S0.contiguous())
+
+
+def make_decode_logit_steps(spec: DecodeSpec, device="cpu", N=None, steps=None):
+    """Every step's raw projections at once: q, k, g [S,N,H,dk] and v
+    [S,N,H,dv] in spec.dtype, b [S,N,H] fp32, all N(0,1)."""
+    N = spec.N if N is None else N
+    steps = spec.steps if steps is None else steps
+    H, dk, dv = spec.H, spec.dk, spec.dv
+    g = _gen(device, spec.seed + 1001)
+    q = torch.randn(steps, N, H, dk, generator=g, device=device).to(spec.dtype)
+    k = torch.randn(steps, N, H, dk, generator=g, device=device).to(spec.dtype)
+    v = torch.randn(steps, N, H, dv, generator=g, device=device).to(spec.dtype)
+    gl = torch.randn(steps, N, H, dk, generator=g, device=device).to(spec.dtype)
+    b = torch.randn(steps, N, H, generator=g, device=device)
+    return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), g=gl.contiguous(),
+                b=b.float().contiguous())
 
 
 def make_decode_state(spec: DecodeSpec, device="cpu", N=None):
