@@ -9,6 +9,8 @@ Alongside the headline it measures, on the same GPU:
   * decode: 256 sequences x 32 heads, 64 KiB fp32 state per head, in-place
     kda_decode_step calls (state GB/s against the HBM peak);
   * the B=8, H=32, T=8192 prefill (tokens/s and roofline);
+  * the H=16 prefill and the 256 x 32-head decode from raw projections
+    (gate logits, write-strength logits, q/k L2-normalised in the kernels);
   * the float64 oracle on the host cores over a bounded sample (cpu_baseline).
 """
 from __future__ import annotations
@@ -35,6 +37,15 @@ def prefill_alg_bytes(B, T, H, dk, dv, esize, with_s0):
     return tok * per_tok + state * (2 if with_s0 else 1)
 
 
+def prefill_logit_alg_bytes(B, T, H, dk, dv, esize, with_s0):
+    """As prefill_alg_bytes, with the gate read as logits of the I/O type
+    instead of fp32 alpha, and beta read as fp32 logits."""
+    tok = B * T * H
+    per_tok = esize * (2 * dk + dv) + esize * dk + 4 + esize * dv
+    state = B * H * dk * dv * 4
+    return tok * per_tok + state * (2 if with_s0 else 1)
+
+
 def prefill_flops(B, T, H, dk, dv, C):
     """Useful flops: 6 dk dv per token-head for the state work (W S, Q S,
     K^T U) plus 2 C (3 dk + 2 dv) for the chunk-local products (gated K K^T,
@@ -42,8 +53,10 @@ def prefill_flops(B, T, H, dk, dv, C):
     return B * T * H * (6 * dk * dv + 2 * C * (3 * dk + 2 * dv))
 
 
-def decode_alg_bytes(N, H, dk, dv, esize):
-    per_head = 2 * dk * dv * 4 + esize * (2 * dk + dv) + 4 * dk + 4 + esize * dv
+def decode_alg_bytes(N, H, dk, dv, esize, gate_bytes=4):
+    """State read and write plus one token's inputs and output per head; the
+    gate is fp32 alpha (4 bytes) or a logit of the I/O type."""
+    per_head = 2 * dk * dv * 4 + esize * (2 * dk + dv) + gate_bytes * dk + 4 + esize * dv
     return N * H * per_head
 
 
@@ -179,7 +192,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="headline prefill only (no decode / large prefill lines)")
-    ap.add_argument("--only", choices=["prefill", "decode", "large", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "large", "logits", "decode_logits",
+                                       "copy"], default=None,
                     help="run one leg only (for profiler runs); 'copy' times a plain "
                          "1 GiB device-to-device copy used to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -204,7 +218,8 @@ def main():
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
                           "ms_per_copy": ms, "GBps": 8 * n / (ms * 1e-3) / 1e9}), flush=True)
         return
-    legs = {"prefill", "decode", "large"} if args.only is None else {args.only}
+    legs = ({"prefill", "decode", "large", "logits", "decode_logits"} if args.only is None
+            else {args.only})
     if args.no_extra:
         legs = {"prefill"}
 
@@ -325,6 +340,62 @@ def extras(args, legs, out, torch, kda, wl, dev):
         }
         print(f"# prefill_b8_h32_t8k: {ms_l:.3f} ms/launch", file=sys.stderr, flush=True)
         del lg, lo, lS
+        torch.cuda.empty_cache()
+
+    if "logits" in legs:
+        # ---------------- H=16 prefill from raw projections (fused prologue)
+        spec = wl.PREFILL["prefill_h16_t4k"]
+        rg = wl.make_prefill_logit_inputs(spec, dev)
+        ro = torch.empty(spec.B, spec.T, spec.H, spec.dv, dtype=spec.dtype, device=dev)
+        rS = torch.empty(spec.B, spec.H, spec.dk, spec.dv, dtype=torch.float32, device=dev)
+
+        def rstep():
+            kda.prefill_chunked_logits(rg["q"], rg["k"], rg["v"], rg["g"], rg["b"], rg["S0"],
+                                       chunk=64, qk_map="l2", out=ro, state_out=rS)
+
+        ms_r, ms_rw = time_launches(rstep, args.steps, args.warmup, torch)
+        B, T, H, dk, dv = spec.B, spec.T, spec.H, spec.dk, spec.dv
+        rb = prefill_logit_alg_bytes(B, T, H, dk, dv, 2, False)
+        rf = prefill_flops(B, T, H, dk, dv, 64)
+        out["prefill_h16_t4k_logits"] = {
+            "C": 64, "qk_map": "l2", "us_per_launch": ms_r * 1e3,
+            "tokens_per_s": B * T / (ms_rw * 1e-3),
+            "GBps": rb / (ms_r * 1e-3) / 1e9, "frac_hbm": rb / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": profiled_traffic("prefill_h16_t4k_logits"), "alg_bytes_per_launch": rb,
+            "tflops": rf / (ms_r * 1e-3) / 1e12,
+            "frac_mfma": rf / (ms_r * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        }
+        print(f"# prefill_h16_t4k_logits: {ms_r * 1e3:.1f} us/launch", file=sys.stderr,
+              flush=True)
+        del rg, ro, rS
+        torch.cuda.empty_cache()
+
+    if "decode_logits" in legs:
+        # ---------------- decode from raw projections: 256 x 32 heads, in place
+        dspec = wl.DECODE["decode_n256_h32"]
+        S = wl.make_decode_state(dspec, dev)
+        nst = 8
+        st = wl.make_decode_logit_steps(dspec, dev, steps=nst)
+        od = torch.empty(dspec.N, dspec.H, dspec.dv, dtype=dspec.dtype, device=dev)
+        it = [0]
+
+        def lstep():
+            i = it[0] % nst
+            it[0] += 1
+            kda.decode_step_logits(st["q"][i], st["k"][i], st["v"][i], st["g"][i], st["b"][i],
+                                   S, qk_map="l2", out=od)
+
+        ms_d, _ = time_launches(lstep, max(args.steps, 20), args.warmup, torch)
+        dbytes = decode_alg_bytes(dspec.N, dspec.H, dspec.dk, dspec.dv, 2, gate_bytes=2)
+        out["decode_n256_h32_logits"] = {
+            "qk_map": "l2", "us_per_step": ms_d * 1e3,
+            "alg_GBps": dbytes / (ms_d * 1e-3) / 1e9,
+            "frac_hbm": dbytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": profiled_traffic("decode_n256_h32_logits"), "alg_bytes_per_step": dbytes,
+        }
+        print(f"# decode_n256_h32_logits: {ms_d * 1e3:.1f} us/step", file=sys.stderr,
+              flush=True)
+        del S, st, od
         torch.cuda.empty_cache()
 
 

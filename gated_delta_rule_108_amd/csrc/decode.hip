@@ -20,9 +20,11 @@
 //
 // kLogit = true runs the input prologue on the fly (kda_device.hpp): the gate
 // comes as logits g in the I/O type, beta as its logit, and q, k pass through
-// qk_map.  The row norms of q and k ride along the same reductions (two more
-// sums), and since every use of k and q is linear in them they are applied
-// after the reductions: r_k, r_q and q.k are rescaled, k^T u uses k / |k|.
+// qk_map.  Each row's mapped gate, key and query are computed once per
+// workgroup and staged in LDS.  The row norms of q and k ride along the same
+// reductions (two more sums), and since every use of k and q is linear in
+// them they are applied after the reductions: r_k, r_q and q.k are rescaled,
+// k^T u uses k / |k|.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -90,20 +92,29 @@ kda_decode_kernel(const typename Ty<IO>::Elem* __restrict__ q,
     const int r = rg + RG * i;
     s[i] = *reinterpret_cast<const float4*>(S_in + sbase + static_cast<size_t>(r) * DV + col0 + 4 * cg);
   }
+  // Row r's gate, key and query are read (and, with the prologue, mapped)
+  // once per workgroup, by thread r (NTH >= DK), and staged in LDS while the
+  // state loads are in flight, instead of by each of the CG threads that hold
+  // a piece of row r.
+  __shared__ float pro[3][DK];
+  if (tid < DK) {
+    float kv = Ty<IO>::to_f32(kh[tid]), qv = Ty<IO>::to_f32(qh[tid]);
+    if (qk_silu) {   // rounded back to the I/O type, as the prefill does
+      kv = Ty<IO>::to_f32(Ty<IO>::from_f32(silu_f(kv)));
+      qv = Ty<IO>::to_f32(Ty<IO>::from_f32(silu_f(qv)));
+    }
+    pro[0][tid] = kLogit ? gate_from_logit(Ty<IO>::to_f32(gh[tid])) : ah[tid];
+    pro[1][tid] = kv;
+    pro[2][tid] = qv;
+  }
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rg + RG * i;
-    float a, kv = Ty<IO>::to_f32(kh[r]), qv = Ty<IO>::to_f32(qh[r]);
+    const float a = pro[0][r], kv = pro[1][r], qv = pro[2][r];
     if constexpr (kLogit) {
-      a = gate_from_logit(Ty<IO>::to_f32(gh[r]));
-      if (qk_silu) {   // rounded back to the I/O type, as the prefill does
-        kv = Ty<IO>::to_f32(Ty<IO>::from_f32(silu_f(kv)));
-        qv = Ty<IO>::to_f32(Ty<IO>::from_f32(silu_f(qv)));
-      }
       nk += kv * kv;
       nq += qv * qv;
-    } else {
-      a = ah[r];
     }
     kr[i] = kv;
     s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;
