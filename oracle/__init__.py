@@ -3,6 +3,7 @@
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
 import anything under this directory.
 """
-from .kda_oracle import kda_recurrence, kda_decode_step, as_f64  # noqa: F401
+from .kda_oracle import (kda_recurrence, kda_decode_step, gdn_recurrence,  # noqa: F401
+                         gdn_decode_step, as_f64)
 from .kda_prologue import (QK_AS_GIVEN, QK_L2, QK_SILU_L2, kda_prologue,  # noqa: F401
                            kda_recurrence_logits, kda_decode_step_logits)

@@ -53,7 +53,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["kda_recurrence", "kda_decode_step", "as_f64"]
+__all__ = ["kda_recurrence", "kda_decode_step", "gdn_recurrence", "gdn_decode_step", "as_f64"]
 
 
 def as_f64(x) -> np.ndarray:
@@ -101,6 +101,33 @@ def kda_decode_step(q, k, v, alpha, beta, S):
     q, k, v, alpha, beta, S = (as_f64(x) for x in (q, k, v, alpha, beta, S))
     S_new, o = _step(q, k, v, alpha, beta, S.copy())
     return o, S_new
+
+
+def _channel_gate(a, like):
+    """A gate that is the same on every key channel: a [...] -> [..., dk];
+    None means 1 everywhere."""
+    if a is None:
+        return np.ones(like.shape)
+    return np.broadcast_to(as_f64(a)[..., None], like.shape)
+
+
+def gdn_recurrence(q, k, v, a, beta, S0=None):
+    """Gated DeltaNet (and, with a = None, DeltaNet) prefill, float64.
+
+    a: [B, T, H], one gate per token and head, or None for a = 1.  The other
+    arguments and the result are those of kda_recurrence.  GDN is the KDA
+    recurrence with the gate equal on every key channel: KDA refines GDN's
+    scalar gate into one value per channel ("From GPT-2 to Kimi K3,
+    Explained", sections "Gated Delta Net" and "KDA/Kimi Linear"), and a = 1
+    is plain DeltaNet (section "Gated Delta Net")."""
+    k64 = as_f64(k)
+    return kda_recurrence(q, k64, v, _channel_gate(a, k64), beta, S0)
+
+
+def gdn_decode_step(q, k, v, a, beta, S):
+    """One Gated DeltaNet decode step; a: [N, H] or None (DeltaNet)."""
+    k64 = as_f64(k)
+    return kda_decode_step(q, k64, v, _channel_gate(a, k64), beta, S)
 
 
 def _step(q, k, v, alpha, beta, S):
