@@ -17,6 +17,12 @@ where alpha = exp(-softplus(g)) (g has the dtype of q), beta = sigmoid(b)
 (b float32), and qk_map is "as_given", "l2" (x / max(|x|, 1e-12)) or
 "silu_l2" (the same after SiLU).
 
+Gated DeltaNet (one gate per token and head, a [B,T,H] / [N,H] float32) and
+DeltaNet (a=None, gate 1):
+
+    o, S_T = gdn_prefill_chunked(q, k, v, a, beta, S0=None, chunk=64)
+    o, S   = gdn_decode_step(q, k, v, a, beta, S)
+
 Layouts (token-major, as the attention projections produce them):
     prefill  q,k [B,T,H,dk]  v [B,T,H,dv]  alpha [B,T,H,dk]  beta [B,T,H]
              S0, S_T [B,H,dk,dv]  o [B,T,H,dv]
@@ -33,7 +39,7 @@ from . import _lib
 from ._lib import KDAError  # noqa: F401
 
 __all__ = ["prefill_chunked", "decode_step", "prefill_chunked_logits", "decode_step_logits",
-           "prefill_workspace_bytes", "KDAError", "lib"]
+           "gdn_prefill_chunked", "gdn_decode_step", "prefill_workspace_bytes", "KDAError", "lib"]
 
 _DT = {torch.bfloat16: _lib.KDA_BF16, torch.float32: _lib.KDA_F32}
 _QK = {"as_given": _lib.KDA_QK_AS_GIVEN, "l2": _lib.KDA_QK_L2, "silu_l2": _lib.KDA_QK_SILU_L2}
@@ -81,7 +87,16 @@ def prefill_chunked_logits(q, k, v, g, b, S0=None, chunk=64, qk_map="l2", out=No
     return _prefill(q, k, v, g, b, S0, chunk, out, state_out, return_state, _QK[qk_map])
 
 
+def gdn_prefill_chunked(q, k, v, a, beta, S0=None, chunk=64, out=None, state_out=None,
+                        return_state=True):
+    """Gated DeltaNet over whole sequences: one gate per token and head
+    (a [B,T,H] float32), or DeltaNet with a=None (gate 1)."""
+    return _prefill(q, k, v, a, beta, S0, chunk, out, state_out, return_state, "gdn")
+
+
 def _prefill(q, k, v, gate, beta, S0, chunk, out, state_out, return_state, qk):
+    """qk: None (per-channel alpha), "gdn" (scalar gate or None), or a QkMap
+    code (raw projections with the fused prologue)."""
     L = lib()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -89,10 +104,17 @@ def _prefill(q, k, v, gate, beta, S0, chunk, out, state_out, return_state, qk):
     if q.dtype not in _DT:
         raise TypeError(f"q: dtype {q.dtype} not supported")
     dt = q.dtype
-    gname, gdt = ("alpha", torch.float32) if qk is None else ("g", dt)
-    for n, t, d, s in (("q", q, dt, (B, T, H, dk)), ("k", k, dt, (B, T, H, dk)),
-                       ("v", v, dt, (B, T, H, dv)), (gname, gate, gdt, (B, T, H, dk)),
-                       ("beta" if qk is None else "b", beta, torch.float32, (B, T, H))):
+    checks = [("q", q, dt, (B, T, H, dk)), ("k", k, dt, (B, T, H, dk)),
+              ("v", v, dt, (B, T, H, dv)),
+              ("b" if isinstance(qk, int) else "beta", beta, torch.float32, (B, T, H))]
+    if qk is None:
+        checks.append(("alpha", gate, torch.float32, (B, T, H, dk)))
+    elif qk == "gdn":
+        if gate is not None:
+            checks.append(("a", gate, torch.float32, (B, T, H)))
+    else:
+        checks.append(("g", gate, dt, (B, T, H, dk)))
+    for n, t, d, s in checks:
         _check(n, t, d, s, dev)
     if S0 is not None:
         _check("S0", S0, torch.float32, (B, H, dk, dv), dev)
@@ -112,6 +134,11 @@ def _prefill(q, k, v, gate, beta, S0, chunk, out, state_out, return_state, qk):
                                    _ptr(o), _ptr(S_T), B, T, H, dk, dv, chunk, _DT[dt],
                                    _ptr(ws), ws_bytes, _stream(dev))
         where = "kda_prefill_chunked"
+    elif qk == "gdn":
+        st = L.kda_gdn_prefill_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
+                                       _ptr(S0), _ptr(o), _ptr(S_T), B, T, H, dk, dv, chunk,
+                                       _DT[dt], _ptr(ws), ws_bytes, _stream(dev))
+        where = "kda_gdn_prefill_chunked"
     else:
         st = L.kda_prefill_chunked_logits(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
                                           _ptr(S0), _ptr(o), _ptr(S_T), B, T, H, dk, dv, chunk,
@@ -135,6 +162,12 @@ def decode_step_logits(q, k, v, g, b, S, qk_map="l2", out=None, state_out=None):
     return _decode(q, k, v, g, b, S, out, state_out, _QK[qk_map])
 
 
+def gdn_decode_step(q, k, v, a, beta, S, out=None, state_out=None):
+    """One Gated DeltaNet step (a [N,H] float32, or None for DeltaNet);
+    state_out defaults to S itself (in place)."""
+    return _decode(q, k, v, a, beta, S, out, state_out, "gdn")
+
+
 def _decode(q, k, v, gate, beta, S, out, state_out, qk):
     L = lib()
     N, H, dk = q.shape
@@ -143,11 +176,17 @@ def _decode(q, k, v, gate, beta, S, out, state_out, qk):
     if q.dtype not in _DT:
         raise TypeError(f"q: dtype {q.dtype} not supported")
     dt = q.dtype
-    gname, gdt = ("alpha", torch.float32) if qk is None else ("g", dt)
-    for n, t, d, s in (("q", q, dt, (N, H, dk)), ("k", k, dt, (N, H, dk)),
-                       ("v", v, dt, (N, H, dv)), (gname, gate, gdt, (N, H, dk)),
-                       ("beta" if qk is None else "b", beta, torch.float32, (N, H)),
-                       ("S", S, torch.float32, (N, H, dk, dv))):
+    checks = [("q", q, dt, (N, H, dk)), ("k", k, dt, (N, H, dk)), ("v", v, dt, (N, H, dv)),
+              ("b" if isinstance(qk, int) else "beta", beta, torch.float32, (N, H)),
+              ("S", S, torch.float32, (N, H, dk, dv))]
+    if qk is None:
+        checks.append(("alpha", gate, torch.float32, (N, H, dk)))
+    elif qk == "gdn":
+        if gate is not None:
+            checks.append(("a", gate, torch.float32, (N, H)))
+    else:
+        checks.append(("g", gate, dt, (N, H, dk)))
+    for n, t, d, s in checks:
         _check(n, t, d, s, dev)
     o = torch.empty((N, H, dv), dtype=dt, device=dev) if out is None else out
     _check("out", o, dt, (N, H, dv), dev)
@@ -157,6 +196,10 @@ def _decode(q, k, v, gate, beta, S, out, state_out, qk):
         st = L.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S),
                                _ptr(o), _ptr(S_out), N, H, dk, dv, _DT[dt], _stream(dev))
         where = "kda_decode_step"
+    elif qk == "gdn":
+        st = L.kda_gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S),
+                                   _ptr(o), _ptr(S_out), N, H, dk, dv, _DT[dt], _stream(dev))
+        where = "kda_gdn_decode_step"
     else:
         st = L.kda_decode_step_logits(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
                                       _ptr(S), _ptr(o), _ptr(S_out), N, H, dk, dv, _DT[dt], qk,

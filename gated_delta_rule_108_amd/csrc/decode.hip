@@ -18,7 +18,9 @@
 // happen in a single pass; reductions over rows go through cross-lane
 // exchanges inside a wave and a small LDS exchange between waves.
 //
-// kLogit = true runs the input prologue on the fly (kda_device.hpp): the gate
+// kIn (GateIn) says how the gate arrives: one fp32 alpha per key channel; one
+// per token and head (Gated DeltaNet), or none (DeltaNet) when the pointer is
+// null; or, with kGateLogit, the input prologue on the fly: the gate
 // comes as logits g in the I/O type, beta as its logit, and q, k pass through
 // qk_map.  Each row's mapped gate, key and query are computed once per
 // workgroup and staged in LDS.  The row norms of q and k ride along the same
@@ -55,7 +57,7 @@ __device__ __forceinline__ void store_streaming(float* p, const float4& w) {
   __builtin_nontemporal_store(t, reinterpret_cast<f4v*>(p));
 }
 
-template <typename IO, int DK, int CW, bool kLogit>
+template <typename IO, int DK, int CW, int kIn>
 __global__ void __launch_bounds__(256)
 kda_decode_kernel(const typename Ty<IO>::Elem* __restrict__ q,
                   const typename Ty<IO>::Elem* __restrict__ k,
@@ -66,6 +68,8 @@ kda_decode_kernel(const typename Ty<IO>::Elem* __restrict__ q,
   using Cf = DecodeCfg<DK, CW>;
   using E = typename Ty<IO>::Elem;
   constexpr int CG = Cf::CG, RG = Cf::RG, RPT = Cf::RPT, NWV = Cf::NWV;
+  constexpr bool kLogit = kIn == kGateLogit;
+  constexpr bool kScalar = kIn == kGateScalar;
 
   const int tiles = DV / CW;
   const int nh = blockIdx.x / tiles;            // (n, h) flattened
@@ -103,7 +107,11 @@ kda_decode_kernel(const typename Ty<IO>::Elem* __restrict__ q,
       kv = Ty<IO>::to_f32(Ty<IO>::from_f32(silu_f(kv)));
       qv = Ty<IO>::to_f32(Ty<IO>::from_f32(silu_f(qv)));
     }
-    pro[0][tid] = kLogit ? gate_from_logit(Ty<IO>::to_f32(gh[tid])) : ah[tid];
+    float a;
+    if constexpr (kLogit) a = gate_from_logit(Ty<IO>::to_f32(gh[tid]));
+    else if constexpr (kScalar) a = gate != nullptr ? static_cast<const float*>(gate)[nh] : 1.f;
+    else a = ah[tid];
+    pro[0][tid] = a;
     pro[1][tid] = kv;
     pro[2][tid] = qv;
   }
@@ -208,13 +216,13 @@ static int pick_cw(long nh, int dv) {
   return cw;
 }
 
-template <typename IO, int DK, int CW, bool kLogit>
+template <typename IO, int DK, int CW, int kIn>
 static hipError_t launch_dec(const DecodeArgs& a) {
   using Cf = DecodeCfg<DK, CW>;
   using E = typename Ty<IO>::Elem;
   const long nh = static_cast<long>(a.N) * a.H;
   dim3 grid(static_cast<unsigned>(nh * (a.dv / CW)));
-  hipLaunchKernelGGL((kda_decode_kernel<IO, DK, CW, kLogit>), grid, dim3(Cf::NTH), 0,
+  hipLaunchKernelGGL((kda_decode_kernel<IO, DK, CW, kIn>), grid, dim3(Cf::NTH), 0,
                      static_cast<hipStream_t>(a.stream),
                      static_cast<const E*>(a.q), static_cast<const E*>(a.k),
                      static_cast<const E*>(a.v), a.gate, a.beta, a.S_in,
@@ -222,32 +230,40 @@ static hipError_t launch_dec(const DecodeArgs& a) {
   return hipGetLastError();
 }
 
-template <typename IO, int DK, bool kLogit>
+template <typename IO, int DK, int kIn>
 static hipError_t dispatch_cw(const DecodeArgs& a, int cw) {
   switch (cw) {
-    case 16: return launch_dec<IO, DK, 16, kLogit>(a);
-    case 32: return launch_dec<IO, DK, 32, kLogit>(a);
-    case 64: return launch_dec<IO, DK, 64, kLogit>(a);
-    case 128: return launch_dec<IO, DK, 128, kLogit>(a);
+    case 16: return launch_dec<IO, DK, 16, kIn>(a);
+    case 32: return launch_dec<IO, DK, 32, kIn>(a);
+    case 64: return launch_dec<IO, DK, 64, kIn>(a);
+    case 128: return launch_dec<IO, DK, 128, kIn>(a);
   }
   return hipErrorInvalidValue;
 }
 
-template <typename IO, bool kLogit>
+template <typename IO, int kIn>
 static hipError_t dispatch_dk(const DecodeArgs& a, int cw) {
   switch (a.dk) {
-    case 16: return dispatch_cw<IO, 16, kLogit>(a, cw);
-    case 32: return dispatch_cw<IO, 32, kLogit>(a, cw);
-    case 64: return dispatch_cw<IO, 64, kLogit>(a, cw);
-    case 128: return dispatch_cw<IO, 128, kLogit>(a, cw);
+    case 16: return dispatch_cw<IO, 16, kIn>(a, cw);
+    case 32: return dispatch_cw<IO, 32, kIn>(a, cw);
+    case 64: return dispatch_cw<IO, 64, kIn>(a, cw);
+    case 128: return dispatch_cw<IO, 128, kIn>(a, cw);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const DecodeArgs& a) {
   const int cw = pick_cw(static_cast<long>(a.N) * a.H, a.dv);
-  if (a.logits) return a.bf16 ? dispatch_dk<bf16_t, true>(a, cw) : dispatch_dk<float, true>(a, cw);
-  return a.bf16 ? dispatch_dk<bf16_t, false>(a, cw) : dispatch_dk<float, false>(a, cw);
+  switch (a.gate_in) {
+    case kGateAlpha:
+      return a.bf16 ? dispatch_dk<bf16_t, kGateAlpha>(a, cw) : dispatch_dk<float, kGateAlpha>(a, cw);
+    case kGateLogit:
+      return a.bf16 ? dispatch_dk<bf16_t, kGateLogit>(a, cw) : dispatch_dk<float, kGateLogit>(a, cw);
+    case kGateScalar:
+      return a.bf16 ? dispatch_dk<bf16_t, kGateScalar>(a, cw)
+                    : dispatch_dk<float, kGateScalar>(a, cw);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kda

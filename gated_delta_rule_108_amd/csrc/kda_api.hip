@@ -81,11 +81,21 @@ size_t kda_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int C, k
 
 namespace {
 
-// Shared by kda_prefill_chunked (alpha: fp32 gates) and
-// kda_prefill_chunked_logits (alpha: gate logits of type dt, beta: logits).
+// Bytes of the gate array per token and head for each way the gate arrives.
+size_t gate_bytes(int gate_in, int dk, size_t esize) {
+  switch (gate_in) {
+    case kda::kGateLogit: return dk * esize;   // logits of the I/O type
+    case kda::kGateScalar: return 4;           // one fp32 gate per token and head
+  }
+  return dk * 4;                               // fp32 alpha per key channel
+}
+
+// Shared by kda_prefill_chunked (alpha: fp32 gates per channel),
+// kda_prefill_chunked_logits (gate logits of type dt, beta as logits) and
+// kda_gdn_prefill_chunked (one gate per token and head, or none).
 kda_status prefill_impl(const void* q, const void* k, const void* v, const void* alpha,
                         const float* beta, const float* S0, void* o, float* S_T, int B, int T,
-                        int H, int dk, int dv, int C, kda_dtype dt, bool logits, int qk_map,
+                        int H, int dk, int dv, int C, kda_dtype dt, int gate_in, int qk_map,
                         void* workspace, size_t workspace_bytes, void* stream) {
   C = chunk_run(C);
   if (B < 1 || H < 1 || T < 0) return KDA_ERR_SHAPE;
@@ -93,7 +103,9 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const void*
   if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
   if (!kda::prefill_supported(dk, dv, C, dt == KDA_BF16)) return KDA_ERR_UNSUPPORTED;
   const bool has_tokens = T > 0;
-  if (has_tokens && (!q || !k || !v || !alpha || !beta || !o)) return KDA_ERR_NULL;
+  const bool gate_optional = gate_in == kda::kGateScalar;   // null: alpha = 1
+  if (has_tokens && (!q || !k || !v || (!alpha && !gate_optional) || !beta || !o))
+    return KDA_ERR_NULL;
   const void* ptrs[] = {q, k, v, alpha, beta, S0, o, S_T, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return KDA_ERR_ALIGN;
@@ -101,13 +113,13 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const void*
   if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need)) return KDA_ERR_WORKSPACE;
 
   const size_t e = (dt == KDA_BF16) ? 2 : 4;
-  const size_t ea = logits ? e : 4;   // gate element: logit of type dt, or fp32 alpha
   const size_t ntok = static_cast<size_t>(B) * T * H;
+  const size_t ga = alpha ? ntok * gate_bytes(gate_in, dk, e) : 0;
   const size_t nst = static_cast<size_t>(B) * H * dk * dv * 4;
   if (has_tokens) {
     const Span so = span(o, ntok * dv * e);
     const Span ins[] = {span(q, ntok * dk * e), span(k, ntok * dk * e), span(v, ntok * dv * e),
-                        span(alpha, ntok * dk * ea), span(beta, ntok * 4),
+                        span(alpha, ga), span(beta, ntok * 4),
                         S0 ? span(S0, nst) : Span{0, 0}, S_T ? span(S_T, nst) : Span{0, 0}};
     for (const Span& s : ins)
       if (overlap(so, s)) return KDA_ERR_ALIAS;
@@ -115,7 +127,7 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const void*
   if (ws_need > 0) {
     const Span sw = span(workspace, ws_need);
     const Span all[] = {span(q, ntok * dk * e), span(k, ntok * dk * e), span(v, ntok * dv * e),
-                        span(alpha, ntok * dk * ea), span(beta, ntok * 4), span(o, ntok * dv * e),
+                        span(alpha, ga), span(beta, ntok * 4), span(o, ntok * dv * e),
                         S0 ? span(S0, nst) : Span{0, 0}, S_T ? span(S_T, nst) : Span{0, 0}};
     for (const Span& s : all)
       if (overlap(sw, s)) return KDA_ERR_ALIAS;
@@ -125,7 +137,7 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const void*
     if (S0 && S0 != S_T && overlap(st, span(S0, nst))) return KDA_ERR_ALIAS;
     if (has_tokens) {
       const Span ins[] = {span(q, ntok * dk * e), span(k, ntok * dk * e), span(v, ntok * dv * e),
-                          span(alpha, ntok * dk * ea), span(beta, ntok * 4)};
+                          span(alpha, ga), span(beta, ntok * 4)};
       for (const Span& s : ins)
         if (overlap(st, s)) return KDA_ERR_ALIAS;
     }
@@ -136,27 +148,29 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const void*
 
   kda::PrefillArgs a{q,  k,  v,  alpha, beta, S0, o,  S_T,          B,         T,
                      H,  dk, dv, C,     dt == KDA_BF16,   stream, workspace, workspace_bytes,
-                     logits, qk_map};
+                     gate_in, qk_map};
   if (kda::launch_prefill(a) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
 }
 
 kda_status decode_impl(const void* q, const void* k, const void* v, const void* alpha,
                        const float* beta, const float* S_in, void* o, float* S_out, int N, int H,
-                       int dk, int dv, kda_dtype dt, bool logits, int qk_map, void* stream) {
+                       int dk, int dv, kda_dtype dt, int gate_in, int qk_map, void* stream) {
   if (N < 1 || H < 1) return KDA_ERR_SHAPE;
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
-  if (!q || !k || !v || !alpha || !beta || !S_in || !o || !S_out) return KDA_ERR_NULL;
+  const bool gate_optional = gate_in == kda::kGateScalar;   // null: alpha = 1
+  if (!q || !k || !v || (!alpha && !gate_optional) || !beta || !S_in || !o || !S_out)
+    return KDA_ERR_NULL;
   const void* ptrs[] = {q, k, v, alpha, beta, S_in, o, S_out};
   for (const void* p : ptrs)
-    if (!aligned16(p)) return KDA_ERR_ALIGN;
+    if (p && !aligned16(p)) return KDA_ERR_ALIGN;
   const size_t e = (dt == KDA_BF16) ? 2 : 4;
-  const size_t ea = logits ? e : 4;
   const size_t nh = static_cast<size_t>(N) * H;
+  const size_t ga = alpha ? nh * gate_bytes(gate_in, dk, e) : 0;
   const size_t nst = nh * dk * dv * 4;
   const Span ins[] = {span(q, nh * dk * e), span(k, nh * dk * e), span(v, nh * dv * e),
-                      span(alpha, nh * dk * ea), span(beta, nh * 4), span(S_in, nst)};
+                      span(alpha, ga), span(beta, nh * 4), span(S_in, nst)};
   const Span so = span(o, nh * dv * e), ss = span(S_out, nst);
   for (const Span& s : ins)
     if (overlap(so, s)) return KDA_ERR_ALIAS;
@@ -167,7 +181,7 @@ kda_status decode_impl(const void* q, const void* k, const void* v, const void* 
   const kda_status dev = check_device();
   if (dev != KDA_OK) return dev;
   kda::DecodeArgs a{q, k, v, alpha, beta, S_in, o, S_out, N, H, dk, dv, dt == KDA_BF16, stream,
-                    logits, qk_map};
+                    gate_in, qk_map};
   if (kda::launch_decode(a) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
 }
@@ -182,8 +196,8 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
                                const float* beta, const float* S0, void* o, float* S_T, int B,
                                int T, int H, int dk, int dv, int C, kda_dtype dt, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  return prefill_impl(q, k, v, alpha, beta, S0, o, S_T, B, T, H, dk, dv, C, dt, false, 0,
-                      workspace, workspace_bytes, stream);
+  return prefill_impl(q, k, v, alpha, beta, S0, o, S_T, B, T, H, dk, dv, C, dt, kda::kGateAlpha,
+                      0, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_prefill_chunked_logits(const void* q, const void* k, const void* v, const void* g,
@@ -192,14 +206,23 @@ kda_status kda_prefill_chunked_logits(const void* q, const void* k, const void* 
                                       kda_qk_map qk_map, void* workspace, size_t workspace_bytes,
                                       void* stream) {
   if (!qk_map_ok(qk_map)) return KDA_ERR_UNSUPPORTED;
-  return prefill_impl(q, k, v, g, b, S0, o, S_T, B, T, H, dk, dv, C, dt, true,
+  return prefill_impl(q, k, v, g, b, S0, o, S_T, B, T, H, dk, dv, C, dt, kda::kGateLogit,
                       static_cast<int>(qk_map), workspace, workspace_bytes, stream);
+}
+
+kda_status kda_gdn_prefill_chunked(const void* q, const void* k, const void* v, const float* a,
+                                   const float* beta, const float* S0, void* o, float* S_T, int B,
+                                   int T, int H, int dk, int dv, int C, kda_dtype dt,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(q, k, v, a, beta, S0, o, S_T, B, T, H, dk, dv, C, dt, kda::kGateScalar, 0,
+                      workspace, workspace_bytes, stream);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* alpha,
                            const float* beta, const float* S_in, void* o, float* S_out, int N,
                            int H, int dk, int dv, kda_dtype dt, void* stream) {
-  return decode_impl(q, k, v, alpha, beta, S_in, o, S_out, N, H, dk, dv, dt, false, 0, stream);
+  return decode_impl(q, k, v, alpha, beta, S_in, o, S_out, N, H, dk, dv, dt, kda::kGateAlpha, 0,
+                     stream);
 }
 
 kda_status kda_decode_step_logits(const void* q, const void* k, const void* v, const void* g,
@@ -207,8 +230,15 @@ kda_status kda_decode_step_logits(const void* q, const void* k, const void* v, c
                                   int N, int H, int dk, int dv, kda_dtype dt, kda_qk_map qk_map,
                                   void* stream) {
   if (!qk_map_ok(qk_map)) return KDA_ERR_UNSUPPORTED;
-  return decode_impl(q, k, v, g, b, S_in, o, S_out, N, H, dk, dv, dt, true,
+  return decode_impl(q, k, v, g, b, S_in, o, S_out, N, H, dk, dv, dt, kda::kGateLogit,
                      static_cast<int>(qk_map), stream);
+}
+
+kda_status kda_gdn_decode_step(const void* q, const void* k, const void* v, const float* a,
+                               const float* beta, const float* S_in, void* o, float* S_out, int N,
+                               int H, int dk, int dv, kda_dtype dt, void* stream) {
+  return decode_impl(q, k, v, a, beta, S_in, o, S_out, N, H, dk, dv, dt, kda::kGateScalar, 0,
+                     stream);
 }
 
 }  // extern "C"

@@ -7,28 +7,37 @@
 
 namespace kda {
 
+// How the gate reaches a kernel (a compile-time switch of the kernels):
+//   kGateAlpha   one alpha per key channel, fp32 (Kimi Delta Attention)
+//   kGateLogit   one gate logit per key channel in the I/O type, with the
+//                whole input prologue of kda_device.hpp
+//   kGateScalar  one alpha per token and head, fp32, the same on every
+//                channel (Gated DeltaNet), or none at all: alpha = 1
+//                (DeltaNet) when the pointer is null
+enum GateIn : int { kGateAlpha = 0, kGateLogit = 1, kGateScalar = 2 };
+
 struct DecodeArgs {
   const void* q;
   const void* k;
   const void* v;
-  const void* gate;   // alpha (fp32), or gate logits g in the I/O type when logits
-  const float* beta;  // beta, or its logit when logits
+  const void* gate;   // per gate_in (GateIn): alpha, gate logits, or a scalar gate
+  const float* beta;  // beta, or its logit with kGateLogit
   const float* S_in;
   void* o;
   float* S_out;
   int N, H, dk, dv;
   bool bf16;
   void* stream;
-  bool logits;        // run the input prologue (see kda_device.hpp)
-  int qk_map;         // QkMap, used when logits
+  int gate_in;        // GateIn (kda_device.hpp)
+  int qk_map;         // QkMap, used with kGateLogit
 };
 
 struct PrefillArgs {
   const void* q;
   const void* k;
   const void* v;
-  const void* gate;   // alpha (fp32), or gate logits g in the I/O type when logits
-  const float* beta;  // beta, or its logit when logits
+  const void* gate;   // per gate_in (GateIn): alpha, gate logits, or a scalar gate
+  const float* beta;  // beta, or its logit with kGateLogit
   const float* S0;   // may be null (zeros)
   void* o;
   float* S_T;        // may be null (not written)
@@ -37,8 +46,8 @@ struct PrefillArgs {
   void* stream;
   void* workspace;          // split path only (see prefill_workspace)
   size_t workspace_bytes;
-  bool logits;              // run the input prologue (see kda_device.hpp)
-  int qk_map;               // QkMap, used when logits
+  int gate_in;              // GateIn (kda_device.hpp)
+  int qk_map;               // QkMap, used with kGateLogit
 };
 
 hipError_t launch_decode(const DecodeArgs& a);

@@ -548,14 +548,17 @@ constexpr int kMaxLds = 160 * 1024;
 // decay, U~; segn records per chain) for the scan kernel; the next chunk's
 // inputs load while the current one is processed.
 //
-// kLogit = false: ggate is alpha (fp32), gbeta is beta, q and k are used as
-// given.  kLogit = true: the input prologue runs on the fly: ggate holds
-// gate logits g in the I/O type (alpha = 1 / (1 + e^g)), gbeta holds
-// write-strength logits (beta = sigmoid), and q, k pass through qk_map
-// (QkMap: as given, L2-normalised, or SiLU then L2-normalised per token).
-// The row norms are sums of squares over the chunk's registers, reduced
-// across the lanes of a wave and, at dk = 128, across two waves in LDS.
-template <typename OpT, int DK, int C, int DVT, bool kPrep = false, bool kLogit = false>
+// kIn (GateIn) says how the gate arrives.  kGateAlpha: ggate is alpha
+// (fp32, one per key channel), gbeta is beta, q and k are used as given.
+// kGateLogit: the input prologue runs on the fly: ggate holds gate logits g
+// in the I/O type (alpha = 1 / (1 + e^g)), gbeta holds write-strength
+// logits (beta = sigmoid), and q, k pass through qk_map (QkMap: as given,
+// L2-normalised, or SiLU then L2-normalised per token); the row norms are
+// sums of squares over the chunk's registers, reduced across the lanes of a
+// wave and, at dk = 128, across two waves in LDS.  kGateScalar: ggate holds
+// one alpha per token and head (Gated DeltaNet), broadcast over the
+// channels as it is loaded, or is null for alpha = 1 (DeltaNet).
+template <typename OpT, int DK, int C, int DVT, bool kPrep = false, int kIn = kGateAlpha>
 __global__ void __launch_bounds__(512)
 kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
                    const typename Ty<OpT>::Elem* __restrict__ gk,
@@ -567,6 +570,8 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
   using Cf = PCfg<OpT, DK, C, DVT>;
   using E = typename Ty<OpT>::Elem;
   using PT = typename Pair<OpT>::T;
+  constexpr bool kLogit = kIn == kGateLogit;
+  constexpr bool kScalar = kIn == kGateScalar;
   constexpr int NB = Cf::NB, NJ = Cf::NJ, NW = Cf::NW, NTH = Cf::NTH;
   constexpr int LDK = Cf::LDK, LDC = Cf::LDC, LDT = Cf::LDT, LDZ = Cf::LDZ;
   static_assert(Cf::kLds <= kMaxLds, "LDS plan exceeds 160 KiB");
@@ -603,7 +608,8 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const float* galpha = static_cast<const float*>(ggate);   // kLogit = false
+  const float* galpha = static_cast<const float*>(ggate);   // kGateAlpha, kGateScalar
+  const bool has_gate = galpha != nullptr;                   // kGateScalar: null is alpha = 1
   const E* glogit = static_cast<const E*>(ggate);           // kLogit = true
   // Per-row sums of squares of k and q, [part][k, q][C], part = which half of
   // the channels at dk = 128.  Lives in ZB, which is idle until phase SO.
@@ -689,6 +695,11 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
           const int off = min(16 * J + 4 * h + j, jmax) * rsK + c;
           if constexpr (kLogit) {
             gg[it][j] = Quad<OpT>::load(pg + off);
+          } else if constexpr (kScalar) {
+            const size_t tr = row0 + static_cast<size_t>(tn + min(16 * J + 4 * h + j, jmax)) * H;
+            const float a = has_gate ? galpha[tr] : 1.f;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) ga[it][j][x] = a;
           } else {
             const float4 a4 = *reinterpret_cast<const float4*>(pa + off);
             ga[it][j][0] = a4.x;
@@ -989,8 +1000,14 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
             return x;
           };
           auto gate = [&](int row, int c) {
-            if constexpr (kLogit) return gate_from_logit(Ty<OpT>::to_f32(glogit[cb + row * rsK + c]));
-            else return galpha[cb + row * rsK + c];
+            if constexpr (kLogit) {
+              return gate_from_logit(Ty<OpT>::to_f32(glogit[cb + row * rsK + c]));
+            } else if constexpr (kScalar) {
+              const size_t tr = row0 + static_cast<size_t>(t0 + 16 * R + row) * H;
+              return has_gate ? galpha[tr] : 1.f;
+            } else {
+              return galpha[cb + row * rsK + c];
+            }
           };
           for (int c = 0; c < DK; ++c) {
             if (sBT[R * DK + c] >= kUnsafeBlockDecay) continue;
@@ -1350,12 +1367,12 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
 // ----------------------------------------------------------------------------
 // Host dispatch
 // ----------------------------------------------------------------------------
-template <typename OpT, int DK, int C, int DVT, bool kLogit>
+template <typename OpT, int DK, int C, int DVT, int kIn>
 hipError_t launch_one(const PrefillArgs& a) {
   using E = typename Ty<OpT>::Elem;
   const long chains = static_cast<long>(a.B) * a.H;
   dim3 grid(static_cast<unsigned>(chains * (a.dv / DVT)));
-  hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT, false, kLogit>), grid,
+  hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT, false, kIn>), grid,
                      dim3(PCfg<OpT, DK, C, DVT>::NTH), 0, static_cast<hipStream_t>(a.stream),
                      static_cast<const E*>(a.q), static_cast<const E*>(a.k),
                      static_cast<const E*>(a.v), a.gate, a.beta, a.S0, static_cast<E*>(a.o),
@@ -1397,14 +1414,14 @@ int pick_dvt(long chains, int dv) {
   return best;
 }
 
-template <typename OpT, int DK, int C, bool kLogit>
+template <typename OpT, int DK, int C, int kIn>
 hipError_t launch_c(const PrefillArgs& a) {
   const int dvt = pick_dvt<OpT, DK, C>(static_cast<long>(a.B) * a.H, a.dv);
   switch (dvt) {
-    case 16: if constexpr (fits<OpT, DK, C, 16>()) return launch_one<OpT, DK, C, 16, kLogit>(a); break;
-    case 32: if constexpr (fits<OpT, DK, C, 32>()) return launch_one<OpT, DK, C, 32, kLogit>(a); break;
-    case 64: if constexpr (fits<OpT, DK, C, 64>()) return launch_one<OpT, DK, C, 64, kLogit>(a); break;
-    case 128: if constexpr (fits<OpT, DK, C, 128>()) return launch_one<OpT, DK, C, 128, kLogit>(a); break;
+    case 16: if constexpr (fits<OpT, DK, C, 16>()) return launch_one<OpT, DK, C, 16, kIn>(a); break;
+    case 32: if constexpr (fits<OpT, DK, C, 32>()) return launch_one<OpT, DK, C, 32, kIn>(a); break;
+    case 64: if constexpr (fits<OpT, DK, C, 64>()) return launch_one<OpT, DK, C, 64, kIn>(a); break;
+    case 128: if constexpr (fits<OpT, DK, C, 128>()) return launch_one<OpT, DK, C, 128, kIn>(a); break;
   }
   return hipErrorInvalidValue;
 }

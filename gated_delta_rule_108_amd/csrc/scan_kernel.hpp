@@ -421,7 +421,7 @@ inline int prep_chunks_per_block(long chains, int nc) {
   return static_cast<int>((nc + runs - 1) / runs);
 }
 
-template <typename OpT, int DK, int C, int DVT, bool kLogit>
+template <typename OpT, int DK, int C, int DVT, int kIn>
 hipError_t launch_prep(const PrefillArgs& a, int seg0, int segn) {
   using E = typename Ty<OpT>::Elem;
   if constexpr (!fits<OpT, DK, C, DVT>()) {
@@ -433,7 +433,7 @@ hipError_t launch_prep(const PrefillArgs& a, int seg0, int segn) {
     // all but the first chunk's loads hide behind compute.
     const int cpb = prep_chunks_per_block(chains, segn);
     const long blocks = chains * ((segn + cpb - 1) / cpb);
-    hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT, true, kLogit>),
+    hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT, true, kIn>),
                        dim3(static_cast<unsigned>(blocks)), dim3(512), 0,
                        static_cast<hipStream_t>(a.stream), static_cast<const E*>(a.q),
                        static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.gate, a.beta,
@@ -443,7 +443,7 @@ hipError_t launch_prep(const PrefillArgs& a, int seg0, int segn) {
   }
 }
 
-template <typename OpT, int DK, int C, bool kLogit>
+template <typename OpT, int DK, int C, int kIn>
 hipError_t launch_split(const PrefillArgs& a) {
   using E = typename Ty<OpT>::Elem;
   if constexpr (!scan_fits<OpT, DK, C>()) {
@@ -459,10 +459,10 @@ hipError_t launch_split(const PrefillArgs& a) {
       const int segn = p.nseg > 0 ? std::min(p.segch, p.nc - seg0) : 0;
       hipError_t e = hipErrorInvalidValue;
       switch (a.dv) {
-        case 16: e = launch_prep<OpT, DK, C, 16, kLogit>(a, seg0, segn); break;
-        case 32: e = launch_prep<OpT, DK, C, 32, kLogit>(a, seg0, segn); break;
-        case 64: e = launch_prep<OpT, DK, C, 64, kLogit>(a, seg0, segn); break;
-        case 128: e = launch_prep<OpT, DK, C, 128, kLogit>(a, seg0, segn); break;
+        case 16: e = launch_prep<OpT, DK, C, 16, kIn>(a, seg0, segn); break;
+        case 32: e = launch_prep<OpT, DK, C, 32, kIn>(a, seg0, segn); break;
+        case 64: e = launch_prep<OpT, DK, C, 64, kIn>(a, seg0, segn); break;
+        case 128: e = launch_prep<OpT, DK, C, 128, kIn>(a, seg0, segn); break;
       }
       if (e != hipSuccess) return e;
       const float* s_in = sgi == 0 ? a.S0 : carry;
@@ -499,9 +499,16 @@ template <typename OpT, int DK, int C>
 hipError_t launch_any(const PrefillArgs& a) {
   const long chains = static_cast<long>(a.B) * a.H;
   const bool split = use_split<OpT, DK, C>(chains, a.dv);
-  if (a.logits)
-    return split ? launch_split<OpT, DK, C, true>(a) : launch_c<OpT, DK, C, true>(a);
-  return split ? launch_split<OpT, DK, C, false>(a) : launch_c<OpT, DK, C, false>(a);
+  switch (a.gate_in) {
+    case kGateAlpha:
+      return split ? launch_split<OpT, DK, C, kGateAlpha>(a) : launch_c<OpT, DK, C, kGateAlpha>(a);
+    case kGateLogit:
+      return split ? launch_split<OpT, DK, C, kGateLogit>(a) : launch_c<OpT, DK, C, kGateLogit>(a);
+    case kGateScalar:
+      return split ? launch_split<OpT, DK, C, kGateScalar>(a)
+                   : launch_c<OpT, DK, C, kGateScalar>(a);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename OpT, int DK>

@@ -186,6 +186,28 @@ kda_status kda_prefill_chunked_logits(const void* q, const void* k, const void* 
                                       void* stream);
 
 /*
+ * kda_gdn_prefill_chunked — the same chunked prefill with one forget gate
+ * per token and head instead of one per key channel: Gated DeltaNet, the
+ * rule KDA refines ("From GPT-2 to Kimi K3, Explained", sections "Gated
+ * Delta Net" and "KDA/Kimi Linear"), or, with a = NULL, DeltaNet (gate 1,
+ * section "DeltaNet (Fast Weight Programmers)").
+ *
+ *   a      [B, T, H]      float32   gate per token and head, expected in
+ *                                   [0, 1], or NULL for a = 1
+ *   all other arguments, the workspace query and the errors as
+ *   kda_prefill_chunked
+ *
+ * The result equals kda_prefill_chunked with alpha[b,t,h,:] = a[b,t,h] on
+ * every channel, up to rounding.  The gate costs 4 bytes per token and head
+ * (0 with NULL) instead of 4*dk.
+ */
+kda_status kda_gdn_prefill_chunked(const void* q, const void* k, const void* v,
+                                   const float* a, const float* beta, const float* S0,
+                                   void* o, float* S_T, int B, int T, int H, int dk, int dv,
+                                   int C, kda_dtype dt, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
  * kda_decode_step — one recurrence step for N sequences x H heads (the same
  * step as one token of the prefill; the pages' decode path calls the layer
  * with t = 1 and the cached state, "From GPT-2 to Kimi K3, Explained",
@@ -221,6 +243,15 @@ kda_status kda_decode_step_logits(const void* q, const void* k, const void* v,
                                   const void* g, const float* b, const float* S_in,
                                   void* o, float* S_out, int N, int H, int dk, int dv,
                                   kda_dtype dt, kda_qk_map qk_map, void* stream);
+
+/*
+ * kda_gdn_decode_step — one Gated DeltaNet step (kda_decode_step with the
+ * gate a [N, H] float32 the same on every key channel, or NULL for DeltaNet);
+ * exactly one token of kda_gdn_prefill_chunked.  Errors: as kda_decode_step.
+ */
+kda_status kda_gdn_decode_step(const void* q, const void* k, const void* v, const float* a,
+                               const float* beta, const float* S_in, void* o, float* S_out,
+                               int N, int H, int dk, int dv, kda_dtype dt, void* stream);
 
 /* kda_status_string — static, human-readable text for a status code. */
 const char* kda_status_string(kda_status s);

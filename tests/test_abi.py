@@ -25,8 +25,9 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_six_calls():
+def test_header_declares_the_eight_calls():
     assert declared_functions() == ["kda_decode_step", "kda_decode_step_logits",
+                                    "kda_gdn_decode_step", "kda_gdn_prefill_chunked",
                                     "kda_prefill_chunked", "kda_prefill_chunked_logits",
                                     "kda_prefill_workspace_bytes", "kda_status_string"]
 
@@ -216,3 +217,38 @@ def test_logits_entry_points_validate_like_the_plain_ones():
     for qk in (0, 1, 2):
         assert prefill_logits(lib, qk=qk) in (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
         assert decode_logits(lib, qk=qk) in (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+
+
+def test_gdn_entry_points_take_a_null_gate_and_validate():
+    L = _lib()
+    lib = L.load()
+    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+
+    def gp(**kw):
+        a = dict(q=addr(0), k=addr(1), v=addr(2), a=addr(3), beta=addr(4), S0=addr(5),
+                 o=addr(6), S_T=addr(7), B=1, T=64, H=2, dk=128, dv=128, C=64, dt=1,
+                 ws=addr(8), wsb=1 << 34, stream=None)
+        a.update(kw)
+        return lib.kda_gdn_prefill_chunked(a["q"], a["k"], a["v"], a["a"], a["beta"], a["S0"],
+                                           a["o"], a["S_T"], a["B"], a["T"], a["H"], a["dk"],
+                                           a["dv"], a["C"], a["dt"], a["ws"], a["wsb"],
+                                           a["stream"])
+
+    def gd(**kw):
+        a = dict(q=addr(0), k=addr(1), v=addr(2), a=addr(3), beta=addr(4), S=addr(5),
+                 o=addr(6), S_out=addr(5), N=4, H=2, dk=128, dv=128, dt=1, stream=None)
+        a.update(kw)
+        return lib.kda_gdn_decode_step(a["q"], a["k"], a["v"], a["a"], a["beta"], a["S"],
+                                       a["o"], a["S_out"], a["N"], a["H"], a["dk"], a["dv"],
+                                       a["dt"], a["stream"])
+
+    assert gp(a=None) in ok and gd(a=None) in ok          # DeltaNet: no gate
+    assert gp() in ok and gd() in ok
+    assert gp(beta=None) == L.KDA_ERR_NULL and gd(beta=None) == L.KDA_ERR_NULL
+    assert gp(a=addr(3) + 4) == L.KDA_ERR_ALIGN and gd(a=addr(3) + 8) == L.KDA_ERR_ALIGN
+    assert gp(ws=None) == L.KDA_ERR_WORKSPACE
+    # the gate array is B*T*H fp32 values: an output just past it is fine
+    g_end = addr(3) + 1 * 64 * 2 * 4
+    assert gp(o=g_end - 16) == L.KDA_ERR_ALIAS
+    assert gp(o=g_end) in ok
+    assert gd(o=addr(3) + 4 * 2 * 4) in ok and gd(o=addr(3)) == L.KDA_ERR_ALIAS

@@ -44,7 +44,8 @@ import torch
 
 __all__ = ["PrefillSpec", "DecodeSpec", "PREFILL", "DECODE",
            "make_prefill_inputs", "make_decode_state", "make_decode_step_inputs",
-           "make_decode_steps", "make_prefill_logit_inputs", "make_decode_logit_steps"]
+           "make_decode_steps", "make_prefill_logit_inputs", "make_decode_logit_steps",
+           "make_gdn_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -200,6 +201,20 @@ def make_decode_logit_steps(spec: DecodeSpec, device="cpu", N=None, steps=None):
     b = torch.randn(steps, N, H, generator=g, device=device)
     return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), g=gl.contiguous(),
                 b=b.float().contiguous())
+
+
+def make_gdn_inputs(spec: PrefillSpec, device="cpu", T=None, B=None, H=None, gated=True):
+    """A Gated DeltaNet batch: make_prefill_inputs with the per-channel alpha
+    replaced by one gate per token and head, a [B,T,H] fp32 drawn like the
+    spec's alpha (exp(-softplus(N(0,1))) or U(0.9, 1)); gated=False gives
+    a=None (DeltaNet).  Returns a dict with keys q, k, v, a, beta, S0."""
+    d = make_prefill_inputs(spec, device, T=T, B=B, H=H)
+    Bv, Tv, Hv = d["beta"].shape
+    a = None
+    if gated:
+        kind = "uniform_0.9_1" if spec.alpha_kind == "uniform_0.9_1" else "softplus"
+        a = _alpha(kind, (Bv, Tv, Hv), _gen(device, spec.seed + 2000), device).float().contiguous()
+    return dict(q=d["q"], k=d["k"], v=d["v"], a=a, beta=d["beta"], S0=d["S0"])
 
 
 def make_decode_state(spec: DecodeSpec, device="cpu", N=None):
