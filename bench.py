@@ -11,6 +11,7 @@ Alongside the headline it measures, on the same GPU:
   * the B=8, H=32, T=8192 prefill (tokens/s and roofline);
   * the H=16 prefill and the 256 x 32-head decode from raw projections
     (gate logits, write-strength logits, q/k L2-normalised in the kernels);
+  * the same two with one gate per token and head (Gated DeltaNet);
   * the float64 oracle on the host cores over a bounded sample (cpu_baseline).
 """
 from __future__ import annotations
@@ -42,6 +43,14 @@ def prefill_logit_alg_bytes(B, T, H, dk, dv, esize, with_s0):
     instead of fp32 alpha, and beta read as fp32 logits."""
     tok = B * T * H
     per_tok = esize * (2 * dk + dv) + esize * dk + 4 + esize * dv
+    state = B * H * dk * dv * 4
+    return tok * per_tok + state * (2 if with_s0 else 1)
+
+
+def gdn_alg_bytes(B, T, H, dk, dv, esize, with_s0):
+    """As prefill_alg_bytes, with one fp32 gate per token and head."""
+    tok = B * T * H
+    per_tok = esize * (2 * dk + dv) + 4 + 4 + esize * dv
     state = B * H * dk * dv * 4
     return tok * per_tok + state * (2 if with_s0 else 1)
 
@@ -193,7 +202,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="headline prefill only (no decode / large prefill lines)")
     ap.add_argument("--only", choices=["prefill", "decode", "large", "logits", "decode_logits",
-                                       "copy"], default=None,
+                                       "gdn", "decode_gdn", "copy"], default=None,
                     help="run one leg only (for profiler runs); 'copy' times a plain "
                          "1 GiB device-to-device copy used to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -218,8 +227,8 @@ def main():
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
                           "ms_per_copy": ms, "GBps": 8 * n / (ms * 1e-3) / 1e9}), flush=True)
         return
-    legs = ({"prefill", "decode", "large", "logits", "decode_logits"} if args.only is None
-            else {args.only})
+    legs = ({"prefill", "decode", "large", "logits", "decode_logits", "gdn", "decode_gdn"}
+            if args.only is None else {args.only})
     if args.no_extra:
         legs = {"prefill"}
 
@@ -396,6 +405,60 @@ def extras(args, legs, out, torch, kda, wl, dev):
         print(f"# decode_n256_h32_logits: {ms_d * 1e3:.1f} us/step", file=sys.stderr,
               flush=True)
         del S, st, od
+        torch.cuda.empty_cache()
+
+    if "gdn" in legs:
+        # ---------------- H=16 prefill with one gate per token and head (GDN)
+        spec = wl.PREFILL["prefill_h16_t4k"]
+        gi = wl.make_gdn_inputs(spec, dev)
+        go = torch.empty(spec.B, spec.T, spec.H, spec.dv, dtype=spec.dtype, device=dev)
+        gS = torch.empty(spec.B, spec.H, spec.dk, spec.dv, dtype=torch.float32, device=dev)
+
+        def gstep():
+            kda.gdn_prefill_chunked(gi["q"], gi["k"], gi["v"], gi["a"], gi["beta"], gi["S0"],
+                                    chunk=64, out=go, state_out=gS)
+
+        ms_g, ms_gw = time_launches(gstep, args.steps, args.warmup, torch)
+        B, T, H, dk, dv = spec.B, spec.T, spec.H, spec.dk, spec.dv
+        gb = gdn_alg_bytes(B, T, H, dk, dv, 2, False)
+        gf = prefill_flops(B, T, H, dk, dv, 64)
+        out["prefill_h16_t4k_gdn"] = {
+            "C": 64, "us_per_launch": ms_g * 1e3, "tokens_per_s": B * T / (ms_gw * 1e-3),
+            "GBps": gb / (ms_g * 1e-3) / 1e9, "frac_hbm": gb / (ms_g * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": profiled_traffic("prefill_h16_t4k_gdn"), "alg_bytes_per_launch": gb,
+            "tflops": gf / (ms_g * 1e-3) / 1e12,
+            "frac_mfma": gf / (ms_g * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        }
+        print(f"# prefill_h16_t4k_gdn: {ms_g * 1e3:.1f} us/launch", file=sys.stderr, flush=True)
+        del gi, go, gS
+        torch.cuda.empty_cache()
+
+    if "decode_gdn" in legs:
+        # ---------------- GDN decode: 256 x 32 heads, one gate per head, in place
+        dspec = wl.DECODE["decode_n256_h32"]
+        S = wl.make_decode_state(dspec, dev)
+        nst = 8
+        st = wl.make_decode_steps(dspec, dev, steps=nst)
+        ga = st["alpha"][..., 0].contiguous()
+        od = torch.empty(dspec.N, dspec.H, dspec.dv, dtype=dspec.dtype, device=dev)
+        it = [0]
+
+        def gdstep():
+            i = it[0] % nst
+            it[0] += 1
+            kda.gdn_decode_step(st["q"][i], st["k"][i], st["v"][i], ga[i], st["beta"][i], S,
+                                out=od)
+
+        ms_d, _ = time_launches(gdstep, max(args.steps, 20), args.warmup, torch)
+        dbytes = decode_alg_bytes(dspec.N, dspec.H, dspec.dk, dspec.dv, 2, gate_bytes=0) \
+            + dspec.N * dspec.H * 4
+        out["decode_n256_h32_gdn"] = {
+            "us_per_step": ms_d * 1e3, "alg_GBps": dbytes / (ms_d * 1e-3) / 1e9,
+            "frac_hbm": dbytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": profiled_traffic("decode_n256_h32_gdn"), "alg_bytes_per_step": dbytes,
+        }
+        print(f"# decode_n256_h32_gdn: {ms_d * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        del S, st, od, ga
         torch.cuda.empty_cache()
 
 
