@@ -192,10 +192,31 @@ __device__ __forceinline__ float vec_elem(const u32x4& v, int q) {
     return __uint_as_float(v[q]);
 }
 
-// Value of lane K of this lane's group of four (a DPP move, no LDS).
-template <int K>
-__device__ __forceinline__ float quad_bcast(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), K * 0x55, 0xF, 0xF, false));
+// Lane layout of the per-chunk input items.  A gate item is (16-row block J,
+// channel quad, row quarter h): four rows x four channels of alpha, k and q.
+// The four lanes of each lane quad hold four consecutive channel quads of
+// the same rows, so each 4-lane group of a load reads contiguous bytes of one
+// row (a layout with the row quarter in the low lane bits made every lane
+// quad touch four rows, and the loads of a chunk cost ~4k more cycles); the
+// four row quarters of a channel quad sit 4 lanes apart in one 16-lane row.
+// Value items (block J, 16-byte column vector, row quarter h) are laid out
+// the same way.
+struct ItemPos {
+  int J, h, v;   // block, row quarter, channel quad (gate) or column vector (value)
+};
+template <int NV>   // channel quads or column vectors per row
+__device__ __forceinline__ ItemPos item_pos(int item) {
+  constexpr int L = NV < 4 ? NV : 4;   // consecutive vectors of one row per lane group
+  const int local = item % (4 * NV);
+  return ItemPos{item / (4 * NV), (local / L) % 4, local % L + L * (local / (4 * L))};
+}
+
+// The value of the lane holding row quarter (h - S) mod 4 of the same
+// channel quad: a DPP rotation by 4 S lanes within the 16-lane row (row_ror,
+// lane i reads lane i - 4 S), no LDS.
+template <int S>
+__device__ __forceinline__ float quarter_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + 4 * S, 0xF, 0xF, false));
 }
 
 // Orders this wave's LDS writes before its later LDS reads (no other wave
@@ -688,8 +709,8 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     for (int it = 0; it < Cf::NGT; ++it) {
       const int item = t_ + NTH * it;
       if (Cf::NGI % NTH == 0 || item < Cf::NGI) {
-        const int h = item % 4, g = item / 4;
-        const int J = g / (DK / 4), c = 4 * (g % (DK / 4));
+        const ItemPos ip = item_pos<DK / 4>(item);
+        const int h = ip.h, J = ip.J, c = 4 * ip.v;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int off = min(16 * J + 4 * h + j, jmax) * rsK + c;
@@ -722,8 +743,8 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     for (int it = 0; it < Cf::NVT; ++it) {
       const int item = t_ + NTH * it;
       if (Cf::NVI % NTH == 0 || item < Cf::NVI) {
-        const int h = item % 4, g = item / 4;
-        const int J = g / (DVT / Cf::VEC), cc = Cf::VEC * (g % (DVT / Cf::VEC));
+        const ItemPos ip = item_pos<DVT / Cf::VEC>(item);
+        const int h = ip.h, J = ip.J, cc = Cf::VEC * ip.v;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           gvv[it][j] = *reinterpret_cast<const u32x4*>(pv + min(16 * J + 4 * h + j, jmax) * rsV + cc);
@@ -761,8 +782,8 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     for (int it = 0; it < Cf::NGT; ++it) {
       const int item = tid + NTH * it;
       if (Cf::NGI % NTH == 0 || item < Cf::NGI) {
-        const int h = item % 4, g = item / 4;
-        const int J = g / (DK / 4), c = 4 * (g % (DK / 4));
+        const ItemPos ip = item_pos<DK / 4>(item);
+        const int h = ip.h, J = ip.J, c = 4 * ip.v;
         if constexpr (kLogit) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
@@ -791,12 +812,13 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         }
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
+          // r_s = product of quarter (h - s) mod 4; the block total is the
+          // same two pair products in every lane, (p_h p_h+2)(p_h+1 p_h+3).
           const float p = ga[it][0][x] * ga[it][1][x] * ga[it][2][x] * ga[it][3][x];
-          const float p0 = quad_bcast<0>(p), p1 = quad_bcast<1>(p);
-          const float p2 = quad_bcast<2>(p), p3 = quad_bcast<3>(p);
-          foff[it][x] = h == 0 ? 1.f : h == 1 ? p0 : h == 2 ? p0 * p1 : p0 * p1 * p2;
-          hoff[it][x] = h == 3 ? 1.f : h == 2 ? p3 : h == 1 ? p2 * p3 : p1 * p2 * p3;
-          bt[it][x] = (p0 * p1) * (p2 * p3);
+          const float r1 = quarter_ror<1>(p), r2 = quarter_ror<2>(p), r3 = quarter_ror<3>(p);
+          foff[it][x] = h == 0 ? 1.f : h == 1 ? r1 : h == 2 ? r1 * r2 : (r1 * r2) * r3;
+          hoff[it][x] = h == 3 ? 1.f : h == 2 ? r3 : h == 1 ? r3 * r2 : (r3 * r2) * r1;
+          bt[it][x] = (p * r2) * (r1 * r3);
         }
         if (h == 0)
           *reinterpret_cast<float4*>(sBT + J * DK + c) =
@@ -804,9 +826,8 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       }
       if (qk_norm) {
         // Row sums of squares of k and q: this lane's four channels, then the
-        // lanes of the wave that hold the same rows (lane bits 2.. pick the
-        // channel quad), then, at dk = 128, the two waves of a block in LDS.
-        constexpr int QPW = (DK / 4) < 16 ? (DK / 4) : 16;   // quads of a row per wave
+        // lanes of the wave that hold the same rows (lane bits 0-1 and 4.. pick
+        // the channel quad), then, at dk = 128, the two waves of a block in LDS.
         const bool active = Cf::NGI % NTH == 0 || item < Cf::NGI;
         float nk[4], nq[4];
 #pragma unroll
@@ -822,16 +843,19 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
           nk[j] = active ? nk[j] : 0.f;
           nq[j] = active ? nq[j] : 0.f;
         }
+        constexpr int kSpan = DK < 64 ? DK : 64;   // lanes of a block within one wave
 #pragma unroll
-        for (int off = 4; off < 4 * QPW; off <<= 1)
+        for (int off = 1; off < kSpan; off <<= 1) {
+          if (off == 4 || off == 8) continue;        // lane bits 2-3: the row quarter
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             nk[j] += __shfl_xor(nk[j], off);
             nq[j] += __shfl_xor(nq[j], off);
           }
-        const int h = item % 4, g = item / 4;
-        const int J = g / (DK / 4), part = (g % (DK / 4)) / 16;
-        if (active && (g % QPW) == 0) {
+        }
+        const ItemPos ip = item_pos<DK / 4>(item);
+        const int h = ip.h, J = ip.J, local = item % DK, part = local / 64;
+        if (active && (local % kSpan) < 16 && (local & 3) == 0) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int r = 16 * J + 4 * h + j;
@@ -845,7 +869,8 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     for (int it = 0; it < Cf::NVT; ++it) {
       const int item = tid + NTH * it;
       if (Cf::NVI % NTH == 0 || item < Cf::NVI) {
-        const int h = item % 4, J = (item / 4) / (DVT / Cf::VEC);
+        const ItemPos ip = item_pos<DVT / Cf::VEC>(item);
+        const int h = ip.h, J = ip.J;
         if (!full) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
@@ -875,8 +900,8 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     for (int it = 0; it < Cf::NGT; ++it) {
       const int item = tid + NTH * it;
       if (Cf::NGI % NTH == 0 || item < Cf::NGI) {
-        const int h = item % 4, g = item / 4;
-        const int J = g / (DK / 4), c = 4 * (g % (DK / 4));
+        const ItemPos ip = item_pos<DK / 4>(item);
+        const int h = ip.h, J = ip.J, c = 4 * ip.v;
         // decay of the blocks before / after J, and 1/BT_J (zero for an
         // unsafe block: its diagonal tile is then done exactly on the VALUs)
         float pre[4], suf[4], rbt[4];
@@ -1075,8 +1100,8 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     for (int it = 0; it < Cf::NVT; ++it) {
       const int item = tid + NTH * it;
       if (Cf::NVI % NTH == 0 || item < Cf::NVI) {
-        const int h = item % 4, g = item / 4;
-        const int J = g / (DVT / Cf::VEC), cc = Cf::VEC * (g % (DVT / Cf::VEC));
+        const ItemPos ip = item_pos<DVT / Cf::VEC>(item);
+        const int h = ip.h, J = ip.J, cc = Cf::VEC * ip.v;
         const int r0 = 16 * J + 4 * h;
         const float b0 = sBE[r0], b1 = sBE[r0 + 1], b2 = sBE[r0 + 2], b3 = sBE[r0 + 3];
 #pragma unroll
