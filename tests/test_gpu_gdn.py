@@ -158,3 +158,27 @@ def test_prefill_then_decode_equals_longer_prefill(gated):
     o_ref, S_ref = oracle(inp)
     assert rel(f64(o_dec), o_ref[:, T0:]) < 2e-2 and rel(f64(S), S_ref) < 2e-2
     assert rel(f64(o_dec), f64(o_long[:, T0:])) < 2e-2 and rel(f64(S), f64(S_long)) < 1e-2
+
+
+@pytest.mark.parametrize("gated,C", [(True, 16), (False, 32)])
+def test_fp32_dk128(gated, C):
+    spec = wl.PrefillSpec("case", 1, 3, 90, 128, 64, torch.float32, (C,), 91, "softplus",
+                          0.05, "sigmoid")
+    check(wl.make_gdn_inputs(spec, gated=gated), C, label="fp32 dk=128")
+
+
+def test_empty_sequence_and_null_state_out():
+    spec = wl.PREFILL["prefill_h16_t4k"]
+    inp = wl.make_gdn_inputs(spec, T=0, H=2)
+    S0 = torch.randn(1, 2, 128, 128, generator=torch.Generator().manual_seed(6))
+    d = {k: (None if t is None else t.to(DEV)) for k, t in inp.items()}
+    o, S = kda().gdn_prefill_chunked(d["q"], d["k"], d["v"], d["a"], d["beta"], S0.to(DEV))
+    torch.cuda.synchronize()
+    assert o.shape == (1, 0, 2, 128) and torch.equal(S.cpu(), S0)
+    inp = wl.make_gdn_inputs(spec, T=70, H=2, gated=False)
+    d = {k: (None if t is None else t.to(DEV)) for k, t in inp.items()}
+    o, S = kda().gdn_prefill_chunked(d["q"], d["k"], d["v"], None, d["beta"], None,
+                                     return_state=False)
+    torch.cuda.synchronize()
+    o_ref, _ = oracle(inp)
+    assert S is None and rel(f64(o), o_ref) < 2e-2

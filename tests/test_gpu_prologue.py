@@ -202,3 +202,30 @@ def test_prefill_then_decode_equals_longer_prefill(qk):
     assert rel(f64(o_dec), o_ref[:, T0:]) < 2e-2 and rel(f64(S), S_ref) < 2e-2
     assert rel(f64(o_dec), f64(o_long[:, T0:])) < 2e-2
     assert rel(f64(S), f64(S_long)) < 1e-2
+
+
+@pytest.mark.parametrize("C,qk", [(16, "silu_l2"), (32, "l2")])
+def test_fp32_dk128(C, qk):
+    """fp32 at dk = 128: a row's 32 channel quads span two waves, so the row
+    norms go through the LDS exchange; fp32 keeps the 1e-4 bar."""
+    spec = wl.PrefillSpec("case", 1, 3, 90, 128, 64, torch.float32, (C,), 81, "softplus",
+                          0.05, "sigmoid")
+    check(wl.make_prefill_logit_inputs(spec), C, qk, label="fp32 dk=128")
+
+
+def test_empty_sequence_and_null_state_out():
+    """T = 0 copies S0 (or zeros) to S_T; S_T may be skipped."""
+    spec = wl.PREFILL["prefill_h16_t4k"]
+    inp = wl.make_prefill_logit_inputs(spec, T=0, H=2)
+    S0 = torch.randn(1, 2, 128, 128, generator=torch.Generator().manual_seed(5))
+    d = {k: (None if t is None else t.to(DEV)) for k, t in inp.items()}
+    o, S = kda().prefill_chunked_logits(d["q"], d["k"], d["v"], d["g"], d["b"], S0.to(DEV))
+    torch.cuda.synchronize()
+    assert o.shape == (1, 0, 2, 128) and torch.equal(S.cpu(), S0)
+    inp = wl.make_prefill_logit_inputs(spec, T=70, H=2)
+    d = {k: (None if t is None else t.to(DEV)) for k, t in inp.items()}
+    o, S = kda().prefill_chunked_logits(d["q"], d["k"], d["v"], d["g"], d["b"], None,
+                                        return_state=False)
+    torch.cuda.synchronize()
+    o_ref, _ = oracle(inp, "l2")
+    assert S is None and rel(f64(o), o_ref) < 2e-2
