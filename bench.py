@@ -12,6 +12,8 @@ Alongside the headline it measures, on the same GPU:
   * the H=16 prefill and the 256 x 32-head decode from raw projections
     (gate logits, write-strength logits, q/k L2-normalised in the kernels);
   * the same two with one gate per token and head (Gated DeltaNet);
+  * the long-context prefill (H=32, T=1,048,576) and 256 single-sequence
+    decode steps from its final state, reported separately;
   * the float64 oracle on the host cores over a bounded sample (cpu_baseline).
 """
 from __future__ import annotations
@@ -202,7 +204,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="headline prefill only (no decode / large prefill lines)")
     ap.add_argument("--only", choices=["prefill", "decode", "large", "logits", "decode_logits",
-                                       "gdn", "decode_gdn", "copy"], default=None,
+                                       "gdn", "decode_gdn", "longctx", "copy"], default=None,
                     help="run one leg only (for profiler runs); 'copy' times a plain "
                          "1 GiB device-to-device copy used to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -227,8 +229,8 @@ def main():
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
                           "ms_per_copy": ms, "GBps": 8 * n / (ms * 1e-3) / 1e9}), flush=True)
         return
-    legs = ({"prefill", "decode", "large", "logits", "decode_logits", "gdn", "decode_gdn"}
-            if args.only is None else {args.only})
+    legs = ({"prefill", "decode", "large", "logits", "decode_logits", "gdn", "decode_gdn",
+             "longctx"} if args.only is None else {args.only})
     if args.no_extra:
         legs = {"prefill"}
 
@@ -459,6 +461,49 @@ def extras(args, legs, out, torch, kda, wl, dev):
         }
         print(f"# decode_n256_h32_gdn: {ms_d * 1e3:.1f} us/step", file=sys.stderr, flush=True)
         del S, st, od, ga
+        torch.cuda.empty_cache()
+
+    if "longctx" in legs:
+        # ---------------- long context: H=32, T=2^20 prefill, then 256 decode steps
+        cspec = wl.PREFILL["longctx_h32_t1m"]
+        cg = wl.make_prefill_inputs(cspec, dev)
+        co = torch.empty(cspec.B, cspec.T, cspec.H, cspec.dv, dtype=cspec.dtype, device=dev)
+        cS = torch.empty(cspec.B, cspec.H, cspec.dk, cspec.dv, dtype=torch.float32, device=dev)
+
+        def cstep():
+            kda.prefill_chunked(cg["q"], cg["k"], cg["v"], cg["alpha"], cg["beta"], None,
+                                chunk=64, out=co, state_out=cS)
+
+        ms_c, ms_cw = time_launches(cstep, 2, 1, torch)
+        B, T, H, dk, dv = cspec.B, cspec.T, cspec.H, cspec.dk, cspec.dv
+        cb = prefill_alg_bytes(B, T, H, dk, dv, 2, False)
+        del cg, co
+        torch.cuda.empty_cache()
+        dspec = wl.DECODE["longctx_decode"]
+        mask = wl.mixture_low_channels(32, 128, cspec.seed)
+        st = wl.make_decode_steps(dspec, dev, N=1, alpha_mask=mask)
+        od = torch.empty(1, 32, 128, dtype=dspec.dtype, device=dev)
+        it = [0]
+
+        def dstep():
+            i = it[0] % dspec.steps
+            it[0] += 1
+            kda.decode_step(st["q"][i], st["k"][i], st["v"][i], st["alpha"][i], st["beta"][i],
+                            cS, out=od)
+
+        ms_d, _ = time_launches(dstep, dspec.steps, 8, torch)
+        out["longctx_h32_t1m"] = {
+            "C": 64, "ms_per_prefill": ms_c, "tokens_per_s": B * T / (ms_cw * 1e-3),
+            "prefill_GBps": cb / (ms_c * 1e-3) / 1e9,
+            "prefill_frac_hbm": cb / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "decode_us_per_step": ms_d * 1e3,
+            "decode_note": "one sequence x 32 heads: 4 MiB of state per step; the events "
+                           "bracket back-to-back calls from Python, so this includes the "
+                           "binding's per-call host time (kernel time: profiles/)",
+        }
+        print(f"# longctx_h32_t1m: prefill {ms_c:.2f} ms, decode {ms_d * 1e3:.1f} us/step",
+              file=sys.stderr, flush=True)
+        del st, od, cS
         torch.cuda.empty_cache()
 
 
