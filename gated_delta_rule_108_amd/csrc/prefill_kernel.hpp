@@ -982,7 +982,12 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         }
       }
     }
-    fetch_gates(more ? t0 + C : t0);
+    // The next chunk's gate loads.  With four blocks, waves 2.. issue theirs in
+    // the second level of the off-diagonal solve below, where only waves 0
+    // and 1 compute: issued here by all eight waves, the loads queue in the
+    // CU's address unit and the last waves reach the barrier ~1.7k cycles
+    // late.  (In the first level they would queue behind the value loads.)
+    if (NB != 4 || wave < 2) fetch_gates(more ? t0 + C : t0);
     lds_barrier();
 
     // ================= AP + SD: gated K K^T (-> L in TT) and Q K^T (-> P) tiles.
@@ -1147,6 +1152,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         put_y(R, I, y, true);
       }
       lds_barrier();
+      if (wave >= 2) fetch_gates(more ? t0 + C : t0);   // idle waves (see G2)
       if (wave < 2) {
         const int c = wave;
         // Y_1c: Y10 (fp32 copy) for c = 0, Y11 (diagonal) for c = 1; Y_0c = 0 for c = 1
