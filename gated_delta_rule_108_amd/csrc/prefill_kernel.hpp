@@ -601,7 +601,6 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
   constexpr bool kStageO = C * LDO * static_cast<int>(sizeof(E)) <= Cf::kR1;
   using SM = TileMap<Cf::NCB, NJ, NW>;   // state tiles (Cb, Jb)
   using UM = TileMap<NB, NJ, NW>;        // chunk-output tiles (R, Jb)
-  using WMp = TileMap<Cf::NCB, NB, NW>;  // W^T tiles (Cb, R)
 
   __shared__ __attribute__((aligned(16))) char smem[Cf::kLds];
   E* Ki = reinterpret_cast<E*>(smem + Cf::oZ1);             // [C][LDK]
@@ -1226,20 +1225,21 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     f32x4 Ureg[UM::RA][UM::CA];
     {
       const Lane ln = lane_now();
-      if (WMp::active(wave)) {
+      // W^T tiles (Cb, R) cost 16 (R + 1) of contraction: tile t = wave + NW i
+      // is (t % NCB, t / NCB), so a wave takes every row block of its key
+      // channels and the waves' totals match (one R per wave left the wave
+      // pair of one SIMD with 4x the work of another).
+      constexpr int NWT = Cf::NCB * NB;
 #pragma unroll
-        for (int a = 0; a < WMp::RA; ++a) {
-          const int Cb = WMp::row0(wave) + a;
-#pragma unroll
-          for (int bb = 0; bb < WMp::CA; ++bb) {
-            const int R = WMp::col0(wave) + bb;
-            const f32x4 acc =
-                mma_k<OpT>(0, 16 * (R + 1), Src<OpT>{KbT + 16 * Cb * LDC, LDC, ln}, ysrc(R, ln));
-            // acc[rr] = W^T[c = 16Cb + 4g + rr][r = 16R + i]
-            E* dst = Wm + (16 * R + ln.i) * LDK + 16 * Cb + 4 * ln.g;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) dst[rr] = Ty<OpT>::from_f32(acc[rr]);
-          }
+      for (int i = 0; i < (NWT + NW - 1) / NW; ++i) {
+        const int t = wave + NW * i;
+        if (NWT % NW == 0 || t < NWT) {
+          const int Cb = t % Cf::NCB, R = t / Cf::NCB;
+          const f32x4 acc =
+              mma_k<OpT>(0, 16 * (R + 1), Src<OpT>{KbT + 16 * Cb * LDC, LDC, ln}, ysrc(R, ln));
+          // acc[rr] = W^T[c = 16Cb + 4g + rr][r = 16R + i]
+          Quad<OpT>::store(Wm + (16 * R + ln.i) * LDK + 16 * Cb + 4 * ln.g, acc[0], acc[1], acc[2],
+                           acc[3]);
         }
       }
 #pragma unroll
