@@ -182,3 +182,22 @@ def test_empty_sequence_and_null_state_out():
     torch.cuda.synchronize()
     o_ref, _ = oracle(inp)
     assert S is None and rel(f64(o), o_ref) < 2e-2
+
+
+@pytest.mark.parametrize("gated", [True, False])
+def test_split_segments(gated):
+    """16 chains x 313 chunks (T = 20000): three segments of the split path
+    with the state carried between them; two chains match the oracle."""
+    spec = wl.PREFILL["prefill_h16_t4k"]
+    T, H = 20000, 16
+    inp = wl.make_gdn_inputs(spec, T=T, H=H, gated=gated)
+    inp["S0"] = 0.05 * torch.randn(1, H, 128, 128, generator=torch.Generator().manual_seed(9))
+    o, S = run(inp, 64)
+    for h in (2, 15):
+        sl = {k: (None if v is None else (v[:, :, h:h + 1].contiguous() if k != "S0"
+                                          else v[:, h:h + 1].contiguous()))
+              for k, v in inp.items()}
+        o_ref, S_ref = oracle(sl)
+        eo, es = rel(f64(o[:, :, h:h + 1]), o_ref), rel(f64(S[:, h:h + 1]), S_ref)
+        print(f"[gdn segments T={T} head {h} gated={gated}] rel_o={eo:.3e} rel_S={es:.3e}", flush=True)
+        assert eo < 2e-2 and es < 2e-2

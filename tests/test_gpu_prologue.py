@@ -229,3 +229,21 @@ def test_empty_sequence_and_null_state_out():
     torch.cuda.synchronize()
     o_ref, _ = oracle(inp, "l2")
     assert S is None and rel(f64(o), o_ref) < 2e-2
+
+
+def test_split_segments():
+    """16 chains x 313 chunks (T = 20000): the split path runs three segments
+    with the state carried between them; two chains match the oracle."""
+    spec = wl.PREFILL["prefill_h16_t4k"]
+    T, H = 20000, 16
+    assert kda().prefill_workspace_bytes(1, T, H, 128, 128, 64) == 16 * 105 * 74240 + 16 * 128 * 128 * 4
+    inp = wl.make_prefill_logit_inputs(spec, T=T, H=H)
+    inp["S0"] = 0.05 * torch.randn(1, H, 128, 128, generator=torch.Generator().manual_seed(8))
+    o, S = run(inp, 64, "l2")
+    for h in (0, 13):
+        sl = {k: (inp[k][:, :, h:h + 1].contiguous() if k != "S0" else inp[k][:, h:h + 1].contiguous())
+              for k in inp}
+        o_ref, S_ref = oracle(sl, "l2")
+        eo, es = rel(f64(o[:, :, h:h + 1]), o_ref), rel(f64(S[:, h:h + 1]), S_ref)
+        print(f"[segments T={T} head {h} qk=l2] rel_o={eo:.3e} rel_S={es:.3e}", flush=True)
+        assert eo < 2e-2 and es < 2e-2
