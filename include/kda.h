@@ -32,8 +32,8 @@
  *     gate matrix.
  * Readings where the pages are silent: the gate scales the key dimension (the
  * rows of S) and acts before the read-back; the output reads the state after
- * the write; q and k are used exactly as given (no scaling, no feature map);
- * a missing initial state is zero.
+ * the write; q and k are used exactly as given (no scaling, no feature map)
+ * unless a *_logits call maps them; a missing initial state is zero.
  *
  * Conventions common to every entry point
  * ---------------------------------------
@@ -41,8 +41,11 @@
  *     row-major, and 16-byte aligned.  The library allocates nothing and keeps
  *     no mutable global state; calls are asynchronous on `stream` (an opaque
  *     hipStream_t; NULL means the null stream) and reentrant.
- *   - q, k, v and o have the element type `dt`; alpha, beta and the states are
- *     always float32.
+ *   - q, k, v and o have the element type `dt`; the states and beta (or its
+ *     logit) are always float32.  The gate is float32 alpha per key channel
+ *     (kda_prefill_chunked, kda_decode_step), a logit of type `dt` per key
+ *     channel (the *_logits calls) or float32 per token and head (the
+ *     kda_gdn_* calls).
  *   - Arguments are validated on the host before any launch; a failed
  *     validation returns a negative status and launches nothing.  A launch
  *     failure returns KDA_ERR_HIP.  Faults inside a kernel surface at the
