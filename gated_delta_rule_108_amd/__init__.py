@@ -23,6 +23,10 @@ DeltaNet (a=None, gate 1):
     o, S_T = gdn_prefill_chunked(q, k, v, a, beta, S0=None, chunk=64)
     o, S   = gdn_decode_step(q, k, v, a, beta, S)
 
+The adjoint of one decode step (gradients of a loss through it):
+
+    dq, dk, dv, dalpha, dbeta, dS = decode_step_backward(q, k, v, alpha, beta, S, dO, dS_new)
+
 Layouts (token-major, as the attention projections produce them):
     prefill  q,k [B,T,H,dk]  v [B,T,H,dv]  alpha [B,T,H,dk]  beta [B,T,H]
              S0, S_T [B,H,dk,dv]  o [B,T,H,dv]
@@ -39,7 +43,8 @@ from . import _lib
 from ._lib import KDAError  # noqa: F401
 
 __all__ = ["prefill_chunked", "decode_step", "prefill_chunked_logits", "decode_step_logits",
-           "gdn_prefill_chunked", "gdn_decode_step", "prefill_workspace_bytes", "KDAError", "lib"]
+           "gdn_prefill_chunked", "gdn_decode_step", "decode_step_backward",
+           "prefill_workspace_bytes", "KDAError", "lib"]
 
 _DT = {torch.bfloat16: _lib.KDA_BF16, torch.float32: _lib.KDA_F32}
 _QK = {"as_given": _lib.KDA_QK_AS_GIVEN, "l2": _lib.KDA_QK_L2, "silu_l2": _lib.KDA_QK_SILU_L2}
@@ -208,3 +213,36 @@ def _decode(q, k, v, gate, beta, S, out, state_out, qk):
     if st != _lib.KDA_OK:
         raise KDAError(st, where)
     return o, S_out
+
+
+def decode_step_backward(q, k, v, alpha, beta, S, dO, dS_new, in_place=False):
+    """Adjoint of decode_step: given dO = dL/do [N,H,dv] (dtype of q) and
+    dS_new = dL/dS after the step [N,H,dk,dv] float32, returns (dq, dk, dv,
+    dalpha, dbeta, dS) with dS = dL/dS before the step; in_place=True writes
+    dS over dS_new."""
+    L = lib()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if q.dtype not in _DT:
+        raise TypeError(f"q: dtype {q.dtype} not supported")
+    dt = q.dtype
+    for n, t, d, s in (("q", q, dt, (N, H, dk)), ("k", k, dt, (N, H, dk)), ("v", v, dt, (N, H, dv)),
+                       ("alpha", alpha, torch.float32, (N, H, dk)),
+                       ("beta", beta, torch.float32, (N, H)),
+                       ("S", S, torch.float32, (N, H, dk, dv)), ("dO", dO, dt, (N, H, dv)),
+                       ("dS_new", dS_new, torch.float32, (N, H, dk, dv))):
+        _check(n, t, d, s, dev)
+    g_q = torch.empty((N, H, dk), dtype=dt, device=dev)
+    g_k = torch.empty((N, H, dk), dtype=dt, device=dev)
+    g_v = torch.empty((N, H, dv), dtype=dt, device=dev)
+    g_a = torch.empty((N, H, dk), dtype=torch.float32, device=dev)
+    g_b = torch.empty((N, H), dtype=torch.float32, device=dev)
+    g_S = dS_new if in_place else torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    st = L.kda_decode_step_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S),
+                                    _ptr(dO), _ptr(dS_new), _ptr(g_q), _ptr(g_k), _ptr(g_v),
+                                    _ptr(g_a), _ptr(g_b), _ptr(g_S), N, H, dk, dv, _DT[dt],
+                                    _stream(dev))
+    if st != _lib.KDA_OK:
+        raise KDAError(st, "kda_decode_step_backward")
+    return g_q, g_k, g_v, g_a, g_b, g_S

@@ -241,4 +241,42 @@ kda_status kda_gdn_decode_step(const void* q, const void* k, const void* v, cons
                      stream);
 }
 
+kda_status kda_decode_step_backward(const void* q, const void* k, const void* v,
+                                    const float* alpha, const float* beta, const float* S_in,
+                                    const void* dO, const float* dS_new, void* dq, void* dk,
+                                    void* dv, float* dalpha, float* dbeta, float* dS, int N, int H,
+                                    int dk_, int dv_, kda_dtype dt, void* stream) {
+  if (N < 1 || H < 1) return KDA_ERR_SHAPE;
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  if (!dim_ok(dk_) || !dim_ok(dv_)) return KDA_ERR_UNSUPPORTED;
+  const void* ptrs[] = {q, k, v, alpha, beta, S_in, dO, dS_new, dq, dk, dv, dalpha, dbeta, dS};
+  for (const void* p : ptrs) {
+    if (!p) return KDA_ERR_NULL;
+    if (!aligned16(p)) return KDA_ERR_ALIGN;
+  }
+  const size_t e = (dt == KDA_BF16) ? 2 : 4;
+  const size_t nh = static_cast<size_t>(N) * H;
+  const size_t nst = nh * dk_ * dv_ * 4;
+  const Span ins[] = {span(q, nh * dk_ * e), span(k, nh * dk_ * e), span(v, nh * dv_ * e),
+                      span(alpha, nh * dk_ * 4), span(beta, nh * 4), span(S_in, nst),
+                      span(dO, nh * dv_ * e), span(dS_new, nst)};
+  const Span outs[] = {span(dq, nh * dk_ * e), span(dk, nh * dk_ * e), span(dv, nh * dv_ * e),
+                       span(dalpha, nh * dk_ * 4), span(dbeta, nh * 4), span(dS, nst)};
+  constexpr int kIns = sizeof(ins) / sizeof(ins[0]), kOuts = sizeof(outs) / sizeof(outs[0]);
+  for (int o = 0; o < kOuts; ++o) {
+    for (int i = 0; i < kIns; ++i) {
+      const bool in_place = (o == kOuts - 1) && (i == kIns - 1) && dS == dS_new;
+      if (!in_place && overlap(outs[o], ins[i])) return KDA_ERR_ALIAS;
+    }
+    for (int p = 0; p < o; ++p)
+      if (overlap(outs[o], outs[p])) return KDA_ERR_ALIAS;
+  }
+  const kda_status dev = check_device();
+  if (dev != KDA_OK) return dev;
+  kda::DecodeBwdArgs a{q,  k,  v,  alpha,  beta,  S_in, dO, dS_new, dq,  dk,
+                       dv, dalpha, dbeta, dS, N, H, dk_, dv_, dt == KDA_BF16, stream};
+  if (kda::launch_decode_backward(a) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
 }  // extern "C"

@@ -50,7 +50,29 @@ struct PrefillArgs {
   int qk_map;               // QkMap, used with kGateLogit
 };
 
+// The adjoint of one decode step (decode_backward.hip).
+struct DecodeBwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* S_in;
+  const void* dO;
+  const float* dS_new;
+  void* g_q;          // gradients written: dq, dk, dv (I/O type), dalpha, dbeta, dS
+  void* g_k;
+  void* g_v;
+  float* g_alpha;
+  float* g_beta;
+  float* g_S;         // may equal dS_new
+  int N, H, dk, dv;
+  bool bf16;
+  void* stream;
+};
+
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_decode_backward(const DecodeBwdArgs& a);
 
 // Returns hipErrorInvalidValue when no compiled kernel covers (dk, C, dtype).
 hipError_t launch_prefill(const PrefillArgs& a);

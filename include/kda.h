@@ -256,6 +256,43 @@ kda_status kda_gdn_decode_step(const void* q, const void* k, const void* v, cons
                                const float* beta, const float* S_in, void* o, float* S_out,
                                int N, int H, int dk, int dv, kda_dtype dt, void* stream);
 
+/*
+ * kda_decode_step_backward — the adjoint of kda_decode_step: given the
+ * gradients of a loss L with respect to the step's output and new state,
+ * the gradients with respect to every input of the step.  Applied backwards
+ * over a sequence's tokens (with the state before each token), it gives the
+ * exact gradient of a prefill or of a run of decode steps.  The forward step
+ * is that of "From GPT-2 to Kimi K3, Explained", sections "DeltaNet (Fast
+ * Weight Programmers)" and "KDA/Kimi Linear"; the adjoint is its chain rule:
+ * with S' = Diag(alpha) S_in, r = k S', u = beta (v - r) and
+ * G = dS_new + q^T dO,
+ *     dq = (S' + k^T u) dO^T        dk = G u^T - beta S' (k G)^T
+ *     dv = beta k G                 dbeta = (k G) . (v - r)
+ *     dalpha = rowsum((G - beta k^T (k G)) * S_in)
+ *     dS = Diag(alpha) (G - beta k^T (k G))
+ *
+ *   q, k, v, alpha, beta, S_in   the step's inputs, as kda_decode_step
+ *   dO      [N, H, dv]      dt        dL/do
+ *   dS_new  [N, H, dk, dv]  float32   dL/dS after the step
+ *   dq, dk  [N, H, dk]      dt        written
+ *   dv      [N, H, dv]      dt        written
+ *   dalpha  [N, H, dk]      float32   written
+ *   dbeta   [N, H]          float32   written
+ *   dS      [N, H, dk, dv]  float32   dL/dS_in (written); may be equal to
+ *                                     dS_new (in place) but may not overlap
+ *                                     it otherwise
+ *
+ * Every pointer is required.  No output may overlap an input or another
+ * output (dS == dS_new aside).  Errors: KDA_ERR_NULL, KDA_ERR_SHAPE,
+ * KDA_ERR_UNSUPPORTED, KDA_ERR_ALIGN, KDA_ERR_ALIAS, KDA_ERR_DEVICE,
+ * KDA_ERR_HIP.
+ */
+kda_status kda_decode_step_backward(const void* q, const void* k, const void* v,
+                                    const float* alpha, const float* beta, const float* S_in,
+                                    const void* dO, const float* dS_new, void* dq, void* dk,
+                                    void* dv, float* dalpha, float* dbeta, float* dS, int N,
+                                    int H, int dk_, int dv_, kda_dtype dt, void* stream);
+
 /* kda_status_string — static, human-readable text for a status code. */
 const char* kda_status_string(kda_status s);
 

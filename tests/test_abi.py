@@ -25,8 +25,9 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_eight_calls():
-    assert declared_functions() == ["kda_decode_step", "kda_decode_step_logits",
+def test_header_declares_the_nine_calls():
+    assert declared_functions() == ["kda_decode_step", "kda_decode_step_backward",
+                                    "kda_decode_step_logits",
                                     "kda_gdn_decode_step", "kda_gdn_prefill_chunked",
                                     "kda_prefill_chunked", "kda_prefill_chunked_logits",
                                     "kda_prefill_workspace_bytes", "kda_status_string"]
@@ -252,3 +253,30 @@ def test_gdn_entry_points_take_a_null_gate_and_validate():
     assert gp(o=g_end - 16) == L.KDA_ERR_ALIAS
     assert gp(o=g_end) in ok
     assert gd(o=addr(3) + 4 * 2 * 4) in ok and gd(o=addr(3)) == L.KDA_ERR_ALIAS
+
+
+def test_step_backward_validation():
+    L = _lib()
+    lib = L.load()
+    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+
+    def bw(**kw):
+        a = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), S=addr(5),
+                 dO=addr(6), dSn=addr(7), dq=addr(8), dk=addr(9), dv=addr(10), da=addr(11),
+                 db=addr(12), dS=addr(13), N=4, H=2, dk_=128, dv_=128, dt=1, stream=None)
+        a.update(kw)
+        return lib.kda_decode_step_backward(a["q"], a["k"], a["v"], a["alpha"], a["beta"],
+                                            a["S"], a["dO"], a["dSn"], a["dq"], a["dk"],
+                                            a["dv"], a["da"], a["db"], a["dS"], a["N"], a["H"],
+                                            a["dk_"], a["dv_"], a["dt"], a["stream"])
+
+    assert bw() in ok
+    assert bw(dS=addr(7)) in ok                                  # in place over dS_new
+    assert bw(dS=addr(5)) == L.KDA_ERR_ALIAS                     # over the state
+    assert bw(dS=addr(7) + 64) == L.KDA_ERR_ALIAS                # partial overlap with dS_new
+    assert bw(dq=addr(9)) == L.KDA_ERR_ALIAS                     # two outputs together
+    assert bw(dv=addr(6)) == L.KDA_ERR_ALIAS                     # output over dO
+    assert bw(db=None) == L.KDA_ERR_NULL
+    assert bw(da=addr(11) + 4) == L.KDA_ERR_ALIGN
+    assert bw(N=0) == L.KDA_ERR_SHAPE
+    assert bw(dk_=24) == L.KDA_ERR_UNSUPPORTED
