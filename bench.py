@@ -14,6 +14,7 @@ Alongside the headline it measures, on the same GPU:
   * the same two with one gate per token and head (Gated DeltaNet);
   * the long-context prefill (H=32, T=1,048,576) and 256 single-sequence
     decode steps from its final state, reported separately;
+  * the adjoint of one decode step for 256 sequences x 32 heads;
   * the float64 oracle on the host cores over a bounded sample (cpu_baseline).
 """
 from __future__ import annotations
@@ -68,6 +69,15 @@ def decode_alg_bytes(N, H, dk, dv, esize, gate_bytes=4):
     """State read and write plus one token's inputs and output per head; the
     gate is fp32 alpha (4 bytes) or a logit of the I/O type."""
     per_head = 2 * dk * dv * 4 + esize * (2 * dk + dv) + gate_bytes * dk + 4 + esize * dv
+    return N * H * per_head
+
+
+def decode_bwd_alg_bytes(N, H, dk, dv, esize):
+    """Step adjoint: state and incoming state gradient read, outgoing state
+    gradient written (fp32), the step's vectors read and their gradients
+    written."""
+    per_head = (3 * dk * dv * 4 + esize * (2 * dk + dv) + 4 * dk + 4 + esize * dv
+                + esize * (2 * dk + dv) + 4 * dk + 4)
     return N * H * per_head
 
 
@@ -204,7 +214,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="headline prefill only (no decode / large prefill lines)")
     ap.add_argument("--only", choices=["prefill", "decode", "large", "logits", "decode_logits",
-                                       "gdn", "decode_gdn", "longctx", "copy"], default=None,
+                                       "gdn", "decode_gdn", "longctx", "decode_bwd", "copy"],
+                    default=None,
                     help="run one leg only (for profiler runs); 'copy' times a plain "
                          "1 GiB device-to-device copy used to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -230,7 +241,7 @@ def main():
                           "ms_per_copy": ms, "GBps": 8 * n / (ms * 1e-3) / 1e9}), flush=True)
         return
     legs = ({"prefill", "decode", "large", "logits", "decode_logits", "gdn", "decode_gdn",
-             "longctx"} if args.only is None else {args.only})
+             "longctx", "decode_bwd"} if args.only is None else {args.only})
     if args.no_extra:
         legs = {"prefill"}
 
@@ -461,6 +472,30 @@ def extras(args, legs, out, torch, kda, wl, dev):
         }
         print(f"# decode_n256_h32_gdn: {ms_d * 1e3:.1f} us/step", file=sys.stderr, flush=True)
         del S, st, od, ga
+        torch.cuda.empty_cache()
+
+    if "decode_bwd" in legs:
+        # ---------------- step adjoint: 256 x 32 heads, dS in place over dS_new
+        dspec = wl.DECODE["decode_n256_h32"]
+        S = wl.make_decode_state(dspec, dev)
+        gS = wl.make_decode_state(dspec, dev, N=dspec.N)
+        st = wl.make_decode_step_inputs(dspec, dev)
+        dO = st["v"].clone()
+
+        def bstep():
+            kda.decode_step_backward(st["q"], st["k"], st["v"], st["alpha"], st["beta"], S, dO,
+                                     gS, in_place=True)
+
+        ms_b, _ = time_launches(bstep, max(args.steps, 20), args.warmup, torch)
+        bbytes = decode_bwd_alg_bytes(dspec.N, dspec.H, dspec.dk, dspec.dv, 2)
+        out["decode_bwd_n256_h32"] = {
+            "us_per_step": ms_b * 1e3, "alg_GBps": bbytes / (ms_b * 1e-3) / 1e9,
+            "frac_hbm": bbytes / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": profiled_traffic("decode_bwd_n256_h32"), "alg_bytes_per_step": bbytes,
+        }
+        print(f"# decode_bwd_n256_h32: {ms_b * 1e3:.1f} us/step, "
+              f"{out['decode_bwd_n256_h32']['alg_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+        del S, gS, st, dO
         torch.cuda.empty_cache()
 
     if "longctx" in legs:
