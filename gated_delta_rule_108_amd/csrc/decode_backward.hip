@@ -22,7 +22,10 @@
 // thread (row group rg, column group cg) holds RPT rows x 4 columns of S and
 // of dS_new, one 16-byte load per row each.  Column sums run over the row
 // groups (lane exchanges, then LDS across waves); row sums over the CG lanes
-// of a row group, which are consecutive lanes of one wave.
+// of a row group, which are consecutive lanes of one wave (DPP moves within
+// 16-lane rows).
+#include <type_traits>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -39,6 +42,28 @@ struct BwdCfg {
   static_assert(RPT * RG == DK, "rows must split evenly");
   static_assert(NTH >= DK, "one thread per key row stages the row vectors");
 };
+
+// Sum of x over the CG consecutive lanes of a row group (CG a power of two,
+// 4..32), returned to every one of them.  Within a 16-lane row the steps are
+// DPP moves (quad_perm for lane xor 1 and 2; row rotations by 4 and 8, which
+// after the quad sums add the other three quads of the row); lane xor 4 for
+// groups of 8, and xor 16 across rows, go through the lane crossbar.
+template <int CG>
+__device__ __forceinline__ float sum_row_group(float x) {
+  auto dpp = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), decltype(ctrl)::value, 0xF,
+                                                    0xF, false));
+  };
+  x += dpp(x, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]: lane xor 1
+  x += dpp(x, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]: lane xor 2
+  if constexpr (CG == 8) x += __shfl_xor(x, 4);
+  if constexpr (CG >= 16) {
+    x += dpp(x, std::integral_constant<int, 0x124>{});  // row_ror:4
+    x += dpp(x, std::integral_constant<int, 0x128>{});  // row_ror:8
+  }
+  if constexpr (CG >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
 
 __device__ __forceinline__ void store_nt(float* p, float a, float b, float c, float d) {
   typedef float f4v __attribute__((ext_vector_type(4)));
@@ -154,8 +179,7 @@ kda_decode_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
     pb += du * (vv[j] - rk[j]);
     if (rg == 0) dv[vbase + j] = Ty<IO>::from_f32(bt * du);
   }
-#pragma unroll
-  for (int off = 1; off < CG; off <<= 1) pb += __shfl_xor(pb, off);
+  pb = sum_row_group<CG>(pb);
   if (tid == 0) dbeta[nh] = pb;
 
   // ---- per element, then row sums over the value columns
@@ -178,12 +202,9 @@ kda_decode_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
       out[j] = a * dsp;
     }
     store_nt(dS + sbase + static_cast<size_t>(r) * DV + 4 * cg, out[0], out[1], out[2], out[3]);
-#pragma unroll
-    for (int off = 1; off < CG; off <<= 1) {
-      pq += __shfl_xor(pq, off);
-      pk += __shfl_xor(pk, off);
-      pa += __shfl_xor(pa, off);
-    }
+    pq = sum_row_group<CG>(pq);
+    pk = sum_row_group<CG>(pk);
+    pa = sum_row_group<CG>(pa);
     if (cg == 0) {
       const size_t ro = static_cast<size_t>(nh) * DK + r;
       dq[ro] = Ty<IO>::from_f32(pq);
