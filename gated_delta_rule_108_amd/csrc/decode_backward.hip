@@ -20,7 +20,9 @@
 // the incoming state gradient and writes the outgoing one (3 dk dv fp32).
 // The row sums need every column, so a workgroup owns one head's whole state:
 // thread (row group rg, column group cg) holds RPT rows x 4 columns of S and
-// of dS_new, one 16-byte load per row each.  Column sums run over the row
+// of dS_new, one 16-byte load per row each.  256 threads (16 rows each at
+// dk = dv = 128) leave room for two workgroups per CU, two heads' loads in
+// flight (512 threads fit one and ran 5% slower).  Column sums run over the row
 // groups (lane exchanges, then LDS across waves); row sums over the CG lanes
 // of a row group, which are consecutive lanes of one wave (DPP moves within
 // 16-lane rows).
@@ -34,7 +36,7 @@ namespace kda {
 template <int DK, int DV>
 struct BwdCfg {
   static constexpr int CG = DV / 4;                                   // float4 column groups
-  static constexpr int NTH = (CG * DK < 512) ? CG * DK : 512;         // threads
+  static constexpr int NTH = (CG * DK < 256) ? CG * DK : 256;         // threads
   static constexpr int RG = NTH / CG;                                  // row groups
   static constexpr int RPT = DK / RG;                                  // rows per thread
   static constexpr int NWV = NTH / kWave;
@@ -76,7 +78,7 @@ __device__ __forceinline__ void store_nt(float* p, float a, float b, float c, fl
 }
 
 template <typename IO, int DK, int DV>
-__global__ void __launch_bounds__(512)   // BwdCfg::NTH <= 512
+__global__ void __launch_bounds__(256)   // BwdCfg::NTH <= 256
 kda_decode_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
                            const typename Ty<IO>::Elem* __restrict__ k,
                            const typename Ty<IO>::Elem* __restrict__ v,
