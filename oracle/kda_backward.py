@@ -26,14 +26,19 @@ tests/test_backward_pins.py against central finite differences of the
 forward oracle (a different computation that a wrong sign, a dropped term or
 a transposed product fails), for one step and for a chain of steps that
 reproduces the gradient of a whole prefill.
+
+kda_prefill_backward is that chain written out: the forward recurrence
+(kda_oracle.kda_recurrence) run once to keep the state before every token,
+then the step adjoint applied from the last token to the first, the state
+gradient carried from token to token and, after token 0, returned as dS0.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .kda_oracle import as_f64
+from .kda_oracle import as_f64, kda_decode_step
 
-__all__ = ["kda_decode_step_backward"]
+__all__ = ["kda_decode_step_backward", "kda_prefill_backward"]
 
 
 def kda_decode_step_backward(q, k, v, alpha, beta, S, dO, dS_new):
@@ -59,3 +64,27 @@ def kda_decode_step_backward(q, k, v, alpha, beta, S, dO, dS_new):
     dalpha = np.sum(dSp * S, axis=-1)
     dS = alpha[..., :, None] * dSp
     return dq, dk, dv, dalpha, dbeta, dS
+
+
+def kda_prefill_backward(q, k, v, alpha, beta, S0, dO, dS_T):
+    """Gradients of L through a whole prefill, float64.
+
+    q, k, alpha: [B, T, H, dk]; v, dO: [B, T, H, dv]; beta: [B, T, H];
+    S0, dS_T: [B, H, dk, dv] or None (zeros).  dO = dL/do for every token,
+    dS_T = dL/dS_T for the final state.  Returns (dq, dk, dv, dalpha, dbeta,
+    dS0), shaped like q, k, v, alpha, beta and the state."""
+    q, k, v, alpha, beta, dO = (as_f64(x) for x in (q, k, v, alpha, beta, dO))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, dk, dv)) if S0 is None else as_f64(S0).copy()
+    before = []                                   # S_{t-1}: the state token t starts from
+    for t in range(T):
+        before.append(S)
+        _, S = kda_decode_step(q[:, t], k[:, t], v[:, t], alpha[:, t], beta[:, t], S)
+    dS = np.zeros((B, H, dk, dv)) if dS_T is None else as_f64(dS_T).copy()
+    dq, dk_, dv_ = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    da, db = np.zeros_like(alpha), np.zeros_like(beta)
+    for t in reversed(range(T)):
+        dq[:, t], dk_[:, t], dv_[:, t], da[:, t], db[:, t], dS = kda_decode_step_backward(
+            q[:, t], k[:, t], v[:, t], alpha[:, t], beta[:, t], before[t], dO[:, t], dS)
+    return dq, dk_, dv_, da, db, dS

@@ -143,3 +143,91 @@ KINDS = ["no_output_term", "dq_from_decayed", "dbeta_without_read", "dr_sign", "
 @pytest.mark.parametrize("kind", KINDS)
 def test_pins_catch_planted_mistake(kind):
     assert step_fd_error(_mutant(kind)) > 1e-4 or chain_fd_error(_mutant(kind)) > 1e-4
+
+
+# ------------------------------------------------ whole-prefill backward --
+#
+# oracle.kda_prefill_backward against central finite differences of the
+# prefill oracle, for every input (S0 included), with and without an initial
+# state and a final-state gradient; planted mistakes in how the chain is
+# walked (wrong state, dropped or frozen state gradient) must fail.
+
+from oracle.kda_backward import kda_prefill_backward  # noqa: E402
+
+PNAMES = ("q", "k", "v", "alpha", "beta", "S0")
+
+
+def prefill_fd_error(backward, seed=7, T=9, with_S0=True, with_dST=True):
+    r = np.random.default_rng(seed)
+    q, k, v, alpha, beta, S0 = pins.rand_case(seed, B=2, T=T, H=2, dk=4, dv=3)
+    if not with_S0:
+        S0 = np.zeros_like(S0)
+    dO = r.standard_normal((2, T, 2, 3))
+    dST = r.standard_normal((2, 2, 4, 3)) if with_dST else None
+
+    def loss(a):
+        o, S = kda_recurrence(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"])
+        return float(np.sum(dO * o) + (0.0 if dST is None else np.sum(dST * S)))
+
+    x = dict(q=q, k=k, v=v, alpha=alpha, beta=beta, S0=S0)
+    g = dict(zip(PNAMES, backward(q, k, v, alpha, beta, S0 if with_S0 else None, dO, dST)))
+    err = 0.0
+    for n in PNAMES:
+        for _ in range(2):
+            e = r.standard_normal(x[n].shape)
+            fd = (loss(dict(x, **{n: x[n] + H_FD * e})) - loss(dict(x, **{n: x[n] - H_FD * e}))) \
+                / (2 * H_FD)
+            err = max(err, abs(fd - float(np.sum(g[n] * e))) / max(abs(fd), 1e-3))
+    return err
+
+
+@pytest.mark.parametrize("with_S0,with_dST", [(True, True), (False, True), (True, False),
+                                              (False, False)])
+def test_prefill_backward_matches_finite_differences(with_S0, with_dST):
+    assert prefill_fd_error(kda_prefill_backward, with_S0=with_S0, with_dST=with_dST) < TOL
+
+
+def test_prefill_backward_single_token_is_the_step_adjoint():
+    q, k, v, alpha, beta, S0 = pins.rand_case(3, B=1, T=1, H=2, dk=4, dv=3)
+    r = np.random.default_rng(3)
+    dO, dST = r.standard_normal((1, 1, 2, 3)), r.standard_normal((1, 2, 4, 3))
+    a = kda_prefill_backward(q, k, v, alpha, beta, S0, dO, dST)
+    b = kda_decode_step_backward(q[:, 0], k[:, 0], v[:, 0], alpha[:, 0], beta[:, 0], S0,
+                                 dO[:, 0], dST)
+    for x, y in zip(a[:5], b[:5]):
+        assert pins.rel(x[:, 0], y) < 1e-15
+    assert pins.rel(a[5], b[5]) < 1e-15
+
+
+def test_prefill_backward_of_zero_gradients_is_zero():
+    q, k, v, alpha, beta, S0 = pins.rand_case(4, B=1, T=5, H=1, dk=3, dv=2)
+    out = kda_prefill_backward(q, k, v, alpha, beta, S0, np.zeros((1, 5, 1, 2)), None)
+    assert all(np.all(x == 0) for x in out)
+
+
+def _chain_mutant(kind):
+    def bwd(q, k, v, alpha, beta, S0, dO, dS_T):
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        S = np.zeros((B, H, dk, dv)) if S0 is None else S0
+        seq = [S]
+        for t in range(T):
+            _, S = kda_decode_step(q[:, t], k[:, t], v[:, t], alpha[:, t], beta[:, t], S)
+            seq.append(S)
+        dS = np.zeros((B, H, dk, dv)) if (dS_T is None or kind == "drop_dST") else dS_T
+        out = [np.zeros_like(x) for x in (q, k, v, alpha, beta)]
+        for t in reversed(range(T)):
+            st = seq[t + 1] if kind == "state_after" else seq[t]
+            res = kda_decode_step_backward(q[:, t], k[:, t], v[:, t], alpha[:, t], beta[:, t],
+                                           st, dO[:, t], dS)
+            for o_, g_ in zip(out, res[:5]):
+                o_[:, t] = g_
+            if kind != "frozen_dS":
+                dS = res[5]
+        return (*out, dS)
+    return bwd
+
+
+@pytest.mark.parametrize("kind", ["state_after", "drop_dST", "frozen_dS"])
+def test_prefill_pins_catch_planted_chain_mistake(kind):
+    assert prefill_fd_error(_chain_mutant(kind)) > 1e-4
