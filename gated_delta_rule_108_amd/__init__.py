@@ -27,6 +27,10 @@ The adjoint of one decode step (gradients of a loss through it):
 
     dq, dk, dv, dalpha, dbeta, dS = decode_step_backward(q, k, v, alpha, beta, S, dO, dS_new)
 
+and of a whole prefill (float32 gradients; S0 and dS_T optional):
+
+    dq, dk, dv, dalpha, dbeta, dS0 = prefill_backward(q, k, v, alpha, beta, dO, S0, dS_T)
+
 Layouts (token-major, as the attention projections produce them):
     prefill  q,k [B,T,H,dk]  v [B,T,H,dv]  alpha [B,T,H,dk]  beta [B,T,H]
              S0, S_T [B,H,dk,dv]  o [B,T,H,dv]
@@ -44,6 +48,7 @@ from ._lib import KDAError  # noqa: F401
 
 __all__ = ["prefill_chunked", "decode_step", "prefill_chunked_logits", "decode_step_logits",
            "gdn_prefill_chunked", "gdn_decode_step", "decode_step_backward",
+           "prefill_backward", "prefill_backward_workspace_bytes",
            "prefill_workspace_bytes", "KDAError", "lib"]
 
 _DT = {torch.bfloat16: _lib.KDA_BF16, torch.float32: _lib.KDA_F32}
@@ -245,4 +250,47 @@ def decode_step_backward(q, k, v, alpha, beta, S, dO, dS_new, in_place=False):
                                     _stream(dev))
     if st != _lib.KDA_OK:
         raise KDAError(st, "kda_decode_step_backward")
+    return g_q, g_k, g_v, g_a, g_b, g_S
+
+
+def prefill_backward_workspace_bytes(B, T, H, dk, dv) -> int:
+    return int(lib().kda_prefill_backward_workspace_bytes(B, T, H, dk, dv))
+
+
+def prefill_backward(q, k, v, alpha, beta, dO, S0=None, dS_T=None):
+    """Gradients of a loss L through prefill_chunked: given dO = dL/do
+    [B,T,H,dv] (dtype of q) and, optionally, dS_T = dL/dS_T [B,H,dk,dv]
+    float32, returns (dq, dk, dv, dalpha, dbeta, dS0), all float32, shaped
+    like q, k, v, alpha, beta and the state."""
+    L = lib()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if q.dtype not in _DT:
+        raise TypeError(f"q: dtype {q.dtype} not supported")
+    dt = q.dtype
+    f32 = torch.float32
+    for n, t, d, s in (("q", q, dt, (B, T, H, dk)), ("k", k, dt, (B, T, H, dk)),
+                       ("v", v, dt, (B, T, H, dv)), ("alpha", alpha, f32, (B, T, H, dk)),
+                       ("beta", beta, f32, (B, T, H)), ("dO", dO, dt, (B, T, H, dv))):
+        _check(n, t, d, s, dev)
+    for n, t in (("S0", S0), ("dS_T", dS_T)):
+        if t is not None:
+            _check(n, t, f32, (B, H, dk, dv), dev)
+    g_q = torch.empty((B, T, H, dk), dtype=f32, device=dev)
+    g_k = torch.empty((B, T, H, dk), dtype=f32, device=dev)
+    g_v = torch.empty((B, T, H, dv), dtype=f32, device=dev)
+    g_a = torch.empty((B, T, H, dk), dtype=f32, device=dev)
+    g_b = torch.empty((B, T, H), dtype=f32, device=dev)
+    g_S = torch.empty((B, H, dk, dv), dtype=f32, device=dev)
+    nws = prefill_backward_workspace_bytes(B, T, H, dk, dv)
+    if nws == (1 << 64) - 1:                      # (size_t)-1: sizes not supported
+        raise KDAError(_lib.KDA_ERR_UNSUPPORTED, "kda_prefill_backward_workspace_bytes")
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    st = L.kda_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0),
+                                _ptr(dO), _ptr(dS_T), _ptr(g_q), _ptr(g_k), _ptr(g_v), _ptr(g_a),
+                                _ptr(g_b), _ptr(g_S), B, T, H, dk, dv, _DT[dt], _ptr(ws), nws,
+                                _stream(dev))
+    if st != _lib.KDA_OK:
+        raise KDAError(st, "kda_prefill_backward")
     return g_q, g_k, g_v, g_a, g_b, g_S

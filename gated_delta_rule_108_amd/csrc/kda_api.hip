@@ -279,4 +279,58 @@ kda_status kda_decode_step_backward(const void* q, const void* k, const void* v,
   return KDA_OK;
 }
 
+size_t kda_prefill_backward_workspace_bytes(int B, int T, int H, int dk, int dv) {
+  if (B < 1 || H < 1 || T < 0 || !dim_ok(dk) || !dim_ok(dv)) return static_cast<size_t>(-1);
+  return kda::prefill_backward_workspace(B, T, H, dk, dv);
+}
+
+kda_status kda_prefill_backward(const void* q, const void* k, const void* v, const float* alpha,
+                                const float* beta, const float* S0, const void* dO,
+                                const float* dS_T, float* dq, float* dk, float* dv,
+                                float* dalpha, float* dbeta, float* dS0, int B, int T, int H,
+                                int dk_, int dv_, kda_dtype dt, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (B < 1 || H < 1 || T < 0) return KDA_ERR_SHAPE;
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  if (!dim_ok(dk_) || !dim_ok(dv_)) return KDA_ERR_UNSUPPORTED;
+  const bool has_tokens = T > 0;
+  if (has_tokens && (!q || !k || !v || !alpha || !beta || !dO || !dq || !dk || !dv || !dalpha ||
+                     !dbeta))
+    return KDA_ERR_NULL;
+  const void* ptrs[] = {q,  k,  v,      alpha, beta, S0,  dO,       dS_T,
+                        dq, dk, dv, dalpha, dbeta, dS0, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+  const size_t ws_need = kda::prefill_backward_workspace(B, T, H, dk_, dv_);
+  if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need)) return KDA_ERR_WORKSPACE;
+
+  const size_t e = (dt == KDA_BF16) ? 2 : 4;
+  const size_t ntok = has_tokens ? static_cast<size_t>(B) * T * H : 0;
+  const size_t nst = static_cast<size_t>(B) * H * dk_ * dv_ * 4;
+  auto sp = [](const void* p, size_t n) { return p ? span(p, n) : Span{0, 0}; };
+  const Span ins[] = {sp(q, ntok * dk_ * e),  sp(k, ntok * dk_ * e), sp(v, ntok * dv_ * e),
+                      sp(alpha, ntok * dk_ * 4), sp(beta, ntok * 4), sp(S0, nst),
+                      sp(dO, ntok * dv_ * e), sp(dS_T, nst)};
+  const Span outs[] = {sp(dq, ntok * dk_ * 4),     sp(dk, ntok * dk_ * 4), sp(dv, ntok * dv_ * 4),
+                       sp(dalpha, ntok * dk_ * 4), sp(dbeta, ntok * 4),    sp(dS0, nst),
+                       sp(workspace, ws_need)};
+  constexpr int kIns = sizeof(ins) / sizeof(ins[0]), kOuts = sizeof(outs) / sizeof(outs[0]);
+  for (int o = 0; o < kOuts; ++o) {
+    for (int i = 0; i < kIns; ++i) {
+      // dS0 may be dS_T itself: each element is read before it is written, by one lane.
+      const bool in_place = (o == 5) && (i == 7) && dS0 == dS_T;
+      if (!in_place && overlap(outs[o], ins[i])) return KDA_ERR_ALIAS;
+    }
+    for (int p = 0; p < o; ++p)
+      if (overlap(outs[o], outs[p])) return KDA_ERR_ALIAS;
+  }
+  const kda_status dev = check_device();
+  if (dev != KDA_OK) return dev;
+  kda::PrefillBwdArgs a{q,  k,  v,      alpha, beta,      S0, dO, dS_T, dq, dk,
+                        dv, dalpha, dbeta, dS0, workspace, B,  T,  H,    dk_, dv_,
+                        dt == KDA_BF16, stream};
+  if (kda::launch_prefill_backward(a) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
 }  // extern "C"

@@ -74,6 +74,30 @@ struct DecodeBwdArgs {
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_decode_backward(const DecodeBwdArgs& a);
 
+// Backward of a whole prefill.  Gradients are float32; g_S0 may be null.
+struct PrefillBwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* S0;     // may be null (zeros)
+  const void* dO;
+  const float* dS_T;   // may be null (zeros)
+  float* g_q;          // [B,T,H,dk]
+  float* g_k;
+  float* g_v;          // [B,T,H,dv]
+  float* g_alpha;      // [B,T,H,dk]
+  float* g_beta;       // [B,T,H]
+  float* g_S0;         // [B,H,dk,dv] or null
+  void* workspace;     // prefill_backward_workspace bytes
+  int B, T, H, dk, dv;
+  bool bf16;
+  void* stream;
+};
+hipError_t launch_prefill_backward(const PrefillBwdArgs& a);
+size_t prefill_backward_workspace(int B, int T, int H, int dk, int dv);
+
 // Returns hipErrorInvalidValue when no compiled kernel covers (dk, C, dtype).
 hipError_t launch_prefill(const PrefillArgs& a);
 bool prefill_supported(int dk, int dv, int C, bool bf16);

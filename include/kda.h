@@ -293,6 +293,57 @@ kda_status kda_decode_step_backward(const void* q, const void* k, const void* v,
                                     void* dv, float* dalpha, float* dbeta, float* dS, int N,
                                     int H, int dk_, int dv_, kda_dtype dt, void* stream);
 
+/*
+ * kda_prefill_backward_workspace_bytes — device workspace, in bytes, that
+ * kda_prefill_backward needs for these sizes: the state of every sequence
+ * and head stored once every 16 tokens, B * H * ceil(T / 16) * dk * dv *
+ * 4 bytes (256 MiB at B = 1, T = 4096, H = 16, dk = dv = 128).
+ * (size_t)-1 for sizes the call does not accept.
+ */
+size_t kda_prefill_backward_workspace_bytes(int B, int T, int H, int dk, int dv);
+
+/*
+ * kda_prefill_backward — the gradients of a loss L through a whole
+ * kda_prefill_chunked call: given dL/do for every token and dL/dS_T for
+ * the final state, the gradients with respect to q, k, v, alpha, beta and
+ * the initial state.  It is kda_decode_step_backward applied from the last
+ * token to the first, each time at the state before that token, with the
+ * state gradient carried from token to token (the chain rule of the
+ * recurrence of "From GPT-2 to Kimi K3, Explained", sections "DeltaNet
+ * (Fast Weight Programmers)" and "KDA/Kimi Linear").  The states are
+ * recomputed from S0: one forward pass stores them every 16 tokens in the
+ * workspace, and each 16-token piece is run forward again before its
+ * backward.
+ *
+ *   q, k, v, alpha, beta, S0   the prefill's inputs, as kda_prefill_chunked
+ *                              (S0 may be NULL: zeros)
+ *   dO      [B, T, H, dv]  dt       dL/do
+ *   dS_T    [B, H, dk, dv] float32  dL/dS_T, or NULL (zeros)
+ *   dq, dk  [B, T, H, dk]  float32  written
+ *   dv      [B, T, H, dv]  float32  written
+ *   dalpha  [B, T, H, dk]  float32  written
+ *   dbeta   [B, T, H]      float32  written
+ *   dS0     [B, H, dk, dv] float32  dL/dS0, written unless NULL; may be
+ *                                   equal to dS_T (in place) but may not
+ *                                   overlap it otherwise
+ *   workspace, workspace_bytes      at least
+ *                                   kda_prefill_backward_workspace_bytes
+ *
+ * Gradients are float32 whatever dt is; dq, dk, dalpha and dbeta are sums
+ * over value-column slabs taken with float atomics, so their last bits may
+ * differ from run to run.  T = 0 writes dS0 = dS_T (or zeros).  No output
+ * or the workspace may overlap an input or another output (dS0 == dS_T
+ * aside).  Errors: KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_UNSUPPORTED,
+ * KDA_ERR_ALIGN, KDA_ERR_ALIAS, KDA_ERR_WORKSPACE, KDA_ERR_DEVICE,
+ * KDA_ERR_HIP.
+ */
+kda_status kda_prefill_backward(const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta, const float* S0,
+                                const void* dO, const float* dS_T, float* dq, float* dk,
+                                float* dv, float* dalpha, float* dbeta, float* dS0, int B,
+                                int T, int H, int dk_, int dv_, kda_dtype dt, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* kda_status_string — static, human-readable text for a status code. */
 const char* kda_status_string(kda_status s);
 

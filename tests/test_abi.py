@@ -25,10 +25,11 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_nine_calls():
+def test_header_declares_the_eleven_calls():
     assert declared_functions() == ["kda_decode_step", "kda_decode_step_backward",
                                     "kda_decode_step_logits",
                                     "kda_gdn_decode_step", "kda_gdn_prefill_chunked",
+                                    "kda_prefill_backward", "kda_prefill_backward_workspace_bytes",
                                     "kda_prefill_chunked", "kda_prefill_chunked_logits",
                                     "kda_prefill_workspace_bytes", "kda_status_string"]
 
@@ -280,3 +281,52 @@ def test_step_backward_validation():
     assert bw(da=addr(11) + 4) == L.KDA_ERR_ALIGN
     assert bw(N=0) == L.KDA_ERR_SHAPE
     assert bw(dk_=24) == L.KDA_ERR_UNSUPPORTED
+
+
+def test_prefill_backward_workspace_bytes():
+    L = _lib()
+    lib = L.load()
+    assert lib.kda_prefill_backward_workspace_bytes(1, 4096, 16, 128, 128) == 256 << 20
+    assert lib.kda_prefill_backward_workspace_bytes(2, 17, 3, 64, 32) == 2 * 3 * 2 * 64 * 32 * 4
+    assert lib.kda_prefill_backward_workspace_bytes(1, 0, 1, 16, 16) == 0
+    bad = ctypes.c_size_t(-1).value
+    assert lib.kda_prefill_backward_workspace_bytes(1, 16, 1, 24, 16) == bad
+    assert lib.kda_prefill_backward_workspace_bytes(0, 16, 1, 16, 16) == bad
+
+
+def test_prefill_backward_validation():
+    L = _lib()
+    lib = L.load()
+    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+    B, T, H, d = 1, 64, 2, 128
+    ws_need = lib.kda_prefill_backward_workspace_bytes(B, T, H, d, d)
+
+    def pb(**kw):
+        a = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), S0=addr(5),
+                 dO=addr(6), dST=addr(7), dq=addr(8), dk=addr(9), dv=addr(10), da=addr(11),
+                 db=addr(12), dS0=addr(13), B=B, T=T, H=H, dk_=d, dv_=d, dt=1, ws=addr(14),
+                 wsb=ws_need, stream=None)
+        a.update(kw)
+        return lib.kda_prefill_backward(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"],
+                                        a["dO"], a["dST"], a["dq"], a["dk"], a["dv"], a["da"],
+                                        a["db"], a["dS0"], a["B"], a["T"], a["H"], a["dk_"],
+                                        a["dv_"], a["dt"], a["ws"], a["wsb"], a["stream"])
+
+    assert pb() in ok
+    assert pb(S0=None, dST=None, dS0=None) in ok                 # optional states
+    assert pb(dS0=addr(7)) in ok                                 # in place over dS_T
+    assert pb(dS0=addr(7) + 64) == L.KDA_ERR_ALIAS               # partial overlap with dS_T
+    assert pb(dS0=addr(5)) == L.KDA_ERR_ALIAS                    # over S0
+    assert pb(dq=addr(9)) == L.KDA_ERR_ALIAS                     # two outputs together
+    assert pb(ws=addr(6)) == L.KDA_ERR_ALIAS                     # workspace over dO
+    # dq is B*T*H*dk fp32: an output just past its end is fine, one inside is not
+    dq_end = addr(8) + B * T * H * d * 4
+    assert pb(dk=dq_end) in ok and pb(dk=dq_end - 16) == L.KDA_ERR_ALIAS
+    assert pb(dO=None) == L.KDA_ERR_NULL and pb(db=None) == L.KDA_ERR_NULL
+    assert pb(da=addr(11) + 4) == L.KDA_ERR_ALIGN
+    assert pb(ws=None) == L.KDA_ERR_WORKSPACE and pb(wsb=ws_need - 1) == L.KDA_ERR_WORKSPACE
+    assert pb(T=-1) == L.KDA_ERR_SHAPE and pb(H=0) == L.KDA_ERR_SHAPE
+    assert pb(dk_=24) == L.KDA_ERR_UNSUPPORTED and pb(dt=7) == L.KDA_ERR_UNSUPPORTED
+    # no tokens: only the state gradient is passed through, the rest may be NULL
+    assert pb(T=0, q=None, k=None, v=None, alpha=None, beta=None, dO=None, dq=None, dk=None,
+              dv=None, da=None, db=None, ws=None, wsb=0) in ok

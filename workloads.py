@@ -217,6 +217,19 @@ def make_gdn_inputs(spec: PrefillSpec, device="cpu", T=None, B=None, H=None, gat
     return dict(q=d["q"], k=d["k"], v=d["v"], a=a, beta=d["beta"], S0=d["S0"])
 
 
+def make_prefill_backward_grads(spec: PrefillSpec, device="cpu", T=None, B=None, H=None,
+                                with_dST=True):
+    """Incoming gradients for a prefill backward: dO [B,T,H,dv] in spec.dtype
+    and dS_T [B,H,dk,dv] fp32 (None if with_dST is False), standard normal."""
+    B = spec.B if B is None else B
+    H = spec.H if H is None else H
+    T = spec.T if T is None else T
+    g = _gen(device, spec.seed + 2000)
+    dO = torch.randn(B, T, H, spec.dv, generator=g, device=device).to(spec.dtype)
+    dST = torch.randn(B, H, spec.dk, spec.dv, generator=g, device=device) if with_dST else None
+    return dict(dO=dO.contiguous(), dS_T=None if dST is None else dST.float().contiguous())
+
+
 def make_decode_state(spec: DecodeSpec, device="cpu", N=None):
     N = spec.N if N is None else N
     g = _gen(device, spec.seed)
