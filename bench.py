@@ -81,6 +81,15 @@ def decode_bwd_alg_bytes(N, H, dk, dv, esize):
     return N * H * per_head
 
 
+def prefill_bwd_alg_bytes(B, T, H, dk, dv, esize):
+    """Prefill backward: the forward inputs (q, k, v, alpha, beta) and dO read
+    once, the gradients (dq, dk, dv, dalpha fp32, dbeta) written once, and
+    dS_T read and dS0 written per head; the stored states (dk dv / 16 floats
+    per token-head, written and read back) are the method's own traffic."""
+    per_tok = esize * (2 * dk + dv) + 4 * dk + 4 + esize * dv + 4 * (3 * dk + dv) + 4
+    return B * T * H * per_tok + 2 * B * H * dk * dv * 4
+
+
 def _code_only(text):
     """C++ source without comments and with whitespace runs collapsed, so that
     editing a comment does not count as changing a kernel."""
@@ -214,7 +223,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="headline prefill only (no decode / large prefill lines)")
     ap.add_argument("--only", choices=["prefill", "decode", "large", "logits", "decode_logits",
-                                       "gdn", "decode_gdn", "longctx", "decode_bwd", "copy"],
+                                       "gdn", "decode_gdn", "longctx", "decode_bwd", "prefill_bwd",
+                                       "copy"],
                     default=None,
                     help="run one leg only (for profiler runs); 'copy' times a plain "
                          "1 GiB device-to-device copy used to calibrate HBM byte counters")
@@ -241,7 +251,7 @@ def main():
                           "ms_per_copy": ms, "GBps": 8 * n / (ms * 1e-3) / 1e9}), flush=True)
         return
     legs = ({"prefill", "decode", "large", "logits", "decode_logits", "gdn", "decode_gdn",
-             "longctx", "decode_bwd"} if args.only is None else {args.only})
+             "longctx", "decode_bwd", "prefill_bwd"} if args.only is None else {args.only})
     if args.no_extra:
         legs = {"prefill"}
 
@@ -496,6 +506,31 @@ def extras(args, legs, out, torch, kda, wl, dev):
         print(f"# decode_bwd_n256_h32: {ms_b * 1e3:.1f} us/step, "
               f"{out['decode_bwd_n256_h32']['alg_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
         del S, gS, st, dO
+        torch.cuda.empty_cache()
+
+    if "prefill_bwd" in legs:
+        # ---------------- prefill backward on the headline workload
+        pspec = wl.PREFILL["prefill_h16_t4k"]
+        px = wl.make_prefill_inputs(pspec, dev)
+        pg = wl.make_prefill_backward_grads(pspec, dev)
+
+        def pbstep():
+            kda.prefill_backward(px["q"], px["k"], px["v"], px["alpha"], px["beta"], pg["dO"],
+                                 S0=px["S0"], dS_T=pg["dS_T"])
+
+        ms_p, _ = time_launches(pbstep, 5, 1, torch)
+        B, T, H, dk, dv = pspec.B, pspec.T, pspec.H, pspec.dk, pspec.dv
+        pbytes = prefill_bwd_alg_bytes(B, T, H, dk, dv, 2)
+        out["prefill_bwd_h16_t4k"] = {
+            "ms_per_call": ms_p, "tokens_per_s": B * T / (ms_p * 1e-3),
+            "alg_GBps": pbytes / (ms_p * 1e-3) / 1e9,
+            "frac_hbm": pbytes / (ms_p * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "alg_bytes_per_call": pbytes,
+            "note": "token-sequential walk per (head, 8-column slab): bound by the per-token "
+                    "dependency chain, not by HBM; the chunked adjoint is the next step",
+        }
+        print(f"# prefill_bwd_h16_t4k: {ms_p:.3f} ms/call", file=sys.stderr, flush=True)
+        del px, pg
         torch.cuda.empty_cache()
 
     if "longctx" in legs:

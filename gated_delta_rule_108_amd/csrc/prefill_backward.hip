@@ -14,35 +14,49 @@
 //   over j:              dbeta = sum_j du_j (v_j - r_j)
 //
 // Every value column of S (and of dS) evolves on its own in both directions;
-// only the row sums and dbeta mix columns.  So one wave owns a slab of 8
-// value columns of one (sequence, head) for the whole sequence: lane
-// (rg = lane / 8, j = lane % 8) holds rows rg, rg + 8, ... of column j in
-// registers.  Column sums (r, du) are an in-lane sum plus three exchanges
-// across the 8 row-group lanes; row sums of the three per-row quantities are
-// one transposed butterfly over the 8 column lanes (each exchange halves the
-// values a lane holds), after which every lane adds its share to the fp32
-// gradient rows with hardware float atomics (the slabs of a head add into the
-// same rows).
+// only the row sums and dbeta mix columns.  A workgroup of four waves (one
+// per SIMD) owns WGC value columns of one (sequence, head) for the whole
+// sequence; each wave holds CPW of them (2, or 4 at dk = 16): lane
+// (rg = lane / CPW, j = lane % CPW) keeps rows rg, rg + RG, ... of its column
+// in registers.  Column sums (r, du) are an in-lane sum plus exchanges across
+// the RG row-group lanes; the row sums of the three per-row quantities are a
+// transposed butterfly over the CPW column lanes, then LDS float atomics into
+// the workgroup's per-piece row buffer, which is added to the fp32 gradient
+// rows once per piece with coalesced global float atomics (the workgroups of a
+// head add into the same rows).
 //
 // The backward needs the state before every token.  Kernel 1 runs the
-// recurrence forward and stores the slab's state every kCk tokens into the
+// recurrence forward and stores the state every kCk tokens into the
 // workspace; kernel 2 walks those pieces from the last to the first: it
 // restores the piece's first state, runs the kCk tokens forward again keeping
 // each state in LDS, then runs them backward.  Per piece the token rows (k,
-// alpha, q; v and dO of the slab; beta) are staged into LDS with 16-byte
-// loads issued one piece ahead.
+// alpha, q; v and dO of the workgroup's columns; beta) are staged into LDS,
+// shared by the four waves, with 16-byte loads issued one piece ahead.
 //
-// The work is sequential in tokens (a latency-bound walk per wave, about
-// 2 dk dv flops of VALU per element per token), unlike the chunked forward:
-// the chunk form of the adjoint, on the matrix cores, is the next step.
+// The work is sequential in tokens (a latency-bound walk, about 2 dk dv
+// flops of VALU per element per token), unlike the chunked forward: the chunk
+// form of the adjoint, on the matrix cores, is the next step.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
 namespace {
 
-constexpr int kSlab = 8;    // value columns per wave
+constexpr int kWaves = 4;   // waves per workgroup, one per SIMD
+constexpr int kThreads = kWaves * kWave;
 constexpr int kCk = 16;     // tokens between stored states
+
+template <int DK>
+struct Geo {
+  static constexpr int CPW = DK >= 32 ? 2 : kWave / DK;   // value columns per wave
+  static constexpr int RG = kWave / CPW;                   // row groups per wave
+  static constexpr int RPT = DK / RG;                      // key rows per lane
+  static constexpr int WGC = kWaves * CPW;                 // value columns per workgroup
+  static constexpr int NV = 3 * RPT;                       // (dq, dk, dalpha) per row
+  static constexpr int VP = (NV + CPW - 1) / CPW * CPW;    // padded for the butterfly
+  static constexpr int PER = VP / CPW;                     // values per lane after it
+  static_assert(RPT >= 1 && RG * RPT == DK, "rows must split evenly");
+};
 
 // Element x of a 16-byte word of IO values, as float.
 template <typename IO> struct Word;
@@ -62,76 +76,98 @@ template <> struct Word<bf16_t> {
 };
 
 // LDS position of key row c in a staged row vector: the RPT rows of row
-// group c % 8 sit together, so a lane reads its rows contiguously.
+// group c % RG sit together, so a lane reads its rows contiguously.
 template <int DK>
-__device__ __forceinline__ int kpos(int c) { return (c % kSlab) * (DK / kSlab) + c / kSlab; }
+__device__ __forceinline__ int kpos(int c) {
+  return (c % Geo<DK>::RG) * Geo<DK>::RPT + c / Geo<DK>::RG;
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-template <int PATTERN>
-__device__ __forceinline__ float swz(float v) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), PATTERN));
+// Value of lane (lane xor X), X = 1 or 2: quad_perm moves.
+template <int X>
+__device__ __forceinline__ float xr(float v) {
+  static_assert(X == 1 || X == 2, "column lanes sit within a quad");
+  return X == 1 ? dpp<0xB1>(v) : dpp<0x4E>(v);
 }
-// Lane exchanges.  xor 1 and 2: quad_perm; xor 8: row_ror:8 (within a row
-// of 16 lanes, rotating by 8 is xor 8); xor 4 and 16: ds_swizzle in bit mode
-// (and-mask 31, xor-mask 4 or 16); xor 32: the lane crossbar.
-__device__ __forceinline__ float xor1(float v) { return dpp<0xB1>(v); }
-__device__ __forceinline__ float xor2(float v) { return dpp<0x4E>(v); }
-__device__ __forceinline__ float xor4(float v) { return swz<(4 << 10) | 0x1F>(v); }
-__device__ __forceinline__ float xor8(float v) { return dpp<0x128>(v); }
-__device__ __forceinline__ float xor16(float v) { return swz<(16 << 10) | 0x1F>(v); }
 
-// Sum over the 8 row-group lanes of a column (lane bits 3..5), to all of them.
+// Sum over the row-group lanes of a column (the lanes equal to it modulo
+// CPW), to all of them, on the VALU only: within each 16-lane row, adding
+// the row rotated by CPW, 2 CPW, ... 8 sums the lanes of the same residue;
+// permlane16_swap then pairs rows 0-1 and 2-3 and permlane32_swap the two
+// halves of the wave (each swap exchanges the rows of two copies of x, so
+// the sum of the two results is the sum over both rows).
+template <int X>
+__device__ __forceinline__ float ror_sum(float x) {
+  if constexpr (X < 16) return ror_sum<2 * X>(x + dpp<0x120 + X>(x));
+  else return x;
+}
+template <int CPW>
 __device__ __forceinline__ float col_sum(float x) {
-  x += xor8(x);
-  x += xor16(x);
-  x += __shfl_xor(x, 32);
-  return x;
+  x = ror_sum<CPW>(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
-// Sum over the 8 column lanes of a row group (lane bits 0..2), to all of them.
+
+// Sum over the CPW column lanes of a row group (lane bits below CPW), to all.
+template <int CPW>
 __device__ __forceinline__ float row_sum(float x) {
-  x += xor1(x);
-  x += xor2(x);
-  x += xor4(x);
+  x += xr<1>(x);
+  if constexpr (CPW == 4) x += xr<2>(x);
   return x;
 }
 
-// One halving step of the transposed butterfly: of the first 2n values, the
-// lane keeps the half its bit selects, summed with the partner's copy of it.
-template <int N, class X>
-__device__ __forceinline__ void halve(float* a, bool hi, X exch) {
+// Transposed butterfly over the CPW column lanes: each step keeps the half of
+// the values that the lane's bit X selects, summed with the partner's copy of
+// it.  Afterwards lane j holds the sums of values j * PER .. j * PER + PER - 1.
+template <int N, int X>
+__device__ __forceinline__ void halve(float* a, bool hi) {
 #pragma unroll
   for (int m = 0; m < N; ++m) {
     const float keep = hi ? a[m + N] : a[m];
     const float send = hi ? a[m] : a[m + N];
-    a[m] = keep + exch(send);
+    a[m] = keep + xr<X>(send);
+  }
+}
+template <int CPW, int VP>
+__device__ __forceinline__ void butterfly(float* a, int lane) {
+  if constexpr (CPW == 4) {
+    halve<VP / 2, 2>(a, (lane & 2) != 0);
+    halve<VP / 4, 1>(a, (lane & 1) != 0);
+  } else {
+    halve<VP / 2, 1>(a, (lane & 1) != 0);
   }
 }
 
-// Token rows of one piece of kCk tokens, loaded into registers (one piece
-// ahead) and then stored to LDS as float.
+// Token rows of one piece of kCk tokens for the whole workgroup, loaded into
+// registers (one piece ahead) and then stored to LDS as float.
 template <typename IO, int DK, bool kBwd>
 struct Stage {
   using E = typename Ty<IO>::Elem;
   static constexpr int VEC = Word<IO>::kVec;
-  static constexpr int NRI = (kCk * DK + kWave * VEC - 1) / (kWave * VEC);   // k, q words
-  static constexpr int NRA = (kCk * DK + kWave * 4 - 1) / (kWave * 4);       // alpha float4s
-  static constexpr int NCV = kCk / kSlab;                                      // v, dO per lane
+  static constexpr int WGC = Geo<DK>::WGC;
+  static constexpr int NRI = (kCk * DK + kThreads * VEC - 1) / (kThreads * VEC);  // k, q words
+  static constexpr int NRA = (kCk * DK + kThreads * 4 - 1) / (kThreads * 4);      // alpha float4s
+  static_assert(kCk * WGC <= kThreads, "one thread per (token, column)");
   uint4 kr[NRI];
   uint4 qr[kBwd ? NRI : 1];
   float4 ar[NRA];
-  float vc[NCV], oc[kBwd ? NCV : 1];
-  float bb;
+  float vc, oc, bb;
+  float sc[kBwd ? Geo<DK>::RPT : 1];   // the piece's first state, this lane's rows
 
-  // Tokens t0 .. t0 + n - 1 of chain (b, h); row offsets in elements.
+  // Tokens of rows tok0, tok0 + H, ... (n of them); columns col0 .. col0 + WGC - 1.
   __device__ __forceinline__ void load(const E* k, const E* q, const float* alpha, const E* v,
                                        const E* dO, const float* beta, size_t tok0, int H,
-                                       int DV, int n, int col, int lane) {
+                                       int DV, int n, int col0, int tid) {
 #pragma unroll
     for (int it = 0; it < NRI; ++it) {
-      const int e = (it * kWave + lane) * VEC, s = e / DK, c = e % DK;
+      const int e = (it * kThreads + tid) * VEC, s = e / DK, c = e % DK;
       const bool ok = e < kCk * DK && s < n;
       const size_t off = (tok0 + static_cast<size_t>(s) * H) * DK + c;
       kr[it] = ok ? *reinterpret_cast<const uint4*>(k + off) : make_uint4(0, 0, 0, 0);
@@ -140,27 +176,31 @@ struct Stage {
     }
 #pragma unroll
     for (int it = 0; it < NRA; ++it) {
-      const int e = (it * kWave + lane) * 4, s = e / DK, c = e % DK;
+      const int e = (it * kThreads + tid) * 4, s = e / DK, c = e % DK;
       const bool ok = e < kCk * DK && s < n;
       const size_t off = (tok0 + static_cast<size_t>(s) * H) * DK + c;
       ar[it] = ok ? *reinterpret_cast<const float4*>(alpha + off) : make_float4(0, 0, 0, 0);
     }
-#pragma unroll
-    for (int m = 0; m < NCV; ++m) {
-      const int s = lane / kSlab + kSlab * m;
-      const bool ok = s < n;
-      const size_t off = (tok0 + static_cast<size_t>(s) * H) * DV + col;
-      vc[m] = ok ? Ty<IO>::to_f32(v[off]) : 0.f;
-      if constexpr (kBwd) oc[m] = ok ? Ty<IO>::to_f32(dO[off]) : 0.f;
+    {
+      const int s = tid / WGC, cc = tid % WGC;
+      const bool ok = tid < kCk * WGC && s < n;
+      const size_t off = (tok0 + static_cast<size_t>(s) * H) * DV + col0 + cc;
+      vc = ok ? Ty<IO>::to_f32(v[off]) : 0.f;
+      if constexpr (kBwd) oc = ok ? Ty<IO>::to_f32(dO[off]) : 0.f;
     }
-    bb = (lane < kCk && lane < n) ? beta[tok0 + static_cast<size_t>(lane) * H] : 0.f;
+    bb = (tid < kCk && tid < n) ? beta[tok0 + static_cast<size_t>(tid) * H] : 0.f;
+  }
+  // The piece's stored state (backward only), this lane's RPT values.
+  __device__ __forceinline__ void load_state(const float* in, int lane) {
+#pragma unroll
+    for (int i = 0; i < Geo<DK>::RPT; ++i) sc[i] = in[i * kWave + lane];
   }
 
   __device__ __forceinline__ void store(float* kS, float* qS, float* aS, float* vS, float* oS,
-                                        float* bS, int lane) const {
+                                        float* bS, int tid) const {
 #pragma unroll
     for (int it = 0; it < NRI; ++it) {
-      const int e = (it * kWave + lane) * VEC, s = e / DK, c = e % DK;
+      const int e = (it * kThreads + tid) * VEC, s = e / DK, c = e % DK;
       if (e < kCk * DK) {
 #pragma unroll
         for (int x = 0; x < VEC; ++x) {
@@ -171,7 +211,7 @@ struct Stage {
     }
 #pragma unroll
     for (int it = 0; it < NRA; ++it) {
-      const int e = (it * kWave + lane) * 4, s = e / DK, c = e % DK;
+      const int e = (it * kThreads + tid) * 4, s = e / DK, c = e % DK;
       if (e < kCk * DK) {
         aS[s * DK + kpos<DK>(c + 0)] = ar[it].x;
         aS[s * DK + kpos<DK>(c + 1)] = ar[it].y;
@@ -179,27 +219,26 @@ struct Stage {
         aS[s * DK + kpos<DK>(c + 3)] = ar[it].w;
       }
     }
-#pragma unroll
-    for (int m = 0; m < NCV; ++m) {
-      const int s = lane / kSlab + kSlab * m, j = lane % kSlab;
-      vS[s * kSlab + j] = vc[m];
-      if constexpr (kBwd) oS[s * kSlab + j] = oc[m];
+    if (tid < kCk * WGC) {
+      vS[tid] = vc;   // [token][column]
+      if constexpr (kBwd) oS[tid] = oc;
     }
-    if (lane < kCk) bS[lane] = bb;
+    if (tid < kCk) bS[tid] = bb;
   }
 };
 
-// One forward token on the lane's rows of column j.  Returns r_j; u_j in *u.
-template <int RPT>
+// One forward token on the lane's rows of its column.  Returns r; u in *u.
+template <int DK>
 __device__ __forceinline__ float fwd_token(float* S, const float* kr, const float* ar, float vj,
                                            float bt, float* u) {
+  constexpr int RPT = Geo<DK>::RPT;
   float sp[RPT], acc = 0.f;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     sp[i] = ar[i] * S[i];
     acc += kr[i] * sp[i];
   }
-  const float r = col_sum(acc);
+  const float r = col_sum<Geo<DK>::CPW>(acc);
   const float uj = bt * (vj - r);
 #pragma unroll
   for (int i = 0; i < RPT; ++i) S[i] = sp[i] + kr[i] * uj;
@@ -207,57 +246,70 @@ __device__ __forceinline__ float fwd_token(float* S, const float* kr, const floa
   return r;
 }
 
-// Stored state layout: [chain][piece][slab][RPT][64 lanes] floats.
-__device__ __forceinline__ size_t ck_off(size_t chain, int piece, int npiece, int slab, int NS,
-                                         int DK) {
-  return ((chain * npiece + piece) * NS + slab) * static_cast<size_t>(DK) * kSlab;
+// Stored state layout: [chain][piece][workgroup][wave][RPT][64 lanes] floats
+// (DK x WGC floats per workgroup and piece).
+__device__ __forceinline__ size_t ck_off(size_t chain, int piece, int npiece, int wg, int NWG,
+                                         int block) {
+  return ((chain * npiece + piece) * NWG + wg) * static_cast<size_t>(block);
 }
 
 template <typename IO, int DK>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(kThreads)
 kda_pb_forward_kernel(const typename Ty<IO>::Elem* __restrict__ k,
                       const typename Ty<IO>::Elem* __restrict__ v,
                       const float* __restrict__ alpha, const float* __restrict__ beta,
                       const float* __restrict__ S0, float* __restrict__ ck, int T, int H,
                       int DV) {
-  constexpr int RPT = DK / kSlab;
-  const int NS = DV / kSlab;
-  const int chain = blockIdx.x / NS, slab = blockIdx.x % NS;
+  using G = Geo<DK>;
+  constexpr int RPT = G::RPT, CPW = G::CPW, RG = G::RG, WGC = G::WGC;
+  const int NWG = DV / WGC;
+  const int chain = blockIdx.x / NWG, wg = blockIdx.x % NWG;
   const int b = chain / H, h = chain % H;
-  const int lane = threadIdx.x, j = lane % kSlab, rg = lane / kSlab;
-  const int col = slab * kSlab + j;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int j = lane % CPW, rg = lane / CPW, cw = wave * CPW + j;
+  const int col = wg * WGC + cw;
   const int npiece = (T + kCk - 1) / kCk;
 
-  __shared__ float kS[kCk * DK], aS[kCk * DK], vS[kCk * kSlab], bS[kCk];
+  __shared__ float kS[kCk * DK], aS[kCk * DK], vS[kCk * WGC], bS[kCk];
+  __shared__ float s0[kWaves * RPT * kWave];
+  // The initial state goes through LDS: values that enter the token loop
+  // straight from a global load make the compiler wait for every vector
+  // memory operation (stores included) in each iteration.
   float S[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
-    S[i] = S0 ? S0[(static_cast<size_t>(chain) * DK + rg + kSlab * i) * DV + col] : 0.f;
+    s0[(wave * RPT + i) * kWave + lane] =
+        S0 ? S0[(static_cast<size_t>(chain) * DK + rg + RG * i) * DV + col] : 0.f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) S[i] = s0[(wave * RPT + i) * kWave + lane];
 
   Stage<IO, DK, false> st;
-  auto tok0 = [&](int p) { return static_cast<size_t>(b) * T * H + static_cast<size_t>(p) * kCk * H + h; };
+  auto tok0 = [&](int p) {
+    return static_cast<size_t>(b) * T * H + static_cast<size_t>(p) * kCk * H + h;
+  };
   auto count = [&](int p) { return min(kCk, T - p * kCk); };
-  st.load(k, nullptr, alpha, v, nullptr, beta, tok0(0), H, DV, count(0), col, lane);
+  st.load(k, nullptr, alpha, v, nullptr, beta, tok0(0), H, DV, count(0), wg * WGC, tid);
   for (int p = 0; p < npiece; ++p) {
-    st.store(kS, nullptr, aS, vS, nullptr, bS, lane);
+    st.store(kS, nullptr, aS, vS, nullptr, bS, tid);
     __syncthreads();
     if (p + 1 < npiece)
-      st.load(k, nullptr, alpha, v, nullptr, beta, tok0(p + 1), H, DV, count(p + 1), col, lane);
-    float* out = ck + ck_off(chain, p, npiece, slab, NS, DK);
+      st.load(k, nullptr, alpha, v, nullptr, beta, tok0(p + 1), H, DV, count(p + 1), wg * WGC,
+              tid);
+    float* out = ck + ck_off(chain, p, npiece, wg, NWG, DK * WGC) + wave * RPT * kWave;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) out[i * kWave + lane] = S[i];
     const int n = count(p);
     for (int s = 0; s < n; ++s) {
       float u;
-      fwd_token<RPT>(S, kS + s * DK + rg * RPT, aS + s * DK + rg * RPT, vS[s * kSlab + j], bS[s],
-                     &u);
+      fwd_token<DK>(S, kS + s * DK + rg * RPT, aS + s * DK + rg * RPT, vS[s * WGC + cw], bS[s],
+                    &u);
     }
     __syncthreads();
   }
 }
 
 template <typename IO, int DK>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(kThreads)
 kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
                        const typename Ty<IO>::Elem* __restrict__ k,
                        const typename Ty<IO>::Elem* __restrict__ v,
@@ -268,50 +320,73 @@ kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
                        float* __restrict__ g_v, float* __restrict__ g_alpha,
                        float* __restrict__ g_beta, float* __restrict__ g_S0, int T, int H,
                        int DV) {
-  constexpr int RPT = DK / kSlab;
-  constexpr int NV = 3 * RPT;                     // (dq, dk, dalpha) per row
-  constexpr int VP = (NV + kSlab - 1) / kSlab * kSlab;
-  constexpr int PER = VP / kSlab;                 // values per lane after the butterfly
-  const int NS = DV / kSlab;
-  const int chain = blockIdx.x / NS, slab = blockIdx.x % NS;
+  using G = Geo<DK>;
+  constexpr int RPT = G::RPT, CPW = G::CPW, RG = G::RG, WGC = G::WGC;
+  constexpr int NV = G::NV, VP = G::VP, PER = G::PER;
+  const int NWG = DV / WGC;
+  const int chain = blockIdx.x / NWG, wg = blockIdx.x % NWG;
   const int b = chain / H, h = chain % H;
-  const int lane = threadIdx.x, j = lane % kSlab, rg = lane / kSlab;
-  const int col = slab * kSlab + j;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int j = lane % CPW, rg = lane / CPW, cw = wave * CPW + j;
+  const int col = wg * WGC + cw;
   const int npiece = (T + kCk - 1) / kCk;
 
   __shared__ float kS[kCk * DK], qS[kCk * DK], aS[kCk * DK];
-  __shared__ float vS[kCk * kSlab], oS[kCk * kSlab], uS[kCk * kSlab], rS[kCk * kSlab], bS[kCk];
-  __shared__ float hist[kCk * RPT * kWave];     // state before each token of the piece
+  __shared__ float vS[kCk * WGC], oS[kCk * WGC], uS[kCk * WGC], rS[kCk * WGC], bS[kCk];
+  __shared__ float hist[kWaves * kCk * RPT * kWave];   // state before each token, per wave
+  __shared__ float part[kCk * 3 * DK];                 // row sums: [token][dq, dk, dalpha][row]
+  __shared__ float partb[kWaves][kCk];                 // dbeta, per wave
+  for (int x = tid; x < kCk * 3 * DK; x += kThreads) part[x] = 0.f;
+  float* myhist = hist + wave * kCk * RPT * kWave;
 
+  // The incoming state gradient and each piece's first state go through LDS:
+  // values that enter a token loop straight from a global load make the
+  // compiler wait for every vector memory operation (the dv stores included)
+  // in each iteration.
   float dS[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
-    dS[i] = dS_T ? dS_T[(static_cast<size_t>(chain) * DK + rg + kSlab * i) * DV + col] : 0.f;
+    myhist[i * kWave + lane] =
+        dS_T ? dS_T[(static_cast<size_t>(chain) * DK + rg + RG * i) * DV + col] : 0.f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) dS[i] = myhist[i * kWave + lane];
 
   Stage<IO, DK, true> st;
-  auto tok0 = [&](int p) { return static_cast<size_t>(b) * T * H + static_cast<size_t>(p) * kCk * H + h; };
+  auto tok0 = [&](int p) {
+    return static_cast<size_t>(b) * T * H + static_cast<size_t>(p) * kCk * H + h;
+  };
   auto count = [&](int p) { return min(kCk, T - p * kCk); };
-  if (npiece > 0)
-    st.load(k, q, alpha, v, dO, beta, tok0(npiece - 1), H, DV, count(npiece - 1), col, lane);
+  auto state_at = [&](int p) {
+    return ck + ck_off(chain, p, npiece, wg, NWG, DK * WGC) + wave * RPT * kWave;
+  };
+  if (npiece > 0) {
+    st.load(k, q, alpha, v, dO, beta, tok0(npiece - 1), H, DV, count(npiece - 1), wg * WGC, tid);
+    st.load_state(state_at(npiece - 1), lane);
+  }
   for (int p = npiece - 1; p >= 0; --p) {
-    st.store(kS, qS, aS, vS, oS, bS, lane);
+    st.store(kS, qS, aS, vS, oS, bS, tid);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) myhist[i * kWave + lane] = st.sc[i];
+    if (tid < kWaves * kCk) partb[tid / kCk][tid % kCk] = 0.f;
     __syncthreads();
-    if (p > 0) st.load(k, q, alpha, v, dO, beta, tok0(p - 1), H, DV, count(p - 1), col, lane);
+    if (p > 0) {
+      st.load(k, q, alpha, v, dO, beta, tok0(p - 1), H, DV, count(p - 1), wg * WGC, tid);
+      st.load_state(state_at(p - 1), lane);
+    }
     const int n = count(p);
     float S[RPT];
-    const float* in = ck + ck_off(chain, p, npiece, slab, NS, DK);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) S[i] = in[i * kWave + lane];
+    for (int i = 0; i < RPT; ++i) S[i] = myhist[i * kWave + lane];
     // forward again over the piece, keeping the state before each token
     for (int s = 0; s < n; ++s) {
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) hist[(s * RPT + i) * kWave + lane] = S[i];
+      for (int i = 0; i < RPT; ++i) myhist[(s * RPT + i) * kWave + lane] = S[i];
       float u;
-      const float r = fwd_token<RPT>(S, kS + s * DK + rg * RPT, aS + s * DK + rg * RPT,
-                                     vS[s * kSlab + j], bS[s], &u);
+      const float r = fwd_token<DK>(S, kS + s * DK + rg * RPT, aS + s * DK + rg * RPT,
+                                    vS[s * WGC + cw], bS[s], &u);
       if (rg == 0) {
-        uS[s * kSlab + j] = u;
-        rS[s * kSlab + j] = r;
+        uS[s * WGC + cw] = u;
+        rS[s * WGC + cw] = r;
       }
     }
     __syncthreads();
@@ -320,54 +395,75 @@ kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
       const float* kr = kS + s * DK + rg * RPT;
       const float* qr = qS + s * DK + rg * RPT;
       const float* ar = aS + s * DK + rg * RPT;
-      const float uj = uS[s * kSlab + j], rj = rS[s * kSlab + j];
-      const float vj = vS[s * kSlab + j], oj = oS[s * kSlab + j], bt = bS[s];
-      float Sb[RPT], G[RPT], acc = 0.f;
+      const float uj = uS[s * WGC + cw], rj = rS[s * WGC + cw];
+      const float vj = vS[s * WGC + cw], oj = oS[s * WGC + cw], bt = bS[s];
+      float Sb[RPT], Gm[RPT], acc = 0.f;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        Sb[i] = hist[(s * RPT + i) * kWave + lane];
-        G[i] = dS[i] + qr[i] * oj;
-        acc += kr[i] * G[i];
+        Sb[i] = myhist[(s * RPT + i) * kWave + lane];
+        Gm[i] = dS[i] + qr[i] * oj;
+        acc += kr[i] * Gm[i];
       }
-      const float du = col_sum(acc);
+      const float du = col_sum<CPW>(acc);
       const size_t row = tok0(p) + static_cast<size_t>(s) * H;   // (b, t, h)
       if (rg == 0) g_v[row * DV + col] = bt * du;
-      const float pb = row_sum(du * (vj - rj));
-      if (lane == 0) unsafeAtomicAdd(g_beta + row, pb);
+      const float pb = row_sum<CPW>(du * (vj - rj));
+      if (lane == 0) partb[wave][s] = pb;
       const float dr = -bt * du;
       float val[VP];
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         const float sp = ar[i] * Sb[i];
         const float sn = sp + kr[i] * uj;
-        const float dsp = G[i] + kr[i] * dr;
-        val[3 * i + 0] = sn * oj;                 // dq
-        val[3 * i + 1] = G[i] * uj + sp * dr;     // dk
-        val[3 * i + 2] = dsp * Sb[i];             // dalpha
+        const float dsp = Gm[i] + kr[i] * dr;
+        val[3 * i + 0] = sn * oj;                  // dq
+        val[3 * i + 1] = Gm[i] * uj + sp * dr;     // dk
+        val[3 * i + 2] = dsp * Sb[i];              // dalpha
         dS[i] = ar[i] * dsp;
       }
 #pragma unroll
       for (int m = NV; m < VP; ++m) val[m] = 0.f;
-      halve<VP / 2>(val, (lane & 4) != 0, xor4);
-      halve<VP / 4>(val, (lane & 2) != 0, xor2);
-      halve<VP / 8>(val, (lane & 1) != 0, xor1);
-      // lane j now holds the sums of values j * PER .. j * PER + PER - 1
+      butterfly<CPW, VP>(val, lane);
 #pragma unroll
       for (int w = 0; w < PER; ++w) {
         const int m = j * PER + w;
         if (m < NV) {
           const int i = m / 3, qn = m % 3;
-          float* dst = qn == 0 ? g_q : (qn == 1 ? g_k : g_alpha);
-          unsafeAtomicAdd(dst + row * DK + rg + kSlab * i, val[w]);
+          atomicAdd(part + (s * 3 + qn) * DK + rg + RG * i, val[w]);
         }
       }
     }
     __syncthreads();
+    // the piece's row sums of this workgroup's columns into the gradient rows:
+    // thread slot x = (quantity, row) adds token s's sum to row tok0 + s H
+    constexpr int NSLOT = 3 * DK;
+#pragma unroll
+    for (int x0 = 0; x0 < NSLOT; x0 += kThreads) {
+      const int x = x0 + tid;
+      if (x < NSLOT) {
+        const int qn = x / DK, c = x % DK;
+        float* dst = (qn == 0 ? g_q : (qn == 1 ? g_k : g_alpha)) + tok0(p) * DK + c;
+        const size_t step = static_cast<size_t>(H) * DK;
+#pragma unroll
+        for (int s = 0; s < kCk; ++s) {
+          if (s < n) {
+            unsafeAtomicAdd(dst + s * step, part[s * NSLOT + x]);
+            part[s * NSLOT + x] = 0.f;
+          }
+        }
+      }
+    }
+    if (tid < n) {
+      float sb = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) sb += partb[w][tid];
+      unsafeAtomicAdd(g_beta + tok0(p) + static_cast<size_t>(tid) * H, sb);
+    }
   }
   if (g_S0) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-      g_S0[(static_cast<size_t>(chain) * DK + rg + kSlab * i) * DV + col] = dS[i];
+      g_S0[(static_cast<size_t>(chain) * DK + rg + RG * i) * DV + col] = dS[i];
   }
 }
 
@@ -386,8 +482,9 @@ __global__ void zero_fill_kernel(float* a, size_t na, float* b, size_t nb, float
 template <typename IO, int DK>
 hipError_t run(const PrefillBwdArgs& a) {
   using E = typename Ty<IO>::Elem;
-  const int NS = a.dv / kSlab;
-  const unsigned grid = static_cast<unsigned>(a.B) * a.H * NS;
+  constexpr int WGC = Geo<DK>::WGC;
+  if (a.dv % WGC != 0) return hipErrorInvalidValue;
+  const unsigned grid = static_cast<unsigned>(a.B) * a.H * (a.dv / WGC);
   const hipStream_t stream = static_cast<hipStream_t>(a.stream);
   if (a.T > 0) {
     const size_t nk = static_cast<size_t>(a.B) * a.T * a.H * a.dk;
@@ -395,13 +492,12 @@ hipError_t run(const PrefillBwdArgs& a) {
     const size_t tot = 3 * nk + nb;
     const size_t zb = (tot + 255) / 256;
     const unsigned zg = static_cast<unsigned>(zb < 4096 ? zb : 4096);
-    zero_fill_kernel<<<zg, 256, 0, stream>>>(a.g_q, nk, a.g_k, nk, a.g_alpha, nk, a.g_beta,
-                                               nb);
-    kda_pb_forward_kernel<IO, DK><<<grid, kWave, 0, stream>>>(
+    zero_fill_kernel<<<zg, 256, 0, stream>>>(a.g_q, nk, a.g_k, nk, a.g_alpha, nk, a.g_beta, nb);
+    kda_pb_forward_kernel<IO, DK><<<grid, kThreads, 0, stream>>>(
         static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.alpha, a.beta, a.S0,
         static_cast<float*>(a.workspace), a.T, a.H, a.dv);
   }
-  kda_pb_backward_kernel<IO, DK><<<grid, kWave, 0, stream>>>(
+  kda_pb_backward_kernel<IO, DK><<<grid, kThreads, 0, stream>>>(
       static_cast<const E*>(a.q), static_cast<const E*>(a.k), static_cast<const E*>(a.v),
       a.alpha, a.beta, static_cast<const E*>(a.dO), a.dS_T,
       static_cast<const float*>(a.workspace), a.g_q, a.g_k, a.g_v, a.g_alpha, a.g_beta, a.g_S0,
@@ -428,7 +524,6 @@ size_t prefill_backward_workspace(int B, int T, int H, int dk, int dv) {
 }
 
 hipError_t launch_prefill_backward(const PrefillBwdArgs& a) {
-  if (a.dv % kSlab != 0) return hipErrorInvalidValue;
   return a.bf16 ? run_dk<bf16_t>(a) : run_dk<float>(a);
 }
 
