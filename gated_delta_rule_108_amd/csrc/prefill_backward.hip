@@ -20,10 +20,10 @@
 // (rg = lane / CPW, j = lane % CPW) keeps rows rg, rg + RG, ... of its column
 // in registers.  Column sums (r, du) are an in-lane sum plus exchanges across
 // the RG row-group lanes; the row sums of the three per-row quantities are a
-// transposed butterfly over the CPW column lanes, then LDS float atomics into
-// the workgroup's per-piece row buffer, which is added to the fp32 gradient
-// rows once per piece with coalesced global float atomics (the workgroups of a
-// head add into the same rows).
+// transposed butterfly over the CPW column lanes, then plain stores into the
+// wave's slots of the workgroup's row buffer; every half piece the four waves'
+// sums are added to the fp32 gradient rows with coalesced global float
+// atomics (the workgroups of a head add into the same rows).
 //
 // The backward needs the state before every token.  Kernel 1 runs the
 // recurrence forward and stores the state every kCk tokens into the
@@ -45,6 +45,7 @@ namespace {
 constexpr int kWaves = 4;   // waves per workgroup, one per SIMD
 constexpr int kThreads = kWaves * kWave;
 constexpr int kCk = 16;     // tokens between stored states
+constexpr int kHalf = kCk / 2;   // tokens per row-sum flush
 
 template <int DK>
 struct Geo {
@@ -334,9 +335,11 @@ kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
   __shared__ float kS[kCk * DK], qS[kCk * DK], aS[kCk * DK];
   __shared__ float vS[kCk * WGC], oS[kCk * WGC], uS[kCk * WGC], rS[kCk * WGC], bS[kCk];
   __shared__ float hist[kWaves * kCk * RPT * kWave];   // state before each token, per wave
-  __shared__ float part[kCk * 3 * DK];                 // row sums: [token][dq, dk, dalpha][row]
+  // Row sums of each wave, for half a piece: [wave][token][dq, dk, dalpha][row].
+  // Plain stores (each slot has one writer); the flush adds the four waves.
+  __shared__ float part[kWaves * kHalf * 3 * DK];
   __shared__ float partb[kWaves][kCk];                 // dbeta, per wave
-  for (int x = tid; x < kCk * 3 * DK; x += kThreads) part[x] = 0.f;
+  float* mypart = part + wave * kHalf * 3 * DK;
   float* myhist = hist + wave * kCk * RPT * kWave;
 
   // The incoming state gradient and each piece's first state go through LDS:
@@ -367,7 +370,6 @@ kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
     st.store(kS, qS, aS, vS, oS, bS, tid);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) myhist[i * kWave + lane] = st.sc[i];
-    if (tid < kWaves * kCk) partb[tid / kCk][tid % kCk] = 0.f;
     __syncthreads();
     if (p > 0) {
       st.load(k, q, alpha, v, dO, beta, tok0(p - 1), H, DV, count(p - 1), wg * WGC, tid);
@@ -390,74 +392,80 @@ kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
       }
     }
     __syncthreads();
-    // backward over the piece
-    for (int s = n - 1; s >= 0; --s) {
-      const float* kr = kS + s * DK + rg * RPT;
-      const float* qr = qS + s * DK + rg * RPT;
-      const float* ar = aS + s * DK + rg * RPT;
-      const float uj = uS[s * WGC + cw], rj = rS[s * WGC + cw];
-      const float vj = vS[s * WGC + cw], oj = oS[s * WGC + cw], bt = bS[s];
-      float Sb[RPT], Gm[RPT], acc = 0.f;
+    // backward over the piece, in two halves of kHalf tokens (last half first)
+    for (int half = 1; half >= 0; --half) {
+      const int lo = half * kHalf, hi = min(n, lo + kHalf);
+      for (int s = hi - 1; s >= lo; --s) {
+        const float* kr = kS + s * DK + rg * RPT;
+        const float* qr = qS + s * DK + rg * RPT;
+        const float* ar = aS + s * DK + rg * RPT;
+        const float uj = uS[s * WGC + cw], rj = rS[s * WGC + cw];
+        const float vj = vS[s * WGC + cw], oj = oS[s * WGC + cw], bt = bS[s];
+        float Sb[RPT], Gm[RPT], acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        Sb[i] = myhist[(s * RPT + i) * kWave + lane];
-        Gm[i] = dS[i] + qr[i] * oj;
-        acc += kr[i] * Gm[i];
-      }
-      const float du = col_sum<CPW>(acc);
-      const size_t row = tok0(p) + static_cast<size_t>(s) * H;   // (b, t, h)
-      if (rg == 0) g_v[row * DV + col] = bt * du;
-      const float pb = row_sum<CPW>(du * (vj - rj));
-      if (lane == 0) partb[wave][s] = pb;
-      const float dr = -bt * du;
-      float val[VP];
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const float sp = ar[i] * Sb[i];
-        const float sn = sp + kr[i] * uj;
-        const float dsp = Gm[i] + kr[i] * dr;
-        val[3 * i + 0] = sn * oj;                  // dq
-        val[3 * i + 1] = Gm[i] * uj + sp * dr;     // dk
-        val[3 * i + 2] = dsp * Sb[i];              // dalpha
-        dS[i] = ar[i] * dsp;
-      }
-#pragma unroll
-      for (int m = NV; m < VP; ++m) val[m] = 0.f;
-      butterfly<CPW, VP>(val, lane);
-#pragma unroll
-      for (int w = 0; w < PER; ++w) {
-        const int m = j * PER + w;
-        if (m < NV) {
-          const int i = m / 3, qn = m % 3;
-          atomicAdd(part + (s * 3 + qn) * DK + rg + RG * i, val[w]);
+        for (int i = 0; i < RPT; ++i) {
+          Sb[i] = myhist[(s * RPT + i) * kWave + lane];
+          Gm[i] = dS[i] + qr[i] * oj;
+          acc += kr[i] * Gm[i];
         }
-      }
-    }
-    __syncthreads();
-    // the piece's row sums of this workgroup's columns into the gradient rows:
-    // thread slot x = (quantity, row) adds token s's sum to row tok0 + s H
-    constexpr int NSLOT = 3 * DK;
+        const float du = col_sum<CPW>(acc);
+        const size_t row = tok0(p) + static_cast<size_t>(s) * H;   // (b, t, h)
+        if (rg == 0) g_v[row * DV + col] = bt * du;
+        const float pb = row_sum<CPW>(du * (vj - rj));
+        if (lane == 0) partb[wave][s] = pb;
+        const float dr = -bt * du;
+        float val[VP];
 #pragma unroll
-    for (int x0 = 0; x0 < NSLOT; x0 += kThreads) {
-      const int x = x0 + tid;
-      if (x < NSLOT) {
-        const int qn = x / DK, c = x % DK;
-        float* dst = (qn == 0 ? g_q : (qn == 1 ? g_k : g_alpha)) + tok0(p) * DK + c;
-        const size_t step = static_cast<size_t>(H) * DK;
+        for (int i = 0; i < RPT; ++i) {
+          const float sp = ar[i] * Sb[i];
+          const float sn = sp + kr[i] * uj;
+          const float dsp = Gm[i] + kr[i] * dr;
+          val[3 * i + 0] = sn * oj;                  // dq
+          val[3 * i + 1] = Gm[i] * uj + sp * dr;     // dk
+          val[3 * i + 2] = dsp * Sb[i];              // dalpha
+          dS[i] = ar[i] * dsp;
+        }
 #pragma unroll
-        for (int s = 0; s < kCk; ++s) {
-          if (s < n) {
-            unsafeAtomicAdd(dst + s * step, part[s * NSLOT + x]);
-            part[s * NSLOT + x] = 0.f;
+        for (int m = NV; m < VP; ++m) val[m] = 0.f;
+        butterfly<CPW, VP>(val, lane);
+#pragma unroll
+        for (int w = 0; w < PER; ++w) {
+          const int m = j * PER + w;
+          if (m < NV) {
+            const int i = m / 3, qn = m % 3;
+            mypart[((s - lo) * 3 + qn) * DK + rg + RG * i] = val[w];
           }
         }
       }
-    }
-    if (tid < n) {
-      float sb = 0.f;
+      __syncthreads();
+      // this half's row sums of the workgroup's columns into the gradient
+      // rows: thread slot x = (quantity, row) adds token s's sum (four waves)
+      constexpr int NSLOT = 3 * DK;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) sb += partb[w][tid];
-      unsafeAtomicAdd(g_beta + tok0(p) + static_cast<size_t>(tid) * H, sb);
+      for (int x0 = 0; x0 < NSLOT; x0 += kThreads) {
+        const int x = x0 + tid;
+        if (x < NSLOT) {
+          const int qn = x / DK, c = x % DK;
+          float* dst = (qn == 0 ? g_q : (qn == 1 ? g_k : g_alpha)) + tok0(p) * DK + c;
+          const size_t step = static_cast<size_t>(H) * DK;
+#pragma unroll
+          for (int e = 0; e < kHalf; ++e) {
+            if (lo + e < hi) {
+              float sum = 0.f;
+#pragma unroll
+              for (int w = 0; w < kWaves; ++w) sum += part[(w * kHalf + e) * NSLOT + x];
+              unsafeAtomicAdd(dst + (lo + e) * step, sum);
+            }
+          }
+        }
+      }
+      if (tid >= lo && tid < hi) {
+        float sb = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) sb += partb[w][tid];
+        unsafeAtomicAdd(g_beta + tok0(p) + static_cast<size_t>(tid) * H, sb);
+      }
+      __syncthreads();
     }
   }
   if (g_S0) {
