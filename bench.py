@@ -525,7 +525,7 @@ def extras(args, legs, out, torch, kda, wl, dev):
             "ms_per_call": ms_p, "tokens_per_s": B * T / (ms_p * 1e-3),
             "alg_GBps": pbytes / (ms_p * 1e-3) / 1e9,
             "frac_hbm": pbytes / (ms_p * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "alg_bytes_per_call": pbytes,
+            "alg_bytes_per_call": pbytes, "traffic": profiled_traffic("prefill_bwd_h16_t4k"),
             "note": "token-sequential walk per (head, 8-column slab): bound by the per-token "
                     "dependency chain, not by HBM; the chunked adjoint is the next step",
         }
