@@ -26,10 +26,11 @@
 // atomics (the workgroups of a head add into the same rows).
 //
 // The backward needs the state before every token.  Kernel 1 runs the
-// recurrence forward and stores the state every kCk tokens into the
-// workspace; kernel 2 walks those pieces from the last to the first: it
-// restores the piece's first state, runs the kCk tokens forward again keeping
-// each state in LDS, then runs them backward.  Per piece the token rows (k,
+// recurrence forward and stores the state every kCk tokens, and every token's
+// write u and read r per column, into the workspace; kernel 2 walks those
+// pieces from the last to the first: it restores the piece's first state,
+// rebuilds the piece's states from it and the stored u (S = Diag(alpha) S +
+// k^T u, no column sum) keeping each in LDS, then runs the tokens backward.  Per piece the token rows (k,
 // alpha, q; v and dO of the workgroup's columns; beta) are staged into LDS,
 // shared by the four waves, with 16-byte loads issued one piece ahead.
 //
@@ -159,13 +160,14 @@ struct Stage {
   uint4 kr[NRI];
   uint4 qr[kBwd ? NRI : 1];
   float4 ar[NRA];
-  float vc, oc, bb;
+  float vc, oc, uc, rc, bb;
   float sc[kBwd ? Geo<DK>::RPT : 1];   // the piece's first state, this lane's rows
 
   // Tokens of rows tok0, tok0 + H, ... (n of them); columns col0 .. col0 + WGC - 1.
   __device__ __forceinline__ void load(const E* k, const E* q, const float* alpha, const E* v,
-                                       const E* dO, const float* beta, size_t tok0, int H,
-                                       int DV, int n, int col0, int tid) {
+                                       const E* dO, const float* beta, const float* uw,
+                                       const float* rw, size_t tok0, int H, int DV, int n,
+                                       int col0, int tid) {
 #pragma unroll
     for (int it = 0; it < NRI; ++it) {
       const int e = (it * kThreads + tid) * VEC, s = e / DK, c = e % DK;
@@ -187,7 +189,11 @@ struct Stage {
       const bool ok = tid < kCk * WGC && s < n;
       const size_t off = (tok0 + static_cast<size_t>(s) * H) * DV + col0 + cc;
       vc = ok ? Ty<IO>::to_f32(v[off]) : 0.f;
-      if constexpr (kBwd) oc = ok ? Ty<IO>::to_f32(dO[off]) : 0.f;
+      if constexpr (kBwd) {
+        oc = ok ? Ty<IO>::to_f32(dO[off]) : 0.f;
+        uc = ok ? uw[off] : 0.f;
+        rc = ok ? rw[off] : 0.f;
+      }
     }
     bb = (tid < kCk && tid < n) ? beta[tok0 + static_cast<size_t>(tid) * H] : 0.f;
   }
@@ -198,7 +204,7 @@ struct Stage {
   }
 
   __device__ __forceinline__ void store(float* kS, float* qS, float* aS, float* vS, float* oS,
-                                        float* bS, int tid) const {
+                                        float* uS, float* rS, float* bS, int tid) const {
 #pragma unroll
     for (int it = 0; it < NRI; ++it) {
       const int e = (it * kThreads + tid) * VEC, s = e / DK, c = e % DK;
@@ -222,7 +228,11 @@ struct Stage {
     }
     if (tid < kCk * WGC) {
       vS[tid] = vc;   // [token][column]
-      if constexpr (kBwd) oS[tid] = oc;
+      if constexpr (kBwd) {
+        oS[tid] = oc;
+        uS[tid] = uc;
+        rS[tid] = rc;
+      }
     }
     if (tid < kCk) bS[tid] = bb;
   }
@@ -259,8 +269,8 @@ __global__ void __launch_bounds__(kThreads)
 kda_pb_forward_kernel(const typename Ty<IO>::Elem* __restrict__ k,
                       const typename Ty<IO>::Elem* __restrict__ v,
                       const float* __restrict__ alpha, const float* __restrict__ beta,
-                      const float* __restrict__ S0, float* __restrict__ ck, int T, int H,
-                      int DV) {
+                      const float* __restrict__ S0, float* __restrict__ ck,
+                      float* __restrict__ uw, float* __restrict__ rw, int T, int H, int DV) {
   using G = Geo<DK>;
   constexpr int RPT = G::RPT, CPW = G::CPW, RG = G::RG, WGC = G::WGC;
   const int NWG = DV / WGC;
@@ -289,21 +299,27 @@ kda_pb_forward_kernel(const typename Ty<IO>::Elem* __restrict__ k,
     return static_cast<size_t>(b) * T * H + static_cast<size_t>(p) * kCk * H + h;
   };
   auto count = [&](int p) { return min(kCk, T - p * kCk); };
-  st.load(k, nullptr, alpha, v, nullptr, beta, tok0(0), H, DV, count(0), wg * WGC, tid);
+  st.load(k, nullptr, alpha, v, nullptr, beta, nullptr, nullptr, tok0(0), H, DV, count(0),
+          wg * WGC, tid);
   for (int p = 0; p < npiece; ++p) {
-    st.store(kS, nullptr, aS, vS, nullptr, bS, tid);
+    st.store(kS, nullptr, aS, vS, nullptr, nullptr, nullptr, bS, tid);
     __syncthreads();
     if (p + 1 < npiece)
-      st.load(k, nullptr, alpha, v, nullptr, beta, tok0(p + 1), H, DV, count(p + 1), wg * WGC,
-              tid);
+      st.load(k, nullptr, alpha, v, nullptr, beta, nullptr, nullptr, tok0(p + 1), H, DV,
+              count(p + 1), wg * WGC, tid);
     float* out = ck + ck_off(chain, p, npiece, wg, NWG, DK * WGC) + wave * RPT * kWave;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) out[i * kWave + lane] = S[i];
     const int n = count(p);
     for (int s = 0; s < n; ++s) {
       float u;
-      fwd_token<DK>(S, kS + s * DK + rg * RPT, aS + s * DK + rg * RPT, vS[s * WGC + cw], bS[s],
-                    &u);
+      const float r = fwd_token<DK>(S, kS + s * DK + rg * RPT, aS + s * DK + rg * RPT,
+                                    vS[s * WGC + cw], bS[s], &u);
+      if (rg == 0) {   // the token's write and read, for the backward's rebuild
+        const size_t o = (tok0(p) + static_cast<size_t>(s) * H) * DV + col;
+        uw[o] = u;
+        rw[o] = r;
+      }
     }
     __syncthreads();
   }
@@ -317,6 +333,7 @@ kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
                        const float* __restrict__ alpha, const float* __restrict__ beta,
                        const typename Ty<IO>::Elem* __restrict__ dO,
                        const float* __restrict__ dS_T, const float* __restrict__ ck,
+                       const float* __restrict__ uw, const float* __restrict__ rw,
                        float* __restrict__ g_q, float* __restrict__ g_k,
                        float* __restrict__ g_v, float* __restrict__ g_alpha,
                        float* __restrict__ g_beta, float* __restrict__ g_S0, int T, int H,
@@ -363,32 +380,35 @@ kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
     return ck + ck_off(chain, p, npiece, wg, NWG, DK * WGC) + wave * RPT * kWave;
   };
   if (npiece > 0) {
-    st.load(k, q, alpha, v, dO, beta, tok0(npiece - 1), H, DV, count(npiece - 1), wg * WGC, tid);
+    st.load(k, q, alpha, v, dO, beta, uw, rw, tok0(npiece - 1), H, DV, count(npiece - 1),
+            wg * WGC, tid);
     st.load_state(state_at(npiece - 1), lane);
   }
   for (int p = npiece - 1; p >= 0; --p) {
-    st.store(kS, qS, aS, vS, oS, bS, tid);
+    st.store(kS, qS, aS, vS, oS, uS, rS, bS, tid);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) myhist[i * kWave + lane] = st.sc[i];
     __syncthreads();
     if (p > 0) {
-      st.load(k, q, alpha, v, dO, beta, tok0(p - 1), H, DV, count(p - 1), wg * WGC, tid);
+      st.load(k, q, alpha, v, dO, beta, uw, rw, tok0(p - 1), H, DV, count(p - 1), wg * WGC,
+              tid);
       st.load_state(state_at(p - 1), lane);
     }
     const int n = count(p);
     float S[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) S[i] = myhist[i * kWave + lane];
-    // forward again over the piece, keeping the state before each token
+    // rebuild the piece's states from its first one and the stored writes u
+    // (S = Diag(alpha) S + k^T u: no column sum), keeping the state before
+    // each token
     for (int s = 0; s < n; ++s) {
+      const float* kr = kS + s * DK + rg * RPT;
+      const float* ar = aS + s * DK + rg * RPT;
+      const float uj = uS[s * WGC + cw];
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) myhist[(s * RPT + i) * kWave + lane] = S[i];
-      float u;
-      const float r = fwd_token<DK>(S, kS + s * DK + rg * RPT, aS + s * DK + rg * RPT,
-                                    vS[s * WGC + cw], bS[s], &u);
-      if (rg == 0) {
-        uS[s * WGC + cw] = u;
-        rS[s * WGC + cw] = r;
+      for (int i = 0; i < RPT; ++i) {
+        myhist[(s * RPT + i) * kWave + lane] = S[i];
+        S[i] = ar[i] * S[i] + kr[i] * uj;
       }
     }
     __syncthreads();
@@ -494,6 +514,11 @@ hipError_t run(const PrefillBwdArgs& a) {
   if (a.dv % WGC != 0) return hipErrorInvalidValue;
   const unsigned grid = static_cast<unsigned>(a.B) * a.H * (a.dv / WGC);
   const hipStream_t stream = static_cast<hipStream_t>(a.stream);
+  // workspace: stored states, then u and r [B, T, H, dv] each
+  float* ck = static_cast<float*>(a.workspace);
+  const size_t npiece = (static_cast<size_t>(a.T) + kCk - 1) / kCk;
+  float* uw = ck + static_cast<size_t>(a.B) * a.H * npiece * a.dk * a.dv;
+  float* rw = uw + static_cast<size_t>(a.B) * a.T * a.H * a.dv;
   if (a.T > 0) {
     const size_t nk = static_cast<size_t>(a.B) * a.T * a.H * a.dk;
     const size_t nb = static_cast<size_t>(a.B) * a.T * a.H;
@@ -502,13 +527,13 @@ hipError_t run(const PrefillBwdArgs& a) {
     const unsigned zg = static_cast<unsigned>(zb < 4096 ? zb : 4096);
     zero_fill_kernel<<<zg, 256, 0, stream>>>(a.g_q, nk, a.g_k, nk, a.g_alpha, nk, a.g_beta, nb);
     kda_pb_forward_kernel<IO, DK><<<grid, kThreads, 0, stream>>>(
-        static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.alpha, a.beta, a.S0,
-        static_cast<float*>(a.workspace), a.T, a.H, a.dv);
+        static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.alpha, a.beta, a.S0, ck, uw,
+        rw, a.T, a.H, a.dv);
   }
   kda_pb_backward_kernel<IO, DK><<<grid, kThreads, 0, stream>>>(
       static_cast<const E*>(a.q), static_cast<const E*>(a.k), static_cast<const E*>(a.v),
       a.alpha, a.beta, static_cast<const E*>(a.dO), a.dS_T,
-      static_cast<const float*>(a.workspace), a.g_q, a.g_k, a.g_v, a.g_alpha, a.g_beta, a.g_S0,
+      ck, uw, rw, a.g_q, a.g_k, a.g_v, a.g_alpha, a.g_beta, a.g_S0,
       a.T, a.H, a.dv);
   return hipGetLastError();
 }
@@ -528,7 +553,8 @@ hipError_t run_dk(const PrefillBwdArgs& a) {
 
 size_t prefill_backward_workspace(int B, int T, int H, int dk, int dv) {
   const size_t npiece = (static_cast<size_t>(T) + kCk - 1) / kCk;
-  return static_cast<size_t>(B) * H * npiece * dk * dv * sizeof(float);
+  return (static_cast<size_t>(B) * H * npiece * dk * dv +
+          2 * static_cast<size_t>(B) * T * H * dv) * sizeof(float);
 }
 
 hipError_t launch_prefill_backward(const PrefillBwdArgs& a) {

@@ -296,8 +296,9 @@ kda_status kda_decode_step_backward(const void* q, const void* k, const void* v,
 /*
  * kda_prefill_backward_workspace_bytes — device workspace, in bytes, that
  * kda_prefill_backward needs for these sizes: the state of every sequence
- * and head stored once every 16 tokens, B * H * ceil(T / 16) * dk * dv *
- * 4 bytes (256 MiB at B = 1, T = 4096, H = 16, dk = dv = 128).
+ * and head stored once every 16 tokens, B * H * ceil(T / 16) * dk * dv * 4
+ * bytes, and every token's write and read per value column, 2 * B * T * H *
+ * dv * 4 bytes (320 MiB at B = 1, T = 4096, H = 16, dk = dv = 128).
  * (size_t)-1 for sizes the call does not accept.
  */
 size_t kda_prefill_backward_workspace_bytes(int B, int T, int H, int dk, int dv);
@@ -312,8 +313,8 @@ size_t kda_prefill_backward_workspace_bytes(int B, int T, int H, int dk, int dv)
  * recurrence of "From GPT-2 to Kimi K3, Explained", sections "DeltaNet
  * (Fast Weight Programmers)" and "KDA/Kimi Linear").  The states are
  * recomputed from S0: one forward pass stores them every 16 tokens in the
- * workspace, and each 16-token piece is run forward again before its
- * backward.
+ * workspace, with each token's write and read, and each 16-token piece's
+ * states are rebuilt from them before its backward.
  *
  *   q, k, v, alpha, beta, S0   the prefill's inputs, as kda_prefill_chunked
  *                              (S0 may be NULL: zeros)

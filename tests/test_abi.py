@@ -286,8 +286,10 @@ def test_step_backward_validation():
 def test_prefill_backward_workspace_bytes():
     L = _lib()
     lib = L.load()
-    assert lib.kda_prefill_backward_workspace_bytes(1, 4096, 16, 128, 128) == 256 << 20
-    assert lib.kda_prefill_backward_workspace_bytes(2, 17, 3, 64, 32) == 2 * 3 * 2 * 64 * 32 * 4
+    # states every 16 tokens, then the write and read of every token and column
+    assert lib.kda_prefill_backward_workspace_bytes(1, 4096, 16, 128, 128) == 320 << 20
+    assert lib.kda_prefill_backward_workspace_bytes(2, 17, 3, 64, 32) == \
+        2 * 3 * 2 * 64 * 32 * 4 + 2 * 2 * 17 * 3 * 32 * 4
     assert lib.kda_prefill_backward_workspace_bytes(1, 0, 1, 16, 16) == 0
     bad = ctypes.c_size_t(-1).value
     assert lib.kda_prefill_backward_workspace_bytes(1, 16, 1, 24, 16) == bad
