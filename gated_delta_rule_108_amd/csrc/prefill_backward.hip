@@ -282,6 +282,7 @@ kda_pb_forward_kernel(const typename Ty<IO>::Elem* __restrict__ k,
   const int npiece = (T + kCk - 1) / kCk;
 
   __shared__ float kS[kCk * DK], aS[kCk * DK], vS[kCk * WGC], bS[kCk];
+  __shared__ float uO[kCk * WGC], rO[kCk * WGC];   // the piece's writes and reads, [token][column]
   __shared__ float s0[kWaves * RPT * kWave];
   // The initial state goes through LDS: values that enter the token loop
   // straight from a global load make the compiler wait for every vector
@@ -316,12 +317,16 @@ kda_pb_forward_kernel(const typename Ty<IO>::Elem* __restrict__ k,
       const float r = fwd_token<DK>(S, kS + s * DK + rg * RPT, aS + s * DK + rg * RPT,
                                     vS[s * WGC + cw], bS[s], &u);
       if (rg == 0) {   // the token's write and read, for the backward's rebuild
-        const size_t o = (tok0(p) + static_cast<size_t>(s) * H) * DV + col;
-        uw[o] = u;
-        rw[o] = r;
+        uO[s * WGC + cw] = u;
+        rO[s * WGC + cw] = r;
       }
     }
     __syncthreads();
+    if (tid < n * WGC) {   // one coalesced store per thread for the piece
+      const size_t o = (tok0(p) + static_cast<size_t>(tid / WGC) * H) * DV + wg * WGC + tid % WGC;
+      uw[o] = uO[tid];
+      rw[o] = rO[tid];
+    }
   }
 }
 
@@ -356,6 +361,7 @@ kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
   // Plain stores (each slot has one writer); the flush adds the four waves.
   __shared__ float part[kWaves * kHalf * 3 * DK];
   __shared__ float partb[kWaves][kCk];                 // dbeta, per wave
+  __shared__ float dvS[kHalf * WGC];                   // dv of the half piece, [token][column]
   float* mypart = part + wave * kHalf * 3 * DK;
   float* myhist = hist + wave * kCk * RPT * kWave;
 
@@ -429,8 +435,7 @@ kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
           acc += kr[i] * Gm[i];
         }
         const float du = col_sum<CPW>(acc);
-        const size_t row = tok0(p) + static_cast<size_t>(s) * H;   // (b, t, h)
-        if (rg == 0) g_v[row * DV + col] = bt * du;
+        if (rg == 0) dvS[(s - lo) * WGC + cw] = bt * du;
         const float pb = row_sum<CPW>(du * (vj - rj));
         if (lane == 0) partb[wave][s] = pb;
         const float dr = -bt * du;
@@ -478,6 +483,11 @@ kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
             }
           }
         }
+      }
+      if (tid < (hi - lo) * WGC) {   // dv: one coalesced store per thread
+        const size_t o =
+            (tok0(p) + static_cast<size_t>(lo + tid / WGC) * H) * DV + wg * WGC + tid % WGC;
+        g_v[o] = dvS[tid];
       }
       if (tid >= lo && tid < hi) {
         float sb = 0.f;
