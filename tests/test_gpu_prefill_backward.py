@@ -129,3 +129,30 @@ def test_full_workload_sampled_heads():
     the oracle on heads 0 and 11."""
     spec = wl.PREFILL["prefill_h16_t4k"]
     run_case(spec, B=1, T=spec.T, H=spec.H, heads=[0, 11])
+
+
+def test_state_gradient_in_place_through_the_abi():
+    """dS0 written over dS_T (the one overlap the call accepts) equals the
+    out-of-place result bit for bit (dS0 takes no atomics)."""
+    import ctypes
+    from gated_delta_rule_108_amd import _lib
+    m = kda()
+    spec = spec_of(64, 64, torch.float32)
+    x = wl.make_prefill_inputs(spec, DEV, T=40, B=1, H=2)
+    gr = wl.make_prefill_backward_grads(spec, DEV, T=40, B=1, H=2)
+    ref = m.prefill_backward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], gr["dO"],
+                             S0=x["S0"], dS_T=gr["dS_T"])
+    L = m.lib()
+    outs = [torch.empty_like(t) for t in ref[:5]]
+    dS = gr["dS_T"].clone()
+    nws = m.prefill_backward_workspace_bytes(1, 40, 2, 64, 64)
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    st = L.kda_prefill_backward(p(x["q"]), p(x["k"]), p(x["v"]), p(x["alpha"]), p(x["beta"]),
+                                p(x["S0"]), p(gr["dO"]), p(dS), *[p(o) for o in outs], p(dS),
+                                1, 40, 2, 64, 64, _lib.KDA_F32, p(ws), nws,
+                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == _lib.KDA_OK
+    assert torch.equal(dS, ref[5])
+    assert torch.equal(outs[2], ref[2])
