@@ -30,12 +30,13 @@
 // write u and read r per column, into the workspace; kernel 2 walks those
 // pieces from the last to the first: it restores the piece's first state,
 // rebuilds the piece's states from it and the stored u (S = Diag(alpha) S +
-// k^T u, no column sum) keeping each in LDS, then runs the tokens backward.  Per piece the token rows (k,
-// alpha, q; v and dO of the workgroup's columns; beta) are staged into LDS,
-// shared by the four waves, with 16-byte loads issued one piece ahead.
+// k^T u, no column sum) keeping each in LDS, then runs the tokens backward.
+// Per piece the token rows (k, alpha, q; v, dO, u and r of the workgroup's
+// columns; beta) and the next piece's first state are staged into LDS,
+// shared by the four waves, with loads issued one piece ahead.
 //
-// The work is sequential in tokens (a latency-bound walk, about 2 dk dv
-// flops of VALU per element per token), unlike the chunked forward: the chunk
+// The work is sequential in tokens (a latency-bound walk, about ten VALU
+// flops per state element per token), unlike the chunked forward: the chunk
 // form of the adjoint, on the matrix cores, is the next step.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
