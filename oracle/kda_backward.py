@@ -27,6 +27,19 @@ forward oracle (a different computation that a wrong sign, a dropped term or
 a transposed product fails), for one step and for a chain of steps that
 reproduces the gradient of a whole prefill.
 
+kda_prologue_backward is the chain rule through the input prologue of
+kda_prologue.py (alpha = exp(-softplus(g)) = sigmoid(-g), beta = sigmoid(b),
+q, k = normalize(phi(x))):
+
+    dg = -dalpha alpha (1 - alpha),   db = dbeta beta (1 - beta)
+    normalize, y = x / max(||x||, eps):  dx = (dy - y (y . dy)) / ||x||  if ||x|| > eps,
+                                         dx = dy / eps                      otherwise
+    silu:  d silu(x) / dx = sigmoid(x) (1 + x (1 - sigmoid(x)))
+
+and kda_prefill_backward_logits chains prologue, prefill backward and
+prologue backward.  Both are pinned against finite differences of the
+forward oracle in tests/test_backward_pins.py.
+
 kda_prefill_backward is that chain written out: the forward recurrence
 (kda_oracle.kda_recurrence) run once to keep the state before every token,
 then the step adjoint applied from the last token to the first, the state
@@ -37,8 +50,10 @@ from __future__ import annotations
 import numpy as np
 
 from .kda_oracle import as_f64, kda_decode_step
+from .kda_prologue import NORM_EPS, QK_AS_GIVEN, QK_L2, QK_SILU_L2, kda_prologue, sigmoid, silu
 
-__all__ = ["kda_decode_step_backward", "kda_prefill_backward"]
+__all__ = ["kda_decode_step_backward", "kda_prefill_backward", "kda_prologue_backward",
+           "kda_prefill_backward_logits"]
 
 
 def kda_decode_step_backward(q, k, v, alpha, beta, S, dO, dS_new):
@@ -88,3 +103,46 @@ def kda_prefill_backward(q, k, v, alpha, beta, S0, dO, dS_T):
         dq[:, t], dk_[:, t], dv_[:, t], da[:, t], db[:, t], dS = kda_decode_step_backward(
             q[:, t], k[:, t], v[:, t], alpha[:, t], beta[:, t], before[t], dO[:, t], dS)
     return dq, dk_, dv_, da, db, dS
+
+
+def _normalize_backward(x, dy):
+    """Adjoint of normalize(x) = x / max(||x||, eps) over the last axis."""
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    big = n > NORM_EPS
+    y = x / np.where(big, n, NORM_EPS)
+    proj = np.sum(y * dy, axis=-1, keepdims=True)
+    return np.where(big, (dy - y * proj) / np.where(big, n, 1.0), dy / NORM_EPS)
+
+
+def kda_prologue_backward(q, k, g, b, dq_hat, dk_hat, dalpha, dbeta, qk_map=QK_L2):
+    """Adjoint of kda_prologue, float64: from the gradients with respect to
+    its outputs (q_hat, k_hat, alpha, beta) to those with respect to its raw
+    inputs.  Returns (dq, dk, dg, db), shaped like q, k, g, b."""
+    q, k, g, b = (as_f64(x) for x in (q, k, g, b))
+    dq_hat, dk_hat, dalpha, dbeta = (as_f64(x) for x in (dq_hat, dk_hat, dalpha, dbeta))
+    alpha = sigmoid(-g)
+    beta = sigmoid(b)
+    dg = -dalpha * alpha * (1.0 - alpha)
+    db = dbeta * beta * (1.0 - beta)
+
+    def feature(x, dy):
+        if qk_map == QK_AS_GIVEN:
+            return dy
+        if qk_map == QK_L2:
+            return _normalize_backward(x, dy)
+        if qk_map == QK_SILU_L2:
+            s = sigmoid(x)
+            return _normalize_backward(silu(x), dy) * s * (1.0 + x * (1.0 - s))
+        raise ValueError(f"unknown qk_map {qk_map}")
+
+    return feature(q, dq_hat), feature(k, dk_hat), dg, db
+
+
+def kda_prefill_backward_logits(q, k, v, g, b, S0, dO, dS_T, qk_map=QK_L2):
+    """Gradients of L through kda_recurrence_logits (prologue, then the
+    recurrence), float64.  Returns (dq, dk, dv, dg, db, dS0) with respect to
+    the raw q, k, v, g, b and S0."""
+    qn, kn, alpha, beta = kda_prologue(q, k, g, b, qk_map)
+    dqh, dkh, dv, da, db_, dS0 = kda_prefill_backward(qn, kn, v, alpha, beta, S0, dO, dS_T)
+    dq, dk, dg, db = kda_prologue_backward(q, k, g, b, dqh, dkh, da, db_, qk_map)
+    return dq, dk, dv, dg, db, dS0
