@@ -31,6 +31,11 @@ and of a whole prefill (float32 gradients; S0 and dS_T optional):
 
     dq, dk, dv, dalpha, dbeta, dS0 = prefill_backward(q, k, v, alpha, beta, dO, S0, dS_T)
 
+and from raw projections (the prologue's forward and adjoint as kernels of
+their own around the prefill backward):
+
+    dq, dk, dv, dg, db, dS0 = prefill_backward_logits(q, k, v, g, b, dO, S0, dS_T, qk_map)
+
 Layouts (token-major, as the attention projections produce them):
     prefill  q,k [B,T,H,dk]  v [B,T,H,dv]  alpha [B,T,H,dk]  beta [B,T,H]
              S0, S_T [B,H,dk,dv]  o [B,T,H,dv]
@@ -48,7 +53,8 @@ from ._lib import KDAError  # noqa: F401
 
 __all__ = ["prefill_chunked", "decode_step", "prefill_chunked_logits", "decode_step_logits",
            "gdn_prefill_chunked", "gdn_decode_step", "decode_step_backward",
-           "prefill_backward", "prefill_backward_workspace_bytes",
+           "prefill_backward", "prefill_backward_workspace_bytes", "prologue_forward",
+           "prologue_backward", "prefill_backward_logits",
            "prefill_workspace_bytes", "KDAError", "lib"]
 
 _DT = {torch.bfloat16: _lib.KDA_BF16, torch.float32: _lib.KDA_F32}
@@ -294,3 +300,72 @@ def prefill_backward(q, k, v, alpha, beta, dO, S0=None, dS_T=None):
     if st != _lib.KDA_OK:
         raise KDAError(st, "kda_prefill_backward")
     return g_q, g_k, g_v, g_a, g_b, g_S
+
+
+def _prologue_rows(q, k, g, b):
+    if q.dtype not in _DT:
+        raise TypeError(f"q: dtype {q.dtype} not supported")
+    dk = q.shape[-1]
+    lead = tuple(q.shape[:-1])
+    for n, t, d, sh in (("q", q, q.dtype, q.shape), ("k", k, q.dtype, q.shape),
+                        ("g", g, q.dtype, q.shape), ("b", b, torch.float32, lead)):
+        _check(n, t, d, sh, q.device)
+    rows = 1
+    for x in lead:
+        rows *= x
+    return rows, dk, lead
+
+
+def prologue_forward(q, k, g, b, qk_map="l2"):
+    """The input prologue alone: raw q, k, g [..., dk] (bf16 or fp32) and b
+    [...] fp32 -> (q_hat, k_hat, alpha, beta), the inputs of prefill_chunked
+    and prefill_backward."""
+    if qk_map not in _QK:
+        raise ValueError(f"qk_map must be one of {sorted(_QK)}")
+    rows, dk, lead = _prologue_rows(q, k, g, b)
+    dev = q.device
+    qh, kh = torch.empty_like(q), torch.empty_like(k)
+    alpha = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    beta = torch.empty(lead, dtype=torch.float32, device=dev)
+    st = lib().kda_prologue_forward(_ptr(q), _ptr(k), _ptr(g), _ptr(b), _ptr(qh), _ptr(kh),
+                                    _ptr(alpha), _ptr(beta), rows, dk, _DT[q.dtype], _QK[qk_map],
+                                    _stream(dev))
+    if st != _lib.KDA_OK:
+        raise KDAError(st, "kda_prologue_forward")
+    return qh, kh, alpha, beta
+
+
+def prologue_backward(q, k, g, b, dq_hat, dk_hat, dalpha, dbeta, qk_map="l2"):
+    """Adjoint of prologue_forward: gradients with respect to (q_hat, k_hat,
+    alpha, beta), fp32, -> gradients with respect to the raw (q, k, g, b),
+    fp32."""
+    if qk_map not in _QK:
+        raise ValueError(f"qk_map must be one of {sorted(_QK)}")
+    rows, dk, lead = _prologue_rows(q, k, g, b)
+    dev = q.device
+    f32 = torch.float32
+    for n, t, sh in (("dq_hat", dq_hat, q.shape), ("dk_hat", dk_hat, q.shape),
+                     ("dalpha", dalpha, q.shape), ("dbeta", dbeta, lead)):
+        _check(n, t, f32, sh, dev)
+    dq = torch.empty(q.shape, dtype=f32, device=dev)
+    dk_ = torch.empty(q.shape, dtype=f32, device=dev)
+    dg = torch.empty(q.shape, dtype=f32, device=dev)
+    db = torch.empty(lead, dtype=f32, device=dev)
+    st = lib().kda_prologue_backward(_ptr(q), _ptr(k), _ptr(g), _ptr(b), _ptr(dq_hat),
+                                     _ptr(dk_hat), _ptr(dalpha), _ptr(dbeta), _ptr(dq), _ptr(dk_),
+                                     _ptr(dg), _ptr(db), rows, dk, _DT[q.dtype], _QK[qk_map],
+                                     _stream(dev))
+    if st != _lib.KDA_OK:
+        raise KDAError(st, "kda_prologue_backward")
+    return dq, dk_, dg, db
+
+
+def prefill_backward_logits(q, k, v, g, b, dO, S0=None, dS_T=None, qk_map="l2"):
+    """Gradients through prefill_chunked_logits: the prologue forward, the
+    prefill backward on its outputs, then the prologue's adjoint (three
+    library calls).  Returns (dq, dk, dv, dg, db, dS0), all float32, with
+    respect to the raw q, k, v, g, b and S0."""
+    qh, kh, alpha, beta = prologue_forward(q, k, g, b, qk_map)
+    dqh, dkh, dv, da, dbeta, dS0 = prefill_backward(qh, kh, v, alpha, beta, dO, S0=S0, dS_T=dS_T)
+    dq, dk_, dg, db = prologue_backward(q, k, g, b, dqh, dkh, da, dbeta, qk_map)
+    return dq, dk_, dv, dg, db, dS0

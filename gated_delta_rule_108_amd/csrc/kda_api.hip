@@ -334,3 +334,85 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
 }
 
 }  // extern "C"
+
+namespace {
+
+// Shared validation of the two prologue calls: rows >= 0, dk and dtype and
+// map supported, every pointer present (when there are rows) and aligned,
+// and no output overlapping an input or another output.
+kda_status prologue_check(const void* const* ins, const size_t* in_bytes, int nin,
+                          void* const* outs, const size_t* out_bytes, int nout, int rows, int dk,
+                          kda_dtype dt, kda_qk_map qk_map) {
+  if (rows < 0) return KDA_ERR_SHAPE;
+  if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  if (!dim_ok(dk) || !qk_map_ok(qk_map)) return KDA_ERR_UNSUPPORTED;
+  if (rows == 0) return KDA_OK;
+  for (int i = 0; i < nin; ++i) {
+    if (!ins[i]) return KDA_ERR_NULL;
+    if (!aligned16(ins[i])) return KDA_ERR_ALIGN;
+  }
+  for (int o = 0; o < nout; ++o) {
+    if (!outs[o]) return KDA_ERR_NULL;
+    if (!aligned16(outs[o])) return KDA_ERR_ALIGN;
+    const Span so = span(outs[o], out_bytes[o]);
+    for (int i = 0; i < nin; ++i)
+      if (overlap(so, span(ins[i], in_bytes[i]))) return KDA_ERR_ALIAS;
+    for (int p = 0; p < o; ++p)
+      if (overlap(so, span(outs[p], out_bytes[p]))) return KDA_ERR_ALIAS;
+  }
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prologue_forward(const void* q, const void* k, const void* g, const float* b,
+                                void* q_hat, void* k_hat, float* alpha, float* beta, int rows,
+                                int dk, kda_dtype dt, kda_qk_map qk_map, void* stream) {
+  const size_t e = (dt == KDA_BF16) ? 2 : 4;
+  const size_t n = rows > 0 ? static_cast<size_t>(rows) : 0;
+  const void* ins[] = {q, k, g, b};
+  const size_t inb[] = {n * dk * e, n * dk * e, n * dk * e, n * 4};
+  void* outs[] = {q_hat, k_hat, alpha, beta};
+  const size_t outb[] = {n * dk * e, n * dk * e, n * dk * 4, n * 4};
+  const kda_status st = prologue_check(ins, inb, 4, outs, outb, 4, rows, dk, dt, qk_map);
+  if (st != KDA_OK || rows == 0) return st;
+  const kda_status dev = check_device();
+  if (dev != KDA_OK) return dev;
+  kda::PrologueArgs a{};
+  a.q = q; a.k = k; a.g = g; a.b = b;
+  a.q_hat = q_hat; a.k_hat = k_hat; a.alpha = alpha; a.beta = beta;
+  a.rows = rows; a.dk = dk; a.bf16 = dt == KDA_BF16; a.qk_map = static_cast<int>(qk_map);
+  a.backward = false; a.stream = stream;
+  if (kda::launch_prologue(a) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+kda_status kda_prologue_backward(const void* q, const void* k, const void* g, const float* b,
+                                 const float* dq_hat, const float* dk_hat, const float* dalpha,
+                                 const float* dbeta, float* dq, float* dk, float* dg, float* db,
+                                 int rows, int dk_, kda_dtype dt, kda_qk_map qk_map,
+                                 void* stream) {
+  const size_t e = (dt == KDA_BF16) ? 2 : 4;
+  const size_t n = rows > 0 ? static_cast<size_t>(rows) : 0;
+  const size_t nk = n * (dk_ > 0 ? dk_ : 0);
+  const void* ins[] = {q, k, g, b, dq_hat, dk_hat, dalpha, dbeta};
+  const size_t inb[] = {nk * e, nk * e, nk * e, n * 4, nk * 4, nk * 4, nk * 4, n * 4};
+  void* outs[] = {dq, dk, dg, db};
+  const size_t outb[] = {nk * 4, nk * 4, nk * 4, n * 4};
+  const kda_status st = prologue_check(ins, inb, 8, outs, outb, 4, rows, dk_, dt, qk_map);
+  if (st != KDA_OK || rows == 0) return st;
+  const kda_status dev = check_device();
+  if (dev != KDA_OK) return dev;
+  kda::PrologueArgs a{};
+  a.q = q; a.k = k; a.g = g; a.b = b;
+  a.dq_hat = dq_hat; a.dk_hat = dk_hat; a.dalpha = dalpha; a.dbeta = dbeta;
+  a.d_q = dq; a.d_k = dk; a.d_g = dg; a.d_b = db;
+  a.rows = rows; a.dk = dk_; a.bf16 = dt == KDA_BF16; a.qk_map = static_cast<int>(qk_map);
+  a.backward = true; a.stream = stream;
+  if (kda::launch_prologue(a) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+}  // extern "C"

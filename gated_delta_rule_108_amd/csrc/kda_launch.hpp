@@ -96,6 +96,34 @@ struct PrefillBwdArgs {
   void* stream;
 };
 hipError_t launch_prefill_backward(const PrefillBwdArgs& a);
+
+// The input prologue alone over `rows` rows of dk channels: forward (raw q,
+// k, g, b -> q_hat, k_hat in the I/O type, alpha, beta fp32) or its adjoint
+// (-> d_q, d_k, d_g, d_b, fp32).
+struct PrologueArgs {
+  const void* q;
+  const void* k;
+  const void* g;
+  const float* b;
+  void* q_hat;            // forward outputs
+  void* k_hat;
+  float* alpha;
+  float* beta;
+  const float* dq_hat;    // adjoint inputs
+  const float* dk_hat;
+  const float* dalpha;
+  const float* dbeta;
+  float* d_q;             // adjoint outputs
+  float* d_k;
+  float* d_g;
+  float* d_b;
+  int rows, dk;
+  bool bf16;
+  int qk_map;
+  bool backward;
+  void* stream;
+};
+hipError_t launch_prologue(const PrologueArgs& a);
 size_t prefill_backward_workspace(int B, int T, int H, int dk, int dv);
 
 // Returns hipErrorInvalidValue when no compiled kernel covers (dk, C, dtype).

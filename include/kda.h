@@ -345,6 +345,54 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v,
                                 int T, int H, int dk_, int dv_, kda_dtype dt, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/*
+ * kda_prologue_forward — the input prologue of kda_prefill_chunked_logits on
+ * its own, for training from raw projections: per row (one token of one
+ * head) alpha = 1 / (1 + e^g) per key channel, beta = sigmoid(b), and q, k
+ * mapped by qk_map, written out as the inputs of kda_prefill_chunked and
+ * kda_prefill_backward.  The gate form keeps every logit inside (0, 1) as
+ * "From GPT-2 to Kimi K3, Explained", section "Gated Delta Net", requires;
+ * SiLU, the L2 map and the sigmoid follow "22580: от GPT-2 до Kimi K3,
+ * объяснение", section "DeltaNet, или Fast Weight Programmers".
+ *
+ *   q, k, g   [rows, dk]  dt       raw queries, keys and gate logits
+ *   b         [rows]      float32  raw write-strength logits
+ *   q_hat, k_hat [rows, dk] dt     mapped queries and keys (written)
+ *   alpha     [rows, dk]  float32  written
+ *   beta      [rows]      float32  written
+ *
+ * rows = B*T*H for [B,T,H,dk] arrays (any row-major leading shape).
+ * rows = 0 does nothing.  Errors: KDA_ERR_NULL, KDA_ERR_SHAPE (rows < 0),
+ * KDA_ERR_UNSUPPORTED (dk, dt or qk_map), KDA_ERR_ALIGN, KDA_ERR_ALIAS (an
+ * output overlapping an input or another output), KDA_ERR_DEVICE,
+ * KDA_ERR_HIP.
+ */
+kda_status kda_prologue_forward(const void* q, const void* k, const void* g, const float* b,
+                                void* q_hat, void* k_hat, float* alpha, float* beta, int rows,
+                                int dk, kda_dtype dt, kda_qk_map qk_map, void* stream);
+
+/*
+ * kda_prologue_backward — the adjoint of kda_prologue_forward: from the
+ * gradients with respect to its outputs (as kda_prefill_backward returns
+ * them) to those with respect to the raw inputs.  The chain rule of the
+ * forward maps:
+ *     dg = -dalpha alpha (1 - alpha),   db = dbeta beta (1 - beta)
+ *     L2 map, y = x / max(||x||, 1e-12):
+ *         dx = (dy - y (y . dy)) / ||x||   (dy / 1e-12 on the floor)
+ *     SiLU:  dq = dx sigmoid(q) (1 + q (1 - sigmoid(q)))
+ *
+ *   q, k, g, b                 the raw inputs, as kda_prologue_forward
+ *   dq_hat, dk_hat, dalpha [rows, dk], dbeta [rows]   float32
+ *   dq, dk, dg [rows, dk], db [rows]                  float32, written
+ *
+ * Errors: as kda_prologue_forward.
+ */
+kda_status kda_prologue_backward(const void* q, const void* k, const void* g, const float* b,
+                                 const float* dq_hat, const float* dk_hat, const float* dalpha,
+                                 const float* dbeta, float* dq, float* dk, float* dg, float* db,
+                                 int rows, int dk_, kda_dtype dt, kda_qk_map qk_map,
+                                 void* stream);
+
 /* kda_status_string — static, human-readable text for a status code. */
 const char* kda_status_string(kda_status s);
 

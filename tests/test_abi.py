@@ -25,13 +25,14 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_eleven_calls():
+def test_header_declares_the_thirteen_calls():
     assert declared_functions() == ["kda_decode_step", "kda_decode_step_backward",
                                     "kda_decode_step_logits",
                                     "kda_gdn_decode_step", "kda_gdn_prefill_chunked",
                                     "kda_prefill_backward", "kda_prefill_backward_workspace_bytes",
                                     "kda_prefill_chunked", "kda_prefill_chunked_logits",
-                                    "kda_prefill_workspace_bytes", "kda_status_string"]
+                                    "kda_prefill_workspace_bytes", "kda_prologue_backward",
+                                    "kda_prologue_forward", "kda_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -332,3 +333,41 @@ def test_prefill_backward_validation():
     # no tokens: only the state gradient is passed through, the rest may be NULL
     assert pb(T=0, q=None, k=None, v=None, alpha=None, beta=None, dO=None, dq=None, dk=None,
               dv=None, da=None, db=None, ws=None, wsb=0) in ok
+
+
+def test_prologue_validation():
+    L = _lib()
+    lib = L.load()
+    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+    rows, d = 64, 128
+
+    def pf(**kw):
+        a = dict(q=addr(0), k=addr(1), g=addr(2), b=addr(3), qh=addr(4), kh=addr(5), al=addr(6),
+                 be=addr(7), rows=rows, dk=d, dt=1, m=1, stream=None)
+        a.update(kw)
+        return lib.kda_prologue_forward(a["q"], a["k"], a["g"], a["b"], a["qh"], a["kh"],
+                                        a["al"], a["be"], a["rows"], a["dk"], a["dt"], a["m"],
+                                        a["stream"])
+
+    def pb(**kw):
+        a = dict(q=addr(0), k=addr(1), g=addr(2), b=addr(3), dqh=addr(4), dkh=addr(5),
+                 da=addr(6), dbe=addr(7), dq=addr(8), dk=addr(9), dg=addr(10), db=addr(11),
+                 rows=rows, dk_=d, dt=1, m=2, stream=None)
+        a.update(kw)
+        return lib.kda_prologue_backward(a["q"], a["k"], a["g"], a["b"], a["dqh"], a["dkh"],
+                                         a["da"], a["dbe"], a["dq"], a["dk"], a["dg"], a["db"],
+                                         a["rows"], a["dk_"], a["dt"], a["m"], a["stream"])
+
+    for f in (pf, pb):
+        assert f() in ok
+        assert f(rows=0, q=None, k=None) in ok                    # nothing to do
+        assert f(rows=-1) == L.KDA_ERR_SHAPE
+        assert f(m=3) == L.KDA_ERR_UNSUPPORTED and f(dt=5) == L.KDA_ERR_UNSUPPORTED
+        assert f(q=None) == L.KDA_ERR_NULL and f(b=addr(3) + 4) == L.KDA_ERR_ALIGN
+    assert pf(dk=24) == L.KDA_ERR_UNSUPPORTED and pb(dk_=24) == L.KDA_ERR_UNSUPPORTED
+    # q_hat over the raw keys, alpha over beta, dg over dalpha: rejected
+    assert pf(qh=addr(1)) == L.KDA_ERR_ALIAS and pf(al=addr(7)) == L.KDA_ERR_ALIAS
+    assert pb(dg=addr(6)) == L.KDA_ERR_ALIAS and pb(db=addr(8)) == L.KDA_ERR_ALIAS
+    # an output right after an input's last byte is fine (bf16 q is rows*dk*2 bytes)
+    assert pf(qh=addr(0) + rows * d * 2) in ok
+    assert pf(qh=addr(0) + rows * d * 2 - 16) == L.KDA_ERR_ALIAS
