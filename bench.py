@@ -90,6 +90,16 @@ def prefill_bwd_alg_bytes(B, T, H, dk, dv, esize):
     return B * T * H * per_tok + 2 * B * H * dk * dv * 4
 
 
+def prologue_alg_bytes(rows, dk, esize):
+    """The prologue alone, per row: forward reads q, k, g (I/O type) and b,
+    writes q_hat, k_hat (I/O type), alpha and beta (fp32); the adjoint reads
+    q, k, g, b and the fp32 gradients of q_hat, k_hat, alpha, beta and writes
+    the fp32 gradients of q, k, g, b.  Returns (forward, adjoint) bytes."""
+    fwd = rows * (3 * esize * dk + 4 + 2 * esize * dk + 4 * dk + 4)
+    bwd = rows * (3 * esize * dk + 4 + 3 * 4 * dk + 4 + 3 * 4 * dk + 4)
+    return fwd, bwd
+
+
 def _code_only(text):
     """C++ source without comments and with whitespace runs collapsed, so that
     editing a comment does not count as changing a kernel."""
@@ -224,7 +234,7 @@ def main():
                     help="headline prefill only (no decode / large prefill lines)")
     ap.add_argument("--only", choices=["prefill", "decode", "large", "logits", "decode_logits",
                                        "gdn", "decode_gdn", "longctx", "decode_bwd", "prefill_bwd",
-                                       "copy"],
+                                       "prologue", "copy"],
                     default=None,
                     help="run one leg only (for profiler runs); 'copy' times a plain "
                          "1 GiB device-to-device copy used to calibrate HBM byte counters")
@@ -251,7 +261,8 @@ def main():
                           "ms_per_copy": ms, "GBps": 8 * n / (ms * 1e-3) / 1e9}), flush=True)
         return
     legs = ({"prefill", "decode", "large", "logits", "decode_logits", "gdn", "decode_gdn",
-             "longctx", "decode_bwd", "prefill_bwd"} if args.only is None else {args.only})
+             "longctx", "decode_bwd", "prefill_bwd", "prologue"} if args.only is None
+            else {args.only})
     if args.no_extra:
         legs = {"prefill"}
 
@@ -531,6 +542,37 @@ def extras(args, legs, out, torch, kda, wl, dev):
         }
         print(f"# prefill_bwd_h16_t4k: {ms_p:.3f} ms/call", file=sys.stderr, flush=True)
         del px, pg
+        torch.cuda.empty_cache()
+
+    if "prologue" in legs:
+        # ---------------- the prologue alone, forward and adjoint, on the H=16 T=4096 rows
+        lspec = wl.PREFILL["prefill_h16_t4k"]
+        lx = wl.make_prefill_logit_inputs(lspec, dev)
+        rows, dk = lspec.B * lspec.T * lspec.H, lspec.dk
+        grad = [torch.randn(lx["q"].shape, device=dev) for _ in range(3)]
+        gb = torch.randn(lx["b"].shape, device=dev)
+
+        def pf():
+            kda.prologue_forward(lx["q"], lx["k"], lx["g"], lx["b"], "silu_l2")
+
+        def pbk():
+            kda.prologue_backward(lx["q"], lx["k"], lx["g"], lx["b"], *grad, gb, "silu_l2")
+
+        ms_f, _ = time_launches(pf, max(args.steps, 20), args.warmup, torch)
+        ms_b, _ = time_launches(pbk, max(args.steps, 20), args.warmup, torch)
+        fb, bb = prologue_alg_bytes(rows, dk, 2)
+        out["prologue_h16_t4k"] = {
+            "forward_us": ms_f * 1e3, "forward_GBps": fb / (ms_f * 1e-3) / 1e9,
+            "adjoint_us": ms_b * 1e3, "adjoint_GBps": bb / (ms_b * 1e-3) / 1e9,
+            "frac_hbm_forward": fb / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "frac_hbm_adjoint": bb / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "alg_bytes": [fb, bb], "traffic": profiled_traffic("prologue_h16_t4k"),
+            "note": "65,536 rows of 128 channels, bf16, SiLU + L2 map; events bracket "
+                    "back-to-back calls from Python (per-call host time included)",
+        }
+        print(f"# prologue_h16_t4k: forward {ms_f * 1e3:.1f} us, adjoint {ms_b * 1e3:.1f} us",
+              file=sys.stderr, flush=True)
+        del lx, grad, gb
         torch.cuda.empty_cache()
 
     if "longctx" in legs:

@@ -84,3 +84,12 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_prologue_bytes_per_row():
+    # forward: q, k, g bf16 read + b; q_hat, k_hat bf16 + alpha fp32 + beta written
+    fwd = 3 * 2 * D + 4 + 2 * 2 * D + 4 * D + 4
+    # adjoint: q, k, g bf16 + b read, three fp32 row gradients + dbeta read,
+    # three fp32 row gradients + db written
+    bwd = 3 * 2 * D + 4 + 3 * 4 * D + 4 + 3 * 4 * D + 4
+    assert bench.prologue_alg_bytes(1, D, 2) == (fwd, bwd) == (1800, 3852)
