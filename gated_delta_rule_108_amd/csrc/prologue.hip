@@ -19,8 +19,11 @@
 //                                        dx = dy / eps                     otherwise
 //   SiLU:  dq = dx sigmoid(q) (1 + q (1 - sigmoid(q)))
 //
-// Both are bound by HBM: one wave per row, lane l holding channels l and
-// l + 64; the row sums (||x||^2, y . dy) are wave butterflies.
+// Both are bound by HBM: one wave per row, lane l holding channels
+// l * EPL .. l * EPL + EPL - 1 (two at dk = 128, so each access is one wider
+// load or store); the row sums (||x||^2, y . dy) are wave butterflies.
+#include <type_traits>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -33,6 +36,36 @@ __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
   return x;
+}
+
+// N consecutive channels of a row as float: two bf16 are one 32-bit load and
+// two fp32 one 64-bit load (the rows start 16-byte aligned and a lane's
+// first channel is even).
+template <typename T, int N>
+__device__ __forceinline__ void load_vec(const typename Ty<T>::Elem* p, float* out) {
+  if constexpr (N == 2 && std::is_same<T, bf16_t>::value) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    out[0] = __uint_as_float(w << 16);
+    out[1] = __uint_as_float(w & 0xFFFF0000u);
+  } else if constexpr (N == 2) {
+    const float2 w = *reinterpret_cast<const float2*>(p);
+    out[0] = w.x;
+    out[1] = w.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = Ty<T>::to_f32(p[i]);
+  }
+}
+template <typename T, int N>
+__device__ __forceinline__ void store_vec(typename Ty<T>::Elem* p, const float* v) {
+  if constexpr (N == 2 && std::is_same<T, bf16_t>::value) {
+    *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(v[0], v[1]);
+  } else if constexpr (N == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) p[i] = Ty<T>::from_f32(v[i]);
+  }
 }
 
 // Value of a feature after the map's element-wise part (SiLU rounded to the
@@ -54,17 +87,19 @@ kda_prologue_forward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
   const int row = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   if (row >= rows) return;   // whole waves: the row is wave-uniform
-  const size_t base = static_cast<size_t>(row) * DK;
-  float xq[EPL], xk[EPL], sq = 0.f, sk = 0.f;
+  const size_t base = static_cast<size_t>(row) * DK + lane * EPL;
+  const bool has = DK >= kWave || lane < DK;   // lanes past dk hold no channel
+  float xq[EPL] = {}, xk[EPL] = {}, gl[EPL] = {}, sq = 0.f, sk = 0.f;
+  if (has) {
+    load_vec<IO, EPL>(q + base, xq);
+    load_vec<IO, EPL>(k + base, xk);
+    load_vec<IO, EPL>(g + base, gl);
+  }
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    const int c = lane + kWave * e;
-    xq[e] = xk[e] = 0.f;
-    if (c < DK) {
-      xq[e] = feature_fwd<IO>(Ty<IO>::to_f32(q[base + c]), qk_map);
-      xk[e] = feature_fwd<IO>(Ty<IO>::to_f32(k[base + c]), qk_map);
-      alpha[base + c] = gate_from_logit(Ty<IO>::to_f32(g[base + c]));
-    }
+    xq[e] = feature_fwd<IO>(xq[e], qk_map);
+    xk[e] = feature_fwd<IO>(xk[e], qk_map);
+    gl[e] = gate_from_logit(gl[e]);
     sq += xq[e] * xq[e];
     sk += xk[e] * xk[e];
   }
@@ -75,11 +110,13 @@ kda_prologue_forward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
   }
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    const int c = lane + kWave * e;
-    if (c < DK) {
-      qh[base + c] = Ty<IO>::from_f32(xq[e] * iq);
-      kh[base + c] = Ty<IO>::from_f32(xk[e] * ik);
-    }
+    xq[e] *= iq;
+    xk[e] *= ik;
+  }
+  if (has) {
+    store_vec<IO, EPL>(qh + base, xq);
+    store_vec<IO, EPL>(kh + base, xk);
+    store_vec<float, EPL>(alpha + base, gl);
   }
   if (lane == 0) beta[row] = sigmoid_f(b[row]);
 }
@@ -131,30 +168,28 @@ kda_prologue_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
   const int row = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   if (row >= rows) return;
-  const size_t base = static_cast<size_t>(row) * DK;
-  float xq[EPL], xk[EPL], gq[EPL], gk[EPL];
+  const size_t base = static_cast<size_t>(row) * DK + lane * EPL;
+  const bool has = DK >= kWave || lane < DK;
+  float xq[EPL] = {}, xk[EPL] = {}, gq[EPL] = {}, gk[EPL] = {}, gl[EPL] = {}, da[EPL] = {};
+  if (has) {
+    load_vec<IO, EPL>(q + base, xq);
+    load_vec<IO, EPL>(k + base, xk);
+    load_vec<IO, EPL>(g + base, gl);
+    load_vec<float, EPL>(dqh + base, gq);
+    load_vec<float, EPL>(dkh + base, gk);
+    load_vec<float, EPL>(dalpha + base, da);
+  }
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    const int c = lane + kWave * e;
-    xq[e] = xk[e] = gq[e] = gk[e] = 0.f;
-    if (c < DK) {
-      xq[e] = Ty<IO>::to_f32(q[base + c]);
-      xk[e] = Ty<IO>::to_f32(k[base + c]);
-      gq[e] = dqh[base + c];
-      gk[e] = dkh[base + c];
-      const float a = gate_from_logit(Ty<IO>::to_f32(g[base + c]));
-      dg[base + c] = -dalpha[base + c] * a * (1.f - a);
-    }
+    const float a = gate_from_logit(gl[e]);
+    da[e] = -da[e] * a * (1.f - a);
   }
   feature_bwd<IO, EPL>(xq, gq, qk_map);
   feature_bwd<IO, EPL>(xk, gk, qk_map);
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const int c = lane + kWave * e;
-    if (c < DK) {
-      dq[base + c] = gq[e];
-      dk[base + c] = gk[e];
-    }
+  if (has) {
+    store_vec<float, EPL>(dq + base, gq);
+    store_vec<float, EPL>(dk + base, gk);
+    store_vec<float, EPL>(dg + base, da);
   }
   if (lane == 0) {
     const float be = sigmoid_f(b[row]);
