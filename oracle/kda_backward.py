@@ -37,7 +37,10 @@ q, k = normalize(phi(x))):
     silu:  d silu(x) / dx = sigmoid(x) (1 + x (1 - sigmoid(x)))
 
 and kda_prefill_backward_logits chains prologue, prefill backward and
-prologue backward.  Both are pinned against finite differences of the
+prologue backward.  gdn_prefill_backward is the prefill backward of Gated
+DeltaNet (one gate per token and head, broadcast over the key channels) and
+DeltaNet (no gate): the gate's gradient is the sum over the channels of the
+per-channel one.  Both are pinned against finite differences of the
 forward oracle in tests/test_backward_pins.py.
 
 kda_prefill_backward is that chain written out: the forward recurrence
@@ -49,11 +52,11 @@ from __future__ import annotations
 
 import numpy as np
 
-from .kda_oracle import as_f64, kda_decode_step
+from .kda_oracle import _channel_gate, as_f64, kda_decode_step
 from .kda_prologue import NORM_EPS, QK_AS_GIVEN, QK_L2, QK_SILU_L2, kda_prologue, sigmoid, silu
 
 __all__ = ["kda_decode_step_backward", "kda_prefill_backward", "kda_prologue_backward",
-           "kda_prefill_backward_logits"]
+           "kda_prefill_backward_logits", "gdn_prefill_backward"]
 
 
 def kda_decode_step_backward(q, k, v, alpha, beta, S, dO, dS_new):
@@ -146,3 +149,12 @@ def kda_prefill_backward_logits(q, k, v, g, b, S0, dO, dS_T, qk_map=QK_L2):
     dqh, dkh, dv, da, db_, dS0 = kda_prefill_backward(qn, kn, v, alpha, beta, S0, dO, dS_T)
     dq, dk, dg, db = kda_prologue_backward(q, k, g, b, dqh, dkh, da, db_, qk_map)
     return dq, dk, dv, dg, db, dS0
+
+
+def gdn_prefill_backward(q, k, v, a, beta, S0, dO, dS_T):
+    """Gradients of L through gdn_recurrence, float64.  a: [B, T, H] or None
+    (DeltaNet).  Returns (dq, dk, dv, da, dbeta, dS0); da is None when a is."""
+    k64 = as_f64(k)
+    dq, dk, dv, dalpha, dbeta, dS0 = kda_prefill_backward(q, k64, v, _channel_gate(a, k64), beta,
+                                                          S0, dO, dS_T)
+    return dq, dk, dv, (None if a is None else dalpha.sum(axis=-1)), dbeta, dS0

@@ -231,3 +231,53 @@ def _chain_mutant(kind):
 @pytest.mark.parametrize("kind", ["state_after", "drop_dST", "frozen_dS"])
 def test_prefill_pins_catch_planted_chain_mistake(kind):
     assert prefill_fd_error(_chain_mutant(kind)) > 1e-4
+
+
+# ------------------------------ Gated DeltaNet / DeltaNet prefill backward --
+#
+# oracle.gdn_prefill_backward against central finite differences of
+# oracle.gdn_recurrence (scalar gate per token and head, and no gate); the
+# gate's gradient summing the wrong axis must fail.
+
+from oracle import gdn_recurrence  # noqa: E402
+from oracle.kda_backward import gdn_prefill_backward  # noqa: E402
+
+
+def gdn_fd_error(backward, gated=True, seed=21, T=8):
+    r = np.random.default_rng(seed)
+    q, k, v, alpha, beta, S0 = pins.rand_case(seed, B=2, T=T, H=2, dk=4, dv=3)
+    a = r.uniform(0.3, 1.0, (2, T, 2)) if gated else None
+    dO = r.standard_normal((2, T, 2, 3))
+    dST = r.standard_normal((2, 2, 4, 3))
+
+    def loss(x):
+        o, S = gdn_recurrence(x["q"], x["k"], x["v"], x["a"], x["beta"], x["S0"])
+        return float(np.sum(dO * o) + np.sum(dST * S))
+
+    x = dict(q=q, k=k, v=v, a=a, beta=beta, S0=S0)
+    g = dict(zip(("q", "k", "v", "a", "beta", "S0"), backward(q, k, v, a, beta, S0, dO, dST)))
+    err = 0.0
+    for n in x:
+        if x[n] is None:
+            assert g[n] is None
+            continue
+        e = r.standard_normal(x[n].shape)
+        fd = (loss(dict(x, **{n: x[n] + H_FD * e})) - loss(dict(x, **{n: x[n] - H_FD * e}))) \
+            / (2 * H_FD)
+        err = max(err, abs(fd - float(np.sum(g[n] * e))) / max(abs(fd), 1e-3))
+    return err
+
+
+@pytest.mark.parametrize("gated", [True, False])
+def test_gdn_prefill_backward_matches_finite_differences(gated):
+    assert gdn_fd_error(gdn_prefill_backward, gated) < TOL
+
+
+def test_gdn_pins_catch_gate_gradient_on_the_wrong_axis():
+    def bwd(q, k, v, a, beta, S0, dO, dST):
+        dq, dk, dv, _, db, dS0 = kda_prefill_backward(q, k, v, np.broadcast_to(
+            a[..., None], q.shape), beta, S0, dO, dST)
+        _, _, _, dal, _, _ = kda_prefill_backward(q, k, v, np.broadcast_to(a[..., None], q.shape),
+                                                  beta, S0, dO, dST)
+        return dq, dk, dv, dal.mean(axis=-1), db, dS0     # mean instead of sum
+    assert gdn_fd_error(bwd) > 1e-4
