@@ -54,7 +54,7 @@ from ._lib import KDAError  # noqa: F401
 __all__ = ["prefill_chunked", "decode_step", "prefill_chunked_logits", "decode_step_logits",
            "gdn_prefill_chunked", "gdn_decode_step", "decode_step_backward",
            "prefill_backward", "prefill_backward_workspace_bytes", "prologue_forward",
-           "prologue_backward", "prefill_backward_logits",
+           "prologue_backward", "prefill_backward_logits", "gdn_prefill_backward",
            "prefill_workspace_bytes", "KDAError", "lib"]
 
 _DT = {torch.bfloat16: _lib.KDA_BF16, torch.float32: _lib.KDA_F32}
@@ -263,11 +263,7 @@ def prefill_backward_workspace_bytes(B, T, H, dk, dv) -> int:
     return int(lib().kda_prefill_backward_workspace_bytes(B, T, H, dk, dv))
 
 
-def prefill_backward(q, k, v, alpha, beta, dO, S0=None, dS_T=None):
-    """Gradients of a loss L through prefill_chunked: given dO = dL/do
-    [B,T,H,dv] (dtype of q) and, optionally, dS_T = dL/dS_T [B,H,dk,dv]
-    float32, returns (dq, dk, dv, dalpha, dbeta, dS0), all float32, shaped
-    like q, k, v, alpha, beta and the state."""
+def _prefill_backward(q, k, v, alpha, beta, dO, S0, dS_T, gdn):
     L = lib()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -276,30 +272,48 @@ def prefill_backward(q, k, v, alpha, beta, dO, S0=None, dS_T=None):
         raise TypeError(f"q: dtype {q.dtype} not supported")
     dt = q.dtype
     f32 = torch.float32
+    gate_shape = (B, T, H) if gdn else (B, T, H, dk)
     for n, t, d, s in (("q", q, dt, (B, T, H, dk)), ("k", k, dt, (B, T, H, dk)),
-                       ("v", v, dt, (B, T, H, dv)), ("alpha", alpha, f32, (B, T, H, dk)),
-                       ("beta", beta, f32, (B, T, H)), ("dO", dO, dt, (B, T, H, dv))):
+                       ("v", v, dt, (B, T, H, dv)), ("beta", beta, f32, (B, T, H)),
+                       ("dO", dO, dt, (B, T, H, dv))):
         _check(n, t, d, s, dev)
+    if alpha is not None or not gdn:
+        _check("a" if gdn else "alpha", alpha, f32, gate_shape, dev)
     for n, t in (("S0", S0), ("dS_T", dS_T)):
         if t is not None:
             _check(n, t, f32, (B, H, dk, dv), dev)
     g_q = torch.empty((B, T, H, dk), dtype=f32, device=dev)
     g_k = torch.empty((B, T, H, dk), dtype=f32, device=dev)
     g_v = torch.empty((B, T, H, dv), dtype=f32, device=dev)
-    g_a = torch.empty((B, T, H, dk), dtype=f32, device=dev)
+    g_a = None if alpha is None else torch.empty(gate_shape, dtype=f32, device=dev)
     g_b = torch.empty((B, T, H), dtype=f32, device=dev)
     g_S = torch.empty((B, H, dk, dv), dtype=f32, device=dev)
     nws = prefill_backward_workspace_bytes(B, T, H, dk, dv)
     if nws == (1 << 64) - 1:                      # (size_t)-1: sizes not supported
         raise KDAError(_lib.KDA_ERR_UNSUPPORTED, "kda_prefill_backward_workspace_bytes")
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
-    st = L.kda_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0),
-                                _ptr(dO), _ptr(dS_T), _ptr(g_q), _ptr(g_k), _ptr(g_v), _ptr(g_a),
-                                _ptr(g_b), _ptr(g_S), B, T, H, dk, dv, _DT[dt], _ptr(ws), nws,
-                                _stream(dev))
+    fn = L.kda_gdn_prefill_backward if gdn else L.kda_prefill_backward
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_T),
+            _ptr(g_q), _ptr(g_k), _ptr(g_v), _ptr(g_a), _ptr(g_b), _ptr(g_S), B, T, H, dk, dv,
+            _DT[dt], _ptr(ws), nws, _stream(dev))
     if st != _lib.KDA_OK:
-        raise KDAError(st, "kda_prefill_backward")
+        raise KDAError(st, "kda_gdn_prefill_backward" if gdn else "kda_prefill_backward")
     return g_q, g_k, g_v, g_a, g_b, g_S
+
+
+def prefill_backward(q, k, v, alpha, beta, dO, S0=None, dS_T=None):
+    """Gradients of a loss L through prefill_chunked: given dO = dL/do
+    [B,T,H,dv] (dtype of q) and, optionally, dS_T = dL/dS_T [B,H,dk,dv]
+    float32, returns (dq, dk, dv, dalpha, dbeta, dS0), all float32, shaped
+    like q, k, v, alpha, beta and the state."""
+    return _prefill_backward(q, k, v, alpha, beta, dO, S0, dS_T, gdn=False)
+
+
+def gdn_prefill_backward(q, k, v, a, beta, dO, S0=None, dS_T=None):
+    """Gradients through gdn_prefill_chunked (a [B,T,H] one gate per token
+    and head, or None for DeltaNet): (dq, dk, dv, da, dbeta, dS0), all
+    float32; da [B,T,H] is None when a is None."""
+    return _prefill_backward(q, k, v, a, beta, dO, S0, dS_T, gdn=True)
 
 
 def _prologue_rows(q, k, g, b):

@@ -284,18 +284,24 @@ size_t kda_prefill_backward_workspace_bytes(int B, int T, int H, int dk, int dv)
   return kda::prefill_backward_workspace(B, T, H, dk, dv);
 }
 
-kda_status kda_prefill_backward(const void* q, const void* k, const void* v, const float* alpha,
-                                const float* beta, const float* S0, const void* dO,
-                                const float* dS_T, float* dq, float* dk, float* dv,
-                                float* dalpha, float* dbeta, float* dS0, int B, int T, int H,
-                                int dk_, int dv_, kda_dtype dt, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+kda_status prefill_backward_impl(const void* q, const void* k, const void* v, const float* alpha,
+                                 const float* beta, const float* S0, const void* dO,
+                                 const float* dS_T, float* dq, float* dk, float* dv,
+                                 float* dalpha, float* dbeta, float* dS0, int B, int T, int H,
+                                 int dk_, int dv_, kda_dtype dt, void* workspace,
+                                 size_t workspace_bytes, void* stream, int gate_in) {
   if (B < 1 || H < 1 || T < 0) return KDA_ERR_SHAPE;
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   if (!dim_ok(dk_) || !dim_ok(dv_)) return KDA_ERR_UNSUPPORTED;
   const bool has_tokens = T > 0;
-  if (has_tokens && (!q || !k || !v || !alpha || !beta || !dO || !dq || !dk || !dv || !dalpha ||
-                     !dbeta))
+  // the scalar gate is optional (NULL: 1, DeltaNet); then so is its gradient
+  const bool scalar = gate_in == kda::kGateScalar;
+  if (has_tokens && (!q || !k || !v || (!alpha && !scalar) || !beta || !dO || !dq || !dk ||
+                     !dv || (!dalpha && !scalar) || !dbeta))
     return KDA_ERR_NULL;
   const void* ptrs[] = {q,  k,  v,      alpha, beta, S0,  dO,       dS_T,
                         dq, dk, dv, dalpha, dbeta, dS0, workspace};
@@ -309,10 +315,11 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
   const size_t nst = static_cast<size_t>(B) * H * dk_ * dv_ * 4;
   auto sp = [](const void* p, size_t n) { return p ? span(p, n) : Span{0, 0}; };
   const Span ins[] = {sp(q, ntok * dk_ * e),  sp(k, ntok * dk_ * e), sp(v, ntok * dv_ * e),
-                      sp(alpha, ntok * dk_ * 4), sp(beta, ntok * 4), sp(S0, nst),
+                      sp(alpha, ntok * (scalar ? 1 : dk_) * 4), sp(beta, ntok * 4), sp(S0, nst),
                       sp(dO, ntok * dv_ * e), sp(dS_T, nst)};
-  const Span outs[] = {sp(dq, ntok * dk_ * 4),     sp(dk, ntok * dk_ * 4), sp(dv, ntok * dv_ * 4),
-                       sp(dalpha, ntok * dk_ * 4), sp(dbeta, ntok * 4),    sp(dS0, nst),
+  const Span outs[] = {sp(dq, ntok * dk_ * 4), sp(dk, ntok * dk_ * 4), sp(dv, ntok * dv_ * 4),
+                       sp(dalpha, ntok * (scalar ? 1 : dk_) * 4), sp(dbeta, ntok * 4),
+                       sp(dS0, nst),
                        sp(workspace, ws_need)};
   constexpr int kIns = sizeof(ins) / sizeof(ins[0]), kOuts = sizeof(outs) / sizeof(outs[0]);
   for (int o = 0; o < kOuts; ++o) {
@@ -329,8 +336,36 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
   kda::PrefillBwdArgs a{q,  k,  v,      alpha, beta,      S0, dO, dS_T, dq, dk,
                         dv, dalpha, dbeta, dS0, workspace, B,  T,  H,    dk_, dv_,
                         dt == KDA_BF16, stream};
+  a.gate_in = gate_in;
+  if (scalar && !alpha) a.g_alpha = nullptr;   // DeltaNet: no gate, no gate gradient
   if (kda::launch_prefill_backward(a) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill_backward(const void* q, const void* k, const void* v, const float* alpha,
+                                const float* beta, const float* S0, const void* dO,
+                                const float* dS_T, float* dq, float* dk, float* dv,
+                                float* dalpha, float* dbeta, float* dS0, int B, int T, int H,
+                                int dk_, int dv_, kda_dtype dt, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return prefill_backward_impl(q, k, v, alpha, beta, S0, dO, dS_T, dq, dk, dv, dalpha, dbeta, dS0,
+                               B, T, H, dk_, dv_, dt, workspace, workspace_bytes, stream,
+                               kda::kGateAlpha);
+}
+
+kda_status kda_gdn_prefill_backward(const void* q, const void* k, const void* v, const float* a,
+                                    const float* beta, const float* S0, const void* dO,
+                                    const float* dS_T, float* dq, float* dk, float* dv,
+                                    float* da, float* dbeta, float* dS0, int B, int T, int H,
+                                    int dk_, int dv_, kda_dtype dt, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return prefill_backward_impl(q, k, v, a, beta, S0, dO, dS_T, dq, dk, dv, a ? da : nullptr,
+                               dbeta, dS0, B, T, H, dk_, dv_, dt, workspace, workspace_bytes,
+                               stream, kda::kGateScalar);
 }
 
 }  // extern "C"

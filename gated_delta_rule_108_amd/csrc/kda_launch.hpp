@@ -94,6 +94,7 @@ struct PrefillBwdArgs {
   int B, T, H, dk, dv;
   bool bf16;
   void* stream;
+  int gate_in = kGateAlpha;   // kGateScalar: alpha, g_alpha [B,T,H] (or both null)
 };
 hipError_t launch_prefill_backward(const PrefillBwdArgs& a);
 

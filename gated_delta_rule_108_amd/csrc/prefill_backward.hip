@@ -150,7 +150,7 @@ __device__ __forceinline__ void butterfly(float* a, int lane) {
 
 // Token rows of one piece of kCk tokens for the whole workgroup, loaded into
 // registers (one piece ahead) and then stored to LDS as float.
-template <typename IO, int DK, bool kBwd>
+template <typename IO, int DK, bool kBwd, int kIn>
 struct Stage {
   using E = typename Ty<IO>::Elem;
   static constexpr int VEC = Word<IO>::kVec;
@@ -183,7 +183,12 @@ struct Stage {
       const int e = (it * kThreads + tid) * 4, s = e / DK, c = e % DK;
       const bool ok = e < kCk * DK && s < n;
       const size_t off = (tok0 + static_cast<size_t>(s) * H) * DK + c;
-      ar[it] = ok ? *reinterpret_cast<const float4*>(alpha + off) : make_float4(0, 0, 0, 0);
+      if constexpr (kIn == kGateScalar) {   // one gate per token and head, or none (1)
+        const float a = ok ? (alpha ? alpha[tok0 + static_cast<size_t>(s) * H] : 1.f) : 0.f;
+        ar[it] = make_float4(a, a, a, a);
+      } else {
+        ar[it] = ok ? *reinterpret_cast<const float4*>(alpha + off) : make_float4(0, 0, 0, 0);
+      }
     }
     {
       const int s = tid / WGC, cc = tid % WGC;
@@ -265,7 +270,7 @@ __device__ __forceinline__ size_t ck_off(size_t chain, int piece, int npiece, in
   return ((chain * npiece + piece) * NWG + wg) * static_cast<size_t>(block);
 }
 
-template <typename IO, int DK>
+template <typename IO, int DK, int kIn>
 __global__ void __launch_bounds__(kThreads)
 kda_pb_forward_kernel(const typename Ty<IO>::Elem* __restrict__ k,
                       const typename Ty<IO>::Elem* __restrict__ v,
@@ -296,7 +301,7 @@ kda_pb_forward_kernel(const typename Ty<IO>::Elem* __restrict__ k,
 #pragma unroll
   for (int i = 0; i < RPT; ++i) S[i] = s0[(wave * RPT + i) * kWave + lane];
 
-  Stage<IO, DK, false> st;
+  Stage<IO, DK, false, kIn> st;
   auto tok0 = [&](int p) {
     return static_cast<size_t>(b) * T * H + static_cast<size_t>(p) * kCk * H + h;
   };
@@ -331,7 +336,7 @@ kda_pb_forward_kernel(const typename Ty<IO>::Elem* __restrict__ k,
   }
 }
 
-template <typename IO, int DK>
+template <typename IO, int DK, int kIn>
 __global__ void __launch_bounds__(kThreads)
 kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
                        const typename Ty<IO>::Elem* __restrict__ k,
@@ -362,6 +367,7 @@ kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
   // Plain stores (each slot has one writer); the flush adds the four waves.
   __shared__ float part[kWaves * kHalf * 3 * DK];
   __shared__ float partb[kWaves][kCk];                 // dbeta, per wave
+  __shared__ float parta[kWaves][kCk];                 // the scalar gate's gradient, per wave
   __shared__ float dvS[kHalf * WGC];                   // dv of the half piece, [token][column]
   float* mypart = part + wave * kHalf * 3 * DK;
   float* myhist = hist + wave * kCk * RPT * kWave;
@@ -378,7 +384,7 @@ kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
 #pragma unroll
   for (int i = 0; i < RPT; ++i) dS[i] = myhist[i * kWave + lane];
 
-  Stage<IO, DK, true> st;
+  Stage<IO, DK, true, kIn> st;
   auto tok0 = [&](int p) {
     return static_cast<size_t>(b) * T * H + static_cast<size_t>(p) * kCk * H + h;
   };
@@ -453,6 +459,13 @@ kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
         }
 #pragma unroll
         for (int m = NV; m < VP; ++m) val[m] = 0.f;
+        if constexpr (kIn == kGateScalar) {   // d(gate) = sum over the slab of dS' (.) S
+          float pa = 0.f;
+#pragma unroll
+          for (int i = 0; i < RPT; ++i) pa += val[3 * i + 2];
+          pa = col_sum<CPW>(row_sum<CPW>(pa));
+          if (lane == 0) parta[wave][s] = pa;
+        }
         butterfly<CPW, VP>(val, lane);
 #pragma unroll
         for (int w = 0; w < PER; ++w) {
@@ -472,6 +485,7 @@ kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
         const int x = x0 + tid;
         if (x < NSLOT) {
           const int qn = x / DK, c = x % DK;
+          if (kIn == kGateScalar && qn == 2) continue;   // the gate's gradient goes below
           float* dst = (qn == 0 ? g_q : (qn == 1 ? g_k : g_alpha)) + tok0(p) * DK + c;
           const size_t step = static_cast<size_t>(H) * DK;
 #pragma unroll
@@ -491,10 +505,15 @@ kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
         g_v[o] = dvS[tid];
       }
       if (tid >= lo && tid < hi) {
-        float sb = 0.f;
+        float sb = 0.f, sa = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) sb += partb[w][tid];
+        for (int w = 0; w < kWaves; ++w) {
+          sb += partb[w][tid];
+          sa += parta[w][tid];
+        }
         unsafeAtomicAdd(g_beta + tok0(p) + static_cast<size_t>(tid) * H, sb);
+        if (kIn == kGateScalar && g_alpha)
+          unsafeAtomicAdd(g_alpha + tok0(p) + static_cast<size_t>(tid) * H, sa);
       }
       __syncthreads();
     }
@@ -518,7 +537,7 @@ __global__ void zero_fill_kernel(float* a, size_t na, float* b, size_t nb, float
   }
 }
 
-template <typename IO, int DK>
+template <typename IO, int DK, int kIn>
 hipError_t run(const PrefillBwdArgs& a) {
   using E = typename Ty<IO>::Elem;
   constexpr int WGC = Geo<DK>::WGC;
@@ -533,15 +552,17 @@ hipError_t run(const PrefillBwdArgs& a) {
   if (a.T > 0) {
     const size_t nk = static_cast<size_t>(a.B) * a.T * a.H * a.dk;
     const size_t nb = static_cast<size_t>(a.B) * a.T * a.H;
-    const size_t tot = 3 * nk + nb;
+    const size_t tot = 3 * nk + 2 * nb;
     const size_t zb = (tot + 255) / 256;
     const unsigned zg = static_cast<unsigned>(zb < 4096 ? zb : 4096);
-    zero_fill_kernel<<<zg, 256, 0, stream>>>(a.g_q, nk, a.g_k, nk, a.g_alpha, nk, a.g_beta, nb);
-    kda_pb_forward_kernel<IO, DK><<<grid, kThreads, 0, stream>>>(
+    // the gate's gradient: one per channel, one per token and head, or none
+    const size_t na = kIn == kGateScalar ? (a.g_alpha ? nb : 0) : nk;
+    zero_fill_kernel<<<zg, 256, 0, stream>>>(a.g_q, nk, a.g_k, nk, a.g_alpha, na, a.g_beta, nb);
+    kda_pb_forward_kernel<IO, DK, kIn><<<grid, kThreads, 0, stream>>>(
         static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.alpha, a.beta, a.S0, ck, uw,
         rw, a.T, a.H, a.dv);
   }
-  kda_pb_backward_kernel<IO, DK><<<grid, kThreads, 0, stream>>>(
+  kda_pb_backward_kernel<IO, DK, kIn><<<grid, kThreads, 0, stream>>>(
       static_cast<const E*>(a.q), static_cast<const E*>(a.k), static_cast<const E*>(a.v),
       a.alpha, a.beta, static_cast<const E*>(a.dO), a.dS_T,
       ck, uw, rw, a.g_q, a.g_k, a.g_v, a.g_alpha, a.g_beta, a.g_S0,
@@ -549,13 +570,13 @@ hipError_t run(const PrefillBwdArgs& a) {
   return hipGetLastError();
 }
 
-template <typename IO>
+template <typename IO, int kIn>
 hipError_t run_dk(const PrefillBwdArgs& a) {
   switch (a.dk) {
-    case 16: return run<IO, 16>(a);
-    case 32: return run<IO, 32>(a);
-    case 64: return run<IO, 64>(a);
-    case 128: return run<IO, 128>(a);
+    case 16: return run<IO, 16, kIn>(a);
+    case 32: return run<IO, 32, kIn>(a);
+    case 64: return run<IO, 64, kIn>(a);
+    case 128: return run<IO, 128, kIn>(a);
     default: return hipErrorInvalidValue;
   }
 }
@@ -569,7 +590,10 @@ size_t prefill_backward_workspace(int B, int T, int H, int dk, int dv) {
 }
 
 hipError_t launch_prefill_backward(const PrefillBwdArgs& a) {
-  return a.bf16 ? run_dk<bf16_t>(a) : run_dk<float>(a);
+  if (a.gate_in == kGateScalar)
+    return a.bf16 ? run_dk<bf16_t, kGateScalar>(a) : run_dk<float, kGateScalar>(a);
+  if (a.gate_in != kGateAlpha) return hipErrorInvalidValue;
+  return a.bf16 ? run_dk<bf16_t, kGateAlpha>(a) : run_dk<float, kGateAlpha>(a);
 }
 
 }  // namespace kda

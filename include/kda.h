@@ -346,6 +346,22 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v,
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * kda_gdn_prefill_backward — kda_prefill_backward for Gated DeltaNet and
+ * DeltaNet (the recurrence of kda_gdn_prefill_chunked): the gate a [B, T, H]
+ * float32 is one value per token and head, the same on every key channel,
+ * or NULL for DeltaNet (gate 1).  Its gradient da [B, T, H] float32 is the
+ * sum over the key channels of the per-channel one; da is written when both
+ * a and da are given, and ignored otherwise.  Every other argument, the
+ * workspace and the errors are those of kda_prefill_backward.
+ */
+kda_status kda_gdn_prefill_backward(const void* q, const void* k, const void* v, const float* a,
+                                    const float* beta, const float* S0, const void* dO,
+                                    const float* dS_T, float* dq, float* dk, float* dv,
+                                    float* da, float* dbeta, float* dS0, int B, int T, int H,
+                                    int dk_, int dv_, kda_dtype dt, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
  * kda_prologue_forward — the input prologue of kda_prefill_chunked_logits on
  * its own, for training from raw projections: per row (one token of one
  * head) alpha = 1 / (1 + e^g) per key channel, beta = sigmoid(b), and q, k

@@ -25,10 +25,11 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_thirteen_calls():
+def test_header_declares_the_fourteen_calls():
     assert declared_functions() == ["kda_decode_step", "kda_decode_step_backward",
                                     "kda_decode_step_logits",
-                                    "kda_gdn_decode_step", "kda_gdn_prefill_chunked",
+                                    "kda_gdn_decode_step", "kda_gdn_prefill_backward",
+                                    "kda_gdn_prefill_chunked",
                                     "kda_prefill_backward", "kda_prefill_backward_workspace_bytes",
                                     "kda_prefill_chunked", "kda_prefill_chunked_logits",
                                     "kda_prefill_workspace_bytes", "kda_prologue_backward",
@@ -371,3 +372,32 @@ def test_prologue_validation():
     # an output right after an input's last byte is fine (bf16 q is rows*dk*2 bytes)
     assert pf(qh=addr(0) + rows * d * 2) in ok
     assert pf(qh=addr(0) + rows * d * 2 - 16) == L.KDA_ERR_ALIAS
+
+
+def test_gdn_prefill_backward_validation():
+    L = _lib()
+    lib = L.load()
+    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+    B, T, H, d = 1, 64, 2, 128
+    ws_need = lib.kda_prefill_backward_workspace_bytes(B, T, H, d, d)
+
+    def gb(**kw):
+        a = dict(q=addr(0), k=addr(1), v=addr(2), a=addr(3), beta=addr(4), S0=addr(5),
+                 dO=addr(6), dST=addr(7), dq=addr(8), dk=addr(9), dv=addr(10), da=addr(11),
+                 db=addr(12), dS0=addr(13), B=B, T=T, H=H, dk_=d, dv_=d, dt=1, ws=addr(14),
+                 wsb=ws_need, stream=None)
+        a.update(kw)
+        return lib.kda_gdn_prefill_backward(a["q"], a["k"], a["v"], a["a"], a["beta"], a["S0"],
+                                            a["dO"], a["dST"], a["dq"], a["dk"], a["dv"],
+                                            a["da"], a["db"], a["dS0"], a["B"], a["T"], a["H"],
+                                            a["dk_"], a["dv_"], a["dt"], a["ws"], a["wsb"],
+                                            a["stream"])
+
+    assert gb() in ok
+    assert gb(a=None, da=None) in ok                      # DeltaNet: no gate
+    assert gb(a=None) in ok                               # da ignored without a gate
+    # the gate and its gradient are B*T*H floats: an output right after them is fine
+    a_end = addr(3) + B * T * H * 4
+    assert gb(dq=a_end) in ok and gb(dq=a_end - 16) == L.KDA_ERR_ALIAS
+    assert gb(da=addr(12)) == L.KDA_ERR_ALIAS and gb(beta=None) == L.KDA_ERR_NULL
+    assert gb(ws=None) == L.KDA_ERR_WORKSPACE and gb(dk_=24) == L.KDA_ERR_UNSUPPORTED

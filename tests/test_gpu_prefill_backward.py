@@ -156,3 +156,29 @@ def test_state_gradient_in_place_through_the_abi():
     assert st == _lib.KDA_OK
     assert torch.equal(dS, ref[5])
     assert torch.equal(outs[2], ref[2])
+
+
+@pytest.mark.parametrize("gated,dk,dv,dtype,T", [(True, 64, 32, torch.float32, 37),
+                                                (True, 16, 16, torch.float32, 16),
+                                                (False, 32, 32, torch.float32, 41),
+                                                (True, 128, 128, torch.bfloat16, 70),
+                                                (False, 128, 128, torch.bfloat16, 33)])
+def test_gdn_backward(gated, dk, dv, dtype, T):
+    """Gated DeltaNet (one gate per token and head) and DeltaNet (no gate)
+    against oracle.gdn_prefill_backward."""
+    from oracle import gdn_prefill_backward
+    print(f"gdn backward gated={gated} dk={dk} dv={dv} {dtype} T={T}", flush=True)
+    spec = spec_of(dk, dv, dtype)
+    x = wl.make_gdn_inputs(spec, "cpu", T=T, B=2, H=2, gated=gated)
+    gr = wl.make_prefill_backward_grads(spec, "cpu", T=T, B=2, H=2)
+    g = {n: (None if t is None else t.to(DEV)) for n, t in {**x, **gr}.items()}
+    out = kda().gdn_prefill_backward(g["q"], g["k"], g["v"], g["a"], g["beta"], g["dO"],
+                                     S0=g["S0"], dS_T=g["dS_T"])
+    torch.cuda.synchronize()
+    ref = gdn_prefill_backward(*(f64(x[n]) for n in ("q", "k", "v", "a", "beta", "S0")),
+                               f64(gr["dO"]), f64(gr["dS_T"]))
+    names = ("dq", "dk", "dv", "da", "dbeta", "dS0")
+    assert (out[3] is None) == (ref[3] is None) == (not gated)
+    errs = {n: rel(f64(a), r) for n, a, r in zip(names, out, ref) if r is not None}
+    print("  " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()), flush=True)
+    assert all(e < TOL[dtype] for e in errs.values()), errs
