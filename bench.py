@@ -532,16 +532,25 @@ def extras(args, legs, out, torch, kda, wl, dev):
         ms_p, _ = time_launches(pbstep, 5, 1, torch)
         B, T, H, dk, dv = pspec.B, pspec.T, pspec.H, pspec.dk, pspec.dv
         pbytes = prefill_bwd_alg_bytes(B, T, H, dk, dv, 2)
+        gx = wl.make_gdn_inputs(pspec, dev)
+
+        def gbstep():
+            kda.gdn_prefill_backward(gx["q"], gx["k"], gx["v"], gx["a"], gx["beta"], pg["dO"],
+                                     S0=gx["S0"], dS_T=pg["dS_T"])
+
+        ms_g, _ = time_launches(gbstep, 5, 1, torch)
         out["prefill_bwd_h16_t4k"] = {
             "ms_per_call": ms_p, "tokens_per_s": B * T / (ms_p * 1e-3),
             "alg_GBps": pbytes / (ms_p * 1e-3) / 1e9,
             "frac_hbm": pbytes / (ms_p * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "alg_bytes_per_call": pbytes, "traffic": profiled_traffic("prefill_bwd_h16_t4k"),
+            "gdn_ms_per_call": ms_g,
             "note": "token-sequential walk per (head, 8-column slab): bound by the per-token "
                     "dependency chain, not by HBM; the chunked adjoint is the next step",
         }
-        print(f"# prefill_bwd_h16_t4k: {ms_p:.3f} ms/call", file=sys.stderr, flush=True)
-        del px, pg
+        print(f"# prefill_bwd_h16_t4k: {ms_p:.3f} ms/call (Gated DeltaNet {ms_g:.3f} ms)",
+              file=sys.stderr, flush=True)
+        del px, pg, gx
         torch.cuda.empty_cache()
 
     if "prologue" in legs:
