@@ -240,7 +240,7 @@ def main():
                          "1 GiB device-to-device copy used to calibrate HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
               "(chains are independent, so N GPUs would each run their own share).",
               file=sys.stderr)
         sys.exit(2)
