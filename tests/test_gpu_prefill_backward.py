@@ -182,3 +182,26 @@ def test_gdn_backward(gated, dk, dv, dtype, T):
     errs = {n: rel(f64(a), r) for n, a, r in zip(names, out, ref) if r is not None}
     print("  " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()), flush=True)
     assert all(e < TOL[dtype] for e in errs.values()), errs
+
+
+def test_largest_workload_sampled_chains():
+    """B = 8, H = 32, T = 8192, d = 128, bf16 (4096 workgroups in 16 rounds):
+    the whole launch on the GPU, the oracle on two chains (b, h) = (3, 17)
+    and (7, 0), each its own independent slice of the inputs."""
+    spec = wl.PREFILL["prefill_b8_h32_t8k"]
+    print(f"case {spec.name} full size", flush=True)
+    x = wl.make_prefill_inputs(spec, DEV)
+    gr = wl.make_prefill_backward_grads(spec, DEV)
+    out = kda().prefill_backward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], gr["dO"],
+                                 S0=x["S0"], dS_T=gr["dS_T"])
+    torch.cuda.synchronize()
+    for b, h in ((3, 17), (7, 0)):
+        tok = lambda t: f64(t[b:b + 1, :, h:h + 1])   # noqa: E731
+        st = lambda t: None if t is None else f64(t[b:b + 1, h:h + 1])   # noqa: E731
+        ref = kda_prefill_backward(tok(x["q"]), tok(x["k"]), tok(x["v"]), tok(x["alpha"]),
+                                   tok(x["beta"]), st(x["S0"]), tok(gr["dO"]), st(gr["dS_T"]))
+        got = [tok(t) for t in out[:5]] + [st(out[5])]
+        errs = {n: rel(a, r) for n, a, r in zip(NAMES, got, ref)}
+        print(f"  chain ({b},{h}): " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()),
+              flush=True)
+        assert all(e < TOL[spec.dtype] for e in errs.values()), errs
