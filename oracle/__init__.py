@@ -7,6 +7,7 @@ from .kda_oracle import (kda_recurrence, kda_decode_step, gdn_recurrence,  # noq
                          gdn_decode_step, as_f64)
 from .kda_prologue import (QK_AS_GIVEN, QK_L2, QK_SILU_L2, kda_prologue,  # noqa: F401
                            kda_recurrence_logits, kda_decode_step_logits)
-from .kda_backward import (gdn_prefill_backward, kda_decode_step_backward,  # noqa: F401
+from .kda_backward import (gdn_decode_step_backward, gdn_prefill_backward,  # noqa: F401
+                           kda_decode_step_backward,
                            kda_prefill_backward, kda_prefill_backward_logits,
                            kda_prologue_backward)

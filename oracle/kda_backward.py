@@ -56,7 +56,7 @@ from .kda_oracle import _channel_gate, as_f64, kda_decode_step
 from .kda_prologue import NORM_EPS, QK_AS_GIVEN, QK_L2, QK_SILU_L2, kda_prologue, sigmoid, silu
 
 __all__ = ["kda_decode_step_backward", "kda_prefill_backward", "kda_prologue_backward",
-           "kda_prefill_backward_logits", "gdn_prefill_backward"]
+           "kda_prefill_backward_logits", "gdn_prefill_backward", "gdn_decode_step_backward"]
 
 
 def kda_decode_step_backward(q, k, v, alpha, beta, S, dO, dS_new):
@@ -158,3 +158,12 @@ def gdn_prefill_backward(q, k, v, a, beta, S0, dO, dS_T):
     dq, dk, dv, dalpha, dbeta, dS0 = kda_prefill_backward(q, k64, v, _channel_gate(a, k64), beta,
                                                           S0, dO, dS_T)
     return dq, dk, dv, (None if a is None else dalpha.sum(axis=-1)), dbeta, dS0
+
+
+def gdn_decode_step_backward(q, k, v, a, beta, S, dO, dS_new):
+    """Adjoint of gdn_decode_step (a [N, H], or None for DeltaNet), float64.
+    Returns (dq, dk, dv, da, dbeta, dS); da is None when a is."""
+    k64 = as_f64(k)
+    dq, dk, dv, dalpha, dbeta, dS = kda_decode_step_backward(q, k64, v, _channel_gate(a, k64),
+                                                              beta, S, dO, dS_new)
+    return dq, dk, dv, (None if a is None else dalpha.sum(axis=-1)), dbeta, dS

@@ -281,3 +281,33 @@ def test_gdn_pins_catch_gate_gradient_on_the_wrong_axis():
                                                   beta, S0, dO, dST)
         return dq, dk, dv, dal.mean(axis=-1), db, dS0     # mean instead of sum
     assert gdn_fd_error(bwd) > 1e-4
+
+
+@pytest.mark.parametrize("gated", [True, False])
+def test_gdn_step_adjoint_matches_finite_differences(gated):
+    from oracle import gdn_decode_step
+    from oracle.kda_backward import gdn_decode_step_backward
+    r = np.random.default_rng(31)
+    N, H, dk, dv = 2, 3, 5, 4
+    k = r.standard_normal((N, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    x = dict(q=r.standard_normal((N, H, dk)), k=k, v=r.standard_normal((N, H, dv)),
+             a=r.uniform(0.3, 1.0, (N, H)) if gated else None, beta=r.uniform(0.1, 1.0, (N, H)),
+             S=r.standard_normal((N, H, dk, dv)))
+    dO, dSn = r.standard_normal((N, H, dv)), r.standard_normal((N, H, dk, dv))
+
+    def loss(y):
+        o, S_new = gdn_decode_step(y["q"], y["k"], y["v"], y["a"], y["beta"], y["S"])
+        return float(np.sum(dO * o) + np.sum(dSn * S_new))
+
+    g = dict(zip(("q", "k", "v", "a", "beta", "S"),
+                 gdn_decode_step_backward(x["q"], x["k"], x["v"], x["a"], x["beta"], x["S"], dO,
+                                          dSn)))
+    for n in x:
+        if x[n] is None:
+            assert g[n] is None
+            continue
+        e = r.standard_normal(x[n].shape)
+        fd = (loss(dict(x, **{n: x[n] + H_FD * e})) - loss(dict(x, **{n: x[n] - H_FD * e}))) \
+            / (2 * H_FD)
+        assert abs(fd - float(np.sum(g[n] * e))) / max(abs(fd), 1e-3) < TOL, n
