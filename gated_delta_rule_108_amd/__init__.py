@@ -55,6 +55,7 @@ __all__ = ["prefill_chunked", "decode_step", "prefill_chunked_logits", "decode_s
            "gdn_prefill_chunked", "gdn_decode_step", "decode_step_backward",
            "prefill_backward", "prefill_backward_workspace_bytes", "prologue_forward",
            "prologue_backward", "prefill_backward_logits", "gdn_prefill_backward",
+           "gdn_decode_step_backward",
            "prefill_workspace_bytes", "KDAError", "lib"]
 
 _DT = {torch.bfloat16: _lib.KDA_BF16, torch.float32: _lib.KDA_F32}
@@ -226,11 +227,7 @@ def _decode(q, k, v, gate, beta, S, out, state_out, qk):
     return o, S_out
 
 
-def decode_step_backward(q, k, v, alpha, beta, S, dO, dS_new, in_place=False):
-    """Adjoint of decode_step: given dO = dL/do [N,H,dv] (dtype of q) and
-    dS_new = dL/dS after the step [N,H,dk,dv] float32, returns (dq, dk, dv,
-    dalpha, dbeta, dS) with dS = dL/dS before the step; in_place=True writes
-    dS over dS_new."""
+def _step_backward(q, k, v, alpha, beta, S, dO, dS_new, in_place, gdn):
     L = lib()
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -238,25 +235,41 @@ def decode_step_backward(q, k, v, alpha, beta, S, dO, dS_new, in_place=False):
     if q.dtype not in _DT:
         raise TypeError(f"q: dtype {q.dtype} not supported")
     dt = q.dtype
+    gate_shape = (N, H) if gdn else (N, H, dk)
     for n, t, d, s in (("q", q, dt, (N, H, dk)), ("k", k, dt, (N, H, dk)), ("v", v, dt, (N, H, dv)),
-                       ("alpha", alpha, torch.float32, (N, H, dk)),
                        ("beta", beta, torch.float32, (N, H)),
                        ("S", S, torch.float32, (N, H, dk, dv)), ("dO", dO, dt, (N, H, dv)),
                        ("dS_new", dS_new, torch.float32, (N, H, dk, dv))):
         _check(n, t, d, s, dev)
+    if alpha is not None or not gdn:
+        _check("a" if gdn else "alpha", alpha, torch.float32, gate_shape, dev)
     g_q = torch.empty((N, H, dk), dtype=dt, device=dev)
     g_k = torch.empty((N, H, dk), dtype=dt, device=dev)
     g_v = torch.empty((N, H, dv), dtype=dt, device=dev)
-    g_a = torch.empty((N, H, dk), dtype=torch.float32, device=dev)
+    g_a = None if alpha is None else torch.empty(gate_shape, dtype=torch.float32, device=dev)
     g_b = torch.empty((N, H), dtype=torch.float32, device=dev)
     g_S = dS_new if in_place else torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    st = L.kda_decode_step_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S),
-                                    _ptr(dO), _ptr(dS_new), _ptr(g_q), _ptr(g_k), _ptr(g_v),
-                                    _ptr(g_a), _ptr(g_b), _ptr(g_S), N, H, dk, dv, _DT[dt],
-                                    _stream(dev))
+    fn = L.kda_gdn_decode_step_backward if gdn else L.kda_decode_step_backward
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S), _ptr(dO), _ptr(dS_new),
+            _ptr(g_q), _ptr(g_k), _ptr(g_v), _ptr(g_a), _ptr(g_b), _ptr(g_S), N, H, dk, dv, _DT[dt],
+            _stream(dev))
     if st != _lib.KDA_OK:
-        raise KDAError(st, "kda_decode_step_backward")
+        raise KDAError(st, "kda_gdn_decode_step_backward" if gdn else "kda_decode_step_backward")
     return g_q, g_k, g_v, g_a, g_b, g_S
+
+
+def decode_step_backward(q, k, v, alpha, beta, S, dO, dS_new, in_place=False):
+    """Adjoint of decode_step: given dO = dL/do [N,H,dv] (dtype of q) and
+    dS_new = dL/dS after the step [N,H,dk,dv] float32, returns (dq, dk, dv,
+    dalpha, dbeta, dS) with dS = dL/dS before the step; in_place=True writes
+    dS over dS_new."""
+    return _step_backward(q, k, v, alpha, beta, S, dO, dS_new, in_place, gdn=False)
+
+
+def gdn_decode_step_backward(q, k, v, a, beta, S, dO, dS_new, in_place=False):
+    """Adjoint of gdn_decode_step (a [N,H] one gate per head, or None for
+    DeltaNet): (dq, dk, dv, da, dbeta, dS); da [N,H] is None when a is None."""
+    return _step_backward(q, k, v, a, beta, S, dO, dS_new, in_place, gdn=True)
 
 
 def prefill_backward_workspace_bytes(B, T, H, dk, dv) -> int:

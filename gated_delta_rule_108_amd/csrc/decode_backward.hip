@@ -77,7 +77,9 @@ __device__ __forceinline__ void store_nt(float* p, float a, float b, float c, fl
   __builtin_nontemporal_store(t, reinterpret_cast<f4v*>(p));
 }
 
-template <typename IO, int DK, int DV>
+// kIn: kGateAlpha (one gate per key channel) or kGateScalar (one per head,
+// or none: Gated DeltaNet / DeltaNet; its gradient is the sum over the rows).
+template <typename IO, int DK, int DV, int kIn>
 __global__ void __launch_bounds__(256)   // BwdCfg::NTH <= 256
 kda_decode_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
                            const typename Ty<IO>::Elem* __restrict__ k,
@@ -113,7 +115,10 @@ kda_decode_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
   // Row vectors (gate, key, query) once per workgroup, by thread r.
   __shared__ float pro[3][DK];
   if (tid < DK) {
-    pro[0][tid] = alpha[static_cast<size_t>(nh) * DK + tid];
+    if constexpr (kIn == kGateScalar)
+      pro[0][tid] = alpha ? alpha[nh] : 1.f;
+    else
+      pro[0][tid] = alpha[static_cast<size_t>(nh) * DK + tid];
     pro[1][tid] = Ty<IO>::to_f32(k[static_cast<size_t>(nh) * DK + tid]);
     pro[2][tid] = Ty<IO>::to_f32(q[static_cast<size_t>(nh) * DK + tid]);
   }
@@ -185,6 +190,7 @@ kda_decode_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
   if (tid == 0) dbeta[nh] = pb;
 
   // ---- per element, then row sums over the value columns
+  float ta = 0.f;   // scalar gate: this row group's share of sum_c dalpha_c
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rg + RG * i;
@@ -207,21 +213,37 @@ kda_decode_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
     pq = sum_row_group<CG>(pq);
     pk = sum_row_group<CG>(pk);
     pa = sum_row_group<CG>(pa);
+    ta += pa;
     if (cg == 0) {
       const size_t ro = static_cast<size_t>(nh) * DK + r;
       dq[ro] = Ty<IO>::from_f32(pq);
       dk[ro] = Ty<IO>::from_f32(pk);
-      dalpha[ro] = pa;
+      if constexpr (kIn != kGateScalar) dalpha[ro] = pa;
+    }
+  }
+  if constexpr (kIn == kGateScalar) {
+    // the rows' sum: over the row groups of the wave (lanes CG apart), then
+    // over the waves through LDS
+#pragma unroll
+    for (int off = CG; off < kWave; off <<= 1) ta += __shfl_xor(ta, off);
+    __shared__ float reda[NWV];
+    if (lane == 0) reda[wave] = ta;
+    __syncthreads();
+    if (tid == 0 && dalpha) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) t += reda[w];
+      dalpha[nh] = t;
     }
   }
 }
 
-template <typename IO, int DK, int DV>
+template <typename IO, int DK, int DV, int kIn>
 static hipError_t launch_bwd(const DecodeBwdArgs& a) {
   using Cf = BwdCfg<DK, DV>;
   using E = typename Ty<IO>::Elem;
   const long nh = static_cast<long>(a.N) * a.H;
-  hipLaunchKernelGGL((kda_decode_backward_kernel<IO, DK, DV>), dim3(static_cast<unsigned>(nh)),
+  hipLaunchKernelGGL((kda_decode_backward_kernel<IO, DK, DV, kIn>), dim3(static_cast<unsigned>(nh)),
                      dim3(Cf::NTH), 0, static_cast<hipStream_t>(a.stream),
                      static_cast<const E*>(a.q), static_cast<const E*>(a.k),
                      static_cast<const E*>(a.v), a.alpha, a.beta, a.S_in,
@@ -230,30 +252,33 @@ static hipError_t launch_bwd(const DecodeBwdArgs& a) {
   return hipGetLastError();
 }
 
-template <typename IO, int DK>
+template <typename IO, int DK, int kIn>
 static hipError_t bwd_dv(const DecodeBwdArgs& a) {
   switch (a.dv) {
-    case 16: return launch_bwd<IO, DK, 16>(a);
-    case 32: return launch_bwd<IO, DK, 32>(a);
-    case 64: return launch_bwd<IO, DK, 64>(a);
-    case 128: return launch_bwd<IO, DK, 128>(a);
+    case 16: return launch_bwd<IO, DK, 16, kIn>(a);
+    case 32: return launch_bwd<IO, DK, 32, kIn>(a);
+    case 64: return launch_bwd<IO, DK, 64, kIn>(a);
+    case 128: return launch_bwd<IO, DK, 128, kIn>(a);
   }
   return hipErrorInvalidValue;
 }
 
-template <typename IO>
+template <typename IO, int kIn>
 static hipError_t bwd_dk(const DecodeBwdArgs& a) {
   switch (a.dk) {
-    case 16: return bwd_dv<IO, 16>(a);
-    case 32: return bwd_dv<IO, 32>(a);
-    case 64: return bwd_dv<IO, 64>(a);
-    case 128: return bwd_dv<IO, 128>(a);
+    case 16: return bwd_dv<IO, 16, kIn>(a);
+    case 32: return bwd_dv<IO, 32, kIn>(a);
+    case 64: return bwd_dv<IO, 64, kIn>(a);
+    case 128: return bwd_dv<IO, 128, kIn>(a);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_backward(const DecodeBwdArgs& a) {
-  return a.bf16 ? bwd_dk<bf16_t>(a) : bwd_dk<float>(a);
+  if (a.gate_in == kGateScalar)
+    return a.bf16 ? bwd_dk<bf16_t, kGateScalar>(a) : bwd_dk<float, kGateScalar>(a);
+  if (a.gate_in != kGateAlpha) return hipErrorInvalidValue;
+  return a.bf16 ? bwd_dk<bf16_t, kGateAlpha>(a) : bwd_dk<float, kGateAlpha>(a);
 }
 
 }  // namespace kda

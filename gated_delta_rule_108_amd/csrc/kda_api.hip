@@ -241,27 +241,35 @@ kda_status kda_gdn_decode_step(const void* q, const void* k, const void* v, cons
                      stream);
 }
 
-kda_status kda_decode_step_backward(const void* q, const void* k, const void* v,
-                                    const float* alpha, const float* beta, const float* S_in,
-                                    const void* dO, const float* dS_new, void* dq, void* dk,
-                                    void* dv, float* dalpha, float* dbeta, float* dS, int N, int H,
-                                    int dk_, int dv_, kda_dtype dt, void* stream) {
+}  // extern "C"
+
+namespace {
+
+kda_status decode_backward_impl(const void* q, const void* k, const void* v, const float* alpha,
+                                const float* beta, const float* S_in, const void* dO,
+                                const float* dS_new, void* dq, void* dk, void* dv,
+                                float* dalpha, float* dbeta, float* dS, int N, int H, int dk_,
+                                int dv_, kda_dtype dt, void* stream, int gate_in) {
   if (N < 1 || H < 1) return KDA_ERR_SHAPE;
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   if (!dim_ok(dk_) || !dim_ok(dv_)) return KDA_ERR_UNSUPPORTED;
+  // the scalar gate is optional (NULL: 1, DeltaNet); then so is its gradient
+  const bool scalar = gate_in == kda::kGateScalar;
   const void* ptrs[] = {q, k, v, alpha, beta, S_in, dO, dS_new, dq, dk, dv, dalpha, dbeta, dS};
   for (const void* p : ptrs) {
-    if (!p) return KDA_ERR_NULL;
-    if (!aligned16(p)) return KDA_ERR_ALIGN;
+    const bool optional = scalar && (p == alpha || p == dalpha);
+    if (!p && !optional) return KDA_ERR_NULL;
+    if (p && !aligned16(p)) return KDA_ERR_ALIGN;
   }
   const size_t e = (dt == KDA_BF16) ? 2 : 4;
   const size_t nh = static_cast<size_t>(N) * H;
   const size_t nst = nh * dk_ * dv_ * 4;
+  auto sp = [](const void* p, size_t n) { return p ? span(p, n) : Span{0, 0}; };
   const Span ins[] = {span(q, nh * dk_ * e), span(k, nh * dk_ * e), span(v, nh * dv_ * e),
-                      span(alpha, nh * dk_ * 4), span(beta, nh * 4), span(S_in, nst),
+                      sp(alpha, nh * (scalar ? 1 : dk_) * 4), span(beta, nh * 4), span(S_in, nst),
                       span(dO, nh * dv_ * e), span(dS_new, nst)};
   const Span outs[] = {span(dq, nh * dk_ * e), span(dk, nh * dk_ * e), span(dv, nh * dv_ * e),
-                       span(dalpha, nh * dk_ * 4), span(dbeta, nh * 4), span(dS, nst)};
+                       sp(dalpha, nh * (scalar ? 1 : dk_) * 4), span(dbeta, nh * 4), span(dS, nst)};
   constexpr int kIns = sizeof(ins) / sizeof(ins[0]), kOuts = sizeof(outs) / sizeof(outs[0]);
   for (int o = 0; o < kOuts; ++o) {
     for (int i = 0; i < kIns; ++i) {
@@ -275,13 +283,38 @@ kda_status kda_decode_step_backward(const void* q, const void* k, const void* v,
   if (dev != KDA_OK) return dev;
   kda::DecodeBwdArgs a{q,  k,  v,  alpha,  beta,  S_in, dO, dS_new, dq,  dk,
                        dv, dalpha, dbeta, dS, N, H, dk_, dv_, dt == KDA_BF16, stream};
+  a.gate_in = gate_in;
+  if (scalar && !alpha) a.g_alpha = nullptr;   // DeltaNet: no gate, no gate gradient
   if (kda::launch_decode_backward(a) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
 }
 
+
+}  // namespace
+
+extern "C" {
+
 size_t kda_prefill_backward_workspace_bytes(int B, int T, int H, int dk, int dv) {
   if (B < 1 || H < 1 || T < 0 || !dim_ok(dk) || !dim_ok(dv)) return static_cast<size_t>(-1);
   return kda::prefill_backward_workspace(B, T, H, dk, dv);
+}
+
+kda_status kda_decode_step_backward(const void* q, const void* k, const void* v,
+                                    const float* alpha, const float* beta, const float* S_in,
+                                    const void* dO, const float* dS_new, void* dq, void* dk,
+                                    void* dv, float* dalpha, float* dbeta, float* dS, int N, int H,
+                                    int dk_, int dv_, kda_dtype dt, void* stream) {
+  return decode_backward_impl(q, k, v, alpha, beta, S_in, dO, dS_new, dq, dk, dv, dalpha, dbeta,
+                              dS, N, H, dk_, dv_, dt, stream, kda::kGateAlpha);
+}
+
+kda_status kda_gdn_decode_step_backward(const void* q, const void* k, const void* v,
+                                        const float* a, const float* beta, const float* S_in,
+                                        const void* dO, const float* dS_new, void* dq, void* dk,
+                                        void* dv, float* da, float* dbeta, float* dS, int N,
+                                        int H, int dk_, int dv_, kda_dtype dt, void* stream) {
+  return decode_backward_impl(q, k, v, a, beta, S_in, dO, dS_new, dq, dk, dv, a ? da : nullptr,
+                              dbeta, dS, N, H, dk_, dv_, dt, stream, kda::kGateScalar);
 }
 
 }  // extern "C"

@@ -69,6 +69,7 @@ struct DecodeBwdArgs {
   int N, H, dk, dv;
   bool bf16;
   void* stream;
+  int gate_in = kGateAlpha;   // kGateScalar: alpha, g_alpha [N,H] (or both null)
 };
 
 hipError_t launch_decode(const DecodeArgs& a);

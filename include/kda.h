@@ -346,6 +346,20 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v,
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * kda_gdn_decode_step_backward — kda_decode_step_backward for Gated
+ * DeltaNet and DeltaNet (the step of kda_gdn_decode_step): the gate a [N, H]
+ * float32 is one value per head, or NULL (gate 1).  Its gradient da [N, H]
+ * float32 is the sum over the key channels of the per-channel one; da is
+ * written when both a and da are given, and ignored otherwise.  Every other
+ * argument and the errors are those of kda_decode_step_backward.
+ */
+kda_status kda_gdn_decode_step_backward(const void* q, const void* k, const void* v,
+                                        const float* a, const float* beta, const float* S_in,
+                                        const void* dO, const float* dS_new, void* dq, void* dk,
+                                        void* dv, float* da, float* dbeta, float* dS, int N,
+                                        int H, int dk_, int dv_, kda_dtype dt, void* stream);
+
+/*
  * kda_gdn_prefill_backward — kda_prefill_backward for Gated DeltaNet and
  * DeltaNet (the recurrence of kda_gdn_prefill_chunked): the gate a [B, T, H]
  * float32 is one value per token and head, the same on every key channel,

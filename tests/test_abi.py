@@ -25,10 +25,11 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_fourteen_calls():
+def test_header_declares_the_fifteen_calls():
     assert declared_functions() == ["kda_decode_step", "kda_decode_step_backward",
                                     "kda_decode_step_logits",
-                                    "kda_gdn_decode_step", "kda_gdn_prefill_backward",
+                                    "kda_gdn_decode_step", "kda_gdn_decode_step_backward",
+                                    "kda_gdn_prefill_backward",
                                     "kda_gdn_prefill_chunked",
                                     "kda_prefill_backward", "kda_prefill_backward_workspace_bytes",
                                     "kda_prefill_chunked", "kda_prefill_chunked_logits",
@@ -401,3 +402,24 @@ def test_gdn_prefill_backward_validation():
     assert gb(dq=a_end) in ok and gb(dq=a_end - 16) == L.KDA_ERR_ALIAS
     assert gb(da=addr(12)) == L.KDA_ERR_ALIAS and gb(beta=None) == L.KDA_ERR_NULL
     assert gb(ws=None) == L.KDA_ERR_WORKSPACE and gb(dk_=24) == L.KDA_ERR_UNSUPPORTED
+
+
+def test_gdn_step_backward_validation():
+    L = _lib()
+    lib = L.load()
+    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+
+    def gs(**kw):
+        a = dict(q=addr(0), k=addr(1), v=addr(2), a=addr(3), beta=addr(4), S=addr(5),
+                 dO=addr(6), dSn=addr(7), dq=addr(8), dk=addr(9), dv=addr(10), da=addr(11),
+                 db=addr(12), dS=addr(13), N=4, H=2, dk_=128, dv_=128, dt=1, stream=None)
+        a.update(kw)
+        return lib.kda_gdn_decode_step_backward(a["q"], a["k"], a["v"], a["a"], a["beta"],
+                                                a["S"], a["dO"], a["dSn"], a["dq"], a["dk"],
+                                                a["dv"], a["da"], a["db"], a["dS"], a["N"],
+                                                a["H"], a["dk_"], a["dv_"], a["dt"], a["stream"])
+
+    assert gs() in ok and gs(a=None, da=None) in ok and gs(dS=addr(7)) in ok
+    a_end = addr(3) + 4 * 2 * 4                            # one gate per head
+    assert gs(dq=a_end) in ok and gs(dq=a_end - 16) == L.KDA_ERR_ALIAS
+    assert gs(beta=None) == L.KDA_ERR_NULL and gs(da=addr(11) + 4) == L.KDA_ERR_ALIGN

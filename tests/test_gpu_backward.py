@@ -109,3 +109,29 @@ def test_chained_steps_give_the_sequence_gradient():
     es = rel(f64(dS_g), dS_r)
     print(f"[chained adjoint T={T}] worst per-token rel={worst:.2e} dS0 rel={es:.2e}", flush=True)
     assert worst < 1e-4 and es < 1e-4
+
+
+@pytest.mark.parametrize("gated,dk,dv,N,H,dtype", [
+    (True, 16, 16, 3, 2, torch.float32), (True, 128, 32, 2, 3, torch.float32),
+    (False, 64, 128, 2, 2, torch.float32), (True, 128, 128, 4, 8, torch.bfloat16),
+    (False, 32, 64, 3, 3, torch.bfloat16),
+])
+def test_gdn_step_adjoint(gated, dk, dv, N, H, dtype):
+    """Gated DeltaNet (one gate per head) and DeltaNet (none) against
+    oracle.gdn_decode_step_backward; the gate's gradient sums every row of
+    the head."""
+    from oracle import gdn_decode_step_backward
+    x = make(dk + dv + N + 7, N, H, dk, dv, dtype)
+    a = (0.8 + 0.2 * torch.rand(N, H, generator=torch.Generator().manual_seed(N))) if gated \
+        else None
+    d = {k: t.to(DEV) for k, t in x.items()}
+    got = kda().gdn_decode_step_backward(d["q"], d["k"], d["v"], None if a is None else a.to(DEV),
+                                         d["beta"], d["S"], d["dO"], d["dS_new"])
+    torch.cuda.synchronize()
+    ref = gdn_decode_step_backward(x["q"], x["k"], x["v"], a, x["beta"], x["S"], x["dO"],
+                                   x["dS_new"])
+    assert (got[3] is None) == (ref[3] is None) == (not gated)
+    errs = {n: rel(f64(g), r) for n, g, r in zip(NAMES, got, ref) if r is not None}
+    print(f"[gdn step adjoint gated={gated} dk={dk} dv={dv} {dtype}] " +
+          " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    assert max(errs.values()) < TOL[dtype], errs
