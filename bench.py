@@ -509,14 +509,22 @@ def extras(args, legs, out, torch, kda, wl, dev):
 
         ms_b, _ = time_launches(bstep, max(args.steps, 20), args.warmup, torch)
         bbytes = decode_bwd_alg_bytes(dspec.N, dspec.H, dspec.dk, dspec.dv, 2)
+        ga = st["alpha"][..., 0].contiguous()            # one gate per head
+
+        def gstep():
+            kda.gdn_decode_step_backward(st["q"], st["k"], st["v"], ga, st["beta"], S, dO, gS,
+                                         in_place=True)
+
+        ms_gb, _ = time_launches(gstep, max(args.steps, 20), args.warmup, torch)
         out["decode_bwd_n256_h32"] = {
             "us_per_step": ms_b * 1e3, "alg_GBps": bbytes / (ms_b * 1e-3) / 1e9,
             "frac_hbm": bbytes / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "traffic": profiled_traffic("decode_bwd_n256_h32"), "alg_bytes_per_step": bbytes,
+            "gdn_us_per_step": ms_gb * 1e3,
         }
         print(f"# decode_bwd_n256_h32: {ms_b * 1e3:.1f} us/step, "
               f"{out['decode_bwd_n256_h32']['alg_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
-        del S, gS, st, dO
+        del S, gS, st, dO, ga
         torch.cuda.empty_cache()
 
     if "prefill_bwd" in legs:
