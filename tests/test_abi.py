@@ -1,12 +1,54 @@
 """The C ABI on the CPU: the library loads, exports every entry point that
 include/kda.h declares, and rejects bad arguments on the host before any GPU
 call (no pointer is dereferenced, so fake aligned addresses are enough).
+
+Cases whose arguments pass validation would, on a machine with a GPU, launch
+kernels on those fake addresses.  They run only where no GPU is visible (the
+GPU-less build container): every such call goes through `may_launch`, which
+skips the test when a GPU is visible, and the tests holding them carry the
+same skip.  Real-buffer versions of those cases are in test_gpu_abi.py.
 """
 import ctypes
 import os
 import re
 
 import pytest
+
+
+def gpu_visible():
+    """True when a GPU could run a kernel launched from this process.
+
+    KDA_TEST_ASSUME_GPU=1 forces True (to check, on a GPU-less machine, that
+    every launching case is skipped)."""
+    if os.environ.get("KDA_TEST_ASSUME_GPU") == "1":
+        return True
+    try:
+        import torch
+        if torch.cuda.device_count() > 0:   # counts devices without initialising them
+            return True
+    except Exception:
+        pass
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        n = ctypes.c_int(0)
+        if hip.hipGetDeviceCount(ctypes.byref(n)) == 0 and n.value > 0:
+            return True
+    except OSError:
+        pass
+    return False
+
+
+HOST_ONLY_REASON = ("fake device addresses pass validation here: with a GPU visible the call "
+                    "would launch kernels on them (real-buffer cases: test_gpu_abi.py)")
+host_only = pytest.mark.skipif(gpu_visible(), reason=HOST_ONLY_REASON)
+
+
+def may_launch(call, **kw):
+    """A call whose arguments are valid: it reaches the device check and, on a
+    GPU, a launch.  Never made where a GPU is visible."""
+    if gpu_visible():
+        pytest.skip(HOST_ONLY_REASON)
+    return call(**kw)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
@@ -99,6 +141,7 @@ def test_prefill_validation_errors():
     assert prefill(lib, S_T=addr(1)) == L.KDA_ERR_ALIAS          # S_T on top of k
 
 
+@host_only
 def test_prefill_valid_arguments_reach_the_device_check():
     L = _lib()
     lib = L.load()
@@ -106,7 +149,7 @@ def test_prefill_valid_arguments_reach_the_device_check():
     # a machine without a GPU the call then fails at the device query.
     for kw in (dict(), dict(S_T=addr(5)), dict(S0=None),
                dict(T=0, q=None, k=None, v=None, alpha=None, beta=None, o=None)):
-        st = prefill(lib, **kw)
+        st = may_launch(prefill, lib=lib, **kw)
         assert st in (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE), (kw, st)
 
 
@@ -120,7 +163,14 @@ def test_decode_validation_errors():
     assert decode(lib, o=addr(2)) == L.KDA_ERR_ALIAS
     assert decode(lib, S_out=addr(5) + 64) == L.KDA_ERR_ALIAS
     assert decode(lib, S_out=addr(3)) == L.KDA_ERR_ALIAS
-    assert decode(lib, S_out=addr(7)) in (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+
+
+@host_only
+def test_decode_valid_arguments_reach_the_device_check():
+    L = _lib()
+    lib = L.load()
+    assert may_launch(decode, lib=lib, S_out=addr(7)) in (L.KDA_OK, L.KDA_ERR_HIP,
+                                                          L.KDA_ERR_DEVICE)
 
 
 def test_prefill_workspace_errors():
@@ -133,7 +183,14 @@ def test_prefill_workspace_errors():
     assert prefill(lib, wsb=need - 1) == L.KDA_ERR_WORKSPACE
     assert prefill(lib, ws=addr(8) + 8) == L.KDA_ERR_ALIGN
     assert prefill(lib, ws=addr(2)) == L.KDA_ERR_ALIAS              # workspace on top of v
-    assert prefill(lib, wsb=need) in (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+
+
+@host_only
+def test_prefill_exact_workspace_reaches_the_device_check():
+    L = _lib()
+    lib = L.load()
+    need = lib.kda_prefill_workspace_bytes(1, 64, 2, 128, 128, 64, 1)
+    assert may_launch(prefill, lib=lib, wsb=need) in (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
 
 
 def test_workspace_query():
@@ -217,65 +274,82 @@ def test_logits_entry_points_validate_like_the_plain_ones():
     ntok = 1 * 64 * 2
     g_end = addr(3) + ntok * 128 * 2
     assert prefill_logits(lib, o=g_end - 16) == L.KDA_ERR_ALIAS
-    assert prefill_logits(lib, o=g_end) in (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
     assert prefill_logits(lib, o=g_end, dt=0, C=32) == L.KDA_ERR_ALIAS   # fp32: 4 bytes each
-    for qk in (0, 1, 2):
-        assert prefill_logits(lib, qk=qk) in (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
-        assert decode_logits(lib, qk=qk) in (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
 
 
-def test_gdn_entry_points_take_a_null_gate_and_validate():
+@host_only
+def test_logits_entry_points_valid_arguments():
     L = _lib()
     lib = L.load()
     ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+    g_end = addr(3) + 1 * 64 * 2 * 128 * 2   # just past the bf16 gate logits
+    assert may_launch(prefill_logits, lib=lib, o=g_end) in ok
+    for qk in (0, 1, 2):
+        assert may_launch(prefill_logits, lib=lib, qk=qk) in ok
+        assert may_launch(decode_logits, lib=lib, qk=qk) in ok
 
-    def gp(**kw):
-        a = dict(q=addr(0), k=addr(1), v=addr(2), a=addr(3), beta=addr(4), S0=addr(5),
-                 o=addr(6), S_T=addr(7), B=1, T=64, H=2, dk=128, dv=128, C=64, dt=1,
-                 ws=addr(8), wsb=1 << 34, stream=None)
-        a.update(kw)
-        return lib.kda_gdn_prefill_chunked(a["q"], a["k"], a["v"], a["a"], a["beta"], a["S0"],
-                                           a["o"], a["S_T"], a["B"], a["T"], a["H"], a["dk"],
-                                           a["dv"], a["C"], a["dt"], a["ws"], a["wsb"],
-                                           a["stream"])
 
-    def gd(**kw):
-        a = dict(q=addr(0), k=addr(1), v=addr(2), a=addr(3), beta=addr(4), S=addr(5),
-                 o=addr(6), S_out=addr(5), N=4, H=2, dk=128, dv=128, dt=1, stream=None)
-        a.update(kw)
-        return lib.kda_gdn_decode_step(a["q"], a["k"], a["v"], a["a"], a["beta"], a["S"],
-                                       a["o"], a["S_out"], a["N"], a["H"], a["dk"], a["dv"],
-                                       a["dt"], a["stream"])
+def gdn_prefill(lib, **kw):
+    a = dict(q=addr(0), k=addr(1), v=addr(2), a=addr(3), beta=addr(4), S0=addr(5),
+             o=addr(6), S_T=addr(7), B=1, T=64, H=2, dk=128, dv=128, C=64, dt=1,
+             ws=addr(8), wsb=1 << 34, stream=None)
+    a.update(kw)
+    return lib.kda_gdn_prefill_chunked(a["q"], a["k"], a["v"], a["a"], a["beta"], a["S0"],
+                                       a["o"], a["S_T"], a["B"], a["T"], a["H"], a["dk"],
+                                       a["dv"], a["C"], a["dt"], a["ws"], a["wsb"], a["stream"])
 
-    assert gp(a=None) in ok and gd(a=None) in ok          # DeltaNet: no gate
-    assert gp() in ok and gd() in ok
+
+def gdn_decode(lib, **kw):
+    a = dict(q=addr(0), k=addr(1), v=addr(2), a=addr(3), beta=addr(4), S=addr(5),
+             o=addr(6), S_out=addr(5), N=4, H=2, dk=128, dv=128, dt=1, stream=None)
+    a.update(kw)
+    return lib.kda_gdn_decode_step(a["q"], a["k"], a["v"], a["a"], a["beta"], a["S"],
+                                   a["o"], a["S_out"], a["N"], a["H"], a["dk"], a["dv"],
+                                   a["dt"], a["stream"])
+
+
+def test_gdn_entry_points_validate():
+    L = _lib()
+    lib = L.load()
+    gp = lambda **kw: gdn_prefill(lib, **kw)
+    gd = lambda **kw: gdn_decode(lib, **kw)
     assert gp(beta=None) == L.KDA_ERR_NULL and gd(beta=None) == L.KDA_ERR_NULL
     assert gp(a=addr(3) + 4) == L.KDA_ERR_ALIGN and gd(a=addr(3) + 8) == L.KDA_ERR_ALIGN
     assert gp(ws=None) == L.KDA_ERR_WORKSPACE
-    # the gate array is B*T*H fp32 values: an output just past it is fine
+    # the gate array is B*T*H fp32 values: an output inside it overlaps
     g_end = addr(3) + 1 * 64 * 2 * 4
     assert gp(o=g_end - 16) == L.KDA_ERR_ALIAS
-    assert gp(o=g_end) in ok
-    assert gd(o=addr(3) + 4 * 2 * 4) in ok and gd(o=addr(3)) == L.KDA_ERR_ALIAS
+    assert gd(o=addr(3)) == L.KDA_ERR_ALIAS
+
+
+@host_only
+def test_gdn_entry_points_take_a_null_gate():
+    L = _lib()
+    lib = L.load()
+    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+    assert may_launch(gdn_prefill, lib=lib, a=None) in ok     # DeltaNet: no gate
+    assert may_launch(gdn_decode, lib=lib, a=None) in ok
+    assert may_launch(gdn_prefill, lib=lib) in ok and may_launch(gdn_decode, lib=lib) in ok
+    # an output just past the B*T*H fp32 gates is fine
+    assert may_launch(gdn_prefill, lib=lib, o=addr(3) + 1 * 64 * 2 * 4) in ok
+    assert may_launch(gdn_decode, lib=lib, o=addr(3) + 4 * 2 * 4) in ok
+
+
+def step_backward(lib, **kw):
+    a = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), S=addr(5),
+             dO=addr(6), dSn=addr(7), dq=addr(8), dk=addr(9), dv=addr(10), da=addr(11),
+             db=addr(12), dS=addr(13), N=4, H=2, dk_=128, dv_=128, dt=1, stream=None)
+    a.update(kw)
+    return lib.kda_decode_step_backward(a["q"], a["k"], a["v"], a["alpha"], a["beta"],
+                                        a["S"], a["dO"], a["dSn"], a["dq"], a["dk"],
+                                        a["dv"], a["da"], a["db"], a["dS"], a["N"], a["H"],
+                                        a["dk_"], a["dv_"], a["dt"], a["stream"])
 
 
 def test_step_backward_validation():
     L = _lib()
     lib = L.load()
-    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
-
-    def bw(**kw):
-        a = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), S=addr(5),
-                 dO=addr(6), dSn=addr(7), dq=addr(8), dk=addr(9), dv=addr(10), da=addr(11),
-                 db=addr(12), dS=addr(13), N=4, H=2, dk_=128, dv_=128, dt=1, stream=None)
-        a.update(kw)
-        return lib.kda_decode_step_backward(a["q"], a["k"], a["v"], a["alpha"], a["beta"],
-                                            a["S"], a["dO"], a["dSn"], a["dq"], a["dk"],
-                                            a["dv"], a["da"], a["db"], a["dS"], a["N"], a["H"],
-                                            a["dk_"], a["dv_"], a["dt"], a["stream"])
-
-    assert bw() in ok
-    assert bw(dS=addr(7)) in ok                                  # in place over dS_new
+    bw = lambda **kw: step_backward(lib, **kw)
     assert bw(dS=addr(5)) == L.KDA_ERR_ALIAS                     # over the state
     assert bw(dS=addr(7) + 64) == L.KDA_ERR_ALIAS                # partial overlap with dS_new
     assert bw(dq=addr(9)) == L.KDA_ERR_ALIAS                     # two outputs together
@@ -284,6 +358,15 @@ def test_step_backward_validation():
     assert bw(da=addr(11) + 4) == L.KDA_ERR_ALIGN
     assert bw(N=0) == L.KDA_ERR_SHAPE
     assert bw(dk_=24) == L.KDA_ERR_UNSUPPORTED
+
+
+@host_only
+def test_step_backward_valid_arguments():
+    L = _lib()
+    lib = L.load()
+    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+    assert may_launch(step_backward, lib=lib) in ok
+    assert may_launch(step_backward, lib=lib, dS=addr(7)) in ok   # in place over dS_new
 
 
 def test_prefill_backward_workspace_bytes():
@@ -299,70 +382,88 @@ def test_prefill_backward_workspace_bytes():
     assert lib.kda_prefill_backward_workspace_bytes(0, 16, 1, 16, 16) == bad
 
 
+PB_B, PB_T, PB_H, PB_D = 1, 64, 2, 128
+
+
+def prefill_backward(lib, fn="kda_prefill_backward", **kw):
+    ws_need = lib.kda_prefill_backward_workspace_bytes(PB_B, PB_T, PB_H, PB_D, PB_D)
+    a = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), S0=addr(5),
+             dO=addr(6), dST=addr(7), dq=addr(8), dk=addr(9), dv=addr(10), da=addr(11),
+             db=addr(12), dS0=addr(13), B=PB_B, T=PB_T, H=PB_H, dk_=PB_D, dv_=PB_D, dt=1,
+             ws=addr(14), wsb=ws_need, stream=None)
+    a.update(kw)
+    return getattr(lib, fn)(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"],
+                            a["dO"], a["dST"], a["dq"], a["dk"], a["dv"], a["da"],
+                            a["db"], a["dS0"], a["B"], a["T"], a["H"], a["dk_"],
+                            a["dv_"], a["dt"], a["ws"], a["wsb"], a["stream"])
+
+
 def test_prefill_backward_validation():
     L = _lib()
     lib = L.load()
-    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
-    B, T, H, d = 1, 64, 2, 128
-    ws_need = lib.kda_prefill_backward_workspace_bytes(B, T, H, d, d)
-
-    def pb(**kw):
-        a = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), S0=addr(5),
-                 dO=addr(6), dST=addr(7), dq=addr(8), dk=addr(9), dv=addr(10), da=addr(11),
-                 db=addr(12), dS0=addr(13), B=B, T=T, H=H, dk_=d, dv_=d, dt=1, ws=addr(14),
-                 wsb=ws_need, stream=None)
-        a.update(kw)
-        return lib.kda_prefill_backward(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"],
-                                        a["dO"], a["dST"], a["dq"], a["dk"], a["dv"], a["da"],
-                                        a["db"], a["dS0"], a["B"], a["T"], a["H"], a["dk_"],
-                                        a["dv_"], a["dt"], a["ws"], a["wsb"], a["stream"])
-
-    assert pb() in ok
-    assert pb(S0=None, dST=None, dS0=None) in ok                 # optional states
-    assert pb(dS0=addr(7)) in ok                                 # in place over dS_T
+    pb = lambda **kw: prefill_backward(lib, **kw)
+    ws_need = lib.kda_prefill_backward_workspace_bytes(PB_B, PB_T, PB_H, PB_D, PB_D)
     assert pb(dS0=addr(7) + 64) == L.KDA_ERR_ALIAS               # partial overlap with dS_T
     assert pb(dS0=addr(5)) == L.KDA_ERR_ALIAS                    # over S0
     assert pb(dq=addr(9)) == L.KDA_ERR_ALIAS                     # two outputs together
     assert pb(ws=addr(6)) == L.KDA_ERR_ALIAS                     # workspace over dO
-    # dq is B*T*H*dk fp32: an output just past its end is fine, one inside is not
-    dq_end = addr(8) + B * T * H * d * 4
-    assert pb(dk=dq_end) in ok and pb(dk=dq_end - 16) == L.KDA_ERR_ALIAS
+    # dq is B*T*H*dk fp32: an output inside it overlaps
+    dq_end = addr(8) + PB_B * PB_T * PB_H * PB_D * 4
+    assert pb(dk=dq_end - 16) == L.KDA_ERR_ALIAS
     assert pb(dO=None) == L.KDA_ERR_NULL and pb(db=None) == L.KDA_ERR_NULL
     assert pb(da=addr(11) + 4) == L.KDA_ERR_ALIGN
     assert pb(ws=None) == L.KDA_ERR_WORKSPACE and pb(wsb=ws_need - 1) == L.KDA_ERR_WORKSPACE
     assert pb(T=-1) == L.KDA_ERR_SHAPE and pb(H=0) == L.KDA_ERR_SHAPE
     assert pb(dk_=24) == L.KDA_ERR_UNSUPPORTED and pb(dt=7) == L.KDA_ERR_UNSUPPORTED
+
+
+@host_only
+def test_prefill_backward_valid_arguments():
+    L = _lib()
+    lib = L.load()
+    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+    pb = lambda **kw: may_launch(prefill_backward, lib=lib, **kw)
+    assert pb() in ok
+    assert pb(S0=None, dST=None, dS0=None) in ok                 # optional states
+    assert pb(dS0=addr(7)) in ok                                 # in place over dS_T
+    dq_end = addr(8) + PB_B * PB_T * PB_H * PB_D * 4
+    assert pb(dk=dq_end) in ok                                   # just past dq
     # no tokens: only the state gradient is passed through, the rest may be NULL
     assert pb(T=0, q=None, k=None, v=None, alpha=None, beta=None, dO=None, dq=None, dk=None,
               dv=None, da=None, db=None, ws=None, wsb=0) in ok
+
+
+PRO_ROWS, PRO_D = 64, 128
+
+
+def prologue_fwd(lib, **kw):
+    a = dict(q=addr(0), k=addr(1), g=addr(2), b=addr(3), qh=addr(4), kh=addr(5), al=addr(6),
+             be=addr(7), rows=PRO_ROWS, dk=PRO_D, dt=1, m=1, stream=None)
+    a.update(kw)
+    return lib.kda_prologue_forward(a["q"], a["k"], a["g"], a["b"], a["qh"], a["kh"],
+                                    a["al"], a["be"], a["rows"], a["dk"], a["dt"], a["m"],
+                                    a["stream"])
+
+
+def prologue_bwd(lib, **kw):
+    a = dict(q=addr(0), k=addr(1), g=addr(2), b=addr(3), dqh=addr(4), dkh=addr(5),
+             da=addr(6), dbe=addr(7), dq=addr(8), dk=addr(9), dg=addr(10), db=addr(11),
+             rows=PRO_ROWS, dk_=PRO_D, dt=1, m=2, stream=None)
+    a.update(kw)
+    return lib.kda_prologue_backward(a["q"], a["k"], a["g"], a["b"], a["dqh"], a["dkh"],
+                                     a["da"], a["dbe"], a["dq"], a["dk"], a["dg"], a["db"],
+                                     a["rows"], a["dk_"], a["dt"], a["m"], a["stream"])
 
 
 def test_prologue_validation():
     L = _lib()
     lib = L.load()
     ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
-    rows, d = 64, 128
-
-    def pf(**kw):
-        a = dict(q=addr(0), k=addr(1), g=addr(2), b=addr(3), qh=addr(4), kh=addr(5), al=addr(6),
-                 be=addr(7), rows=rows, dk=d, dt=1, m=1, stream=None)
-        a.update(kw)
-        return lib.kda_prologue_forward(a["q"], a["k"], a["g"], a["b"], a["qh"], a["kh"],
-                                        a["al"], a["be"], a["rows"], a["dk"], a["dt"], a["m"],
-                                        a["stream"])
-
-    def pb(**kw):
-        a = dict(q=addr(0), k=addr(1), g=addr(2), b=addr(3), dqh=addr(4), dkh=addr(5),
-                 da=addr(6), dbe=addr(7), dq=addr(8), dk=addr(9), dg=addr(10), db=addr(11),
-                 rows=rows, dk_=d, dt=1, m=2, stream=None)
-        a.update(kw)
-        return lib.kda_prologue_backward(a["q"], a["k"], a["g"], a["b"], a["dqh"], a["dkh"],
-                                         a["da"], a["dbe"], a["dq"], a["dk"], a["dg"], a["db"],
-                                         a["rows"], a["dk_"], a["dt"], a["m"], a["stream"])
-
+    pf = lambda **kw: prologue_fwd(lib, **kw)
+    pb = lambda **kw: prologue_bwd(lib, **kw)
     for f in (pf, pb):
-        assert f() in ok
-        assert f(rows=0, q=None, k=None) in ok                    # nothing to do
+        # rows = 0 returns before the device check and launches nothing
+        assert f(rows=0, q=None, k=None) == L.KDA_OK              # nothing to do
         assert f(rows=-1) == L.KDA_ERR_SHAPE
         assert f(m=3) == L.KDA_ERR_UNSUPPORTED and f(dt=5) == L.KDA_ERR_UNSUPPORTED
         assert f(q=None) == L.KDA_ERR_NULL and f(b=addr(3) + 4) == L.KDA_ERR_ALIGN
@@ -370,56 +471,87 @@ def test_prologue_validation():
     # q_hat over the raw keys, alpha over beta, dg over dalpha: rejected
     assert pf(qh=addr(1)) == L.KDA_ERR_ALIAS and pf(al=addr(7)) == L.KDA_ERR_ALIAS
     assert pb(dg=addr(6)) == L.KDA_ERR_ALIAS and pb(db=addr(8)) == L.KDA_ERR_ALIAS
-    # an output right after an input's last byte is fine (bf16 q is rows*dk*2 bytes)
-    assert pf(qh=addr(0) + rows * d * 2) in ok
-    assert pf(qh=addr(0) + rows * d * 2 - 16) == L.KDA_ERR_ALIAS
+    # an output inside an input's last bytes overlaps (bf16 q is rows*dk*2 bytes)
+    assert pf(qh=addr(0) + PRO_ROWS * PRO_D * 2 - 16) == L.KDA_ERR_ALIAS
+
+
+@host_only
+def test_prologue_valid_arguments():
+    L = _lib()
+    lib = L.load()
+    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+    assert may_launch(prologue_fwd, lib=lib) in ok
+    assert may_launch(prologue_bwd, lib=lib) in ok
+    # an output right after an input's last byte is fine
+    assert may_launch(prologue_fwd, lib=lib, qh=addr(0) + PRO_ROWS * PRO_D * 2) in ok
 
 
 def test_gdn_prefill_backward_validation():
     L = _lib()
     lib = L.load()
-    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
-    B, T, H, d = 1, 64, 2, 128
-    ws_need = lib.kda_prefill_backward_workspace_bytes(B, T, H, d, d)
-
-    def gb(**kw):
-        a = dict(q=addr(0), k=addr(1), v=addr(2), a=addr(3), beta=addr(4), S0=addr(5),
-                 dO=addr(6), dST=addr(7), dq=addr(8), dk=addr(9), dv=addr(10), da=addr(11),
-                 db=addr(12), dS0=addr(13), B=B, T=T, H=H, dk_=d, dv_=d, dt=1, ws=addr(14),
-                 wsb=ws_need, stream=None)
-        a.update(kw)
-        return lib.kda_gdn_prefill_backward(a["q"], a["k"], a["v"], a["a"], a["beta"], a["S0"],
-                                            a["dO"], a["dST"], a["dq"], a["dk"], a["dv"],
-                                            a["da"], a["db"], a["dS0"], a["B"], a["T"], a["H"],
-                                            a["dk_"], a["dv_"], a["dt"], a["ws"], a["wsb"],
-                                            a["stream"])
-
-    assert gb() in ok
-    assert gb(a=None, da=None) in ok                      # DeltaNet: no gate
-    assert gb(a=None) in ok                               # da ignored without a gate
-    # the gate and its gradient are B*T*H floats: an output right after them is fine
-    a_end = addr(3) + B * T * H * 4
-    assert gb(dq=a_end) in ok and gb(dq=a_end - 16) == L.KDA_ERR_ALIAS
+    gb = lambda **kw: prefill_backward(lib, fn="kda_gdn_prefill_backward", **kw)
+    # the gate and its gradient are B*T*H floats: an output inside them overlaps
+    a_end = addr(3) + PB_B * PB_T * PB_H * 4
+    assert gb(dq=a_end - 16) == L.KDA_ERR_ALIAS
     assert gb(da=addr(12)) == L.KDA_ERR_ALIAS and gb(beta=None) == L.KDA_ERR_NULL
     assert gb(ws=None) == L.KDA_ERR_WORKSPACE and gb(dk_=24) == L.KDA_ERR_UNSUPPORTED
+
+
+@host_only
+def test_gdn_prefill_backward_valid_arguments():
+    L = _lib()
+    lib = L.load()
+    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+    gb = lambda **kw: may_launch(prefill_backward, lib=lib, fn="kda_gdn_prefill_backward", **kw)
+    assert gb() in ok
+    assert gb(alpha=None, da=None) in ok                  # DeltaNet: no gate
+    assert gb(alpha=None) in ok                           # da ignored without a gate
+    assert gb(dq=addr(3) + PB_B * PB_T * PB_H * 4) in ok  # just past the gates
 
 
 def test_gdn_step_backward_validation():
     L = _lib()
     lib = L.load()
-    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
-
-    def gs(**kw):
-        a = dict(q=addr(0), k=addr(1), v=addr(2), a=addr(3), beta=addr(4), S=addr(5),
-                 dO=addr(6), dSn=addr(7), dq=addr(8), dk=addr(9), dv=addr(10), da=addr(11),
-                 db=addr(12), dS=addr(13), N=4, H=2, dk_=128, dv_=128, dt=1, stream=None)
-        a.update(kw)
-        return lib.kda_gdn_decode_step_backward(a["q"], a["k"], a["v"], a["a"], a["beta"],
-                                                a["S"], a["dO"], a["dSn"], a["dq"], a["dk"],
-                                                a["dv"], a["da"], a["db"], a["dS"], a["N"],
-                                                a["H"], a["dk_"], a["dv_"], a["dt"], a["stream"])
-
-    assert gs() in ok and gs(a=None, da=None) in ok and gs(dS=addr(7)) in ok
+    gs = lambda **kw: gdn_step_backward(lib, **kw)
     a_end = addr(3) + 4 * 2 * 4                            # one gate per head
-    assert gs(dq=a_end) in ok and gs(dq=a_end - 16) == L.KDA_ERR_ALIAS
+    assert gs(dq=a_end - 16) == L.KDA_ERR_ALIAS
     assert gs(beta=None) == L.KDA_ERR_NULL and gs(da=addr(11) + 4) == L.KDA_ERR_ALIGN
+
+
+def gdn_step_backward(lib, **kw):
+    a = dict(q=addr(0), k=addr(1), v=addr(2), a=addr(3), beta=addr(4), S=addr(5),
+             dO=addr(6), dSn=addr(7), dq=addr(8), dk=addr(9), dv=addr(10), da=addr(11),
+             db=addr(12), dS=addr(13), N=4, H=2, dk_=128, dv_=128, dt=1, stream=None)
+    a.update(kw)
+    return lib.kda_gdn_decode_step_backward(a["q"], a["k"], a["v"], a["a"], a["beta"],
+                                            a["S"], a["dO"], a["dSn"], a["dq"], a["dk"],
+                                            a["dv"], a["da"], a["db"], a["dS"], a["N"],
+                                            a["H"], a["dk_"], a["dv_"], a["dt"], a["stream"])
+
+
+@host_only
+def test_gdn_step_backward_valid_arguments():
+    L = _lib()
+    lib = L.load()
+    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+    gs = lambda **kw: may_launch(gdn_step_backward, lib=lib, **kw)
+    assert gs() in ok and gs(a=None, da=None) in ok and gs(dS=addr(7)) in ok
+    assert gs(dq=addr(3) + 4 * 2 * 4) in ok
+
+
+def test_every_launching_case_is_host_only():
+    """Every test here that calls with arguments passing validation is marked
+    host_only and goes through may_launch (checked on the source)."""
+    import inspect
+    import sys
+    mod = sys.modules[__name__]
+    for name, fn in inspect.getmembers(mod, inspect.isfunction):
+        if not name.startswith("test_") or name == "test_every_launching_case_is_host_only":
+            continue
+        body = inspect.getsource(fn)
+        launches = "may_launch(" in body
+        marked = any(m.name == "skipif" for m in getattr(fn, "pytestmark", []))
+        if launches:
+            assert marked, f"{name} may launch kernels but is not host_only"
+        if marked:
+            assert launches, f"{name} is host_only but makes no may_launch call"
