@@ -343,11 +343,11 @@ kda_pb_backward_kernel(const typename Ty<IO>::Elem* __restrict__ q,
                        const typename Ty<IO>::Elem* __restrict__ v,
                        const float* __restrict__ alpha, const float* __restrict__ beta,
                        const typename Ty<IO>::Elem* __restrict__ dO,
-                       const float* __restrict__ dS_T, const float* __restrict__ ck,
+                       const float* dS_T, const float* __restrict__ ck,
                        const float* __restrict__ uw, const float* __restrict__ rw,
                        float* __restrict__ g_q, float* __restrict__ g_k,
                        float* __restrict__ g_v, float* __restrict__ g_alpha,
-                       float* __restrict__ g_beta, float* __restrict__ g_S0, int T, int H,
+                       float* __restrict__ g_beta, float* g_S0, int T, int H,
                        int DV) {
   using G = Geo<DK>;
   constexpr int RPT = G::RPT, CPW = G::CPW, RG = G::RG, WGC = G::WGC;
