@@ -36,7 +36,11 @@ Readings taken:
 Every function here is pinned in tests/test_prologue_pins.py: special values
 that the definitions fix exactly (g = 0 gives alpha = 1/2, g = ln 3 gives
 1/4), limits, the odd-part identity of SiLU, unit norm and scale invariance,
-and every pin of the recurrence run through exact inverse logits.
+and every pin of the recurrence run through exact inverse logits.  The decode
+step from logits is pinned on its own: chained over a sequence it must give
+the prefill from logits, every recurrence pin must hold through it on exact
+inverse logits, a unit key reads back its value in one step, and g = ln 3
+with b = -inf only decays the state by 1/4.
 """
 from __future__ import annotations
 

@@ -267,3 +267,141 @@ def test_prologue_pins_catch_planted_mistake(name):
         if not err < 1e-9:
             caught.append(cname)
     assert caught, f"no pin catches {name}"
+
+
+# ------------------------------------------- one decode step from logits --
+#
+# oracle.kda_decode_step_logits(q, k, v, g, b, S, qk_map) -> (o, S') is one
+# token of the recurrence from raw projections.  What fixes its answers:
+#   * a run of such steps is the whole prefill from raw projections, so
+#     chained over a sequence it must give kda_recurrence_logits' o at every
+#     token and its final state, for every q/k map;
+#   * through the exact inverse logits it must hand the recurrence back its
+#     own alpha and beta, so every recurrence pin (tests/oracle_pins.py)
+#     holds for the chained steps;
+#   * with the L2 map and b = +inf (beta = 1) the normalised key reads back
+#     the written value exactly, whatever the raw key's length ("22580: от
+#     GPT-2 до Kimi K3, объяснение", section "DeltaNet, или Fast Weight
+#     Programmers");
+#   * g = ln 3 gives alpha = 1/4 and b = -inf gives beta = 0: one step then
+#     only decays, S' = S / 4, and o = q S / 4.
+from oracle.kda_prologue import kda_decode_step_logits  # noqa: E402
+
+STEP_CHECKS = {}
+
+
+def step_check(name):
+    def deco(fn):
+        STEP_CHECKS[name] = fn
+        return fn
+    return deco
+
+
+def _chain(step, q, k, v, g, b, S0, qk_map):
+    """Steps over t = 0..T-1 of [B, T, H, .] arrays -> (o [B, T, H, dv], S_T)."""
+    B, T, H, dk = np.shape(k)
+    dv = np.shape(v)[-1]
+    S = np.zeros((B, H, dk, dv)) if S0 is None else np.asarray(S0, float)
+    outs = []
+    for t in range(T):
+        o, S = step(q[:, t], k[:, t], v[:, t], g[:, t], b[:, t], S, qk_map)
+        outs.append(o)
+    return np.stack(outs, axis=1) if outs else np.zeros((B, 0, H, dv)), S
+
+
+@step_check("chain_equals_prefill_from_logits")
+def chain_equals_prefill_from_logits(step):
+    q, k = _raw(11, B=2, T=7, H=3, dk=5)
+    r = np.random.default_rng(12)
+    v = r.standard_normal(q.shape[:3] + (4,))
+    g = r.standard_normal(q.shape) * 2.0
+    b = r.standard_normal(q.shape[:3])
+    S0 = r.standard_normal((2, 3, 5, 4))
+    err = 0.0
+    for m in (QK_AS_GIVEN, QK_L2, QK_SILU_L2):
+        o, S = _chain(step, q, k, v, g, b, S0, m)
+        o_ref, S_ref = kda_recurrence_logits(q, k, v, g, b, S0, qk_map=m)
+        err = max(err, pins.rel(o, o_ref), pins.rel(S, S_ref))
+    return err
+
+
+@step_check("recurrence_pins_through_steps")
+def recurrence_pins_through_steps(step):
+    def run(q, k, v, alpha, beta, S0=None):
+        g, b = inverse_logits(np.asarray(alpha, float), np.asarray(beta, float))
+        return _chain(step, np.asarray(q, float), np.asarray(k, float), np.asarray(v, float),
+                      g, b, S0, QK_AS_GIVEN)
+    return max(pins.run_all(run).values())
+
+
+@step_check("unit_key_reads_back_in_one_step")
+def unit_key_reads_back_in_one_step(step):
+    r = np.random.default_rng(13)
+    q, k = r.standard_normal((3, 2, 6)), r.standard_normal((3, 2, 6)) * 7.0
+    v = r.standard_normal((3, 2, 4))
+    g = r.standard_normal((3, 2, 6))
+    S = r.standard_normal((3, 2, 6, 4))
+    _, S1 = step(q, k, v, g, np.full((3, 2), np.inf), S, QK_L2)
+    kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    return pins.rel(np.einsum("nhc,nhcj->nhj", kn, S1), v)
+
+
+@step_check("decay_only_step")
+def decay_only_step(step):
+    r = np.random.default_rng(14)
+    q, k = r.standard_normal((2, 3, 4)), r.standard_normal((2, 3, 4))
+    v = r.standard_normal((2, 3, 5))
+    S = r.standard_normal((2, 3, 4, 5))
+    o, S1 = step(q, k, v, np.full((2, 3, 4), LN3), np.full((2, 3), -np.inf), S, QK_AS_GIVEN)
+    return max(pins.rel(S1, S / 4.0), pins.rel(o, np.einsum("nhc,nhcj->nhj", q, S) / 4.0))
+
+
+@pytest.mark.parametrize("name", sorted(STEP_CHECKS))
+def test_decode_step_logits_pin(name):
+    err = STEP_CHECKS[name](kda_decode_step_logits)
+    assert err < TOL, f"{name}: {err}"
+
+
+def _step_mut(kind):
+    """A copy of the decode step from logits with one mistake planted."""
+    def step(q, k, v, g, b, S, qk_map):
+        q, k, v, S = (np.asarray(x, float) for x in (q, k, v, S))
+        if kind != "no_normalisation" and qk_map != QK_AS_GIVEN:
+            f = silu if qk_map == QK_SILU_L2 else (lambda x: x)
+            q, k = normalize(f(q)), normalize(f(k))
+        alpha = sigmoid(g) if kind == "gate_is_sigmoid" else np.exp(-softplus(g))
+        beta = sigmoid(-np.asarray(b, float)) if kind == "beta_sign" else sigmoid(b)
+        if kind == "decay_after_write":
+            r = np.einsum("nhc,nhcj->nhj", k, S)
+            u = beta[..., None] * (v - r)
+            S1 = alpha[..., None] * (S + k[..., None] * u[..., None, :])
+        else:
+            Sd = alpha[..., None] * S
+            r = np.einsum("nhc,nhcj->nhj", k, Sd)
+            u = beta[..., None] * (v - r)
+            S1 = Sd + k[..., None] * u[..., None, :]
+        return np.einsum("nhc,nhcj->nhj", q, S1), S1
+    return step
+
+
+STEP_MUTANTS = ["gate_is_sigmoid", "beta_sign", "decay_after_write", "no_normalisation"]
+
+
+def test_unmutated_step_copy_passes():
+    """The mutant harness itself, with no mistake, passes every step pin."""
+    for name, fn in STEP_CHECKS.items():
+        assert fn(_step_mut("none")) < TOL, name
+
+
+@pytest.mark.parametrize("kind", STEP_MUTANTS)
+def test_decode_step_logits_pins_catch_planted_mistake(kind):
+    caught = []
+    for cname, fn in STEP_CHECKS.items():
+        with np.errstate(all="ignore"):
+            try:
+                err = fn(_step_mut(kind))
+            except Exception:
+                err = np.inf
+        if not err < 1e-9:
+            caught.append(cname)
+    assert caught, f"no pin catches {kind}"
