@@ -6,6 +6,7 @@ import torch
 
 import workloads as wl
 from oracle import kda_decode_step
+from tests import parity
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -96,9 +97,7 @@ def test_decode_n256_h32_1000_steps():
         o_r, Sr = kda_decode_step(ref_steps["q"][s], ref_steps["k"][s], ref_steps["v"][s],
                                   ref_steps["alpha"][s], ref_steps["beta"][s], Sr)
         orf.append(o_r)
-    eo = rel(og, np.stack(orf))
-    es = rel(f64(S[seqs]), Sr)
-    print(f"[decode_n256_h32 1000 steps, seqs {seqs}] rel_o={eo:.3e} rel_S={es:.3e}", flush=True)
-    assert eo < 2e-2 and es < 2e-2
+    parity.report(f"decode_n256_h32 1000 steps, seqs {seqs}", 2e-2, og, np.stack(orf),
+                  f64(S[seqs]), Sr, steps_major=True)
     del steps
     torch.cuda.empty_cache()

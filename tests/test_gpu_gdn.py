@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import workloads as wl
+from tests import parity
 from oracle import gdn_decode_step, gdn_recurrence
 
 pytestmark = pytest.mark.gpu
@@ -51,11 +52,8 @@ def check(inp, C, label=""):
     tol = TOL[inp["q"].dtype]
     o, S = run(inp, C)
     o_ref, S_ref = oracle(inp)
-    eo, es = rel(f64(o), o_ref), rel(f64(S), S_ref)
-    print(f"[{label} C={C} gate={'scalar' if inp['a'] is not None else 'none'}] "
-          f"rel_o={eo:.3e} rel_S={es:.3e}", flush=True)
-    assert np.isfinite(f64(o)).all() and np.isfinite(f64(S)).all()
-    assert eo < tol and es < tol, (eo, es)
+    parity.report(f"{label} C={C} gate={'scalar' if inp['a'] is not None else 'none'}", tol,
+                  f64(o), o_ref, f64(S), S_ref)
 
 
 @pytest.mark.parametrize("gated", [True, False])
@@ -80,7 +78,7 @@ def test_fused_and_split_paths(gated):
     o_few, S_few = run(few, 64)
     o_ref, S_ref = oracle(few)
     for o, S in ((o_big[3:4], S_big[3:4]), (o_few, S_few)):
-        assert rel(f64(o), o_ref) < 2e-2 and rel(f64(S), S_ref) < 2e-2
+        parity.report("gdn paths", 2e-2, f64(o), o_ref, f64(S), S_ref)
 
 
 @pytest.mark.parametrize("dk,dv,dtype,C,T", [

@@ -18,6 +18,7 @@ import pytest
 import torch
 
 import workloads as wl
+from tests import parity
 from oracle import kda_decode_step_logits, kda_recurrence_logits
 
 pytestmark = pytest.mark.gpu
@@ -68,10 +69,7 @@ def check(inp, C, qk, label=""):
     tol = TOL[inp["q"].dtype]
     o, S = run(inp, C, qk)
     o_ref, S_ref = oracle(inp, qk)
-    eo, es = rel(f64(o), o_ref), rel(f64(S), S_ref)
-    print(f"[{label} C={C} qk={qk}] rel_o={eo:.3e} rel_S={es:.3e}", flush=True)
-    assert np.isfinite(f64(o)).all() and np.isfinite(f64(S)).all()
-    assert eo < tol and es < tol, (eo, es)
+    parity.report(f"{label} C={C} qk={qk}", tol, f64(o), o_ref, f64(S), S_ref)
     return o, S
 
 
@@ -105,9 +103,7 @@ def test_fused_and_split_paths(qk):
     o_few, S_few = run(few, 64, qk)
     o_ref, S_ref = oracle(few, qk)
     for o, S in ((o_big[3:4], S_big[3:4]), (o_few, S_few)):
-        eo, es = rel(f64(o), o_ref), rel(f64(S), S_ref)
-        print(f"[paths qk={qk}] rel_o={eo:.3e} rel_S={es:.3e}", flush=True)
-        assert eo < 2e-2 and es < 2e-2
+        parity.report(f"paths qk={qk}", 2e-2, f64(o), o_ref, f64(S), S_ref)
 
 
 @pytest.mark.parametrize("dk,dv,dtype,C,T,qk", [
