@@ -3,19 +3,22 @@ GB/s) with roofline fractions and the CPU oracle as a reported baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
 
-A step is one kda_prefill_chunked call over the H=16, T=4096, d=128 bf16
-workload (B=1, C=64, inputs already resident in HBM).  Prints ONE JSON line.
-Alongside the headline it measures, on the same GPU:
+A step is one kda_prefill_chunked call over the long-context workload, the
+largest that fits one GPU: B=1, H=32, T=1,048,576, dk=dv=128, bf16 q/k/v/o,
+fp32 gates, strengths and state, C=64, inputs already resident in HBM.  Prints
+ONE JSON line.  Alongside the headline it measures, on the same GPU:
+  * the H=16, T=4096 prefill and the B=8, H=32, T=8192 prefill (tokens/s and
+    roofline);
+  * 256 single-sequence decode steps from the long-context final state;
   * decode: 256 sequences x 32 heads, 64 KiB fp32 state per head, in-place
     kda_decode_step calls (state GB/s against the HBM peak);
-  * the B=8, H=32, T=8192 prefill (tokens/s and roofline);
   * the H=16 prefill and the 256 x 32-head decode from raw projections
     (gate logits, write-strength logits, q/k L2-normalised in the kernels);
   * the same two with one gate per token and head (Gated DeltaNet);
-  * the long-context prefill (H=32, T=1,048,576) and 256 single-sequence
-    decode steps from its final state, reported separately;
-  * the adjoint of one decode step for 256 sequences x 32 heads;
-  * the float64 oracle on the host cores over a bounded sample (cpu_baseline).
+  * the adjoint of one decode step for 256 sequences x 32 heads, the prefill
+    backward and the prologue kernels on the H=16 workload;
+  * the float64 oracle on the host cores over bounded samples of the
+    long-context prefill and of the decode workload (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -194,33 +197,75 @@ def _oracle_chain(args):
     return time.perf_counter() - t
 
 
-def cpu_baseline(inp, torch):
-    """The float64 oracle as it stands, one process per host core, each
-    running whole (b, h) chains with single-threaded BLAS."""
+def _oracle_decode_run(args):
+    """One sequence's decode steps through the oracle: (seconds, steps)."""
+    from oracle import kda_decode_step
+    S, q, k, v, a, b = args
+    t = time.perf_counter()
+    for i in range(q.shape[0]):
+        _, S = kda_decode_step(q[i], k[i], v[i], a[i], b[i], S)
+    return time.perf_counter() - t
+
+
+# Bounded samples the oracle is timed on (seconds of work, not the full jobs).
+CPU_PREFILL_SAMPLE_T = 4096        # tokens of every head of the long-context workload
+CPU_DECODE_SAMPLE_N = 8            # sequences x 32 heads of the decode workload
+CPU_DECODE_SAMPLE_STEPS = 1000          # all steps of the decode workload
+
+
+def cpu_baseline(wl):
+    """The float64 oracle as it stands, one process per host core (at most 16),
+    each running whole chains with single-threaded BLAS, on bounded samples:
+    the long-context prefill's first CPU_PREFILL_SAMPLE_T tokens of all 32
+    heads (the same distributions and channel-mixture gates), repeated to
+    about 10 core-s, and 8 sequences x 32 heads of the decode workload over
+    all of its 1000 steps."""
     import concurrent.futures as cf
     import multiprocessing as mp
+    spec = wl.PREFILL["longctx_h32_t1m"]
+    inp = wl.make_prefill_inputs(spec, "cpu", T=CPU_PREFILL_SAMPLE_T)
     B, T, H, _ = inp["q"].shape
     f = lambda t: t.float().numpy()  # noqa: E731  (bf16 -> fp32 is exact)
     chains = [(f(inp["q"][b:b + 1, :, h:h + 1]), f(inp["k"][b:b + 1, :, h:h + 1]),
                f(inp["v"][b:b + 1, :, h:h + 1]), f(inp["alpha"][b:b + 1, :, h:h + 1]),
                f(inp["beta"][b:b + 1, :, h:h + 1]))
               for b in range(B) for h in range(H)]
+    dspec = wl.DECODE["decode_n256_h32"]
+    S = wl.make_decode_state(dspec, "cpu", N=CPU_DECODE_SAMPLE_N)
+    st = wl.make_decode_steps(dspec, "cpu", N=CPU_DECODE_SAMPLE_N, steps=CPU_DECODE_SAMPLE_STEPS)
+    runs = [(S[n:n + 1].double().numpy(),) + tuple(f(st[x][:, n:n + 1])
+                                                   for x in ("q", "k", "v", "alpha", "beta"))
+            for n in range(CPU_DECODE_SAMPLE_N)]
     cores = min(len(os.sched_getaffinity(0)), 16, len(chains))
     ctx = mp.get_context("spawn")
     with cf.ProcessPoolExecutor(max_workers=cores, mp_context=ctx,
                                 initializer=_single_thread_blas) as ex:
         # one untimed pass starts the processes and sizes the sample: the
-        # timed sample repeats the whole workload to about 10 core-s of work
+        # timed sample repeats the prefill slice to about 10 core-s of work
         first = sum(ex.map(_oracle_chain, chains))
         reps = max(1, min(40, math.ceil(10.0 / max(first, 1e-3))))
         t0 = time.perf_counter()
         busy = sum(ex.map(_oracle_chain, chains * reps))
         wall = time.perf_counter() - t0
-    return dict(value=reps * B * T / wall, unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"the whole H=16 T=4096 d=128 workload ({B * T * H} token-heads, "
-                       f"{len(chains)} chains) run {reps} times over {cores} processes; "
-                       f"{busy:.1f} core-s of oracle work, {wall:.1f} s wall",
-                tok_heads_per_s=reps * B * T * H / wall)
+        t1 = time.perf_counter()
+        dbusy = sum(ex.map(_oracle_decode_run, runs))
+        dwall = time.perf_counter() - t1
+    head_steps = CPU_DECODE_SAMPLE_N * dspec.H * CPU_DECODE_SAMPLE_STEPS
+    dcores = min(cores, CPU_DECODE_SAMPLE_N)
+    return dict(
+        value=reps * B * T / wall, unit="tokens/s", cores=cores, kind="oracle",
+        sample=f"the long-context workload's first {T} tokens of all {H} heads "
+               f"({B * T * H} token-heads, {len(chains)} chains, same distributions and "
+               f"gates) run {reps} times over {cores} processes; {busy:.1f} core-s of oracle "
+               f"work, {wall:.1f} s wall",
+        tok_heads_per_s=reps * B * T * H / wall,
+        decode={"head_steps_per_s": head_steps / dwall, "unit": "head-steps/s",
+                "state_GBps": head_steps * 2 * dspec.dk * dspec.dv * 4 / dwall / 1e9,
+                "cores": dcores, "kind": "oracle",
+                "sample": f"{CPU_DECODE_SAMPLE_N} sequences x {dspec.H} heads of the decode "
+                          f"workload (state sd 0.01, alpha U(0.95, 1), bf16 q/k/v), "
+                          f"{CPU_DECODE_SAMPLE_STEPS} steps each, one process per sequence; "
+                          f"{dbusy:.1f} core-s, {dwall:.1f} s wall"})
 
 
 def _single_thread_blas():
@@ -237,9 +282,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="headline prefill only (no decode / large prefill lines)")
-    ap.add_argument("--only", choices=["prefill", "decode", "large", "logits", "decode_logits",
-                                       "gdn", "decode_gdn", "longctx", "decode_bwd", "prefill_bwd",
-                                       "prologue", "copy"],
+    ap.add_argument("--only", choices=["longctx", "prefill", "decode", "large", "logits",
+                                       "decode_logits", "gdn", "decode_gdn", "longctx_decode",
+                                       "decode_bwd", "prefill_bwd", "prologue", "copy"],
                     default=None,
                     help="run one leg only (for profiler runs); 'copy' times a plain "
                          "1 GiB device-to-device copy used to calibrate HBM byte counters")
@@ -265,67 +310,87 @@ def main():
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
                           "ms_per_copy": ms, "GBps": 8 * n / (ms * 1e-3) / 1e9}), flush=True)
         return
-    legs = ({"prefill", "decode", "large", "logits", "decode_logits", "gdn", "decode_gdn",
-             "longctx", "decode_bwd", "prefill_bwd", "prologue"} if args.only is None
-            else {args.only})
+    legs = ({"longctx", "prefill", "decode", "large", "logits", "decode_logits", "gdn",
+             "decode_gdn", "longctx_decode", "decode_bwd", "prefill_bwd", "prologue"}
+            if args.only is None else {args.only})
     if args.no_extra:
-        legs = {"prefill"}
+        legs = {"longctx"}
 
-    # ---------------- headline: prefill, H=16, T=4096, d=128, bf16, C=64
-    spec = wl.PREFILL["prefill_h16_t4k"]
-    inp_cpu = wl.make_prefill_inputs(spec, "cpu")
-    if "prefill" in legs:
-        headline(args, spec, inp_cpu, out, torch, kda, dev)
+    # ---------------- headline: long-context prefill, H=32, T=2^20, d=128, bf16, C=64
+    if "longctx" in legs:
+        headline(args, out, torch, kda, wl, dev)
     extras(args, legs, out, torch, kda, wl, dev)
     if not args.no_cpu and args.only is None:
-        out["cpu_baseline"] = cpu_baseline(inp_cpu, torch)
-        print(f"# cpu_baseline: {out['cpu_baseline']['value']:.1f} tokens/s",
+        out["cpu_baseline"] = cpu_baseline(wl)
+        print(f"# cpu_baseline: {out['cpu_baseline']['value']:.1f} tokens/s; decode "
+              f"{out['cpu_baseline']['decode']['head_steps_per_s']:.0f} head-steps/s",
               file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 
-def headline(args, spec, inp_cpu, out, torch, kda, dev):
-    C = 64
-    g = {k: (None if t is None else t.to(dev)) for k, t in inp_cpu.items()}
+def measure_prefill(args, spec, C, torch, kda, dev, steps, warmup, name):
+    """Time kda_prefill_chunked on one workload (inputs drawn on the device);
+    returns the figures of one call against the HBM and bf16 MFMA peaks."""
+    import workloads as wl
+    g = wl.make_prefill_inputs(spec, dev)
     o = torch.empty(spec.B, spec.T, spec.H, spec.dv, dtype=spec.dtype, device=dev)
     S_T = torch.empty(spec.B, spec.H, spec.dk, spec.dv, dtype=torch.float32, device=dev)
+    B, T, H, dk, dv = spec.B, spec.T, spec.H, spec.dk, spec.dv
+    ws_bytes = kda.prefill_workspace_bytes(B, T, H, dk, dv, C)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     def step():
         kda.prefill_chunked(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["S0"], chunk=C,
-                            out=o, state_out=S_T)
+                            out=o, state_out=S_T, workspace=ws)
 
-    ms_ev, ms_wall = time_launches(step, args.steps, args.warmup, torch)
-    B, T, H, dk, dv = spec.B, spec.T, spec.H, spec.dk, spec.dv
+    ms_ev, ms_wall = time_launches(step, steps, warmup, torch)
     nbytes = prefill_alg_bytes(B, T, H, dk, dv, 2, g["S0"] is not None)
     flops = prefill_flops(B, T, H, dk, dv, C)
     gbs = nbytes / (ms_ev * 1e-3) / 1e9
     tfl = flops / (ms_ev * 1e-3) / 1e12
-    tokens_per_s = B * T / (ms_wall * 1e-3)
+    del g, o, S_T, ws
+    torch.cuda.empty_cache()
+    return dict(C=C, kernel=prefill_kernels(kda, B, T, H, dk, dv, C), ms_per_launch=ms_ev,
+                ms_wall=ms_wall, tokens_per_s=B * T / (ms_wall * 1e-3),
+                tok_heads_per_s=B * T * H / (ms_wall * 1e-3), GBps=gbs,
+                frac_hbm=gbs / HBM_PEAK_GBS, traffic=profiled_traffic(name),
+                alg_bytes_per_launch=nbytes, tflops=tfl,
+                frac_mfma=tfl / MFMA_BF16_PEAK_TFLOPS, flops_per_launch=flops)
+
+
+def headline(args, out, torch, kda, wl, dev):
+    """The long-context prefill: B=1, H=32, T=1,048,576, d=128, bf16, C=64."""
+    spec = wl.PREFILL["longctx_h32_t1m"]
+    C = 64
+    r = measure_prefill(args, spec, C, torch, kda, dev, args.steps, args.warmup,
+                        "longctx_h32_t1m")
+    B, T, H, dk, dv = spec.B, spec.T, spec.H, spec.dk, spec.dv
     out.update({
         "metric": "KDA prefill tokens/s + % bf16 MFMA peak; decode state GB/s + % HBM peak",
-        "value": tokens_per_s,
+        "value": r["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_wall,
+        "ms_per_step": r["ms_wall"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "prefill_h16_t4k", "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
-                   "C": C, "io_dtype": "bf16", "state_dtype": "fp32"},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": profiled_traffic("prefill_h16_t4k"),
-                     "kernel": prefill_kernels(kda, B, T, H, dk, dv, C),
-                     "kernel_ms": ms_ev, "alg_bytes_per_launch": nbytes},
-        "mfma": {"achieved_tflops": tfl, "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-                 "frac": tfl / MFMA_BF16_PEAK_TFLOPS, "flops_per_launch": flops},
-        "tok_heads_per_s": B * T * H / (ms_wall * 1e-3),
+        "config": {"workload": "longctx_h32_t1m", "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
+                   "C": C, "io_dtype": "bf16", "state_dtype": "fp32",
+                   "gates": "13 of 128 channels per head U(0, 0.5), the rest U(0.99, 1)"},
+        "roofline": {"bound": "hbm", "achieved": r["GBps"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": r["frac_hbm"], "traffic": r["traffic"],
+                     "kernel": r["kernel"], "kernel_ms": r["ms_per_launch"],
+                     "alg_bytes_per_launch": r["alg_bytes_per_launch"]},
+        "mfma": {"achieved_tflops": r["tflops"], "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                 "frac": r["frac_mfma"], "flops_per_launch": r["flops_per_launch"]},
+        "tok_heads_per_s": r["tok_heads_per_s"],
     })
-    print(f"# prefill_h16_t4k: {ms_ev * 1e3:.1f} us/launch (events), {gbs:.0f} GB/s, "
-          f"{tfl:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    print(f"# longctx_h32_t1m: {r['ms_per_launch']:.2f} ms/launch (events), "
+          f"{r['GBps']:.0f} GB/s, {r['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
 
 
@@ -363,32 +428,23 @@ def extras(args, legs, out, torch, kda, wl, dev):
         del S, st, od
         torch.cuda.empty_cache()
 
+    if "prefill" in legs:
+        # ---------------- the H=16, T=4096 prefill (split path, launch-latency regime)
+        spec = wl.PREFILL["prefill_h16_t4k"]
+        r = measure_prefill(args, spec, 64, torch, kda, dev, args.steps, args.warmup,
+                            "prefill_h16_t4k")
+        out["prefill_h16_t4k"] = {k_: v_ for k_, v_ in r.items() if k_ != "ms_wall"}
+        print(f"# prefill_h16_t4k: {r['ms_per_launch'] * 1e3:.1f} us/launch, "
+              f"{r['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+
     if "large" in legs:
-        # ---------------- large prefill: B=8, H=32, T=8192
+        # ---------------- large prefill: B=8, H=32, T=8192 (fused path)
         lspec = wl.PREFILL["prefill_b8_h32_t8k"]
-        lg = wl.make_prefill_inputs(lspec, dev)
-        lo = torch.empty(lspec.B, lspec.T, lspec.H, lspec.dv, dtype=lspec.dtype, device=dev)
-        lS = torch.empty(lspec.B, lspec.H, lspec.dk, lspec.dv, dtype=torch.float32, device=dev)
-
-        def lstep():
-            kda.prefill_chunked(lg["q"], lg["k"], lg["v"], lg["alpha"], lg["beta"], lg["S0"],
-                                chunk=64, out=lo, state_out=lS)
-
         lsteps = max(3, args.steps // 5)
-        ms_l, ms_lw = time_launches(lstep, lsteps, 2, torch)
-        lb = prefill_alg_bytes(lspec.B, lspec.T, lspec.H, 128, 128, 2, True)
-        lf = prefill_flops(lspec.B, lspec.T, lspec.H, 128, 128, 64)
-        out["prefill_b8_h32_t8k"] = {
-            "C": 64, "kernel": prefill_kernels(kda, lspec.B, lspec.T, lspec.H, 128, 128, 64),
-            "ms_per_launch": ms_l, "tokens_per_s": lspec.B * lspec.T / (ms_lw * 1e-3),
-            "GBps": lb / (ms_l * 1e-3) / 1e9, "frac_hbm": lb / (ms_l * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": profiled_traffic("prefill_b8_h32_t8k"), "alg_bytes_per_launch": lb,
-            "tflops": lf / (ms_l * 1e-3) / 1e12,
-            "frac_mfma": lf / (ms_l * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-        }
-        print(f"# prefill_b8_h32_t8k: {ms_l:.3f} ms/launch", file=sys.stderr, flush=True)
-        del lg, lo, lS
-        torch.cuda.empty_cache()
+        r = measure_prefill(args, lspec, 64, torch, kda, dev, lsteps, 2, "prefill_b8_h32_t8k")
+        out["prefill_b8_h32_t8k"] = {k_: v_ for k_, v_ in r.items() if k_ != "ms_wall"}
+        print(f"# prefill_b8_h32_t8k: {r['ms_per_launch']:.3f} ms/launch", file=sys.stderr,
+              flush=True)
 
     if "logits" in legs:
         # ---------------- H=16 prefill from raw projections (fused prologue)
@@ -597,21 +653,13 @@ def extras(args, legs, out, torch, kda, wl, dev):
         del lx, grad, gb
         torch.cuda.empty_cache()
 
-    if "longctx" in legs:
-        # ---------------- long context: H=32, T=2^20 prefill, then 256 decode steps
+    if "longctx_decode" in legs:
+        # ---------------- 256 single-sequence decode steps after the long-context prefill
         cspec = wl.PREFILL["longctx_h32_t1m"]
         cg = wl.make_prefill_inputs(cspec, dev)
-        co = torch.empty(cspec.B, cspec.T, cspec.H, cspec.dv, dtype=cspec.dtype, device=dev)
-        cS = torch.empty(cspec.B, cspec.H, cspec.dk, cspec.dv, dtype=torch.float32, device=dev)
-
-        def cstep():
-            kda.prefill_chunked(cg["q"], cg["k"], cg["v"], cg["alpha"], cg["beta"], None,
-                                chunk=64, out=co, state_out=cS)
-
-        ms_c, ms_cw = time_launches(cstep, 2, 1, torch)
-        B, T, H, dk, dv = cspec.B, cspec.T, cspec.H, cspec.dk, cspec.dv
-        cb = prefill_alg_bytes(B, T, H, dk, dv, 2, False)
-        del cg, co
+        _, cS = kda.prefill_chunked(cg["q"], cg["k"], cg["v"], cg["alpha"], cg["beta"], None,
+                                    chunk=64)
+        del cg
         torch.cuda.empty_cache()
         dspec = wl.DECODE["longctx_decode"]
         mask = wl.mixture_low_channels(32, 128, cspec.seed)
@@ -626,20 +674,15 @@ def extras(args, legs, out, torch, kda, wl, dev):
                             cS, out=od)
 
         ms_d, _ = time_launches(dstep, dspec.steps, 8, torch)
-        out["longctx_h32_t1m"] = {
-            "C": 64, "ms_per_prefill": ms_c, "tokens_per_s": B * T / (ms_cw * 1e-3),
-            "prefill_GBps": cb / (ms_c * 1e-3) / 1e9,
-            "prefill_frac_hbm": cb / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "decode_us_per_step": ms_d * 1e3,
+        out["longctx_decode"] = {
+            "N": 1, "H": 32, "steps": dspec.steps, "decode_us_per_step": ms_d * 1e3,
             "decode_note": "one sequence x 32 heads: 4 MiB of state per step; the events "
                            "bracket back-to-back calls from Python, so this includes the "
                            "binding's per-call host time (kernel time: profiles/)",
         }
-        print(f"# longctx_h32_t1m: prefill {ms_c:.2f} ms, decode {ms_d * 1e3:.1f} us/step",
-              file=sys.stderr, flush=True)
+        print(f"# longctx_decode: {ms_d * 1e3:.1f} us/step", file=sys.stderr, flush=True)
         del st, od, cS
         torch.cuda.empty_cache()
-
 
 if __name__ == "__main__":
     main()

@@ -90,28 +90,46 @@ def prefill_workspace_bytes(B, T, H, dk, dv, chunk, dtype=torch.bfloat16) -> int
 
 
 def prefill_chunked(q, k, v, alpha, beta, S0=None, chunk=64, out=None, state_out=None,
-                    return_state=True):
-    """KDA over whole sequences; returns (o, S_T) (S_T None if not requested)."""
-    return _prefill(q, k, v, alpha, beta, S0, chunk, out, state_out, return_state, None)
+                    return_state=True, workspace=None):
+    """KDA over whole sequences; returns (o, S_T) (S_T None if not requested).
+
+    workspace: optional uint8 device tensor of at least prefill_workspace_bytes
+    bytes, reused instead of a fresh allocation per call."""
+    return _prefill(q, k, v, alpha, beta, S0, chunk, out, state_out, return_state, None,
+                    workspace)
 
 
 def prefill_chunked_logits(q, k, v, g, b, S0=None, chunk=64, qk_map="l2", out=None,
-                           state_out=None, return_state=True):
+                           state_out=None, return_state=True, workspace=None):
     """KDA over whole sequences from raw projections: alpha = exp(-softplus(g)),
     beta = sigmoid(b), q and k mapped by qk_map, all inside the kernels."""
     if qk_map not in _QK:
         raise ValueError(f"qk_map {qk_map!r}: expected one of {sorted(_QK)}")
-    return _prefill(q, k, v, g, b, S0, chunk, out, state_out, return_state, _QK[qk_map])
+    return _prefill(q, k, v, g, b, S0, chunk, out, state_out, return_state, _QK[qk_map],
+                    workspace)
 
 
 def gdn_prefill_chunked(q, k, v, a, beta, S0=None, chunk=64, out=None, state_out=None,
-                        return_state=True):
+                        return_state=True, workspace=None):
     """Gated DeltaNet over whole sequences: one gate per token and head
     (a [B,T,H] float32), or DeltaNet with a=None (gate 1)."""
-    return _prefill(q, k, v, a, beta, S0, chunk, out, state_out, return_state, "gdn")
+    return _prefill(q, k, v, a, beta, S0, chunk, out, state_out, return_state, "gdn",
+                    workspace)
 
 
-def _prefill(q, k, v, gate, beta, S0, chunk, out, state_out, return_state, qk):
+def _workspace(ws, ws_bytes, dev):
+    """The caller's workspace tensor (checked), or a fresh one when none is given."""
+    if ws is None:
+        return torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    if ws.device != dev or not ws.is_contiguous():
+        raise ValueError("workspace: must be a contiguous tensor on the inputs' device")
+    if ws.numel() * ws.element_size() < ws_bytes:
+        raise ValueError(f"workspace: {ws.numel() * ws.element_size()} bytes, "
+                         f"{ws_bytes} needed")
+    return ws
+
+
+def _prefill(q, k, v, gate, beta, S0, chunk, out, state_out, return_state, qk, workspace=None):
     """qk: None (per-channel alpha), "gdn" (scalar gate or None), or a QkMap
     code (raw projections with the fused prologue)."""
     L = lib()
@@ -145,7 +163,9 @@ def _prefill(q, k, v, gate, beta, S0, chunk, out, state_out, return_state, qk):
     ws_bytes = int(L.kda_prefill_workspace_bytes(B, T, H, dk, dv, chunk, _DT[dt]))
     if ws_bytes == (1 << 64) - 1:
         raise KDAError(_lib.KDA_ERR_UNSUPPORTED, "kda_prefill_workspace_bytes")
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    ws = _workspace(workspace, ws_bytes, dev)
+    if ws is not None:
+        ws_bytes = ws.numel() * ws.element_size()
     if qk is None:
         st = L.kda_prefill_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S0),
                                    _ptr(o), _ptr(S_T), B, T, H, dk, dv, chunk, _DT[dt],
