@@ -51,7 +51,7 @@ import torch
 from . import _lib
 from ._lib import KDAError  # noqa: F401
 
-__all__ = ["prefill_chunked", "decode_step", "prefill_chunked_logits", "decode_step_logits",
+__all__ = ["prefill_chunked", "prefill_chunked_noalloc", "decode_step", "prefill_chunked_logits", "decode_step_logits",
            "gdn_prefill_chunked", "gdn_decode_step", "decode_step_backward",
            "prefill_backward", "prefill_backward_workspace_bytes", "prologue_forward",
            "prologue_backward", "prefill_backward_logits", "gdn_prefill_backward",
@@ -115,6 +115,38 @@ def gdn_prefill_chunked(q, k, v, a, beta, S0=None, chunk=64, out=None, state_out
     (a [B,T,H] float32), or DeltaNet with a=None (gate 1)."""
     return _prefill(q, k, v, a, beta, S0, chunk, out, state_out, return_state, "gdn",
                     workspace)
+
+
+def prefill_chunked_noalloc(q, k, v, alpha, beta, S0=None, chunk=64, out=None, state_out=None):
+    """prefill_chunked through kda_prefill_chunked_noalloc: the library uses its
+    own fixed device scratch instead of a workspace, and the C call allocates
+    nothing.  Pass `out` and `state_out` to allocate nothing here either.
+    Calls overlapping in time on one GPU must not be issued (they share the
+    scratch).  Returns (o, S_T)."""
+    L = lib()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if q.dtype not in _DT:
+        raise TypeError(f"q: dtype {q.dtype} not supported")
+    dt = q.dtype
+    for n, t, d, sh in (("q", q, dt, (B, T, H, dk)), ("k", k, dt, (B, T, H, dk)),
+                        ("v", v, dt, (B, T, H, dv)), ("alpha", alpha, torch.float32, (B, T, H, dk)),
+                        ("beta", beta, torch.float32, (B, T, H))):
+        _check(n, t, d, sh, dev)
+    if S0 is not None:
+        _check("S0", S0, torch.float32, (B, H, dk, dv), dev)
+    o = torch.empty((B, T, H, dv), dtype=dt, device=dev) if out is None else out
+    _check("out", o, dt, (B, T, H, dv), dev)
+    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) \
+        if state_out is None else state_out
+    _check("state_out", S_T, torch.float32, (B, H, dk, dv), dev)
+    st = L.kda_prefill_chunked_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                       _ptr(S0), _ptr(o), _ptr(S_T), B, T, H, dk, dv, chunk,
+                                       _DT[dt], _stream(dev))
+    if st != _lib.KDA_OK:
+        raise KDAError(st, "kda_prefill_chunked_noalloc")
+    return o, S_T
 
 
 def _workspace(ws, ws_bytes, dev):

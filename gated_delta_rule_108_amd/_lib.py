@@ -20,6 +20,7 @@ KDA_ERR_ALIAS = -5
 KDA_ERR_WORKSPACE = -6
 KDA_ERR_DEVICE = -7
 KDA_ERR_HIP = -8
+KDA_ERR_SCRATCH = -9
 
 KDA_F32 = 0
 KDA_BF16 = 1
@@ -36,6 +37,8 @@ SIGNATURES = {
                                              _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "kda_decode_step": (ctypes.c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _i, _i, _i, _i, _i, _vp]),
+    "kda_prefill_chunked_noalloc": (ctypes.c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                     _i, _i, _i, _i, _i, _i, _i, _vp]),
     "kda_prefill_chunked_logits": (ctypes.c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                     _i, _i, _i, _i, _i, _i, _i, _i, _vp, _sz,
                                                     _vp]),

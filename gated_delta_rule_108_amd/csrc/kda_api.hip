@@ -64,6 +64,8 @@ const char* kda_status_string(kda_status s) {
     case KDA_ERR_WORKSPACE: return "workspace missing or too small";
     case KDA_ERR_DEVICE: return "current device is not gfx950";
     case KDA_ERR_HIP: return "HIP runtime error";
+    case KDA_ERR_SCRATCH:
+      return "sizes need more device scratch than the library's fixed scratch array holds";
   }
   return "unknown status";
 }
@@ -78,6 +80,37 @@ size_t kda_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int C, k
 }
 
 }  // extern "C"
+
+// ----------------------------------------------------------------------------
+// The device scratch of kda_prefill_chunked_noalloc, for callers that cannot
+// allocate device memory: a file-scope device array, one copy per GPU, held
+// until the process ends.  Host code never passes the array's name to a
+// kernel or a copy (on the host the name only stands in for the symbol): the
+// device address of each GPU's copy comes from hipGetSymbolAddress, looked up
+// on the first call on that GPU with it current, and is kept per device.
+// ----------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[kda::kNoallocScratchBytes];
+
+namespace {
+
+std::atomic<void*> g_scratch[kMaxDevices];   // device address of `scratch`, per device
+
+// Device address of the current device's copy of `scratch`.
+kda_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return KDA_ERR_DEVICE;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return KDA_ERR_HIP;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return KDA_OK;
+}
+
+}  // namespace
 
 namespace {
 
@@ -96,7 +129,8 @@ size_t gate_bytes(int gate_in, int dk, size_t esize) {
 kda_status prefill_impl(const void* q, const void* k, const void* v, const void* alpha,
                         const float* beta, const float* S0, void* o, float* S_T, int B, int T,
                         int H, int dk, int dv, int C, kda_dtype dt, int gate_in, int qk_map,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        size_t segment_budget = 0, bool use_scratch = false) {
   C = chunk_run(C);
   if (B < 1 || H < 1 || T < 0) return KDA_ERR_SHAPE;
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
@@ -109,8 +143,13 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const void*
   const void* ptrs[] = {q, k, v, alpha, beta, S0, o, S_T, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return KDA_ERR_ALIGN;
-  const size_t ws_need = kda::prefill_workspace(B, T, H, dk, dv, C, dt == KDA_BF16);
-  if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need)) return KDA_ERR_WORKSPACE;
+  const size_t ws_need =
+      kda::prefill_workspace(B, T, H, dk, dv, C, dt == KDA_BF16, segment_budget);
+  if (use_scratch) {
+    if (ws_need > kda::kNoallocScratchBytes) return KDA_ERR_SCRATCH;
+  } else if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need)) {
+    return KDA_ERR_WORKSPACE;
+  }
 
   const size_t e = (dt == KDA_BF16) ? 2 : 4;
   const size_t ntok = static_cast<size_t>(B) * T * H;
@@ -124,7 +163,7 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const void*
     for (const Span& s : ins)
       if (overlap(so, s)) return KDA_ERR_ALIAS;
   }
-  if (ws_need > 0) {
+  if (ws_need > 0 && !use_scratch) {   // the library's own scratch overlaps no caller buffer
     const Span sw = span(workspace, ws_need);
     const Span all[] = {span(q, ntok * dk * e), span(k, ntok * dk * e), span(v, ntok * dv * e),
                         span(alpha, ga), span(beta, ntok * 4), span(o, ntok * dv * e),
@@ -145,10 +184,16 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const void*
   const kda_status dev = check_device();
   if (dev != KDA_OK) return dev;
   if (!S_T && !has_tokens) return KDA_OK;  // nothing to compute or write
+  if (use_scratch && ws_need > 0) {
+    const kda_status st = scratch_address(&workspace);
+    if (st != KDA_OK) return st;
+    workspace_bytes = kda::kNoallocScratchBytes;
+  }
 
   kda::PrefillArgs a{q,  k,  v,  alpha, beta, S0, o,  S_T,          B,         T,
                      H,  dk, dv, C,     dt == KDA_BF16,   stream, workspace, workspace_bytes,
                      gate_in, qk_map};
+  a.segment_budget = segment_budget;
   if (kda::launch_prefill(a) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
 }
@@ -481,6 +526,30 @@ kda_status kda_prologue_backward(const void* q, const void* k, const void* g, co
   a.backward = true; a.stream = stream;
   if (kda::launch_prologue(a) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
+}
+
+}  // extern "C"
+
+
+extern "C" {
+
+// Every call on a device shares that device's scratch array: the records of
+// one segment and the carried state are overwritten before they are read, so
+// nothing needs clearing between calls, but two calls in flight at once on
+// one device (two streams, two threads) race on it.
+kda_status kda_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* beta, const float* S0,
+                                       void* o, float* S_T, int B, int T, int H, int dk, int dv,
+                                       int C, kda_dtype dt, void* stream) {
+  // Segments of records sized so that the records and the carried state fit
+  // the scratch array: more segments than kda_prefill_chunked may use, with
+  // bit-identical results (a segment boundary does not change the arithmetic).
+  const size_t carry = (B > 0 && H > 0 && dk > 0 && dv > 0)
+                           ? static_cast<size_t>(B) * H * dk * dv * 4 : 0;
+  const size_t budget =
+      carry < kda::kNoallocScratchBytes ? kda::kNoallocScratchBytes - carry : 1;
+  return prefill_impl(q, k, v, alpha, beta, S0, o, S_T, B, T, H, dk, dv, C, dt, kda::kGateAlpha,
+                      0, nullptr, 0, stream, budget, /*use_scratch=*/true);
 }
 
 }  // extern "C"

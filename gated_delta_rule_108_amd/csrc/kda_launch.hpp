@@ -48,6 +48,9 @@ struct PrefillArgs {
   size_t workspace_bytes;
   int gate_in;              // GateIn (kda_device.hpp)
   int qk_map;               // QkMap, used with kGateLogit
+  // Split path: bytes of records per segment (0: the default budget).  The
+  // same value must size the workspace (prefill_workspace).
+  size_t segment_budget = 0;
 };
 
 // The adjoint of one decode step (decode_backward.hip).
@@ -131,7 +134,12 @@ size_t prefill_backward_workspace(int B, int T, int H, int dk, int dv);
 // Returns hipErrorInvalidValue when no compiled kernel covers (dk, C, dtype).
 hipError_t launch_prefill(const PrefillArgs& a);
 bool prefill_supported(int dk, int dv, int C, bool bf16);
-// Device workspace bytes the prefill needs for these sizes (0: none).
-size_t prefill_workspace(int B, int T, int H, int dk, int dv, int C, bool bf16);
+// Bytes of the fixed device scratch array of kda_prefill_chunked_noalloc.
+constexpr size_t kNoallocScratchBytes = size_t{64} << 20;
+
+// Device workspace bytes the prefill needs for these sizes (0: none), with
+// segments of at most `budget` bytes of records (0: the default budget).
+size_t prefill_workspace(int B, int T, int H, int dk, int dv, int C, bool bf16,
+                         size_t budget = 0);
 
 }  // namespace kda

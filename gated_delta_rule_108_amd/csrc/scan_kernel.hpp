@@ -388,15 +388,17 @@ struct SplitPlan {
   size_t records = 0, carry = 0;   // workspace bytes: records, then carry
 };
 
+// budget: bytes of records one segment may hold (kSegmentBudget, or less
+// when the workspace itself is bounded).
 template <typename OpT, int DK, int C>
-SplitPlan split_plan(int B, int T, int H, int dv) {
+SplitPlan split_plan(int B, int T, int H, int dv, size_t budget = kSegmentBudget) {
   SplitPlan p;
   const size_t chains = static_cast<size_t>(B) * H;
   const size_t rec = RecCfg<OpT, DK, C>::bytes(dv);
   p.nc = (T + C - 1) / C;
   if (p.nc == 0) return p;
   const size_t per_chunk = chains * rec;   // one chunk of every chain
-  const size_t segmax = std::max<size_t>(1, kSegmentBudget / per_chunk);
+  const size_t segmax = std::max<size_t>(1, budget / per_chunk);
   p.nseg = static_cast<int>((static_cast<size_t>(p.nc) + segmax - 1) / segmax);
   p.segch = (p.nc + p.nseg - 1) / p.nseg;
   p.records = chains * p.segch * rec;
@@ -405,8 +407,8 @@ SplitPlan split_plan(int B, int T, int H, int dv) {
 }
 
 template <typename OpT, int DK, int C>
-size_t split_workspace_bytes(int B, int T, int H, int dv) {
-  const SplitPlan p = split_plan<OpT, DK, C>(B, T, H, dv);
+size_t split_workspace_bytes(int B, int T, int H, int dv, size_t budget) {
+  const SplitPlan p = split_plan<OpT, DK, C>(B, T, H, dv, budget);
   return p.records + p.carry;
 }
 
@@ -449,7 +451,8 @@ hipError_t launch_split(const PrefillArgs& a) {
   if constexpr (!scan_fits<OpT, DK, C>()) {
     return hipErrorInvalidValue;
   } else {
-    const SplitPlan p = split_plan<OpT, DK, C>(a.B, a.T, a.H, a.dv);
+    const SplitPlan p = split_plan<OpT, DK, C>(a.B, a.T, a.H, a.dv,
+                                               a.segment_budget ? a.segment_budget : kSegmentBudget);
     const long chains = static_cast<long>(a.B) * a.H;
     float* carry = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + p.records);
     // T = 0 still runs one (empty) scan: it copies S0, or zeros, to S_T.
@@ -537,17 +540,17 @@ bool supported_dk(int dv, int C) {
 }
 
 template <typename OpT, int DK, int C>
-size_t workspace_c(int B, int T, int H, int dv) {
+size_t workspace_c(int B, int T, int H, int dv, size_t budget) {
   if (!use_split<OpT, DK, C>(static_cast<long>(B) * H, dv)) return 0;
-  return split_workspace_bytes<OpT, DK, C>(B, T, H, dv);
+  return split_workspace_bytes<OpT, DK, C>(B, T, H, dv, budget);
 }
 
 template <typename OpT, int DK>
-size_t workspace_dk(int B, int T, int H, int dv, int C) {
+size_t workspace_dk(int B, int T, int H, int dv, int C, size_t budget) {
   switch (C) {
-    case 16: return workspace_c<OpT, DK, 16>(B, T, H, dv);
-    case 32: return workspace_c<OpT, DK, 32>(B, T, H, dv);
-    case 64: return workspace_c<OpT, DK, 64>(B, T, H, dv);
+    case 16: return workspace_c<OpT, DK, 16>(B, T, H, dv, budget);
+    case 32: return workspace_c<OpT, DK, 32>(B, T, H, dv, budget);
+    case 64: return workspace_c<OpT, DK, 64>(B, T, H, dv, budget);
   }
   return 0;
 }
@@ -558,14 +561,15 @@ size_t workspace_dk(int B, int T, int H, int dv, int C) {
     return launch_dk<OPT, DK>(a);                                                      \
   }                                                                                    \
   bool prefill_supported_##NAME##_##DK(int dv, int C) { return supported_dk<OPT, DK>(dv, C); } \
-  size_t prefill_workspace_##NAME##_##DK(int B, int T, int H, int dv, int C) {         \
-    return workspace_dk<OPT, DK>(B, T, H, dv, C);                                      \
+  size_t prefill_workspace_##NAME##_##DK(int B, int T, int H, int dv, int C,           \
+                                         size_t budget) {                             \
+    return workspace_dk<OPT, DK>(B, T, H, dv, C, budget);                              \
   }
 
 #define KDA_PREFILL_DECLARE(NAME, DK)                                                  \
   hipError_t launch_prefill_##NAME##_##DK(const PrefillArgs& a);                       \
   bool prefill_supported_##NAME##_##DK(int dv, int C);                                 \
-  size_t prefill_workspace_##NAME##_##DK(int B, int T, int H, int dv, int C);
+  size_t prefill_workspace_##NAME##_##DK(int B, int T, int H, int dv, int C, size_t budget);
 
 KDA_PREFILL_DECLARE(bf16, 16)
 KDA_PREFILL_DECLARE(bf16, 32)

@@ -73,7 +73,9 @@ enum {
   KDA_ERR_ALIAS = -5,       /* an output overlaps an input it may not overlap      */
   KDA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than the query says    */
   KDA_ERR_DEVICE = -7,      /* current device is not gfx950                        */
-  KDA_ERR_HIP = -8          /* a HIP runtime call or kernel launch failed          */
+  KDA_ERR_HIP = -8,         /* a HIP runtime call or kernel launch failed          */
+  KDA_ERR_SCRATCH = -9      /* sizes need more than the fixed device scratch of    */
+                            /* kda_prefill_chunked_noalloc                         */
 };
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -155,6 +157,35 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v,
                                int B, int T, int H, int dk, int dv, int C,
                                kda_dtype dt, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/*
+ * kda_prefill_chunked_noalloc — kda_prefill_chunked for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It takes no workspace; it allocates
+ * nothing and calls no allocating routine.
+ *
+ * Where kda_prefill_chunked needs a workspace (the chunk-record path), this
+ * call uses a device array inside the library instead: 64 MiB, one copy per
+ * GPU, held until the process ends.  It splits the sequence into more
+ * segments than kda_prefill_chunked may use, so that one segment's records
+ * plus the carried state (B*H*dk*dv*4 bytes) fit that array.  The results
+ * are bit-identical to kda_prefill_chunked's for the same arguments.
+ *
+ * Every call on a GPU shares that GPU's array.  Nothing in it needs clearing
+ * between calls, but calls that overlap in time on one GPU (two streams, two
+ * threads) race on it and must not be issued.
+ *
+ * Arguments, layouts and the other errors are those of kda_prefill_chunked,
+ * without workspace and workspace_bytes.  KDA_ERR_SCRATCH: the sizes need
+ * more than the array holds (only when one chunk of every chain plus the
+ * carried state exceeds 64 MiB, which no size the chunk-record path accepts
+ * reaches at dk, dv <= 128).
+ */
+kda_status kda_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* beta,
+                                       const float* S0, void* o, float* S_T,
+                                       int B, int T, int H, int dk, int dv, int C,
+                                       kda_dtype dt, void* stream);
 
 /*
  * kda_prefill_chunked_logits — kda_prefill_chunked with the input prologue

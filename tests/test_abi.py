@@ -67,7 +67,7 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_fifteen_calls():
+def test_header_declares_the_sixteen_calls():
     assert declared_functions() == ["kda_decode_step", "kda_decode_step_backward",
                                     "kda_decode_step_logits",
                                     "kda_gdn_decode_step", "kda_gdn_decode_step_backward",
@@ -75,6 +75,7 @@ def test_header_declares_the_fifteen_calls():
                                     "kda_gdn_prefill_chunked",
                                     "kda_prefill_backward", "kda_prefill_backward_workspace_bytes",
                                     "kda_prefill_chunked", "kda_prefill_chunked_logits",
+                                    "kda_prefill_chunked_noalloc",
                                     "kda_prefill_workspace_bytes", "kda_prologue_backward",
                                     "kda_prologue_forward", "kda_status_string"]
 
@@ -89,7 +90,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     L = _lib()
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         s = L.status_string(code)
         assert s and s != "unknown status"
     assert L.status_string(5) == "unknown status"
@@ -151,6 +152,40 @@ def test_prefill_valid_arguments_reach_the_device_check():
                dict(T=0, q=None, k=None, v=None, alpha=None, beta=None, o=None)):
         st = may_launch(prefill, lib=lib, **kw)
         assert st in (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE), (kw, st)
+
+
+def prefill_noalloc(lib, **kw):
+    a = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), S0=addr(5),
+             o=addr(6), S_T=addr(7), B=1, T=64, H=2, dk=128, dv=128, C=64, dt=1, stream=None)
+    a.update(kw)
+    return lib.kda_prefill_chunked_noalloc(a["q"], a["k"], a["v"], a["alpha"], a["beta"],
+                                           a["S0"], a["o"], a["S_T"], a["B"], a["T"], a["H"],
+                                           a["dk"], a["dv"], a["C"], a["dt"], a["stream"])
+
+
+def test_prefill_noalloc_validation_errors():
+    """The same host checks as kda_prefill_chunked, before any device call
+    (the scratch address is looked up only after them)."""
+    L = _lib()
+    lib = L.load()
+    pn = lambda **kw: prefill_noalloc(lib, **kw)
+    assert pn(q=None) == L.KDA_ERR_NULL and pn(o=None) == L.KDA_ERR_NULL
+    assert pn(B=0) == L.KDA_ERR_SHAPE and pn(T=-1) == L.KDA_ERR_SHAPE
+    assert pn(dk=48) == L.KDA_ERR_UNSUPPORTED and pn(C=8) == L.KDA_ERR_UNSUPPORTED
+    assert pn(dt=0) == L.KDA_ERR_UNSUPPORTED                     # fp32, dk=128, C=64: no fit
+    assert pn(alpha=addr(3) + 4) == L.KDA_ERR_ALIGN
+    assert pn(o=addr(0)) == L.KDA_ERR_ALIAS and pn(S_T=addr(5) + 256) == L.KDA_ERR_ALIAS
+
+
+@host_only
+def test_prefill_noalloc_valid_arguments_reach_the_device_check():
+    L = _lib()
+    lib = L.load()
+    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+    for kw in (dict(), dict(S_T=addr(5)), dict(S0=None), dict(B=8, H=32, T=8192),
+               dict(T=1 << 20, H=32), dict(T=0, q=None, k=None, v=None, alpha=None,
+                                           beta=None, o=None)):
+        assert may_launch(prefill_noalloc, lib=lib, **kw) in ok, kw
 
 
 def test_decode_validation_errors():
