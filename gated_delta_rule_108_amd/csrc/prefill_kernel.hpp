@@ -253,6 +253,14 @@ __device__ __forceinline__ f32x4 mfma(typename Frag<OpT, KS>::T a, typename Frag
   else return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Four floats -> a bf16x4 matrix-core operand (round to nearest even), built
+// from two packed pairs.  (Converting a float vector to a bf16 vector and then
+// reading single elements back out of it was seen to compile every element
+// to element 0; packed pairs and whole-register bit casts avoid that form.)
+__device__ __forceinline__ bf16x4 bf16_quad(float a, float b, float c, float d) {
+  return __builtin_bit_cast(bf16x4, make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d)));
+}
+
 // Products on the matrix cores.  Each call returns A[.., kb..ke) * B[kb..ke, ..]
 // (kb, ke multiples of 16) in fresh accumulators; callers combine partial
 // products with vector adds.  A chain on one accumulator only ever uses one
@@ -518,7 +526,8 @@ struct PCfg {
   static constexpr int kKB = align16(imax(DK, DVT) * LDC * EB);
   static constexpr int kTT = align16(C * LDT * 4);
   static constexpr int kZB = align16(imax(NB, 1) * 16 * LDZ * 4);
-  static constexpr int kYF = align16(imax(NB * (NB - 1) / 2, 1) * 16 * LDZ * 4);
+  static constexpr int kYF = align16(imax(imax(NB * (NB - 1) / 2, 1) * 16 * LDZ * 4,
+                                          (NB * (NB - 1) / 2 + NB) * 64 * 4 * 2));
   static constexpr int kPP = align16(C * LDC * EB);
   static constexpr int kBT = align16(NB * DK * 4);
   static constexpr int kMID = align16(imax(imax(NB * NB, 1) * DK * 4, C * LDC * EB));
@@ -597,6 +606,8 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
   constexpr int LDK = Cf::LDK, LDC = Cf::LDC, LDT = Cf::LDT, LDZ = Cf::LDZ;
   static_assert(Cf::kLds <= kMaxLds, "LDS plan exceeds 160 KiB");
   constexpr bool kBF = sizeof(E) == 2;
+  // bf16 operands: W and U~ by blocked substitution (no off-diagonal Y).
+  constexpr bool kSubst = kBF;
   constexpr int LDO = DVT + 16 / static_cast<int>(sizeof(E));
   constexpr bool kStageO = C * LDO * static_cast<int>(sizeof(E)) <= Cf::kR1;
   using SM = TileMap<Cf::NCB, NJ, NW>;   // state tiles (Cb, Jb)
@@ -616,6 +627,10 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
   float* TT = reinterpret_cast<float*>(smem + Cf::oTT);      // [C][LDT]
   float* ZB = reinterpret_cast<float*>(smem + Cf::oZB);      // [NB-1][16][LDZ]
   float* YF = reinterpret_cast<float*>(smem + Cf::oYF);      // off-diagonal Y blocks, fp32
+  // (bf16 operands) -L_RJ and Y_RR as matrix-core A fragments: fragment f,
+  // lane l = 16 g + i holds elements [i][4g .. 4g + 3] of its 16x16 block
+  E* LF = reinterpret_cast<E*>(smem + Cf::oYF);
+  constexpr int kNLF = NB * (NB - 1) / 2;                    // first Y_RR fragment
   E* PP = reinterpret_cast<E*>(smem + Cf::oPP);              // [C][LDC]
   float* sBT = reinterpret_cast<float*>(smem + Cf::oBT);     // [NB][DK]
   float* sPRE = reinterpret_cast<float*>(smem + Cf::oPRE);   // [NB][DK]
@@ -986,7 +1001,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     // and 1 compute: issued here by all eight waves, the loads queue in the
     // CU's address unit and the last waves reach the barrier ~1.7k cycles
     // late.  (In the first level they would queue behind the value loads.)
-    if (NB != 4 || wave < 2) fetch_gates(more ? t0 + C : t0);
+    if (NB != 4 || wave < 2) fetch_gates(more ? t0 + C : t0);   // waves 2.. issue theirs later
     lds_barrier();
 
     // ================= AP + SD: gated K K^T (-> L in TT) and Q K^T (-> P) tiles.
@@ -1076,6 +1091,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
           // still be reading in this phase: Yb is filled after the barrier.)
 #pragma unroll
           for (int r = 0; r < 16; ++r) TT[(16 * R + r) * LDT + 16 * R + j] = y[r];
+
         }
       } else {
         for (int p = wave - NB; p < Cf::NAP - NB; p += NW - NB) {
@@ -1094,12 +1110,20 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         }
       }
     }
+    // With four blocks and the substitution below, waves 2, 3, 6 and 7 wait
+    // here for waves 4 and 5 (two off-diagonal pairs each): they issue their
+    // next-chunk gate loads now; waves 4 and 5 issue theirs in WU.
+    if constexpr (kSubst) {
+      if (NB == 4 && wave >= 2 && wave != 4 && wave != 5) fetch_gates(more ? t0 + C : t0);
+    }
     lds_barrier();
 
-    // ================= SO: stage beta V (transposed) for U~, then the
-    // off-diagonal blocks of Y, one block row per barrier:
+    // ================= SO: stage beta V (transposed) for U~.  With fp32
+    // operands, then the off-diagonal blocks of Y, one block row per barrier:
     //   Y_RI = -Y_RR * sum_{J=I}^{R-1} L_RJ Y_JI
-    // L stays in TT; off-diagonal Y goes to YF (fp32) and to Yb.
+    // (L stays in TT; off-diagonal Y goes to YF (fp32) and to Yb).  With bf16
+    // operands Y is never formed off the diagonal: WU solves for W and U~ by
+    // blocked substitution instead.
 #pragma unroll
     for (int it = 0; it < Cf::NVT; ++it) {
       const int item = tid + NTH * it;
@@ -1116,6 +1140,28 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       }
     }
     fetch_values(more ? t0 + C : t0);
+    if constexpr (kSubst) {
+      // -L_RJ and Y_RR from TT as bf16 A fragments (LF), one 16x16 block per
+      // wave at a time: lane 16 g + i converts row i, columns 4g .. 4g + 3.
+      {
+        const int lane = tid % kWave;
+        const int gi = lane % 16, gg = lane / 16;
+        for (int f = wave; f < kNLF + NB; f += NW) {
+          int R = f - kNLF, J = R;   // a Y_RR fragment ...
+          if (f < kNLF) {            // ... or the off-diagonal block (R, J), f = yf_block(R, J)
+            R = 1;
+            int rem = f;
+            while (rem >= R) { rem -= R; ++R; }
+            J = rem;
+          }
+          const float4 v = *reinterpret_cast<const float4*>(TT + (16 * R + gi) * LDT + 16 * J + 4 * gg);
+          const float sg = f < kNLF ? -1.f : 1.f;
+          *reinterpret_cast<bf16x4*>(LF + f * 256 + 4 * lane) =
+              bf16_quad(sg * v.x, sg * v.y, sg * v.z, sg * v.w);
+        }
+      }
+      lds_barrier();   // beta V staged, the L and Y_RR fragments in LF
+    } else {
     // diagonal blocks of Y into the operand-type copy
     for (int x = tid; x < NB * 256; x += NTH) {
       const int R = x / 256, r = (x % 256) / 16, j = x % 16;
@@ -1209,11 +1255,125 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     }
     if (NB == 1) lds_barrier();
     }
+    }   // !kSubst
 
     // Y as a matrix-core operand (a copy in the operand type).
     auto ysrc = [&](int R, const Lane& ln) { return Src<OpT>{Yb + 16 * R * LDC, LDC, ln}; };
 
     // ================= WU: W = Y (beta K E) (stored row-major) and U~ = Y (beta V)
+    f32x4 Ureg[UM::RA][UM::CA];
+    if constexpr (kSubst) {
+      // (I + L) [W | U~] = [beta K E | beta V], block row by block row:
+      //   X_R = beta (K E | V)_R - sum_{J<R} L_RJ [W | U~]_J,  [W | U~]_R = Y_RR X_R
+      // with L_RJ and Y_RR = (I + L_RR)^-1 from TT.  One wave owns whole
+      // 16-column tiles of [U~ | W] over every block row, so the solve needs
+      // no barrier: a 16x16x16 matrix-core result sits in exactly the lane
+      // layout of the next product's B operand (lane (g, i) holds rows 4g..4g+3
+      // of column i), and the solved blocks stay in registers as bf16 B
+      // operands for the block rows below.  U~ tiles come first so that, with
+      // a 128-column slab, wave w owns U~ column tile w: the tile the output
+      // map UM gives it, so U~ stays in fp32 registers.  Otherwise U~ goes
+      // back over beta V (bf16, in place) for the UM owners.
+      constexpr int NCOL = NJ + Cf::NCB;
+      constexpr int NCW = (NCOL + NW - 1) / NW;   // column tiles per wave
+      constexpr bool kUdirect = NJ == NW && UM::RA == NB && UM::CA == 1 && UM::WC == NW;
+      const Lane ln = lane_now();
+      // -L_RJ and Y_RR as bf16 A operands, shared by this wave's columns, and
+      // every column's right-hand side, all loaded before the first product so
+      // that the products of the columns interleave without waiting on LDS.
+      bf16x4 la[kNLF + 1], ya[NB];
+      {
+        const int lane = tid % kWave;
+#pragma unroll
+        for (int f = 0; f < kNLF; ++f) la[f] = *reinterpret_cast<const bf16x4*>(LF + f * 256 + 4 * lane);
+#pragma unroll
+        for (int R = 0; R < NB; ++R)
+          ya[R] = *reinterpret_cast<const bf16x4*>(LF + (kNLF + R) * 256 + 4 * lane);
+      }
+      E* xs[NCW];
+      bool isU[NCW], live[NCW];
+      f32x4 rhs[NCW][NB];
+#pragma unroll
+      for (int ci = 0; ci < NCW; ++ci) {
+        const int col = wave + NW * ci;
+        live[ci] = NCOL % NW == 0 || col < NCOL;
+        const int cc = live[ci] ? col : 0;   // a dead slot reads column 0 and stores nothing
+        isU[ci] = cc < NJ;
+        xs[ci] = (isU[ci] ? VbT + 16 * cc * LDC : KbT + 16 * (cc - NJ) * LDC) + ln.i * LDC +
+                 4 * ln.g;
+#pragma unroll
+        for (int R = 0; R < NB; ++R) rhs[ci][R] = Acc4<OpT>::cvt(Acc4<OpT>::load(xs[ci] + 16 * R));
+      }
+      // Q E = Q F * (decay of the blocks before), in place (P is done with Q F);
+      // independent LDS work that overlaps the products below.
+      {
+        constexpr int NQ = C * DK / 8;   // 16-byte units of 8 elements
+        auto qe = [&](int x) {
+          const int r = x / (DK / 8), c = 8 * (x % (DK / 8));
+          u32x4* qp = reinterpret_cast<u32x4*>(Qr + r * LDK + c);
+          const float4* pr = reinterpret_cast<const float4*>(sPRE + (r / 16) * DK + c);
+          const float4 p0 = pr[0], p1 = pr[1];
+          const u32x4 v = *qp;
+          *qp = u32x4{pack_bf16x2(vec_elem<OpT>(v, 0) * p0.x, vec_elem<OpT>(v, 1) * p0.y),
+                      pack_bf16x2(vec_elem<OpT>(v, 2) * p0.z, vec_elem<OpT>(v, 3) * p0.w),
+                      pack_bf16x2(vec_elem<OpT>(v, 4) * p1.x, vec_elem<OpT>(v, 5) * p1.y),
+                      pack_bf16x2(vec_elem<OpT>(v, 6) * p1.z, vec_elem<OpT>(v, 7) * p1.w)};
+        };
+        if constexpr (NQ % NTH == 0) {
+#pragma unroll
+          for (int k = 0; k < NQ / NTH; ++k) qe(tid + NTH * k);
+        } else {
+          for (int x = tid; x < NQ; x += NTH) qe(x);
+        }
+      }
+      bf16x4 ob[NCW][NB];
+#pragma unroll
+      for (int R = 0; R < NB; ++R) {
+        f32x4 out[NCW];
+#pragma unroll
+        for (int ci = 0; ci < NCW; ++ci) {
+          f32x4 x = rhs[ci][R];
+#pragma unroll
+          for (int J = 0; J < R; ++J) x = mfma<OpT, 16>(la[yf_block(R, J)], ob[ci][J], x);
+          out[ci] = mfma<OpT, 16>(ya[R], bf16_quad(x[0], x[1], x[2], x[3]), zero4());
+          ob[ci][R] = bf16_quad(out[ci][0], out[ci][1], out[ci][2], out[ci][3]);
+        }
+#pragma unroll
+        for (int ci = 0; ci < NCW; ++ci) {
+          if (!live[ci]) continue;
+          if (isU[ci]) {
+            if constexpr (kUdirect) {
+              if (ci == 0) Ureg[R][0] = out[ci];   // col == wave == UM::col0(wave)
+            } else {
+              Acc4<OpT>::store(xs[ci] + 16 * R, out[ci]);
+            }
+          } else {
+            // W[16R + 4g + r][16 (col - NJ) + i], row-major for the matrix-core A operand
+            E* wd = Wm + (16 * R + 4 * ln.g) * LDK + 16 * (wave + NW * ci - NJ) + ln.i;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wd[r * LDK] = Ty<OpT>::from_f32(out[ci][r]);
+          }
+        }
+      }
+      // gate prefetch of waves 4 and 5, the slowest in the A/P phase (see there)
+      if (NB == 4 && (wave == 4 || wave == 5)) fetch_gates(more ? t0 + C : t0);
+      lds_barrier();
+      if constexpr (!kUdirect) {
+#pragma unroll
+        for (int a = 0; a < UM::RA; ++a)
+#pragma unroll
+          for (int bb = 0; bb < UM::CA; ++bb) {
+            Ureg[a][bb] = zero4();
+            if (UM::active(wave)) {
+              const int R = UM::row0(wave) + a, Jb = UM::col0(wave) + bb;
+              Ureg[a][bb] = Acc4<OpT>::cvt(
+                  Acc4<OpT>::load(VbT + (16 * Jb + ln.i) * LDC + 16 * R + 4 * ln.g));
+            }
+          }
+        // the scan below writes S^T over beta V: every wave must have read U~
+        if constexpr (!kPrep) lds_barrier();
+      }
+    } else {
     // Q E = Q F * (decay of the blocks before), in place: P is done with Q F.
     for (int x = tid; x < C * DK / 2; x += NTH) {
       const int r = x / (DK / 2), c = 2 * (x % (DK / 2));
@@ -1222,7 +1382,6 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       const PT v = *qp;
       *qp = Pair<OpT>::pack(Pair<OpT>::get(v, 0) * pr[0], Pair<OpT>::get(v, 1) * pr[1]);
     }
-    f32x4 Ureg[UM::RA][UM::CA];
     {
       const Lane ln = lane_now();
       // W^T tiles (Cb, R) cost 16 (R + 1) of contraction: tile t = wave + NW i
@@ -1254,6 +1413,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       }
     }
     lds_barrier();
+    }   // !kSubst
 
     if constexpr (kPrep) {
       // chunk record -> workspace: operand packets, decay, U~ (this slab is all of dv)
