@@ -257,6 +257,15 @@ __device__ __forceinline__ f32x4 mfma(typename Frag<OpT, KS>::T a, typename Frag
 // from two packed pairs.  (Converting a float vector to a bf16 vector and then
 // reading single elements back out of it was seen to compile every element
 // to element 0; packed pairs and whole-register bit casts avoid that form.)
+// Lane move inside each row of 16 lanes (CDNA data-parallel primitives:
+// 0x100 + d = row_shl:d, lane l reads lane l + d; 0x110 + d = row_shr:d, lane
+// l reads lane l - d); lanes whose source falls outside the row read 1.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_or_one(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x), kCtrl,
+                                                    0xF, 0xF, false));
+}
+
 __device__ __forceinline__ bf16x4 bf16_quad(float a, float b, float c, float d) {
   return __builtin_bit_cast(bf16x4, make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d)));
 }
@@ -640,6 +649,21 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
   float* sGC = reinterpret_cast<float*>(smem + Cf::oGC);     // [DK]
   float* sBE = reinterpret_cast<float*>(smem + Cf::oBE);     // [C]
   int* sFL = reinterpret_cast<int*>(smem + Cf::oFL);         // [NB]
+  // One gate per row: per-row decays in LDS the per-channel path uses for
+  // its gated copies of K (idle here until beta V is staged after the A/P
+  // products) and for its decay table before each block (idle up to Q E).
+  // The gates, the within-block prefix / suffix products, the decays between
+  // blocks and E' (decay to the chunk end) are read up to the A/P products,
+  // E (decay from the chunk start) up to Q E.
+  float* sRowA = reinterpret_cast<float*>(smem + Cf::oZ1);   // [C]
+  float* sRowF = sRowA + C;          // [C]
+  float* sRowH = sRowA + 2 * C;      // [C]
+  float* sRowEp = sRowA + 3 * C;     // [C]
+  float* sRowMID = sRowA + 4 * C;    // [NB][NB]
+  float* sRowE = sPRE;               // [C]
+  static_assert(!kScalar || ((4 * C + NB * NB) * 4 <= 2 * C * LDK * static_cast<int>(sizeof(E)) &&
+                             C <= NB * DK && C <= kWave),
+                "per-row gate tables");
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -710,6 +734,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
   QT gkk[Cf::NGT][4], gqq[Cf::NGT][4];
   u32x4 gvv[Cf::NVT][4];
   float gbe = 0.f;
+  float gsa = 1.f;              // scalar gate of row `lane` (wave 0, kScalar)
   auto fetch_gates = [&](int tn) {
     const size_t base = (row0 + static_cast<size_t>(tn) * H) * DK;
     const float* pa = galpha + base;
@@ -731,10 +756,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
           if constexpr (kLogit) {
             gg[it][j] = Quad<OpT>::load(pg + off);
           } else if constexpr (kScalar) {
-            const size_t tr = row0 + static_cast<size_t>(tn + min(16 * J + 4 * h + j, jmax)) * H;
-            const float a = has_gate ? galpha[tr] : 1.f;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) ga[it][j][x] = a;
+            // one gate per row: fetched below by wave 0, lane = row
           } else {
             const float4 a4 = *reinterpret_cast<const float4*>(pa + off);
             ga[it][j][0] = a4.x;
@@ -746,6 +768,10 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
           gqq[it][j] = Quad<OpT>::load(pq + off);
         }
       }
+    }
+    if constexpr (kScalar) {
+      if (wave == 0 && has_gate)
+        gsa = galpha[row0 + static_cast<size_t>(tn + min(tid, jmax)) * H];
     }
   };
   auto fetch_values = [&](int tn) {
@@ -825,7 +851,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
           }
         }
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
+        for (int x = 0; x < 4 && !kScalar; ++x) {
           // r_s = product of quarter (h - s) mod 4; the block total is the
           // same two pair products in every lane, (p_h p_h+2)(p_h+1 p_h+3).
           const float p = ga[it][0][x] * ga[it][1][x] * ga[it][2][x] * ga[it][3][x];
@@ -834,7 +860,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
           hoff[it][x] = h == 3 ? 1.f : h == 2 ? r3 : h == 1 ? r3 * r2 : (r3 * r2) * r1;
           bt[it][x] = (p * r2) * (r1 * r3);
         }
-        if (h == 0)
+        if (!kScalar && h == 0)
           *reinterpret_cast<float4*>(sBT + J * DK + c) =
               make_float4(bt[it][0], bt[it][1], bt[it][2], bt[it][3]);
       }
@@ -892,10 +918,62 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         }
       }
     }
+    if constexpr (kScalar) {
+      // One gate per row: wave 0, lane r = row r, makes every per-row decay
+      // with lane products (DPP within each 16-row block, lane reads across
+      // blocks).  Only products: an exact zero gate stays exact.
+      //   F_r  = prod of a from the block start through r     (inclusive)
+      //   H_r  = prod of a after r to the block end           (exclusive)
+      //   BT_J = block total, E_r = prod_{J<R} BT_J F_r, E'_r = H_r prod_{J>R} BT_J
+      //   MID(R, I) = prod_{I<J<R} BT_J, the chunk decay = prod_J BT_J
+      if (wave == 0) {
+        const int r = tid;
+        const float a = (r < C && t0 + r < T) ? gsa : 1.f;
+        float F = a, Hin = a;   // inclusive prefix / suffix products within the block
+        F *= dpp_or_one<0x111>(F);
+        Hin *= dpp_or_one<0x101>(Hin);
+        F *= dpp_or_one<0x112>(F);
+        Hin *= dpp_or_one<0x102>(Hin);
+        F *= dpp_or_one<0x114>(F);
+        Hin *= dpp_or_one<0x104>(Hin);
+        F *= dpp_or_one<0x118>(F);
+        Hin *= dpp_or_one<0x108>(Hin);
+        const float Hx = dpp_or_one<0x101>(Hin);   // exclusive suffix
+        float bt[4], all = 1.f;
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          bt[J] = J < NB ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(F), 16 * J + 15)) : 1.f;
+          all *= bt[J];
+        }
+        const int R = r / 16;
+        float pre = 1.f, suf = 1.f;
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          if (J < R) pre *= bt[J];
+          if (J > R && J < NB) suf *= bt[J];
+        }
+        if (r < C) {
+          sRowA[r] = a;
+          sRowF[r] = F;
+          sRowH[r] = Hx;
+          sRowE[r] = pre * F;
+          sRowEp[r] = Hx * suf;
+        }
+        if (r < NB * NB) {   // MID(R, I) at R * NB + I
+          const int RR = r / NB, II = r % NB;
+          float m = 1.f;
+#pragma unroll
+          for (int J = 0; J < 4; ++J)
+            if (J > II && J < RR) m *= bt[J];
+          sRowMID[r] = m;
+        }
+        for (int c = r; c < DK; c += kWave) sGC[c] = all;
+      }
+    }
     lds_barrier();
 
     // ================= G2: chunk-level gate products and MFMA operands
-    if (tid < DK) {
+    if (!kScalar && tid < DK) {
       const int c = tid;
       float acc = 1.f;
       for (int J = 0; J < NB; ++J) {
@@ -911,7 +989,39 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         }
     }
 #pragma unroll
-    for (int it = 0; it < Cf::NGT; ++it) {
+    for (int it = 0; it < Cf::NGT && kScalar; ++it) {
+      // One gate per row: K and Q go to the A/P products unscaled (the decay
+      // is a per-row-pair scalar applied to the product tiles), beta K E and
+      // K E' are rows scaled by one value each.
+      const int item = tid + NTH * it;
+      if (Cf::NGI % NTH == 0 || item < Cf::NGI) {
+        const ItemPos ip = item_pos<DK / 4>(item);
+        const int h = ip.h, J = ip.J, c = 4 * ip.v;
+        float kb[4][4], kg[4][4];   // [channel][row of the quarter]
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * J + 4 * h + j;
+          const float be = sBE[r] * sRowE[r], ep = sRowEp[r];
+          float kk[4], qq[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            kk[x] = Quad<OpT>::get(gkk[it][j], x);
+            qq[x] = Quad<OpT>::get(gqq[it][j], x);
+            kb[x][j] = be * kk[x];
+            kg[x][j] = ep * kk[x];
+          }
+          Quad<OpT>::store(Kr + r * LDK + c, kk[0], kk[1], kk[2], kk[3]);
+          Quad<OpT>::store(Qr + r * LDK + c, qq[0], qq[1], qq[2], qq[3]);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          Quad<OpT>::store(KbT + (c + x) * LDC + 16 * J + 4 * h, kb[x][0], kb[x][1], kb[x][2], kb[x][3]);
+          Quad<OpT>::store(KgT + (c + x) * LDC + 16 * J + 4 * h, kg[x][0], kg[x][1], kg[x][2], kg[x][3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < Cf::NGT && !kScalar; ++it) {
       const int item = tid + NTH * it;
       if (Cf::NGI % NTH == 0 || item < Cf::NGI) {
         const ItemPos ip = item_pos<DK / 4>(item);
@@ -1024,9 +1134,29 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       if (wave < NB) {
         const int R = wave;
         f32x4 accA, accP;
-        mma_k2<OpT>(accA, accP, 0, DK, Src<OpT>{Kr + 16 * R * LDK, LDK, ln},
-                    Src<OpT>{Qr + 16 * R * LDK, LDK, ln}, Src<OpT>{Kinv + 16 * R * LDK, LDK, ln});
-        if (sFL[R]) {
+        if constexpr (kScalar) {
+          // decay from column i to row r inside block R: the gates of rows
+          // i+1 .. r, multiplied out (no division, no underflow short of the
+          // true value's)
+          mma_k2<OpT>(accA, accP, 0, DK, Src<OpT>{Kr + 16 * R * LDK, LDK, ln},
+                      Src<OpT>{Qr + 16 * R * LDK, LDK, ln}, Src<OpT>{Kr + 16 * R * LDK, LDK, ln});
+          const float* ar = sRowA + 16 * R;
+          float p = 1.f;
+#pragma unroll
+          for (int j = 1; j < 16; ++j)
+            if (j > ln.i && j < 4 * ln.g) p *= ar[j];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int rl = 4 * ln.g + rr;
+            if (rl > ln.i) p *= ar[rl];
+            accA[rr] *= p;
+            accP[rr] *= p;
+          }
+        } else {
+          mma_k2<OpT>(accA, accP, 0, DK, Src<OpT>{Kr + 16 * R * LDK, LDK, ln},
+                      Src<OpT>{Qr + 16 * R * LDK, LDK, ln}, Src<OpT>{Kinv + 16 * R * LDK, LDK, ln});
+        }
+        if (!kScalar && sFL[R]) {
           // Channels whose block decay fell below 2^-100: exact pairwise
           // products of alpha on the vector units.
           const size_t cb = (row0 + static_cast<size_t>(t0 + 16 * R) * H) * DK;
@@ -1100,7 +1230,18 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
           const int I = rem;
           f32x4 accA, accP;
           const Src<OpT> sKr{Kr + 16 * R * LDK, LDK, ln}, sQr{Qr + 16 * R * LDK, LDK, ln};
-          if (R == I + 1) {
+          if constexpr (kScalar) {
+            // rows i+1 .. r = the rest of block I, the blocks between, and
+            // block R through r
+            mma_k2<OpT>(accA, accP, 0, DK, sKr, sQr, Src<OpT>{Kr + 16 * I * LDK, LDK, ln});
+            const float m = sRowMID[R * NB + I] * sRowH[16 * I + ln.i];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const float g = sRowF[16 * R + 4 * ln.g + rr] * m;
+              accA[rr] *= g;
+              accP[rr] *= g;
+            }
+          } else if (R == I + 1) {
             mma_k2<OpT>(accA, accP, 0, DK, sKr, sQr, Src<OpT>{Ki + 16 * I * LDK, LDK, ln});
           } else {
             mma_k2<OpT>(accA, accP, 0, DK, sKr, sQr,
@@ -1311,8 +1452,15 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         auto qe = [&](int x) {
           const int r = x / (DK / 8), c = 8 * (x % (DK / 8));
           u32x4* qp = reinterpret_cast<u32x4*>(Qr + r * LDK + c);
-          const float4* pr = reinterpret_cast<const float4*>(sPRE + (r / 16) * DK + c);
-          const float4 p0 = pr[0], p1 = pr[1];
+          float4 p0, p1;
+          if constexpr (kScalar) {
+            const float e = sRowE[r];
+            p0 = p1 = make_float4(e, e, e, e);
+          } else {
+            const float4* pr = reinterpret_cast<const float4*>(sPRE + (r / 16) * DK + c);
+            p0 = pr[0];
+            p1 = pr[1];
+          }
           const u32x4 v = *qp;
           *qp = u32x4{pack_bf16x2(vec_elem<OpT>(v, 0) * p0.x, vec_elem<OpT>(v, 1) * p0.y),
                       pack_bf16x2(vec_elem<OpT>(v, 2) * p0.z, vec_elem<OpT>(v, 3) * p0.w),
@@ -1378,9 +1526,10 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     for (int x = tid; x < C * DK / 2; x += NTH) {
       const int r = x / (DK / 2), c = 2 * (x % (DK / 2));
       PT* qp = reinterpret_cast<PT*>(Qr + r * LDK + c);
-      const float* pr = sPRE + (r / 16) * DK + c;
+      const float p0 = kScalar ? sRowE[r] : sPRE[(r / 16) * DK + c];
+      const float p1 = kScalar ? sRowE[r] : sPRE[(r / 16) * DK + c + 1];
       const PT v = *qp;
-      *qp = Pair<OpT>::pack(Pair<OpT>::get(v, 0) * pr[0], Pair<OpT>::get(v, 1) * pr[1]);
+      *qp = Pair<OpT>::pack(Pair<OpT>::get(v, 0) * p0, Pair<OpT>::get(v, 1) * p1);
     }
     {
       const Lane ln = lane_now();
