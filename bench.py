@@ -601,6 +601,14 @@ def extras(args, legs, out, torch, kda, wl, dev):
         ms_p, _ = time_launches(pbstep, 5, 1, torch)
         B, T, H, dk, dv = pspec.B, pspec.T, pspec.H, pspec.dk, pspec.dv
         pbytes = prefill_bwd_alg_bytes(B, T, H, dk, dv, 2)
+        cws = torch.empty(kda.prefill_backward_chunked_workspace_bytes(B, T, H, dk, dv),
+                          dtype=torch.uint8, device=dev)
+
+        def cbstep():
+            kda.prefill_backward_chunked(px["q"], px["k"], px["v"], px["alpha"], px["beta"],
+                                         pg["dO"], S0=px["S0"], dS_T=pg["dS_T"], workspace=cws)
+
+        ms_c, _ = time_launches(cbstep, 20, 3, torch)
         gx = wl.make_gdn_inputs(pspec, dev)
 
         def gbstep():
@@ -609,17 +617,42 @@ def extras(args, legs, out, torch, kda, wl, dev):
 
         ms_g, _ = time_launches(gbstep, 5, 1, torch)
         out["prefill_bwd_h16_t4k"] = {
-            "ms_per_call": ms_p, "tokens_per_s": B * T / (ms_p * 1e-3),
-            "alg_GBps": pbytes / (ms_p * 1e-3) / 1e9,
-            "frac_hbm": pbytes / (ms_p * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kernel": "kda_prefill_backward_chunked (forward split path with chunk states, "
+                      "sub-chunk records, state-gradient scan, gradient kernel)",
+            "ms_per_call": ms_c, "tokens_per_s": B * T / (ms_c * 1e-3),
+            "alg_GBps": pbytes / (ms_c * 1e-3) / 1e9,
+            "frac_hbm": pbytes / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "alg_bytes_per_call": pbytes, "traffic": profiled_traffic("prefill_bwd_h16_t4k"),
-            "gdn_ms_per_call": ms_g,
-            "note": "token-sequential walk per (head, 8-column slab): bound by the per-token "
-                    "dependency chain, not by HBM; the chunked adjoint is the next step",
+            "deterministic": True,
+            "token_walk_ms_per_call": ms_p,
+            "gdn_token_walk_ms_per_call": ms_g,
         }
-        print(f"# prefill_bwd_h16_t4k: {ms_p:.3f} ms/call (Gated DeltaNet {ms_g:.3f} ms)",
-              file=sys.stderr, flush=True)
-        del px, pg, gx
+        print(f"# prefill_bwd_h16_t4k: chunked {ms_c:.3f} ms/call, token walk {ms_p:.3f} ms "
+              f"(Gated DeltaNet {ms_g:.3f} ms)", file=sys.stderr, flush=True)
+        del px, pg, gx, cws
+        torch.cuda.empty_cache()
+        # the largest batch, chunked only
+        lspec = wl.PREFILL["prefill_b8_h32_t8k"]
+        lx = wl.make_prefill_inputs(lspec, dev)
+        lg = wl.make_prefill_backward_grads(lspec, dev)
+        B, T, H, dk, dv = lspec.B, lspec.T, lspec.H, lspec.dk, lspec.dv
+        lws = torch.empty(kda.prefill_backward_chunked_workspace_bytes(B, T, H, dk, dv),
+                          dtype=torch.uint8, device=dev)
+
+        def lbstep():
+            kda.prefill_backward_chunked(lx["q"], lx["k"], lx["v"], lx["alpha"], lx["beta"],
+                                         lg["dO"], S0=lx["S0"], dS_T=lg["dS_T"], workspace=lws)
+
+        ms_l, _ = time_launches(lbstep, 5, 1, torch)
+        lbytes = prefill_bwd_alg_bytes(B, T, H, dk, dv, 2)
+        out["prefill_bwd_b8_h32_t8k"] = {
+            "ms_per_call": ms_l, "tokens_per_s": B * T / (ms_l * 1e-3),
+            "alg_GBps": lbytes / (ms_l * 1e-3) / 1e9,
+            "frac_hbm": lbytes / (ms_l * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "alg_bytes_per_call": lbytes, "traffic": profiled_traffic("prefill_bwd_b8_h32_t8k"),
+        }
+        print(f"# prefill_bwd_b8_h32_t8k: chunked {ms_l:.3f} ms/call", file=sys.stderr, flush=True)
+        del lx, lg, lws
         torch.cuda.empty_cache()
 
     if "prologue" in legs:

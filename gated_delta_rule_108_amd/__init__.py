@@ -53,7 +53,8 @@ from ._lib import KDAError  # noqa: F401
 
 __all__ = ["prefill_chunked", "prefill_chunked_noalloc", "decode_step", "prefill_chunked_logits", "decode_step_logits",
            "gdn_prefill_chunked", "gdn_decode_step", "decode_step_backward",
-           "prefill_backward", "prefill_backward_workspace_bytes", "prologue_forward",
+           "prefill_backward", "prefill_backward_workspace_bytes", "prefill_backward_chunked",
+           "prefill_backward_chunked_workspace_bytes", "prologue_forward",
            "prologue_backward", "prefill_backward_logits", "gdn_prefill_backward",
            "gdn_decode_step_backward",
            "prefill_workspace_bytes", "KDAError", "lib"]
@@ -328,7 +329,11 @@ def prefill_backward_workspace_bytes(B, T, H, dk, dv) -> int:
     return int(lib().kda_prefill_backward_workspace_bytes(B, T, H, dk, dv))
 
 
-def _prefill_backward(q, k, v, alpha, beta, dO, S0, dS_T, gdn):
+def prefill_backward_chunked_workspace_bytes(B, T, H, dk, dv) -> int:
+    return int(lib().kda_prefill_backward_chunked_workspace_bytes(B, T, H, dk, dv))
+
+
+def _prefill_backward(q, k, v, alpha, beta, dO, S0, dS_T, gdn, chunked=False, workspace=None):
     L = lib()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -353,16 +358,18 @@ def _prefill_backward(q, k, v, alpha, beta, dO, S0, dS_T, gdn):
     g_a = None if alpha is None else torch.empty(gate_shape, dtype=f32, device=dev)
     g_b = torch.empty((B, T, H), dtype=f32, device=dev)
     g_S = torch.empty((B, H, dk, dv), dtype=f32, device=dev)
-    nws = prefill_backward_workspace_bytes(B, T, H, dk, dv)
+    wsfn = prefill_backward_chunked_workspace_bytes if chunked else prefill_backward_workspace_bytes
+    nws = wsfn(B, T, H, dk, dv)
     if nws == (1 << 64) - 1:                      # (size_t)-1: sizes not supported
-        raise KDAError(_lib.KDA_ERR_UNSUPPORTED, "kda_prefill_backward_workspace_bytes")
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
-    fn = L.kda_gdn_prefill_backward if gdn else L.kda_prefill_backward
-    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_T),
-            _ptr(g_q), _ptr(g_k), _ptr(g_v), _ptr(g_a), _ptr(g_b), _ptr(g_S), B, T, H, dk, dv,
-            _DT[dt], _ptr(ws), nws, _stream(dev))
+        raise KDAError(_lib.KDA_ERR_UNSUPPORTED, wsfn.__name__)
+    ws = _workspace(workspace, nws, dev)
+    name = ("kda_prefill_backward_chunked" if chunked else
+            "kda_gdn_prefill_backward" if gdn else "kda_prefill_backward")
+    st = getattr(L, name)(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(dO),
+                          _ptr(dS_T), _ptr(g_q), _ptr(g_k), _ptr(g_v), _ptr(g_a), _ptr(g_b),
+                          _ptr(g_S), B, T, H, dk, dv, _DT[dt], _ptr(ws), nws, _stream(dev))
     if st != _lib.KDA_OK:
-        raise KDAError(st, "kda_gdn_prefill_backward" if gdn else "kda_prefill_backward")
+        raise KDAError(st, name)
     return g_q, g_k, g_v, g_a, g_b, g_S
 
 
@@ -372,6 +379,15 @@ def prefill_backward(q, k, v, alpha, beta, dO, S0=None, dS_T=None):
     float32, returns (dq, dk, dv, dalpha, dbeta, dS0), all float32, shaped
     like q, k, v, alpha, beta and the state."""
     return _prefill_backward(q, k, v, alpha, beta, dO, S0, dS_T, gdn=False)
+
+
+def prefill_backward_chunked(q, k, v, alpha, beta, dO, S0=None, dS_T=None, workspace=None):
+    """prefill_backward in chunk form on the matrix cores (bf16, dk = dv =
+    128): the same gradients, within the bf16 bar instead of fp32 rounding,
+    deterministic, with no float atomics.  `workspace`: an optional uint8
+    device tensor of at least prefill_backward_chunked_workspace_bytes."""
+    return _prefill_backward(q, k, v, alpha, beta, dO, S0, dS_T, gdn=False, chunked=True,
+                             workspace=workspace)
 
 
 def gdn_prefill_backward(q, k, v, a, beta, dO, S0=None, dS_T=None):

@@ -52,6 +52,8 @@ SIGNATURES = {
     "kda_prefill_backward_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "kda_prefill_backward": (ctypes.c_int32, [_vp] * 14 + [_i] * 6 + [_vp, _sz, _vp]),
     "kda_gdn_prefill_backward": (ctypes.c_int32, [_vp] * 14 + [_i] * 6 + [_vp, _sz, _vp]),
+    "kda_prefill_backward_chunked_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "kda_prefill_backward_chunked": (ctypes.c_int32, [_vp] * 14 + [_i] * 6 + [_vp, _sz, _vp]),
     "kda_gdn_decode_step_backward": (ctypes.c_int32, [_vp] * 14 + [_i, _i, _i, _i, _i, _vp]),
     "kda_prologue_forward": (ctypes.c_int32, [_vp] * 8 + [_i] * 4 + [_vp]),
     "kda_prologue_backward": (ctypes.c_int32, [_vp] * 12 + [_i] * 4 + [_vp]),

@@ -371,10 +371,12 @@ kda_status prefill_backward_impl(const void* q, const void* k, const void* v, co
                                  const float* dS_T, float* dq, float* dk, float* dv,
                                  float* dalpha, float* dbeta, float* dS0, int B, int T, int H,
                                  int dk_, int dv_, kda_dtype dt, void* workspace,
-                                 size_t workspace_bytes, void* stream, int gate_in) {
+                                 size_t workspace_bytes, void* stream, int gate_in,
+                                 bool chunked = false) {
   if (B < 1 || H < 1 || T < 0) return KDA_ERR_SHAPE;
   if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   if (!dim_ok(dk_) || !dim_ok(dv_)) return KDA_ERR_UNSUPPORTED;
+  if (chunked && (dt != KDA_BF16 || dk_ != 128 || dv_ != 128)) return KDA_ERR_UNSUPPORTED;
   const bool has_tokens = T > 0;
   // the scalar gate is optional (NULL: 1, DeltaNet); then so is its gradient
   const bool scalar = gate_in == kda::kGateScalar;
@@ -385,7 +387,8 @@ kda_status prefill_backward_impl(const void* q, const void* k, const void* v, co
                         dq, dk, dv, dalpha, dbeta, dS0, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return KDA_ERR_ALIGN;
-  const size_t ws_need = kda::prefill_backward_workspace(B, T, H, dk_, dv_);
+  const size_t ws_need = chunked ? kda::prefill_backward_chunked_workspace(B, T, H, dk_, dv_)
+                                 : kda::prefill_backward_workspace(B, T, H, dk_, dv_);
   if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need)) return KDA_ERR_WORKSPACE;
 
   const size_t e = (dt == KDA_BF16) ? 2 : 4;
@@ -416,7 +419,9 @@ kda_status prefill_backward_impl(const void* q, const void* k, const void* v, co
                         dt == KDA_BF16, stream};
   a.gate_in = gate_in;
   if (scalar && !alpha) a.g_alpha = nullptr;   // DeltaNet: no gate, no gate gradient
-  if (kda::launch_prefill_backward(a) != hipSuccess) return KDA_ERR_HIP;
+  const hipError_t err =
+      chunked ? kda::launch_prefill_backward_chunked(a) : kda::launch_prefill_backward(a);
+  if (err != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
 }
 
@@ -433,6 +438,22 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
   return prefill_backward_impl(q, k, v, alpha, beta, S0, dO, dS_T, dq, dk, dv, dalpha, dbeta, dS0,
                                B, T, H, dk_, dv_, dt, workspace, workspace_bytes, stream,
                                kda::kGateAlpha);
+}
+
+size_t kda_prefill_backward_chunked_workspace_bytes(int B, int T, int H, int dk, int dv) {
+  if (B < 1 || H < 1 || T < 0 || dk != 128 || dv != 128) return static_cast<size_t>(-1);
+  return kda::prefill_backward_chunked_workspace(B, T, H, dk, dv);
+}
+
+kda_status kda_prefill_backward_chunked(const void* q, const void* k, const void* v,
+                                        const float* alpha, const float* beta, const float* S0,
+                                        const void* dO, const float* dS_T, float* dq, float* dk,
+                                        float* dv, float* dalpha, float* dbeta, float* dS0,
+                                        int B, int T, int H, int dk_, int dv_, kda_dtype dt,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_backward_impl(q, k, v, alpha, beta, S0, dO, dS_T, dq, dk, dv, dalpha, dbeta, dS0,
+                               B, T, H, dk_, dv_, dt, workspace, workspace_bytes, stream,
+                               kda::kGateAlpha, true);
 }
 
 kda_status kda_gdn_prefill_backward(const void* q, const void* k, const void* v, const float* a,

@@ -51,6 +51,11 @@ struct PrefillArgs {
   // Split path: bytes of records per segment (0: the default budget).  The
   // same value must size the workspace (prefill_workspace).
   size_t segment_budget = 0;
+  // Split path: when set, the state every chunk of C tokens starts from,
+  // fp32 [B*H][ceil(T/C)][dk][dv] (the forward half of the chunked backward).
+  float* chunk_states = nullptr;
+  // Take the split path whatever the chain count (chunk_states needs it).
+  bool force_split = false;
 };
 
 // The adjoint of one decode step (decode_backward.hip).
@@ -101,6 +106,10 @@ struct PrefillBwdArgs {
   int gate_in = kGateAlpha;   // kGateScalar: alpha, g_alpha [B,T,H] (or both null)
 };
 hipError_t launch_prefill_backward(const PrefillBwdArgs& a);
+// The chunked backward (chunk_backward.hip): bf16, dk = dv = 128, one alpha
+// per channel; 0 / hipErrorInvalidValue for anything else.
+size_t prefill_backward_chunked_workspace(int B, int T, int H, int dk, int dv);
+hipError_t launch_prefill_backward_chunked(const PrefillBwdArgs& a);
 
 // The input prologue alone over `rows` rows of dk channels: forward (raw q,
 // k, g, b -> q_hat, k_hat in the I/O type, alpha, beta fp32) or its adjoint
@@ -140,6 +149,6 @@ constexpr size_t kNoallocScratchBytes = size_t{64} << 20;
 // Device workspace bytes the prefill needs for these sizes (0: none), with
 // segments of at most `budget` bytes of records (0: the default budget).
 size_t prefill_workspace(int B, int T, int H, int dk, int dv, int C, bool bf16,
-                         size_t budget = 0);
+                         size_t budget = 0, bool force_split = false);
 
 }  // namespace kda

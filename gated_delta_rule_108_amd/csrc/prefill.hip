@@ -14,13 +14,14 @@ bool prefill_supported(int dk, int dv, int C, bool bf16) {
   return false;
 }
 
-size_t prefill_workspace(int B, int T, int H, int dk, int dv, int C, bool bf16, size_t budget) {
+size_t prefill_workspace(int B, int T, int H, int dk, int dv, int C, bool bf16, size_t budget,
+                         bool force_split) {
   if (budget == 0) budget = kSegmentBudget;
   switch (dk) {
-    case 16: return bf16 ? prefill_workspace_bf16_16(B, T, H, dv, C, budget) : prefill_workspace_f32_16(B, T, H, dv, C, budget);
-    case 32: return bf16 ? prefill_workspace_bf16_32(B, T, H, dv, C, budget) : prefill_workspace_f32_32(B, T, H, dv, C, budget);
-    case 64: return bf16 ? prefill_workspace_bf16_64(B, T, H, dv, C, budget) : prefill_workspace_f32_64(B, T, H, dv, C, budget);
-    case 128: return bf16 ? prefill_workspace_bf16_128(B, T, H, dv, C, budget) : prefill_workspace_f32_128(B, T, H, dv, C, budget);
+    case 16: return bf16 ? prefill_workspace_bf16_16(B, T, H, dv, C, budget, force_split) : prefill_workspace_f32_16(B, T, H, dv, C, budget, force_split);
+    case 32: return bf16 ? prefill_workspace_bf16_32(B, T, H, dv, C, budget, force_split) : prefill_workspace_f32_32(B, T, H, dv, C, budget, force_split);
+    case 64: return bf16 ? prefill_workspace_bf16_64(B, T, H, dv, C, budget, force_split) : prefill_workspace_f32_64(B, T, H, dv, C, budget, force_split);
+    case 128: return bf16 ? prefill_workspace_bf16_128(B, T, H, dv, C, budget, force_split) : prefill_workspace_f32_128(B, T, H, dv, C, budget, force_split);
   }
   return 0;
 }

@@ -112,7 +112,8 @@ struct OutOps {
 template <typename OpT, int DK, int C>
 __global__ void __launch_bounds__(3 * kWave * (C / 16))
 kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float* gST,
-                const char* __restrict__ gws, int B, int T, int H, int DV, int seg0, int segn) {
+                const char* __restrict__ gws, int B, int T, int H, int DV, int seg0, int segn,
+                float* __restrict__ gSc) {
   using Cf = SCfg<OpT, DK, C>;
   using RC = typename Cf::RC;
   using E = typename Ty<OpT>::Elem;
@@ -171,6 +172,19 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
     for (int ch = 0; ch < NC; ++ch) {
       const Lane ln = lane_now();
       const char* ob = buf(ch);
+      if (gSc != nullptr) {
+        // the state each chunk starts from, fp32 [chain][chunk][DK][DV]
+        const int nct = (T + C - 1) / C;
+        float* dst = gSc + (static_cast<size_t>(chain) * nct + seg0 + ch) * DK * DV + 16 * jt;
+#pragma unroll
+        for (int m = 0; m < CPW; ++m) {
+          const int cb = R + NB * m;
+          if (cb < NCB) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(16 * cb + 4 * ln.g + r) * DV + ln.i] = S[m][r];
+          }
+        }
+      }
       // publish this wave's state rows as S^T (operand type)
 #pragma unroll
       for (int m = 0; m < CPW; ++m) {
@@ -473,7 +487,8 @@ hipError_t launch_split(const PrefillArgs& a) {
       dim3 grid(static_cast<unsigned>(chains * (a.dv / 16)));
       hipLaunchKernelGGL((kda_scan_kernel<OpT, DK, C>), grid, dim3(SCfg<OpT, DK, C>::NTH), 0,
                          static_cast<hipStream_t>(a.stream), s_in, static_cast<E*>(a.o), s_out,
-                         static_cast<const char*>(a.workspace), a.B, a.T, a.H, a.dv, seg0, segn);
+                         static_cast<const char*>(a.workspace), a.B, a.T, a.H, a.dv, seg0, segn,
+                         a.chunk_states);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -501,7 +516,8 @@ bool use_split(long chains, int dv) {
 template <typename OpT, int DK, int C>
 hipError_t launch_any(const PrefillArgs& a) {
   const long chains = static_cast<long>(a.B) * a.H;
-  const bool split = use_split<OpT, DK, C>(chains, a.dv);
+  if (a.force_split && !split_fits<OpT, DK, C>(a.dv)) return hipErrorInvalidValue;
+  const bool split = a.force_split || use_split<OpT, DK, C>(chains, a.dv);
   switch (a.gate_in) {
     case kGateAlpha:
       return split ? launch_split<OpT, DK, C, kGateAlpha>(a) : launch_c<OpT, DK, C, kGateAlpha>(a);
@@ -540,17 +556,18 @@ bool supported_dk(int dv, int C) {
 }
 
 template <typename OpT, int DK, int C>
-size_t workspace_c(int B, int T, int H, int dv, size_t budget) {
-  if (!use_split<OpT, DK, C>(static_cast<long>(B) * H, dv)) return 0;
+size_t workspace_c(int B, int T, int H, int dv, size_t budget, bool force_split) {
+  if (force_split ? !split_fits<OpT, DK, C>(dv) : !use_split<OpT, DK, C>(static_cast<long>(B) * H, dv))
+    return 0;
   return split_workspace_bytes<OpT, DK, C>(B, T, H, dv, budget);
 }
 
 template <typename OpT, int DK>
-size_t workspace_dk(int B, int T, int H, int dv, int C, size_t budget) {
+size_t workspace_dk(int B, int T, int H, int dv, int C, size_t budget, bool force_split) {
   switch (C) {
-    case 16: return workspace_c<OpT, DK, 16>(B, T, H, dv, budget);
-    case 32: return workspace_c<OpT, DK, 32>(B, T, H, dv, budget);
-    case 64: return workspace_c<OpT, DK, 64>(B, T, H, dv, budget);
+    case 16: return workspace_c<OpT, DK, 16>(B, T, H, dv, budget, force_split);
+    case 32: return workspace_c<OpT, DK, 32>(B, T, H, dv, budget, force_split);
+    case 64: return workspace_c<OpT, DK, 64>(B, T, H, dv, budget, force_split);
   }
   return 0;
 }
@@ -562,14 +579,15 @@ size_t workspace_dk(int B, int T, int H, int dv, int C, size_t budget) {
   }                                                                                    \
   bool prefill_supported_##NAME##_##DK(int dv, int C) { return supported_dk<OPT, DK>(dv, C); } \
   size_t prefill_workspace_##NAME##_##DK(int B, int T, int H, int dv, int C,           \
-                                         size_t budget) {                             \
-    return workspace_dk<OPT, DK>(B, T, H, dv, C, budget);                              \
+                                         size_t budget, bool force_split) {           \
+    return workspace_dk<OPT, DK>(B, T, H, dv, C, budget, force_split);                 \
   }
 
 #define KDA_PREFILL_DECLARE(NAME, DK)                                                  \
   hipError_t launch_prefill_##NAME##_##DK(const PrefillArgs& a);                       \
   bool prefill_supported_##NAME##_##DK(int dv, int C);                                 \
-  size_t prefill_workspace_##NAME##_##DK(int B, int T, int H, int dv, int C, size_t budget);
+  size_t prefill_workspace_##NAME##_##DK(int B, int T, int H, int dv, int C, size_t budget, \
+                                         bool force_split);
 
 KDA_PREFILL_DECLARE(bf16, 16)
 KDA_PREFILL_DECLARE(bf16, 32)

@@ -377,6 +377,45 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v,
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * kda_prefill_backward_chunked_workspace_bytes — device workspace, in bytes,
+ * that kda_prefill_backward_chunked needs: the forward's split-path records
+ * (kda_prefill_workspace_bytes at C = 64 with the split path), a scratch copy
+ * of the forward output, the state and the state gradient at every 64-token
+ * chunk boundary (2 * B * H * ceil(T / 64) * dk * dv * 4 bytes) and one
+ * 15 KiB record per 16 tokens of every sequence and head.  (size_t)-1 for
+ * sizes the call does not accept (dk or dv other than 128).
+ */
+size_t kda_prefill_backward_chunked_workspace_bytes(int B, int T, int H, int dk, int dv);
+
+/*
+ * kda_prefill_backward_chunked — the gradients of kda_prefill_backward in
+ * chunk form on the matrix cores, for bf16 I/O at dk = dv = 128: the chunk
+ * algebra of "From GPT-2 to Kimi K3, Explained", section "DeltaNet
+ * (Parallelizing Linear Transformers with Delta Rule)", with the per-channel
+ * decay of section "KDA/Kimi Linear", differentiated.  The state gradient
+ * runs backwards over 16-token sub-chunks through their WY factors; every
+ * other gradient is local to a sub-chunk given its start state (from a
+ * forward pass that stores the state every 64 tokens) and its end state
+ * gradient, with the pairwise decays taken exactly as running products of
+ * alpha (closed gates, alpha = 0, included).  Operands are bf16 with fp32
+ * accumulation, so the results carry bf16-level rounding (relative error
+ * around 3e-3, against the fp32 rounding of kda_prefill_backward); every
+ * element is written once, with no atomics, so repeated calls agree bit
+ * for bit.
+ *
+ * Arguments, layouts, T = 0, dS0 == dS_T and the errors are those of
+ * kda_prefill_backward, with the workspace of
+ * kda_prefill_backward_chunked_workspace_bytes; dt must be KDA_BF16 and
+ * dk = dv = 128 (else KDA_ERR_UNSUPPORTED).
+ */
+kda_status kda_prefill_backward_chunked(const void* q, const void* k, const void* v,
+                                        const float* alpha, const float* beta, const float* S0,
+                                        const void* dO, const float* dS_T, float* dq, float* dk,
+                                        float* dv, float* dalpha, float* dbeta, float* dS0,
+                                        int B, int T, int H, int dk_, int dv_, kda_dtype dt,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * kda_gdn_decode_step_backward — kda_decode_step_backward for Gated
  * DeltaNet and DeltaNet (the step of kda_gdn_decode_step): the gate a [N, H]
  * float32 is one value per head, or NULL (gate 1).  Its gradient da [N, H]

@@ -67,13 +67,15 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_sixteen_calls():
+def test_header_declares_the_eighteen_calls():
     assert declared_functions() == ["kda_decode_step", "kda_decode_step_backward",
                                     "kda_decode_step_logits",
                                     "kda_gdn_decode_step", "kda_gdn_decode_step_backward",
                                     "kda_gdn_prefill_backward",
                                     "kda_gdn_prefill_chunked",
-                                    "kda_prefill_backward", "kda_prefill_backward_workspace_bytes",
+                                    "kda_prefill_backward", "kda_prefill_backward_chunked",
+                                    "kda_prefill_backward_chunked_workspace_bytes",
+                                    "kda_prefill_backward_workspace_bytes",
                                     "kda_prefill_chunked", "kda_prefill_chunked_logits",
                                     "kda_prefill_chunked_noalloc",
                                     "kda_prefill_workspace_bytes", "kda_prologue_backward",
