@@ -50,17 +50,22 @@ constexpr int kCB = 64;            // tokens between stored states (forward chun
 constexpr int kNSB = kCB / kSB;    // sub-chunks per chunk
 constexpr int kCbThreads = 512;
 
-// One sub-chunk record (bytes).  "Fragment" = one 16x16 bf16 operand of the
-// 16x16x16 matrix-core product in lane order: 64 lanes x 4 values, lane
-// (g, i) holding row i, columns 4g .. 4g+3 of the operand (A layout).
+// One sub-chunk record (bytes).  A "fragment" is one bf16 A operand of a
+// matrix-core product in lane order.  16x16x16 (512 B): lane (g, i) holds
+// row i, columns 4g .. 4g+3.  16x16x32 (1 KiB): lane (g, i) holds row i at
+// eight contraction slots, numbered so that the B operand is a lane's own
+// registers -- its four rows 4g .. 4g+3 of two 16-row blocks:
+//   [(Q.E)^T | -W^T] for row block R of DK: slots (Q.E)[4g+x][16R+i],
+//        then -W[4g+x][16R+i]   (contracts with [dO ; u] over the 16 rows)
+//   K.E' for channels 32kk .. 32kk+31: slots (K.E')[i][32kk+4g+x], then
+//        (K.E')[i][32kk+16+4g+x]  (contracts with state rows 2kk, 2kk+1)
 template <int DK>
 struct BRec {
-  static constexpr int NM = DK / 16;
-  static constexpr int kFrag = 64 * 4 * 2;
-  static constexpr int oW = 0;                   // W^T, row blocks of DK: [NM] fragments
-  static constexpr int oQ = oW + NM * kFrag;     // (Q.E)^T, [NM] fragments
-  static constexpr int oK = oQ + NM * kFrag;     // K.E', column blocks of DK: [NM] fragments
-  static constexpr int oP = oK + NM * kFrag;     // P^T, one fragment
+  static constexpr int NM = DK / 16, NK = DK / 32;
+  static constexpr int kFrag = 64 * 4 * 2, kFrag32 = 64 * 8 * 2;
+  static constexpr int oQW = 0;                    // [(Q.E)^T | -W^T]: [NM] 16x16x32 fragments
+  static constexpr int oK = oQW + NM * kFrag32;    // K.E': [NK] 16x16x32 fragments
+  static constexpr int oP = oK + NK * kFrag32;     // P^T, one 16x16x16 fragment
   static constexpr int oG = oP + kFrag;          // decay of the sub-chunk, fp32 [DK]
   static constexpr int oY = oG + 4 * DK;         // Y, fp32 [16][16]
   static constexpr int oA = oY + 1024;           // A (before beta), fp32 [16][16]
@@ -71,8 +76,18 @@ struct BRec {
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
+// A 16x16x32 contraction as two 16x16x16 products: lane (g, i) splits its
+// eight contraction slots into the four of each half, which is the
+// 16x16x16 operand layout.  (Single 16x16x32 bf16 products here were seen to
+// read an accumulator that the compiler let following vector instructions
+// overwrite a few cycles later: corrupted sums that varied from run to run.)
 __device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  const uint4 ua = __builtin_bit_cast(uint4, a), ub = __builtin_bit_cast(uint4, b);
+  const bf16x4 alo = __builtin_bit_cast(bf16x4, make_uint2(ua.x, ua.y));
+  const bf16x4 ahi = __builtin_bit_cast(bf16x4, make_uint2(ua.z, ua.w));
+  const bf16x4 blo = __builtin_bit_cast(bf16x4, make_uint2(ub.x, ub.y));
+  const bf16x4 bhi = __builtin_bit_cast(bf16x4, make_uint2(ub.z, ub.w));
+  return mma16(ahi, bhi, mma16(alo, blo, c));
 }
 __device__ __forceinline__ bf16x4 quad4(const f32x4& v) { return bf16_quad(v[0], v[1], v[2], v[3]); }
 __device__ __forceinline__ bf16x4 ld4(const uint16_t* p) {
@@ -80,6 +95,10 @@ __device__ __forceinline__ bf16x4 ld4(const uint16_t* p) {
 }
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+  const uint2 x = __builtin_bit_cast(uint2, a), y = __builtin_bit_cast(uint2, b);
+  return __builtin_bit_cast(bf16x8, make_uint4(x.x, x.y, y.x, y.y));
 }
 __device__ __forceinline__ bf16x4 bits4(uint16_t a, uint16_t b, uint16_t c, uint16_t d) {
   return __builtin_bit_cast(bf16x4, make_uint2(a | (static_cast<uint32_t>(b) << 16),
@@ -179,10 +198,11 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
     if (live(J)) {
       char* rec = rec_of(J);
       reinterpret_cast<float*>(rec + RB::oG)[c] = bt;
-      // (Q.E)^T fragment c / 16, lane (g, c % 16): rows 4g .. 4g+3 of Q.F, channel c
+      // (Q.E)^T half of fragment c / 16, lane (g, c % 16): rows 4g .. 4g+3 of
+      // Q.F, channel c
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<uint2*>(rec + RB::oQ + ((c / 16) * 64 + g * 16 + c % 16) * 8) =
+        *reinterpret_cast<uint2*>(rec + RB::oQW + ((c / 16) * 64 + g * 16 + c % 16) * 16) =
             make_uint2(pack_bf16x2(qq[4 * g] * F[4 * g], qq[4 * g + 1] * F[4 * g + 1]),
                        pack_bf16x2(qq[4 * g + 2] * F[4 * g + 2], qq[4 * g + 3] * F[4 * g + 3]));
     }
@@ -271,54 +291,123 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   lds_barrier();
 
   // ---- W = Y (beta K.F): tile (J, channel block R) has lane (g, i) holding
-  // W[4g .. 4g+3][16R + i] = row i of the W^T fragment R
+  // W[4g .. 4g+3][16R + i], the -W^T half of fragment R
   for (int t = wave; t < kNSB * NM; t += kCbThreads / kWave) {
     const int J = t / NM, R = t % NM;
     if (!live(J)) continue;
     const Lane ln = lane_now();
     const f32x4 acc = mma16(ld4(sY[J] + ln.i * LDT + 4 * ln.g),
                             ld4(sBK[J] + (16 * R + ln.i) * LDT + 4 * ln.g), zero4());
-    *reinterpret_cast<bf16x4*>(rec_of(J) + RB::oW + (R * 64 + lane) * 8) = quad4(acc);
+    *reinterpret_cast<bf16x4*>(rec_of(J) + RB::oQW + (R * 64 + lane) * 16 + 8) =
+        bf16_quad(-acc[0], -acc[1], -acc[2], -acc[3]);
   }
-  // ---- K.E' fragments (A layout over the channel blocks m): lane (g, i)
-  // holds row i, channels 16m + 4g .. +3
-  for (int x = tid; x < kNSB * NM * 64; x += kCbThreads) {
-    const int J = x / (NM * 64), m = (x / 64) % NM, l = x % 64;
+  // ---- K.E' fragments: lane (g, i) holds row i, channels 32kk + 4g .. +3
+  // and 32kk + 16 + 4g .. +3
+  constexpr int NK = DK / 32;
+  for (int x = tid; x < kNSB * NK * 64; x += kCbThreads) {
+    const int J = x / (NK * 64), kk = (x / 64) % NK, l = x % 64;
     if (!live(J)) continue;
-    *reinterpret_cast<uint2*>(rec_of(J) + RB::oK + (m * 64 + l) * 8) =
-        *reinterpret_cast<const uint2*>(sKH[J] + (l % 16) * LDK + 16 * m + 4 * (l / 16));
+    const uint16_t* row = sKH[J] + (l % 16) * LDK + 32 * kk + 4 * (l / 16);
+    const uint2 lo = *reinterpret_cast<const uint2*>(row), hi = *reinterpret_cast<const uint2*>(row + 16);
+    *reinterpret_cast<uint4*>(rec_of(J) + RB::oK + (kk * 64 + l) * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
 }
 
 // ---------------------------------------------------------------------------
-// 3. The state gradient, backwards over the sub-chunks.  One wave per (chain,
-// 16-column tile); the tile lives in registers, lane (g, i) holding rows
-// 16m + 4g + r, column i of it (the product's output layout, which is also
-// the layout of the next product's B operand).
-//   dS <- Diag(E_last) dS + (Q.E)^T dO - W^T (P^T dO + (K.E') dS)
+// 3. The state gradient, backwards over the sub-chunks.  One workgroup per
+// (chain, 16-column tile): a state wave holds the tile in registers, lane
+// (g, i) holding rows 16m + 4g + r, column i of it (the product's output
+// layout, which is also the layout of the next product's B operand),
+//   dS <- Diag(E_last) dS + (Q.E)^T dO - W^T (P^T dO + (K.E') dS),
+// and two loader waves stream each sub-chunk's record and dO tile into a ring
+// of LDS slots with direct global-to-LDS loads, kAhead sub-chunks ahead (the
+// walk is a chain of short matrix products: without the ring every step
+// waited for its own loads; each loader issues half of every slot so that
+// kAhead slots fit the 6-bit count of loads a wave can wait on).  One
+// barrier per sub-chunk.
 // ---------------------------------------------------------------------------
 template <int DK>
-struct ScanOps {
-  bf16x4 w[DK / 16], q[DK / 16], k[DK / 16], p;
-  float4 g[DK / 16];
-  bf16x4 d;   // dO, B layout
+struct ScanRing {
+  using RB = BRec<DK>;
+  static constexpr int kRec = RB::oG + 4 * DK;   // bytes of a record the walk reads
+  static constexpr int kDO = 16 * 16 * 2;        // dO tile, 16 rows x 16 columns bf16
+  static constexpr int kBuf = kRec + kDO;
+  static constexpr int kAhead = 7, kNBuf = kAhead + 1;
+  static constexpr int kInsts = kRec / 1024;                       // 16-byte-lane loads of a record
+  static constexpr int kSplit = (kInsts + 1) / 2;                  // loader 1: [0, kSplit), loader 2: the rest
+  static constexpr int kFill1 = kSplit, kFill2 = kInsts - kSplit + kDO / 256;   // loads per slot
+  // every load of kAhead slots fits the wave's 6-bit count of loads in flight,
+  // so waiting down to (kAhead - 1) slots means the oldest slot has landed
+  static_assert(kRec % 1024 == 0 && kAhead * kFill1 <= 63 && kAhead * kFill2 <= 63, "fill plan");
 };
 
 template <int DK>
-__global__ void __launch_bounds__(kWave)
+__global__ void __launch_bounds__(3 * kWave)
 kda_cb_scan_kernel(const char* __restrict__ grec, const uint16_t* __restrict__ gdO,
                    const float* __restrict__ gdST, float* __restrict__ gdSc, float* gdS0, int T,
                    int H, int DV) {
   using RB = BRec<DK>;
+  using RG = ScanRing<DK>;
   constexpr int NM = DK / 16;
+  __shared__ __attribute__((aligned(16))) char ring[RG::kNBuf * RG::kBuf];
   const int NJV = DV / 16;
   const int chain = blockIdx.x / NJV, jt = blockIdx.x % NJV;
   const int b = chain / H, h = chain % H;
   const int NS = (T + kSB - 1) / kSB, NC = (T + kCB - 1) / kCB;
-  const Lane ln = lane_now();
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x % kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const size_t row0 = static_cast<size_t>(b) * T * H + h;
+  auto slot = [&](int n) { return ring + (n % RG::kNBuf) * RG::kBuf; };
 
+  if (wv > 0) {
+    // ---- loaders: order n (= sub-chunk NS - 1 - n) into slot n % kNBuf;
+    // loader 1 the first kSplit KiB of the record, loader 2 the rest of it
+    // and the dO tile
+    const bool first = wv == 1;
+    auto fill = [&](int n) {
+      const int s = NS - 1 - n;
+      char* dst = slot(n);
+      const char* src = grec + (static_cast<size_t>(chain) * NS + s) * RB::kBytes;
+      if (first) {
+#pragma unroll
+        for (int i = 0; i < RG::kSplit; ++i)
+          __builtin_amdgcn_global_load_lds((gbl_void*)(src + 1024 * i + 16 * lane),
+                                           (lds_void*)(dst + 1024 * i), 16, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = RG::kSplit; i < RG::kInsts; ++i)
+          __builtin_amdgcn_global_load_lds((gbl_void*)(src + 1024 * i + 16 * lane),
+                                           (lds_void*)(dst + 1024 * i), 16, 0, 0);
+#pragma unroll
+        for (int p = 0; p < RG::kDO / 256; ++p) {
+          const int d = 64 * p + lane;           // dword of the tile: row d / 8, dword d % 8
+          const int t = min(kSB * s + d / 8, T - 1);
+          __builtin_amdgcn_global_load_lds(
+              (gbl_void*)(gdO + (row0 + static_cast<size_t>(t) * H) * DV + 16 * jt + 2 * (d % 8)),
+              (lds_void*)(dst + RG::kRec + 256 * p), 4, 0, 0);
+        }
+      }
+    };
+    // at most (kAhead - 1) slots of this wave's loads in flight: the oldest landed
+    auto wait_oldest = [&] {
+      if (first) __builtin_amdgcn_s_waitcnt(vmcnt_only((RG::kAhead - 1) * RG::kFill1));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_only((RG::kAhead - 1) * RG::kFill2));
+    };
+    if (NS > 0) {
+#pragma unroll
+      for (int i = 0; i < RG::kAhead; ++i) fill(min(i, NS - 1));
+      wait_oldest();   // order 0 landed
+    }
+    for (int n = 0; n < NS; ++n) {
+      barrier_keep_fills();   // slot n is ready; slot n + kAhead (used by n - 1) is free
+      fill(min(n + RG::kAhead, NS - 1));
+      wait_oldest();          // order n + 1 landed
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    return;
+  }
+
+  const Lane ln = lane_now();
   f32x4 dS[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m)
@@ -327,30 +416,10 @@ kda_cb_scan_kernel(const char* __restrict__ grec, const uint16_t* __restrict__ g
       dS[m][r] = gdST ? gdST[(static_cast<size_t>(chain) * DK + 16 * m + 4 * ln.g + r) * DV +
                              16 * jt + ln.i]
                       : 0.f;
-
-  auto load = [&](ScanOps<DK>& o, int s) {
-    const char* rec = grec + (static_cast<size_t>(chain) * NS + s) * RB::kBytes;
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      o.w[m] = *reinterpret_cast<const bf16x4*>(rec + RB::oW + (m * 64 + lane) * 8);
-      o.q[m] = *reinterpret_cast<const bf16x4*>(rec + RB::oQ + (m * 64 + lane) * 8);
-      o.k[m] = *reinterpret_cast<const bf16x4*>(rec + RB::oK + (m * 64 + lane) * 8);
-      o.g[m] = *reinterpret_cast<const float4*>(rec + RB::oG + 4 * (16 * m + 4 * ln.g));
-    }
-    o.p = *reinterpret_cast<const bf16x4*>(rec + RB::oP + lane * 8);
-    uint16_t d[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = kSB * s + 4 * ln.g + r;
-      d[r] = t < T ? gdO[(row0 + static_cast<size_t>(t) * H) * DV + 16 * jt + ln.i] : 0;
-    }
-    o.d = bits4(d[0], d[1], d[2], d[3]);
-  };
-
-  ScanOps<DK> cur, nxt;
-  if (NS > 0) load(cur, NS - 1);
-  for (int s = NS - 1; s >= 0; --s) {
-    load(nxt, s > 0 ? s - 1 : 0);
+  for (int n = 0; n < NS; ++n) {
+    const int s = NS - 1 - n;
+    lds_barrier();
+    const char* sb = slot(n);
     if (s == NS - 1 || (s % kNSB) == kNSB - 1) {
       // the gradient at the end of chunk s / 4, for the gradient kernel
       float* dst = gdSc + (static_cast<size_t>(chain) * NC + s / kNSB) * DK * DV + 16 * jt + ln.i;
@@ -359,27 +428,33 @@ kda_cb_scan_kernel(const char* __restrict__ grec, const uint16_t* __restrict__ g
 #pragma unroll
         for (int r = 0; r < 4; ++r) dst[(16 * m + 4 * ln.g + r) * DV] = dS[m][r];
     }
-    f32x4 t1a = mma16(cur.p, cur.d, zero4()), t1b = zero4();
+    const uint16_t* dt = reinterpret_cast<const uint16_t*>(sb + RG::kRec);
+    const bf16x4 dob = bits4(dt[(4 * ln.g) * 16 + ln.i], dt[(4 * ln.g + 1) * 16 + ln.i],
+                             dt[(4 * ln.g + 2) * 16 + ln.i], dt[(4 * ln.g + 3) * 16 + ln.i]);
+    auto frag32 = [&](int off, int m) {
+      return *reinterpret_cast<const bf16x8*>(sb + off + (m * 64 + lane) * 16);
+    };
+    // u = P^T dO + (K.E') dS, then dS <- Diag(E_last) dS + [(Q.E)^T | -W^T] [dO ; u]
+    const f32x4 pd = mma16(*reinterpret_cast<const bf16x4*>(sb + RB::oP + lane * 8), dob, zero4());
+    f32x4 t1a = zero4(), t1b = zero4();
 #pragma unroll
-    for (int m = 0; m < NM; m += 2) {
-      t1a = mma16(cur.k[m], quad4(dS[m]), t1a);
-      t1b = mma16(cur.k[m + 1], quad4(dS[m + 1]), t1b);
+    for (int kk = 0; kk < NM / 2; kk += 2) {
+      t1a = mma32(frag32(RB::oK, kk), cat8(quad4(dS[2 * kk]), quad4(dS[2 * kk + 1])), t1a);
+      t1b = mma32(frag32(RB::oK, kk + 1), cat8(quad4(dS[2 * kk + 2]), quad4(dS[2 * kk + 3])), t1b);
     }
     f32x4 u;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) u[r] = t1a[r] + t1b[r];
-    const bf16x4 ub = quad4(u);
+    for (int r = 0; r < 4; ++r) u[r] = t1a[r] + t1b[r] + pd[r];
+    const bf16x8 du8 = cat8(dob, quad4(u));
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      const f32x4 aq = mma16(cur.q[m], cur.d, zero4());
-      const f32x4 aw = mma16(cur.w[m], ub, zero4());
-      const float4 gc = cur.g[m];
-      dS[m][0] = gc.x * dS[m][0] + aq[0] - aw[0];
-      dS[m][1] = gc.y * dS[m][1] + aq[1] - aw[1];
-      dS[m][2] = gc.z * dS[m][2] + aq[2] - aw[2];
-      dS[m][3] = gc.w * dS[m][3] + aq[3] - aw[3];
+      const f32x4 aq = mma32(frag32(RB::oQW, m), du8, zero4());
+      const float4 gc = *reinterpret_cast<const float4*>(sb + RB::oG + 4 * (16 * m + 4 * ln.g));
+      dS[m][0] = gc.x * dS[m][0] + aq[0];
+      dS[m][1] = gc.y * dS[m][1] + aq[1];
+      dS[m][2] = gc.z * dS[m][2] + aq[2];
+      dS[m][3] = gc.w * dS[m][3] + aq[3];
     }
-    cur = nxt;
   }
   if (gdS0) {
 #pragma unroll
@@ -414,7 +489,6 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   __shared__ __attribute__((aligned(16))) uint16_t sW[kSB * LDK];   // W
   __shared__ __attribute__((aligned(16))) uint16_t sKE[kSB * LDK];  // K.E
   __shared__ __attribute__((aligned(16))) uint16_t sKpT[DK * LDT];  // (K.E')^T
-  __shared__ __attribute__((aligned(16))) uint16_t sKET[DK * LDT];  // (K.E)^T
   __shared__ __attribute__((aligned(16))) uint16_t sY[kSB * LDT];
   __shared__ __attribute__((aligned(16))) uint16_t sYT[kSB * LDT];
   __shared__ __attribute__((aligned(16))) uint16_t sdO[kSB * LDV];
@@ -426,8 +500,11 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   __shared__ float sOS[kSB * LDF];                                   // dO S^T
   __shared__ float sZS[kSB * LDF];                                   // dZ S^T
   __shared__ float sUS[kSB * LDF];                                   // U dS^T
-  __shared__ float sdP[kSB * 17];
-  __shared__ float sdA[kSB * 17];
+  constexpr int LDP = kSB + 4;                                      // 16-byte rows
+  __shared__ __attribute__((aligned(16))) float sdP[kSB * LDP];     // dP, dA and transposes
+  __shared__ __attribute__((aligned(16))) float sdA[kSB * LDP];
+  __shared__ __attribute__((aligned(16))) float sdPT[kSB * LDP];
+  __shared__ __attribute__((aligned(16))) float sdAT[kSB * LDP];
   __shared__ float sPC[DK];
   __shared__ float sFin[kCbThreads / kWave][DK];
   __shared__ float sDb1[kCbThreads / kWave][kSB];
@@ -469,35 +546,63 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   auto sb_slot = [&](int J, int m) {
     return sbw + (static_cast<size_t>(J - 1) * (kCbThreads / kWave) * NM + m) * kWave;
   };
-  bf16x4 Ub[kNSB];       // U of each sub-chunk (this wave's columns)
+  // U of each sub-chunk (this wave's columns), after them: [chain][chunk][J][wave][lane]
+  bf16x4* ubw = gSb + static_cast<size_t>(gridDim.x) * (kNSB - 1) * (kCbThreads / kWave) * NM * kWave +
+                ((static_cast<size_t>(chain) * NC + cc) * kNSB * (kCbThreads / kWave) + wave) * kWave + lane;
+  auto ub_slot = [&](int J) { return ubw + static_cast<size_t>(J) * (kCbThreads / kWave) * kWave; };
 
-  // ======== forward over the sub-chunks: S_J and U_J
-#pragma unroll
-  for (int J = 0; J < kNSB; ++J) {
-    if (J >= ns) break;
+  // ======== forward over the sub-chunks: S_J and U_J.  Each sub-chunk's
+  // record pieces and value rows are loaded one sub-chunk ahead.
+  static_assert(NM * 64 == kCbThreads && (DK / 32) * 64 <= kCbThreads, "one fragment lane per thread");
+  struct FwdIn {
+    uint2 wv;          // the -W^T half of one fragment lane
+    uint4 kv;          // one K.E' fragment lane (threads below DK / 32 * 64)
+    float y, pc;       // Y[tid], decay[tid]
+    uint16_t v[4];     // V of this wave's column tile, rows 4g .. 4g+3
+  };
+  auto fetch_fwd = [&](int J, FwdIn& f) {
     const char* rec = rec_of(J);
+    const int R = tid / 64, l = tid % 64;
+    f.wv = *reinterpret_cast<const uint2*>(rec + RB::oQW + (R * 64 + l) * 16 + 8);
+    f.kv = tid < (DK / 32) * 64 ? *reinterpret_cast<const uint4*>(rec + RB::oK + (tid % ((DK / 32) * 64)) * 16)
+                                : make_uint4(0, 0, 0, 0);
+    f.y = tid < kSB * kSB ? reinterpret_cast<const float*>(rec + RB::oY)[tid % (kSB * kSB)] : 0.f;
+    f.pc = tid < DK ? reinterpret_cast<const float*>(rec + RB::oG)[tid % DK] : 0.f;
+    const Lane ln = lane_now();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + kSB * J + 4 * ln.g + r;
+      f.v[r] = t < T ? gv[trow(t) * DV + 16 * jt + ln.i] : 0;
+    }
+  };
+  FwdIn fin_cur;
+  fetch_fwd(0, fin_cur);
+#pragma nounroll
+  for (int J = 0; J < ns; ++J) {
+    const FwdIn cur = fin_cur;
+    if (J + 1 < ns) fetch_fwd(J + 1, fin_cur);
     // W (from its W^T fragments), (K.E')^T (from the K.E' fragments), Y
     {
-      const int R = tid / 64, l = tid % 64;   // NM * 64 == kCbThreads
-      const bf16x4 wv = *reinterpret_cast<const bf16x4*>(rec + RB::oW + (R * 64 + l) * 8);
-      const bf16x4 kv = *reinterpret_cast<const bf16x4*>(rec + RB::oK + (R * 64 + l) * 8);
+      const int R = tid / 64, l = tid % 64;
       const int g = l / 16, i = l % 16;
-      const uint2 wu = __builtin_bit_cast(uint2, wv), ku = __builtin_bit_cast(uint2, kv);
-      const uint16_t w4[4] = {static_cast<uint16_t>(wu.x & 0xffff), static_cast<uint16_t>(wu.x >> 16),
-                              static_cast<uint16_t>(wu.y & 0xffff), static_cast<uint16_t>(wu.y >> 16)};
-      const uint16_t k4[4] = {static_cast<uint16_t>(ku.x & 0xffff), static_cast<uint16_t>(ku.x >> 16),
-                              static_cast<uint16_t>(ku.y & 0xffff), static_cast<uint16_t>(ku.y >> 16)};
+      // -W, negated back (sign bit): W[4g+x][16R+i]
+      const uint32_t wh[2] = {cur.wv.x ^ 0x80008000u, cur.wv.y ^ 0x80008000u};
+      // K.E' lane (g, i) of fragment kk = R: row i, channels 32R+4g+x and 32R+16+4g+x
+      const uint32_t kh[4] = {cur.kv.x, cur.kv.y, cur.kv.z, cur.kv.w};
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        sW[(4 * g + x) * LDK + 16 * R + i] = w4[x];          // W[4g+x][16R+i]
-        sKpT[(16 * R + 4 * g + x) * LDT + i] = k4[x];        // (K.E')[i][16R+4g+x]
+        sW[(4 * g + x) * LDK + 16 * R + i] = static_cast<uint16_t>(wh[x / 2] >> (16 * (x % 2)));
+        if (R < DK / 32) {
+          sKpT[(32 * R + 4 * g + x) * LDT + i] = static_cast<uint16_t>(kh[x / 2] >> (16 * (x % 2)));
+          sKpT[(32 * R + 16 + 4 * g + x) * LDT + i] =
+              static_cast<uint16_t>(kh[2 + x / 2] >> (16 * (x % 2)));
+        }
       }
       if (tid < kSB * kSB) {
-        const float y = reinterpret_cast<const float*>(rec + RB::oY)[tid];
-        sY[(tid / kSB) * LDT + tid % kSB] = f32_to_bf16(y);
-        sYT[(tid % kSB) * LDT + tid / kSB] = f32_to_bf16(y);
+        sY[(tid / kSB) * LDT + tid % kSB] = f32_to_bf16(cur.y);
+        sYT[(tid % kSB) * LDT + tid / kSB] = f32_to_bf16(cur.y);
       }
-      if (tid < DK) sPC[tid] = reinterpret_cast<const float*>(rec + RB::oG)[tid];
+      if (tid < DK) sPC[tid] = cur.pc;
     }
     lds_barrier();
     {
@@ -505,11 +610,7 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
       // U~ = Y (beta V)
       uint16_t vb[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = kSB * J + 4 * ln.g + r, t = t0 + row;
-        const float v = t < T ? bf16_to_f32(gv[trow(t) * DV + 16 * jt + ln.i]) : 0.f;
-        vb[r] = f32_to_bf16(sBe[row] * v);
-      }
+      for (int r = 0; r < 4; ++r) vb[r] = f32_to_bf16(sBe[kSB * J + 4 * ln.g + r] * bf16_to_f32(cur.v[r]));
       f32x4 u = mma16(ld4(sY + ln.i * LDT + 4 * ln.g), bits4(vb[0], vb[1], vb[2], vb[3]), zero4());
       // U = U~ - W S
       f32x4 ws = zero4();
@@ -521,12 +622,13 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) u[r] -= ws[r];
-      Ub[J] = quad4(u);
+      const bf16x4 ub = quad4(u);
+      *ub_slot(J) = ub;
       // S <- Diag(E_last) S + (K.E')^T U
       if (J + 1 < ns) {
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-          const f32x4 x = mma16(ld4(sKpT + (16 * m + ln.i) * LDT + 4 * ln.g), Ub[J], zero4());
+          const f32x4 x = mma16(ld4(sKpT + (16 * m + ln.i) * LDT + 4 * ln.g), ub, zero4());
           const float4 gc = *reinterpret_cast<const float4*>(sPC + 16 * m + 4 * ln.g);
           Sw[m][0] = gc.x * Sw[m][0] + x[0];
           Sw[m][1] = gc.y * Sw[m][1] + x[1];
@@ -548,12 +650,47 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
       for (int r = 0; r < 4; ++r)
         dS[m][r] = gdSc[sbase + (16 * m + 4 * ln.g + r) * DV + 16 * jt + ln.i];
   }
-  const int c = tid % DK, part = tid / DK;   // gate phase: key channel, quarter of the rows
+  // gate phase: key channel, quarter of the rows (wave-uniform: DK is a
+  // multiple of the wave size)
+  const int c = tid % DK, part = __builtin_amdgcn_readfirstlane(tid / DK);
+  // raw alpha, k, q of rows 4 part .. +3 of a sub-chunk, loaded one
+  // sub-chunk ahead
+  float na[4];
+  uint16_t nk[4], nq[4];
+  auto fetch_rows = [&](int J) {
 #pragma unroll
-  for (int J = kNSB - 1; J >= 0; --J) {
-    if (J >= ns) continue;
+    for (int x = 0; x < 4; ++x) {
+      const int t = t0 + kSB * J + 4 * part + x;
+      const bool ok = t < T;
+      const size_t e = trow(ok ? t : 0) * DK + c;
+      na[x] = ok ? galpha[e] : 1.f;
+      nk[x] = ok ? gk[e] : 0;
+      nq[x] = ok ? gq[e] : 0;
+    }
+  };
+  fetch_rows(ns - 1);
+#pragma nounroll
+  for (int J = ns - 1; J >= 0; --J) {
     const char* rec = rec_of(J);
     const int tb = t0 + kSB * J;
+    float a[4];
+    uint16_t kbv[4], qbv[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      a[x] = na[x];
+      kbv[x] = nk[x];
+      qbv[x] = nq[x];
+    }
+    // record fragments of this sub-chunk, used after the next barriers
+    const bf16x4 pfr = *reinterpret_cast<const bf16x4*>(rec + RB::oP + lane * 8);
+    bf16x8 kfr[NM / 2], qwfr[NM];
+#pragma unroll
+    for (int m = 0; m < NM / 2; ++m)
+      kfr[m] = *reinterpret_cast<const bf16x8*>(rec + RB::oK + (m * 64 + lane) * 16);
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+      qwfr[m] = *reinterpret_cast<const bf16x8*>(rec + RB::oQW + (m * 64 + lane) * 16);
+    const bf16x4 uj = *ub_slot(J);
     bf16x4 Sj[NM];   // S of this sub-chunk, this wave's columns
     {
       const Lane ln = lane_now();
@@ -571,19 +708,16 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
     }
     // ---- stage: raw q, k, alpha of the sub-chunk; K.E and (K.E)^T; Y^T; decay
     {
-      float a[4], kk[4];
+      float kk[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const int r = 4 * part + x, t = tb + r;
-        const bool ok = t < T;
-        const size_t e = trow(ok ? t : 0) * DK + c;
-        a[x] = ok ? galpha[e] : 1.f;
-        const uint16_t kb = ok ? gk[e] : 0, qb = ok ? gq[e] : 0;
-        kk[x] = bf16_to_f32(kb);
-        sKr[r * LDK + c] = kb;
-        sQr[r * LDK + c] = qb;
+        const int r = 4 * part + x;
+        kk[x] = bf16_to_f32(kbv[x]);
+        sKr[r * LDK + c] = kbv[x];
+        sQr[r * LDK + c] = qbv[x];
         sAl[r * DK + c] = a[x];
       }
+      if (J > 0) fetch_rows(J - 1);
       lds_barrier();
       // F_r = prod of alpha through r within the sub-chunk
       float F = 1.f;
@@ -593,9 +727,7 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
       for (int x = 0; x < 4; ++x) {
         const int r = 4 * part + x;
         F *= a[x];
-        const uint16_t ke = f32_to_bf16(kk[x] * F);
-        sKE[r * LDK + c] = ke;
-        sKET[c * LDT + r] = ke;
+        sKE[r * LDK + c] = f32_to_bf16(kk[x] * F);
       }
       if (tid < kSB * kSB) {
         const float y = reinterpret_cast<const float*>(rec + RB::oY)[tid];
@@ -604,7 +736,6 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
       if (tid < DK) sPC[tid] = reinterpret_cast<const float*>(rec + RB::oG)[tid];
     }
     // ---- this wave's column tile: S, dS, dO, U into LDS (operand type)
-    bf16x4 dob;
     {
       const Lane ln = lane_now();
 #pragma unroll
@@ -617,27 +748,32 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
           sdS[row * LDV + 16 * jt + ln.i] = f32_to_bf16(unbf(dsb, r));
         }
       }
-      uint16_t d[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = tb + 4 * ln.g + r;
-        d[r] = t < T ? gdO[trow(t) * DV + 16 * jt + ln.i] : 0;
-        sdO[(4 * ln.g + r) * LDV + 16 * jt + ln.i] = d[r];
-        sU[(4 * ln.g + r) * LDV + 16 * jt + ln.i] = f32_to_bf16(unbf(Ub[J], r));
+        sdO[(4 * ln.g + r) * LDV + 16 * jt + ln.i] = t < T ? gdO[trow(t) * DV + 16 * jt + ln.i] : 0;
+        sU[(4 * ln.g + r) * LDV + 16 * jt + ln.i] = f32_to_bf16(unbf(uj, r));
       }
-      dob = bits4(d[0], d[1], d[2], d[3]);
     }
     lds_barrier();
+    // dO of this wave's column tile as a B operand (rows 4g .. 4g+3, column i),
+    // read back from LDS; sdO holds it until the next sub-chunk
+    auto dO_operand = [&] {
+      const Lane ln = lane_now();
+      const uint16_t* col = sdO + 16 * jt + ln.i;
+      return bits4(col[(4 * ln.g) * LDV], col[(4 * ln.g + 1) * LDV], col[(4 * ln.g + 2) * LDV],
+                   col[(4 * ln.g + 3) * LDV]);
+    };
+    const bf16x4 dob = dO_operand();
     // ---- per column tile: dU, dZ, dv, X, the dbeta and fin partial sums
-    f32x4 dZ;
+    f32x4 du;
     {
       const Lane ln = lane_now();
-      f32x4 du = mma16(*reinterpret_cast<const bf16x4*>(rec + RB::oP + lane * 8), dob, zero4());
+      du = mma16(pfr, dob, zero4());
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
-        du = mma16(*reinterpret_cast<const bf16x4*>(rec + RB::oK + (m * 64 + lane) * 8),
-                   quad4(dS[m]), du);
-      dZ = mma16(ld4(sYT + ln.i * LDT + 4 * ln.g), quad4(du), zero4());
+      for (int m = 0; m < NM / 2; ++m)
+        du = mma32(kfr[m], cat8(quad4(dS[2 * m]), quad4(dS[2 * m + 1])), du);
+      const f32x4 dZ = mma16(ld4(sYT + ln.i * LDT + 4 * ln.g), quad4(du), zero4());
       f32x4 ks = zero4();
 #pragma unroll
       for (int m = 0; m < NM; ++m) ks = mma16(ld4(sKE + ln.i * LDK + 16 * m + 4 * ln.g), Sj[m], ks);
@@ -691,10 +827,13 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
         for (int r = 0; r < 4; ++r) {
           const int row = 4 * ln.g + r;
           if (wave == 0) {
-            sdP[row * 17 + ln.i] = ln.i <= row ? pp[r] : 0.f;
+            const float dp = ln.i <= row ? pp[r] : 0.f;
+            sdP[row * LDP + ln.i] = dp;
+            sdPT[ln.i * LDP + row] = dp;
           } else {
             const float dl = ln.i < row ? -pp[r] : 0.f;
-            sdA[row * 17 + ln.i] = sBe[kSB * J + row] * dl;
+            sdA[row * LDP + ln.i] = sBe[kSB * J + row] * dl;
+            sdAT[ln.i * LDP + row] = sBe[kSB * J + row] * dl;
             const float s2 = row16_sum(dl * Af[row * kSB + ln.i]);
             if (ln.i == 0) sDb2[row] = s2;
           }
@@ -703,9 +842,9 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
     }
     lds_barrier();
     // ---- gate phase: thread (channel c, quarter `part`); exact running
-    // products of alpha over the 16 rows.  The row values of channel c sit in
-    // registers (compile-time row index); the rows / gates of the quarter are
-    // a runtime loop.
+    // products of alpha over the 16 rows of channel c (row values in
+    // registers).  Quarters 0 and 1: dalpha for t < 8 and t >= 8; quarters 2
+    // and 3: dq and dk for rows 0..7 and 8..15.
     {
       float a[kSB], kq[kSB], qq[kSB];
 #pragma unroll
@@ -714,86 +853,113 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
         kq[r] = bf16_to_f32(sKr[r * LDK + c]);
         qq[r] = bf16_to_f32(sQr[r * LDK + c]);
       }
-      float fin = 0.f;
+      if (part < 2) {
+        // dalpha_t with alpha_t's own factor left out, t ascending; the pair
+        // sums advance with t:  sp_r(t) = sum_{i<t} dP_ri k_i Gam(t-1, i),
+        //   sp_r(t+1) = alpha_t sp_r(t) + dP_rt k_t   (sa_r the same with dA)
+        float fin = 0.f;
 #pragma unroll
-      for (int w = 0; w < kCbThreads / kWave; ++w) fin += sFin[w][c];
-      for (int e = 0; e < 4; ++e) {
-        const int x = 4 * part + e;
-        // an opaque zero keeps the dP / dA loads inside this loop (hoisted
-        // out of it they would hold hundreds of registers)
-        int z = 0;
-        asm volatile("" : "+v"(z));
-        const float* dP = sdP + z;
-        const float* dA = sdA + z;
-        // G1, G2: sum over i <= x of Gam(x, i) = prod_{i<j<=x} alpha_j
-        // G3: sum over r >= x of Gam(r, x);  F_x, H_x
-        float g1 = 0.f, g2 = 0.f, g = 1.f;
-#pragma unroll
-        for (int i = kSB - 1; i >= 0; --i) {
-          if (i <= x) {
-            g = (i == x) ? 1.f : g * a[i + 1 < kSB ? i + 1 : i];
-            const float kg = kq[i] * g;
-            g1 += dP[x * 17 + i] * kg;
-            g2 += dA[x * 17 + i] * kg;     // zero on the diagonal
-          }
-        }
-        float g3 = 0.f, F = 1.f, Hx = 1.f;
-        g = 1.f;
+        for (int w = 0; w < kCbThreads / kWave; ++w) fin += sFin[w][c];
+        float rho[kSB], sp[kSB], sa[kSB];
 #pragma unroll
         for (int r = 0; r < kSB; ++r) {
-          if (r >= x) {
-            g = (r == x) ? 1.f : g * a[r];
-            g3 += (dP[r * 17 + x] * qq[r] + dA[r * 17 + x] * kq[r]) * g;
-          }
-          if (r <= x) F *= a[r];
-          else Hx *= a[r];
+          rho[r] = qq[r] * sOS[r * LDF + c] - sBe[kSB * J + r] * kq[r] * sZS[r * LDF + c];
+          sp[r] = 0.f;
+          sa[r] = 0.f;
         }
-        const int t = tb + x;
-        if (t < T) {
-          const size_t ex = trow(t) * DK + c;
-          gdq[ex] = F * sOS[x * LDF + c] + g1;
-          gdk[ex] = -sBe[kSB * J + x] * F * sZS[x * LDF + c] + g2 + g3 + Hx * sUS[x * LDF + c];
-        }
-      }
-      // gates t of this quarter: dalpha_t with alpha_t's own factor left out
-      for (int e = 0; e < 4; ++e) {
-        const int t = 4 * part + e;
-        int z = 0;
-        asm volatile("" : "+v"(z));
-        const float* dP = sdP + z;
-        const float* dA = sdA + z;
-        float Fm = 1.f, Ht = 1.f;          // F_{t-1}, H_t
-        float wk[kSB];                      // k_i Gam(t-1, i) for i < t, else 0
-        float colp = 0.f, g = 1.f;
+        float Fm = 1.f, colp = 0.f;     // F_{t-1}; sum_{i<t} sig_i Gam(t-1, i)
+        const int tlo = 8 * part, thi = tlo + 8;
 #pragma unroll
-        for (int i = kSB - 1; i >= 0; --i) {
-          g = (i >= t - 1) ? 1.f : g * a[i + 1 < kSB ? i + 1 : i];
-          const bool on = i < t;
-          wk[i] = on ? kq[i] * g : 0.f;
-          colp += on ? wk[i] * sUS[i * LDF + c] : 0.f;
-        }
-        // over r >= t, with Gam(r, t): rho_r and the pairs (r, i < t)
-        float rowp = 0.f, pair = 0.f;
-        g = 1.f;
+        for (int t = 0; t < kSB; ++t) {
+          if (t >= thi) break;
+          if (t >= tlo) {
+            float rowp = 0.f, pair = 0.f, g = 1.f;
 #pragma unroll
-        for (int r = 0; r < kSB; ++r) {
-          if (r < t) Fm *= a[r];
-          if (r > t) Ht *= a[r];
-          if (r >= t) {
-            g = (r == t) ? 1.f : g * a[r];
-            const float rho = qq[r] * sOS[r * LDF + c] - sBe[kSB * J + r] * kq[r] * sZS[r * LDF + c];
-            float sp = 0.f, sa = 0.f;
-#pragma unroll
-            for (int i = 0; i < kSB; ++i) {
-              sp += dP[r * 17 + i] * wk[i];
-              sa += dA[r * 17 + i] * wk[i];
+            for (int r = t; r < kSB; ++r) {
+              if (r > t) g *= a[r];
+              rowp += rho[r] * g;
+              pair += (qq[r] * sp[r] + kq[r] * sa[r]) * g;
             }
-            rowp += rho * g;
-            pair += (qq[r] * sp + kq[r] * sa) * g;
+            const float Ht = g;              // Gam(15, t) = H_t
+            const int tt = tb + t;
+            if (tt < T) gda[trow(tt) * DK + c] = Fm * rowp + Ht * colp + Fm * Ht * fin + pair;
+          }
+          if (t + 1 < thi) {
+            // column t of dP and dA (rows r > t matter from here on)
+#pragma unroll
+            for (int q4 = (t + 1) / 4; q4 < kSB / 4; ++q4) {
+              const float4 p4 = *reinterpret_cast<const float4*>(sdPT + t * LDP + 4 * q4);
+              const float4 a4 = *reinterpret_cast<const float4*>(sdAT + t * LDP + 4 * q4);
+              const float pv[4] = {p4.x, p4.y, p4.z, p4.w}, av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * q4 + e;
+                if (r > t) {
+                  sp[r] = a[t] * sp[r] + pv[e] * kq[t];
+                  sa[r] = a[t] * sa[r] + av[e] * kq[t];
+                }
+              }
+            }
+            colp = a[t] * colp + kq[t] * sUS[t * LDF + c];
+            Fm *= a[t];
           }
         }
-        const int tt = tb + t;
-        if (tt < T) gda[trow(tt) * DK + c] = Fm * rowp + Ht * colp + Fm * Ht * fin + pair;
+      } else {
+        float F[kSB], Hs[kSB];
+        F[0] = a[0];
+#pragma unroll
+        for (int r = 1; r < kSB; ++r) F[r] = F[r - 1] * a[r];
+        Hs[kSB - 1] = 1.f;
+#pragma unroll
+        for (int r = kSB - 2; r >= 0; --r) Hs[r] = Hs[r + 1] * a[r + 1];
+        const int xlo = 8 * (part - 2);
+#pragma unroll
+        for (int x = 0; x < kSB; ++x) {
+          if (x < xlo || x >= xlo + 8) continue;
+          // row x and column x of dP, dA
+          int z = 0;
+          asm volatile("" : "+v"(z));
+          // G1, G2 over i <= x with Gam(x, i), from row x of dP and dA
+          float g1 = 0.f, g2 = 0.f, g = 1.f;
+#pragma unroll
+          for (int q4 = x / 4; q4 >= 0; --q4) {
+            const float4 p4 = *reinterpret_cast<const float4*>(sdP + z + x * LDP + 4 * q4);
+            const float4 a4 = *reinterpret_cast<const float4*>(sdA + z + x * LDP + 4 * q4);
+            const float pv[4] = {p4.x, p4.y, p4.z, p4.w}, av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+            for (int e = 3; e >= 0; --e) {
+              const int i = 4 * q4 + e;
+              if (i <= x) {
+                if (i < x) g *= a[i + 1];
+                g1 += pv[e] * kq[i] * g;
+                g2 += av[e] * kq[i] * g;
+              }
+            }
+          }
+          // G3 over r >= x with Gam(r, x), from column x
+          float g3 = 0.f;
+          g = 1.f;
+#pragma unroll
+          for (int q4 = x / 4; q4 < kSB / 4; ++q4) {
+            const float4 p4 = *reinterpret_cast<const float4*>(sdPT + z + x * LDP + 4 * q4);
+            const float4 a4 = *reinterpret_cast<const float4*>(sdAT + z + x * LDP + 4 * q4);
+            const float pv[4] = {p4.x, p4.y, p4.z, p4.w}, av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * q4 + e;
+              if (r >= x) {
+                if (r > x) g *= a[r];
+                g3 += (pv[e] * qq[r] + av[e] * kq[r]) * g;
+              }
+            }
+          }
+          const int t = tb + x;
+          if (t < T) {
+            const size_t ex = trow(t) * DK + c;
+            gdq[ex] = F[x] * sOS[x * LDF + c] + g1;
+            gdk[ex] = -sBe[kSB * J + x] * F[x] * sZS[x * LDF + c] + g2 + g3 + Hs[x] * sUS[x * LDF + c];
+          }
+        }
       }
       if (tid < kSB) {
         const int t = tb + tid;
@@ -803,23 +969,18 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
         if (t < T) gdb[trow(t)] = db;
       }
     }
-    // ---- dS <- Diag(E_last) dS + (Q.E)^T dO - (K.E)^T Diag(beta) dZ
+    // ---- dS <- Diag(E_last) dS + (Q.E)^T dO - W^T dU   (W^T dU = (K.E)^T Diag(beta) dZ)
     {
       const Lane ln = lane_now();
-      uint16_t bz[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) bz[r] = f32_to_bf16(sBe[kSB * J + 4 * ln.g + r] * dZ[r]);
-      const bf16x4 bzb = bits4(bz[0], bz[1], bz[2], bz[3]);
+      const bf16x8 du8 = cat8(dO_operand(), quad4(du));
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        const f32x4 aq = mma16(*reinterpret_cast<const bf16x4*>(rec + RB::oQ + (m * 64 + lane) * 8),
-                               dob, zero4());
-        const f32x4 ak = mma16(ld4(sKET + (16 * m + ln.i) * LDT + 4 * ln.g), bzb, zero4());
+        const f32x4 aq = mma32(qwfr[m], du8, zero4());
         const float4 gc = *reinterpret_cast<const float4*>(sPC + 16 * m + 4 * ln.g);
-        dS[m][0] = gc.x * dS[m][0] + aq[0] - ak[0];
-        dS[m][1] = gc.y * dS[m][1] + aq[1] - ak[1];
-        dS[m][2] = gc.z * dS[m][2] + aq[2] - ak[2];
-        dS[m][3] = gc.w * dS[m][3] + aq[3] - ak[3];
+        dS[m][0] = gc.x * dS[m][0] + aq[0];
+        dS[m][1] = gc.y * dS[m][1] + aq[1];
+        dS[m][2] = gc.z * dS[m][2] + aq[2];
+        dS[m][3] = gc.w * dS[m][3] + aq[3];
       }
     }
     lds_barrier();
@@ -838,7 +999,8 @@ size_t prefill_backward_chunked_workspace(int B, int T, int H, int dk, int dv) {
   const size_t states = chains * nc * dk * dv * sizeof(float);
   const size_t recs = chains * ns * BRec<128>::kBytes;
   const size_t sub_states = chains * nc * (kNSB - 1) * dk * dv * 2;   // bf16
-  return fwd + o + 2 * states + recs + sub_states;
+  const size_t sub_u = chains * nc * kNSB * kSB * dv * 2;            // bf16
+  return fwd + o + 2 * states + recs + sub_states + sub_u;
 }
 
 hipError_t launch_prefill_backward_chunked(const PrefillBwdArgs& a) {
@@ -867,7 +1029,7 @@ hipError_t launch_prefill_backward_chunked(const PrefillBwdArgs& a) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  kda_cb_scan_kernel<128><<<static_cast<unsigned>(chains * (a.dv / 16)), kWave, 0, stream>>>(
+  kda_cb_scan_kernel<128><<<static_cast<unsigned>(chains * (a.dv / 16)), 3 * kWave, 0, stream>>>(
       recs, static_cast<const uint16_t*>(a.dO), a.dS_T, dSc, a.g_S0, a.T, a.H, a.dv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.T == 0) return e;
