@@ -443,8 +443,20 @@ def extras(args, legs, out, torch, kda, wl, dev):
         lsteps = max(3, args.steps // 5)
         r = measure_prefill(args, lspec, 64, torch, kda, dev, lsteps, 2, "prefill_b8_h32_t8k")
         out["prefill_b8_h32_t8k"] = {k_: v_ for k_, v_ in r.items() if k_ != "ms_wall"}
-        print(f"# prefill_b8_h32_t8k: {r['ms_per_launch']:.3f} ms/launch", file=sys.stderr,
-              flush=True)
+        # the chunk-size comparison on the same workload: C = 16 and 32 are
+        # their own kernels; C = 128 runs as two 64-token chunks (its tiles do
+        # not fit one CU's LDS), so its row is the C = 64 kernel
+        sweep = {}
+        for C in (16, 32):
+            rc = measure_prefill(args, lspec, C, torch, kda, dev, lsteps, 1, None)
+            sweep[f"C{C}_ms_per_launch"] = rc["ms_per_launch"]
+        sweep["C64_ms_per_launch"] = r["ms_per_launch"]
+        sweep["C128_ms_per_launch"] = r["ms_per_launch"]
+        sweep["C128_note"] = "runs as two 64-token chunks (same kernel as C = 64)"
+        out["prefill_b8_h32_t8k"]["chunk_sweep"] = sweep
+        print(f"# prefill_b8_h32_t8k: {r['ms_per_launch']:.3f} ms/launch; C=16 "
+              f"{sweep['C16_ms_per_launch']:.3f}, C=32 {sweep['C32_ms_per_launch']:.3f}",
+              file=sys.stderr, flush=True)
 
     if "logits" in legs:
         # ---------------- H=16 prefill from raw projections (fused prologue)
@@ -707,13 +719,26 @@ def extras(args, legs, out, torch, kda, wl, dev):
                             cS, out=od)
 
         ms_d, _ = time_launches(dstep, dspec.steps, 8, torch)
+        # the same steady loop captured once as a HIP graph (no memset nodes:
+        # the steps write o and the state in place) and replayed
+        graph = torch.cuda.CUDAGraph()
+        it[0] = 0
+        with torch.cuda.graph(graph):
+            for _ in range(dspec.steps):
+                dstep()
+        ms_g, _ = time_launches(graph.replay, 4, 1, torch)
         out["longctx_decode"] = {
             "N": 1, "H": 32, "steps": dspec.steps, "decode_us_per_step": ms_d * 1e3,
-            "decode_note": "one sequence x 32 heads: 4 MiB of state per step; the events "
-                           "bracket back-to-back calls from Python, so this includes the "
-                           "binding's per-call host time (kernel time: profiles/)",
+            "graph_us_per_step": ms_g * 1e3 / dspec.steps,
+            "decode_note": "one sequence x 32 heads: 4 MiB of state per step; "
+                           "decode_us_per_step: events around back-to-back calls from "
+                           "Python (the binding's per-call host time included); "
+                           "graph_us_per_step: the 256 steps captured as one HIP graph "
+                           "and replayed (kernel time: profiles/)",
         }
-        print(f"# longctx_decode: {ms_d * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        print(f"# longctx_decode: {ms_d * 1e3:.1f} us/step eager, "
+              f"{ms_g * 1e3 / dspec.steps:.1f} us/step graph", file=sys.stderr, flush=True)
+        del graph
         del st, od, cS
         torch.cuda.empty_cache()
 

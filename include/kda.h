@@ -135,7 +135,11 @@ size_t kda_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int C,
  *                                   depend on C beyond rounding.  C = 128 runs
  *                                   as two 64-token chunks (a 128-row chunk's
  *                                   tiles do not fit one CU's LDS), so its
- *                                   workspace and results are those of C = 64
+ *                                   workspace and results are those of C = 64.
+ *                                   With float32 q/k/v/o at dk = 128, C = 64
+ *                                   (and so C = 128) is KDA_ERR_UNSUPPORTED:
+ *                                   the fp32 tiles of a 64-token chunk do not
+ *                                   fit beside each other; C = 16 and 32 run
  *   workspace, workspace_bytes      caller-owned device scratch of at least
  *                                   kda_prefill_workspace_bytes(...) bytes,
  *                                   16-byte aligned, overlapping no other
