@@ -96,6 +96,15 @@ __device__ __forceinline__ bf16x4 ld4(const uint16_t* p) {
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
+// f(std::integral_constant<int, I>) for I = B .. E-1, as straight-line code.
+template <int I, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < E) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, E>(f);
+  }
+}
+
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
   const uint2 x = __builtin_bit_cast(uint2, a), y = __builtin_bit_cast(uint2, b);
   return __builtin_bit_cast(bf16x8, make_uint4(x.x, x.y, y.x, y.y));
@@ -315,7 +324,7 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
 
 // ---------------------------------------------------------------------------
 // 3. The state gradient, backwards over the sub-chunks.  One workgroup per
-// (chain, 16-column tile): a state wave holds the tile in registers, lane
+// (chain, NT 16-column tiles): a state wave holds the tiles in registers, lane
 // (g, i) holding rows 16m + 4g + r, column i of it (the product's output
 // layout, which is also the layout of the next product's B operand),
 //   dS <- Diag(E_last) dS + (Q.E)^T dO - W^T (P^T dO + (K.E') dS),
@@ -326,13 +335,14 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
 // kAhead slots fit the 6-bit count of loads a wave can wait on).  One
 // barrier per sub-chunk.
 // ---------------------------------------------------------------------------
-template <int DK>
+template <int DK, int NT>
 struct ScanRing {
   using RB = BRec<DK>;
-  static constexpr int kRec = RB::oG + 4 * DK;   // bytes of a record the walk reads
-  static constexpr int kDO = 16 * 16 * 2;        // dO tile, 16 rows x 16 columns bf16
+  static constexpr int kTiles = NT;                  // 16-column tiles per state wave
+  static constexpr int kRec = RB::oG + 4 * DK;       // bytes of a record the walk reads
+  static constexpr int kDO = kTiles * 16 * 16 * 2;   // dO tiles, 16 rows x 16 columns bf16 each
   static constexpr int kBuf = kRec + kDO;
-  static constexpr int kAhead = 7, kNBuf = kAhead + 1;
+  static constexpr int kAhead = NT == 1 ? 7 : 6, kNBuf = kAhead + 1;
   static constexpr int kInsts = kRec / 1024;                       // 16-byte-lane loads of a record
   static constexpr int kSplit = (kInsts + 1) / 2;                  // loader 1: [0, kSplit), loader 2: the rest
   static constexpr int kFill1 = kSplit, kFill2 = kInsts - kSplit + kDO / 256;   // loads per slot
@@ -341,17 +351,17 @@ struct ScanRing {
   static_assert(kRec % 1024 == 0 && kAhead * kFill1 <= 63 && kAhead * kFill2 <= 63, "fill plan");
 };
 
-template <int DK>
+template <int DK, int NT>
 __global__ void __launch_bounds__(3 * kWave)
 kda_cb_scan_kernel(const char* __restrict__ grec, const uint16_t* __restrict__ gdO,
                    const float* __restrict__ gdST, float* __restrict__ gdSc, float* gdS0, int T,
                    int H, int DV) {
   using RB = BRec<DK>;
-  using RG = ScanRing<DK>;
+  using RG = ScanRing<DK, NT>;
   constexpr int NM = DK / 16;
   __shared__ __attribute__((aligned(16))) char ring[RG::kNBuf * RG::kBuf];
-  const int NJV = DV / 16;
-  const int chain = blockIdx.x / NJV, jt = blockIdx.x % NJV;
+  const int NJV = DV / (16 * NT);                    // workgroups per chain
+  const int chain = blockIdx.x / NJV, jt0 = NT * (blockIdx.x % NJV);
   const int b = chain / H, h = chain % H;
   const int NS = (T + kSB - 1) / kSB, NC = (T + kCB - 1) / kCB;
   const int lane = threadIdx.x % kWave;
@@ -362,7 +372,7 @@ kda_cb_scan_kernel(const char* __restrict__ grec, const uint16_t* __restrict__ g
   if (wv > 0) {
     // ---- loaders: order n (= sub-chunk NS - 1 - n) into slot n % kNBuf;
     // loader 1 the first kSplit KiB of the record, loader 2 the rest of it
-    // and the dO tile
+    // and the dO tiles
     const bool first = wv == 1;
     auto fill = [&](int n) {
       const int s = NS - 1 - n;
@@ -380,15 +390,15 @@ kda_cb_scan_kernel(const char* __restrict__ grec, const uint16_t* __restrict__ g
                                            (lds_void*)(dst + 1024 * i), 16, 0, 0);
 #pragma unroll
         for (int p = 0; p < RG::kDO / 256; ++p) {
-          const int d = 64 * p + lane;           // dword of the tile: row d / 8, dword d % 8
-          const int t = min(kSB * s + d / 8, T - 1);
+          const int d = 64 * p + lane;           // dword d: tile d / 128, row (d / 8) % 16, dword d % 8
+          const int tt = d / 128;
+          const int t = min(kSB * s + (d / 8) % 16, T - 1);
           __builtin_amdgcn_global_load_lds(
-              (gbl_void*)(gdO + (row0 + static_cast<size_t>(t) * H) * DV + 16 * jt + 2 * (d % 8)),
+              (gbl_void*)(gdO + (row0 + static_cast<size_t>(t) * H) * DV + 16 * (jt0 + tt) + 2 * (d % 8)),
               (lds_void*)(dst + RG::kRec + 256 * p), 4, 0, 0);
         }
       }
     };
-    // at most (kAhead - 1) slots of this wave's loads in flight: the oldest landed
     auto wait_oldest = [&] {
       if (first) __builtin_amdgcn_s_waitcnt(vmcnt_only((RG::kAhead - 1) * RG::kFill1));
       else __builtin_amdgcn_s_waitcnt(vmcnt_only((RG::kAhead - 1) * RG::kFill2));
@@ -408,61 +418,85 @@ kda_cb_scan_kernel(const char* __restrict__ grec, const uint16_t* __restrict__ g
   }
 
   const Lane ln = lane_now();
-  f32x4 dS[NM];
+  f32x4 dS[NT][NM];
 #pragma unroll
-  for (int m = 0; m < NM; ++m)
+  for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      dS[m][r] = gdST ? gdST[(static_cast<size_t>(chain) * DK + 16 * m + 4 * ln.g + r) * DV +
-                             16 * jt + ln.i]
-                      : 0.f;
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        dS[tt][m][r] = gdST ? gdST[(static_cast<size_t>(chain) * DK + 16 * m + 4 * ln.g + r) * DV +
+                                   16 * (jt0 + tt) + ln.i]
+                            : 0.f;
   for (int n = 0; n < NS; ++n) {
     const int s = NS - 1 - n;
     lds_barrier();
     const char* sb = slot(n);
     if (s == NS - 1 || (s % kNSB) == kNSB - 1) {
       // the gradient at the end of chunk s / 4, for the gradient kernel
-      float* dst = gdSc + (static_cast<size_t>(chain) * NC + s / kNSB) * DK * DV + 16 * jt + ln.i;
+      float* dst = gdSc + (static_cast<size_t>(chain) * NC + s / kNSB) * DK * DV + 16 * jt0 + ln.i;
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
+      for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(16 * m + 4 * ln.g + r) * DV] = dS[m][r];
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[(16 * m + 4 * ln.g + r) * DV + 16 * tt] = dS[tt][m][r];
     }
-    const uint16_t* dt = reinterpret_cast<const uint16_t*>(sb + RG::kRec);
-    const bf16x4 dob = bits4(dt[(4 * ln.g) * 16 + ln.i], dt[(4 * ln.g + 1) * 16 + ln.i],
-                             dt[(4 * ln.g + 2) * 16 + ln.i], dt[(4 * ln.g + 3) * 16 + ln.i]);
     auto frag32 = [&](int off, int m) {
       return *reinterpret_cast<const bf16x8*>(sb + off + (m * 64 + lane) * 16);
     };
-    // u = P^T dO + (K.E') dS, then dS <- Diag(E_last) dS + [(Q.E)^T | -W^T] [dO ; u]
-    const f32x4 pd = mma16(*reinterpret_cast<const bf16x4*>(sb + RB::oP + lane * 8), dob, zero4());
-    f32x4 t1a = zero4(), t1b = zero4();
+    // per tile: u = P^T dO + (K.E') dS, then
+    // dS <- Diag(E_last) dS + [(Q.E)^T | -W^T] [dO ; u]; each fragment read
+    // from LDS serves both tiles
+    const bf16x4 pfr = *reinterpret_cast<const bf16x4*>(sb + RB::oP + lane * 8);
+    bf16x4 dob[NT];
+    f32x4 t1[NT][2];
 #pragma unroll
-    for (int kk = 0; kk < NM / 2; kk += 2) {
-      t1a = mma32(frag32(RB::oK, kk), cat8(quad4(dS[2 * kk]), quad4(dS[2 * kk + 1])), t1a);
-      t1b = mma32(frag32(RB::oK, kk + 1), cat8(quad4(dS[2 * kk + 2]), quad4(dS[2 * kk + 3])), t1b);
+    for (int tt = 0; tt < NT; ++tt) {
+      const uint16_t* dt = reinterpret_cast<const uint16_t*>(sb + RG::kRec) + 256 * tt;
+      dob[tt] = bits4(dt[(4 * ln.g) * 16 + ln.i], dt[(4 * ln.g + 1) * 16 + ln.i],
+                      dt[(4 * ln.g + 2) * 16 + ln.i], dt[(4 * ln.g + 3) * 16 + ln.i]);
+      t1[tt][0] = mma16(pfr, dob[tt], zero4());
+      t1[tt][1] = zero4();
     }
-    f32x4 u;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) u[r] = t1a[r] + t1b[r] + pd[r];
-    const bf16x8 du8 = cat8(dob, quad4(u));
+    for (int kk = 0; kk < NM / 2; ++kk) {
+      const bf16x8 kf = frag32(RB::oK, kk);
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+        t1[tt][kk % 2] = mma32(kf, cat8(quad4(dS[tt][2 * kk]), quad4(dS[tt][2 * kk + 1])), t1[tt][kk % 2]);
+    }
+    bf16x8 du8[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      f32x4 u;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) u[r] = t1[tt][0][r] + t1[tt][1][r];
+      du8[tt] = cat8(dob[tt], quad4(u));
+    }
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      const f32x4 aq = mma32(frag32(RB::oQW, m), du8, zero4());
+      const bf16x8 qw = frag32(RB::oQW, m);
       const float4 gc = *reinterpret_cast<const float4*>(sb + RB::oG + 4 * (16 * m + 4 * ln.g));
-      dS[m][0] = gc.x * dS[m][0] + aq[0];
-      dS[m][1] = gc.y * dS[m][1] + aq[1];
-      dS[m][2] = gc.z * dS[m][2] + aq[2];
-      dS[m][3] = gc.w * dS[m][3] + aq[3];
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        const f32x4 aq = mma32(qw, du8[tt], zero4());
+        dS[tt][m][0] = gc.x * dS[tt][m][0] + aq[0];
+        dS[tt][m][1] = gc.y * dS[tt][m][1] + aq[1];
+        dS[tt][m][2] = gc.z * dS[tt][m][2] + aq[2];
+        dS[tt][m][3] = gc.w * dS[tt][m][3] + aq[3];
+      }
     }
   }
   if (gdS0) {
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+    for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        gdS0[(static_cast<size_t>(chain) * DK + 16 * m + 4 * ln.g + r) * DV + 16 * jt + ln.i] =
-            dS[m][r];
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          gdS0[(static_cast<size_t>(chain) * DK + 16 * m + 4 * ln.g + r) * DV + 16 * (jt0 + tt) +
+               ln.i] = dS[tt][m][r];
   }
 }
 
@@ -867,43 +901,47 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
           sp[r] = 0.f;
           sa[r] = 0.f;
         }
-        float Fm = 1.f, colp = 0.f;     // F_{t-1}; sum_{i<t} sig_i Gam(t-1, i)
-        const int tlo = 8 * part, thi = tlo + 8;
+        // quarter 0: t = 0..7; quarter 1: t = 8..15 (its recurrence starts at 0)
+        auto dalpha = [&](auto lo_c) {
+          constexpr int tlo = decltype(lo_c)::value, thi = tlo + 8;
+          float Fm = 1.f, colp = 0.f;     // F_{t-1}; sum_{i<t} sig_i Gam(t-1, i)
+          static_for<0, thi>([&](auto t_c) {
+            constexpr int t = decltype(t_c)::value;
+            if constexpr (t >= tlo) {
+              float rowp = 0.f, pair = 0.f, g = 1.f;
 #pragma unroll
-        for (int t = 0; t < kSB; ++t) {
-          if (t >= thi) break;
-          if (t >= tlo) {
-            float rowp = 0.f, pair = 0.f, g = 1.f;
-#pragma unroll
-            for (int r = t; r < kSB; ++r) {
-              if (r > t) g *= a[r];
-              rowp += rho[r] * g;
-              pair += (qq[r] * sp[r] + kq[r] * sa[r]) * g;
+              for (int r = t; r < kSB; ++r) {
+                if (r > t) g *= a[r];
+                rowp += rho[r] * g;
+                pair += (qq[r] * sp[r] + kq[r] * sa[r]) * g;
+              }
+              const float Ht = g;              // Gam(15, t) = H_t
+              const int tt = tb + t;
+              if (tt < T) gda[trow(tt) * DK + c] = Fm * rowp + Ht * colp + Fm * Ht * fin + pair;
             }
-            const float Ht = g;              // Gam(15, t) = H_t
-            const int tt = tb + t;
-            if (tt < T) gda[trow(tt) * DK + c] = Fm * rowp + Ht * colp + Fm * Ht * fin + pair;
-          }
-          if (t + 1 < thi) {
-            // column t of dP and dA (rows r > t matter from here on)
+            if constexpr (t + 1 < thi) {
+              // column t of dP and dA (rows r > t matter from here on)
 #pragma unroll
-            for (int q4 = (t + 1) / 4; q4 < kSB / 4; ++q4) {
-              const float4 p4 = *reinterpret_cast<const float4*>(sdPT + t * LDP + 4 * q4);
-              const float4 a4 = *reinterpret_cast<const float4*>(sdAT + t * LDP + 4 * q4);
-              const float pv[4] = {p4.x, p4.y, p4.z, p4.w}, av[4] = {a4.x, a4.y, a4.z, a4.w};
+              for (int q4 = (t + 1) / 4; q4 < kSB / 4; ++q4) {
+                const float4 p4 = *reinterpret_cast<const float4*>(sdPT + t * LDP + 4 * q4);
+                const float4 a4 = *reinterpret_cast<const float4*>(sdAT + t * LDP + 4 * q4);
+                const float pv[4] = {p4.x, p4.y, p4.z, p4.w}, av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int r = 4 * q4 + e;
-                if (r > t) {
-                  sp[r] = a[t] * sp[r] + pv[e] * kq[t];
-                  sa[r] = a[t] * sa[r] + av[e] * kq[t];
+                for (int e = 0; e < 4; ++e) {
+                  const int r = 4 * q4 + e;
+                  if (r > t) {
+                    sp[r] = a[t] * sp[r] + pv[e] * kq[t];
+                    sa[r] = a[t] * sa[r] + av[e] * kq[t];
+                  }
                 }
               }
+              colp = a[t] * colp + kq[t] * sUS[t * LDF + c];
+              Fm *= a[t];
             }
-            colp = a[t] * colp + kq[t] * sUS[t * LDF + c];
-            Fm *= a[t];
-          }
-        }
+          });
+        };
+        if (part == 0) dalpha(std::integral_constant<int, 0>{});
+        else dalpha(std::integral_constant<int, 8>{});
       } else {
         float F[kSB], Hs[kSB];
         F[0] = a[0];
@@ -1029,8 +1067,15 @@ hipError_t launch_prefill_backward_chunked(const PrefillBwdArgs& a) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  kda_cb_scan_kernel<128><<<static_cast<unsigned>(chains * (a.dv / 16)), 3 * kWave, 0, stream>>>(
-      recs, static_cast<const uint16_t*>(a.dO), a.dS_T, dSc, a.g_S0, a.T, a.H, a.dv);
+  // two column tiles per state wave once one tile per workgroup would fill
+  // the chip (a state wave is issue-bound: two tiles share its fragment reads
+  // but lengthen its step)
+  if (chains * (a.dv / 16) >= 256)
+    kda_cb_scan_kernel<128, 2><<<static_cast<unsigned>(chains * (a.dv / 32)), 3 * kWave, 0, stream>>>(
+        recs, static_cast<const uint16_t*>(a.dO), a.dS_T, dSc, a.g_S0, a.T, a.H, a.dv);
+  else
+    kda_cb_scan_kernel<128, 1><<<static_cast<unsigned>(chains * (a.dv / 16)), 3 * kWave, 0, stream>>>(
+        recs, static_cast<const uint16_t*>(a.dO), a.dS_T, dSc, a.g_S0, a.T, a.H, a.dv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.T == 0) return e;
   kda_cb_grad_kernel<128, 128><<<static_cast<unsigned>(chains * NC), kCbThreads, 0, stream>>>(

@@ -89,6 +89,11 @@ def test_lengths(T):
     run(spec(), B=2, T=T, H=2)
 
 
+def test_many_chains():
+    """64 chains: the state-gradient walk takes two column tiles per wave."""
+    run(spec(), B=4, T=100, H=16)
+
+
 def test_optional_states():
     run(spec(s0_std=0.0), B=1, T=70, H=2, with_dST=False)
 
