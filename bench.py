@@ -284,7 +284,8 @@ def main():
                     help="headline prefill only (no decode / large prefill lines)")
     ap.add_argument("--only", choices=["longctx", "prefill", "decode", "large", "logits",
                                        "decode_logits", "gdn", "decode_gdn", "longctx_decode",
-                                       "decode_bwd", "prefill_bwd", "prologue", "copy"],
+                                       "decode_bwd", "prefill_bwd", "prefill_bwd_large",
+                                       "prologue", "copy"],
                     default=None,
                     help="run one leg only (for profiler runs); 'copy' times a plain "
                          "1 GiB device-to-device copy used to calibrate HBM byte counters")
@@ -311,7 +312,8 @@ def main():
                           "ms_per_copy": ms, "GBps": 8 * n / (ms * 1e-3) / 1e9}), flush=True)
         return
     legs = ({"longctx", "prefill", "decode", "large", "logits", "decode_logits", "gdn",
-             "decode_gdn", "longctx_decode", "decode_bwd", "prefill_bwd", "prologue"}
+             "decode_gdn", "longctx_decode", "decode_bwd", "prefill_bwd", "prefill_bwd_large",
+             "prologue"}
             if args.only is None else {args.only})
     if args.no_extra:
         legs = {"longctx"}
@@ -643,7 +645,9 @@ def extras(args, legs, out, torch, kda, wl, dev):
               f"(Gated DeltaNet {ms_g:.3f} ms)", file=sys.stderr, flush=True)
         del px, pg, gx, cws
         torch.cuda.empty_cache()
-        # the largest batch, chunked only
+
+    if "prefill_bwd_large" in legs:
+        # ---------------- the chunked backward on the largest batch
         lspec = wl.PREFILL["prefill_b8_h32_t8k"]
         lx = wl.make_prefill_inputs(lspec, dev)
         lg = wl.make_prefill_backward_grads(lspec, dev)
