@@ -184,6 +184,39 @@ template <> struct Quad<float> {
 
 // A 16-byte vector of 16 / sizeof(element) values.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Input loads with or without the non-temporal hint.  On a long sequence the
+// split path streams every input once and keeps its chunk records in the
+// last-level cache between the two kernels; hinting the input loads as
+// streaming keeps them from evicting those records.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ uint2 ld_in(const uint16_t* p) {
+  if constexpr (NT) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    return make_uint2(v.x, v.y);
+  } else {
+    return *reinterpret_cast<const uint2*>(p);
+  }
+}
+template <bool NT>
+__device__ __forceinline__ float4 ld_in(const float* p) {
+  if constexpr (NT) {
+    const f32x4v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+  } else {
+    return *reinterpret_cast<const float4*>(p);
+  }
+}
+template <bool NT>
+__device__ __forceinline__ u32x4 ld_in16(const void* p) {
+  if constexpr (NT) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  } else {
+    return *reinterpret_cast<const u32x4*>(p);
+  }
+}
 template <typename OpT>
 __device__ __forceinline__ float vec_elem(const u32x4& v, int q) {
   if constexpr (Ty<OpT>::kBytes == 2)
@@ -605,7 +638,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
                    const void* __restrict__ ggate, const float* __restrict__ gbeta,
                    const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float* gST,
                    int B, int T, int H, int DV, char* __restrict__ gws, int cpb, int seg0,
-                   int segn, int qk_map) {
+                   int segn, int qk_map, int nt_in) {
   using Cf = PCfg<OpT, DK, C, DVT>;
   using E = typename Ty<OpT>::Elem;
   using PT = typename Pair<OpT>::T;
@@ -735,7 +768,8 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
   u32x4 gvv[Cf::NVT][4];
   float gbe = 0.f;
   float gsa = 1.f;              // scalar gate of row `lane` (wave 0, kScalar)
-  auto fetch_gates = [&](int tn) {
+  auto fetch_gates_nt = [&](int tn, auto nt) {
+    constexpr bool NT = decltype(nt)::value;
     const size_t base = (row0 + static_cast<size_t>(tn) * H) * DK;
     const float* pa = galpha + base;
     const E* pg = glogit + base;
@@ -758,14 +792,14 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
           } else if constexpr (kScalar) {
             // one gate per row: fetched below by wave 0, lane = row
           } else {
-            const float4 a4 = *reinterpret_cast<const float4*>(pa + off);
+            const float4 a4 = ld_in<NT>(pa + off);
             ga[it][j][0] = a4.x;
             ga[it][j][1] = a4.y;
             ga[it][j][2] = a4.z;
             ga[it][j][3] = a4.w;
           }
-          gkk[it][j] = Quad<OpT>::load(pk + off);
-          gqq[it][j] = Quad<OpT>::load(pq + off);
+          gkk[it][j] = ld_in<NT>(pk + off);
+          gqq[it][j] = ld_in<NT>(pq + off);
         }
       }
     }
@@ -774,7 +808,16 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         gsa = galpha[row0 + static_cast<size_t>(tn + min(tid, jmax)) * H];
     }
   };
-  auto fetch_values = [&](int tn) {
+  auto fetch_gates = [&](int tn) {
+    if constexpr (kPrep) {
+      if (nt_in) fetch_gates_nt(tn, std::true_type{});
+      else fetch_gates_nt(tn, std::false_type{});
+    } else {
+      fetch_gates_nt(tn, std::false_type{});
+    }
+  };
+  auto fetch_values_nt = [&](int tn, auto nt) {
+    constexpr bool NT = decltype(nt)::value;
     const E* pv = gv + (row0 + static_cast<size_t>(tn) * H) * DV + j0;
     const int jmax = T - 1 - tn;
     int t_ = tid;
@@ -787,8 +830,16 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         const int h = ip.h, J = ip.J, cc = Cf::VEC * ip.v;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          gvv[it][j] = *reinterpret_cast<const u32x4*>(pv + min(16 * J + 4 * h + j, jmax) * rsV + cc);
+          gvv[it][j] = ld_in16<NT>(pv + min(16 * J + 4 * h + j, jmax) * rsV + cc);
       }
+    }
+  };
+  auto fetch_values = [&](int tn) {
+    if constexpr (kPrep) {
+      if (nt_in) fetch_values_nt(tn, std::true_type{});
+      else fetch_values_nt(tn, std::false_type{});
+    } else {
+      fetch_values_nt(tn, std::false_type{});
     }
   };
   auto fetch_beta = [&](int tn) {   // every thread loads (only tid < C keep it): no branch
@@ -1716,7 +1767,7 @@ hipError_t launch_one(const PrefillArgs& a) {
                      dim3(PCfg<OpT, DK, C, DVT>::NTH), 0, static_cast<hipStream_t>(a.stream),
                      static_cast<const E*>(a.q), static_cast<const E*>(a.k),
                      static_cast<const E*>(a.v), a.gate, a.beta, a.S0, static_cast<E*>(a.o),
-                     a.S_T, a.B, a.T, a.H, a.dv, nullptr, 0, 0, 0, a.qk_map);
+                     a.S_T, a.B, a.T, a.H, a.dv, nullptr, 0, 0, 0, a.qk_map, 0);
   return hipGetLastError();
 }
 

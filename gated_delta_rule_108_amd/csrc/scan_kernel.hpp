@@ -392,12 +392,14 @@ bool split_fits(int dv) {
 // kSegmentBudget bytes so that they stay in the chip's last-level cache
 // (256 MiB of Infinity Cache on MI355X) between the two kernels, and the
 // workspace does not grow with T.  Between segments the fp32 state goes
-// through a carry region after the records.  Measured on 32 chains of
-// 131,072 tokens (dk = dv = 128, C = 64): the scan reads its records at
-// 0.77 us per chunk up to 128 MiB segments and 0.92 / 1.11 / 1.20 us at
-// 160 / 192 / 240 MiB, while the prep pays ~16 us per launch; 128 MiB is the
-// best sum (96 / 128 / 160 MiB: 4.13 / 3.98 / 4.19 ms).
-constexpr size_t kSegmentBudget = size_t{128} << 20;
+// through a carry region after the records.  Each prep launch pays ~16 us
+// of fixed cost, so segments should be as large as the cache lets the scan
+// find its records there.  With plain input loads that was 128 MiB (the scan
+// read its records at 0.77 us per chunk up to 128 MiB, 0.92 / 1.11 us at 160
+// / 192 MiB); with the inputs of a multi-segment call loaded non-temporally
+// (launch_split) it is 192 MiB (32 chains x 2^20 tokens, dk = dv = 128,
+// C = 64: 30.2 / 29.7 / 30.5 ms at 160 / 192 / 224 MiB).
+constexpr size_t kSegmentBudget = size_t{192} << 20;
 
 struct SplitPlan {
   int nc = 0;        // chunks per chain
@@ -442,7 +444,7 @@ inline int prep_chunks_per_block(long chains, int nc) {
 }
 
 template <typename OpT, int DK, int C, int DVT, int kIn>
-hipError_t launch_prep(const PrefillArgs& a, int seg0, int segn) {
+hipError_t launch_prep(const PrefillArgs& a, int seg0, int segn, bool nt_in) {
   using E = typename Ty<OpT>::Elem;
   if constexpr (!fits<OpT, DK, C, DVT>()) {
     return hipErrorInvalidValue;
@@ -458,7 +460,8 @@ hipError_t launch_prep(const PrefillArgs& a, int seg0, int segn) {
                        static_cast<hipStream_t>(a.stream), static_cast<const E*>(a.q),
                        static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.gate, a.beta,
                        a.S0, static_cast<E*>(a.o), a.S_T, a.B, a.T, a.H, a.dv,
-                       static_cast<char*>(a.workspace), cpb, seg0, segn, a.qk_map);
+                       static_cast<char*>(a.workspace), cpb, seg0, segn, a.qk_map,
+                       nt_in ? 1 : 0);
     return hipGetLastError();
   }
 }
@@ -475,15 +478,21 @@ hipError_t launch_split(const PrefillArgs& a) {
     float* carry = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + p.records);
     // T = 0 still runs one (empty) scan: it copies S0, or zeros, to S_T.
     const int nlaunch = p.nseg > 0 ? p.nseg : 1;
+    // Several segments: the inputs are streamed once and cannot stay in the
+    // cache anyway, so the prep loads them with the non-temporal hint and the
+    // records keep the cache (32 chains x 2^20 tokens: 32.1 -> 29.7 ms with
+    // 192 MiB segments).  One segment: plain loads (inputs a caller has just
+    // written, or re-reads, may still be cached).
+    const bool nt_in = p.nseg > 1;
     for (int sgi = 0; sgi < nlaunch; ++sgi) {
       const int seg0 = sgi * p.segch;
       const int segn = p.nseg > 0 ? std::min(p.segch, p.nc - seg0) : 0;
       hipError_t e = hipErrorInvalidValue;
       switch (a.dv) {
-        case 16: e = launch_prep<OpT, DK, C, 16, kIn>(a, seg0, segn); break;
-        case 32: e = launch_prep<OpT, DK, C, 32, kIn>(a, seg0, segn); break;
-        case 64: e = launch_prep<OpT, DK, C, 64, kIn>(a, seg0, segn); break;
-        case 128: e = launch_prep<OpT, DK, C, 128, kIn>(a, seg0, segn); break;
+        case 16: e = launch_prep<OpT, DK, C, 16, kIn>(a, seg0, segn, nt_in); break;
+        case 32: e = launch_prep<OpT, DK, C, 32, kIn>(a, seg0, segn, nt_in); break;
+        case 64: e = launch_prep<OpT, DK, C, 64, kIn>(a, seg0, segn, nt_in); break;
+        case 128: e = launch_prep<OpT, DK, C, 128, kIn>(a, seg0, segn, nt_in); break;
       }
       if (e != hipSuccess) return e;
       const float* s_in = sgi == 0 ? a.S0 : carry;

@@ -100,12 +100,12 @@ typedef enum { KDA_QK_AS_GIVEN = 0, KDA_QK_L2 = 1, KDA_QK_SILU_L2 = 2 } kda_qk_m
  *     chunk to the workspace (the state-free chunk quantities W, Q.E,
  *     (K.E')^T, P, the chunk decay and Y diag(beta) V), then a scan kernel
  *     walks the chunks in order.  Long sequences go in segments of whole
- *     chunks (records of one segment at a time, at most 128 MiB unless one
+ *     chunks (records of one segment at a time, at most 192 MiB unless one
  *     chunk of every chain is larger), with the fp32 state carried between
  *     segments.  With
  *       rec    = round_up((3*C*dk + C*C + C*dv) * sizeof(dt) + 4*dk, 256)
  *       nc     = ceil(T / C)
- *       segmax = max(1, floor(128 MiB / (B*H*rec)))
+ *       segmax = max(1, floor(192 MiB / (B*H*rec)))
  *       nseg   = ceil(nc / segmax),  segch = ceil(nc / nseg)
  *     the workspace is B*H*segch*rec bytes, plus B*H*dk*dv*4 bytes of
  *     carried state when nseg > 1 (0 bytes when T = 0);

@@ -184,10 +184,10 @@ def test_empty_sequence_and_null_state_out():
 
 @pytest.mark.parametrize("gated", [True, False])
 def test_split_segments(gated):
-    """16 chains x 313 chunks (T = 20000): three segments of the split path
+    """16 chains x 438 chunks (T = 28000): three segments of the split path
     with the state carried between them; two chains match the oracle."""
     spec = wl.PREFILL["prefill_h16_t4k"]
-    T, H = 20000, 16
+    T, H = 28000, 16
     inp = wl.make_gdn_inputs(spec, T=T, H=H, gated=gated)
     inp["S0"] = 0.05 * torch.randn(1, H, 128, 128, generator=torch.Generator().manual_seed(9))
     o, S = run(inp, 64)

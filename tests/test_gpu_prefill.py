@@ -219,15 +219,16 @@ def test_prep_chunk_runs_ragged():
 
 
 def test_split_segments():
-    """A sequence whose records exceed one segment: 16 chains x 313 chunks
-    (T = 20000, the last chunk 32 rows) run as three segments of 105, 105 and
-    103 chunks with the state carried between them.  Two chains match the
-    oracle; resuming at a chunk boundary (tokens 6720.., itself two segments
-    with other boundaries) reproduces the full run bit for bit."""
+    """A sequence whose records exceed one segment: 16 chains x 438 chunks
+    (T = 28000, the last chunk 32 rows) run as three segments of 146 chunks
+    with the state carried between them (inputs loaded non-temporally).  Two
+    chains match the oracle; resuming at a chunk boundary (tokens 6400..,
+    itself two segments with other boundaries) reproduces the full run bit
+    for bit."""
     spec = wl.PREFILL["prefill_h16_t4k"]
-    T, H, cut = 20000, 16, 105 * 64
+    T, H, cut = 28000, 16, 100 * 64
     ws = kda().prefill_workspace_bytes(1, T, H, 128, 128, 64)
-    assert ws == 16 * 105 * 74240 + 16 * 128 * 128 * 4            # three segments
+    assert ws == 16 * 146 * 74240 + 16 * 128 * 128 * 4            # three segments
     inp = wl.make_prefill_inputs(spec, T=T, H=H)
     inp["S0"] = 0.05 * torch.randn(1, H, 128, 128, generator=torch.Generator().manual_seed(7))
     g = to_dev(inp)

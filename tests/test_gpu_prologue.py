@@ -228,11 +228,11 @@ def test_empty_sequence_and_null_state_out():
 
 
 def test_split_segments():
-    """16 chains x 313 chunks (T = 20000): the split path runs three segments
+    """16 chains x 438 chunks (T = 28000): the split path runs three segments
     with the state carried between them; two chains match the oracle."""
     spec = wl.PREFILL["prefill_h16_t4k"]
-    T, H = 20000, 16
-    assert kda().prefill_workspace_bytes(1, T, H, 128, 128, 64) == 16 * 105 * 74240 + 16 * 128 * 128 * 4
+    T, H = 28000, 16
+    assert kda().prefill_workspace_bytes(1, T, H, 128, 128, 64) == 16 * 146 * 74240 + 16 * 128 * 128 * 4
     inp = wl.make_prefill_logit_inputs(spec, T=T, H=H)
     inp["S0"] = 0.05 * torch.randn(1, H, 128, 128, generator=torch.Generator().manual_seed(8))
     o, S = run(inp, 64, "l2")
