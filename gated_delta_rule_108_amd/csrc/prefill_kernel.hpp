@@ -1658,14 +1658,37 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         }
     }
     lds_barrier();
+    // One column tile of S^T (and of U^T) per wave, the same tile for the
+    // output and the state maps: its matrix-core B fragments load from LDS
+    // once per chunk and serve every row block, instead of once per row
+    // block (the state phases are bound by LDS bandwidth).
+    constexpr bool kHoldB = kBF && UM::WR == 1 && SM::WR == 1 && UM::CA == 1 && SM::CA == 1 &&
+                            UM::WC == SM::WC && DK % 32 == 0 && C % 32 == 0;
+    using FB = typename Frag<OpT, kBF ? 32 : 4>::T;
+    FB sB[kHoldB ? DK / 32 : 1];
+    if constexpr (kHoldB) {
+      if (UM::active(wave)) {
+        const Lane ln = lane_now();
+        const Src<OpT> sb{ST + 16 * UM::col0(wave) * LDK, LDK, ln};
+#pragma unroll
+        for (int k = 0; k < DK / 32; ++k) sB[k] = sb.template get<32>(32 * k);
+      }
+    }
     if (UM::active(wave)) {
       const Lane ln = lane_now();
 #pragma unroll
       for (int a = 0; a < UM::RA; ++a) {
         const int R = UM::row0(wave) + a;
         f32x4 x[UM::CA];
-        mma_row<OpT, UM::CA>(x, 0, DK, Src<OpT>{Wm + 16 * R * LDK, LDK, ln},
-                             Src<OpT>{ST + 16 * UM::col0(wave) * LDK, LDK, ln}, 16 * LDK);
+        if constexpr (kHoldB) {
+          const Src<OpT> wa{Wm + 16 * R * LDK, LDK, ln};
+          x[0] = zero4();
+#pragma unroll
+          for (int k = 0; k < DK / 32; ++k) x[0] = mfma<OpT, 32>(wa.template get<32>(32 * k), sB[k], x[0]);
+        } else {
+          mma_row<OpT, UM::CA>(x, 0, DK, Src<OpT>{Wm + 16 * R * LDK, LDK, ln},
+                               Src<OpT>{ST + 16 * UM::col0(wave) * LDK, LDK, ln}, 16 * LDK);
+        }
         // U = U~ - W S, staged transposed for the products over tokens
 #pragma unroll
         for (int bb = 0; bb < UM::CA; ++bb) {
@@ -1682,15 +1705,36 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
     {
       // O = (Q E) S + P U
       const Lane ln = lane_now();
+      FB uB[kHoldB ? C / 32 : 1];
+      if constexpr (kHoldB) {
+        if (UM::active(wave)) {
+          const Src<OpT> ub{UT + 16 * UM::col0(wave) * LDC, LDC, ln};
+#pragma unroll
+          for (int k = 0; k < C / 32; ++k) uB[k] = ub.template get<32>(32 * k);
+        }
+      }
       if (UM::active(wave)) {
 #pragma unroll
         for (int a = 0; a < UM::RA; ++a) {
           const int R = UM::row0(wave) + a;
           f32x4 o[UM::CA], pu[UM::CA];
-          mma_row<OpT, UM::CA>(o, 0, DK, Src<OpT>{Qr + 16 * R * LDK, LDK, ln},
-                               Src<OpT>{ST + 16 * UM::col0(wave) * LDK, LDK, ln}, 16 * LDK);
-          mma_row<OpT, UM::CA>(pu, 0, 16 * (R + 1), Src<OpT>{PP + 16 * R * LDC, LDC, ln},
-                               Src<OpT>{UT + 16 * UM::col0(wave) * LDC, LDC, ln}, 16 * LDC);
+          if constexpr (kHoldB) {
+            // P's blocks right of the diagonal are zeros in LDS, so the
+            // product over tokens may run to the next multiple of 32
+            const Src<OpT> qa{Qr + 16 * R * LDK, LDK, ln}, pa{PP + 16 * R * LDC, LDC, ln};
+            o[0] = zero4();
+            pu[0] = zero4();
+#pragma unroll
+            for (int k = 0; k < DK / 32; ++k) o[0] = mfma<OpT, 32>(qa.template get<32>(32 * k), sB[k], o[0]);
+#pragma unroll
+            for (int k = 0; k < C / 32; ++k)
+              if (32 * k < 16 * (R + 1)) pu[0] = mfma<OpT, 32>(pa.template get<32>(32 * k), uB[k], pu[0]);
+          } else {
+            mma_row<OpT, UM::CA>(o, 0, DK, Src<OpT>{Qr + 16 * R * LDK, LDK, ln},
+                                 Src<OpT>{ST + 16 * UM::col0(wave) * LDK, LDK, ln}, 16 * LDK);
+            mma_row<OpT, UM::CA>(pu, 0, 16 * (R + 1), Src<OpT>{PP + 16 * R * LDC, LDC, ln},
+                                 Src<OpT>{UT + 16 * UM::col0(wave) * LDC, LDC, ln}, 16 * LDC);
+          }
 #pragma unroll
           for (int bb = 0; bb < UM::CA; ++bb) add4(o[bb], pu[bb]);
 #pragma unroll
@@ -1714,8 +1758,15 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
         for (int a = 0; a < SM::RA; ++a) {
           const int Cb = SM::row0(wave) + a;
           f32x4 acc[SM::CA];
-          mma_row<OpT, SM::CA>(acc, 0, C, Src<OpT>{KgT + 16 * Cb * LDC, LDC, ln},
-                               Src<OpT>{UT + 16 * SM::col0(wave) * LDC, LDC, ln}, 16 * LDC);
+          if constexpr (kHoldB) {
+            const Src<OpT> ka{KgT + 16 * Cb * LDC, LDC, ln};
+            acc[0] = zero4();
+#pragma unroll
+            for (int k = 0; k < C / 32; ++k) acc[0] = mfma<OpT, 32>(ka.template get<32>(32 * k), uB[k], acc[0]);
+          } else {
+            mma_row<OpT, SM::CA>(acc, 0, C, Src<OpT>{KgT + 16 * Cb * LDC, LDC, ln},
+                                 Src<OpT>{UT + 16 * SM::col0(wave) * LDC, LDC, ln}, 16 * LDC);
+          }
           const float4 gc = *reinterpret_cast<const float4*>(sGC + 16 * Cb + 4 * ln.g);
 #pragma unroll
           for (int bb = 0; bb < SM::CA; ++bb) {
