@@ -173,9 +173,12 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
       const int t = t0 + kSB * J + r;
       const bool ok = t < T;
       const size_t e = (row0 + static_cast<size_t>(ok ? t : 0) * H) * DK + c;
-      a[r] = ok ? galpha[e] : 1.f;
-      kk[r] = ok ? bf16_to_f32(gk[e]) : 0.f;
-      qq[r] = ok ? bf16_to_f32(gq[e]) : 0.f;
+      // loads from a clamped row, then a select: no branch around a load
+      const float av = galpha[e];
+      const uint16_t kv = gk[e], qv = gq[e];
+      a[r] = ok ? av : 1.f;
+      kk[r] = ok ? bf16_to_f32(kv) : 0.f;
+      qq[r] = ok ? bf16_to_f32(qv) : 0.f;
     }
     float F[kSB], Hs[kSB];
     F[0] = a[0];
@@ -572,16 +575,17 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
       for (int r = 0; r < 4; ++r)
         Sw[m][r] = gSc[sbase + (16 * m + 4 * ln.g + r) * DV + 16 * jt + ln.i];
   }
-  // S of sub-chunks 1 .. 3 (operand type) wait in the workspace between the
-  // two passes (registers cannot hold all four next to the gate phase):
-  // [chain][chunk][sub-chunk - 1][wave][m][lane]
-  bf16x4* sbw = gSb + ((static_cast<size_t>(chain) * NC + cc) * (kNSB - 1) * (kCbThreads / kWave) +
+  // S of each sub-chunk (operand type) waits in the workspace between the
+  // two passes (registers cannot hold them next to the gate phase), the
+  // first one too, so that the backward pass loads every sub-chunk's S the
+  // same way: [chain][chunk][sub-chunk][wave][m][lane]
+  bf16x4* sbw = gSb + ((static_cast<size_t>(chain) * NC + cc) * kNSB * (kCbThreads / kWave) +
                        wave) * NM * kWave + lane;
   auto sb_slot = [&](int J, int m) {
-    return sbw + (static_cast<size_t>(J - 1) * (kCbThreads / kWave) * NM + m) * kWave;
+    return sbw + (static_cast<size_t>(J) * (kCbThreads / kWave) * NM + m) * kWave;
   };
   // U of each sub-chunk (this wave's columns), after them: [chain][chunk][J][wave][lane]
-  bf16x4* ubw = gSb + static_cast<size_t>(gridDim.x) * (kNSB - 1) * (kCbThreads / kWave) * NM * kWave +
+  bf16x4* ubw = gSb + static_cast<size_t>(gridDim.x) * kNSB * (kCbThreads / kWave) * NM * kWave +
                 ((static_cast<size_t>(chain) * NC + cc) * kNSB * (kCbThreads / kWave) + wave) * kWave + lane;
   auto ub_slot = [&](int J) { return ubw + static_cast<size_t>(J) * (kCbThreads / kWave) * kWave; };
 
@@ -598,15 +602,18 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
     const char* rec = rec_of(J);
     const int R = tid / 64, l = tid % 64;
     f.wv = *reinterpret_cast<const uint2*>(rec + RB::oQW + (R * 64 + l) * 16 + 8);
-    f.kv = tid < (DK / 32) * 64 ? *reinterpret_cast<const uint4*>(rec + RB::oK + (tid % ((DK / 32) * 64)) * 16)
-                                : make_uint4(0, 0, 0, 0);
-    f.y = tid < kSB * kSB ? reinterpret_cast<const float*>(rec + RB::oY)[tid % (kSB * kSB)] : 0.f;
-    f.pc = tid < DK ? reinterpret_cast<const float*>(rec + RB::oG)[tid % DK] : 0.f;
+    // every load unconditional (indices wrap into range; the lanes past a
+    // table's end load a repeat and never use it), and rows past T are
+    // zeroed where they are used, so that nothing waits for these loads
+    // before the next sub-chunk
+    f.kv = *reinterpret_cast<const uint4*>(rec + RB::oK + (tid % ((DK / 32) * 64)) * 16);
+    f.y = reinterpret_cast<const float*>(rec + RB::oY)[tid % (kSB * kSB)];
+    f.pc = reinterpret_cast<const float*>(rec + RB::oG)[tid % DK];
     const Lane ln = lane_now();
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = t0 + kSB * J + 4 * ln.g + r;
-      f.v[r] = t < T ? gv[trow(t) * DV + 16 * jt + ln.i] : 0;
+      f.v[r] = gv[trow(min(t, T - 1)) * DV + 16 * jt + ln.i];
     }
   };
   FwdIn fin_cur;
@@ -644,14 +651,17 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
       // U~ = Y (beta V)
       uint16_t vb[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vb[r] = f32_to_bf16(sBe[kSB * J + 4 * ln.g + r] * bf16_to_f32(cur.v[r]));
+      for (int r = 0; r < 4; ++r) {
+        // beta is zero past T, so is its product with the repeated row
+        vb[r] = f32_to_bf16(sBe[kSB * J + 4 * ln.g + r] * bf16_to_f32(cur.v[r]));
+      }
       f32x4 u = mma16(ld4(sY + ln.i * LDT + 4 * ln.g), bits4(vb[0], vb[1], vb[2], vb[3]), zero4());
       // U = U~ - W S
       f32x4 ws = zero4();
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const bf16x4 sb = quad4(Sw[m]);
-        if (J > 0) *sb_slot(J, m) = sb;
+        *sb_slot(J, m) = sb;
         ws = mma16(ld4(sW + ln.i * LDK + 16 * m + 4 * ln.g), sb, ws);
       }
 #pragma unroll
@@ -695,11 +705,12 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int t = t0 + kSB * J + 4 * part + x;
-      const bool ok = t < T;
-      const size_t e = trow(ok ? t : 0) * DK + c;
-      na[x] = ok ? galpha[e] : 1.f;
-      nk[x] = ok ? gk[e] : 0;
-      nq[x] = ok ? gq[e] : 0;
+      // raw loads from a clamped row; rows past T are fixed up where they
+      // are used (a select here would wait for the load)
+      const size_t e = trow(min(t, T - 1)) * DK + c;
+      na[x] = galpha[e];
+      nk[x] = gk[e];
+      nq[x] = gq[e];
     }
   };
   fetch_rows(ns - 1);
@@ -707,13 +718,25 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   for (int J = ns - 1; J >= 0; --J) {
     const char* rec = rec_of(J);
     const int tb = t0 + kSB * J;
-    float a[4];
-    uint16_t kbv[4], qbv[4];
+    // Global loads of this sub-chunk, in the order they are needed: a vector
+    // memory wait covers every load issued before the one it waits for, so a
+    // value needed early that loaded late would drain the next sub-chunk's row
+    // prefetch (issued during staging) as well.
+    const float ypre = reinterpret_cast<const float*>(rec + RB::oY)[tid % (kSB * kSB)];
+    const float pcpre = reinterpret_cast<const float*>(rec + RB::oG)[tid % DK];
+    uint16_t dov[4], vv[4];
+    {
+      const Lane ln = lane_now();
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      a[x] = na[x];
-      kbv[x] = nk[x];
-      qbv[x] = nq[x];
+      for (int r = 0; r < 4; ++r) {
+        const int t = tb + 4 * ln.g + r;
+        dov[r] = gdO[trow(min(t, T - 1)) * DV + 16 * jt + ln.i];   // rows past T: zeroed at use
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = tb + 4 * ln.g + r;
+        vv[r] = gv[trow(min(t, T - 1)) * DV + 16 * jt + ln.i];   // rows past T: zeroed at use
+      }
     }
     // record fragments of this sub-chunk, used after the next barriers
     const bf16x4 pfr = *reinterpret_cast<const bf16x4*>(rec + RB::oP + lane * 8);
@@ -726,22 +749,23 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
       qwfr[m] = *reinterpret_cast<const bf16x8*>(rec + RB::oQW + (m * 64 + lane) * 16);
     const bf16x4 uj = *ub_slot(J);
     bf16x4 Sj[NM];   // S of this sub-chunk, this wave's columns
-    {
-      const Lane ln = lane_now();
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        if (J > 0) {
-          Sj[m] = *sb_slot(J, m);
-        } else {
-          f32x4 x;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) x[r] = gSc[sbase + (16 * m + 4 * ln.g + r) * DV + 16 * jt + ln.i];
-          Sj[m] = quad4(x);
-        }
-      }
-    }
+    for (int m = 0; m < NM; ++m) Sj[m] = *sb_slot(J, m);
+    // keep these loads ahead of the next sub-chunk's row prefetch below
+    asm volatile("" ::: "memory");
     // ---- stage: raw q, k, alpha of the sub-chunk; K.E and (K.E)^T; Y^T; decay
     {
+      // this sub-chunk's rows, prefetched during the last one (read only
+      // now, after this sub-chunk's loads have been issued)
+      float a[4];
+      uint16_t kbv[4], qbv[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const bool ok = tb + 4 * part + x < T;
+        a[x] = ok ? na[x] : 1.f;
+        kbv[x] = ok ? nk[x] : 0;
+        qbv[x] = ok ? nq[x] : 0;
+      }
       float kk[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
@@ -751,7 +775,10 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
         sQr[r * LDK + c] = qbv[x];
         sAl[r * DK + c] = a[x];
       }
-      if (J > 0) fetch_rows(J - 1);
+      // unconditional (the last sub-chunk re-fetches its own rows) so that the
+      // memory-operation count is the same on every path and later waits can
+      // leave these loads in flight
+      fetch_rows(J > 0 ? J - 1 : 0);
       lds_barrier();
       // F_r = prod of alpha through r within the sub-chunk
       float F = 1.f;
@@ -763,14 +790,13 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
         F *= a[x];
         sKE[r * LDK + c] = f32_to_bf16(kk[x] * F);
       }
-      if (tid < kSB * kSB) {
-        const float y = reinterpret_cast<const float*>(rec + RB::oY)[tid];
-        sYT[(tid % kSB) * LDT + tid / kSB] = f32_to_bf16(y);
-      }
-      if (tid < DK) sPC[tid] = reinterpret_cast<const float*>(rec + RB::oG)[tid];
     }
-    // ---- this wave's column tile: S, dS, dO, U into LDS (operand type)
+    // ---- this wave's column tile: S, dS, dO, U into LDS (operand type);
+    // Y^T and the decay (used from the column phase on, so the staging above
+    // does not wait for this sub-chunk's loads)
     {
+      if (tid < kSB * kSB) sYT[(tid % kSB) * LDT + tid / kSB] = f32_to_bf16(ypre);
+      if (tid < DK) sPC[tid] = pcpre;
       const Lane ln = lane_now();
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
@@ -785,7 +811,7 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = tb + 4 * ln.g + r;
-        sdO[(4 * ln.g + r) * LDV + 16 * jt + ln.i] = t < T ? gdO[trow(t) * DV + 16 * jt + ln.i] : 0;
+        sdO[(4 * ln.g + r) * LDV + 16 * jt + ln.i] = t < T ? dov[r] : 0;
         sU[(4 * ln.g + r) * LDV + 16 * jt + ln.i] = f32_to_bf16(unbf(uj, r));
       }
     }
@@ -814,7 +840,7 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * ln.g + r, t = tb + row;
-        const float v = t < T ? bf16_to_f32(gv[trow(t) * DV + 16 * jt + ln.i]) : 0.f;
+        const float v = t < T ? bf16_to_f32(vv[r]) : 0.f;
         const float x = v - ks[r];
         if (t < T) gdv[trow(t) * DV + 16 * jt + ln.i] = sBe[kSB * J + row] * dZ[r];
         const float db = row16_sum(dZ[r] * x);
@@ -1036,7 +1062,7 @@ size_t prefill_backward_chunked_workspace(int B, int T, int H, int dk, int dv) {
   const size_t o = (chains * T * dv * 2 + 255) / 256 * 256;
   const size_t states = chains * nc * dk * dv * sizeof(float);
   const size_t recs = chains * ns * BRec<128>::kBytes;
-  const size_t sub_states = chains * nc * (kNSB - 1) * dk * dv * 2;   // bf16
+  const size_t sub_states = chains * nc * kNSB * dk * dv * 2;   // bf16
   const size_t sub_u = chains * nc * kNSB * kSB * dv * 2;            // bf16
   return fwd + o + 2 * states + recs + sub_states + sub_u;
 }
