@@ -579,10 +579,12 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   // two passes (registers cannot hold them next to the gate phase), the
   // first one too, so that the backward pass loads every sub-chunk's S the
   // same way: [chain][chunk][sub-chunk][wave][m][lane]
-  bf16x4* sbw = gSb + ((static_cast<size_t>(chain) * NC + cc) * kNSB * (kCbThreads / kWave) +
-                       wave) * NM * kWave + lane;
-  auto sb_slot = [&](int J, int m) {
-    return sbw + (static_cast<size_t>(J) * (kCbThreads / kWave) * NM + m) * kWave;
+  // (two row blocks m per 16-byte element: [..][wave][m / 2][lane])
+  uint4* sbw = reinterpret_cast<uint4*>(gSb) +
+               ((static_cast<size_t>(chain) * NC + cc) * kNSB * (kCbThreads / kWave) + wave) *
+                   (NM / 2) * kWave + lane;
+  auto sb_slot = [&](int J, int mp) {
+    return sbw + (static_cast<size_t>(J) * (kCbThreads / kWave) * (NM / 2) + mp) * kWave;
   };
   // U of each sub-chunk (this wave's columns), after them: [chain][chunk][J][wave][lane]
   bf16x4* ubw = gSb + static_cast<size_t>(gridDim.x) * kNSB * (kCbThreads / kWave) * NM * kWave +
@@ -658,10 +660,13 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
       f32x4 u = mma16(ld4(sY + ln.i * LDT + 4 * ln.g), bits4(vb[0], vb[1], vb[2], vb[3]), zero4());
       // U = U~ - W S
       f32x4 ws = zero4();
+      uint2 sbp = make_uint2(0u, 0u);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const bf16x4 sb = quad4(Sw[m]);
-        *sb_slot(J, m) = sb;
+        const uint2 sw = __builtin_bit_cast(uint2, sb);
+        if (m % 2 == 0) sbp = sw;
+        else *sb_slot(J, m / 2) = make_uint4(sbp.x, sbp.y, sw.x, sw.y);
         ws = mma16(ld4(sW + ln.i * LDK + 16 * m + 4 * ln.g), sb, ws);
       }
 #pragma unroll
@@ -697,21 +702,21 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   // gate phase: key channel, quarter of the rows (wave-uniform: DK is a
   // multiple of the wave size)
   const int c = tid % DK, part = __builtin_amdgcn_readfirstlane(tid / DK);
-  // raw alpha, k, q of rows 4 part .. +3 of a sub-chunk, loaded one
-  // sub-chunk ahead
-  float na[4];
-  uint16_t nk[4], nq[4];
+  // raw alpha, k, q of a sub-chunk, loaded one sub-chunk ahead: thread
+  // (row rr, channel quad cq) holds channels 4cq .. 4cq+3 of row rr, so a row
+  // piece is one 16-byte and two 8-byte loads
+  static_assert(kSB * DK / 4 == kCbThreads, "one channel quad of one row per thread");
+  const int rr = tid / (DK / 4), cq = 4 * (tid % (DK / 4));
+  float4 na;
+  uint2 nk, nq;
   auto fetch_rows = [&](int J) {
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int t = t0 + kSB * J + 4 * part + x;
-      // raw loads from a clamped row; rows past T are fixed up where they
-      // are used (a select here would wait for the load)
-      const size_t e = trow(min(t, T - 1)) * DK + c;
-      na[x] = galpha[e];
-      nk[x] = gk[e];
-      nq[x] = gq[e];
-    }
+    // raw loads from a clamped row; a row past T is fixed up where it is
+    // used (a select here would wait for the load)
+    const int t = t0 + kSB * J + rr;
+    const size_t e = trow(min(t, T - 1)) * DK + cq;
+    na = *reinterpret_cast<const float4*>(galpha + e);
+    nk = *reinterpret_cast<const uint2*>(gk + e);
+    nq = *reinterpret_cast<const uint2*>(gq + e);
   };
   fetch_rows(ns - 1);
 #pragma nounroll
@@ -750,30 +755,23 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
     const bf16x4 uj = *ub_slot(J);
     bf16x4 Sj[NM];   // S of this sub-chunk, this wave's columns
 #pragma unroll
-    for (int m = 0; m < NM; ++m) Sj[m] = *sb_slot(J, m);
+    for (int mp = 0; mp < NM / 2; ++mp) {
+      const uint4 v = *sb_slot(J, mp);
+      Sj[2 * mp] = __builtin_bit_cast(bf16x4, make_uint2(v.x, v.y));
+      Sj[2 * mp + 1] = __builtin_bit_cast(bf16x4, make_uint2(v.z, v.w));
+    }
     // keep these loads ahead of the next sub-chunk's row prefetch below
     asm volatile("" ::: "memory");
     // ---- stage: raw q, k, alpha of the sub-chunk; K.E and (K.E)^T; Y^T; decay
     {
       // this sub-chunk's rows, prefetched during the last one (read only
-      // now, after this sub-chunk's loads have been issued)
-      float a[4];
-      uint16_t kbv[4], qbv[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const bool ok = tb + 4 * part + x < T;
-        a[x] = ok ? na[x] : 1.f;
-        kbv[x] = ok ? nk[x] : 0;
-        qbv[x] = ok ? nq[x] : 0;
-      }
-      float kk[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int r = 4 * part + x;
-        kk[x] = bf16_to_f32(kbv[x]);
-        sKr[r * LDK + c] = kbv[x];
-        sQr[r * LDK + c] = qbv[x];
-        sAl[r * DK + c] = a[x];
+      // now, after this sub-chunk's loads have been issued); a row past T
+      // is alpha = 1, k = q = 0
+      {
+        const bool ok = tb + rr < T;
+        *reinterpret_cast<float4*>(sAl + rr * DK + cq) = ok ? na : make_float4(1.f, 1.f, 1.f, 1.f);
+        *reinterpret_cast<uint2*>(sKr + rr * LDK + cq) = ok ? nk : make_uint2(0u, 0u);
+        *reinterpret_cast<uint2*>(sQr + rr * LDK + cq) = ok ? nq : make_uint2(0u, 0u);
       }
       // unconditional (the last sub-chunk re-fetches its own rows) so that the
       // memory-operation count is the same on every path and later waits can
@@ -787,8 +785,8 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int r = 4 * part + x;
-        F *= a[x];
-        sKE[r * LDK + c] = f32_to_bf16(kk[x] * F);
+        F *= sAl[r * DK + c];
+        sKE[r * LDK + c] = f32_to_bf16(bf16_to_f32(sKr[r * LDK + c]) * F);
       }
     }
     // ---- this wave's column tile: S, dS, dO, U into LDS (operand type);

@@ -418,9 +418,16 @@ SplitPlan split_plan(int B, int T, int H, int dv, size_t budget = kSegmentBudget
   p.nc = (T + C - 1) / C;
   if (p.nc == 0) return p;
   const size_t per_chunk = chains * rec;   // one chunk of every chain
-  const size_t segmax = std::max<size_t>(1, budget / per_chunk);
+  size_t segmax = std::max<size_t>(1, budget / per_chunk);
+  // The prep kernel splits a segment's chunks of each chain into
+  // floor(256 / chains) equal runs (prep_chunks_per_block); a segment length
+  // that is a multiple of that count leaves no run shorter than the others.
+  const size_t runs = chains < 256 ? 256 / chains : 1;
+  if (segmax > runs) segmax -= segmax % runs;
   p.nseg = static_cast<int>((static_cast<size_t>(p.nc) + segmax - 1) / segmax);
-  p.segch = (p.nc + p.nseg - 1) / p.nseg;
+  size_t segch = (static_cast<size_t>(p.nc) + p.nseg - 1) / p.nseg;
+  if (p.nseg > 1) segch = std::min(segmax, (segch + runs - 1) / runs * runs);
+  p.segch = static_cast<int>(segch);
   p.records = chains * p.segch * rec;
   p.carry = p.nseg > 1 ? chains * DK * dv * sizeof(float) : 0;
   return p;

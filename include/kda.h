@@ -105,8 +105,11 @@ typedef enum { KDA_QK_AS_GIVEN = 0, KDA_QK_L2 = 1, KDA_QK_SILU_L2 = 2 } kda_qk_m
  *     segments.  With
  *       rec    = round_up((3*C*dk + C*C + C*dv) * sizeof(dt) + 4*dk, 256)
  *       nc     = ceil(T / C)
- *       segmax = max(1, floor(192 MiB / (B*H*rec)))
- *       nseg   = ceil(nc / segmax),  segch = ceil(nc / nseg)
+ *       runs   = floor(256 / (B*H))   (1 from 256 chains up)
+ *       segmax = max(1, floor(192 MiB / (B*H*rec))), less its remainder
+ *                mod runs when it exceeds runs
+ *       nseg   = ceil(nc / segmax),  segch = ceil(nc / nseg), and when
+ *                nseg > 1 rounded up to a multiple of runs (at most segmax)
  *     the workspace is B*H*segch*rec bytes, plus B*H*dk*dv*4 bytes of
  *     carried state when nseg > 1 (0 bytes when T = 0);
  *   - otherwise one fused kernel per (chain, value-column slab) keeps every

@@ -246,18 +246,24 @@ def test_workspace_query():
         if nc == 0:
             return 0
         segmax = max(1, (192 << 20) // (B * H * r))
+        runs = 256 // (B * H) if B * H < 256 else 1
+        if segmax > runs:
+            segmax -= segmax % runs
         nseg = -(-nc // segmax)
         segch = -(-nc // nseg)
+        if nseg > 1:
+            segch = min(segmax, -(-segch // runs) * runs)
         return B * H * segch * r + (B * H * dk * dv * 4 if nseg > 1 else 0)
     assert lib.kda_prefill_workspace_bytes(1, 4096, 16, 128, 128, 64, 1) == 16 * 64 * rec(64, 128, 128, 2)
     assert lib.kda_prefill_workspace_bytes(1, 4096, 16, 128, 64, 64, 1) == 16 * 64 * rec(64, 128, 64, 2)
     assert lib.kda_prefill_workspace_bytes(8, 8192, 32, 128, 128, 64, 1) == 0   # fused path
-    # one segment up to 192 MiB of records: 16 heads x 169 chunks of 74240 bytes
+    # one segment up to 192 MiB of records, in a multiple of the prep's 16
+    # runs per chain: 16 heads x 160 chunks of 74240 bytes
     assert rec(64, 128, 128, 2) == 74240
-    assert lib.kda_prefill_workspace_bytes(1, 169 * 64, 16, 128, 128, 64, 1) == 16 * 169 * 74240
-    # one chunk more: two segments of 85 chunks, plus the carried state
-    assert (lib.kda_prefill_workspace_bytes(1, 169 * 64 + 1, 16, 128, 128, 64, 1)
-            == 16 * 85 * 74240 + 16 * 128 * 128 * 4)
+    assert lib.kda_prefill_workspace_bytes(1, 160 * 64, 16, 128, 128, 64, 1) == 16 * 160 * 74240
+    # one chunk more: two segments of 96 and 65 chunks, plus the carried state
+    assert (lib.kda_prefill_workspace_bytes(1, 160 * 64 + 1, 16, 128, 128, 64, 1)
+            == 16 * 96 * 74240 + 16 * 128 * 128 * 4)
     for args in ((1, 20000, 16, 128, 128, 64, 2), (1, 1 << 20, 32, 128, 128, 64, 2),
                  (4, 100000, 8, 64, 32, 32, 2), (1, 5000, 3, 16, 16, 16, 4)):
         B, T, H, dk, dv, C, eb = args

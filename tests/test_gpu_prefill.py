@@ -220,15 +220,15 @@ def test_prep_chunk_runs_ragged():
 
 def test_split_segments():
     """A sequence whose records exceed one segment: 16 chains x 438 chunks
-    (T = 28000, the last chunk 32 rows) run as three segments of 146 chunks
-    with the state carried between them (inputs loaded non-temporally).  Two
-    chains match the oracle; resuming at a chunk boundary (tokens 6400..,
-    itself two segments with other boundaries) reproduces the full run bit
-    for bit."""
+    (T = 28000, the last chunk 32 rows) run as three segments of 160, 160 and
+    118 chunks with the state carried between them (inputs loaded
+    non-temporally).  Two chains match the oracle; resuming at a chunk
+    boundary (tokens 6400.., itself three segments with other boundaries)
+    reproduces the full run bit for bit."""
     spec = wl.PREFILL["prefill_h16_t4k"]
     T, H, cut = 28000, 16, 100 * 64
     ws = kda().prefill_workspace_bytes(1, T, H, 128, 128, 64)
-    assert ws == 16 * 146 * 74240 + 16 * 128 * 128 * 4            # three segments
+    assert ws == 16 * 160 * 74240 + 16 * 128 * 128 * 4            # three segments
     inp = wl.make_prefill_inputs(spec, T=T, H=H)
     inp["S0"] = 0.05 * torch.randn(1, H, 128, 128, generator=torch.Generator().manual_seed(7))
     g = to_dev(inp)

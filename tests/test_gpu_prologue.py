@@ -232,7 +232,7 @@ def test_split_segments():
     with the state carried between them; two chains match the oracle."""
     spec = wl.PREFILL["prefill_h16_t4k"]
     T, H = 28000, 16
-    assert kda().prefill_workspace_bytes(1, T, H, 128, 128, 64) == 16 * 146 * 74240 + 16 * 128 * 128 * 4
+    assert kda().prefill_workspace_bytes(1, T, H, 128, 128, 64) == 16 * 160 * 74240 + 16 * 128 * 128 * 4
     inp = wl.make_prefill_logit_inputs(spec, T=T, H=H)
     inp["S0"] = 0.05 * torch.randn(1, H, 128, 128, generator=torch.Generator().manual_seed(8))
     o, S = run(inp, 64, "l2")
