@@ -129,43 +129,48 @@ __device__ __forceinline__ float row16_sum(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// 2. Sub-chunk records.  One workgroup per (chain, 64-token chunk).
+// 2. Sub-chunk records.  One workgroup of two waves per (chain, sub-chunk):
+// 26 KiB of LDS and ~100 registers, so that six workgroups share a CU and
+// one's loads overlap another's arithmetic (one workgroup of eight waves per
+// 64-token chunk, one per CU by its LDS, took 88 us on H=16 T=4096).
 // ---------------------------------------------------------------------------
+constexpr int kPS = 1;   // sub-chunks per record workgroup (2 measured the same)
 template <int DK>
-__global__ void __launch_bounds__(kCbThreads)
+__global__ void __launch_bounds__(DK * kPS)
 kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__ gk,
                    const float* __restrict__ galpha, const float* __restrict__ gbeta,
                    char* __restrict__ grec, int T, int H) {
   using RB = BRec<DK>;
   constexpr int NM = DK / 16, LDK = DK + 8, LDT = kSB + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t sKF[kNSB][kSB * LDK];   // K.F
-  __shared__ __attribute__((aligned(16))) uint16_t sKI[kNSB][kSB * LDK];   // K / F (safe channels)
-  __shared__ __attribute__((aligned(16))) uint16_t sQF[kNSB][kSB * LDK];   // Q.F
-  __shared__ __attribute__((aligned(16))) uint16_t sKH[kNSB][kSB * LDK];   // K.H
-  __shared__ __attribute__((aligned(16))) uint16_t sBK[kNSB][DK * LDT];    // (beta K.F)^T
-  __shared__ __attribute__((aligned(16))) uint16_t sY[kNSB][kSB * LDT];    // Y
-  __shared__ float sA[kNSB][kSB * 17];
-  __shared__ float sBT[kNSB][DK];
-  __shared__ float sBe[kCB];
-  __shared__ int sFl[kNSB];
+  constexpr int NTH = DK * kPS;
+  __shared__ __attribute__((aligned(16))) uint16_t sKF[kPS][kSB * LDK];   // K.F
+  __shared__ __attribute__((aligned(16))) uint16_t sKI[kPS][kSB * LDK];   // K / F (safe channels)
+  __shared__ __attribute__((aligned(16))) uint16_t sQF[kPS][kSB * LDK];   // Q.F
+  __shared__ __attribute__((aligned(16))) uint16_t sKH[kPS][kSB * LDK];   // K.H
+  __shared__ __attribute__((aligned(16))) uint16_t sBK[kPS][DK * LDT];    // (beta K.F)^T
+  __shared__ __attribute__((aligned(16))) uint16_t sY[kPS][kSB * LDT];    // Y
+  __shared__ float sA[kPS][kSB * 17];
+  __shared__ float sBT[kPS][DK];
+  __shared__ float sBe[kPS * kSB];
+  __shared__ int sFl[kPS];
 
-  const int NC = (T + kCB - 1) / kCB, NS = (T + kSB - 1) / kSB;
-  const int chain = blockIdx.x / NC, cc = blockIdx.x % NC;
+  const int NS = (T + kSB - 1) / kSB, NP = (NS + kPS - 1) / kPS;
+  const int chain = blockIdx.x / NP, cp = blockIdx.x % NP;
   const int b = chain / H, h = chain % H;
-  const int t0 = cc * kCB;
+  const int t0 = cp * kPS * kSB;
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const size_t row0 = static_cast<size_t>(b) * T * H + h;
-  auto rec_of = [&](int J) { return grec + (static_cast<size_t>(chain) * NS + cc * kNSB + J) * RB::kBytes; };
+  auto rec_of = [&](int J) { return grec + (static_cast<size_t>(chain) * NS + cp * kPS + J) * RB::kBytes; };
   auto live = [&](int J) { return t0 + kSB * J < T; };
 
-  if (tid < kNSB) sFl[tid] = 0;
-  if (tid < kCB) sBe[tid] = (t0 + tid < T) ? gbeta[row0 + static_cast<size_t>(t0 + tid) * H] : 0.f;
+  if (tid < kPS) sFl[tid] = 0;
+  if (tid < kPS * kSB) sBe[tid] = (t0 + tid < T) ? gbeta[row0 + static_cast<size_t>(t0 + tid) * H] : 0.f;
   lds_barrier();
 
   // ---- gates and gated operands, item (channel c, sub-chunk J); rows past T
   // are identity steps (alpha 1, k = q = 0, beta 0)
-  for (int it = tid; it < DK * kNSB; it += kCbThreads) {
+  for (int it = tid; it < DK * kPS; it += NTH) {
     const int c = it % DK, J = it / DK;
     float a[kSB], kk[kSB], qq[kSB];
 #pragma unroll
@@ -274,7 +279,7 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
 
   // ---- Y = (I + Diag(beta) A)^-1 per sub-chunk by forward substitution:
   // wave J, lane j < 16 owns column j
-  if (wave < kNSB) {
+  if (wave < kPS) {
     const int J = wave;
     if (lane < kSB) {
       const int j = lane;
@@ -304,7 +309,7 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
 
   // ---- W = Y (beta K.F): tile (J, channel block R) has lane (g, i) holding
   // W[4g .. 4g+3][16R + i], the -W^T half of fragment R
-  for (int t = wave; t < kNSB * NM; t += kCbThreads / kWave) {
+  for (int t = wave; t < kPS * NM; t += NTH / kWave) {
     const int J = t / NM, R = t % NM;
     if (!live(J)) continue;
     const Lane ln = lane_now();
@@ -316,7 +321,7 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   // ---- K.E' fragments: lane (g, i) holds row i, channels 32kk + 4g .. +3
   // and 32kk + 16 + 4g .. +3
   constexpr int NK = DK / 32;
-  for (int x = tid; x < kNSB * NK * 64; x += kCbThreads) {
+  for (int x = tid; x < kPS * NK * 64; x += NTH) {
     const int J = x / (NK * 64), kk = (x / 64) % NK, l = x % 64;
     if (!live(J)) continue;
     const uint16_t* row = sKH[J] + (l % 16) * LDK + 32 * kk + 4 * (l / 16);
@@ -1084,8 +1089,9 @@ hipError_t launch_prefill_backward_chunked(const PrefillBwdArgs& a) {
     f.force_split = true;
     hipError_t e = launch_prefill(f);
     if (e != hipSuccess) return e;
-    const unsigned blocks = static_cast<unsigned>(chains * NC);
-    kda_cb_prep_kernel<128><<<blocks, kCbThreads, 0, stream>>>(
+    const unsigned pblocks =
+        static_cast<unsigned>(chains * (((a.T + kSB - 1) / kSB + kPS - 1) / kPS));
+    kda_cb_prep_kernel<128><<<pblocks, 128 * kPS, 0, stream>>>(
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), a.alpha, a.beta,
         recs, a.T, a.H);
     e = hipGetLastError();
