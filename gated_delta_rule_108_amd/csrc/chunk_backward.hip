@@ -441,14 +441,16 @@ kda_cb_scan_kernel(const char* __restrict__ grec, const uint16_t* __restrict__ g
     lds_barrier();
     const char* sb = slot(n);
     if (s == NS - 1 || (s % kNSB) == kNSB - 1) {
-      // the gradient at the end of chunk s / 4, for the gradient kernel
-      float* dst = gdSc + (static_cast<size_t>(chain) * NC + s / kNSB) * DK * DV + 16 * jt0 + ln.i;
+      // the gradient at the end of chunk s / 4, for the gradient kernel, in
+      // fragment order [chain][chunk][column tile][row block][lane][4]
+      float* dst = gdSc + ((static_cast<size_t>(chain) * NC + s / kNSB) * (DV / 16) + jt0) * DK * 16 +
+                   4 * lane;
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int m = 0; m < NM; ++m)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dst[(16 * m + 4 * ln.g + r) * DV + 16 * tt] = dS[tt][m][r];
+          *reinterpret_cast<float4*>(dst + (tt * NM + m) * kWave * 4) =
+              make_float4(dS[tt][m][0], dS[tt][m][1], dS[tt][m][2], dS[tt][m][3]);
     }
     auto frag32 = [&](int off, int m) {
       return *reinterpret_cast<const bf16x8*>(sb + off + (m * 64 + lane) * 16);
@@ -562,7 +564,6 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int jt = wave;
   const size_t row0 = static_cast<size_t>(b) * T * H + h;
-  const size_t sbase = (static_cast<size_t>(chain) * NC + cc) * DK * DV;
   auto rec_of = [&](int J) {
     return grec + (static_cast<size_t>(chain) * NS + cc * kNSB + J) * RB::kBytes;
   };
@@ -571,14 +572,14 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   if (tid < kCB) sBe[tid] = (t0 + tid < T) ? gbeta[trow(t0 + tid)] : 0.f;
 
   // state tile of this wave: rows 16m + 4g + r, column 16 jt + i
+  // (chunk states and state gradients in fragment order: [chain][chunk]
+  // [column tile][row block][lane][4], one 16-byte access per block)
+  const size_t fbase = ((static_cast<size_t>(chain) * NC + cc) * (DV / 16) + jt) * DK * 16 + 4 * lane;
   f32x4 Sw[NM];
-  {
-    const Lane ln = lane_now();
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        Sw[m][r] = gSc[sbase + (16 * m + 4 * ln.g + r) * DV + 16 * jt + ln.i];
+  for (int m = 0; m < NM; ++m) {
+    const float4 v = *reinterpret_cast<const float4*>(gSc + fbase + m * kWave * 4);
+    Sw[m][0] = v.x; Sw[m][1] = v.y; Sw[m][2] = v.z; Sw[m][3] = v.w;
   }
   // S of each sub-chunk (operand type) waits in the workspace between the
   // two passes (registers cannot hold them next to the gate phase), the
@@ -696,13 +697,10 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
 
   // ======== backward over the sub-chunks
   f32x4 dS[NM];
-  {
-    const Lane ln = lane_now();
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        dS[m][r] = gdSc[sbase + (16 * m + 4 * ln.g + r) * DV + 16 * jt + ln.i];
+  for (int m = 0; m < NM; ++m) {
+    const float4 v = *reinterpret_cast<const float4*>(gdSc + fbase + m * kWave * 4);
+    dS[m][0] = v.x; dS[m][1] = v.y; dS[m][2] = v.z; dS[m][3] = v.w;
   }
   // gate phase: key channel, quarter of the rows (wave-uniform: DK is a
   // multiple of the wave size)

@@ -52,7 +52,9 @@ struct PrefillArgs {
   // same value must size the workspace (prefill_workspace).
   size_t segment_budget = 0;
   // Split path: when set, the state every chunk of C tokens starts from,
-  // fp32 [B*H][ceil(T/C)][dk][dv] (the forward half of the chunked backward).
+  // fp32 in matrix-core fragment order [B*H][ceil(T/C)][dv/16][dk/16][64][4]
+  // (lane 16g + i holds rows 4g .. 4g+3 of a 16 x 16 block, column i), for
+  // the chunked backward.
   float* chunk_states = nullptr;
   // Take the split path whatever the chain count (chunk_states needs it).
   bool force_split = false;

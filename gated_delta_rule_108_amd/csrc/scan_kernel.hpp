@@ -173,16 +173,17 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
       const Lane ln = lane_now();
       const char* ob = buf(ch);
       if (gSc != nullptr) {
-        // the state each chunk starts from, fp32 [chain][chunk][DK][DV]
+        // the state each chunk starts from, fp32, in fragment order:
+        // [chain][chunk][column tile][row block][lane][4] (lane (g, i): rows
+        // 4g .. 4g+3 of the block, column i), one 16-byte store per block
         const int nct = (T + C - 1) / C;
-        float* dst = gSc + (static_cast<size_t>(chain) * nct + seg0 + ch) * DK * DV + 16 * jt;
+        float* dst = gSc + ((static_cast<size_t>(chain) * nct + seg0 + ch) * (DV / 16) + jt) * DK * 16;
 #pragma unroll
         for (int m = 0; m < CPW; ++m) {
           const int cb = R + NB * m;
-          if (cb < NCB) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(16 * cb + 4 * ln.g + r) * DV + ln.i] = S[m][r];
-          }
+          if (cb < NCB)
+            *reinterpret_cast<float4*>(dst + (cb * kWave + lane) * 4) =
+                make_float4(S[m][0], S[m][1], S[m][2], S[m][3]);
         }
       }
       // publish this wave's state rows as S^T (operand type)
