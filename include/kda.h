@@ -392,7 +392,7 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v,
  * 15 KiB record per 16 tokens of every sequence and head, and, per 64-token
  * chunk, the states at its four 16-token blocks and their writes (bf16:
  * 4 * dk * dv * 2 + 64 * dv * 2 bytes) that the gradient pass rebuilds
- * (about 421 MiB at B = 1, H = 16, T = 4096).  (size_t)-1 for
+ * (about 420 MiB at B = 1, H = 16, T = 4096).  (size_t)-1 for
  * sizes the call does not accept (dk or dv other than 128).
  */
 size_t kda_prefill_backward_chunked_workspace_bytes(int B, int T, int H, int dk, int dv);

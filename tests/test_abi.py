@@ -476,6 +476,77 @@ def test_prefill_backward_valid_arguments():
               dv=None, da=None, db=None, ws=None, wsb=0) in ok
 
 
+
+def test_prefill_backward_chunked_workspace_bytes():
+    """The forward's split-path records (C = 64, split path), the forward
+    output, the state and the state gradient every 64 tokens (fp32), one
+    15 KiB record per 16 tokens, and per 64 tokens the four 16-token states
+    and their writes (bf16)."""
+    L = _lib()
+    lib = L.load()
+
+    def expect(B, T, H):
+        chains, nc, ns = B * H, -(-T // 64), -(-T // 16)
+        fwd_rec = ((3 * 64 * 128 + 64 * 64 + 64 * 128) * 2 + 4 * 128 + 255) // 256 * 256
+        segmax = max(1, (192 << 20) // (chains * fwd_rec))
+        runs = 256 // chains if chains < 256 else 1
+        if segmax > runs:
+            segmax -= segmax % runs
+        nseg = -(-nc // segmax)
+        segch = -(-nc // nseg)
+        if nseg > 1:
+            segch = min(segmax, -(-segch // runs) * runs)
+        fwd = chains * segch * fwd_rec + (chains * 128 * 128 * 4 if nseg > 1 else 0)
+        o = (chains * T * 128 * 2 + 255) // 256 * 256
+        return (fwd + o + 2 * chains * nc * 128 * 128 * 4 + chains * ns * 15360
+                + chains * nc * 4 * 128 * 128 * 2 + chains * nc * 4 * 16 * 128 * 2)
+
+    for B, T, H in ((1, 4096, 16), (2, 100, 3), (8, 8192, 32), (1, 1, 1)):
+        assert lib.kda_prefill_backward_chunked_workspace_bytes(B, T, H, 128, 128) == expect(B, T, H)
+    assert lib.kda_prefill_backward_chunked_workspace_bytes(1, 4096, 16, 128, 128) >> 20 == 420
+    bad = ctypes.c_size_t(-1).value
+    assert lib.kda_prefill_backward_chunked_workspace_bytes(1, 64, 2, 64, 128) == bad   # dk
+    assert lib.kda_prefill_backward_chunked_workspace_bytes(1, 64, 2, 128, 64) == bad   # dv
+    assert lib.kda_prefill_backward_chunked_workspace_bytes(0, 64, 2, 128, 128) == bad
+
+
+def prefill_backward_chunked(lib, **kw):
+    kw.setdefault("wsb", lib.kda_prefill_backward_chunked_workspace_bytes(
+        kw.get("B", PB_B), kw.get("T", PB_T), kw.get("H", PB_H), PB_D, PB_D))
+    return prefill_backward(lib, fn="kda_prefill_backward_chunked", **kw)
+
+
+def test_prefill_backward_chunked_validation():
+    """The host checks of the token-walk backward, plus its own sizes: bf16 at
+    dk = dv = 128 only."""
+    L = _lib()
+    lib = L.load()
+    pb = lambda **kw: prefill_backward_chunked(lib, **kw)
+    ws_need = lib.kda_prefill_backward_chunked_workspace_bytes(PB_B, PB_T, PB_H, PB_D, PB_D)
+    assert pb(dS0=addr(7) + 64) == L.KDA_ERR_ALIAS               # partial overlap with dS_T
+    assert pb(dq=addr(9)) == L.KDA_ERR_ALIAS                     # two outputs together
+    assert pb(ws=addr(6)) == L.KDA_ERR_ALIAS                     # workspace over dO
+    assert pb(dO=None) == L.KDA_ERR_NULL and pb(db=None) == L.KDA_ERR_NULL
+    assert pb(da=addr(11) + 4) == L.KDA_ERR_ALIGN
+    assert pb(ws=None) == L.KDA_ERR_WORKSPACE and pb(wsb=ws_need - 1) == L.KDA_ERR_WORKSPACE
+    assert pb(T=-1) == L.KDA_ERR_SHAPE and pb(H=0) == L.KDA_ERR_SHAPE
+    assert pb(dt=0) == L.KDA_ERR_UNSUPPORTED                     # fp32 I/O: the token walk's
+    assert pb(dk_=64, dv_=64) == L.KDA_ERR_UNSUPPORTED
+    assert pb(dt=7) == L.KDA_ERR_UNSUPPORTED
+
+
+@host_only
+def test_prefill_backward_chunked_valid_arguments():
+    L = _lib()
+    lib = L.load()
+    ok = (L.KDA_OK, L.KDA_ERR_HIP, L.KDA_ERR_DEVICE)
+    pb = lambda **kw: may_launch(prefill_backward_chunked, lib=lib, **kw)
+    assert pb() in ok
+    assert pb(S0=None, dST=None, dS0=None) in ok                 # optional states
+    assert pb(dS0=addr(7)) in ok                                 # in place over dS_T
+    assert pb(T=0, q=None, k=None, v=None, alpha=None, beta=None, dO=None, dq=None, dk=None,
+              dv=None, da=None, db=None, ws=None, wsb=0) in ok
+
 PRO_ROWS, PRO_D = 64, 128
 
 
