@@ -98,6 +98,17 @@ def test_optional_states():
     run(spec(s0_std=0.0), B=1, T=70, H=2, with_dST=False)
 
 
+def test_initial_state_without_final_gradient():
+    """S0 given, dS_T absent: the state gradient starts at zero at the end."""
+    run(spec(), B=1, T=70, H=2, with_dST=False)
+
+
+def test_odd_chain_count_and_ragged_chunks():
+    """Nine chains (one state-gradient tile per workgroup, a grid that is no
+    multiple of the CU count) over 11 chunks, the last of 60 rows."""
+    run(spec(), B=3, T=700, H=3)
+
+
 def test_closed_gates_and_mixture():
     run(spec(), B=1, T=90, H=2, zero_gates=True)
     run(spec(alpha_kind="mixture"), B=1, T=128, H=2)
