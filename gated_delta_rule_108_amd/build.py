@@ -28,6 +28,16 @@ HIPFLAGS = [
 ]
 
 
+# Per-file extra flags.  The state-gradient scan of the chunked backward
+# otherwise keeps its matrix-core results in accumulation registers and copies
+# each out before use (40 copies per 16-token step of a wave that is bound by
+# instruction issue); this backend option makes the products write ordinary
+# vector registers.
+EXTRA = {
+    "chunk_backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
@@ -58,7 +68,8 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
         for s in srcs:
             o = os.path.join(tmp, os.path.basename(s) + ".o")
             objs.append(o)
-            work.append(([hipcc, *HIPFLAGS, "-c", s, "-o", o], s))
+            extra = EXTRA.get(os.path.basename(s), [])
+            work.append(([hipcc, *HIPFLAGS, *extra, "-c", s, "-o", o], s))
         with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
             for s in ex.map(_compile, work):
                 if verbose:
