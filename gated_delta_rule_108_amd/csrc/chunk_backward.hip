@@ -332,16 +332,22 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
 
 // ---------------------------------------------------------------------------
 // 3. The state gradient, backwards over the sub-chunks.  One workgroup per
-// (chain, NT 16-column tiles): a state wave holds the tiles in registers, lane
-// (g, i) holding rows 16m + 4g + r, column i of it (the product's output
-// layout, which is also the layout of the next product's B operand),
+// (chain, NT 16-column tiles): two state waves hold the tiles in registers,
+// state wave h the row blocks m of its half of the key channels, lane (g, i)
+// holding rows 16m + 4g + r, column i (the product's output layout, which is
+// also the layout of the next product's B operand),
 //   dS <- Diag(E_last) dS + (Q.E)^T dO - W^T (P^T dO + (K.E') dS),
+// each forming the part of P^T dO + (K.E') dS that its rows contribute and
+// taking the other's through LDS (a step is bound by instruction issue, so
+// halving each wave's products and conversions beats the extra exchange);
 // and two loader waves stream each sub-chunk's record and dO tile into a ring
 // of LDS slots with direct global-to-LDS loads, kAhead sub-chunks ahead (the
 // walk is a chain of short matrix products: without the ring every step
 // waited for its own loads; each loader issues half of every slot so that
 // kAhead slots fit the 6-bit count of loads a wave can wait on).  One
-// barrier per sub-chunk.
+// barrier per sub-chunk: the exchange of u, after which the next slot has
+// landed (the loaders wait for it before they arrive) and the state waves
+// read it together with u, so that its latency hides behind the update.
 // ---------------------------------------------------------------------------
 template <int DK, int NT>
 struct ScanRing {
@@ -360,14 +366,15 @@ struct ScanRing {
 };
 
 template <int DK, int NT>
-__global__ void __launch_bounds__(3 * kWave)
+__global__ void __launch_bounds__(4 * kWave)
 kda_cb_scan_kernel(const char* __restrict__ grec, const uint16_t* __restrict__ gdO,
                    const float* __restrict__ gdST, float* __restrict__ gdSc, float* gdS0, int T,
                    int H, int DV) {
   using RB = BRec<DK>;
   using RG = ScanRing<DK, NT>;
-  constexpr int NM = DK / 16;
+  constexpr int NM = DK / 16, NH = NM / 2;          // row blocks per state wave
   __shared__ __attribute__((aligned(16))) char ring[RG::kNBuf * RG::kBuf];
+  __shared__ __attribute__((aligned(16))) float xu[2][2][NT][kWave * 4];   // [step parity][part] of u
   const int NJV = DV / (16 * NT);                    // workgroups per chain
   const int chain = blockIdx.x / NJV, jt0 = NT * (blockIdx.x % NJV);
   const int b = chain / H, h = chain % H;
@@ -377,11 +384,11 @@ kda_cb_scan_kernel(const char* __restrict__ grec, const uint16_t* __restrict__ g
   const size_t row0 = static_cast<size_t>(b) * T * H + h;
   auto slot = [&](int n) { return ring + (n % RG::kNBuf) * RG::kBuf; };
 
-  if (wv > 0) {
+  if (wv >= 2) {
     // ---- loaders: order n (= sub-chunk NS - 1 - n) into slot n % kNBuf;
     // loader 1 the first kSplit KiB of the record, loader 2 the rest of it
     // and the dO tiles
-    const bool first = wv == 1;
+    const bool first = wv == 2;
     auto fill = [&](int n) {
       const int s = NS - 1 - n;
       char* dst = slot(n);
@@ -414,32 +421,62 @@ kda_cb_scan_kernel(const char* __restrict__ grec, const uint16_t* __restrict__ g
     if (NS > 0) {
 #pragma unroll
       for (int i = 0; i < RG::kAhead; ++i) fill(min(i, NS - 1));
-      wait_oldest();   // order 0 landed
+      wait_oldest();          // order 0 landed
+      barrier_keep_fills();   // slot 0 is ready
     }
     for (int n = 0; n < NS; ++n) {
-      barrier_keep_fills();   // slot n is ready; slot n + kAhead (used by n - 1) is free
+      // into the slot of order n - 1, whose reads ended before the last barrier
       fill(min(n + RG::kAhead, NS - 1));
       wait_oldest();          // order n + 1 landed
+      barrier_keep_fills();   // the exchange of step n; slot n + 1 is ready
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
     return;
   }
 
   const Lane ln = lane_now();
-  f32x4 dS[NT][NM];
+  const int hh = wv;                                 // this state wave's half
+  f32x4 dS[NT][NH];                                  // row blocks m = NH hh + mm
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+    for (int mm = 0; mm < NH; ++mm)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        dS[tt][m][r] = gdST ? gdST[(static_cast<size_t>(chain) * DK + 16 * m + 4 * ln.g + r) * DV +
-                                   16 * (jt0 + tt) + ln.i]
-                            : 0.f;
-  for (int n = 0; n < NS; ++n) {
+        dS[tt][mm][r] = gdST ? gdST[(static_cast<size_t>(chain) * DK + 16 * (NH * hh + mm) + 4 * ln.g + r) * DV +
+                                    16 * (jt0 + tt) + ln.i]
+                             : 0.f;
+  // a slot's operands, in registers: P^T (the first wave's; the other's is
+  // zeroed at use), the dO tiles, this wave's K.E' fragments, rows of
+  // [(Q.E)^T | -W^T] and decays
+  struct Ops {
+    uint2 pw;
+    uint32_t d[NT][4];                               // dO halves, packed at use
+    bf16x8 kf[NH / 2], qw[NH];
+    float4 gc[NH];
+  };
+  auto read_slot = [&](const char* sb, Ops& o) {
+    o.pw = *reinterpret_cast<const uint2*>(sb + RB::oP + lane * 8);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const uint16_t* dt = reinterpret_cast<const uint16_t*>(sb + RG::kRec) + 256 * tt;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o.d[tt][r] = dt[(4 * ln.g + r) * 16 + ln.i];
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < NH / 2; ++k2)
+      o.kf[k2] = *reinterpret_cast<const bf16x8*>(sb + RB::oK + ((NH / 2 * hh + k2) * 64 + lane) * 16);
+#pragma unroll
+    for (int mm = 0; mm < NH; ++mm) {
+      const int m = NH * hh + mm;
+      o.qw[mm] = *reinterpret_cast<const bf16x8*>(sb + RB::oQW + (m * 64 + lane) * 16);
+      o.gc[mm] = *reinterpret_cast<const float4*>(sb + RB::oG + 4 * (16 * m + 4 * ln.g));
+    }
+  };
+  const uint32_t pmask = hh == 0 ? ~0u : 0u;
+  // step n with the operands of slot n in cur; reads slot n + 1 into nxt
+  auto step = [&](int n, const Ops& cur, Ops& nxt) {
     const int s = NS - 1 - n;
-    lds_barrier();
-    const char* sb = slot(n);
     if (s == NS - 1 || (s % kNSB) == kNSB - 1) {
       // the gradient at the end of chunk s / 4, for the gradient kernel, in
       // fragment order [chain][chunk][column tile][row block][lane][4]
@@ -448,65 +485,99 @@ kda_cb_scan_kernel(const char* __restrict__ grec, const uint16_t* __restrict__ g
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
-          *reinterpret_cast<float4*>(dst + (tt * NM + m) * kWave * 4) =
-              make_float4(dS[tt][m][0], dS[tt][m][1], dS[tt][m][2], dS[tt][m][3]);
+        for (int mm = 0; mm < NH; ++mm)
+          *reinterpret_cast<float4*>(dst + (tt * NM + NH * hh + mm) * kWave * 4) =
+              make_float4(dS[tt][mm][0], dS[tt][mm][1], dS[tt][mm][2], dS[tt][mm][3]);
     }
-    auto frag32 = [&](int off, int m) {
-      return *reinterpret_cast<const bf16x8*>(sb + off + (m * 64 + lane) * 16);
-    };
-    // per tile: u = P^T dO + (K.E') dS, then
-    // dS <- Diag(E_last) dS + [(Q.E)^T | -W^T] [dO ; u]; each fragment read
-    // from LDS serves both tiles
-    const bf16x4 pfr = *reinterpret_cast<const bf16x4*>(sb + RB::oP + lane * 8);
+    // this wave's part of u = P^T dO + (K.E') dS: its row blocks' share
+    const bf16x4 pfr = __builtin_bit_cast(bf16x4, make_uint2(cur.pw.x & pmask, cur.pw.y & pmask));
     bf16x4 dob[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+      dob[tt] = __builtin_bit_cast(bf16x4, make_uint2(cur.d[tt][0] | (cur.d[tt][1] << 16),
+                                                      cur.d[tt][2] | (cur.d[tt][3] << 16)));
     f32x4 t1[NT][2];
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
-      const uint16_t* dt = reinterpret_cast<const uint16_t*>(sb + RG::kRec) + 256 * tt;
-      dob[tt] = bits4(dt[(4 * ln.g) * 16 + ln.i], dt[(4 * ln.g + 1) * 16 + ln.i],
-                      dt[(4 * ln.g + 2) * 16 + ln.i], dt[(4 * ln.g + 3) * 16 + ln.i]);
       t1[tt][0] = mma16(pfr, dob[tt], zero4());
       t1[tt][1] = zero4();
     }
 #pragma unroll
-    for (int kk = 0; kk < NM / 2; ++kk) {
-      const bf16x8 kf = frag32(RB::oK, kk);
+    for (int k2 = 0; k2 < NH / 2; ++k2)
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt)
-        t1[tt][kk % 2] = mma32(kf, cat8(quad4(dS[tt][2 * kk]), quad4(dS[tt][2 * kk + 1])), t1[tt][kk % 2]);
-    }
-    bf16x8 du8[NT];
+        t1[tt][k2 % 2] = mma32(cur.kf[k2], cat8(quad4(dS[tt][2 * k2]), quad4(dS[tt][2 * k2 + 1])),
+                               t1[tt][k2 % 2]);
+    float (*xs)[NT][kWave * 4] = xu[n & 1];
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      f32x4 u;
+    for (int tt = 0; tt < NT; ++tt)
+      *reinterpret_cast<float4*>(&xs[hh][tt][4 * lane]) =
+          make_float4(t1[tt][0][0] + t1[tt][1][0], t1[tt][0][1] + t1[tt][1][1],
+                      t1[tt][0][2] + t1[tt][1][2], t1[tt][0][3] + t1[tt][1][3]);
+    // the part of the update that u does not enter:
+    // Diag(E_last) dS + (Q.E)^T dO, the dO half of each 16x16x32 row
 #pragma unroll
-      for (int r = 0; r < 4; ++r) u[r] = t1[tt][0][r] + t1[tt][1][r];
-      du8[tt] = cat8(dob[tt], quad4(u));
-    }
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const bf16x8 qw = frag32(RB::oQW, m);
-      const float4 gc = *reinterpret_cast<const float4*>(sb + RB::oG + 4 * (16 * m + 4 * ln.g));
+    for (int mm = 0; mm < NH; ++mm) {
+      const uint4 q = __builtin_bit_cast(uint4, cur.qw[mm]);
+      const bf16x4 qlo = __builtin_bit_cast(bf16x4, make_uint2(q.x, q.y));
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
-        const f32x4 aq = mma32(qw, du8[tt], zero4());
-        dS[tt][m][0] = gc.x * dS[tt][m][0] + aq[0];
-        dS[tt][m][1] = gc.y * dS[tt][m][1] + aq[1];
-        dS[tt][m][2] = gc.z * dS[tt][m][2] + aq[2];
-        dS[tt][m][3] = gc.w * dS[tt][m][3] + aq[3];
+        f32x4 e;
+        e[0] = cur.gc[mm].x * dS[tt][mm][0];
+        e[1] = cur.gc[mm].y * dS[tt][mm][1];
+        e[2] = cur.gc[mm].z * dS[tt][mm][2];
+        e[3] = cur.gc[mm].w * dS[tt][mm][3];
+        dS[tt][mm] = mma16(qlo, dob[tt], e);
       }
     }
+    bf16x4 qhi[NH];
+#pragma unroll
+    for (int mm = 0; mm < NH; ++mm) {
+      const uint4 q = __builtin_bit_cast(uint4, cur.qw[mm]);
+      qhi[mm] = __builtin_bit_cast(bf16x4, make_uint2(q.z, q.w));
+    }
+    lds_barrier();   // both parts of u written; slot n + 1 is ready; slot n is read
+    // u (the two parts summed in the same order in both waves) and the next
+    // slot's operands, all issued before the first use
+    float4 ua[NT], uc[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      ua[tt] = *reinterpret_cast<const float4*>(&xs[0][tt][4 * lane]);
+      uc[tt] = *reinterpret_cast<const float4*>(&xs[1][tt][4 * lane]);
+    }
+    read_slot(slot(min(n + 1, NS - 1)), nxt);
+    asm volatile("" ::: "memory");       // the reads stay here, not sunk to their uses
+    __builtin_amdgcn_sched_barrier(0);   // nor moved by the scheduler
+    // dS <- (that) - W^T u
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const bf16x4 uq = bf16_quad(ua[tt].x + uc[tt].x, ua[tt].y + uc[tt].y, ua[tt].z + uc[tt].z,
+                                  ua[tt].w + uc[tt].w);
+#pragma unroll
+      for (int mm = 0; mm < NH; ++mm) dS[tt][mm] = mma16(qhi[mm], uq, dS[tt][mm]);
+    }
+  };
+  Ops oa, ob;
+  if (NS > 0) {
+    lds_barrier();   // slot 0 is ready
+    read_slot(slot(0), oa);
   }
+  // two steps per pass, the operand sets alternating (no copies between steps)
+  int n = 0;
+  for (; n + 1 < NS; n += 2) {
+    step(n, oa, ob);
+    step(n + 1, ob, oa);
+  }
+  if (n < NS) step(n, oa, ob);
   if (gdS0) {
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
+      for (int mm = 0; mm < NH; ++mm)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          gdS0[(static_cast<size_t>(chain) * DK + 16 * m + 4 * ln.g + r) * DV + 16 * (jt0 + tt) +
-               ln.i] = dS[tt][m][r];
+          gdS0[(static_cast<size_t>(chain) * DK + 16 * (NH * hh + mm) + 4 * ln.g + r) * DV +
+               16 * (jt0 + tt) + ln.i] = dS[tt][mm][r];
   }
 }
 
@@ -1099,10 +1170,10 @@ hipError_t launch_prefill_backward_chunked(const PrefillBwdArgs& a) {
   // the chip (a state wave is issue-bound: two tiles share its fragment reads
   // but lengthen its step)
   if (chains * (a.dv / 16) >= 256)
-    kda_cb_scan_kernel<128, 2><<<static_cast<unsigned>(chains * (a.dv / 32)), 3 * kWave, 0, stream>>>(
+    kda_cb_scan_kernel<128, 2><<<static_cast<unsigned>(chains * (a.dv / 32)), 4 * kWave, 0, stream>>>(
         recs, static_cast<const uint16_t*>(a.dO), a.dS_T, dSc, a.g_S0, a.T, a.H, a.dv);
   else
-    kda_cb_scan_kernel<128, 1><<<static_cast<unsigned>(chains * (a.dv / 16)), 3 * kWave, 0, stream>>>(
+    kda_cb_scan_kernel<128, 1><<<static_cast<unsigned>(chains * (a.dv / 16)), 4 * kWave, 0, stream>>>(
         recs, static_cast<const uint16_t*>(a.dO), a.dS_T, dSc, a.g_S0, a.T, a.H, a.dv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.T == 0) return e;
