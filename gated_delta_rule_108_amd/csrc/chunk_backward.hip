@@ -113,6 +113,12 @@ __device__ __forceinline__ bf16x4 bits4(uint16_t a, uint16_t b, uint16_t c, uint
   return __builtin_bit_cast(bf16x4, make_uint2(a | (static_cast<uint32_t>(b) << 16),
                                                c | (static_cast<uint32_t>(d) << 16)));
 }
+// Element x of a bf16x4, its bits.
+__device__ __forceinline__ uint16_t half16(bf16x4 v, int x) {
+  const uint2 u = __builtin_bit_cast(uint2, v);
+  const uint32_t w = x < 2 ? u.x : u.y;
+  return static_cast<uint16_t>((x & 1) ? (w >> 16) : w);
+}
 __device__ __forceinline__ float unbf(bf16x4 v, int x) {
   const uint2 u = __builtin_bit_cast(uint2, v);
   const uint32_t w = x < 2 ? u.x : u.y;
@@ -621,7 +627,7 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   __shared__ __attribute__((aligned(16))) float sdPT[kSB * LDP];
   __shared__ __attribute__((aligned(16))) float sdAT[kSB * LDP];
   __shared__ float sPC[DK];
-  __shared__ float sFin[kCbThreads / kWave][DK];
+  __shared__ float sFin[DK];                                          // sum_j dS[c][j] S[c][j]
   __shared__ float sDb1[kCbThreads / kWave][kSB];
   __shared__ float sDb2[kSB];
   __shared__ float sBe[kCB];
@@ -876,15 +882,15 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * m + 4 * ln.g + r;
-          sS[row * LDV + 16 * jt + ln.i] = f32_to_bf16(unbf(Sj[m], r));
-          sdS[row * LDV + 16 * jt + ln.i] = f32_to_bf16(unbf(dsb, r));
+          sS[row * LDV + 16 * jt + ln.i] = half16(Sj[m], r);
+          sdS[row * LDV + 16 * jt + ln.i] = half16(dsb, r);
         }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = tb + 4 * ln.g + r;
         sdO[(4 * ln.g + r) * LDV + 16 * jt + ln.i] = t < T ? dov[r] : 0;
-        sU[(4 * ln.g + r) * LDV + 16 * jt + ln.i] = f32_to_bf16(unbf(uj, r));
+        sU[(4 * ln.g + r) * LDV + 16 * jt + ln.i] = half16(uj, r);
       }
     }
     lds_barrier();
@@ -919,27 +925,21 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
         if (ln.i == 0) sDb1[wave][row] = db;
         sdZ[row * LDV + 16 * jt + ln.i] = f32_to_bf16(dZ[r]);
       }
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float f = row16_sum(dS[m][r] * unbf(Sj[m], r));
-          if (ln.i == 0) sFin[wave][16 * m + 4 * ln.g + r] = f;
-        }
     }
     lds_barrier();
     // ---- contractions over the value columns: dO S^T, dZ S^T, U dS^T (tile
     // = channel block `wave`), dP and dA (waves 0 and 1)
     {
       const Lane ln = lane_now();
-      f32x4 os = zero4(), zs = zero4(), us = zero4();
+      f32x4 os = zero4(), zs = zero4(), us = zero4(), fd = zero4();
 #pragma unroll
       for (int k0 = 0; k0 < DV; k0 += 32) {
         const bf16x8 sb = ld8(sS + (16 * wave + ln.i) * LDV + k0 + 8 * ln.g);
+        const bf16x8 db = ld8(sdS + (16 * wave + ln.i) * LDV + k0 + 8 * ln.g);
         os = mma32(ld8(sdO + ln.i * LDV + k0 + 8 * ln.g), sb, os);
         zs = mma32(ld8(sdZ + ln.i * LDV + k0 + 8 * ln.g), sb, zs);
-        us = mma32(ld8(sU + ln.i * LDV + k0 + 8 * ln.g),
-                   ld8(sdS + (16 * wave + ln.i) * LDV + k0 + 8 * ln.g), us);
+        us = mma32(ld8(sU + ln.i * LDV + k0 + 8 * ln.g), db, us);
+        fd = mma32(db, sb, fd);   // dS S^T over the block's channels
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -947,6 +947,7 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
         sOS[row * LDF + 16 * wave + ln.i] = os[r];
         sZS[row * LDF + 16 * wave + ln.i] = zs[r];
         sUS[row * LDF + 16 * wave + ln.i] = us[r];
+        if (row == ln.i) sFin[16 * wave + ln.i] = fd[r];   // its diagonal
       }
       if (wave < 2) {
         f32x4 pp = zero4();
@@ -986,51 +987,54 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
         qq[r] = bf16_to_f32(sQr[r * LDK + c]);
       }
       if (part < 2) {
-        // dalpha_t with alpha_t's own factor left out, t ascending; the pair
-        // sums advance with t:  sp_r(t) = sum_{i<t} dP_ri k_i Gam(t-1, i),
-        //   sp_r(t+1) = alpha_t sp_r(t) + dP_rt k_t   (sa_r the same with dA)
-        float fin = 0.f;
+        // dalpha_t with alpha_t's own factor left out, t ascending:
+        //   dalpha_t = F_{t-1} R_t + H_t colp_t + F_{t-1} H_t fin + pair_t,
+        // R_t = sum_{r>=t} rho_r Gam(r, t), H_t = Gam(15, t) (backward
+        // recurrences), colp_t = sum_{i<t} k_i (U dS^T)_i Gam(t-1, i), and
+        //   pair_t = sum_{r>=t} Gam(r, t) v_r(t),
+        //   v_r(t) = sum_{i<t} k_i (q_r dP_ri + k_r dA_ri) Gam(t-1, i),
+        // v advanced with t (v_r(t+1) = alpha_t v_r(t) + k_t (q_r dP_rt + k_r dA_rt))
+        // and pair_t summed by Horner's rule from r = 15 down
+        const float fin = sFin[c];
+        float R[kSB], Hh[kSB], v[kSB];
+        {
+          float rn = 0.f, hn = 1.f;
 #pragma unroll
-        for (int w = 0; w < kCbThreads / kWave; ++w) fin += sFin[w][c];
-        float rho[kSB], sp[kSB], sa[kSB];
-#pragma unroll
-        for (int r = 0; r < kSB; ++r) {
-          rho[r] = qq[r] * sOS[r * LDF + c] - sBe[kSB * J + r] * kq[r] * sZS[r * LDF + c];
-          sp[r] = 0.f;
-          sa[r] = 0.f;
+          for (int r = kSB - 1; r >= 0; --r) {
+            const float rho = qq[r] * sOS[r * LDF + c] - sBe[kSB * J + r] * kq[r] * sZS[r * LDF + c];
+            rn = r == kSB - 1 ? rho : fmaf(a[r + 1], rn, rho);
+            if (r < kSB - 1) hn *= a[r + 1];
+            R[r] = rn;
+            Hh[r] = hn;
+            v[r] = 0.f;
+          }
         }
-        // quarter 0: t = 0..7; quarter 1: t = 8..15 (its recurrence starts at 0)
+        // quarter 0: t = 0..7; quarter 1: t = 8..15, which needs v only for
+        // rows r >= 8 (its recurrence still starts at t = 0)
         auto dalpha = [&](auto lo_c) {
           constexpr int tlo = decltype(lo_c)::value, thi = tlo + 8;
-          float Fm = 1.f, colp = 0.f;     // F_{t-1}; sum_{i<t} sig_i Gam(t-1, i)
+          float Fm = 1.f, colp = 0.f;     // F_{t-1}; colp_t
           static_for<0, thi>([&](auto t_c) {
             constexpr int t = decltype(t_c)::value;
             if constexpr (t >= tlo) {
-              float rowp = 0.f, pair = 0.f, g = 1.f;
+              float pr = v[kSB - 1];
 #pragma unroll
-              for (int r = t; r < kSB; ++r) {
-                if (r > t) g *= a[r];
-                rowp += rho[r] * g;
-                pair += (qq[r] * sp[r] + kq[r] * sa[r]) * g;
-              }
-              const float Ht = g;              // Gam(15, t) = H_t
+              for (int r = kSB - 2; r >= t; --r) pr = fmaf(a[r + 1], pr, v[r]);
               const int tt = tb + t;
-              if (tt < T) gda[trow(tt) * DK + c] = Fm * rowp + Ht * colp + Fm * Ht * fin + pair;
+              if (tt < T) gda[trow(tt) * DK + c] = Fm * R[t] + Hh[t] * colp + Fm * Hh[t] * fin + pr;
             }
             if constexpr (t + 1 < thi) {
-              // column t of dP and dA (rows r > t matter from here on)
+              // column t of dP and dA, rows r > t (and r >= tlo)
+              constexpr int rlo = (t + 1 > tlo ? t + 1 : tlo);
 #pragma unroll
-              for (int q4 = (t + 1) / 4; q4 < kSB / 4; ++q4) {
+              for (int q4 = rlo / 4; q4 < kSB / 4; ++q4) {
                 const float4 p4 = *reinterpret_cast<const float4*>(sdPT + t * LDP + 4 * q4);
                 const float4 a4 = *reinterpret_cast<const float4*>(sdAT + t * LDP + 4 * q4);
                 const float pv[4] = {p4.x, p4.y, p4.z, p4.w}, av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                   const int r = 4 * q4 + e;
-                  if (r > t) {
-                    sp[r] = a[t] * sp[r] + pv[e] * kq[t];
-                    sa[r] = a[t] * sa[r] + av[e] * kq[t];
-                  }
+                  if (r >= rlo) v[r] = fmaf(a[t], v[r], kq[t] * fmaf(qq[r], pv[e], kq[r] * av[e]));
                 }
               }
               colp = a[t] * colp + kq[t] * sUS[t * LDF + c];
@@ -1052,40 +1056,43 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
 #pragma unroll
         for (int x = 0; x < kSB; ++x) {
           if (x < xlo || x >= xlo + 8) continue;
-          // row x and column x of dP, dA
+          // row x and column x of dP, dA (an offset the compiler cannot see
+          // through keeps each row's loads next to their use; its low bits
+          // are clear, so the loads stay 16 bytes wide)
           int z = 0;
           asm volatile("" : "+v"(z));
-          // G1, G2 over i <= x with Gam(x, i), from row x of dP and dA
-          float g1 = 0.f, g2 = 0.f, g = 1.f;
+          z &= ~3;
+          // G1, G2 over i <= x with Gam(x, i), from row x of dP and dA, by
+          // Horner's rule from i = 0 up
+          float g1 = 0.f, g2 = 0.f;
 #pragma unroll
-          for (int q4 = x / 4; q4 >= 0; --q4) {
+          for (int q4 = 0; q4 <= x / 4; ++q4) {
             const float4 p4 = *reinterpret_cast<const float4*>(sdP + z + x * LDP + 4 * q4);
             const float4 a4 = *reinterpret_cast<const float4*>(sdA + z + x * LDP + 4 * q4);
             const float pv[4] = {p4.x, p4.y, p4.z, p4.w}, av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
-            for (int e = 3; e >= 0; --e) {
+            for (int e = 0; e < 4; ++e) {
               const int i = 4 * q4 + e;
               if (i <= x) {
-                if (i < x) g *= a[i + 1];
-                g1 += pv[e] * kq[i] * g;
-                g2 += av[e] * kq[i] * g;
+                g1 = i == 0 ? pv[e] * kq[i] : fmaf(a[i], g1, pv[e] * kq[i]);
+                g2 = i == 0 ? av[e] * kq[i] : fmaf(a[i], g2, av[e] * kq[i]);
               }
             }
           }
-          // G3 over r >= x with Gam(r, x), from column x
+          // G3 over r >= x with Gam(r, x), from column x, by Horner's rule
+          // from r = 15 down
           float g3 = 0.f;
-          g = 1.f;
 #pragma unroll
-          for (int q4 = x / 4; q4 < kSB / 4; ++q4) {
+          for (int q4 = kSB / 4 - 1; q4 >= x / 4; --q4) {
             const float4 p4 = *reinterpret_cast<const float4*>(sdPT + z + x * LDP + 4 * q4);
             const float4 a4 = *reinterpret_cast<const float4*>(sdAT + z + x * LDP + 4 * q4);
             const float pv[4] = {p4.x, p4.y, p4.z, p4.w}, av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int e = 3; e >= 0; --e) {
               const int r = 4 * q4 + e;
               if (r >= x) {
-                if (r > x) g *= a[r];
-                g3 += (pv[e] * qq[r] + av[e] * kq[r]) * g;
+                const float y = fmaf(pv[e], qq[r], av[e] * kq[r]);
+                g3 = r == kSB - 1 ? y : fmaf(a[r + 1], g3, y);
               }
             }
           }
