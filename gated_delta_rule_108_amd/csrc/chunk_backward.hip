@@ -627,6 +627,11 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   __shared__ __attribute__((aligned(16))) float sdPT[kSB * LDP];
   __shared__ __attribute__((aligned(16))) float sdAT[kSB * LDP];
   __shared__ float sPC[DK];
+  // the record's fragments and decay for the backward pass, [(Q.E)^T | -W^T],
+  // K.E', P^T, decay: loaded once per sub-chunk, read by every wave
+  constexpr int kRecB = RB::oY - RB::oQW;
+  static_assert(RB::oQW == 0 && kRecB % 1024 == 0, "record prefix in 1 KiB pieces");
+  __shared__ __attribute__((aligned(16))) char sRec[kRecB];
   __shared__ float sFin[DK];                                          // sum_j dS[c][j] S[c][j]
   __shared__ float sDb1[kCbThreads / kWave][kSB];
   __shared__ float sDb2[kSB];
@@ -703,6 +708,35 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   };
   FwdIn fin_cur;
   fetch_fwd(0, fin_cur);
+  // The backward pass's first loads (the state gradient at the chunk's end
+  // and the last sub-chunk's rows) are issued here, next to the forward
+  // pass's first ones, so that both wait for memory once.
+  f32x4 dS[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const float4 v = *reinterpret_cast<const float4*>(gdSc + fbase + m * kWave * 4);
+    dS[m][0] = v.x; dS[m][1] = v.y; dS[m][2] = v.z; dS[m][3] = v.w;
+  }
+  // gate phase: key channel, quarter of the rows (wave-uniform: DK is a
+  // multiple of the wave size)
+  const int c = tid % DK, part = __builtin_amdgcn_readfirstlane(tid / DK);
+  // raw alpha, k, q of a sub-chunk, loaded one sub-chunk ahead: thread
+  // (row rr, channel quad cq) holds channels 4cq .. 4cq+3 of row rr, so a row
+  // piece is one 16-byte and two 8-byte loads
+  static_assert(kSB * DK / 4 == kCbThreads, "one channel quad of one row per thread");
+  const int rr = tid / (DK / 4), cq = 4 * (tid % (DK / 4));
+  float4 na;
+  uint2 nk, nq;
+  auto fetch_rows = [&](int J) {
+    // raw loads from a clamped row; a row past T is fixed up where it is
+    // used (a select here would wait for the load)
+    const int t = t0 + kSB * J + rr;
+    const size_t e = trow(min(t, T - 1)) * DK + cq;
+    na = *reinterpret_cast<const float4*>(galpha + e);
+    nk = *reinterpret_cast<const uint2*>(gk + e);
+    nq = *reinterpret_cast<const uint2*>(gq + e);
+  };
+  fetch_rows(ns - 1);
 #pragma nounroll
   for (int J = 0; J < ns; ++J) {
     const FwdIn cur = fin_cur;
@@ -773,32 +807,37 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   }
 
   // ======== backward over the sub-chunks
-  f32x4 dS[NM];
+  // The gate phase leaves its results in LDS (the sS area, unused from the
+  // contractions to the next column write): slot x of thread tid at
+  // res[x * kCbThreads + tid], dalpha of rows 8 part + x (quarters 0, 1),
+  // dq and dk of rows 8 (part - 2) + x in slots 2x, 2x + 1 (quarters 2, 3),
+  // dbeta of row tid in slot 8 (threads below 16).  They go to memory at the
+  // top of the next sub-chunk, after its prefetched rows have been waited
+  // for and before the next prefetch is issued: a wait for a load covers
+  // every store issued before it, and these stores are then a whole
+  // sub-chunk old.
+  float* const res = reinterpret_cast<float*>(sS) + tid;
+  static_assert(16 * kCbThreads * sizeof(float) <= sizeof(sS), "result slots");
+  auto flush = [&](int Jp) {
+    const int tbp = t0 + kSB * Jp;
+    if (part < 2) {
 #pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    const float4 v = *reinterpret_cast<const float4*>(gdSc + fbase + m * kWave * 4);
-    dS[m][0] = v.x; dS[m][1] = v.y; dS[m][2] = v.z; dS[m][3] = v.w;
-  }
-  // gate phase: key channel, quarter of the rows (wave-uniform: DK is a
-  // multiple of the wave size)
-  const int c = tid % DK, part = __builtin_amdgcn_readfirstlane(tid / DK);
-  // raw alpha, k, q of a sub-chunk, loaded one sub-chunk ahead: thread
-  // (row rr, channel quad cq) holds channels 4cq .. 4cq+3 of row rr, so a row
-  // piece is one 16-byte and two 8-byte loads
-  static_assert(kSB * DK / 4 == kCbThreads, "one channel quad of one row per thread");
-  const int rr = tid / (DK / 4), cq = 4 * (tid % (DK / 4));
-  float4 na;
-  uint2 nk, nq;
-  auto fetch_rows = [&](int J) {
-    // raw loads from a clamped row; a row past T is fixed up where it is
-    // used (a select here would wait for the load)
-    const int t = t0 + kSB * J + rr;
-    const size_t e = trow(min(t, T - 1)) * DK + cq;
-    na = *reinterpret_cast<const float4*>(galpha + e);
-    nk = *reinterpret_cast<const uint2*>(gk + e);
-    nq = *reinterpret_cast<const uint2*>(gq + e);
+      for (int x = 0; x < 8; ++x) {
+        const int t = tbp + 8 * part + x;
+        if (t < T) gda[trow(t) * DK + c] = res[x * kCbThreads];
+      }
+    } else {
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int t = tbp + 8 * (part - 2) + x;
+        if (t < T) {
+          gdq[trow(t) * DK + c] = res[2 * x * kCbThreads];
+          gdk[trow(t) * DK + c] = res[(2 * x + 1) * kCbThreads];
+        }
+      }
+    }
+    if (tid < kSB && tbp + tid < T) gdb[trow(tbp + tid)] = res[8 * kCbThreads];
   };
-  fetch_rows(ns - 1);
 #pragma nounroll
   for (int J = ns - 1; J >= 0; --J) {
     const char* rec = rec_of(J);
@@ -808,7 +847,6 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
     // value needed early that loaded late would drain the next sub-chunk's row
     // prefetch (issued during staging) as well.
     const float ypre = reinterpret_cast<const float*>(rec + RB::oY)[tid % (kSB * kSB)];
-    const float pcpre = reinterpret_cast<const float*>(rec + RB::oG)[tid % DK];
     uint16_t dov[4], vv[4];
     {
       const Lane ln = lane_now();
@@ -823,15 +861,6 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
         vv[r] = gv[trow(min(t, T - 1)) * DV + 16 * jt + ln.i];   // rows past T: zeroed at use
       }
     }
-    // record fragments of this sub-chunk, used after the next barriers
-    const bf16x4 pfr = *reinterpret_cast<const bf16x4*>(rec + RB::oP + lane * 8);
-    bf16x8 kfr[NM / 2], qwfr[NM];
-#pragma unroll
-    for (int m = 0; m < NM / 2; ++m)
-      kfr[m] = *reinterpret_cast<const bf16x8*>(rec + RB::oK + (m * 64 + lane) * 16);
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-      qwfr[m] = *reinterpret_cast<const bf16x8*>(rec + RB::oQW + (m * 64 + lane) * 16);
     const bf16x4 uj = *ub_slot(J);
     bf16x4 Sj[NM];   // S of this sub-chunk, this wave's columns
 #pragma unroll
@@ -840,6 +869,14 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
       Sj[2 * mp] = __builtin_bit_cast(bf16x4, make_uint2(v.x, v.y));
       Sj[2 * mp + 1] = __builtin_bit_cast(bf16x4, make_uint2(v.z, v.w));
     }
+    // The record's fragments and decay, one copy in LDS for every wave (not
+    // eight through each wave's registers): 16-byte pieces tid and
+    // kCbThreads + min(tid, ..) (the threads past the end repeat the last
+    // piece: the same bytes to the same place), stored at the column write.
+    static_assert(kRecB / 16 > kCbThreads && kRecB / 16 <= 2 * kCbThreads, "two pieces per thread");
+    const int rq1 = kCbThreads + min(tid, kRecB / 16 - kCbThreads - 1);
+    const uint4 rp0 = *reinterpret_cast<const uint4*>(rec + RB::oQW + 16 * tid);
+    const uint4 rp1 = *reinterpret_cast<const uint4*>(rec + RB::oQW + 16 * rq1);
     // keep these loads ahead of the next sub-chunk's row prefetch below
     asm volatile("" ::: "memory");
     // ---- stage: raw q, k, alpha of the sub-chunk; K.E and (K.E)^T; Y^T; decay
@@ -853,6 +890,8 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
         *reinterpret_cast<uint2*>(sKr + rr * LDK + cq) = ok ? nk : make_uint2(0u, 0u);
         *reinterpret_cast<uint2*>(sQr + rr * LDK + cq) = ok ? nq : make_uint2(0u, 0u);
       }
+      // the last sub-chunk's results, then the next prefetch
+      if (J + 1 < ns) flush(J + 1);
       // unconditional (the last sub-chunk re-fetches its own rows) so that the
       // memory-operation count is the same on every path and later waits can
       // leave these loads in flight
@@ -874,7 +913,6 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
     // does not wait for this sub-chunk's loads)
     {
       if (tid < kSB * kSB) sYT[(tid % kSB) * LDT + tid / kSB] = f32_to_bf16(ypre);
-      if (tid < DK) sPC[tid] = pcpre;
       const Lane ln = lane_now();
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
@@ -893,6 +931,9 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
         sU[(4 * ln.g + r) * LDV + 16 * jt + ln.i] = half16(uj, r);
       }
     }
+    // (the last pass's reads of sRec ended before the barrier that closed it)
+    *reinterpret_cast<uint4*>(sRec + 16 * tid) = rp0;
+    *reinterpret_cast<uint4*>(sRec + 16 * rq1) = rp1;
     lds_barrier();
     // dO of this wave's column tile as a B operand (rows 4g .. 4g+3, column i),
     // read back from LDS; sdO holds it until the next sub-chunk
@@ -907,10 +948,11 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
     f32x4 du;
     {
       const Lane ln = lane_now();
-      du = mma16(pfr, dob, zero4());
+      du = mma16(*reinterpret_cast<const bf16x4*>(sRec + RB::oP + lane * 8), dob, zero4());
 #pragma unroll
       for (int m = 0; m < NM / 2; ++m)
-        du = mma32(kfr[m], cat8(quad4(dS[2 * m]), quad4(dS[2 * m + 1])), du);
+        du = mma32(*reinterpret_cast<const bf16x8*>(sRec + RB::oK + (m * 64 + lane) * 16),
+                   cat8(quad4(dS[2 * m]), quad4(dS[2 * m + 1])), du);
       const f32x4 dZ = mma16(ld4(sYT + ln.i * LDT + 4 * ln.g), quad4(du), zero4());
       f32x4 ks = zero4();
 #pragma unroll
@@ -1020,8 +1062,7 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
               float pr = v[kSB - 1];
 #pragma unroll
               for (int r = kSB - 2; r >= t; --r) pr = fmaf(a[r + 1], pr, v[r]);
-              const int tt = tb + t;
-              if (tt < T) gda[trow(tt) * DK + c] = Fm * R[t] + Hh[t] * colp + Fm * Hh[t] * fin + pr;
+              res[(t - tlo) * kCbThreads] = Fm * R[t] + Hh[t] * colp + Fm * Hh[t] * fin + pr;
             }
             if constexpr (t + 1 < thi) {
               // column t of dP and dA, rows r > t (and r >= tlo)
@@ -1096,20 +1137,16 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
               }
             }
           }
-          const int t = tb + x;
-          if (t < T) {
-            const size_t ex = trow(t) * DK + c;
-            gdq[ex] = F[x] * sOS[x * LDF + c] + g1;
-            gdk[ex] = -sBe[kSB * J + x] * F[x] * sZS[x * LDF + c] + g2 + g3 + Hs[x] * sUS[x * LDF + c];
-          }
+          res[2 * (x % 8) * kCbThreads] = F[x] * sOS[x * LDF + c] + g1;
+          res[(2 * (x % 8) + 1) * kCbThreads] =
+              -sBe[kSB * J + x] * F[x] * sZS[x * LDF + c] + g2 + g3 + Hs[x] * sUS[x * LDF + c];
         }
       }
       if (tid < kSB) {
-        const int t = tb + tid;
         float db = sDb2[tid];
 #pragma unroll
         for (int w = 0; w < kCbThreads / kWave; ++w) db += sDb1[w][tid];
-        if (t < T) gdb[trow(t)] = db;
+        res[8 * kCbThreads] = db;
       }
     }
     // ---- dS <- Diag(E_last) dS + (Q.E)^T dO - W^T dU   (W^T dU = (K.E)^T Diag(beta) dZ)
@@ -1118,8 +1155,9 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
       const bf16x8 du8 = cat8(dO_operand(), quad4(du));
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        const f32x4 aq = mma32(qwfr[m], du8, zero4());
-        const float4 gc = *reinterpret_cast<const float4*>(sPC + 16 * m + 4 * ln.g);
+        const f32x4 aq = mma32(*reinterpret_cast<const bf16x8*>(sRec + RB::oQW + (m * 64 + lane) * 16), du8,
+                               zero4());
+        const float4 gc = *reinterpret_cast<const float4*>(sRec + RB::oG + 4 * (16 * m + 4 * ln.g));
         dS[m][0] = gc.x * dS[m][0] + aq[0];
         dS[m][1] = gc.y * dS[m][1] + aq[1];
         dS[m][2] = gc.z * dS[m][2] + aq[2];
@@ -1128,6 +1166,7 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
     }
     lds_barrier();
   }
+  flush(0);
 }
 
 }  // namespace
