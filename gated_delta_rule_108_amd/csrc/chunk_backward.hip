@@ -1177,12 +1177,11 @@ size_t prefill_backward_chunked_workspace(int B, int T, int H, int dk, int dv) {
   const size_t nc = (static_cast<size_t>(T) + kCB - 1) / kCB;
   const size_t ns = (static_cast<size_t>(T) + kSB - 1) / kSB;
   const size_t fwd = prefill_workspace(B, T, H, dk, dv, kCB, true, 0, true);
-  const size_t o = (chains * T * dv * 2 + 255) / 256 * 256;
   const size_t states = chains * nc * dk * dv * sizeof(float);
   const size_t recs = chains * ns * BRec<128>::kBytes;
   const size_t sub_states = chains * nc * kNSB * dk * dv * 2;   // bf16
   const size_t sub_u = chains * nc * kNSB * kSB * dv * 2;            // bf16
-  return fwd + o + 2 * states + recs + sub_states + sub_u;
+  return fwd + 2 * states + recs + sub_states + sub_u;
 }
 
 hipError_t launch_prefill_backward_chunked(const PrefillBwdArgs& a) {
@@ -1192,13 +1191,12 @@ hipError_t launch_prefill_backward_chunked(const PrefillBwdArgs& a) {
   const int NC = (a.T + kCB - 1) / kCB;
   const size_t fwd = prefill_workspace(a.B, a.T, a.H, a.dk, a.dv, kCB, true, 0, true);
   char* ws = static_cast<char*>(a.workspace);
-  void* o = ws + fwd;
-  float* Sc = reinterpret_cast<float*>(ws + fwd + (chains * a.T * a.dv * 2 + 255) / 256 * 256);
+  float* Sc = reinterpret_cast<float*>(ws + fwd);
   float* dSc = Sc + chains * NC * a.dk * a.dv;
   char* recs = reinterpret_cast<char*>(dSc + chains * NC * a.dk * a.dv);
   bf16x4* sbs = reinterpret_cast<bf16x4*>(recs + chains * ((a.T + kSB - 1) / kSB) * BRec<128>::kBytes);
   if (a.T > 0) {
-    PrefillArgs f{a.q, a.k, a.v, a.alpha, a.beta, a.S0, o, nullptr, a.B, a.T, a.H, a.dk, a.dv,
+    PrefillArgs f{a.q, a.k, a.v, a.alpha, a.beta, a.S0, nullptr, nullptr, a.B, a.T, a.H, a.dk, a.dv,
                   kCB, true, a.stream, ws, fwd, kGateAlpha, kQkAsGiven};
     f.chunk_states = Sc;
     f.force_split = true;

@@ -54,7 +54,8 @@ struct PrefillArgs {
   // Split path: when set, the state every chunk of C tokens starts from,
   // fp32 in matrix-core fragment order [B*H][ceil(T/C)][dv/16][dk/16][64][4]
   // (lane 16g + i holds rows 4g .. 4g+3 of a 16 x 16 block, column i), for
-  // the chunked backward.
+  // the chunked backward; o may then be null (the states alone: the scan
+  // neither reads the output's record parts nor writes o).
   float* chunk_states = nullptr;
   // Take the split path whatever the chain count (chunk_states needs it).
   bool force_split = false;

@@ -242,6 +242,13 @@ kda_scan_kernel(const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float
         }
       }
     }
+  } else if (role == 1 && go == nullptr) {
+    // ---------------- no output wanted (only the chunk states): the output
+    // waves load nothing and keep the two barriers of every chunk
+    for (int ch = 0; ch < NC; ++ch) {
+      lds_barrier();
+      lds_barrier();
+    }
   } else if (role == 1) {
     // ---------------- output wave: O_R = (Q.E)_R S + P_R U
     auto fetch = [&](OO& x, int ch) {

@@ -386,13 +386,13 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v,
 /*
  * kda_prefill_backward_chunked_workspace_bytes — device workspace, in bytes,
  * that kda_prefill_backward_chunked needs: the forward's split-path records
- * (kda_prefill_workspace_bytes at C = 64 with the split path), a scratch copy
- * of the forward output, the state and the state gradient at every 64-token
- * chunk boundary (2 * B * H * ceil(T / 64) * dk * dv * 4 bytes), one
+ * (kda_prefill_workspace_bytes at C = 64 with the split path), the state and
+ * the state gradient at every 64-token chunk boundary
+ * (2 * B * H * ceil(T / 64) * dk * dv * 4 bytes), one
  * 15 KiB record per 16 tokens of every sequence and head, and, per 64-token
  * chunk, the states at its four 16-token blocks and their writes (bf16:
  * 4 * dk * dv * 2 + 64 * dv * 2 bytes) that the gradient pass rebuilds
- * (about 420 MiB at B = 1, H = 16, T = 4096).  (size_t)-1 for
+ * (about 404 MiB at B = 1, H = 16, T = 4096).  (size_t)-1 for
  * sizes the call does not accept (dk or dv other than 128).
  */
 size_t kda_prefill_backward_chunked_workspace_bytes(int B, int T, int H, int dk, int dv);

@@ -478,8 +478,8 @@ def test_prefill_backward_valid_arguments():
 
 
 def test_prefill_backward_chunked_workspace_bytes():
-    """The forward's split-path records (C = 64, split path), the forward
-    output, the state and the state gradient every 64 tokens (fp32), one
+    """The forward's split-path records (C = 64, split path), the state
+    and the state gradient every 64 tokens (fp32), one
     15 KiB record per 16 tokens, and per 64 tokens the four 16-token states
     and their writes (bf16)."""
     L = _lib()
@@ -497,13 +497,12 @@ def test_prefill_backward_chunked_workspace_bytes():
         if nseg > 1:
             segch = min(segmax, -(-segch // runs) * runs)
         fwd = chains * segch * fwd_rec + (chains * 128 * 128 * 4 if nseg > 1 else 0)
-        o = (chains * T * 128 * 2 + 255) // 256 * 256
-        return (fwd + o + 2 * chains * nc * 128 * 128 * 4 + chains * ns * 15360
+        return (fwd + 2 * chains * nc * 128 * 128 * 4 + chains * ns * 15360
                 + chains * nc * 4 * 128 * 128 * 2 + chains * nc * 4 * 16 * 128 * 2)
 
     for B, T, H in ((1, 4096, 16), (2, 100, 3), (8, 8192, 32), (1, 1, 1)):
         assert lib.kda_prefill_backward_chunked_workspace_bytes(B, T, H, 128, 128) == expect(B, T, H)
-    assert lib.kda_prefill_backward_chunked_workspace_bytes(1, 4096, 16, 128, 128) >> 20 == 420
+    assert lib.kda_prefill_backward_chunked_workspace_bytes(1, 4096, 16, 128, 128) >> 20 == 404
     bad = ctypes.c_size_t(-1).value
     assert lib.kda_prefill_backward_chunked_workspace_bytes(1, 64, 2, 64, 128) == bad   # dk
     assert lib.kda_prefill_backward_chunked_workspace_bytes(1, 64, 2, 128, 64) == bad   # dv
