@@ -599,7 +599,8 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
                    const float* __restrict__ gSc, const float* __restrict__ gdSc,
                    const char* __restrict__ grec, bf16x4* __restrict__ gSb,
                    float* __restrict__ gdq, float* __restrict__ gdk, float* __restrict__ gdv,
-                   float* __restrict__ gda, float* __restrict__ gdb, int T, int H) {
+                   float* __restrict__ gda, float* __restrict__ gdb, float* __restrict__ gsink,
+                   int T, int H) {
   using RB = BRec<DK>;
   constexpr int NM = DK / 16;
   constexpr int LDK = DK + 8, LDV = DV + 8, LDT = kSB + 8, LDF = DK + 4;
@@ -627,10 +628,10 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   __shared__ __attribute__((aligned(16))) float sdPT[kSB * LDP];
   __shared__ __attribute__((aligned(16))) float sdAT[kSB * LDP];
   __shared__ float sPC[DK];
-  // the record's fragments and decay for the backward pass, [(Q.E)^T | -W^T],
-  // K.E', P^T, decay: loaded once per sub-chunk, read by every wave
-  constexpr int kRecB = RB::oY - RB::oQW;
-  static_assert(RB::oQW == 0 && kRecB % 1024 == 0, "record prefix in 1 KiB pieces");
+  // the whole sub-chunk record for the backward pass, [(Q.E)^T | -W^T],
+  // K.E', P^T, decay, Y, A: loaded once per sub-chunk, read by every wave
+  constexpr int kRecB = RB::kBytes - RB::oQW;
+  static_assert(RB::oQW == 0 && kRecB % 1024 == 0, "record in 1 KiB pieces");
   __shared__ __attribute__((aligned(16))) char sRec[kRecB];
   __shared__ float sFin[DK];                                          // sum_j dS[c][j] S[c][j]
   __shared__ float sDb1[kCbThreads / kWave][kSB];
@@ -812,73 +813,84 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   // res[x * kCbThreads + tid], dalpha of rows 8 part + x (quarters 0, 1),
   // dq and dk of rows 8 (part - 2) + x in slots 2x, 2x + 1 (quarters 2, 3),
   // dbeta of row tid in slot 8 (threads below 16).  They go to memory at the
-  // top of the next sub-chunk, after its prefetched rows have been waited
-  // for and before the next prefetch is issued: a wait for a load covers
-  // every store issued before it, and these stores are then a whole
-  // sub-chunk old.
-  float* const res = reinterpret_cast<float*>(sS) + tid;
+  // top of the next sub-chunk (after the barrier that ends this one), before
+  // its row prefetch: thread (row rr, channel quad cq) stores 16 bytes of
+  // each of dalpha, dq and dk of its row and one dbeta, the same four stores
+  // in every thread and on every path (a row past T, and dbeta past the 16
+  // rows, goes to a dump slot), so that the compiler knows how many stores
+  // follow each load and never waits for a store to wait for a load.
+  float* const res = reinterpret_cast<float*>(sS);
   static_assert(16 * kCbThreads * sizeof(float) <= sizeof(sS), "result slots");
-  auto flush = [&](int Jp) {
-    const int tbp = t0 + kSB * Jp;
-    if (part < 2) {
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const int t = tbp + 8 * part + x;
-        if (t < T) gda[trow(t) * DK + c] = res[x * kCbThreads];
-      }
-    } else {
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const int t = tbp + 8 * (part - 2) + x;
-        if (t < T) {
-          gdq[trow(t) * DK + c] = res[2 * x * kCbThreads];
-          gdk[trow(t) * DK + c] = res[(2 * x + 1) * kCbThreads];
-        }
-      }
-    }
-    if (tid < kSB && tbp + tid < T) gdb[trow(tbp + tid)] = res[8 * kCbThreads];
+  float* const dump = gsink + 4 * lane;
+  auto flush = [&](int Jp, bool valid) {
+    const int tbp = t0 + kSB * Jp, t = tbp + rr, x = rr % 8, hq = rr / 8;
+    const bool ok = valid && t < T;
+    const size_t e = trow(min(t, T - 1)) * DK + cq;
+    const float4 va = *reinterpret_cast<const float4*>(res + x * kCbThreads + hq * DK + cq);
+    const float4 vq = *reinterpret_cast<const float4*>(res + 2 * x * kCbThreads + (2 + hq) * DK + cq);
+    const float4 vk = *reinterpret_cast<const float4*>(res + (2 * x + 1) * kCbThreads + (2 + hq) * DK + cq);
+    const int rb = min(tid, kSB - 1);
+    const float vb = res[8 * kCbThreads + rb];
+    *reinterpret_cast<float4*>(ok ? gda + e : dump) = va;
+    *reinterpret_cast<float4*>(ok ? gdq + e : dump) = vq;
+    *reinterpret_cast<float4*>(ok ? gdk + e : dump) = vk;
+    *(valid && tid < kSB && tbp + rb < T ? gdb + trow(min(tbp + rb, T - 1)) : dump) = vb;
   };
+  // Per-wave loads of a sub-chunk (in the order they are needed): Y, the dO
+  // and V rows of this wave's columns, U and S of the sub-chunk, and two
+  // 16-byte pieces of the record's fragments and decay (every thread loads
+  // pieces tid and kCbThreads + min(tid, ..), the threads past the end
+  // repeating the last piece: the same bytes to the same place; stored to
+  // LDS at the column write, one copy for every wave).  Issued at the end of
+  // the sub-chunk before, after its gate phase, so that they land while it
+  // finishes; rows past T load a repeat of row T - 1, zeroed at use.
+  static_assert(kRecB / 16 > kCbThreads && kRecB / 16 <= 2 * kCbThreads, "two pieces per thread");
+  const int rq1 = kCbThreads + min(tid, kRecB / 16 - kCbThreads - 1);
+  struct WaveIn {
+    float ypre;
+    uint16_t dov[4], vv[4];
+    bf16x4 uj;
+    uint4 sb[NM / 2];
+    uint4 rp0, rp1;
+  };
+  auto load_wave = [&](int J, WaveIn& w) {
+    const char* rec = rec_of(J);
+    const int tb = t0 + kSB * J;
+    const Lane ln = lane_now();
+    w.ypre = reinterpret_cast<const float*>(rec + RB::oY)[tid % (kSB * kSB)];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w.dov[r] = gdO[trow(min(tb + 4 * ln.g + r, T - 1)) * DV + 16 * jt + ln.i];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w.vv[r] = gv[trow(min(tb + 4 * ln.g + r, T - 1)) * DV + 16 * jt + ln.i];
+    w.uj = *ub_slot(J);
+#pragma unroll
+    for (int mp = 0; mp < NM / 2; ++mp) w.sb[mp] = *sb_slot(J, mp);
+    w.rp0 = *reinterpret_cast<const uint4*>(rec + RB::oQW + 16 * tid);
+    w.rp1 = *reinterpret_cast<const uint4*>(rec + RB::oQW + 16 * rq1);
+  };
+  WaveIn wnext;
+  load_wave(ns - 1, wnext);
 #pragma nounroll
   for (int J = ns - 1; J >= 0; --J) {
     const char* rec = rec_of(J);
     const int tb = t0 + kSB * J;
-    // Global loads of this sub-chunk, in the order they are needed: a vector
-    // memory wait covers every load issued before the one it waits for, so a
-    // value needed early that loaded late would drain the next sub-chunk's row
-    // prefetch (issued during staging) as well.
-    const float ypre = reinterpret_cast<const float*>(rec + RB::oY)[tid % (kSB * kSB)];
+    // this sub-chunk's per-wave loads, issued at the end of the last one
+    const WaveIn win = wnext;
+    const float ypre = win.ypre;
     uint16_t dov[4], vv[4];
-    {
-      const Lane ln = lane_now();
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = tb + 4 * ln.g + r;
-        dov[r] = gdO[trow(min(t, T - 1)) * DV + 16 * jt + ln.i];   // rows past T: zeroed at use
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = tb + 4 * ln.g + r;
-        vv[r] = gv[trow(min(t, T - 1)) * DV + 16 * jt + ln.i];   // rows past T: zeroed at use
-      }
+    for (int r = 0; r < 4; ++r) {
+      dov[r] = win.dov[r];
+      vv[r] = win.vv[r];
     }
-    const bf16x4 uj = *ub_slot(J);
+    const bf16x4 uj = win.uj;
     bf16x4 Sj[NM];   // S of this sub-chunk, this wave's columns
 #pragma unroll
     for (int mp = 0; mp < NM / 2; ++mp) {
-      const uint4 v = *sb_slot(J, mp);
-      Sj[2 * mp] = __builtin_bit_cast(bf16x4, make_uint2(v.x, v.y));
-      Sj[2 * mp + 1] = __builtin_bit_cast(bf16x4, make_uint2(v.z, v.w));
+      Sj[2 * mp] = __builtin_bit_cast(bf16x4, make_uint2(win.sb[mp].x, win.sb[mp].y));
+      Sj[2 * mp + 1] = __builtin_bit_cast(bf16x4, make_uint2(win.sb[mp].z, win.sb[mp].w));
     }
-    // The record's fragments and decay, one copy in LDS for every wave (not
-    // eight through each wave's registers): 16-byte pieces tid and
-    // kCbThreads + min(tid, ..) (the threads past the end repeat the last
-    // piece: the same bytes to the same place), stored at the column write.
-    static_assert(kRecB / 16 > kCbThreads && kRecB / 16 <= 2 * kCbThreads, "two pieces per thread");
-    const int rq1 = kCbThreads + min(tid, kRecB / 16 - kCbThreads - 1);
-    const uint4 rp0 = *reinterpret_cast<const uint4*>(rec + RB::oQW + 16 * tid);
-    const uint4 rp1 = *reinterpret_cast<const uint4*>(rec + RB::oQW + 16 * rq1);
-    // keep these loads ahead of the next sub-chunk's row prefetch below
-    asm volatile("" ::: "memory");
+    const uint4 rp0 = win.rp0, rp1 = win.rp1;
     // ---- stage: raw q, k, alpha of the sub-chunk; K.E and (K.E)^T; Y^T; decay
     {
       // this sub-chunk's rows, prefetched during the last one (read only
@@ -890,8 +902,9 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
         *reinterpret_cast<uint2*>(sKr + rr * LDK + cq) = ok ? nk : make_uint2(0u, 0u);
         *reinterpret_cast<uint2*>(sQr + rr * LDK + cq) = ok ? nq : make_uint2(0u, 0u);
       }
-      // the last sub-chunk's results, then the next prefetch
-      if (J + 1 < ns) flush(J + 1);
+      // the last sub-chunk's results (none yet before the first: the same
+      // stores, to the dump), then the next prefetch
+      flush(J + 1, J + 1 < ns);
       // unconditional (the last sub-chunk re-fetches its own rows) so that the
       // memory-operation count is the same on every path and later waits can
       // leave these loads in flight
@@ -962,7 +975,8 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
         const int row = 4 * ln.g + r, t = tb + row;
         const float v = t < T ? bf16_to_f32(vv[r]) : 0.f;
         const float x = v - ks[r];
-        if (t < T) gdv[trow(t) * DV + 16 * jt + ln.i] = sBe[kSB * J + row] * dZ[r];
+        // unconditional (a row past T to the dump slot): a known store count
+        *(t < T ? gdv + trow(min(t, T - 1)) * DV + 16 * jt + ln.i : dump) = sBe[kSB * J + row] * dZ[r];
         const float db = row16_sum(dZ[r] * x);
         if (ln.i == 0) sDb1[wave][row] = db;
         sdZ[row * LDV + 16 * jt + ln.i] = f32_to_bf16(dZ[r]);
@@ -997,7 +1011,7 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
 #pragma unroll
         for (int k0 = 0; k0 < DV; k0 += 32)
           pp = mma32(ld8(am + ln.i * LDV + k0 + 8 * ln.g), ld8(sU + ln.i * LDV + k0 + 8 * ln.g), pp);
-        const float* Af = reinterpret_cast<const float*>(rec + RB::oA);
+        const float* Af = reinterpret_cast<const float*>(sRec + RB::oA);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 4 * ln.g + r;
@@ -1062,7 +1076,7 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
               float pr = v[kSB - 1];
 #pragma unroll
               for (int r = kSB - 2; r >= t; --r) pr = fmaf(a[r + 1], pr, v[r]);
-              res[(t - tlo) * kCbThreads] = Fm * R[t] + Hh[t] * colp + Fm * Hh[t] * fin + pr;
+              res[(t - tlo) * kCbThreads + tid] = Fm * R[t] + Hh[t] * colp + Fm * Hh[t] * fin + pr;
             }
             if constexpr (t + 1 < thi) {
               // column t of dP and dA, rows r > t (and r >= tlo)
@@ -1137,8 +1151,8 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
               }
             }
           }
-          res[2 * (x % 8) * kCbThreads] = F[x] * sOS[x * LDF + c] + g1;
-          res[(2 * (x % 8) + 1) * kCbThreads] =
+          res[2 * (x % 8) * kCbThreads + tid] = F[x] * sOS[x * LDF + c] + g1;
+          res[(2 * (x % 8) + 1) * kCbThreads + tid] =
               -sBe[kSB * J + x] * F[x] * sZS[x * LDF + c] + g2 + g3 + Hs[x] * sUS[x * LDF + c];
         }
       }
@@ -1146,9 +1160,12 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
         float db = sDb2[tid];
 #pragma unroll
         for (int w = 0; w < kCbThreads / kWave; ++w) db += sDb1[w][tid];
-        res[8 * kCbThreads] = db;
+        res[8 * kCbThreads + tid] = db;
       }
     }
+    // the next sub-chunk's per-wave loads (unconditional: the first
+    // sub-chunk reloads its own)
+    load_wave(J > 0 ? J - 1 : 0, wnext);
     // ---- dS <- Diag(E_last) dS + (Q.E)^T dO - W^T dU   (W^T dU = (K.E)^T Diag(beta) dZ)
     {
       const Lane ln = lane_now();
@@ -1166,7 +1183,7 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
     }
     lds_barrier();
   }
-  flush(0);
+  flush(0, true);
 }
 
 }  // namespace
@@ -1224,7 +1241,8 @@ hipError_t launch_prefill_backward_chunked(const PrefillBwdArgs& a) {
   kda_cb_grad_kernel<128, 128><<<static_cast<unsigned>(chains * NC), kCbThreads, 0, stream>>>(
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
       static_cast<const uint16_t*>(a.v), a.alpha, a.beta, static_cast<const uint16_t*>(a.dO), Sc,
-      dSc, recs, sbs, a.g_q, a.g_k, a.g_v, a.g_alpha, a.g_beta, a.T, a.H);
+      dSc, recs, sbs, a.g_q, a.g_k, a.g_v, a.g_alpha, a.g_beta, reinterpret_cast<float*>(ws), a.T,
+      a.H);
   return hipGetLastError();
 }
 
