@@ -203,10 +203,12 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
     const bool safe = bt >= kUnsafeBlockDecay;
     if (!safe) atomicOr(&sFl[J], 1);
     sBT[J][c] = bt;
+    // 1/F_r = H_r / bt: one reciprocal per channel instead of a division per row
+    const float rbt = safe ? 1.f / bt : 0.f;
 #pragma unroll
     for (int r = 0; r < kSB; ++r) {
       sKF[J][r * LDK + c] = f32_to_bf16(kk[r] * F[r]);
-      sKI[J][r * LDK + c] = f32_to_bf16(safe ? kk[r] / F[r] : 0.f);
+      sKI[J][r * LDK + c] = f32_to_bf16(kk[r] * Hs[r] * rbt);
       sQF[J][r * LDK + c] = f32_to_bf16(qq[r] * F[r]);
       sKH[J][r * LDK + c] = f32_to_bf16(kk[r] * Hs[r]);
     }
