@@ -384,7 +384,12 @@ kda_cb_scan_kernel(const char* __restrict__ grec, const uint16_t* __restrict__ g
   __shared__ __attribute__((aligned(16))) char ring[RG::kNBuf * RG::kBuf];
   __shared__ __attribute__((aligned(16))) float xu[2][2][NT][kWave * 4];   // [step parity][part] of u
   const int NJV = DV / (16 * NT);                    // workgroups per chain
-  const int chain = blockIdx.x / NJV, jt0 = NT * (blockIdx.x % NJV);
+  // Consecutive workgroup IDs are dealt round-robin to the 8 XCDs; the
+  // workgroups of one chain read the same records, so they are gathered on
+  // one XCD, where the records come from its L2 after the first read.
+  int L = blockIdx.x;
+  if (NJV > 1 && (gridDim.x % 8) == 0) L = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+  const int chain = L / NJV, jt0 = NT * (L % NJV);
   const int b = chain / H, h = chain % H;
   const int NS = (T + kSB - 1) / kSB, NC = (T + kCB - 1) / kCB;
   const int lane = threadIdx.x % kWave;
