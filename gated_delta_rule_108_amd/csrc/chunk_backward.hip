@@ -40,6 +40,8 @@
 //   4. kda_cb_grad_kernel: per 64-token chunk, the states of its four
 //      sub-chunks (forward from the stored chunk state), then the sub-chunks
 //      from the last to the first: all gradients of their tokens.
+#include <mutex>
+
 #include "scan_kernel.hpp"
 
 namespace kda {
@@ -1193,6 +1195,42 @@ kda_cb_grad_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   flush(0, true);
 }
 
+// A second stream per device, with the events of a fork and a join: the
+// forward half (chunk states) and the record kernel's half (state gradients)
+// of the backward share no data until the gradient kernel, and when the
+// state-gradient scan fills at most half of the chip the forward runs beside
+// it.  Created on first use with the device current and kept until the
+// process ends; default priority.  The mutex makes each call's fork and join
+// one unit against other host threads (the events are reused).
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxSideDevices = 64;
+SideStream g_side[kMaxSideDevices];
+std::mutex g_side_mu;
+
+// The current device's side stream; the caller holds g_side_mu.
+hipError_t side_stream(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxSideDevices) return hipErrorInvalidDevice;
+  SideStream& ss = g_side[dev];
+  if (ss.s == nullptr) {
+    hipStream_t st = nullptr;
+    hipEvent_t a = nullptr, b = nullptr;
+    if ((e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&a, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&b, hipEventDisableTiming)) != hipSuccess) return e;
+    ss.fork = a;
+    ss.join = b;
+    ss.s = st;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
+
 }  // namespace
 
 size_t prefill_backward_chunked_workspace(int B, int T, int H, int dk, int dv) {
@@ -1219,32 +1257,61 @@ hipError_t launch_prefill_backward_chunked(const PrefillBwdArgs& a) {
   float* dSc = Sc + chains * NC * a.dk * a.dv;
   char* recs = reinterpret_cast<char*>(dSc + chains * NC * a.dk * a.dv);
   bf16x4* sbs = reinterpret_cast<bf16x4*>(recs + chains * ((a.T + kSB - 1) / kSB) * BRec<128>::kBytes);
-  if (a.T > 0) {
+  hipError_t e = hipSuccess;
+  // the record kernel (sub-chunk records of the state-gradient scan)
+  auto records = [&](hipStream_t st) {
+    const unsigned pblocks =
+        static_cast<unsigned>(chains * (((a.T + kSB - 1) / kSB + kPS - 1) / kPS));
+    kda_cb_prep_kernel<128><<<pblocks, 128 * kPS, 0, st>>>(
+        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), a.alpha, a.beta,
+        recs, a.T, a.H);
+    return hipGetLastError();
+  };
+  // the forward split path, chunk states only (no output)
+  auto forward = [&]() {
     PrefillArgs f{a.q, a.k, a.v, a.alpha, a.beta, a.S0, nullptr, nullptr, a.B, a.T, a.H, a.dk, a.dv,
                   kCB, true, a.stream, ws, fwd, kGateAlpha, kQkAsGiven};
     f.chunk_states = Sc;
     f.force_split = true;
-    hipError_t e = launch_prefill(f);
-    if (e != hipSuccess) return e;
-    const unsigned pblocks =
-        static_cast<unsigned>(chains * (((a.T + kSB - 1) / kSB + kPS - 1) / kPS));
-    kda_cb_prep_kernel<128><<<pblocks, 128 * kPS, 0, stream>>>(
-        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), a.alpha, a.beta,
-        recs, a.T, a.H);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+    return launch_prefill(f);
+  };
   // two column tiles per state wave once one tile per workgroup would fill
   // the chip (a state wave is issue-bound: two tiles share its fragment reads
   // but lengthen its step)
-  if (chains * (a.dv / 16) >= 256)
-    kda_cb_scan_kernel<128, 2><<<static_cast<unsigned>(chains * (a.dv / 32)), 4 * kWave, 0, stream>>>(
-        recs, static_cast<const uint16_t*>(a.dO), a.dS_T, dSc, a.g_S0, a.T, a.H, a.dv);
-  else
-    kda_cb_scan_kernel<128, 1><<<static_cast<unsigned>(chains * (a.dv / 16)), 4 * kWave, 0, stream>>>(
-        recs, static_cast<const uint16_t*>(a.dO), a.dS_T, dSc, a.g_S0, a.T, a.H, a.dv);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.T == 0) return e;
+  const bool two = chains * (a.dv / 16) >= 256;
+  auto state_grad = [&](hipStream_t st) {
+    if (two)
+      kda_cb_scan_kernel<128, 2><<<static_cast<unsigned>(chains * (a.dv / 32)), 4 * kWave, 0, st>>>(
+          recs, static_cast<const uint16_t*>(a.dO), a.dS_T, dSc, a.g_S0, a.T, a.H, a.dv);
+    else
+      kda_cb_scan_kernel<128, 1><<<static_cast<unsigned>(chains * (a.dv / 16)), 4 * kWave, 0, st>>>(
+          recs, static_cast<const uint16_t*>(a.dO), a.dS_T, dSc, a.g_S0, a.T, a.H, a.dv);
+    return hipGetLastError();
+  };
+  if (a.T == 0) return state_grad(stream);   // dS0 = dS_T: no forward, no gradient kernel
+  // With at most half of the chip taken by the state-gradient scan, it runs on
+  // the side stream beside the forward, which takes the other CUs; the
+  // gradient kernel waits for both.
+  if (chains * (a.dv / 16) <= 128) {
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    SideStream* ss = nullptr;
+    if ((e = side_stream(&ss)) != hipSuccess) return e;
+    if ((e = hipEventRecord(ss->fork, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return e;
+    if ((e = records(ss->s)) != hipSuccess) return e;
+    if ((e = state_grad(ss->s)) != hipSuccess) return e;
+    if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess) return e;
+    e = forward();
+    // the caller's stream waits for the side stream's work whatever happened
+    // to the forward, so that nothing of this call outlives it there
+    const hipError_t ej = hipStreamWaitEvent(stream, ss->join, 0);
+    if (e != hipSuccess) return e;
+    if (ej != hipSuccess) return ej;
+  } else {
+    if ((e = records(stream)) != hipSuccess) return e;
+    if ((e = forward()) != hipSuccess) return e;
+    if ((e = state_grad(stream)) != hipSuccess) return e;
+  }
   kda_cb_grad_kernel<128, 128><<<static_cast<unsigned>(chains * NC), kCbThreads, 0, stream>>>(
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
       static_cast<const uint16_t*>(a.v), a.alpha, a.beta, static_cast<const uint16_t*>(a.dO), Sc,

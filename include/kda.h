@@ -417,6 +417,16 @@ size_t kda_prefill_backward_chunked_workspace_bytes(int B, int T, int H, int dk,
  * kda_prefill_backward, with the workspace of
  * kda_prefill_backward_chunked_workspace_bytes; dt must be KDA_BF16 and
  * dk = dv = 128 (else KDA_ERR_UNSUPPORTED).
+ *
+ * Streams: when B * H * dv / 16 <= 128 the state-gradient half runs on a
+ * second stream of the library's own (one per device, default priority,
+ * created on the first such call and kept until the process ends), forked
+ * from `stream` by an event at the start of the call and joined back into it
+ * before the last kernel, so all of the call's work is ordered on `stream`
+ * as usual.  Calls from several host threads are serialised while they
+ * enqueue.  A call made while `stream` is being captured into a graph puts
+ * that second stream into the capture too; no other backward call on the
+ * same device may run until the capture ends.
  */
 kda_status kda_prefill_backward_chunked(const void* q, const void* k, const void* v,
                                         const float* alpha, const float* beta, const float* S0,
