@@ -1267,12 +1267,12 @@ hipError_t launch_prefill_backward_chunked(const PrefillBwdArgs& a) {
         recs, a.T, a.H);
     return hipGetLastError();
   };
-  // the forward split path, chunk states only (no output)
+  // the forward, chunk states only (no output): the split path for few
+  // chains, the fused kernel for many (the prefill's own choice)
   auto forward = [&]() {
     PrefillArgs f{a.q, a.k, a.v, a.alpha, a.beta, a.S0, nullptr, nullptr, a.B, a.T, a.H, a.dk, a.dv,
                   kCB, true, a.stream, ws, fwd, kGateAlpha, kQkAsGiven};
     f.chunk_states = Sc;
-    f.force_split = true;
     return launch_prefill(f);
   };
   // two column tiles per state wave once one tile per workgroup would fill

@@ -51,13 +51,15 @@ struct PrefillArgs {
   // Split path: bytes of records per segment (0: the default budget).  The
   // same value must size the workspace (prefill_workspace).
   size_t segment_budget = 0;
-  // Split path: when set, the state every chunk of C tokens starts from,
-  // fp32 in matrix-core fragment order [B*H][ceil(T/C)][dv/16][dk/16][64][4]
-  // (lane 16g + i holds rows 4g .. 4g+3 of a 16 x 16 block, column i), for
-  // the chunked backward; o may then be null (the states alone: the scan
-  // neither reads the output's record parts nor writes o).
+  // When set, the state every chunk of C tokens starts from, fp32 in
+  // matrix-core fragment order [B*H][ceil(T/C)][dv/16][dk/16][64][4] (lane
+  // 16g + i holds rows 4g .. 4g+3 of a 16 x 16 block, column i), for the
+  // chunked backward; o may then be null (the states alone: the split scan
+  // neither reads the output's record parts nor writes o, the fused kernel
+  // skips its output products).  The fused kernel writes them only with
+  // per-channel gates (kGateAlpha).
   float* chunk_states = nullptr;
-  // Take the split path whatever the chain count (chunk_states needs it).
+  // Take the split path whatever the chain count.
   bool force_split = false;
 };
 

@@ -43,6 +43,8 @@
 // units from running products of alpha.
 #pragma once
 
+#include <type_traits>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -630,7 +632,8 @@ constexpr int kMaxLds = 160 * 1024;
 // wave and, at dk = 128, across two waves in LDS.  kGateScalar: ggate holds
 // one alpha per token and head (Gated DeltaNet), broadcast over the
 // channels as it is loaded, or is null for alpha = 1 (DeltaNet).
-template <typename OpT, int DK, int C, int DVT, bool kPrep = false, int kIn = kGateAlpha>
+template <typename OpT, int DK, int C, int DVT, bool kPrep = false, int kIn = kGateAlpha,
+          bool kStates = false>
 __global__ void __launch_bounds__(512)
 kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
                    const typename Ty<OpT>::Elem* __restrict__ gk,
@@ -638,7 +641,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
                    const void* __restrict__ ggate, const float* __restrict__ gbeta,
                    const float* gS0, typename Ty<OpT>::Elem* __restrict__ go, float* gST,
                    int B, int T, int H, int DV, char* __restrict__ gws, int cpb, int seg0,
-                   int segn, int qk_map, int nt_in) {
+                   int segn, int qk_map, int nt_in, float* __restrict__ gSc) {
   using Cf = PCfg<OpT, DK, C, DVT>;
   using E = typename Ty<OpT>::Elem;
   using PT = typename Pair<OpT>::T;
@@ -1743,7 +1746,10 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       }
     }
     lds_barrier();
-    E* po = go + (row0 + static_cast<size_t>(t0) * H) * DV + j0;
+    // kStates (the chunked backward's forward pass): the chunk states are
+    // stored and the output products and stores are left out
+    constexpr bool want_o = !kStates;
+    E* po = want_o ? go + (row0 + static_cast<size_t>(t0) * H) * DV + j0 : nullptr;
     const int nrows = min(C, T - t0);
     {
       // O = (Q E) S + P U
@@ -1756,7 +1762,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
           for (int k = 0; k < C / 32; ++k) uB[k] = ub.template get<32>(32 * k);
         }
       }
-      if (UM::active(wave)) {
+      if (want_o && UM::active(wave)) {
 #pragma unroll
         for (int a = 0; a < UM::RA; ++a) {
           const int R = UM::row0(wave) + a;
@@ -1795,6 +1801,20 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
           }
         }
       }
+      // the state this chunk starts from, fp32, in fragment order:
+      // [chain][chunk][column tile][row block][lane][4], one 16-byte store
+      // per block (the layout of the scan kernel's chunk states)
+      if (kStates && SM::active(wave)) {
+#pragma unroll
+        for (int a = 0; a < SM::RA; ++a)
+#pragma unroll
+          for (int bb = 0; bb < SM::CA; ++bb) {
+            const int Cb = SM::row0(wave) + a, jt = (j0 >> 4) + SM::col0(wave) + bb;
+            float* dst = gSc + ((static_cast<size_t>(chain) * NC + ch) * (DV / 16) + jt) * DK * 16;
+            *reinterpret_cast<float4*>(dst + (Cb * kWave + (tid & 63)) * 4) =
+                make_float4(Sreg[a][bb][0], Sreg[a][bb][1], Sreg[a][bb][2], Sreg[a][bb][3]);
+          }
+      }
       // S <- Diag(decay of the chunk) S + (K E')^T U
       if (SM::active(wave)) {
 #pragma unroll
@@ -1826,7 +1846,7 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
       // staged output rows -> HBM with 16-byte stores
       constexpr int VPR = DVT * static_cast<int>(sizeof(E)) / 16;   // vectors per row
       constexpr int EPV = 16 / static_cast<int>(sizeof(E));          // elements per vector
-      for (int x = tid; x < C * VPR; x += NTH) {
+      for (int x = want_o ? tid : C * VPR; x < C * VPR; x += NTH) {
         const int r = x / VPR, cv = x % VPR;
         if (full || r < nrows)
           *reinterpret_cast<uint4*>(po + r * rsV + cv * EPV) =
@@ -1852,16 +1872,17 @@ kda_prefill_kernel(const typename Ty<OpT>::Elem* __restrict__ gq,
 // ----------------------------------------------------------------------------
 // Host dispatch
 // ----------------------------------------------------------------------------
-template <typename OpT, int DK, int C, int DVT, int kIn>
+template <typename OpT, int DK, int C, int DVT, int kIn, bool kStates = false>
 hipError_t launch_one(const PrefillArgs& a) {
   using E = typename Ty<OpT>::Elem;
   const long chains = static_cast<long>(a.B) * a.H;
   dim3 grid(static_cast<unsigned>(chains * (a.dv / DVT)));
-  hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT, false, kIn>), grid,
+  hipLaunchKernelGGL((kda_prefill_kernel<OpT, DK, C, DVT, false, kIn, kStates>), grid,
                      dim3(PCfg<OpT, DK, C, DVT>::NTH), 0, static_cast<hipStream_t>(a.stream),
                      static_cast<const E*>(a.q), static_cast<const E*>(a.k),
-                     static_cast<const E*>(a.v), a.gate, a.beta, a.S0, static_cast<E*>(a.o),
-                     a.S_T, a.B, a.T, a.H, a.dv, nullptr, 0, 0, 0, a.qk_map, 0);
+                     static_cast<const E*>(a.v), a.gate, a.beta, a.S0,
+                     kStates ? nullptr : static_cast<E*>(a.o), a.S_T, a.B, a.T, a.H, a.dv,
+                     nullptr, 0, 0, 0, a.qk_map, 0, kStates ? a.chunk_states : nullptr);
   return hipGetLastError();
 }
 
@@ -1902,6 +1923,17 @@ int pick_dvt(long chains, int dv) {
 template <typename OpT, int DK, int C, int kIn>
 hipError_t launch_c(const PrefillArgs& a) {
   const int dvt = pick_dvt<OpT, DK, C>(static_cast<long>(a.B) * a.H, a.dv);
+  if (a.chunk_states != nullptr) {
+    // chunk states without output: built for the chunked backward's
+    // configuration only (bf16, dk = 128, C = 64, per-channel gates)
+    if constexpr (std::is_same<OpT, bf16_t>::value && DK == 128 && C == 64 && kIn == kGateAlpha) {
+      switch (dvt) {
+        case 64: return launch_one<OpT, DK, C, 64, kIn, true>(a);
+        case 128: return launch_one<OpT, DK, C, 128, kIn, true>(a);
+      }
+    }
+    return hipErrorInvalidValue;
+  }
   switch (dvt) {
     case 16: if constexpr (fits<OpT, DK, C, 16>()) return launch_one<OpT, DK, C, 16, kIn>(a); break;
     case 32: if constexpr (fits<OpT, DK, C, 32>()) return launch_one<OpT, DK, C, 32, kIn>(a); break;

@@ -476,7 +476,7 @@ hipError_t launch_prep(const PrefillArgs& a, int seg0, int segn, bool nt_in) {
                        static_cast<const E*>(a.k), static_cast<const E*>(a.v), a.gate, a.beta,
                        a.S0, static_cast<E*>(a.o), a.S_T, a.B, a.T, a.H, a.dv,
                        static_cast<char*>(a.workspace), cpb, seg0, segn, a.qk_map,
-                       nt_in ? 1 : 0);
+                       nt_in ? 1 : 0, nullptr);
     return hipGetLastError();
   }
 }

@@ -94,6 +94,12 @@ def test_many_chains():
     run(spec(), B=4, T=100, H=16)
 
 
+def test_more_chains_than_the_split_path_takes():
+    """144 chains: the forward pass runs the fused chunk kernel, which stores
+    the chunk states and writes no output (ragged last chunk)."""
+    run(spec(), B=2, T=150, H=72, heads=[0, 35, 71])
+
+
 def test_optional_states():
     run(spec(s0_std=0.0), B=1, T=70, H=2, with_dST=False)
 
