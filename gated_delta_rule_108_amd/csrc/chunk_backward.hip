@@ -1292,10 +1292,21 @@ hipError_t launch_prefill_backward_chunked(const PrefillBwdArgs& a) {
   // With at most half of the chip taken by the state-gradient scan, it runs on
   // the side stream beside the forward, which takes the other CUs; the
   // gradient kernel waits for both.
-  if (chains * (a.dv / 16) <= 128) {
-    std::lock_guard<std::mutex> lk(g_side_mu);
-    SideStream* ss = nullptr;
-    if ((e = side_stream(&ss)) != hipSuccess) return e;
+  // A call on a stream that is being captured into a graph runs in order on
+  // that stream alone, and so does one whose side stream cannot be made.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if ((e = hipStreamIsCapturing(stream, &cap)) != hipSuccess) return e;
+  std::unique_lock<std::mutex> lk(g_side_mu, std::defer_lock);
+  SideStream* ss = nullptr;
+  if (chains * (a.dv / 16) <= 128 && cap == hipStreamCaptureStatusNone) {
+    lk.lock();
+    if (side_stream(&ss) != hipSuccess) {
+      ss = nullptr;
+      lk.unlock();
+      (void)hipGetLastError();   // clear the failed creation's error
+    }
+  }
+  if (ss != nullptr) {
     if ((e = hipEventRecord(ss->fork, stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return e;
     if ((e = records(ss->s)) != hipSuccess) return e;

@@ -424,9 +424,9 @@ size_t kda_prefill_backward_chunked_workspace_bytes(int B, int T, int H, int dk,
  * from `stream` by an event at the start of the call and joined back into it
  * before the last kernel, so all of the call's work is ordered on `stream`
  * as usual.  Calls from several host threads are serialised while they
- * enqueue.  A call made while `stream` is being captured into a graph puts
- * that second stream into the capture too; no other backward call on the
- * same device may run until the capture ends.
+ * enqueue.  A call made while `stream` is being captured into a graph, or
+ * one for which the second stream cannot be created, runs in order on
+ * `stream` alone (same results, bit for bit).
  */
 kda_status kda_prefill_backward_chunked(const void* q, const void* k, const void* v,
                                         const float* alpha, const float* beta, const float* S0,

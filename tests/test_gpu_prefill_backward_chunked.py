@@ -133,6 +133,35 @@ def test_repeat_calls_are_bit_identical():
         assert torch.equal(s, t), n
 
 
+def test_graph_capture_replays_match_the_eager_call():
+    """Captured into a graph the call runs in order on the captured stream
+    (eagerly, with few chains, part of it runs on the library's second
+    stream); every replay, with eager work and synchronisations between,
+    equals the eager call bit for bit."""
+    sp = spec()
+    x = wl.make_prefill_inputs(sp, DEV, T=200, B=1, H=4)
+    gr = wl.make_prefill_backward_grads(sp, DEV, T=200, B=1, H=4)
+    args = (x["q"], x["k"], x["v"], x["alpha"], x["beta"], gr["dO"])
+    ref = kda().prefill_backward_chunked(*args, S0=x["S0"], dS_T=gr["dS_T"])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        kda().prefill_backward_chunked(*args, S0=x["S0"], dS_T=gr["dS_T"])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = kda().prefill_backward_chunked(*args, S0=x["S0"], dS_T=gr["dS_T"])
+    for i in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        for n, a, b in zip(NAMES, out, ref):
+            assert torch.equal(a, b), (i, n)
+        (x["q"].float() * 2.0).sum().item()
+        torch.cuda.synchronize()
+
+
 def test_no_tokens_passes_the_state_gradient_through():
     m = kda()
     B, H, d = 2, 3, 128
