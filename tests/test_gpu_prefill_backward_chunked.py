@@ -162,6 +162,42 @@ def test_graph_capture_replays_match_the_eager_call():
         torch.cuda.synchronize()
 
 
+def test_concurrent_calls_from_two_threads():
+    """Two host threads call the backward at once, each on a stream of its
+    own, five times: they share the library's second stream and its events,
+    and every result equals the single-threaded call bit for bit."""
+    import threading
+    sp = spec()
+    x = wl.make_prefill_inputs(sp, DEV, T=300, B=1, H=4)
+    gr = wl.make_prefill_backward_grads(sp, DEV, T=300, B=1, H=4)
+    args = (x["q"], x["k"], x["v"], x["alpha"], x["beta"], gr["dO"])
+    ref = kda().prefill_backward_chunked(*args, S0=x["S0"], dS_T=gr["dS_T"])
+    torch.cuda.synchronize()
+    outs, errs = [[], []], []
+
+    def work(i):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for _ in range(5):
+                    outs[i].append(kda().prefill_backward_chunked(*args, S0=x["S0"], dS_T=gr["dS_T"]))
+            st.synchronize()
+        except Exception as e:  # noqa: BLE001 - reported below
+            errs.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errs, errs
+    for i in range(2):
+        assert len(outs[i]) == 5
+        for o in outs[i]:
+            for n, a, b in zip(NAMES, o, ref):
+                assert torch.equal(a, b), (i, n)
+
+
 def test_no_tokens_passes_the_state_gradient_through():
     m = kda()
     B, H, d = 2, 3, 128
