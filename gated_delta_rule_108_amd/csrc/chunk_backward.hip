@@ -138,7 +138,7 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 // ---------------------------------------------------------------------------
 // 2. Sub-chunk records.  One workgroup of two waves per (chain, sub-chunk):
-// 26 KiB of LDS and ~100 registers, so that six workgroups share a CU and
+// 19.8 KiB of LDS and ~90 registers, so that eight workgroups share a CU and
 // one's loads overlap another's arithmetic (one workgroup of eight waves per
 // 64-token chunk, one per CU by its LDS, took 88 us on H=16 T=4096).
 // ---------------------------------------------------------------------------
@@ -151,11 +151,16 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   using RB = BRec<DK>;
   constexpr int NM = DK / 16, LDK = DK + 8, LDT = kSB + 8;
   constexpr int NTH = DK * kPS;
-  __shared__ __attribute__((aligned(16))) uint16_t sKF[kPS][kSB * LDK];   // K.F
-  __shared__ __attribute__((aligned(16))) uint16_t sKI[kPS][kSB * LDK];   // K / F (safe channels)
+  // K.F and K / F (safe channels) feed only the A and P products; after
+  // them the same bytes hold (beta K.F)^T, so that eight workgroups share a CU
+  static_assert(kPS == 1, "one sub-chunk per workgroup");
+  static_assert(DK * LDT <= 2 * kSB * LDK, "(beta K.F)^T fits where K.F and K / F were");
+  __shared__ __attribute__((aligned(16))) uint16_t sKFI[2 * kSB * LDK];
+  uint16_t (*sKF)[kSB * LDK] = reinterpret_cast<uint16_t (*)[kSB * LDK]>(sKFI);            // K.F
+  uint16_t (*sKI)[kSB * LDK] = reinterpret_cast<uint16_t (*)[kSB * LDK]>(sKFI + kSB * LDK);  // K / F
+  uint16_t (*sBK)[DK * LDT] = reinterpret_cast<uint16_t (*)[DK * LDT]>(sKFI);               // (beta K.F)^T
   __shared__ __attribute__((aligned(16))) uint16_t sQF[kPS][kSB * LDK];   // Q.F
   __shared__ __attribute__((aligned(16))) uint16_t sKH[kPS][kSB * LDK];   // K.H
-  __shared__ __attribute__((aligned(16))) uint16_t sBK[kPS][DK * LDT];    // (beta K.F)^T
   __shared__ __attribute__((aligned(16))) uint16_t sY[kPS][kSB * LDT];    // Y
   __shared__ float sA[kPS][kSB * 17];
   __shared__ float sBT[kPS][DK];
@@ -177,9 +182,12 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   lds_barrier();
 
   // ---- gates and gated operands, item (channel c, sub-chunk J); rows past T
-  // are identity steps (alpha 1, k = q = 0, beta 0)
-  for (int it = tid; it < DK * kPS; it += NTH) {
-    const int c = it % DK, J = it / DK;
+  // are identity steps (alpha 1, k = q = 0, beta 0).  The beta K.F row of
+  // channel c waits in registers until the A and P products are done.
+  static_assert(DK == NTH, "one channel per thread");
+  uint32_t bkw[8];
+  {
+    const int c = tid, J = 0;
     float a[kSB], kk[kSB], qq[kSB];
 #pragma unroll
     for (int r = 0; r < kSB; ++r) {
@@ -214,14 +222,10 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
       sQF[J][r * LDK + c] = f32_to_bf16(qq[r] * F[r]);
       sKH[J][r * LDK + c] = f32_to_bf16(kk[r] * Hs[r]);
     }
-    uint32_t w[8];
 #pragma unroll
     for (int x = 0; x < 8; ++x)
-      w[x] = pack_bf16x2(sBe[kSB * J + 2 * x] * kk[2 * x] * F[2 * x],
-                         sBe[kSB * J + 2 * x + 1] * kk[2 * x + 1] * F[2 * x + 1]);
-    uint4* bk = reinterpret_cast<uint4*>(sBK[J] + c * LDT);
-    bk[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    bk[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      bkw[x] = pack_bf16x2(sBe[kSB * J + 2 * x] * kk[2 * x] * F[2 * x],
+                           sBe[kSB * J + 2 * x + 1] * kk[2 * x + 1] * F[2 * x + 1]);
     if (live(J)) {
       char* rec = rec_of(J);
       reinterpret_cast<float*>(rec + RB::oG)[c] = bt;
@@ -286,6 +290,12 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
     }
   }
   lds_barrier();
+  {
+    // K.F and K / F are spent: (beta K.F)^T row c in their place
+    uint4* bk = reinterpret_cast<uint4*>(sBK[0] + tid * LDT);
+    bk[0] = make_uint4(bkw[0], bkw[1], bkw[2], bkw[3]);
+    bk[1] = make_uint4(bkw[4], bkw[5], bkw[6], bkw[7]);
+  }
 
   // ---- Y = (I + Diag(beta) A)^-1 per sub-chunk by forward substitution:
   // wave J, lane j < 16 owns column j
