@@ -138,13 +138,13 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 // ---------------------------------------------------------------------------
 // 2. Sub-chunk records.  One workgroup of two waves per (chain, sub-chunk):
-// 19.8 KiB of LDS and ~90 registers, so that eight workgroups share a CU and
+// 15.5 KiB of LDS and ~100 registers, so that ten workgroups share a CU and
 // one's loads overlap another's arithmetic (one workgroup of eight waves per
 // 64-token chunk, one per CU by its LDS, took 88 us on H=16 T=4096).
 // ---------------------------------------------------------------------------
 constexpr int kPS = 1;   // sub-chunks per record workgroup (2 measured the same)
 template <int DK>
-__global__ void __launch_bounds__(DK * kPS)
+__global__ void __launch_bounds__(DK * kPS) __attribute__((amdgpu_waves_per_eu(5)))
 kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__ gk,
                    const float* __restrict__ galpha, const float* __restrict__ gbeta,
                    char* __restrict__ grec, int T, int H) {
@@ -159,8 +159,9 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   uint16_t (*sKF)[kSB * LDK] = reinterpret_cast<uint16_t (*)[kSB * LDK]>(sKFI);            // K.F
   uint16_t (*sKI)[kSB * LDK] = reinterpret_cast<uint16_t (*)[kSB * LDK]>(sKFI + kSB * LDK);  // K / F
   uint16_t (*sBK)[DK * LDT] = reinterpret_cast<uint16_t (*)[DK * LDT]>(sKFI);               // (beta K.F)^T
+  // Q.F feeds only the P product; after it the same bytes hold K.H
   __shared__ __attribute__((aligned(16))) uint16_t sQF[kPS][kSB * LDK];   // Q.F
-  __shared__ __attribute__((aligned(16))) uint16_t sKH[kPS][kSB * LDK];   // K.H
+  uint16_t (*sKH)[kSB * LDK] = sQF;                                        // K.H
   __shared__ __attribute__((aligned(16))) uint16_t sY[kPS][kSB * LDT];    // Y
   __shared__ float sA[kPS][kSB * 17];
   __shared__ float sBT[kPS][DK];
@@ -185,7 +186,7 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   // are identity steps (alpha 1, k = q = 0, beta 0).  The beta K.F row of
   // channel c waits in registers until the A and P products are done.
   static_assert(DK == NTH, "one channel per thread");
-  uint32_t bkw[8];
+  uint32_t bkw[8], khw[8];
   {
     const int c = tid, J = 0;
     float a[kSB], kk[kSB], qq[kSB];
@@ -220,8 +221,9 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
       sKF[J][r * LDK + c] = f32_to_bf16(kk[r] * F[r]);
       sKI[J][r * LDK + c] = f32_to_bf16(kk[r] * Hs[r] * rbt);
       sQF[J][r * LDK + c] = f32_to_bf16(qq[r] * F[r]);
-      sKH[J][r * LDK + c] = f32_to_bf16(kk[r] * Hs[r]);
     }
+#pragma unroll
+    for (int x = 0; x < 8; ++x) khw[x] = pack_bf16x2(kk[2 * x] * Hs[2 * x], kk[2 * x + 1] * Hs[2 * x + 1]);
 #pragma unroll
     for (int x = 0; x < 8; ++x)
       bkw[x] = pack_bf16x2(sBe[kSB * J + 2 * x] * kk[2 * x] * F[2 * x],
@@ -291,10 +293,16 @@ kda_cb_prep_kernel(const uint16_t* __restrict__ gq, const uint16_t* __restrict__
   }
   lds_barrier();
   {
-    // K.F and K / F are spent: (beta K.F)^T row c in their place
+    // K.F and K / F are spent: (beta K.F)^T row c in their place; Q.F is
+    // spent: K.H channel c in its place
     uint4* bk = reinterpret_cast<uint4*>(sBK[0] + tid * LDT);
     bk[0] = make_uint4(bkw[0], bkw[1], bkw[2], bkw[3]);
     bk[1] = make_uint4(bkw[4], bkw[5], bkw[6], bkw[7]);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      sKH[0][(2 * x) * LDK + tid] = static_cast<uint16_t>(khw[x] & 0xffffu);
+      sKH[0][(2 * x + 1) * LDK + tid] = static_cast<uint16_t>(khw[x] >> 16);
+    }
   }
 
   // ---- Y = (I + Diag(beta) A)^-1 per sub-chunk by forward substitution:
